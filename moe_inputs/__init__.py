@@ -1,0 +1,192 @@
+"""Seeded synthetic inputs for the routed-expert MXFP4 MoE layer.
+
+This module only draws random numbers and lays them out; it holds none of the
+method's arithmetic (no decoding, routing or matrix products).  Both the fp64
+CPU oracle and the GPU library consume what it produces, so neither side ever
+takes an input from the other.
+
+Every tensor comes from its own keyed PCG64 stream,
+``numpy.random.default_rng([seed, config_id, tensor_id, expert])``, so any
+single expert matrix can be regenerated alone (the FFN oracle only needs the
+experts a batch actually routes to).
+
+Workload shapes follow the Kimi-K3 routed experts described on the llama.cpp
+pull-request page "model: add Kimi-K3 text model": 896 experts, 16 used,
+sigmoid gating with an ``exp_probs_b`` bias (comment "Dry run: prepare_tensors()
+completes"), and expert w1 of logical shape [3072, 3584] (comment
+"repack_mxfp4_blocks is bit-exact"); the verify width 8 (current token plus 7
+proposals) comes from the lucebox page "feat(kimi-k3): add DSpark Q8 artifact
+and shared speculative runtime", comment "DSpark acceptance-contract correction".
+"""
+
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import numpy as np
+
+# tensor ids used as keys of the per-tensor streams
+T_W1, T_W3, T_W2, T_X, T_LOGITS, T_BIAS, T_PERM, T_SINGLE = 1, 2, 3, 4, 5, 6, 7, 8
+
+
+def rng(seed: int, *key: int) -> np.random.Generator:
+    """PCG64 stream keyed by (seed, *key)."""
+    return np.random.default_rng([int(seed), *[int(k) for k in key]])
+
+
+def mxfp4_source(g: np.random.Generator, rows: int, cols: int, e_lo: int, e_hi: int):
+    """Source-layout MXFP4 matrix with uniform random 4-bit codes.
+
+    Returns ``packed`` u8 [rows, cols/2] (two uniform codes per byte, the
+    negative-zero code included) and ``scale`` u8 [rows, cols/32] with E8M0
+    exponents uniform over the closed range [e_lo, e_hi].
+    """
+    assert cols % 32 == 0
+    packed = np.frombuffer(g.bytes(rows * cols // 2), dtype=np.uint8).reshape(rows, cols // 2).copy()
+    scale = g.integers(e_lo, e_hi + 1, size=(rows, cols // 32), dtype=np.uint8)
+    return packed, scale
+
+
+def bf16_bits(a: np.ndarray) -> np.ndarray:
+    """Round fp32 values to bfloat16 (nearest-even) and return the raw u16 bits.
+
+    Input preparation only: the layer consumes bf16 activations.
+    """
+    import torch
+
+    t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(torch.bfloat16)
+    return t.view(torch.int16).numpy().view(np.uint16).copy()
+
+
+def bf16_to_f32(bits: np.ndarray) -> np.ndarray:
+    """Widen raw bf16 bits to fp32 (exact)."""
+    return (bits.astype(np.uint32) << 16).view(np.float32)
+
+
+@dataclass(frozen=True)
+class LayerConfig:
+    """One synthetic MoE-layer workload."""
+
+    name: str
+    config_id: int
+    E: int
+    k: int
+    D: int
+    I: int
+    T: int
+    e_lo: int = 118
+    e_hi: int = 124
+    logits: str = "normal"  # "normal" | "uniform" | "zipf"
+    bias_sigma: float = 0.0  # 0 -> bias is identically zero
+    zipf_s: float = 1.1
+    seed: int = 0
+    weight_id: int = -1  # key of the expert-weight streams; -1 -> config_id
+    notes: str = ""
+
+    def with_(self, **kw) -> "LayerConfig":
+        d = dict(self.__dict__)
+        d.update(kw)
+        return LayerConfig(**d)
+
+
+# The five workloads (shapes from the pages; distributions as stated for each).
+TINY = LayerConfig("tiny", 0, E=8, k=2, D=128, I=256, T=64, logits="normal", bias_sigma=0.1,
+                   notes="8 experts, top-2, bias N(0,0.1), exps 118..124, 64 tokens")
+# All K3-shaped workloads share one set of expert weights (weight_id 2).
+K3_WEIGHTS = 2
+DECODE1 = LayerConfig("decode-t1", 2, E=896, k=16, D=3584, I=3072, T=1, logits="uniform", weight_id=K3_WEIGHTS,
+                      notes="K3 decode, 1 token, uniform logits, zero bias")
+DECODE8 = DECODE1.with_(name="decode-t8", config_id=5, T=8, notes="K3 decode, 8 tokens, uniform logits, zero bias")
+VERIFY = LayerConfig("verify", 3, E=896, k=16, D=3584, I=3072, T=128, logits="zipf", weight_id=K3_WEIGHTS,
+                     notes="K3 speculative verify: 16 sequences x width 8, Zipf(1.1) skewed logits")
+PREFILL = LayerConfig("prefill", 4, E=896, k=16, D=3584, I=3072, T=4096, logits="normal", bias_sigma=0.5,
+                      weight_id=K3_WEIGHTS, notes="K3 prefill: 4096 tokens, logits N(0,1), bias N(0,0.5)")
+
+CONFIGS = {c.name: c for c in (TINY, DECODE1, DECODE8, VERIFY, PREFILL)}
+
+# Repack/dequant workload: one K3-shaped expert tensor [3072, 3584].
+REPACK_ROWS, REPACK_COLS = 3072, 3584
+REPACK_CONFIG_ID = 1
+
+
+def repack_tensor(seed: int = 0, e_lo: int = 0, e_hi: int = 254):
+    """One [3072, 3584] source tensor with uniform nibbles and E8M0 in [e_lo, e_hi]."""
+    sub = 0 if (e_lo, e_hi) == (0, 254) else 1
+    return mxfp4_source(rng(seed, REPACK_CONFIG_ID, T_SINGLE, sub), REPACK_ROWS, REPACK_COLS, e_lo, e_hi)
+
+
+class ExpertSource:
+    """Lazily generated source-layout weights of every expert of one config.
+
+    ``src[e]`` returns ``((p1, s1), (p3, s3), (p2, s2))``: w1 and w3 are
+    [I, D] (rows = intermediate features, blocks along D) and w2 is [D, I]
+    (rows = latent features, blocks along I).
+    """
+
+    def __init__(self, cfg: LayerConfig):
+        self.cfg = cfg
+
+    def matrix(self, tensor_id: int, e: int):
+        c = self.cfg
+        rows, cols = (c.I, c.D) if tensor_id in (T_W1, T_W3) else (c.D, c.I)
+        wid = c.config_id if c.weight_id < 0 else c.weight_id
+        return mxfp4_source(rng(c.seed, 100 + wid, tensor_id, e), rows, cols, c.e_lo, c.e_hi)
+
+    def __getitem__(self, e: int):
+        return self.matrix(T_W1, e), self.matrix(T_W3, e), self.matrix(T_W2, e)
+
+    def __len__(self):
+        return self.cfg.E
+
+
+def activations(cfg: LayerConfig, seed: int | None = None) -> np.ndarray:
+    """x ~ bf16(N(0,1)), shape [T, D], returned as raw bf16 bits (u16)."""
+    s = cfg.seed if seed is None else seed
+    g = rng(s, cfg.config_id, T_X)
+    return bf16_bits(g.standard_normal((cfg.T, cfg.D), dtype=np.float32))
+
+
+def router_inputs(cfg: LayerConfig, seed: int | None = None):
+    """Router logits z [T, E] fp32 and expert bias b [E] fp32.
+
+    * "normal":  z ~ N(0,1)
+    * "uniform": z ~ U[0,1)
+    * "zipf":    z[t,e] = N(0,1) + ln p_rank(e), p_r proportional to r^-s over
+                 a seeded permutation of the experts (a few experts are hot)
+    The bias is N(0, bias_sigma), or exactly zero when bias_sigma == 0.
+    """
+    s = cfg.seed if seed is None else seed
+    g = rng(s, cfg.config_id, T_LOGITS)
+    T, E = cfg.T, cfg.E
+    if cfg.logits == "uniform":
+        z = g.random((T, E), dtype=np.float32)
+    elif cfg.logits == "normal":
+        z = g.standard_normal((T, E), dtype=np.float32)
+    elif cfg.logits == "zipf":
+        ranks = rng(s, cfg.config_id, T_PERM).permutation(E) + 1  # rank of expert e, 1..E
+        p = ranks.astype(np.float64) ** (-cfg.zipf_s)
+        p /= p.sum()
+        z = (g.standard_normal((T, E)) + np.log(p)[None, :]).astype(np.float32)
+    else:
+        raise ValueError(cfg.logits)
+    if cfg.bias_sigma > 0:
+        b = (rng(s, cfg.config_id, T_BIAS).standard_normal(E) * cfg.bias_sigma).astype(np.float32)
+    else:
+        b = np.zeros(E, np.float32)
+    return np.ascontiguousarray(z), b
+
+
+@dataclass
+class Batch:
+    """Everything one forward pass of the layer consumes (host side)."""
+
+    cfg: LayerConfig
+    x: np.ndarray  # u16 bf16 bits [T, D]
+    z: np.ndarray  # f32 [T, E]
+    b: np.ndarray  # f32 [E]
+    experts: ExpertSource = field(repr=False, default=None)
+
+
+def make_batch(cfg: LayerConfig, seed: int | None = None) -> Batch:
+    z, b = router_inputs(cfg, seed)
+    return Batch(cfg, activations(cfg, seed), z, b, ExpertSource(cfg))

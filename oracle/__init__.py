@@ -1,0 +1,41 @@
+"""Plain fp64 CPU oracle for the routed-expert MXFP4 MoE layer.
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import, call or
+execute this package: only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` use it.  It shares no code, table or
+constant with the HIP library (``mxfp4_mixture_experts_moe_amd``), and the
+library never imports it.
+
+It is written straight from the definitions on the pages it cites, in the
+simplest form a reader can check by eye: numpy in fp64, with library
+primitives (matmul, stable sort) as single steps and no blocking or fusion.
+
+Modules
+-------
+``mxfp4``   the two MXFP4 block encodings: source decode, repack, ggml dequant
+``route``   sigmoid + bias top-k routing
+``permute`` stable grouping of (token, slot) entries by expert
+``ffn``     the routed-expert FFN: route -> per-expert SiLU-gated MLP -> weighted sum
+
+Parity status
+-------------
+Every function here is pinned by ``tests/test_oracle_*.py`` against something
+other than itself (values printed on the pages, IEEE-754 closed forms, a
+library decode of E8M0, a textbook sort, brute-force loops, an identity-weight
+closed form).  The FFN's numerics beyond those closed forms have no worked
+example on the pages; ``ffn_ref`` is pinned by a pure-Python loop evaluation
+and the identity case only.
+"""
+
+from .mxfp4 import (  # noqa: F401
+    E2M1,
+    KVALUES,
+    decode_ct,
+    dequant_ref,
+    repack_ref,
+    source_codes,
+    unrepack_ref,
+)
+from .route import route_ref  # noqa: F401
+from .permute import permute_ref, valid_entries  # noqa: F401
+from .ffn import ffn_ref, silu_mul  # noqa: F401

@@ -1,0 +1,33 @@
+import os
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def pytest_configure(config):
+    config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) and the built HIP library")
+    config.addinivalue_line("markers", "slow: full-size case (seconds to minutes)")
+
+
+def read_golden(name):
+    """Parse a golden fixture: '#' comments, then 'key v1 v2 ...' lines."""
+    out = {}
+    with open(os.path.join(GOLDEN, name)) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            key, *vals = line.split()
+            out[key] = vals
+    return out
+
+
+@pytest.fixture
+def golden():
+    return read_golden
