@@ -1,0 +1,167 @@
+/*
+ * k3moe.h — C ABI of the routed-expert MXFP4 MoE layer for MI355X (gfx950).
+ *
+ * The layer is the Kimi-K3 routed-expert FFN: each token's latent activation is
+ * routed by sigmoid scores plus a per-expert bias to the top-k experts; every
+ * expert is a SiLU-gated MLP whose three matrices are stored as MXFP4 (4-bit
+ * E2M1 codes in 32-element blocks, one E8M0 exponent per block) in 17-byte ggml
+ * blocks; the expert outputs are summed with the gate weights.
+ *
+ * General conventions (all entry points):
+ *   - Array pointers are DEVICE pointers unless stated otherwise. The caller
+ *     allocates and owns every buffer; the library allocates nothing, keeps no
+ *     state between calls and never synchronizes the host.
+ *   - `stream` is a hipStream_t (NULL = the default stream). Every call only
+ *     enqueues work on it and returns; results are ready when the stream is.
+ *   - Arrays are row-major and contiguous. Inputs are never written. Outputs
+ *     are fully overwritten (never accumulated into).
+ *   - Every argument check runs on the host before anything is enqueued; a
+ *     failing check returns a negative k3moe_status and enqueues nothing. The
+ *     library never aborts the process. Device pointers must be 16-byte
+ *     aligned (K3MOE_ERR_ALIGN otherwise).
+ *   - Calls are reentrant; calls on different streams may run concurrently as
+ *     long as their output/workspace buffers are distinct.
+ */
+#ifndef K3MOE_H
+#define K3MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  K3MOE_OK = 0,
+  K3MOE_ERR_NULL = -1,        /* a required pointer is NULL */
+  K3MOE_ERR_SHAPE = -2,       /* a size argument is out of range or inconsistent */
+  K3MOE_ERR_ALIGN = -3,       /* a device pointer is not 16-byte aligned */
+  K3MOE_ERR_WORKSPACE = -4,   /* workspace smaller than moe_mxfp4_ffn_workspace_size() */
+  K3MOE_ERR_UNSUPPORTED = -5, /* unknown enum value (activation, output dtype) */
+  K3MOE_ERR_DEVICE = -6       /* the HIP runtime refused a launch (e.g. no gfx950 device) */
+} k3moe_status;
+
+/* Largest top-k the router and FFN accept. */
+#define K3MOE_MAX_TOPK 64
+/* Largest expert count moe_mxfp4_ffn accepts (its grouping keeps one 64-bit
+   token bitmap per expert in LDS). moe_route_topk has no expert limit. */
+#define K3MOE_MAX_EXPERTS_FFN 8192
+
+/* Activation hook ids ("situ" is named but not defined by the sources; the
+   only hook provided is SiLU(gate) * up). */
+#define K3MOE_ACT_SILU_MUL 0
+
+/* Output dtypes of mxfp4_dequant. */
+#define K3MOE_DTYPE_F32 0
+#define K3MOE_DTYPE_BF16 1
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* k3moe_status_str(int status);
+
+/*
+ * moe_route_topk — sigmoid + bias top-k routing.
+ * Source: llama.cpp pull request "model: add Kimi-K3 text model", review
+ * comment on the converter dry run (expert count 896, experts used 16, expert
+ * score gating function sigmoid, per-expert bias tensor exp_probs_b).
+ *
+ *   logits  f32 [T, E]   router logits z
+ *   bias    f32 [E]      per-expert selection bias b, or NULL for zero
+ *   topk_ids i32 [T, k]  out: selected experts, best first
+ *   topk_w   f32 [T, k]  out: gate weights, aligned with topk_ids
+ *
+ * Score s[t,e] = 1/(1+exp(-z[t,e])) + b[e], evaluated in fp64; a NaN score
+ * ranks below every number. Experts are taken in order of decreasing score,
+ * the lower index first among equal scores. The gate weight of a selected
+ * expert is its sigmoid(z) (the bias only steers selection), divided by the
+ * sum over the k selected when `normalize` != 0, then times `route_scale`,
+ * rounded once to f32.
+ * Sizes: T >= 0 (T == 0 is a no-op), 1 <= k <= min(E, K3MOE_MAX_TOPK), E >= 1
+ * (no upper limit). K3MOE_ERR_SHAPE otherwise.
+ */
+int moe_route_topk(const float* logits, const float* bias, int64_t T, int32_t E, int32_t k,
+                   int32_t normalize, float route_scale, int32_t* topk_ids, float* topk_w,
+                   void* stream);
+
+/*
+ * mxfp4_repack — compressed-tensors MXFP4 -> 17-byte ggml blocks (lossless).
+ * Source: llama.cpp pull request "model: add Kimi-K3 text model", review
+ * comment "repack_mxfp4_blocks is bit-exact — 0 mismatches over 11,010,048
+ * values" (reference-side and ggml-side layouts, byte accounting).
+ *
+ *   packed  u8 [R, K/2]       element 2i of a row in the low nibble of byte i,
+ *                             element 2i+1 in the high nibble
+ *   scale   u8 [R, K/32]      E8M0 exponent of each 32-element block
+ *   blocks  u8 [R, K/32, 17]  out: byte 0 = the exponent byte unchanged,
+ *                             byte 1+j = code(j) | code(j+16) << 4
+ *
+ * Every 4-bit code and every exponent byte is copied unchanged, only moved;
+ * with ggml's doubled value table and halved scale the represented values
+ * are unchanged. Sizes: R >= 0 (R == 0 is a no-op), K > 0 and K % 32 == 0.
+ */
+int mxfp4_repack(const uint8_t* packed, const uint8_t* scale, int64_t R, int64_t K, uint8_t* blocks,
+                 void* stream);
+
+/*
+ * mxfp4_dequant — decode 17-byte ggml MXFP4 blocks.
+ * Source: same review comment (ggml-side decode: dequantize_row_mxfp4 with
+ * kvalues_fp4 = doubled E2M1 values and the half scale 2^(x-128), whose bits
+ * are (x-1) << 23 for x >= 2).
+ *
+ *   blocks  u8 [R, K/32, 17]
+ *   out     [R, K] f32 (out_dtype K3MOE_DTYPE_F32) or bf16 (K3MOE_DTYPE_BF16)
+ *
+ * Element j of a block is kvalues[low nibble of byte 1+j] * 2^(x-128), element
+ * j+16 uses the high nibble. The product is exact: x = 0 and 1 give fp32
+ * subnormals, large x overflow to +-inf, the zero codes give +0. Every finite
+ * value is also exact in bf16. Sizes: R >= 0, K > 0, K % 32 == 0.
+ * Unknown out_dtype -> K3MOE_ERR_UNSUPPORTED.
+ */
+int mxfp4_dequant(const uint8_t* blocks, int64_t R, int64_t K, int32_t out_dtype, void* out, void* stream);
+
+/*
+ * moe_mxfp4_ffn_workspace_size — bytes of device workspace moe_mxfp4_ffn needs
+ * for these sizes (0 when T == 0). Pure host computation.
+ */
+size_t moe_mxfp4_ffn_workspace_size(int64_t T, int32_t D, int32_t I, int32_t E, int32_t k);
+
+/*
+ * moe_mxfp4_ffn — the routed-expert FFN with MXFP4 expert weights.
+ * Sources: llama.cpp pull request "model: add Kimi-K3 text model": opening
+ * comment (latent MoE: routed experts run at the latent width; the "situ"
+ * activation), the dry-run comment (each expert is a w1 | w2 | w3 group), the
+ * repack comment (w1 of one expert is logical [3072, 3584]; ggml block layout);
+ * and the LLAMA_MAX_EXPERTS comment (build_moe_ffn: route -> per-expert
+ * products -> weighted sum).
+ *
+ *   x_bf16   bf16 [T, D]        latent activations
+ *   topk_ids i32  [T, k]        routed experts of each token
+ *   topk_w   f32  [T, k]        gate weights
+ *   w1, w3   u8 [E, I, D/32, 17] gate / up matrices ([I, D] per expert,
+ *                               blocks along D) as ggml MXFP4 blocks
+ *   w2       u8 [E, D, I/32, 17] down matrix ([D, I] per expert)
+ *   out      f32  [T, D]        out[t] = sum_j w[t,j] * W2 act(W1 x_t, W3 x_t)
+ *   workspace device buffer of at least moe_mxfp4_ffn_workspace_size() bytes;
+ *             its contents on entry do not matter and are clobbered
+ *
+ * act must be K3MOE_ACT_SILU_MUL: act(g, u) = g * sigmoid(g) * u.
+ * Precision: bf16 x and bf16-exact weights, bf16 MFMA with fp32 accumulation;
+ * h = act(g, u) is formed in fp32 and enters the down product as the bf16 pair
+ * hi = bf16(h), lo = bf16(h - hi) (about 16 significant bits); fp32 output.
+ * The k expert outputs of a token are summed in slot order (deterministic, no
+ * atomics).
+ * Entry (t, j) is skipped (contributes nothing) when topk_ids[t,j] is outside
+ * [0, E) or repeats an id earlier in the same row.
+ * Sizes: T >= 0 (T == 0 is a no-op), D > 0 and I > 0 multiples of 128,
+ * 1 <= k <= K3MOE_MAX_TOPK, 1 <= E <= K3MOE_MAX_EXPERTS_FFN.
+ * E8M0 exponent bytes of the weights must be <= 254 (255 is not supported).
+ */
+int moe_mxfp4_ffn(const void* x_bf16, const int32_t* topk_ids, const float* topk_w, const uint8_t* w1,
+                  const uint8_t* w3, const uint8_t* w2, int64_t T, int32_t D, int32_t I, int32_t E, int32_t k,
+                  int32_t act, float* out, void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* K3MOE_H */

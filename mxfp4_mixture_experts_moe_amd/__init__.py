@@ -1,0 +1,190 @@
+"""Python binding of libk3moe (the routed-expert MXFP4 MoE layer for MI355X).
+
+Argument marshalling only: every function checks dtypes, devices and
+contiguity, allocates outputs with torch when the caller passes none, and calls
+the C entry point of the same name (include/k3moe.h) on torch's current HIP
+stream.  All arithmetic runs in the library's HIP kernels; there is no CPU or
+PyTorch fallback, and importing the package fails loudly when the library has
+not been built.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "K3MoeError",
+    "LIB_PATH",
+    "ACT_SILU_MUL",
+    "moe_route_topk",
+    "mxfp4_repack",
+    "mxfp4_dequant",
+    "moe_mxfp4_ffn_workspace_size",
+    "moe_mxfp4_ffn",
+    "status_str",
+    "lib",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libk3moe.so")
+ACT_SILU_MUL = 0
+DTYPE_F32, DTYPE_BF16 = 0, 1
+MAX_TOPK = 64
+MAX_EXPERTS_FFN = 8192
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is missing: build it with `python -m mxfp4_mixture_experts_moe_amd.build` "
+        "(there is no fallback implementation)"
+    )
+lib = ctypes.CDLL(LIB_PATH)
+
+_vp, _i32, _i64, _f32, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+lib.k3moe_status_str.restype = ctypes.c_char_p
+lib.k3moe_status_str.argtypes = [ctypes.c_int]
+lib.moe_route_topk.restype = ctypes.c_int
+lib.moe_route_topk.argtypes = [_vp, _vp, _i64, _i32, _i32, _i32, _f32, _vp, _vp, _vp]
+lib.mxfp4_repack.restype = ctypes.c_int
+lib.mxfp4_repack.argtypes = [_vp, _vp, _i64, _i64, _vp, _vp]
+lib.mxfp4_dequant.restype = ctypes.c_int
+lib.mxfp4_dequant.argtypes = [_vp, _i64, _i64, _i32, _vp, _vp]
+lib.moe_mxfp4_ffn_workspace_size.restype = _sz
+lib.moe_mxfp4_ffn_workspace_size.argtypes = [_i64, _i32, _i32, _i32, _i32]
+lib.moe_mxfp4_ffn.restype = ctypes.c_int
+lib.moe_mxfp4_ffn.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _sz, _vp]
+
+
+class K3MoeError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn}: {status_str(status)} (status {status})")
+        self.status = status
+
+
+def status_str(status: int) -> str:
+    return lib.k3moe_status_str(int(status)).decode()
+
+
+def _check(fn: str, status: int) -> None:
+    if status != 0:
+        raise K3MoeError(fn, status)
+
+
+def _ptr(t: torch.Tensor | None) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _dev(t: torch.Tensor, name: str, dtype: torch.dtype | tuple) -> None:
+    dts = dtype if isinstance(dtype, tuple) else (dtype,)
+    if t.dtype not in dts:
+        raise TypeError(f"{name}: expected dtype {dts}, got {t.dtype}")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name}: must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+
+
+def _stream(device: torch.device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def moe_route_topk(logits: torch.Tensor, bias: torch.Tensor | None, k: int, normalize: bool = True,
+                   route_scale: float = 1.0, ids: torch.Tensor | None = None, weights: torch.Tensor | None = None):
+    """Sigmoid + bias top-k routing. logits f32 [T, E], bias f32 [E] or None.
+
+    Returns (ids int32 [T, k], weights f32 [T, k]).
+    """
+    _dev(logits, "logits", torch.float32)
+    T, E = logits.shape
+    if bias is not None:
+        _dev(bias, "bias", torch.float32)
+        if bias.shape != (E,):
+            raise ValueError("bias must be [E]")
+    if ids is None:
+        ids = torch.empty((T, k), dtype=torch.int32, device=logits.device)
+    if weights is None:
+        weights = torch.empty((T, k), dtype=torch.float32, device=logits.device)
+    _dev(ids, "ids", torch.int32)
+    _dev(weights, "weights", torch.float32)
+    if ids.shape != (T, k) or weights.shape != (T, k):
+        raise ValueError("ids / weights must be [T, k]")
+    _check("moe_route_topk", lib.moe_route_topk(_ptr(logits), _ptr(bias), T, E, k, int(bool(normalize)),
+                                                float(route_scale), _ptr(ids), _ptr(weights),
+                                                _stream(logits.device)))
+    return ids, weights
+
+
+def mxfp4_repack(packed: torch.Tensor, scale: torch.Tensor, blocks: torch.Tensor | None = None) -> torch.Tensor:
+    """compressed-tensors MXFP4 (packed u8 [..., R, K/2], scale u8 [..., R, K/32]) -> u8 [..., R, K/32, 17].
+
+    Leading dimensions are flattened into rows (the layout is row-independent).
+    """
+    _dev(packed, "packed", torch.uint8)
+    _dev(scale, "scale", torch.uint8)
+    K = packed.shape[-1] * 2
+    if scale.shape[:-1] != packed.shape[:-1] or scale.shape[-1] * 32 != K:
+        raise ValueError("scale must be [..., R, K/32] for packed [..., R, K/2]")
+    R = packed.numel() // (K // 2)
+    if blocks is None:
+        blocks = torch.empty((*packed.shape[:-1], K // 32, 17), dtype=torch.uint8, device=packed.device)
+    _dev(blocks, "blocks", torch.uint8)
+    if blocks.numel() != R * (K // 32) * 17:
+        raise ValueError("blocks has the wrong size")
+    _check("mxfp4_repack", lib.mxfp4_repack(_ptr(packed), _ptr(scale), R, K, _ptr(blocks), _stream(packed.device)))
+    return blocks
+
+
+def mxfp4_dequant(blocks: torch.Tensor, out_dtype: torch.dtype = torch.float32,
+                  out: torch.Tensor | None = None) -> torch.Tensor:
+    """ggml MXFP4 blocks u8 [..., R, K/32, 17] -> [..., R, K] f32 or bf16."""
+    _dev(blocks, "blocks", torch.uint8)
+    if blocks.shape[-1] != 17:
+        raise ValueError("blocks must end in a 17-byte dimension")
+    nb = blocks.shape[-2]
+    K = nb * 32
+    R = blocks.numel() // (nb * 17)
+    code = {torch.float32: DTYPE_F32, torch.bfloat16: DTYPE_BF16}.get(out_dtype)
+    if code is None:
+        raise TypeError("out_dtype must be float32 or bfloat16")
+    if out is None:
+        out = torch.empty((*blocks.shape[:-2], K), dtype=out_dtype, device=blocks.device)
+    _dev(out, "out", out_dtype)
+    if out.numel() != R * K:
+        raise ValueError("out has the wrong size")
+    _check("mxfp4_dequant", lib.mxfp4_dequant(_ptr(blocks), R, K, code, _ptr(out), _stream(blocks.device)))
+    return out
+
+
+def moe_mxfp4_ffn_workspace_size(T: int, D: int, I: int, E: int, k: int) -> int:
+    return int(lib.moe_mxfp4_ffn_workspace_size(T, D, I, E, k))
+
+
+def moe_mxfp4_ffn(x: torch.Tensor, ids: torch.Tensor, weights: torch.Tensor, w1: torch.Tensor, w3: torch.Tensor,
+                  w2: torch.Tensor, act: int = ACT_SILU_MUL, out: torch.Tensor | None = None,
+                  workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """Routed-expert FFN. x bf16 [T, D]; ids int32 [T, k]; weights f32 [T, k];
+    w1/w3 u8 [E, I, D/32, 17]; w2 u8 [E, D, I/32, 17]. Returns out f32 [T, D]."""
+    _dev(x, "x", torch.bfloat16)
+    _dev(ids, "ids", torch.int32)
+    _dev(weights, "weights", torch.float32)
+    for n, t in (("w1", w1), ("w3", w3), ("w2", w2)):
+        _dev(t, n, torch.uint8)
+    T, D = x.shape
+    k = ids.shape[1]
+    E, I = w1.shape[0], w1.shape[1]
+    if ids.shape != (T, k) or weights.shape != (T, k):
+        raise ValueError("ids / weights must be [T, k]")
+    if w1.shape != (E, I, D // 32, 17) or w3.shape != w1.shape or w2.shape != (E, D, I // 32, 17):
+        raise ValueError("expert weights have inconsistent shapes")
+    if out is None:
+        out = torch.empty((T, D), dtype=torch.float32, device=x.device)
+    _dev(out, "out", torch.float32)
+    need = moe_mxfp4_ffn_workspace_size(T, D, I, E, k)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    _dev(workspace, "workspace", torch.uint8)
+    _check("moe_mxfp4_ffn", lib.moe_mxfp4_ffn(_ptr(x), _ptr(ids), _ptr(weights), _ptr(w1), _ptr(w3), _ptr(w2),
+                                              T, D, I, E, k, act, _ptr(out), _ptr(workspace), workspace.numel(),
+                                              _stream(x.device)))
+    return out

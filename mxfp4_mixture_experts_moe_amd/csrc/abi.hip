@@ -1,0 +1,184 @@
+// Host side of the k3moe C ABI: argument checks, workspace layout, launches.
+// Every check runs before anything is enqueued; nothing here aborts.
+#include "../../include/k3moe.h"
+#include "k3moe_internal.h"
+
+namespace k3moe {
+
+static size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+FfnWorkspace ffn_workspace_layout(int64_t T, int32_t D, int32_t I, int32_t E, int32_t k) {
+  FfnWorkspace w{};
+  const int64_t entries = T * (int64_t)k;
+  const int64_t active = entries < E ? entries : E;
+  w.max_tiles = entries / kMinTileRows + active;
+  w.n_chunks = (T + kChunkTokens - 1) / kChunkTokens;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off = align_up(off + bytes, 256);
+    return at;
+  };
+  w.counts = take(sizeof(int32_t) * (size_t)E);
+  w.offsets = take(sizeof(int32_t) * (size_t)(E + 1));
+  w.tile_count = take(sizeof(int32_t));
+  w.tiles = take(sizeof(Tile) * (size_t)(w.max_tiles > 0 ? w.max_tiles : 1));
+  w.row_tok = take(sizeof(int32_t) * (size_t)entries);
+  w.slot_row = take(sizeof(int32_t) * (size_t)entries);
+  w.chunk_base = take(sizeof(int32_t) * (size_t)(w.n_chunks * E));
+  w.chunk_mask = take(sizeof(unsigned long long) * (size_t)(w.n_chunks * E));
+  w.x_perm = take(sizeof(uint16_t) * (size_t)(T * D));
+  w.h = take(sizeof(uint16_t) * (size_t)(entries * I));
+  w.h_lo = take(sizeof(uint16_t) * (size_t)(entries * I));
+  w.y = take(sizeof(float) * (size_t)(entries * D));
+  w.total = off;
+  return w;
+}
+
+}  // namespace k3moe
+
+using namespace k3moe;
+
+namespace {
+
+bool misaligned(const void* p) { return p != nullptr && (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
+
+int device_status(hipError_t e) { return e == hipSuccess ? K3MOE_OK : K3MOE_ERR_DEVICE; }
+
+}  // namespace
+
+extern "C" {
+
+const char* k3moe_status_str(int status) {
+  switch (status) {
+    case K3MOE_OK: return "ok";
+    case K3MOE_ERR_NULL: return "a required pointer is NULL";
+    case K3MOE_ERR_SHAPE: return "a size argument is out of range or inconsistent";
+    case K3MOE_ERR_ALIGN: return "a device pointer is not 16-byte aligned";
+    case K3MOE_ERR_WORKSPACE: return "workspace is smaller than moe_mxfp4_ffn_workspace_size()";
+    case K3MOE_ERR_UNSUPPORTED: return "unsupported enum value";
+    case K3MOE_ERR_DEVICE: return "the HIP runtime refused a launch";
+    default: return "unknown status";
+  }
+}
+
+int moe_route_topk(const float* logits, const float* bias, int64_t T, int32_t E, int32_t k, int32_t normalize,
+                   float route_scale, int32_t* topk_ids, float* topk_w, void* stream) {
+  if (T < 0 || E < 1 || k < 1 || k > E || k > K3MOE_MAX_TOPK) return K3MOE_ERR_SHAPE;
+  if (T > (int64_t)0x7FFFFFFF * 4) return K3MOE_ERR_SHAPE;  // grid limit
+  if (T == 0) return K3MOE_OK;
+  if (!logits || !topk_ids || !topk_w) return K3MOE_ERR_NULL;
+  if (misaligned(logits) || misaligned(bias) || misaligned(topk_ids) || misaligned(topk_w)) return K3MOE_ERR_ALIGN;
+  return device_status(launch_route_topk(logits, bias, T, E, k, normalize, route_scale, topk_ids, topk_w,
+                                         static_cast<hipStream_t>(stream)));
+}
+
+int mxfp4_repack(const uint8_t* packed, const uint8_t* scale, int64_t R, int64_t K, uint8_t* blocks,
+                 void* stream) {
+  if (R < 0 || K <= 0 || (K % 32) != 0) return K3MOE_ERR_SHAPE;
+  const int64_t nblocks = R * (K / 32);
+  if (nblocks / 1024 > 0x7FFFFFFF) return K3MOE_ERR_SHAPE;
+  if (R == 0) return K3MOE_OK;
+  if (!packed || !scale || !blocks) return K3MOE_ERR_NULL;
+  if (misaligned(packed) || misaligned(scale) || misaligned(blocks)) return K3MOE_ERR_ALIGN;
+  return device_status(launch_repack(packed, scale, nblocks, blocks, static_cast<hipStream_t>(stream)));
+}
+
+int mxfp4_dequant(const uint8_t* blocks, int64_t R, int64_t K, int32_t out_dtype, void* out, void* stream) {
+  if (R < 0 || K <= 0 || (K % 32) != 0) return K3MOE_ERR_SHAPE;
+  if (out_dtype != K3MOE_DTYPE_F32 && out_dtype != K3MOE_DTYPE_BF16) return K3MOE_ERR_UNSUPPORTED;
+  const int64_t nblocks = R * (K / 32);
+  if (nblocks / 256 > 0x7FFFFFFF) return K3MOE_ERR_SHAPE;
+  if (R == 0) return K3MOE_OK;
+  if (!blocks || !out) return K3MOE_ERR_NULL;
+  if (misaligned(blocks) || misaligned(out)) return K3MOE_ERR_ALIGN;
+  return device_status(launch_dequant(blocks, nblocks, out_dtype == K3MOE_DTYPE_BF16, out,
+                                      static_cast<hipStream_t>(stream)));
+}
+
+static int ffn_shape_status(int64_t T, int32_t D, int32_t I, int32_t E, int32_t k) {
+  if (T < 0 || D <= 0 || I <= 0 || (D % 128) != 0 || (I % 128) != 0) return K3MOE_ERR_SHAPE;
+  if (E < 1 || E > K3MOE_MAX_EXPERTS_FFN || k < 1 || k > K3MOE_MAX_TOPK) return K3MOE_ERR_SHAPE;
+  // grouped rows and element offsets are int32 / int64 inside the kernels
+  if (T * (int64_t)k > 0x7FFFFFFF || T > 0x7FFFFFFF) return K3MOE_ERR_SHAPE;
+  return K3MOE_OK;
+}
+
+size_t moe_mxfp4_ffn_workspace_size(int64_t T, int32_t D, int32_t I, int32_t E, int32_t k) {
+  if (ffn_shape_status(T, D, I, E, k) != K3MOE_OK || T == 0) return 0;
+  return ffn_workspace_layout(T, D, I, E, k).total;
+}
+
+int moe_mxfp4_ffn(const void* x_bf16, const int32_t* topk_ids, const float* topk_w, const uint8_t* w1,
+                  const uint8_t* w3, const uint8_t* w2, int64_t T, int32_t D, int32_t I, int32_t E, int32_t k,
+                  int32_t act, float* out, void* workspace, size_t workspace_bytes, void* stream) {
+  const int st = ffn_shape_status(T, D, I, E, k);
+  if (st != K3MOE_OK) return st;
+  if (act != K3MOE_ACT_SILU_MUL) return K3MOE_ERR_UNSUPPORTED;
+  if (T == 0) return K3MOE_OK;
+  if (!x_bf16 || !topk_ids || !topk_w || !w1 || !w3 || !w2 || !out || !workspace) return K3MOE_ERR_NULL;
+  if (misaligned(x_bf16) || misaligned(topk_ids) || misaligned(topk_w) || misaligned(w1) || misaligned(w3) ||
+      misaligned(w2) || misaligned(out) || misaligned(workspace))
+    return K3MOE_ERR_ALIGN;
+  const FfnWorkspace L = ffn_workspace_layout(T, D, I, E, k);
+  if (workspace_bytes < L.total) return K3MOE_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  const int rpt = choose_rows_per_tile(T, k, E);
+
+  GroupArgs g{};
+  g.ids = topk_ids;
+  g.x = static_cast<const uint16_t*>(x_bf16);
+  g.T = T;
+  g.D = D;
+  g.E = E;
+  g.k = k;
+  g.rows_per_tile = rpt;
+  g.counts = reinterpret_cast<int32_t*>(ws + L.counts);
+  g.offsets = reinterpret_cast<int32_t*>(ws + L.offsets);
+  g.tile_count = reinterpret_cast<int32_t*>(ws + L.tile_count);
+  g.tiles = reinterpret_cast<Tile*>(ws + L.tiles);
+  g.row_tok = reinterpret_cast<int32_t*>(ws + L.row_tok);
+  g.slot_row = reinterpret_cast<int32_t*>(ws + L.slot_row);
+  g.chunk_base = reinterpret_cast<int32_t*>(ws + L.chunk_base);
+  g.chunk_mask = reinterpret_cast<unsigned long long*>(ws + L.chunk_mask);
+  g.x_perm = reinterpret_cast<uint16_t*>(ws + L.x_perm);
+  hipError_t err = launch_group(g, s);
+  if (err != hipSuccess) return K3MOE_ERR_DEVICE;
+
+  const int64_t max_tiles = T * (int64_t)k / rpt + (T * (int64_t)k < E ? T * (int64_t)k : E);
+  GemmArgs gu{};
+  gu.act = g.x_perm;
+  gu.row_tok = g.row_tok;
+  gu.wa = w1;
+  gu.wb = w3;
+  gu.tiles = g.tiles;
+  gu.tile_count = g.tile_count;
+  gu.max_tiles = max_tiles;
+  gu.K = D;
+  gu.N = I;
+  gu.out = ws + L.h;
+  gu.out_lo = ws + L.h_lo;
+  err = launch_gate_up(gu, rpt, s);
+  if (err != hipSuccess) return K3MOE_ERR_DEVICE;
+
+  GemmArgs dn{};
+  dn.act = reinterpret_cast<const uint16_t*>(ws + L.h);
+  dn.act_lo = reinterpret_cast<const uint16_t*>(ws + L.h_lo);
+  dn.row_tok = nullptr;
+  dn.wa = w2;
+  dn.wb = nullptr;
+  dn.tiles = g.tiles;
+  dn.tile_count = g.tile_count;
+  dn.max_tiles = max_tiles;
+  dn.K = I;
+  dn.N = D;
+  dn.out = ws + L.y;
+  err = launch_down(dn, rpt, s);
+  if (err != hipSuccess) return K3MOE_ERR_DEVICE;
+
+  err = launch_combine(reinterpret_cast<const float*>(ws + L.y), g.slot_row, topk_w, T, D, k, out, s);
+  return device_status(err);
+}
+
+}  // extern "C"

@@ -1,0 +1,287 @@
+// Grouped expert GEMMs with the MXFP4 decode fused in, and the weighted combine.
+//
+// Shapes (llama.cpp pull request "model: add Kimi-K3 text model"): an expert
+// is w1 | w2 | w3 (dry-run comment); w1 and w3 are [I, D] (logical [3072, 3584]
+// for K3, repack comment), w2 is [D, I]; every row is stored as 17-byte ggml
+// MXFP4 blocks along the contraction dimension.
+//
+// MFMA mapping (v_mfma_f32_16x16x32_bf16, fp32 accumulate): the 16 MFMA rows
+// are 16 weight rows (output features), the 16 columns are 16 tokens.  A lane
+// owns one weight row and one of four K slices.  One ggml block holds 32
+// weights with a single E8M0 exponent; the decode multiplies each 4-bit code by
+// that block's scale while converting to bf16 (v_cvt_scalef32_pk_bf16_fp4),
+// which is exact for every code and every exponent that keeps the product in
+// range, so the MFMA needs no rescale afterwards.  Because qs byte j holds
+// elements j and j+16, a decoded dword is the pair (j, j+16); the activations
+// are stored in the same order inside each 32-block ("P order": position
+// 8i + 2t + h holds element 16h + 4i + t), so A and B agree on K.
+//
+// Precision: h = SiLU(g) * u is formed in fp32 and handed to the down product
+// as two bf16 terms, hi = bf16(h) and lo = bf16(h - hi); both multiply the same
+// decoded w2 operand, so h enters with about 16 significant bits while every
+// MFMA stays bf16 x bf16 -> fp32.
+//
+// Work decomposition: a workgroup of 4 waves computes 64 output features for
+// one tile of up to 16*NT grouped rows of one expert.  Weight rows are staged
+// through LDS one K segment (up to 16 blocks = 272 bytes per row) at a time
+// with coalesced loads; each wave decodes its own 16 rows.
+#include "k3moe_internal.h"
+
+#include <math.h>
+
+namespace k3moe {
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kFeatPerWg = 64;   // output features per workgroup (16 per wave)
+constexpr int kSegBlocks = 16;   // MXFP4 blocks per K segment
+constexpr int kLdsRowDw = 68;    // LDS dwords per staged row (16 blocks * 17 B / 4)
+
+// Element of a 32-block stored at P-order position p.
+__device__ __forceinline__ int p_to_elem(int p) { return 16 * (p & 1) + 4 * (p >> 3) + ((p >> 1) & 3); }
+
+// Block scale 2^(e-127) as fp32 (e = 0 gives the subnormal 2^-127).
+__device__ __forceinline__ float e8m0_to_f32(uint32_t e) {
+  return __uint_as_float(e ? (e << 23) : 0x00400000u);
+}
+
+// 8 weights (qs dword q = 4 nibble pairs) -> bf16x8 in P order, scaled.
+__device__ __forceinline__ bf16x8_t decode_dword(uint32_t q, float sf) {
+  uint4 r;
+  r.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, sf, 0));
+  r.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, sf, 1));
+  r.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, sf, 2));
+  r.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, sf, 3));
+  return __builtin_bit_cast(bf16x8_t, r);
+}
+
+__device__ __forceinline__ bf16x8_t load_bf16x8(const uint16_t* p) {
+  return __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(p));
+}
+
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)f);  // round to nearest even
+}
+
+// Stage rows [0, 64) x bytes [byte0, byte0 + seg_bytes) of a weight tile into LDS.
+// kVec16: rows and the segment are 16-byte aligned and 272 bytes long.
+template <bool kVec16>
+__device__ __forceinline__ void stage_weights(const uint8_t* __restrict__ w, size_t row_bytes, size_t byte0,
+                                              int seg_bytes, uint32_t* lds) {
+  if (kVec16) {
+    for (int idx = threadIdx.x; idx < kFeatPerWg * 17; idx += blockDim.x) {
+      const int r = idx / 17, c = idx - r * 17;
+      const uint4 v = *reinterpret_cast<const uint4*>(w + r * row_bytes + byte0 + 16 * c);
+      *reinterpret_cast<uint4*>(lds + r * kLdsRowDw + 4 * c) = v;
+    }
+  } else {
+    const int dpr = seg_bytes >> 2;  // seg_bytes = 17 * (multiple of 4 blocks)
+    for (int idx = threadIdx.x; idx < kFeatPerWg * dpr; idx += blockDim.x) {
+      const int r = idx / dpr, c = idx - r * dpr;
+      lds[r * kLdsRowDw + c] = *reinterpret_cast<const uint32_t*>(w + r * row_bytes + byte0 + 4 * c);
+    }
+  }
+}
+
+// Decode block (4*rnd + g) of the staged segment for LDS row `lrow`: the lane's
+// four operands (P-order positions 8i..8i+7, i = 0..3).
+__device__ __forceinline__ void decode_block(const uint32_t* lds, int lrow, int rnd, int g, bf16x8_t op[4]) {
+  // block 4*rnd + g starts at byte 68*rnd + 17*g = dword 17*rnd + 4*g, byte g
+  const uint32_t* L = lds + lrow * kLdsRowDw + 17 * rnd + 4 * g;
+  const uint32_t d0 = L[0], d1 = L[1], d2 = L[2], d3 = L[3], d4 = L[4];
+  const float sf = e8m0_to_f32((d0 >> (8 * g)) & 0xFFu);
+  // qs dword i = bytes g+1+4i .. g+4+4i of d0..d4
+  uint32_t q0, q1, q2, q3;
+  if (g == 3) {
+    q0 = d1; q1 = d2; q2 = d3; q3 = d4;
+  } else {
+    const int sh = g + 1;
+    q0 = __builtin_amdgcn_alignbyte(d1, d0, sh);
+    q1 = __builtin_amdgcn_alignbyte(d2, d1, sh);
+    q2 = __builtin_amdgcn_alignbyte(d3, d2, sh);
+    q3 = __builtin_amdgcn_alignbyte(d4, d3, sh);
+  }
+  op[0] = decode_dword(q0, sf);
+  op[1] = decode_dword(q1, sf);
+  op[2] = decode_dword(q2, sf);
+  op[3] = decode_dword(q3, sf);
+}
+
+template <int NT, bool kGateUp, bool kVec16>
+__global__ __launch_bounds__(256) void ffn_gemm_kernel(GemmArgs a) {
+  constexpr int kMats = kGateUp ? 2 : 1;
+  __shared__ uint32_t wlds[kMats][kFeatPerWg * kLdsRowDw];
+
+  const int64_t tile_idx = blockIdx.x;
+  if (tile_idx >= *a.tile_count) return;  // uniform over the workgroup
+  const Tile tile = a.tiles[tile_idx];
+  const int f0 = blockIdx.y * kFeatPerWg;
+  const int nb = a.K >> 5;
+  const size_t row_bytes = (size_t)nb * 17;
+  const size_t mat_bytes = (size_t)a.N * row_bytes;
+  const uint8_t* wA = a.wa + (size_t)tile.expert * mat_bytes + (size_t)f0 * row_bytes;
+  const uint8_t* wB = kGateUp ? a.wb + (size_t)tile.expert * mat_bytes + (size_t)f0 * row_bytes : nullptr;
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int rho = lane & 15, g = lane >> 4;
+  // LDS row (feature f0 + lrow) that feeds MFMA row rho of this wave.  For
+  // gate/up the rows are chosen so that a lane's four outputs are four
+  // consecutive P-order positions of h (one 8-byte store).
+  const int lrow = kGateUp ? 32 * (wave >> 1) + p_to_elem(16 * (wave & 1) + rho) : 16 * wave + rho;
+
+  const uint16_t* brow[NT];
+  const uint16_t* brow_lo[NT];
+  bool bvalid[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    const int m = nt * 16 + rho;
+    bvalid[nt] = m < tile.nrows;
+    const int row = tile.row0 + (bvalid[nt] ? m : 0);
+    const int64_t src_row = kGateUp ? (int64_t)a.row_tok[row] : (int64_t)row;
+    brow[nt] = a.act + src_row * a.K;
+    brow_lo[nt] = kGateUp ? nullptr : a.act_lo + src_row * a.K;
+  }
+
+  f32x4_t acc[kMats][NT];
+#pragma unroll
+  for (int mi = 0; mi < kMats; ++mi)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) acc[mi][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  for (int seg0 = 0; seg0 < nb; seg0 += kSegBlocks) {
+    const int nbs = (nb - seg0) < kSegBlocks ? (nb - seg0) : kSegBlocks;  // multiple of 4
+    __syncthreads();  // previous segment fully consumed
+    stage_weights<kVec16>(wA, row_bytes, (size_t)seg0 * 17, nbs * 17, wlds[0]);
+    if (kGateUp) stage_weights<kVec16>(wB, row_bytes, (size_t)seg0 * 17, nbs * 17, wlds[kMats - 1]);
+    __syncthreads();
+    for (int rnd = 0; rnd < (nbs >> 2); ++rnd) {
+      // activations: block (seg0 + 4*rnd + g), P-order positions 8i..8i+7
+      bf16x8_t bop[NT][4];
+      bf16x8_t bop_lo[kGateUp ? 1 : NT][4];
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        const size_t off = (size_t)(seg0 + 4 * rnd + g) * 32;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          bop[nt][i] = bvalid[nt] ? load_bf16x8(brow[nt] + off + 8 * i) : bf16x8_t{};
+          if (!kGateUp) bop_lo[kGateUp ? 0 : nt][i] = bvalid[nt] ? load_bf16x8(brow_lo[nt] + off + 8 * i) : bf16x8_t{};
+        }
+      }
+#pragma unroll
+      for (int mi = 0; mi < kMats; ++mi) {
+        bf16x8_t aop[4];
+        decode_block(wlds[mi], lrow, rnd, g, aop);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) {
+            acc[mi][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop[i], bop[nt][i], acc[mi][nt], 0, 0, 0);
+            if (!kGateUp)
+              acc[mi][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop[i], bop_lo[kGateUp ? 0 : nt][i],
+                                                                    acc[mi][nt], 0, 0, 0);
+          }
+      }
+    }
+  }
+
+  // Epilogue.  Lane holds rows 4g..4g+3 (features) of column rho (token).
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    const int m = nt * 16 + rho;
+    if (m >= tile.nrows) continue;
+    const int64_t row = tile.row0 + m;
+    if (kGateUp) {
+      uint32_t hb[4], lb[4];
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const float gt = acc[0][nt][v], up = acc[kMats - 1][nt][v];
+        const float h = gt / (1.0f + expf(-gt)) * up;
+        hb[v] = f32_to_bf16_bits(h);
+        lb[v] = f32_to_bf16_bits(h - __uint_as_float(hb[v] << 16));
+      }
+      // P-order positions 16*(wave&1) + 4g + v of I-block (f0/32 + wave/2)
+      const int pos = f0 + 32 * (wave >> 1) + 16 * (wave & 1) + 4 * g;
+      uint16_t* hrow = reinterpret_cast<uint16_t*>(a.out) + row * a.N;
+      uint16_t* lrow_out = reinterpret_cast<uint16_t*>(a.out_lo) + row * a.N;
+      *reinterpret_cast<uint2*>(hrow + pos) = make_uint2(hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16));
+      *reinterpret_cast<uint2*>(lrow_out + pos) = make_uint2(lb[0] | (lb[1] << 16), lb[2] | (lb[3] << 16));
+    } else {
+      float* yrow = reinterpret_cast<float*>(a.out) + row * a.N;
+      const int f = f0 + 16 * wave + 4 * g;
+      *reinterpret_cast<float4*>(yrow + f) =
+          make_float4(acc[0][nt][0], acc[0][nt][1], acc[0][nt][2], acc[0][nt][3]);
+    }
+  }
+}
+
+template <bool kGateUp>
+hipError_t launch_gemm(const GemmArgs& a, int rows_per_tile, hipStream_t s) {
+  const dim3 grid((unsigned)a.max_tiles, (unsigned)(a.N / kFeatPerWg));
+  const bool vec16 = ((a.K / 32) % kSegBlocks) == 0;
+  const int nt = rows_per_tile / 16;
+#define K3_LAUNCH(NT_, V_) hipLaunchKernelGGL((ffn_gemm_kernel<NT_, kGateUp, V_>), grid, dim3(256), 0, s, a)
+  if (nt == 1) {
+    if (vec16) K3_LAUNCH(1, true); else K3_LAUNCH(1, false);
+  } else if (nt == 2) {
+    if (vec16) K3_LAUNCH(2, true); else K3_LAUNCH(2, false);
+  } else {
+    if (vec16) K3_LAUNCH(4, true); else K3_LAUNCH(4, false);
+  }
+#undef K3_LAUNCH
+  return hipGetLastError();
+}
+
+// out[t] = sum_j w[t,j] * y[slot_row[t*k+j]], in slot order; 4 features per thread.
+__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ y, const int32_t* __restrict__ slot_row,
+                                                       const float* __restrict__ w, int64_t T, int D, int k,
+                                                       float* __restrict__ out) {
+  const int q = D / 4;
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= T * q) return;
+  const int64_t t = idx / q;
+  const int d = (int)(idx - t * q) * 4;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int j = 0; j < k; ++j) {
+    const int32_t r = slot_row[t * k + j];
+    if (r < 0) continue;
+    const float wj = w[t * k + j];
+    const float4 v = *reinterpret_cast<const float4*>(y + (int64_t)r * D + d);
+    acc.x += wj * v.x;
+    acc.y += wj * v.y;
+    acc.z += wj * v.z;
+    acc.w += wj * v.w;
+  }
+  *reinterpret_cast<float4*>(out + t * D + d) = acc;
+}
+
+}  // namespace
+
+hipError_t launch_gate_up(const GemmArgs& a, int rows_per_tile, hipStream_t s) {
+  return launch_gemm<true>(a, rows_per_tile, s);
+}
+
+hipError_t launch_down(const GemmArgs& a, int rows_per_tile, hipStream_t s) {
+  return launch_gemm<false>(a, rows_per_tile, s);
+}
+
+hipError_t launch_combine(const float* y, const int32_t* slot_row, const float* w, int64_t T, int D, int k,
+                          float* out, hipStream_t s) {
+  const int64_t n = T * (D / 4);
+  const int64_t blocks = (n + 255) / 256;
+  hipLaunchKernelGGL(combine_kernel, dim3((unsigned)blocks), dim3(256), 0, s, y, slot_row, w, T, D, k, out);
+  return hipGetLastError();
+}
+
+int choose_rows_per_tile(int64_t T, int k, int E) {
+  const int64_t entries = T * k;
+  const int64_t active = entries < E ? entries : E;
+  const int64_t avg = active > 0 ? entries / active : 0;
+  if (avg >= 48) return 64;
+  if (avg >= 24) return 32;
+  return 16;
+}
+
+}  // namespace k3moe

@@ -1,0 +1,222 @@
+// Grouping of routed (token, slot) entries by expert, the GEMM tile list, and
+// the activation re-layout the GEMM consumes.
+//
+// The routed-MoE FFN ("build_moe_ffn", llama.cpp pull request "model: add
+// Kimi-K3 text model", LLAMA_MAX_EXPERTS comment) runs every expert on the
+// tokens routed to it.  Rows of the grouped activations are ordered by
+// (expert, token, slot); an entry whose id is outside [0, E) or repeats an id
+// earlier in its token's row is skipped.
+//
+// Tokens are cut into chunks of 64.  For every (chunk, expert) a 64-bit LDS
+// bitmap records which tokens of the chunk chose the expert (atomic OR, so the
+// result does not depend on thread order).  A single-workgroup scan turns the
+// per-chunk popcounts into per-expert offsets and per-(chunk, expert) bases;
+// an entry's grouped row is then base + popcount(bitmap & tokens before it).
+// Small batches (one chunk) run all phases in one launch.
+#include "k3moe_internal.h"
+
+namespace k3moe {
+namespace {
+
+constexpr int kScanThreads = 1024;
+constexpr int kMaxExpertsPerScanThread = 8;  // 8 * 1024 = K3MOE_MAX_EXPERTS_FFN
+
+__device__ __forceinline__ bool entry_expert(const int32_t* ids_t, int j, int E, int& e_out) {
+  const int e = ids_t[j];
+  if (e < 0 || e >= E) return false;
+  for (int jj = 0; jj < j; ++jj)
+    if (ids_t[jj] == e) return false;
+  e_out = e;
+  return true;
+}
+
+// Phase 1: token bitmaps of chunk c into mask[0..E) (LDS). Ends with a barrier.
+__device__ void build_masks(const int32_t* __restrict__ ids, int64_t T, int k, int E, int64_t c,
+                            unsigned long long* mask) {
+  const int tid = threadIdx.x, nthr = blockDim.x;
+  for (int e = tid; e < E; e += nthr) mask[e] = 0ull;
+  __syncthreads();
+  const int64_t t0 = c * kChunkTokens;
+  for (int idx = tid; idx < kChunkTokens * k; idx += nthr) {
+    const int tl = idx / k, j = idx - tl * k;
+    const int64_t t = t0 + tl;
+    int e;
+    if (t < T && entry_expert(ids + t * k, j, E, e)) atomicOr(&mask[e], 1ull << tl);
+  }
+  __syncthreads();
+}
+
+// Block-wide exclusive scan of one int per thread (blockDim.x == 1024).
+__device__ int block_exclusive_scan(int v, int* total_out) {
+  __shared__ int wave_tot[kScanThreads / 64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int incl = v;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int o = __shfl_up(incl, d, 64);
+    if (lane >= d) incl += o;
+  }
+  if (lane == 63) wave_tot[wave] = incl;
+  __syncthreads();
+  int before = 0, total = 0;
+  for (int w = 0; w < kScanThreads / 64; ++w) {
+    const int tw = wave_tot[w];
+    if (w < wave) before += tw;
+    total += tw;
+  }
+  __syncthreads();  // wave_tot may be reused by the next call
+  *total_out = total;
+  return before + incl - v;
+}
+
+// Phase 2 (one workgroup of 1024 threads): per-expert counts and offsets, the
+// tile list, and base[c][e] = offsets[e] + rows of e in chunks before c.
+// masks: [n_chunks][E] (global, or LDS when n_chunks == 1); base: [n_chunks][E].
+__device__ void scan_experts(const unsigned long long* masks, int64_t n_chunks, int E, int rows_per_tile,
+                             int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+                             int32_t* __restrict__ tile_count, Tile* __restrict__ tiles, int32_t* base) {
+  const int tid = threadIdx.x;
+  const int e0 = tid * kMaxExpertsPerScanThread;
+  int cnt[kMaxExpertsPerScanThread];
+  int my_rows = 0, my_tiles = 0;
+#pragma unroll
+  for (int i = 0; i < kMaxExpertsPerScanThread; ++i) {
+    cnt[i] = 0;
+    const int e = e0 + i;
+    if (e < E)
+      for (int64_t c = 0; c < n_chunks; ++c) cnt[i] += __popcll(masks[c * E + e]);
+    my_rows += cnt[i];
+    my_tiles += (cnt[i] + rows_per_tile - 1) / rows_per_tile;
+  }
+  int total_rows, total_tiles;
+  int row_off = block_exclusive_scan(my_rows, &total_rows);
+  int tile_off = block_exclusive_scan(my_tiles, &total_tiles);
+#pragma unroll
+  for (int i = 0; i < kMaxExpertsPerScanThread; ++i) {
+    const int e = e0 + i;
+    if (e >= E) break;
+    counts[e] = cnt[i];
+    offsets[e] = row_off;
+    int run = row_off;
+    for (int64_t c = 0; c < n_chunks; ++c) {
+      base[c * E + e] = run;
+      run += __popcll(masks[c * E + e]);
+    }
+    for (int r = 0; r < cnt[i]; r += rows_per_tile) {
+      Tile tl;
+      tl.expert = e;
+      tl.row0 = row_off + r;
+      tl.nrows = cnt[i] - r < rows_per_tile ? cnt[i] - r : rows_per_tile;
+      tl.pad = 0;
+      tiles[tile_off++] = tl;
+    }
+    row_off += cnt[i];
+  }
+  if (tid == 0) {
+    offsets[E] = total_rows;
+    *tile_count = total_tiles;
+  }
+}
+
+// Phase 3: grouped row of every entry of chunk c.
+__device__ void place_entries(const int32_t* __restrict__ ids, int64_t T, int k, int E, int64_t c,
+                              const unsigned long long* mask_c, const int32_t* base_c, int32_t* __restrict__ row_tok,
+                              int32_t* __restrict__ slot_row) {
+  const int tid = threadIdx.x, nthr = blockDim.x;
+  const int64_t t0 = c * kChunkTokens;
+  for (int idx = tid; idx < kChunkTokens * k; idx += nthr) {
+    const int tl = idx / k, j = idx - tl * k;
+    const int64_t t = t0 + tl;
+    if (t >= T) continue;
+    int e;
+    int32_t row = -1;
+    if (entry_expert(ids + t * k, j, E, e)) {
+      const unsigned long long before = tl ? (mask_c[e] & ((1ull << tl) - 1ull)) : 0ull;
+      row = base_c[e] + __popcll(before);
+      row_tok[row] = (int32_t)t;
+    }
+    slot_row[t * k + j] = row;
+  }
+}
+
+// Activation re-layout: inside every 32-element block of a row, position
+// p = 8i + 2t + h holds element 16h + 4i + t (i, t in 0..3, h in 0..1).  This
+// is the order in which the GEMM decodes a block's nibble pairs (qs byte j
+// holds elements j and j+16), so both MFMA operands see the same K order.
+__device__ __forceinline__ void perm_group(const uint16_t* __restrict__ xrow, uint16_t* __restrict__ prow, int g) {
+  const int b = g >> 2, i = g & 3;
+  const uint2 lo = *reinterpret_cast<const uint2*>(xrow + 32 * b + 4 * i);
+  const uint2 hi = *reinterpret_cast<const uint2*>(xrow + 32 * b + 16 + 4 * i);
+  uint4 o;
+  o.x = __builtin_amdgcn_perm(hi.x, lo.x, 0x05040100u);  // elements 4i,   16+4i
+  o.y = __builtin_amdgcn_perm(hi.x, lo.x, 0x07060302u);  // elements 4i+1, 17+4i
+  o.z = __builtin_amdgcn_perm(hi.y, lo.y, 0x05040100u);  // elements 4i+2, 18+4i
+  o.w = __builtin_amdgcn_perm(hi.y, lo.y, 0x07060302u);  // elements 4i+3, 19+4i
+  *reinterpret_cast<uint4*>(prow + 8 * g) = o;
+}
+
+__device__ void permute_chunk_rows(const uint16_t* __restrict__ x, uint16_t* __restrict__ xp, int64_t T, int D,
+                                   int64_t c) {
+  const int groups = D / 8;
+  const int64_t t0 = c * kChunkTokens;
+  const int64_t nt = (T - t0) < kChunkTokens ? (T - t0) : kChunkTokens;
+  for (int64_t idx = threadIdx.x; idx < nt * groups; idx += blockDim.x) {
+    const int64_t tl = idx / groups;
+    const int g = (int)(idx - tl * groups);
+    const int64_t t = t0 + tl;
+    perm_group(x + t * D, xp + t * D, g);
+  }
+}
+
+__global__ __launch_bounds__(256) void group_count_kernel(GroupArgs a) {
+  extern __shared__ unsigned long long lmask[];
+  const int64_t c = blockIdx.x;
+  build_masks(a.ids, a.T, a.k, a.E, c, lmask);
+  for (int e = threadIdx.x; e < a.E; e += blockDim.x) a.chunk_mask[c * a.E + e] = lmask[e];
+}
+
+__global__ __launch_bounds__(kScanThreads) void group_scan_kernel(GroupArgs a, int64_t n_chunks) {
+  scan_experts(a.chunk_mask, n_chunks, a.E, a.rows_per_tile, a.counts, a.offsets, a.tile_count, a.tiles,
+               a.chunk_base);
+}
+
+__global__ __launch_bounds__(256) void group_place_kernel(GroupArgs a) {
+  const int64_t c = blockIdx.x;
+  place_entries(a.ids, a.T, a.k, a.E, c, a.chunk_mask + c * a.E, a.chunk_base + c * a.E, a.row_tok, a.slot_row);
+  permute_chunk_rows(a.x, a.x_perm, a.T, a.D, c);
+}
+
+// All phases for a batch of at most one chunk (T <= 64), one launch.
+// LDS: E bitmaps (8 B) + E bases (4 B).
+__global__ __launch_bounds__(kScanThreads) void group_fused_kernel(GroupArgs a) {
+  extern __shared__ unsigned long long lmask[];
+  int32_t* lbase = reinterpret_cast<int32_t*>(lmask + a.E);
+  build_masks(a.ids, a.T, a.k, a.E, 0, lmask);
+  scan_experts(lmask, 1, a.E, a.rows_per_tile, a.counts, a.offsets, a.tile_count, a.tiles, lbase);
+  __syncthreads();
+  place_entries(a.ids, a.T, a.k, a.E, 0, lmask, lbase, a.row_tok, a.slot_row);
+  permute_chunk_rows(a.x, a.x_perm, a.T, a.D, 0);
+}
+
+}  // namespace
+
+hipError_t launch_group(const GroupArgs& a, hipStream_t s) {
+  const int64_t n_chunks = (a.T + kChunkTokens - 1) / kChunkTokens;
+  const size_t fused_lds = (size_t)a.E * (sizeof(unsigned long long) + sizeof(int32_t));
+  // leave room for the scan's static LDS (64 ints) under the 64 KB limit
+  if (n_chunks == 1 && fused_lds <= 60 * 1024) {
+    hipLaunchKernelGGL(group_fused_kernel, dim3(1), dim3(kScanThreads), fused_lds, s, a);
+    return hipGetLastError();
+  }
+  const size_t mask_lds = (size_t)a.E * sizeof(unsigned long long);
+  hipLaunchKernelGGL(group_count_kernel, dim3((unsigned)n_chunks), dim3(256), mask_lds, s, a);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(group_scan_kernel, dim3(1), dim3(kScanThreads), 0, s, a, n_chunks);
+  err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(group_place_kernel, dim3((unsigned)n_chunks), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace k3moe

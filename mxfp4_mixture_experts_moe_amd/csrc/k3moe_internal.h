@@ -1,0 +1,84 @@
+// Internal declarations shared by the k3moe HIP sources (not part of the ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace k3moe {
+
+// ---------------------------------------------------------------------------
+// Grouped-GEMM work list.  One tile = up to `rows_per_tile` consecutive grouped
+// rows of one expert (rows of an expert are contiguous after grouping).
+struct Tile {
+  int32_t expert;
+  int32_t row0;   // first grouped row
+  int32_t nrows;  // 1..rows_per_tile
+  int32_t pad;
+};
+
+// Tokens per grouping chunk: one 64-bit bitmap per (chunk, expert).
+constexpr int kChunkTokens = 64;
+// The smallest tile height any GEMM variant uses; sizes the tile list.
+constexpr int kMinTileRows = 16;
+
+// Byte layout of the moe_mxfp4_ffn workspace (every region 256-byte aligned).
+struct FfnWorkspace {
+  size_t counts, offsets, tile_count, tiles, row_tok, slot_row, chunk_base, chunk_mask;
+  size_t x_perm, h, h_lo, y;
+  size_t total;
+  int64_t max_tiles, n_chunks;
+};
+
+FfnWorkspace ffn_workspace_layout(int64_t T, int32_t D, int32_t I, int32_t E, int32_t k);
+
+// ---------------------------------------------------------------------------
+// Launchers (host side; enqueue only, return the hipError_t of the launch).
+hipError_t launch_route_topk(const float* z, const float* bias, int64_t T, int E, int k, int normalize,
+                             float route_scale, int32_t* ids, float* w, hipStream_t s);
+hipError_t launch_repack(const uint8_t* packed, const uint8_t* scale, int64_t nblocks, uint8_t* blocks,
+                         hipStream_t s);
+hipError_t launch_dequant(const uint8_t* blocks, int64_t nblocks, int out_bf16, void* out, hipStream_t s);
+
+struct GroupArgs {
+  const int32_t* ids;
+  const uint16_t* x;  // bf16 bits [T, D]
+  int64_t T;
+  int D, E, k, rows_per_tile;
+  // workspace views
+  int32_t* counts;
+  int32_t* offsets;
+  int32_t* tile_count;
+  Tile* tiles;
+  int32_t* row_tok;
+  int32_t* slot_row;
+  int32_t* chunk_base;
+  unsigned long long* chunk_mask;
+  uint16_t* x_perm;
+};
+hipError_t launch_group(const GroupArgs& a, hipStream_t s);
+
+struct GemmArgs {
+  const uint16_t* act;      // gate/up: x_perm [T, D] (rows via row_tok); down: h_hi [rows, I]
+  const uint16_t* act_lo;   // down only: h_lo [rows, I] (h = h_hi + h_lo)
+  const int32_t* row_tok;   // gate/up only
+  const uint8_t* wa;        // w1 (gate/up) or w2 (down)
+  const uint8_t* wb;        // w3 (gate/up) or unused
+  const Tile* tiles;
+  const int32_t* tile_count;
+  int64_t max_tiles;
+  int K;      // contraction length (D for gate/up, I for down)
+  int N;      // output features (I for gate/up, D for down)
+  void* out;     // gate/up: h_hi bf16 [rows, I] (P-order blocks); down: y f32 [rows, D]
+  void* out_lo;  // gate/up: h_lo bf16 [rows, I]
+};
+hipError_t launch_gate_up(const GemmArgs& a, int rows_per_tile, hipStream_t s);
+hipError_t launch_down(const GemmArgs& a, int rows_per_tile, hipStream_t s);
+
+hipError_t launch_combine(const float* y, const int32_t* slot_row, const float* w, int64_t T, int D, int k,
+                          float* out, hipStream_t s);
+
+// Token-tile height the FFN uses for a batch of T tokens with k routed experts.
+int choose_rows_per_tile(int64_t T, int k, int E);
+
+}  // namespace k3moe

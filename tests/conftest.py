@@ -31,3 +31,18 @@ def read_golden(name):
 @pytest.fixture
 def golden():
     return read_golden
+
+
+LIB = os.path.join(ROOT, "mxfp4_mixture_experts_moe_amd", "libk3moe.so")
+
+
+@pytest.fixture(scope="session")
+def k3():
+    """The HIP library's Python binding (built in-tree first if nothing is built)."""
+    if not os.path.exists(LIB):
+        from mxfp4_mixture_experts_moe_amd import build as _build
+
+        _build.build(verbose=False)
+    import mxfp4_mixture_experts_moe_amd as m
+
+    return m

@@ -1,0 +1,102 @@
+"""The C ABI without a GPU: symbols, host-side argument checks, workspace sizes.
+
+Every call here fails (or succeeds as a no-op) in the host checks, before the
+library touches the HIP runtime; the pointer values are never dereferenced.
+"""
+
+import os
+import re
+
+import pytest
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "k3moe.h")
+
+OK, ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_WORKSPACE, ERR_UNSUPPORTED = 0, -1, -2, -3, -4, -5
+A = 0x10000  # an aligned fake device address (never dereferenced)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?(\w+)\s*\(", text, flags=re.M)))
+
+
+def test_library_exports_every_declared_symbol(k3):
+    names = declared_functions()
+    assert set(names) == {"k3moe_status_str", "moe_route_topk", "mxfp4_repack", "mxfp4_dequant",
+                          "moe_mxfp4_ffn_workspace_size", "moe_mxfp4_ffn"}
+    for n in names:
+        assert hasattr(k3.lib, n), n
+
+
+def test_status_strings(k3):
+    for s in range(-6, 1):
+        assert k3.status_str(s) and k3.status_str(s) != "unknown status"
+    assert k3.status_str(-99) == "unknown status"
+
+
+def test_route_checks(k3):
+    f = k3.lib.moe_route_topk
+    assert f(A, None, 4, 8, 0, 1, 1.0, A, A, None) == ERR_SHAPE  # k < 1
+    assert f(A, None, 4, 8, 9, 1, 1.0, A, A, None) == ERR_SHAPE  # k > E
+    assert f(A, None, 4, 100, 65, 1, 1.0, A, A, None) == ERR_SHAPE  # k > 64
+    assert f(A, None, -1, 8, 2, 1, 1.0, A, A, None) == ERR_SHAPE  # T < 0
+    assert f(A, None, 4, 0, 1, 1, 1.0, A, A, None) == ERR_SHAPE  # E < 1
+    assert f(None, None, 0, 8, 2, 1, 1.0, None, None, None) == OK  # T == 0: no-op
+    assert f(None, None, 4, 8, 2, 1, 1.0, A, A, None) == ERR_NULL
+    assert f(A, None, 4, 8, 2, 1, 1.0, None, A, None) == ERR_NULL
+    assert f(A + 4, None, 4, 8, 2, 1, 1.0, A, A, None) == ERR_ALIGN
+    assert f(A, A + 8, 4, 8, 2, 1, 1.0, A, A, None) == ERR_ALIGN
+
+
+def test_codec_checks(k3):
+    r, d = k3.lib.mxfp4_repack, k3.lib.mxfp4_dequant
+    assert r(A, A, 4, 33, A, None) == ERR_SHAPE
+    assert r(A, A, 4, 0, A, None) == ERR_SHAPE
+    assert r(A, A, -1, 32, A, None) == ERR_SHAPE
+    assert r(None, None, 0, 32, None, None) == OK
+    assert r(A, None, 4, 32, A, None) == ERR_NULL
+    assert r(A, A + 1, 4, 32, A, None) == ERR_ALIGN
+    assert d(A, 4, 48, 0, A, None) == ERR_SHAPE
+    assert d(A, 4, 64, 2, A, None) == ERR_UNSUPPORTED
+    assert d(None, 0, 64, 1, None, None) == OK
+    assert d(A, 4, 64, 0, None, None) == ERR_NULL
+    assert d(A + 2, 4, 64, 0, A, None) == ERR_ALIGN
+
+
+def ffn(k3, T=8, D=256, I=256, E=8, k=2, act=0, ws_bytes=None, **ptrs):
+    p = dict(x=A, ids=A, w=A, w1=A, w3=A, w2=A, out=A, ws=A)
+    p.update(ptrs)
+    if ws_bytes is None:
+        ws_bytes = k3.moe_mxfp4_ffn_workspace_size(T, D, I, E, k)
+    return k3.lib.moe_mxfp4_ffn(p["x"], p["ids"], p["w"], p["w1"], p["w3"], p["w2"], T, D, I, E, k, act, p["out"],
+                                p["ws"], ws_bytes, None)
+
+
+def test_ffn_checks(k3):
+    assert ffn(k3, D=96) == ERR_SHAPE  # D % 128
+    assert ffn(k3, I=200) == ERR_SHAPE
+    assert ffn(k3, E=0) == ERR_SHAPE
+    assert ffn(k3, E=8193, k=2) == ERR_SHAPE
+    assert ffn(k3, k=0) == ERR_SHAPE
+    assert ffn(k3, k=65) == ERR_SHAPE
+    assert ffn(k3, T=-3) == ERR_SHAPE
+    assert ffn(k3, act=1) == ERR_UNSUPPORTED
+    assert ffn(k3, T=0, x=None, ids=None, w=None, w1=None, w3=None, w2=None, out=None, ws=None, ws_bytes=0) == OK
+    assert ffn(k3, w3=None) == ERR_NULL
+    assert ffn(k3, ws=None) == ERR_NULL
+    assert ffn(k3, out=A + 4) == ERR_ALIGN
+    need = k3.moe_mxfp4_ffn_workspace_size(8, 256, 256, 8, 2)
+    assert ffn(k3, ws_bytes=need - 1) == ERR_WORKSPACE
+
+
+def test_workspace_size(k3):
+    ws = k3.moe_mxfp4_ffn_workspace_size
+    assert ws(0, 3584, 3072, 896, 16) == 0
+    assert ws(4, 100, 3072, 896, 16) == 0  # invalid shape -> 0
+    a, b = ws(1, 3584, 3072, 896, 16), ws(4096, 3584, 3072, 896, 16)
+    assert 0 < a < b
+    T, D, I, k = 4096, 3584, 3072, 16
+    # at least h (bf16) + y (fp32) + the re-laid-out activations
+    assert b >= T * k * I * 2 + T * k * D * 4 + T * D * 2
+    assert b % 256 == 0

@@ -1,0 +1,155 @@
+"""GPU parity of moe_mxfp4_ffn (and route -> FFN end to end) against the fp64 oracle.
+
+Bar (per token set): relative L2 error <= 2e-3 and max abs error <= 1e-2 * max|ref|.
+Small configs are compared on every output; the K3-shaped configs (896
+experts resident, the launch configuration the benchmark times) on sampled
+tokens, which the oracle evaluates one expert at a time.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import moe_inputs
+from moe_inputs.device import upload_experts
+from oracle.ffn import ffn_ref
+from oracle.route import route_ref
+from tests.gpu_util import assert_ffn_close, bf16_dev, to_dev_u8
+
+pytestmark = pytest.mark.gpu
+
+
+class HostExperts:
+    """Source-layout experts held in host memory (small configs)."""
+
+    def __init__(self, cfg):
+        self.src = moe_inputs.ExpertSource(cfg)
+        self.mats = [self.src[e] for e in range(cfg.E)]
+
+    def __getitem__(self, e):
+        return self.mats[e]
+
+    def __len__(self):
+        return len(self.mats)
+
+
+def device_experts(k3, cfg):
+    return upload_experts(cfg, lambda p, s, out: k3.mxfp4_repack(p, s, blocks=out))
+
+
+def run_ffn(k3, dev, x_bits, ids, w):
+    out = k3.moe_mxfp4_ffn(bf16_dev(x_bits), torch.from_numpy(ids).cuda(), torch.from_numpy(w).cuda(),
+                           dev.w1, dev.w3, dev.w2)
+    return out.cpu().numpy()
+
+
+def small_case(k3, cfg, ids=None, w=None):
+    batch = moe_inputs.make_batch(cfg)
+    if ids is None:
+        ids, w = route_ref(batch.z, batch.b, cfg.k)
+    dev = device_experts(k3, cfg)
+    got = run_ffn(k3, dev, batch.x, ids.astype(np.int32), w.astype(np.float32))
+    ref = ffn_ref(batch.x, ids, w, HostExperts(cfg))
+    return got, ref, batch, dev
+
+
+def test_tiny(k3):
+    print("[ffn] tiny", flush=True)
+    got, ref, _, _ = small_case(k3, moe_inputs.TINY)
+    assert_ffn_close(got, ref, "tiny")
+
+
+@pytest.mark.parametrize(
+    "E,k,D,I,T",
+    [
+        (16, 4, 512, 384, 200),  # 64-row tiles with ragged tails, 4 D-segments, partial last segment
+        (8, 2, 128, 256, 100),  # 32-row tiles
+        (5, 1, 256, 128, 1),  # single token, k = 1
+        (12, 3, 640, 512, 65),  # two grouping chunks, one token in the second
+        (8192, 2, 128, 128, 40),  # largest supported expert count
+    ],
+)
+def test_shapes(k3, E, k, D, I, T):
+    print(f"[ffn] shape E={E} k={k} D={D} I={I} T={T}", flush=True)
+    cfg = moe_inputs.TINY.with_(E=E, k=k, D=D, I=I, T=T, config_id=40)
+    got, ref, _, _ = small_case(k3, cfg)
+    assert_ffn_close(got, ref, f"E={E} k={k} D={D} I={I} T={T}")
+
+
+def test_hot_expert_invalid_and_duplicate_ids(k3):
+    cfg = moe_inputs.TINY.with_(E=6, k=3, T=300, config_id=41)
+    g = np.random.default_rng(11)
+    ids = g.integers(0, cfg.E, size=(cfg.T, cfg.k)).astype(np.int32)
+    ids[:, 0] = 2  # one hot expert: every token, 5 tiles of 64 rows
+    ids[::7, 1] = -1  # out of range -> skipped
+    ids[::5, 2] = cfg.E + 4
+    ids[1::3, 2] = ids[1::3, 0]  # repeats an earlier slot -> skipped
+    w = g.random((cfg.T, cfg.k)).astype(np.float32)
+    got, ref, batch, dev = small_case(k3, cfg, ids, w)
+    assert_ffn_close(got, ref, "hot/invalid/duplicate")
+    # all entries invalid -> exact zeros
+    bad = np.full_like(ids, -5)
+    out = run_ffn(k3, dev, batch.x, bad, w)
+    assert np.all(out == 0)
+    # determinism: bitwise-identical reruns
+    a = run_ffn(k3, dev, batch.x, ids, w)
+    b = run_ffn(k3, dev, batch.x, ids, w)
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
+def test_identity_weights_closed_form(k3):
+    """W1 = W3 = [I; 0], W2 = 2^e [I | 0]: out[t] = sum_j w_j 2^(e_j) SiLU(x) x."""
+    E, D, I, T, k = 4, 128, 256, 48, 2
+    g = np.random.default_rng(12)
+
+    def ident(rows, cols, p):
+        codes = np.zeros((rows, cols), np.uint8)
+        n = min(rows, cols)
+        codes[np.arange(n), np.arange(n)] = 2
+        return (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8), np.full((rows, cols // 32), 127 + p, np.uint8)
+
+    w1 = torch.stack([k3.mxfp4_repack(*map(to_dev_u8, ident(I, D, 0))) for _ in range(E)])
+    w2 = torch.stack([k3.mxfp4_repack(*map(to_dev_u8, ident(D, I, e))) for e in range(E)])
+    x_bits = moe_inputs.bf16_bits(g.standard_normal((T, D)).astype(np.float32))
+    ids = np.stack([g.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
+    w = g.random((T, k)).astype(np.float32)
+    out = k3.moe_mxfp4_ffn(bf16_dev(x_bits), torch.from_numpy(ids).cuda(), torch.from_numpy(w).cuda(),
+                           w1, w1.clone(), w2).cpu().numpy()
+    x = moe_inputs.bf16_to_f32(x_bits).astype(np.float64)
+    base = x * x / (1.0 + np.exp(-x))
+    expect = (w.astype(np.float64) * np.exp2(ids)).sum(axis=1, keepdims=True) * base
+    assert_ffn_close(out, expect, "identity closed form")
+
+
+# ---------------------------------------------------------------------------
+# K3-shaped configs: all 896 experts resident on the device (15.7 GB).
+
+@pytest.fixture(scope="module")
+def k3_experts(k3):
+    print("[ffn] uploading 896 K3 experts", flush=True)
+    return device_experts(k3, moe_inputs.PREFILL)
+
+
+def sample_tokens(T, n, seed):
+    if T <= n:
+        return np.arange(T)
+    return np.sort(np.random.default_rng(seed).choice(T, size=n, replace=False))
+
+
+@pytest.mark.parametrize("name,n_sample", [("decode-t1", 1), ("decode-t8", 2), ("verify", 2), ("prefill", 2)])
+def test_k3_configs_end_to_end(k3, k3_experts, name, n_sample):
+    """GPU route -> GPU FFN at full size vs oracle route -> oracle FFN on sampled tokens."""
+    cfg = moe_inputs.CONFIGS[name]
+    print(f"[ffn] K3 {name} T={cfg.T}", flush=True)
+    batch, x, z, b = moe_inputs.device.upload_batch(cfg)
+    ids_d, w_d = k3.moe_route_topk(z, b, cfg.k)
+    out = k3.moe_mxfp4_ffn(x, ids_d, w_d, k3_experts.w1, k3_experts.w3, k3_experts.w2).cpu().numpy()
+    ids, w = route_ref(batch.z, batch.b, cfg.k)
+    assert np.array_equal(ids_d.cpu().numpy(), ids)
+    assert np.all(np.isfinite(out))
+    toks = sample_tokens(cfg.T, n_sample, seed=cfg.config_id)
+    # include the token routed to the hottest expert (the longest run of tiles)
+    hot = np.bincount(ids.reshape(-1), minlength=cfg.E).argmax()
+    toks = np.unique(np.concatenate([toks, [np.argwhere(ids == hot)[-1][0]]]))
+    ref = ffn_ref(batch.x, ids, w, batch.experts, tokens=toks)
+    assert_ffn_close(out[toks], ref, f"{name} tokens {toks.tolist()}")

@@ -1,0 +1,79 @@
+"""GPU parity of moe_route_topk: ids bit-exact, weights to fp32 rounding."""
+
+import numpy as np
+import pytest
+import torch
+
+import moe_inputs
+from oracle.route import route_ref, scores
+
+pytestmark = pytest.mark.gpu
+
+W_RTOL = 4e-7  # weights: fp64 -> fp32 rounding of sums taken in different orders
+
+
+def run(k3, z, b, k, normalize=True, route_scale=1.0):
+    zd = torch.from_numpy(np.ascontiguousarray(z)).cuda()
+    bd = None if b is None else torch.from_numpy(np.ascontiguousarray(b)).cuda()
+    ids, w = k3.moe_route_topk(zd, bd, k, normalize, route_scale)
+    return ids.cpu().numpy(), w.cpu().numpy()
+
+
+def check(k3, z, b, k, normalize=True, route_scale=1.0, what=""):
+    ids, w = run(k3, z, b, k, normalize, route_scale)
+    rid, rw = route_ref(z, b, k, normalize, route_scale)
+    if not np.array_equal(ids, rid):
+        bad = np.argwhere(ids != rid)
+        t = int(bad[0][0])
+        s = scores(z[t:t + 1], b)[0]
+        gap = abs(s[ids[t]] - s[rid[t]]).max() if len(bad) else 0.0
+        raise AssertionError(f"{what}: {len(bad)} id mismatches, first token {t}, fp64 score gap {gap:.3e}")
+    fin = np.isfinite(rw)
+    assert np.array_equal(fin, np.isfinite(w)), what
+    np.testing.assert_allclose(w[fin], rw[fin], rtol=W_RTOL, atol=0, err_msg=what)
+
+
+@pytest.mark.parametrize("name", ["tiny", "decode-t1", "decode-t8", "verify", "prefill"])
+def test_configs(k3, name):
+    cfg = moe_inputs.CONFIGS[name]
+    print(f"[route] {name}", flush=True)
+    z, b = moe_inputs.router_inputs(cfg)
+    check(k3, z, b if cfg.bias_sigma > 0 else None, cfg.k, what=name)
+    check(k3, z, b, cfg.k, what=name + " (explicit zero bias)")
+
+
+@pytest.mark.parametrize("E,k", [(8, 1), (8, 8), (896, 16), (1024, 64), (2048, 16), (9000, 16), (12000, 3)])
+def test_expert_counts(k3, E, k):
+    """No expert cap: LDS-resident scores up to 8192 experts, recomputed beyond."""
+    g = np.random.default_rng(E + k)
+    T = 37
+    z = g.standard_normal((T, E)).astype(np.float32)
+    b = (g.standard_normal(E) * 0.5).astype(np.float32)
+    check(k3, z, b, k, what=f"E={E} k={k}")
+
+
+def test_ties_nan_and_options(k3):
+    z = np.zeros((5, 40), np.float32)
+    check(k3, z, np.zeros(40, np.float32), 7, what="all equal")
+    g = np.random.default_rng(9)
+    z = np.round(g.standard_normal((64, 896)), 1).astype(np.float32)  # many exact ties
+    check(k3, z, None, 16, what="rounded logits")
+    z[3, 10] = np.nan
+    z[5, :] = np.nan
+    z[6, 7] = np.inf
+    z[7, 100] = -np.inf
+    check(k3, z, None, 16, what="nan/inf")
+    zz = g.standard_normal((20, 896)).astype(np.float32)
+    bb = (g.standard_normal(896) * 0.5).astype(np.float32)
+    check(k3, zz, bb, 16, normalize=False, what="unnormalized")
+    check(k3, zz, bb, 16, route_scale=2.827, what="scaled")
+    check(k3, zz[:, :16].copy(), bb[:16].copy(), 16, what="k == E")
+
+
+def test_empty_and_determinism(k3):
+    ids, w = k3.moe_route_topk(torch.empty((0, 896), device="cuda"), None, 16)
+    assert ids.shape == (0, 16)
+    z, b = moe_inputs.router_inputs(moe_inputs.PREFILL)
+    a = run(k3, z, b, 16)
+    c = run(k3, z, b, 16)
+    assert np.array_equal(a[0], c[0]) and np.array_equal(a[1].view(np.uint32), c[1].view(np.uint32))
