@@ -160,6 +160,25 @@ int moe_mxfp4_ffn(const void* x_bf16, const int32_t* topk_ids, const float* topk
                   const uint8_t* w3, const uint8_t* w2, int64_t T, int32_t D, int32_t I, int32_t E, int32_t k,
                   int32_t act, float* out, void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * moe_mxfp4_ffn_profiled — moe_mxfp4_ffn that also records caller-created
+ * hipEvent_t handles on `stream` at its stage boundaries, for timing the
+ * stages on the stream they run on (the layer's arithmetic is identical).
+ *
+ *   stage_events  host array of K3MOE_FFN_STAGE_EVENTS hipEvent_t (each may be
+ *                 NULL to skip it): [0] before grouping, [1] before the gate/up
+ *                 product, [2] before the down product, [3] before the combine,
+ *                 [4] after the combine. NULL array = plain moe_mxfp4_ffn.
+ *
+ * Same arguments, checks and results as moe_mxfp4_ffn; an event the runtime
+ * refuses to record gives K3MOE_ERR_DEVICE.
+ */
+#define K3MOE_FFN_STAGE_EVENTS 5
+int moe_mxfp4_ffn_profiled(const void* x_bf16, const int32_t* topk_ids, const float* topk_w, const uint8_t* w1,
+                           const uint8_t* w3, const uint8_t* w2, int64_t T, int32_t D, int32_t I, int32_t E,
+                           int32_t k, int32_t act, float* out, void* workspace, size_t workspace_bytes,
+                           void* stream, void* const* stage_events);
+
 #ifdef __cplusplus
 }
 #endif

@@ -24,6 +24,7 @@ __all__ = [
     "mxfp4_dequant",
     "moe_mxfp4_ffn_workspace_size",
     "moe_mxfp4_ffn",
+    "FFN_STAGES",
     "status_str",
     "lib",
 ]
@@ -54,6 +55,10 @@ lib.moe_mxfp4_ffn_workspace_size.restype = _sz
 lib.moe_mxfp4_ffn_workspace_size.argtypes = [_i64, _i32, _i32, _i32, _i32]
 lib.moe_mxfp4_ffn.restype = ctypes.c_int
 lib.moe_mxfp4_ffn.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _sz, _vp]
+lib.moe_mxfp4_ffn_profiled.restype = ctypes.c_int
+lib.moe_mxfp4_ffn_profiled.argtypes = lib.moe_mxfp4_ffn.argtypes + [ctypes.POINTER(ctypes.c_void_p)]
+FFN_STAGE_EVENTS = 5
+FFN_STAGES = ("group", "gate_up", "down", "combine")
 
 
 class K3MoeError(RuntimeError):
@@ -162,9 +167,12 @@ def moe_mxfp4_ffn_workspace_size(T: int, D: int, I: int, E: int, k: int) -> int:
 
 def moe_mxfp4_ffn(x: torch.Tensor, ids: torch.Tensor, weights: torch.Tensor, w1: torch.Tensor, w3: torch.Tensor,
                   w2: torch.Tensor, act: int = ACT_SILU_MUL, out: torch.Tensor | None = None,
-                  workspace: torch.Tensor | None = None) -> torch.Tensor:
+                  workspace: torch.Tensor | None = None, stage_events=None) -> torch.Tensor:
     """Routed-expert FFN. x bf16 [T, D]; ids int32 [T, k]; weights f32 [T, k];
-    w1/w3 u8 [E, I, D/32, 17]; w2 u8 [E, D, I/32, 17]. Returns out f32 [T, D]."""
+    w1/w3 u8 [E, I, D/32, 17]; w2 u8 [E, D, I/32, 17]. Returns out f32 [T, D].
+
+    stage_events: optional list of 5 torch.cuda.Event recorded at the stage
+    boundaries (moe_mxfp4_ffn_profiled)."""
     _dev(x, "x", torch.bfloat16)
     _dev(ids, "ids", torch.int32)
     _dev(weights, "weights", torch.float32)
@@ -184,7 +192,17 @@ def moe_mxfp4_ffn(x: torch.Tensor, ids: torch.Tensor, weights: torch.Tensor, w1:
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
     _dev(workspace, "workspace", torch.uint8)
-    _check("moe_mxfp4_ffn", lib.moe_mxfp4_ffn(_ptr(x), _ptr(ids), _ptr(weights), _ptr(w1), _ptr(w3), _ptr(w2),
-                                              T, D, I, E, k, act, _ptr(out), _ptr(workspace), workspace.numel(),
-                                              _stream(x.device)))
+    args = (_ptr(x), _ptr(ids), _ptr(weights), _ptr(w1), _ptr(w3), _ptr(w2), T, D, I, E, k, act, _ptr(out),
+            _ptr(workspace), workspace.numel(), _stream(x.device))
+    if stage_events is None:
+        _check("moe_mxfp4_ffn", lib.moe_mxfp4_ffn(*args))
+    else:
+        if len(stage_events) != FFN_STAGE_EVENTS:
+            raise ValueError(f"stage_events must hold {FFN_STAGE_EVENTS} events")
+        handles = (ctypes.c_void_p * FFN_STAGE_EVENTS)()
+        for i, ev in enumerate(stage_events):
+            if ev is not None and not ev.cuda_event:
+                ev.record()  # torch creates its events lazily
+            handles[i] = None if ev is None else ev.cuda_event
+        _check("moe_mxfp4_ffn_profiled", lib.moe_mxfp4_ffn_profiled(*args, handles))
     return out

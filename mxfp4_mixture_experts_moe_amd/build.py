@@ -1,6 +1,9 @@
 """Build libk3moe.so (HIP for gfx950) in-tree.
 
-    python -m mxfp4_mixture_experts_moe_amd.build
+    python mxfp4_mixture_experts_moe_amd/build.py
+
+Run it by path (or load it with importlib from its path): importing the
+package itself loads the library, which must not be required to build it.
 
 Every .hip source under csrc/ is compiled to an object with hipcc for gfx950
 (in parallel), then linked into ``libk3moe.so`` next to this file.  hipcc

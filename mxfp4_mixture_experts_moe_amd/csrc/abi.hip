@@ -112,6 +112,14 @@ size_t moe_mxfp4_ffn_workspace_size(int64_t T, int32_t D, int32_t I, int32_t E, 
 int moe_mxfp4_ffn(const void* x_bf16, const int32_t* topk_ids, const float* topk_w, const uint8_t* w1,
                   const uint8_t* w3, const uint8_t* w2, int64_t T, int32_t D, int32_t I, int32_t E, int32_t k,
                   int32_t act, float* out, void* workspace, size_t workspace_bytes, void* stream) {
+  return moe_mxfp4_ffn_profiled(x_bf16, topk_ids, topk_w, w1, w3, w2, T, D, I, E, k, act, out, workspace,
+                                workspace_bytes, stream, nullptr);
+}
+
+int moe_mxfp4_ffn_profiled(const void* x_bf16, const int32_t* topk_ids, const float* topk_w, const uint8_t* w1,
+                           const uint8_t* w3, const uint8_t* w2, int64_t T, int32_t D, int32_t I, int32_t E,
+                           int32_t k, int32_t act, float* out, void* workspace, size_t workspace_bytes,
+                           void* stream, void* const* stage_events) {
   const int st = ffn_shape_status(T, D, I, E, k);
   if (st != K3MOE_OK) return st;
   if (act != K3MOE_ACT_SILU_MUL) return K3MOE_ERR_UNSUPPORTED;
@@ -143,8 +151,13 @@ int moe_mxfp4_ffn(const void* x_bf16, const int32_t* topk_ids, const float* topk
   g.chunk_base = reinterpret_cast<int32_t*>(ws + L.chunk_base);
   g.chunk_mask = reinterpret_cast<unsigned long long*>(ws + L.chunk_mask);
   g.x_perm = reinterpret_cast<uint16_t*>(ws + L.x_perm);
+  auto mark = [&](int i) -> bool {
+    if (!stage_events || !stage_events[i]) return true;
+    return hipEventRecord(static_cast<hipEvent_t>(stage_events[i]), s) == hipSuccess;
+  };
+  if (!mark(0)) return K3MOE_ERR_DEVICE;
   hipError_t err = launch_group(g, s);
-  if (err != hipSuccess) return K3MOE_ERR_DEVICE;
+  if (err != hipSuccess || !mark(1)) return K3MOE_ERR_DEVICE;
 
   const int64_t max_tiles = T * (int64_t)k / rpt + (T * (int64_t)k < E ? T * (int64_t)k : E);
   GemmArgs gu{};
@@ -160,7 +173,7 @@ int moe_mxfp4_ffn(const void* x_bf16, const int32_t* topk_ids, const float* topk
   gu.out = ws + L.h;
   gu.out_lo = ws + L.h_lo;
   err = launch_gate_up(gu, rpt, s);
-  if (err != hipSuccess) return K3MOE_ERR_DEVICE;
+  if (err != hipSuccess || !mark(2)) return K3MOE_ERR_DEVICE;
 
   GemmArgs dn{};
   dn.act = reinterpret_cast<const uint16_t*>(ws + L.h);
@@ -175,10 +188,11 @@ int moe_mxfp4_ffn(const void* x_bf16, const int32_t* topk_ids, const float* topk
   dn.N = D;
   dn.out = ws + L.y;
   err = launch_down(dn, rpt, s);
-  if (err != hipSuccess) return K3MOE_ERR_DEVICE;
+  if (err != hipSuccess || !mark(3)) return K3MOE_ERR_DEVICE;
 
   err = launch_combine(reinterpret_cast<const float*>(ws + L.y), g.slot_row, topk_w, T, D, k, out, s);
-  return device_status(err);
+  if (err != hipSuccess || !mark(4)) return K3MOE_ERR_DEVICE;
+  return K3MOE_OK;
 }
 
 }  // extern "C"

@@ -40,9 +40,12 @@ LIB = os.path.join(ROOT, "mxfp4_mixture_experts_moe_amd", "libk3moe.so")
 def k3():
     """The HIP library's Python binding (built in-tree first if nothing is built)."""
     if not os.path.exists(LIB):
-        from mxfp4_mixture_experts_moe_amd import build as _build
+        import importlib.util
 
-        _build.build(verbose=False)
+        spec = importlib.util.spec_from_file_location("_k3moe_build", os.path.join(ROOT, "mxfp4_mixture_experts_moe_amd", "build.py"))
+        builder = importlib.util.module_from_spec(spec)
+        spec.loader.exec_module(builder)
+        builder.build(verbose=False)
     import mxfp4_mixture_experts_moe_amd as m
 
     return m

@@ -24,7 +24,7 @@ def declared_functions():
 def test_library_exports_every_declared_symbol(k3):
     names = declared_functions()
     assert set(names) == {"k3moe_status_str", "moe_route_topk", "mxfp4_repack", "mxfp4_dequant",
-                          "moe_mxfp4_ffn_workspace_size", "moe_mxfp4_ffn"}
+                          "moe_mxfp4_ffn_workspace_size", "moe_mxfp4_ffn", "moe_mxfp4_ffn_profiled"}
     for n in names:
         assert hasattr(k3.lib, n), n
 
