@@ -21,8 +21,9 @@ FfnWorkspace ffn_workspace_layout(int64_t T, int32_t D, int32_t I, int32_t E, in
   };
   w.counts = take(sizeof(int32_t) * (size_t)E);
   w.offsets = take(sizeof(int32_t) * (size_t)(E + 1));
-  w.tile_count = take(sizeof(int32_t));
+  w.tile_count = take(2 * sizeof(int32_t));
   w.tiles = take(sizeof(Tile) * (size_t)(w.max_tiles > 0 ? w.max_tiles : 1));
+  w.tiles_b = take(sizeof(Tile) * (size_t)(w.max_tiles > 0 ? w.max_tiles : 1));
   w.row_tok = take(sizeof(int32_t) * (size_t)entries);
   w.slot_row = take(sizeof(int32_t) * (size_t)entries);
   w.chunk_base = take(sizeof(int32_t) * (size_t)(w.n_chunks * E));
@@ -132,7 +133,13 @@ int moe_mxfp4_ffn_profiled(const void* x_bf16, const int32_t* topk_ids, const fl
   if (workspace_bytes < L.total) return K3MOE_ERR_WORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
   uint8_t* ws = static_cast<uint8_t*>(workspace);
-  const int rpt = choose_rows_per_tile(T, k, E);
+  const int64_t entries = T * (int64_t)k;
+  const int64_t active = entries < E ? entries : E;
+  // Large-tile GEMMs once experts average 48+ rows (prefill-sized batches).
+  const bool big = big_gemm_supported(D, I) && entries / active >= 48;
+  const int rpt_small = choose_rows_per_tile(T, k, E);
+  const int rpt_gu = big ? big_rows_per_tile(true) : rpt_small;
+  const int rpt_dn = big ? big_rows_per_tile(false) : rpt_small;
 
   GroupArgs g{};
   g.ids = topk_ids;
@@ -141,11 +148,13 @@ int moe_mxfp4_ffn_profiled(const void* x_bf16, const int32_t* topk_ids, const fl
   g.D = D;
   g.E = E;
   g.k = k;
-  g.rows_per_tile = rpt;
+  g.rows_per_tile[0] = rpt_gu;
+  g.rows_per_tile[1] = rpt_dn;
   g.counts = reinterpret_cast<int32_t*>(ws + L.counts);
   g.offsets = reinterpret_cast<int32_t*>(ws + L.offsets);
   g.tile_count = reinterpret_cast<int32_t*>(ws + L.tile_count);
-  g.tiles = reinterpret_cast<Tile*>(ws + L.tiles);
+  g.tiles[0] = reinterpret_cast<Tile*>(ws + L.tiles);
+  g.tiles[1] = reinterpret_cast<Tile*>(ws + L.tiles_b);
   g.row_tok = reinterpret_cast<int32_t*>(ws + L.row_tok);
   g.slot_row = reinterpret_cast<int32_t*>(ws + L.slot_row);
   g.chunk_base = reinterpret_cast<int32_t*>(ws + L.chunk_base);
@@ -159,20 +168,20 @@ int moe_mxfp4_ffn_profiled(const void* x_bf16, const int32_t* topk_ids, const fl
   hipError_t err = launch_group(g, s);
   if (err != hipSuccess || !mark(1)) return K3MOE_ERR_DEVICE;
 
-  const int64_t max_tiles = T * (int64_t)k / rpt + (T * (int64_t)k < E ? T * (int64_t)k : E);
+  // upper bound of each tile list's length: sum over experts of ceil(n_e / rpt)
   GemmArgs gu{};
   gu.act = g.x_perm;
   gu.row_tok = g.row_tok;
   gu.wa = w1;
   gu.wb = w3;
-  gu.tiles = g.tiles;
+  gu.tiles = g.tiles[0];
   gu.tile_count = g.tile_count;
-  gu.max_tiles = max_tiles;
+  gu.max_tiles = entries / rpt_gu + active;
   gu.K = D;
   gu.N = I;
   gu.out = ws + L.h;
   gu.out_lo = ws + L.h_lo;
-  err = launch_gate_up(gu, rpt, s);
+  err = big ? launch_big_gate_up(gu, s) : launch_gate_up(gu, rpt_gu, s);
   if (err != hipSuccess || !mark(2)) return K3MOE_ERR_DEVICE;
 
   GemmArgs dn{};
@@ -181,13 +190,13 @@ int moe_mxfp4_ffn_profiled(const void* x_bf16, const int32_t* topk_ids, const fl
   dn.row_tok = nullptr;
   dn.wa = w2;
   dn.wb = nullptr;
-  dn.tiles = g.tiles;
-  dn.tile_count = g.tile_count;
-  dn.max_tiles = max_tiles;
+  dn.tiles = g.tiles[1];
+  dn.tile_count = g.tile_count + 1;
+  dn.max_tiles = entries / rpt_dn + active;
   dn.K = I;
   dn.N = D;
   dn.out = ws + L.y;
-  err = launch_down(dn, rpt, s);
+  err = big ? launch_big_down(dn, s) : launch_down(dn, rpt_dn, s);
   if (err != hipSuccess || !mark(3)) return K3MOE_ERR_DEVICE;
 
   err = launch_combine(reinterpret_cast<const float*>(ws + L.y), g.slot_row, topk_w, T, D, k, out, s);

@@ -31,7 +31,7 @@ __device__ __forceinline__ bool entry_expert(const int32_t* ids_t, int j, int E,
 }
 
 // Phase 1: token bitmaps of chunk c into mask[0..E) (LDS). Ends with a barrier.
-__device__ void build_masks(const int32_t* __restrict__ ids, int64_t T, int k, int E, int64_t c,
+__device__ __forceinline__ void build_masks(const int32_t* __restrict__ ids, int64_t T, int k, int E, int64_t c,
                             unsigned long long* mask) {
   const int tid = threadIdx.x, nthr = blockDim.x;
   for (int e = tid; e < E; e += nthr) mask[e] = 0ull;
@@ -47,7 +47,7 @@ __device__ void build_masks(const int32_t* __restrict__ ids, int64_t T, int k, i
 }
 
 // Block-wide exclusive scan of one int per thread (blockDim.x == 1024).
-__device__ int block_exclusive_scan(int v, int* total_out) {
+__device__ __forceinline__ int block_exclusive_scan(int v, int* total_out) {
   __shared__ int wave_tot[kScanThreads / 64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   int incl = v;
@@ -70,56 +70,70 @@ __device__ int block_exclusive_scan(int v, int* total_out) {
 }
 
 // Phase 2 (one workgroup of 1024 threads): per-expert counts and offsets, the
-// tile list, and base[c][e] = offsets[e] + rows of e in chunks before c.
+// two tile lists (one per tile height), and base[c][e] = offsets[e] + rows of e
+// in chunks before c.
 // masks: [n_chunks][E] (global, or LDS when n_chunks == 1); base: [n_chunks][E].
-__device__ void scan_experts(const unsigned long long* masks, int64_t n_chunks, int E, int rows_per_tile,
+__device__ __forceinline__ void scan_experts(const unsigned long long* masks, int64_t n_chunks, int E, int rpt0, int rpt1,
                              int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
-                             int32_t* __restrict__ tile_count, Tile* __restrict__ tiles, int32_t* base) {
+                             int32_t* __restrict__ tile_count, Tile* __restrict__ tiles0, Tile* __restrict__ tiles1,
+                             int32_t* base) {
   const int tid = threadIdx.x;
   const int e0 = tid * kMaxExpertsPerScanThread;
-  int cnt[kMaxExpertsPerScanThread];
-  int my_rows = 0, my_tiles = 0;
-#pragma unroll
-  for (int i = 0; i < kMaxExpertsPerScanThread; ++i) {
-    cnt[i] = 0;
-    const int e = e0 + i;
-    if (e < E)
-      for (int64_t c = 0; c < n_chunks; ++c) cnt[i] += __popcll(masks[c * E + e]);
-    my_rows += cnt[i];
-    my_tiles += (cnt[i] + rows_per_tile - 1) / rows_per_tile;
-  }
-  int total_rows, total_tiles;
-  int row_off = block_exclusive_scan(my_rows, &total_rows);
-  int tile_off = block_exclusive_scan(my_tiles, &total_tiles);
-#pragma unroll
+  // pass 1: this thread's row and tile totals (counts are recomputed in pass 2
+  // rather than kept in a per-thread array)
+  int my_rows = 0, my_tiles0 = 0, my_tiles1 = 0;
   for (int i = 0; i < kMaxExpertsPerScanThread; ++i) {
     const int e = e0 + i;
     if (e >= E) break;
-    counts[e] = cnt[i];
+    int cnt = 0;
+    for (int64_t c = 0; c < n_chunks; ++c) cnt += __popcll(masks[c * E + e]);
+    my_rows += cnt;
+    my_tiles0 += (cnt + rpt0 - 1) / rpt0;
+    my_tiles1 += (cnt + rpt1 - 1) / rpt1;
+  }
+  int total_rows, total_tiles0, total_tiles1;
+  int row_off = block_exclusive_scan(my_rows, &total_rows);
+  int tile_off0 = block_exclusive_scan(my_tiles0, &total_tiles0);
+  int tile_off1 = block_exclusive_scan(my_tiles1, &total_tiles1);
+  // pass 2: offsets, per-chunk bases and tiles of each expert
+  for (int i = 0; i < kMaxExpertsPerScanThread; ++i) {
+    const int e = e0 + i;
+    if (e >= E) break;
     offsets[e] = row_off;
     int run = row_off;
     for (int64_t c = 0; c < n_chunks; ++c) {
       base[c * E + e] = run;
       run += __popcll(masks[c * E + e]);
     }
-    for (int r = 0; r < cnt[i]; r += rows_per_tile) {
+    const int cnt = run - row_off;
+    counts[e] = cnt;
+    for (int r = 0; r < cnt; r += rpt0) {
       Tile tl;
       tl.expert = e;
       tl.row0 = row_off + r;
-      tl.nrows = cnt[i] - r < rows_per_tile ? cnt[i] - r : rows_per_tile;
+      tl.nrows = cnt - r < rpt0 ? cnt - r : rpt0;
       tl.pad = 0;
-      tiles[tile_off++] = tl;
+      tiles0[tile_off0++] = tl;
     }
-    row_off += cnt[i];
+    for (int r = 0; r < cnt; r += rpt1) {
+      Tile tl;
+      tl.expert = e;
+      tl.row0 = row_off + r;
+      tl.nrows = cnt - r < rpt1 ? cnt - r : rpt1;
+      tl.pad = 0;
+      tiles1[tile_off1++] = tl;
+    }
+    row_off = run;
   }
   if (tid == 0) {
     offsets[E] = total_rows;
-    *tile_count = total_tiles;
+    tile_count[0] = total_tiles0;
+    tile_count[1] = total_tiles1;
   }
 }
 
 // Phase 3: grouped row of every entry of chunk c.
-__device__ void place_entries(const int32_t* __restrict__ ids, int64_t T, int k, int E, int64_t c,
+__device__ __forceinline__ void place_entries(const int32_t* __restrict__ ids, int64_t T, int k, int E, int64_t c,
                               const unsigned long long* mask_c, const int32_t* base_c, int32_t* __restrict__ row_tok,
                               int32_t* __restrict__ slot_row) {
   const int tid = threadIdx.x, nthr = blockDim.x;
@@ -155,7 +169,7 @@ __device__ __forceinline__ void perm_group(const uint16_t* __restrict__ xrow, ui
   *reinterpret_cast<uint4*>(prow + 8 * g) = o;
 }
 
-__device__ void permute_chunk_rows(const uint16_t* __restrict__ x, uint16_t* __restrict__ xp, int64_t T, int D,
+__device__ __forceinline__ void permute_chunk_rows(const uint16_t* __restrict__ x, uint16_t* __restrict__ xp, int64_t T, int D,
                                    int64_t c) {
   const int groups = D / 8;
   const int64_t t0 = c * kChunkTokens;
@@ -176,8 +190,8 @@ __global__ __launch_bounds__(256) void group_count_kernel(GroupArgs a) {
 }
 
 __global__ __launch_bounds__(kScanThreads) void group_scan_kernel(GroupArgs a, int64_t n_chunks) {
-  scan_experts(a.chunk_mask, n_chunks, a.E, a.rows_per_tile, a.counts, a.offsets, a.tile_count, a.tiles,
-               a.chunk_base);
+  scan_experts(a.chunk_mask, n_chunks, a.E, a.rows_per_tile[0], a.rows_per_tile[1], a.counts, a.offsets,
+               a.tile_count, a.tiles[0], a.tiles[1], a.chunk_base);
 }
 
 __global__ __launch_bounds__(256) void group_place_kernel(GroupArgs a) {
@@ -192,7 +206,8 @@ __global__ __launch_bounds__(kScanThreads) void group_fused_kernel(GroupArgs a) 
   extern __shared__ unsigned long long lmask[];
   int32_t* lbase = reinterpret_cast<int32_t*>(lmask + a.E);
   build_masks(a.ids, a.T, a.k, a.E, 0, lmask);
-  scan_experts(lmask, 1, a.E, a.rows_per_tile, a.counts, a.offsets, a.tile_count, a.tiles, lbase);
+  scan_experts(lmask, 1, a.E, a.rows_per_tile[0], a.rows_per_tile[1], a.counts, a.offsets, a.tile_count,
+               a.tiles[0], a.tiles[1], lbase);
   __syncthreads();
   place_entries(a.ids, a.T, a.k, a.E, 0, lmask, lbase, a.row_tok, a.slot_row);
   permute_chunk_rows(a.x, a.x_perm, a.T, a.D, 0);

@@ -24,7 +24,7 @@ constexpr int kMinTileRows = 16;
 
 // Byte layout of the moe_mxfp4_ffn workspace (every region 256-byte aligned).
 struct FfnWorkspace {
-  size_t counts, offsets, tile_count, tiles, row_tok, slot_row, chunk_base, chunk_mask;
+  size_t counts, offsets, tile_count, tiles, tiles_b, row_tok, slot_row, chunk_base, chunk_mask;
   size_t x_perm, h, h_lo, y;
   size_t total;
   int64_t max_tiles, n_chunks;
@@ -44,12 +44,13 @@ struct GroupArgs {
   const int32_t* ids;
   const uint16_t* x;  // bf16 bits [T, D]
   int64_t T;
-  int D, E, k, rows_per_tile;
+  int D, E, k;
+  int rows_per_tile[2];  // tile heights of the two tile lists (gate/up, down)
   // workspace views
   int32_t* counts;
   int32_t* offsets;
-  int32_t* tile_count;
-  Tile* tiles;
+  int32_t* tile_count;  // [2]
+  Tile* tiles[2];
   int32_t* row_tok;
   int32_t* slot_row;
   int32_t* chunk_base;
@@ -74,6 +75,11 @@ struct GemmArgs {
 };
 hipError_t launch_gate_up(const GemmArgs& a, int rows_per_tile, hipStream_t s);
 hipError_t launch_down(const GemmArgs& a, int rows_per_tile, hipStream_t s);
+
+bool big_gemm_supported(int D, int I);
+int big_rows_per_tile(bool gate_up);
+hipError_t launch_big_gate_up(const GemmArgs& a, hipStream_t s);
+hipError_t launch_big_down(const GemmArgs& a, hipStream_t s);
 
 hipError_t launch_combine(const float* y, const int32_t* slot_row, const float* w, int64_t T, int D, int k,
                           float* out, hipStream_t s);
