@@ -1,6 +1,6 @@
 // Host side of the k3moe C ABI: argument checks, workspace layout, launches.
 // Every check runs before anything is enqueued; nothing here aborts.
-#include "../../include/k3moe.h"
+#include "k3moe.h"
 #include "k3moe_internal.h"
 
 namespace k3moe {
@@ -136,7 +136,10 @@ int moe_mxfp4_ffn_profiled(const void* x_bf16, const int32_t* topk_ids, const fl
   const int64_t entries = T * (int64_t)k;
   const int64_t active = entries < E ? entries : E;
   // Large-tile GEMMs once experts average 48+ rows (prefill-sized batches).
-  const bool big = big_gemm_supported(D, I) && entries / active >= 48;
+  // They address activations through 32-bit buffer offsets, so x and h must
+  // stay below 2 GiB; bigger batches take the general path.
+  const bool offsets_fit = entries * (int64_t)(I > D ? I : D) * 2 < ((int64_t)1 << 31);
+  const bool big = big_gemm_supported(D, I) && offsets_fit && entries / active >= 48;
   const int rpt_small = choose_rows_per_tile(T, k, E);
   const int rpt_gu = big ? big_rows_per_tile(true) : rpt_small;
   const int rpt_dn = big ? big_rows_per_tile(false) : rpt_small;
@@ -171,6 +174,7 @@ int moe_mxfp4_ffn_profiled(const void* x_bf16, const int32_t* topk_ids, const fl
   // upper bound of each tile list's length: sum over experts of ceil(n_e / rpt)
   GemmArgs gu{};
   gu.act = g.x_perm;
+  gu.act_rows = T;
   gu.row_tok = g.row_tok;
   gu.wa = w1;
   gu.wb = w3;
@@ -187,6 +191,7 @@ int moe_mxfp4_ffn_profiled(const void* x_bf16, const int32_t* topk_ids, const fl
   GemmArgs dn{};
   dn.act = reinterpret_cast<const uint16_t*>(ws + L.h);
   dn.act_lo = reinterpret_cast<const uint16_t*>(ws + L.h_lo);
+  dn.act_rows = entries;
   dn.row_tok = nullptr;
   dn.wa = w2;
   dn.wb = nullptr;

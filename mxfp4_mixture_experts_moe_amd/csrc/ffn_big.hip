@@ -4,8 +4,9 @@
 // accumulation, h carried as a bf16 hi + lo pair); only the work decomposition
 // differs.
 //
-// A workgroup of 8 waves (4 along features x 2 along tokens) owns an output
-// tile of kF features x kN tokens of one expert and walks K in steps of 128
+// A workgroup of 8 waves owns an output tile of kF features x kN tokens of one
+// expert; each wave takes kF/8 features and all kN tokens, so every weight row
+// is decoded by exactly one wave.  K is walked in steps of 128
 // (four MXFP4 blocks).  Each step is double-buffered in LDS and filled with
 // direct global -> LDS loads, so staging costs no VGPRs:
 //   weights:     kMats * kF rows x 68 bytes (the four 17-byte ggml blocks of
@@ -17,10 +18,10 @@
 // and converts one qs dword per MFMA slice.
 //
 // gate/up: kF = 256 features of w1 and of w3, kN = 128 tokens; wave tile
-//          64 features x 64 tokens for both matrices.  Weight rows are placed
-//          so each lane's four outputs are four consecutive P-order positions of
-//          h (8-byte stores of h_hi and h_lo).
-// down:    kF = 512 features of w2, kN = 64 tokens; wave tile 128 x 32; the B
+//          32 features (one I-block) x 128 tokens for both matrices.  The MFMA
+//          rows are assigned so each lane's four outputs are four consecutive
+//          P-order positions of h (8-byte stores of h_hi and h_lo).
+// down:    kF = 512 features of w2, kN = 64 tokens; wave tile 64 x 64; the B
 //          operand is h_hi and h_lo (two MFMAs per decoded weight operand).
 //
 // Workgroups are numbered so that those the hardware sends to the same XCD
@@ -47,12 +48,12 @@ constexpr int kXcds = 8;
 template <bool kGateUp>
 struct BigCfg;
 template <>
-struct BigCfg<true> {
-  static constexpr int kF = 256, kN = 128, kRG = 4, kTG = 4, kMats = 2, kSrc = 1;
+struct BigCfg<true> {  // wave: 2 row groups (32 features) x 8 token groups, 2 matrices
+  static constexpr int kF = 256, kN = 128, kRG = 2, kTG = 8, kMats = 2, kSrc = 1;
 };
 template <>
-struct BigCfg<false> {
-  static constexpr int kF = 512, kN = 64, kRG = 8, kTG = 2, kMats = 1, kSrc = 2;
+struct BigCfg<false> {  // wave: 4 row groups (64 features) x 4 token groups, h_hi and h_lo
+  static constexpr int kF = 512, kN = 64, kRG = 4, kTG = 4, kMats = 1, kSrc = 2;
 };
 
 constexpr int kWDw = 2 * 256 * kWRowDw;        // weight dwords per stage (both variants: 512 rows)
@@ -120,7 +121,6 @@ __global__ __launch_bounds__(kThreads) void ffn_big_kernel(GemmArgs a) {
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
-  const int wf = wave & 3, wn = wave >> 2;  // 4 waves along features, 2 along tokens
   const int rho = lane & 15, g = lane >> 4;
 
   if (tid < C::kN) {
@@ -131,19 +131,42 @@ __global__ __launch_bounds__(kThreads) void ffn_big_kernel(GemmArgs a) {
   __syncthreads();
 
   // ---- per-lane load descriptors (constant over K) ----
-  // Weights: wave w fills LDS rows 64w..64w+63 (natural feature order, all of
-  // one matrix); load j moves flat dword f = 64j + lane of those rows, i.e.
-  // byte 4f - 68*(f/17) + (f/17)*row_bytes from the first row.
-  const int wmat = (64 * wave) / C::kF;  // matrix of this wave's rows
+  // All loads are buffer loads straight into LDS: an SGPR resource per source,
+  // a per-lane byte offset fixed for the whole kernel, and the K step in the
+  // scalar offset.  Out-of-range offsets would read zeros instead of faulting.
+  //
+  // Weights: loader wave w fills LDS rows 64w..64w+63, all of one matrix; load
+  // j moves flat dword f = 64j + lane of those rows (row f/17, dword f%17).
+  // LDS row r of consumer wave c (its 32 rows per matrix for gate/up, 64 for
+  // down) holds MFMA row rho of row group rg with
+  //   r = 32*(rg/2) + 8*(rho/4) + 4*(rg%2) + rho%4,
+  // which keeps the 64 lanes of every A-side LDS read in distinct banks.
+  const int wmat = (64 * wave) / C::kF;  // matrix of the rows this wave loads
   const int wrow0 = 64 * wave - wmat * C::kF;
-  const uint8_t* wsrc = (wmat == 0 ? a.wa : a.wb) + (size_t)tile.expert * mat_bytes + (size_t)(f0 + wrow0) * row_bytes;
-  const uint32_t wstride = (uint32_t)row_bytes - 4 * kWRowDw;
+  const uint8_t* wmat_base = (wmat == 0 ? a.wa : a.wb) + (size_t)tile.expert * mat_bytes + (size_t)f0 * row_bytes;
+  const __amdgpu_buffer_rsrc_t wrsrc =
+      __builtin_amdgcn_make_buffer_rsrc((void*)wmat_base, 0, (int)(C::kF * row_bytes), 0x00020000);
+  uint32_t woffs[kWRowDw];
+#pragma unroll
+  for (int j = 0; j < kWRowDw; ++j) {
+    const int f = 64 * j + lane;
+    const int sl = f / kWRowDw, dw = f - sl * kWRowDw;
+    const int r_tile = wrow0 + sl;                   // LDS row within the matrix tile
+    const int cw = r_tile / (C::kRG * 16);           // consumer wave
+    const int r = r_tile - cw * (C::kRG * 16);       // row within the consumer wave
+    const int rg = 2 * (r >> 5) + ((r >> 2) & 1);
+    const int rh = 4 * ((r >> 3) & 3) + (r & 3);
+    const int feat_in_wave = kGateUp ? p_to_elem(16 * rg + rh) : 16 * rg + rh;
+    woffs[j] = (uint32_t)((cw * (C::kRG * 16) + feat_in_wave) * row_bytes) + 4 * dw;
+  }
   // Activations: wave w fills rows 16w..16w+15 (272 flat 16-byte chunks), all
   // of one source (x / h_hi for gate/up, h_hi or h_lo for down); load j moves
   // chunk f = 64j + lane of them (row f/17, chunk f%17; chunk 16 is padding and
   // re-reads chunk 15; lanes past the 272 chunks are never issued).
   const int asrc = (16 * wave) / C::kN;
   const uint16_t* abase = (kGateUp || asrc == 0) ? a.act : a.act_lo;
+  const __amdgpu_buffer_rsrc_t arsrc =
+      __builtin_amdgcn_make_buffer_rsrc((void*)abase, 0, (int)(a.act_rows * (size_t)K * 2), 0x00020000);
   uint32_t aoffs[5];
 #pragma unroll
   for (int j = 0; j < 5; ++j) {
@@ -153,33 +176,34 @@ __global__ __launch_bounds__(kThreads) void ffn_big_kernel(GemmArgs a) {
     ch = ch > 15 ? 15 : ch;
     rl = rl > 15 ? 15 : rl;
     const int t = 16 * wave + rl - asrc * C::kN;
-    aoffs[j] = (uint32_t)tok_src[t] * (uint32_t)K + 8 * ch;  // in bf16 elements
+    aoffs[j] = ((uint32_t)tok_src[t] * (uint32_t)K + 8 * ch) * 2;  // bytes
   }
 
   auto issue = [&](int stage, int buf) {
     uint32_t* wl = &lds[buf][0] + 64 * wave * kWRowDw;
     uint32_t* al = &lds[buf][kWDw] + 272 * 4 * wave;
-    const uint8_t* wstage = wsrc + (size_t)stage * 68;
+    const int wso = stage * 68;
 #pragma unroll
-    for (int j = 0; j < kWRowDw; ++j) {
-      const uint32_t f = 64 * j + lane;
-      const uint32_t sl = (f * 3856u) >> 16;  // f / 17 for f < 1088
-      __builtin_amdgcn_global_load_lds(wstage + 4 * f + sl * wstride, wl + 64 * j, 4, 0, 0);
-    }
-    const uint16_t* astage = abase + (size_t)stage * kKStep;
+    for (int j = 0; j < kWRowDw; ++j) __builtin_amdgcn_raw_ptr_buffer_load_lds(wrsrc, wl + 64 * j, 4, woffs[j], wso, 0, 0);
+    const int aso = stage * kKStep * 2;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) __builtin_amdgcn_global_load_lds(astage + aoffs[j], al + 256 * j, 16, 0, 0);
-    if (lane < 16) __builtin_amdgcn_global_load_lds(astage + aoffs[4], al + 256 * 4, 16, 0, 0);
+    for (int j = 0; j < 4; ++j) __builtin_amdgcn_raw_ptr_buffer_load_lds(arsrc, al + 256 * j, 16, aoffs[j], aso, 0, 0);
+    if (lane < 16) __builtin_amdgcn_raw_ptr_buffer_load_lds(arsrc, al + 256 * 4, 16, aoffs[4], aso, 0, 0);
   };
 
-  // LDS row (relative to the wave's feature range) feeding MFMA row rho of row
-  // group rg.  gate/up: row groups (2b, 2b+1) cover I-block b of the wave and
-  // MFMA row rho of half t of the block is the feature at P-order position
-  // 16t + rho, so a lane's four outputs are consecutive P-order positions.
-  int rrow[C::kRG];
+  // LDS dword where this lane's block g of MFMA row rho of row group rg starts
+  // (block g of a 68-byte row: dword 4g, byte g).
+  int wrow_dw[C::kMats][C::kRG];
 #pragma unroll
-  for (int rg = 0; rg < C::kRG; ++rg)
-    rrow[rg] = kGateUp ? 32 * (rg >> 1) + p_to_elem(16 * (rg & 1) + rho) : 16 * rg + rho;
+  for (int mi = 0; mi < C::kMats; ++mi)
+#pragma unroll
+    for (int rg = 0; rg < C::kRG; ++rg) {
+      const int r = 32 * (rg >> 1) + 8 * (rho >> 2) + 4 * (rg & 1) + (rho & 3);
+      wrow_dw[mi][rg] = (mi * C::kF + wave * (C::kRG * 16) + r) * kWRowDw + 4 * g;
+    }
+  // qs bytes of block g start at byte g+1 of its first dword: the lane's qs
+  // dword i is bytes g+1..g+4 of the dword pair (4g+i, 4g+i+1)
+  const uint32_t qsel = 0x03020100u + 0x01010101u * (uint32_t)(g + 1);
 
   f32x4_t acc[C::kMats][C::kRG][C::kTG];
 #pragma unroll
@@ -200,53 +224,54 @@ __global__ __launch_bounds__(kThreads) void ffn_big_kernel(GemmArgs a) {
     const uint32_t* wl = &lds[buf][0];
     const uint32_t* al = &lds[buf][kWDw];
 
-    // Two half-steps of two MFMA slices each.  For every (matrix, row group)
-    // the lane pulls the qs dwords of block g it needs for the half (plus the
-    // block's exponent byte) out of the raw 17-byte layout.
+    // Two half-steps of two MFMA slices each; per half the lane pulls the two
+    // qs dwords of its block it needs out of the raw 17-byte layout (and, in
+    // the first half, the block's exponent byte).
+    float sf[C::kMats][C::kRG];
 #pragma unroll
     for (int half = 0; half < 2; ++half) {
       uint32_t q[C::kMats][C::kRG][2];
-      float sf[C::kMats][C::kRG];
 #pragma unroll
       for (int mi = 0; mi < C::kMats; ++mi)
 #pragma unroll
         for (int rg = 0; rg < C::kRG; ++rg) {
-          const int slot = mi * C::kF + wf * (C::kRG * 16) + rrow[rg];
-          const uint32_t* L = wl + slot * kWRowDw + 4 * g;  // block g: dword 4g, byte g
-          const uint32_t d0 = L[0];
-          const uint32_t da = L[2 * half], db = L[2 * half + 1], dc = L[2 * half + 2];
-          sf[mi][rg] = e8m0_to_f32(__builtin_amdgcn_ubfe(d0, 8 * g, 8));
-          // qs dword i = bytes g+1+4i .. g+4+4i of the block's dwords
-          const int sh = (g + 1) & 3;
-          const bool whole = g == 3;  // qs starts on a dword boundary
-          q[mi][rg][0] = whole ? db : __builtin_amdgcn_alignbyte(db, da, sh);
-          q[mi][rg][1] = whole ? dc : __builtin_amdgcn_alignbyte(dc, db, sh);
+          const uint32_t* L = wl + wrow_dw[mi][rg] + 2 * half;
+          const uint32_t da = L[0], db = L[1], dc = L[2];
+          if (half == 0) sf[mi][rg] = e8m0_to_f32(__builtin_amdgcn_ubfe(da, 8 * g, 8));
+          q[mi][rg][0] = __builtin_amdgcn_perm(db, da, qsel);
+          q[mi][rg][1] = __builtin_amdgcn_perm(dc, db, qsel);
         }
 #pragma unroll
       for (int ii = 0; ii < 2; ++ii) {
         const int i = 2 * half + ii;
-        // activations: block g of the step, P-order positions 8i..8i+7 (chunk 4g+i)
-        bf16x8_t bop[C::kSrc][C::kTG];
-#pragma unroll
-        for (int src = 0; src < C::kSrc; ++src)
-#pragma unroll
-          for (int tg = 0; tg < C::kTG; ++tg) {
-            const int row = src * C::kN + wn * (C::kTG * 16) + tg * 16 + rho;
-            bop[src][tg] =
-                __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(al + row * kARowDw + 4 * (4 * g + i)));
-          }
+        bf16x8_t aop[C::kMats][C::kRG];
 #pragma unroll
         for (int mi = 0; mi < C::kMats; ++mi)
 #pragma unroll
           for (int rg = 0; rg < C::kRG; ++rg) {
-            const bf16x8_t aop = decode_dword(q[mi][rg][ii], sf[mi][rg]);
-#pragma unroll
-            for (int src = 0; src < C::kSrc; ++src)
-#pragma unroll
-              for (int tg = 0; tg < C::kTG; ++tg)
-                acc[mi][rg][tg] =
-                    __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop, bop[src][tg], acc[mi][rg][tg], 0, 0, 0);
+            aop[mi][rg] = decode_dword(q[mi][rg][ii], sf[mi][rg]);
           }
+        // activations: block g of the step, P-order positions 8i..8i+7 (chunk
+        // 4g+i); one operand is read ahead while the previous one feeds its MFMAs
+        constexpr int kB = C::kTG * C::kSrc;
+        auto bread = [&](int n) {
+          const int tg = n / C::kSrc, src = n % C::kSrc;
+          const int row = src * C::kN + tg * 16 + rho;
+          return __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(al + row * kARowDw + 4 * (4 * g + i)));
+        };
+        bf16x8_t bnext = bread(0);
+#pragma unroll
+        for (int n = 0; n < kB; ++n) {
+          const bf16x8_t bop = bnext;
+          if (n + 1 < kB) bnext = bread(n + 1);
+          const int tg = n / C::kSrc;
+#pragma unroll
+          for (int mi = 0; mi < C::kMats; ++mi)
+#pragma unroll
+            for (int rg = 0; rg < C::kRG; ++rg)
+              acc[mi][rg][tg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop[mi][rg], bop, acc[mi][rg][tg], 0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -256,7 +281,7 @@ __global__ __launch_bounds__(kThreads) void ffn_big_kernel(GemmArgs a) {
   // ---- epilogue ----
 #pragma unroll
   for (int tg = 0; tg < C::kTG; ++tg) {
-    const int m = wn * (C::kTG * 16) + tg * 16 + rho;
+    const int m = tg * 16 + rho;
     if (m >= tile.nrows) continue;
     const int64_t row = tile.row0 + m;
 #pragma unroll
@@ -270,14 +295,14 @@ __global__ __launch_bounds__(kThreads) void ffn_big_kernel(GemmArgs a) {
           hb[v] = f32_to_bf16_bits(h);
           lb[v] = f32_to_bf16_bits(h - __uint_as_float(hb[v] << 16));
         }
-        const int pos = f0 + 64 * wf + 32 * (rg >> 1) + 16 * (rg & 1) + 4 * g;
+        const int pos = f0 + 32 * wave + 16 * rg + 4 * g;
         uint16_t* hrow = reinterpret_cast<uint16_t*>(a.out) + row * a.N;
         uint16_t* lrow = reinterpret_cast<uint16_t*>(a.out_lo) + row * a.N;
         *reinterpret_cast<uint2*>(hrow + pos) = make_uint2(hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16));
         *reinterpret_cast<uint2*>(lrow + pos) = make_uint2(lb[0] | (lb[1] << 16), lb[2] | (lb[3] << 16));
       } else {
         float* yrow = reinterpret_cast<float*>(a.out) + row * a.N;
-        const int f = f0 + 128 * wf + 16 * rg + 4 * g;
+        const int f = f0 + 64 * wave + 16 * rg + 4 * g;
         *reinterpret_cast<float4*>(yrow + f) =
             make_float4(acc[0][rg][tg][0], acc[0][rg][tg][1], acc[0][rg][tg][2], acc[0][rg][tg][3]);
       }

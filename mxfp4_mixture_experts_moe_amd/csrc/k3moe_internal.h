@@ -62,6 +62,7 @@ hipError_t launch_group(const GroupArgs& a, hipStream_t s);
 struct GemmArgs {
   const uint16_t* act;      // gate/up: x_perm [T, D] (rows via row_tok); down: h_hi [rows, I]
   const uint16_t* act_lo;   // down only: h_lo [rows, I] (h = h_hi + h_lo)
+  int64_t act_rows;         // rows of act (and act_lo)
   const int32_t* row_tok;   // gate/up only
   const uint8_t* wa;        // w1 (gate/up) or w2 (down)
   const uint8_t* wb;        // w3 (gate/up) or unused
