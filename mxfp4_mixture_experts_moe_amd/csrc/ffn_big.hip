@@ -8,14 +8,17 @@
 // expert; each wave takes kF/8 features and all kN tokens, so every weight row
 // is decoded by exactly one wave.  K is walked in steps of 128
 // (four MXFP4 blocks).  Each step is double-buffered in LDS and filled with
-// direct global -> LDS loads, so staging costs no VGPRs:
-//   weights:     kMats * kF rows x 68 bytes (the four 17-byte ggml blocks of
-//                the row, exactly as stored), one dword per lane per load;
+// direct global -> LDS buffer loads of 16 bytes per lane, so staging costs no
+// VGPRs:
+//   weights:     kMats * kF rows x 80 bytes: the 16-byte-aligned window that
+//                holds the step's 68 bytes of the row (its four 17-byte ggml
+//                blocks, exactly as stored) starting at byte 4*(step % 4);
 //   activations: kSrc * kN rows x 256 bytes (+16 bytes of padding so the 16
 //                tokens a ds_read_b128 touches fall in distinct banks).
-// A lane (row rho, lane group g) owns block g of the step for its row: it pulls
-// the block's exponent byte and 16 qs bytes out of the raw row once per step
-// and converts one qs dword per MFMA slice.
+// A lane (row rho, lane group g) owns block g of the step for its row: it reads
+// the two 16-byte chunks holding the block, pulls out the exponent byte and the
+// 16 qs bytes, and converts one qs dword per MFMA slice.  The K loop is
+// unrolled by four so the window phase is a compile-time constant.
 //
 // gate/up: kF = 256 features of w1 and of w3, kN = 128 tokens; wave tile
 //          32 features (one I-block) x 128 tokens for both matrices.  The MFMA
@@ -32,6 +35,8 @@
 
 #include <math.h>
 
+#include <type_traits>
+
 namespace k3moe {
 namespace {
 
@@ -40,7 +45,8 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 512;
 constexpr int kKStep = 128;     // K per stage (4 MXFP4 blocks)
-constexpr int kWRowDw = 17;     // LDS dwords per weight row per stage (68 bytes)
+constexpr int kWRowDw = 20;     // LDS dwords per weight row per stage: an aligned 80-byte window
+constexpr int kWRowChunks = 5;  // 16-byte chunks per weight row window
 constexpr int kARowDw = 68;     // LDS dwords per activation row per stage (256 + 16 bytes)
 constexpr int kARowChunks = 17; // 16-byte chunks per activation row (16 data + 1 pad)
 constexpr int kXcds = 8;
@@ -58,7 +64,7 @@ struct BigCfg<false> {  // wave: 4 row groups (64 features) x 4 token groups, h_
 
 constexpr int kWDw = 2 * 256 * kWRowDw;        // weight dwords per stage (both variants: 512 rows)
 constexpr int kADw = 128 * kARowDw;            // activation dwords per stage (both variants: 128 rows)
-constexpr int kStageDw = kWDw + kADw;          // 17408 dwords = 69632 bytes
+constexpr int kStageDw = kWDw + kADw;          // 18944 dwords = 75776 bytes
 
 __device__ __forceinline__ int p_to_elem(int p) { return 16 * (p & 1) + 4 * (p >> 3) + ((p >> 1) & 3); }
 
@@ -102,11 +108,22 @@ __global__ __launch_bounds__(kThreads) void ffn_big_kernel(GemmArgs a) {
   int64_t tile_idx;
   int ftile;
   if (kGateUp) {
+    // super-tiles of 8 token tiles x fb feature tiles, feature tiles fastest:
+    // the workgroups of an XCD round share both the weight rows and the
+    // activation rows of a super-tile, so its per-step footprint stays small
     const int64_t ntiles = *a.tile_count;
-    // order: feature tile major within runs of the same expert is not known
-    // here, so take token tiles fastest inside each feature tile
-    ftile = (int)(logical / ntiles);
-    tile_idx = logical % ntiles;
+    const int fb = (n_ftiles % 4 == 0) ? 4 : (n_ftiles % 2 == 0) ? 2 : 1;
+    const int fgrp = (int)(logical / (ntiles * fb));
+    const int64_t L = logical - (int64_t)fgrp * ntiles * fb;
+    const int64_t nfull = ntiles / 8;
+    if (L < nfull * 8 * fb) {
+      tile_idx = (L / (8 * fb)) * 8 + (L % (8 * fb)) / fb;
+      ftile = fgrp * fb + (int)(L % fb);
+    } else {
+      const int64_t L2 = L - nfull * 8 * fb;
+      tile_idx = nfull * 8 + L2 / fb;
+      ftile = fgrp * fb + (int)(L2 % fb);
+    }
   } else {
     tile_idx = logical / n_ftiles;
     ftile = (int)(logical % n_ftiles);
@@ -136,28 +153,23 @@ __global__ __launch_bounds__(kThreads) void ffn_big_kernel(GemmArgs a) {
   // scalar offset.  Out-of-range offsets would read zeros instead of faulting.
   //
   // Weights: loader wave w fills LDS rows 64w..64w+63, all of one matrix; load
-  // j moves flat dword f = 64j + lane of those rows (row f/17, dword f%17).
-  // LDS row r of consumer wave c (its 32 rows per matrix for gate/up, 64 for
-  // down) holds MFMA row rho of row group rg with
-  //   r = 32*(rg/2) + 8*(rho/4) + 4*(rg%2) + rho%4,
-  // which keeps the 64 lanes of every A-side LDS read in distinct banks.
+  // j moves 16-byte chunk t = 64j + lane of those rows (row t/5, chunk t%5).
+  // LDS rows are in consumer order: row (mi, consumer wave, row group, rho).
   const int wmat = (64 * wave) / C::kF;  // matrix of the rows this wave loads
   const int wrow0 = 64 * wave - wmat * C::kF;
   const uint8_t* wmat_base = (wmat == 0 ? a.wa : a.wb) + (size_t)tile.expert * mat_bytes + (size_t)f0 * row_bytes;
   const __amdgpu_buffer_rsrc_t wrsrc =
       __builtin_amdgcn_make_buffer_rsrc((void*)wmat_base, 0, (int)(C::kF * row_bytes), 0x00020000);
-  uint32_t woffs[kWRowDw];
+  uint32_t woffs[kWRowChunks];
 #pragma unroll
-  for (int j = 0; j < kWRowDw; ++j) {
-    const int f = 64 * j + lane;
-    const int sl = f / kWRowDw, dw = f - sl * kWRowDw;
+  for (int j = 0; j < kWRowChunks; ++j) {
+    const int t = 64 * j + lane;
+    const int sl = t / kWRowChunks, ch = t - sl * kWRowChunks;
     const int r_tile = wrow0 + sl;                   // LDS row within the matrix tile
     const int cw = r_tile / (C::kRG * 16);           // consumer wave
-    const int r = r_tile - cw * (C::kRG * 16);       // row within the consumer wave
-    const int rg = 2 * (r >> 5) + ((r >> 2) & 1);
-    const int rh = 4 * ((r >> 3) & 3) + (r & 3);
-    const int feat_in_wave = kGateUp ? p_to_elem(16 * rg + rh) : 16 * rg + rh;
-    woffs[j] = (uint32_t)((cw * (C::kRG * 16) + feat_in_wave) * row_bytes) + 4 * dw;
+    const int r = r_tile - cw * (C::kRG * 16);       // (row group, rho) within the consumer wave
+    const int feat_in_wave = kGateUp ? p_to_elem(r) : r;
+    woffs[j] = (uint32_t)((cw * (C::kRG * 16) + feat_in_wave) * row_bytes) + 16 * ch;
   }
   // Activations: wave w fills rows 16w..16w+15 (272 flat 16-byte chunks), all
   // of one source (x / h_hi for gate/up, h_hi or h_lo for down); load j moves
@@ -182,27 +194,25 @@ __global__ __launch_bounds__(kThreads) void ffn_big_kernel(GemmArgs a) {
   auto issue = [&](int stage, int buf) {
     uint32_t* wl = &lds[buf][0] + 64 * wave * kWRowDw;
     uint32_t* al = &lds[buf][kWDw] + 272 * 4 * wave;
-    const int wso = stage * 68;
+    const int wso = 64 * stage + 16 * (stage >> 2);  // 16-byte aligned start of the step's 68 bytes
 #pragma unroll
-    for (int j = 0; j < kWRowDw; ++j) __builtin_amdgcn_raw_ptr_buffer_load_lds(wrsrc, wl + 64 * j, 4, woffs[j], wso, 0, 0);
+    for (int j = 0; j < kWRowChunks; ++j) __builtin_amdgcn_raw_ptr_buffer_load_lds(wrsrc, wl + 256 * j, 16, woffs[j], wso, 0, 0);
     const int aso = stage * kKStep * 2;
 #pragma unroll
     for (int j = 0; j < 4; ++j) __builtin_amdgcn_raw_ptr_buffer_load_lds(arsrc, al + 256 * j, 16, aoffs[j], aso, 0, 0);
     if (lane < 16) __builtin_amdgcn_raw_ptr_buffer_load_lds(arsrc, al + 256 * 4, 16, aoffs[4], aso, 0, 0);
   };
 
-  // LDS dword where this lane's block g of MFMA row rho of row group rg starts
-  // (block g of a 68-byte row: dword 4g, byte g).
+  // LDS dword of chunk g of the window of MFMA row rho of row group rg (block g
+  // of the step lies in chunks g and g+1).
   int wrow_dw[C::kMats][C::kRG];
 #pragma unroll
   for (int mi = 0; mi < C::kMats; ++mi)
 #pragma unroll
-    for (int rg = 0; rg < C::kRG; ++rg) {
-      const int r = 32 * (rg >> 1) + 8 * (rho >> 2) + 4 * (rg & 1) + (rho & 3);
-      wrow_dw[mi][rg] = (mi * C::kF + wave * (C::kRG * 16) + r) * kWRowDw + 4 * g;
-    }
-  // qs bytes of block g start at byte g+1 of its first dword: the lane's qs
-  // dword i is bytes g+1..g+4 of the dword pair (4g+i, 4g+i+1)
+    for (int rg = 0; rg < C::kRG; ++rg)
+      wrow_dw[mi][rg] = (mi * C::kF + wave * (C::kRG * 16) + rg * 16 + rho) * kWRowDw + 4 * g;
+  // block g starts at byte 4*phase + g of chunk g; its qs dword i is bytes
+  // g+1..g+4 of the dword pair (phase+i, phase+i+1) of the two chunks
   const uint32_t qsel = 0x03020100u + 0x01010101u * (uint32_t)(g + 1);
 
   f32x4_t acc[C::kMats][C::kRG][C::kTG];
@@ -214,68 +224,71 @@ __global__ __launch_bounds__(kThreads) void ffn_big_kernel(GemmArgs a) {
       for (int tg = 0; tg < C::kTG; ++tg) acc[mi][rg][tg] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   const int nstages = K / kKStep;
-  issue(0, 0);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
 
-  for (int s = 0; s < nstages; ++s) {
-    const int buf = s & 1;
+  // One K step from LDS buffer `buf` whose weight window starts at phase PH.
+  auto run_stage = [&](auto ph_tag, int s) {
+    constexpr int PH = decltype(ph_tag)::value;
+    const int buf = PH & 1;  // s % 2 == PH % 2 because s % 4 == PH
     if (s + 1 < nstages) issue(s + 1, buf ^ 1);
     const uint32_t* wl = &lds[buf][0];
     const uint32_t* al = &lds[buf][kWDw];
 
-    // Two half-steps of two MFMA slices each; per half the lane pulls the two
-    // qs dwords of its block it needs out of the raw 17-byte layout (and, in
-    // the first half, the block's exponent byte).
+    // qs dwords and block scale of block g of every (matrix, row group)
+    uint32_t q[C::kMats][C::kRG][4];
     float sf[C::kMats][C::kRG];
 #pragma unroll
-    for (int half = 0; half < 2; ++half) {
-      uint32_t q[C::kMats][C::kRG][2];
+    for (int mi = 0; mi < C::kMats; ++mi)
+#pragma unroll
+      for (int rg = 0; rg < C::kRG; ++rg) {
+        const uint4 c0 = *reinterpret_cast<const uint4*>(wl + wrow_dw[mi][rg]);
+        const uint4 c1 = *reinterpret_cast<const uint4*>(wl + wrow_dw[mi][rg] + 4);
+        const uint32_t w[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+        sf[mi][rg] = e8m0_to_f32(__builtin_amdgcn_ubfe(w[PH], 8 * g, 8));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) q[mi][rg][i] = __builtin_amdgcn_perm(w[PH + i + 1], w[PH + i], qsel);
+      }
+
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      bf16x8_t aop[C::kMats][C::kRG];
 #pragma unroll
       for (int mi = 0; mi < C::kMats; ++mi)
 #pragma unroll
-        for (int rg = 0; rg < C::kRG; ++rg) {
-          const uint32_t* L = wl + wrow_dw[mi][rg] + 2 * half;
-          const uint32_t da = L[0], db = L[1], dc = L[2];
-          if (half == 0) sf[mi][rg] = e8m0_to_f32(__builtin_amdgcn_ubfe(da, 8 * g, 8));
-          q[mi][rg][0] = __builtin_amdgcn_perm(db, da, qsel);
-          q[mi][rg][1] = __builtin_amdgcn_perm(dc, db, qsel);
-        }
+        for (int rg = 0; rg < C::kRG; ++rg) aop[mi][rg] = decode_dword(q[mi][rg][i], sf[mi][rg]);
+      // activations: block g of the step, P-order positions 8i..8i+7 (chunk
+      // 4g+i); one operand is read ahead while the previous one feeds its MFMAs
+      constexpr int kB = C::kTG * C::kSrc;
+      auto bread = [&](int n) {
+        const int tg = n / C::kSrc, src = n % C::kSrc;
+        const int row = src * C::kN + tg * 16 + rho;
+        return __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(al + row * kARowDw + 4 * (4 * g + i)));
+      };
+      bf16x8_t bnext = bread(0);
 #pragma unroll
-      for (int ii = 0; ii < 2; ++ii) {
-        const int i = 2 * half + ii;
-        bf16x8_t aop[C::kMats][C::kRG];
+      for (int n = 0; n < kB; ++n) {
+        const bf16x8_t bop = bnext;
+        if (n + 1 < kB) bnext = bread(n + 1);
+        const int tg = n / C::kSrc;
 #pragma unroll
         for (int mi = 0; mi < C::kMats; ++mi)
 #pragma unroll
-          for (int rg = 0; rg < C::kRG; ++rg) {
-            aop[mi][rg] = decode_dword(q[mi][rg][ii], sf[mi][rg]);
-          }
-        // activations: block g of the step, P-order positions 8i..8i+7 (chunk
-        // 4g+i); one operand is read ahead while the previous one feeds its MFMAs
-        constexpr int kB = C::kTG * C::kSrc;
-        auto bread = [&](int n) {
-          const int tg = n / C::kSrc, src = n % C::kSrc;
-          const int row = src * C::kN + tg * 16 + rho;
-          return __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(al + row * kARowDw + 4 * (4 * g + i)));
-        };
-        bf16x8_t bnext = bread(0);
-#pragma unroll
-        for (int n = 0; n < kB; ++n) {
-          const bf16x8_t bop = bnext;
-          if (n + 1 < kB) bnext = bread(n + 1);
-          const int tg = n / C::kSrc;
-#pragma unroll
-          for (int mi = 0; mi < C::kMats; ++mi)
-#pragma unroll
-            for (int rg = 0; rg < C::kRG; ++rg)
-              acc[mi][rg][tg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop[mi][rg], bop, acc[mi][rg][tg], 0, 0, 0);
-          __builtin_amdgcn_sched_barrier(0);
-        }
+          for (int rg = 0; rg < C::kRG; ++rg)
+            acc[mi][rg][tg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop[mi][rg], bop, acc[mi][rg][tg], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
+  };
+
+  issue(0, 0);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  for (int s = 0; s < nstages; s += 4) {
+    run_stage(std::integral_constant<int, 0>{}, s);
+    if (s + 1 < nstages) run_stage(std::integral_constant<int, 1>{}, s + 1);
+    if (s + 2 < nstages) run_stage(std::integral_constant<int, 2>{}, s + 2);
+    if (s + 3 < nstages) run_stage(std::integral_constant<int, 3>{}, s + 3);
   }
 
   // ---- epilogue ----
@@ -312,7 +325,12 @@ __global__ __launch_bounds__(kThreads) void ffn_big_kernel(GemmArgs a) {
 
 }  // namespace
 
-bool big_gemm_supported(int D, int I) { return (I % BigCfg<true>::kF) == 0 && (D % BigCfg<false>::kF) == 0; }
+// Feature tiles must divide the outputs, and K must be a multiple of 4 steps
+// (512) so the last 80-byte weight window of a row ends exactly at the row end.
+bool big_gemm_supported(int D, int I) {
+  return (I % BigCfg<true>::kF) == 0 && (D % BigCfg<false>::kF) == 0 && (D % (4 * kKStep)) == 0 &&
+         (I % (4 * kKStep)) == 0;
+}
 
 int big_rows_per_tile(bool gate_up) { return gate_up ? BigCfg<true>::kN : BigCfg<false>::kN; }
 

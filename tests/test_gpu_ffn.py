@@ -67,8 +67,9 @@ def test_tiny(k3):
         (5, 1, 256, 128, 1),  # single token, k = 1
         (12, 3, 640, 512, 65),  # two grouping chunks, one token in the second
         (8192, 2, 128, 128, 40),  # largest supported expert count
-        (8, 2, 512, 256, 300),  # large-tile path: ragged 128-row (gate/up) and 64-row (down) tiles
+        (8, 2, 512, 512, 300),  # large-tile path: ragged 128-row (gate/up) and 64-row (down) tiles
         (16, 4, 1024, 512, 400),  # large-tile path with two feature tiles per matrix
+        (12, 4, 2048, 1024, 700),  # large-tile path, 4 gate/up feature tiles (2D work order)
     ],
 )
 def test_shapes(k3, E, k, D, I, T):
