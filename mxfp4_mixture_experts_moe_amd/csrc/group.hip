@@ -186,18 +186,124 @@ __global__ __launch_bounds__(256) void group_count_kernel(GroupArgs a) {
   extern __shared__ unsigned long long lmask[];
   const int64_t c = blockIdx.x;
   build_masks(a.ids, a.T, a.k, a.E, c, lmask);
-  for (int e = threadIdx.x; e < a.E; e += blockDim.x) a.chunk_mask[c * a.E + e] = lmask[e];
+  for (int e = threadIdx.x; e < a.E; e += blockDim.x) {
+    const unsigned long long m = lmask[e];
+    a.chunk_mask[c * a.E + e] = m;
+    a.chunk_base[c * a.E + e] = __popcll(m);  // per-chunk count; the scan turns it into a base
+  }
 }
 
+// Multi-chunk scan (one workgroup of 1024 threads).  chunk_base holds the
+// per-(chunk, expert) counts on entry and the per-(chunk, expert) bases on exit.
 __global__ __launch_bounds__(kScanThreads) void group_scan_kernel(GroupArgs a, int64_t n_chunks) {
-  scan_experts(a.chunk_mask, n_chunks, a.E, a.rows_per_tile[0], a.rows_per_tile[1], a.counts, a.offsets,
-               a.tile_count, a.tiles[0], a.tiles[1], a.chunk_base);
+  extern __shared__ int32_t ltot[];  // [E] per-expert totals
+  const int E = a.E, tid = threadIdx.x;
+  for (int e = tid; e < E; e += kScanThreads) ltot[e] = 0;
+  __syncthreads();
+  const int64_t n = n_chunks * E;
+  for (int64_t i = tid; i < n; i += kScanThreads) {
+    const int32_t v = a.chunk_base[i];
+    if (v) atomicAdd(&ltot[(int)(i % E)], v);
+  }
+  __syncthreads();
+  // offsets and tiles: thread t owns experts 8t..8t+7
+  const int rpt0 = a.rows_per_tile[0], rpt1 = a.rows_per_tile[1];
+  const int e0 = tid * kMaxExpertsPerScanThread;
+  int my_rows = 0, my_tiles0 = 0, my_tiles1 = 0;
+  for (int i = 0; i < kMaxExpertsPerScanThread; ++i) {
+    const int e = e0 + i;
+    if (e >= E) break;
+    const int cnt = ltot[e];
+    my_rows += cnt;
+    my_tiles0 += (cnt + rpt0 - 1) / rpt0;
+    my_tiles1 += (cnt + rpt1 - 1) / rpt1;
+  }
+  int total_rows, total_tiles0, total_tiles1;
+  int row_off = block_exclusive_scan(my_rows, &total_rows);
+  int tile_off0 = block_exclusive_scan(my_tiles0, &total_tiles0);
+  int tile_off1 = block_exclusive_scan(my_tiles1, &total_tiles1);
+  for (int i = 0; i < kMaxExpertsPerScanThread; ++i) {
+    const int e = e0 + i;
+    if (e >= E) break;
+    const int cnt = ltot[e];
+    a.counts[e] = cnt;
+    a.offsets[e] = row_off;
+    for (int r = 0; r < cnt; r += rpt0) {
+      Tile tl;
+      tl.expert = e;
+      tl.row0 = row_off + r;
+      tl.nrows = cnt - r < rpt0 ? cnt - r : rpt0;
+      tl.pad = 0;
+      a.tiles[0][tile_off0++] = tl;
+    }
+    for (int r = 0; r < cnt; r += rpt1) {
+      Tile tl;
+      tl.expert = e;
+      tl.row0 = row_off + r;
+      tl.nrows = cnt - r < rpt1 ? cnt - r : rpt1;
+      tl.pad = 0;
+      a.tiles[1][tile_off1++] = tl;
+    }
+    row_off += cnt;
+    ltot[e] = a.offsets[e];  // reuse: the expert's first grouped row
+  }
+  if (tid == 0) {
+    a.offsets[E] = total_rows;
+    a.tile_count[0] = total_tiles0;
+    a.tile_count[1] = total_tiles1;
+  }
+  __syncthreads();
+  // bases: expert-parallel running sums over the chunks (loads kept in flight)
+  for (int e = tid; e < E; e += kScanThreads) {
+    int run = ltot[e];
+    int64_t c = 0;
+    for (; c + 8 <= n_chunks; c += 8) {
+      int32_t v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = a.chunk_base[(c + u) * E + e];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        a.chunk_base[(c + u) * E + e] = run;
+        run += v[u];
+      }
+    }
+    for (; c < n_chunks; ++c) {
+      const int32_t v = a.chunk_base[c * E + e];
+      a.chunk_base[c * E + e] = run;
+      run += v;
+    }
+  }
 }
 
+// Grouped rows of chunk c (part blockIdx.y of kPlaceParts) and the re-laid-out
+// activations of its tokens.
+constexpr int kPlaceParts = 8;
 __global__ __launch_bounds__(256) void group_place_kernel(GroupArgs a) {
   const int64_t c = blockIdx.x;
-  place_entries(a.ids, a.T, a.k, a.E, c, a.chunk_mask + c * a.E, a.chunk_base + c * a.E, a.row_tok, a.slot_row);
-  permute_chunk_rows(a.x, a.x_perm, a.T, a.D, c);
+  const int part = blockIdx.y;
+  const int64_t t0 = c * kChunkTokens;
+  const unsigned long long* mask_c = a.chunk_mask + c * a.E;
+  const int32_t* base_c = a.chunk_base + c * a.E;
+  for (int idx = part * blockDim.x + threadIdx.x; idx < kChunkTokens * a.k; idx += kPlaceParts * blockDim.x) {
+    const int tl = idx / a.k, j = idx - tl * a.k;
+    const int64_t t = t0 + tl;
+    if (t >= a.T) continue;
+    int e;
+    int32_t row = -1;
+    if (entry_expert(a.ids + t * a.k, j, a.E, e)) {
+      const unsigned long long before = tl ? (mask_c[e] & ((1ull << tl) - 1ull)) : 0ull;
+      row = base_c[e] + __popcll(before);
+      a.row_tok[row] = (int32_t)t;
+    }
+    a.slot_row[t * a.k + j] = row;
+  }
+  const int groups = a.D / 8;
+  const int64_t nt = (a.T - t0) < kChunkTokens ? (a.T - t0) : kChunkTokens;
+  for (int64_t idx = part * blockDim.x + threadIdx.x; idx < nt * groups; idx += kPlaceParts * blockDim.x) {
+    const int64_t tl = idx / groups;
+    const int g = (int)(idx - tl * groups);
+    perm_group(a.x + (t0 + tl) * a.D, a.x_perm + (t0 + tl) * a.D, g);
+  }
 }
 
 // All phases for a batch of at most one chunk (T <= 64), one launch.
@@ -227,10 +333,10 @@ hipError_t launch_group(const GroupArgs& a, hipStream_t s) {
   hipLaunchKernelGGL(group_count_kernel, dim3((unsigned)n_chunks), dim3(256), mask_lds, s, a);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(group_scan_kernel, dim3(1), dim3(kScanThreads), 0, s, a, n_chunks);
+  hipLaunchKernelGGL(group_scan_kernel, dim3(1), dim3(kScanThreads), (size_t)a.E * sizeof(int32_t), s, a, n_chunks);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(group_place_kernel, dim3((unsigned)n_chunks), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(group_place_kernel, dim3((unsigned)n_chunks, kPlaceParts), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
