@@ -32,21 +32,31 @@ METRIC = "routed-MoE tokens/s at K3 shape; achieved HBM GB/s (decode) / MFMA % (
 PEAK_HBM_GBS = 8000.0  # MI355X HBM3E
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 RIDGE = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)  # flop per byte
-KERNEL_NAMES = {
-    "route": "route_topk_kernel",
-    "group": "group_*_kernel",
-    "gate_up": "ffn_gemm_kernel<gate/up>",
-    "down": "ffn_gemm_kernel<down>",
-    "combine": "combine_kernel",
-}
 TRAFFIC_DIR = os.path.join(ROOT, "profiles")
-KERNEL_SOURCES = {
-    "gate_up": "mxfp4_mixture_experts_moe_amd/csrc/ffn.hip",
-    "down": "mxfp4_mixture_experts_moe_amd/csrc/ffn.hip",
-    "combine": "mxfp4_mixture_experts_moe_amd/csrc/ffn.hip",
-    "route": "mxfp4_mixture_experts_moe_amd/csrc/route.hip",
-    "group": "mxfp4_mixture_experts_moe_amd/csrc/group.hip",
-}
+CSRC = "mxfp4_mixture_experts_moe_amd/csrc/"
+
+
+def gemm_path(cfg) -> str:
+    """Which grouped-GEMM kernels moe_mxfp4_ffn launches for this shape (the
+    library's own selection rule, restated for labelling the roofline)."""
+    entries = cfg.T * cfg.k
+    active = min(entries, cfg.E)
+    fits = entries * max(cfg.I, cfg.D) * 2 < (1 << 31)
+    if cfg.D % 512 == 0 and cfg.I % 512 == 0 and fits and entries // active >= 48:
+        return "big"
+    if cfg.D % 512 == 0 and cfg.I % 512 == 0 and entries <= 4 * active:
+        return "stream"
+    return "small"
+
+
+def kernel_info(stage: str, path: str):
+    """(kernel name as rocprofv3 reports it, source file) of a stage."""
+    gemm = {"big": ("ffn_big_kernel<{}>", "ffn_big.hip"), "stream": ("ffn_stream_kernel<{}>", "ffn_stream.hip"),
+            "small": ("ffn_gemm_kernel<NT, {}, ...>", "ffn.hip")}[path]
+    if stage in ("gate_up", "down"):
+        return gemm[0].format("true" if stage == "gate_up" else "false"), CSRC + gemm[1]
+    return {"route": ("route_topk_kernel", CSRC + "route.hip"), "group": ("group_*_kernel", CSRC + "group.hip"),
+            "combine": ("combine_kernel", CSRC + "ffn.hip")}[stage]
 
 
 def parse_args():
@@ -67,7 +77,7 @@ def source_sha(rel: str) -> str:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def stored_traffic(stage: str, workload: str):
+def stored_traffic(stage: str, workload: str, source: str):
     """HBM bytes per launch from a committed rocprofv3 --pmc summary, if it was taken
     on the current kernel source (else None)."""
     path = os.path.join(TRAFFIC_DIR, f"{stage}_{workload}_traffic.txt")
@@ -78,7 +88,7 @@ def stored_traffic(stage: str, workload: str):
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             kv[k.strip()] = v.strip()
-    if kv.get("source_sha") != source_sha(KERNEL_SOURCES[stage]):
+    if kv.get("source_sha") != source_sha(source):
         return None
     try:
         return float(kv["hbm_bytes_per_launch"])
@@ -210,7 +220,8 @@ def main():
         achieved, peak, unit = flops / dur_s / 1e12, PEAK_BF16_TFLOPS, "TFLOP/s"
     else:
         achieved, peak, unit = byts / dur_s / 1e9, PEAK_HBM_GBS, "GB/s"
-    traffic = stored_traffic(dom, args.workload)
+    kname, ksrc = kernel_info(dom, gemm_path(cfg))
+    traffic = stored_traffic(dom, args.workload, ksrc)
 
     value = cfg.T * steps / elapsed
     weight_bytes = float(np.mean(act_steps)) * (2 * cfg.I * (cfg.D // 32) * 17 + cfg.D * (cfg.I // 32) * 17)
@@ -240,7 +251,7 @@ def main():
             "mean_active_experts": float(np.mean(act_steps)),
         },
         "roofline": {
-            "kernel": KERNEL_NAMES[dom],
+            "kernel": kname,
             "bound": bound,
             "achieved": achieved,
             "peak": peak,

@@ -5,10 +5,12 @@ method's arithmetic (no decoding, routing or matrix products).  Both the fp64
 CPU oracle and the GPU library consume what it produces, so neither side ever
 takes an input from the other.
 
-Every tensor comes from its own keyed PCG64 stream,
-``numpy.random.default_rng([seed, config_id, tensor_id, expert])``, so any
-single expert matrix can be regenerated alone (the FFN oracle only needs the
-experts a batch actually routes to).
+Every tensor comes from its own keyed PCG64 stream: activations and router
+inputs from ``numpy.random.default_rng([seed, config_id, tensor_id])``, expert
+matrices from ``default_rng([seed, 100 + weight_id, tensor_id, expert])`` (all
+K3-shaped workloads share one weight set), so any single expert matrix can be
+regenerated alone (the FFN oracle only needs the experts a batch actually
+routes to).
 
 Workload shapes follow the Kimi-K3 routed experts described on the llama.cpp
 pull-request page "model: add Kimi-K3 text model": 896 experts, 16 used,

@@ -140,7 +140,11 @@ int moe_mxfp4_ffn_profiled(const void* x_bf16, const int32_t* topk_ids, const fl
   // stay below 2 GiB; bigger batches take the general path.
   const bool offsets_fit = entries * (int64_t)(I > D ? I : D) * 2 < ((int64_t)1 << 31);
   const bool big = big_gemm_supported(D, I) && offsets_fit && entries / active >= 48;
-  const int rpt_small = choose_rows_per_tile(T, k, E);
+  // Weight-streaming GEMMs when experts average at most 4 rows (decode-sized
+  // batches): the product is bound by reading the active experts' weights.
+  // They also address activations through 32-bit buffer offsets.
+  const bool streaming = !big && stream_gemm_supported(D, I) && offsets_fit && entries <= 4 * active;
+  const int rpt_small = streaming ? stream_rows_per_tile() : choose_rows_per_tile(T, k, E);
   const int rpt_gu = big ? big_rows_per_tile(true) : rpt_small;
   const int rpt_dn = big ? big_rows_per_tile(false) : rpt_small;
 
@@ -185,7 +189,7 @@ int moe_mxfp4_ffn_profiled(const void* x_bf16, const int32_t* topk_ids, const fl
   gu.N = I;
   gu.out = ws + L.h;
   gu.out_lo = ws + L.h_lo;
-  err = big ? launch_big_gate_up(gu, s) : launch_gate_up(gu, rpt_gu, s);
+  err = big ? launch_big_gate_up(gu, s) : streaming ? launch_stream_gate_up(gu, s) : launch_gate_up(gu, rpt_gu, s);
   if (err != hipSuccess || !mark(2)) return K3MOE_ERR_DEVICE;
 
   GemmArgs dn{};
@@ -201,7 +205,7 @@ int moe_mxfp4_ffn_profiled(const void* x_bf16, const int32_t* topk_ids, const fl
   dn.K = I;
   dn.N = D;
   dn.out = ws + L.y;
-  err = big ? launch_big_down(dn, s) : launch_down(dn, rpt_dn, s);
+  err = big ? launch_big_down(dn, s) : streaming ? launch_stream_down(dn, s) : launch_down(dn, rpt_dn, s);
   if (err != hipSuccess || !mark(3)) return K3MOE_ERR_DEVICE;
 
   err = launch_combine(reinterpret_cast<const float*>(ws + L.y), g.slot_row, topk_w, T, D, k, out, s);

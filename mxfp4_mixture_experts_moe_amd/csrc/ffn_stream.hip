@@ -1,0 +1,371 @@
+// Weight-streaming grouped GEMMs for batches in which every expert sees only a
+// few tokens (decode-sized batches).  Same arithmetic as ffn.hip (bf16 MFMA,
+// the MXFP4 block scale folded into the exact fp4 -> bf16 conversion, fp32
+// accumulation, h carried as a bf16 hi + lo pair); only the work decomposition
+// differs.
+//
+// With one or two tokens per expert the product is a stream over the active
+// experts' weight bytes (about 4 flop per byte), so the kernel is laid out for
+// HBM, not for the matrix cores:
+//   - every wave works alone: a unit is 16 output features of one tile (up to
+//     4 grouped rows of one expert) over the whole K, and the wave stages the
+//     unit's weight rows through a private ring of three LDS buffers with
+//     direct global -> LDS loads of 16 bytes per lane, two stages ahead of the
+//     one it decodes; no workgroup barrier anywhere;
+//   - a stage is 16 MXFP4 blocks (512 K) of each row: 272 bytes, 17 aligned
+//     16-byte chunks, so rows of 1904 / 1632 bytes stream without over-fetch;
+//   - the tile's activation rows for the same 512 K (x for gate/up, h_hi and
+//     h_lo for down) ride in the same stage, one 1 KB load per row the tile
+//     actually has (the wait counts follow the per-stage load count); for down
+//     the h_hi and h_lo rows sit in different MFMA columns, so one MFMA per
+//     decoded operand covers both halves of h;
+//   - the waves are persistent: one workgroup of four waves per CU, wave w
+//     takes units w, w + W, w + 2W, ..., and the ring runs across unit
+//     boundaries so the stream never drains between units.
+// The MFMA still does the multiply: its 16 columns are the tile's (up to 4)
+// rows, the unused columns hold whatever the LDS row slots hold and are never
+// stored.
+#include "k3moe_internal.h"
+
+#include <math.h>
+
+namespace k3moe {
+namespace {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kWaves = 4;            // waves per workgroup (one workgroup per CU)
+constexpr int kRing = 3;             // LDS stage buffers per wave
+constexpr int kStageK = 512;         // K per stage (16 MXFP4 blocks)
+constexpr int kStageRowBytes = 272;  // bytes of one weight row per stage (17 chunks of 16 B)
+constexpr int kRowChunks = 17;
+constexpr int kRowDw = 68;           // LDS dwords per staged weight row
+constexpr int kBRowBytes = 1040;     // LDS bytes per activation row per stage (1024 + 16 padding)
+constexpr int kTileRows = 4;         // grouped rows per tile
+
+template <bool kGateUp>
+struct StreamCfg;
+template <>
+struct StreamCfg<true> {  // w1 and w3: 16 rows x 17 chunks each (5 loads per matrix), 4 x rows
+  static constexpr int kMats = 2, kWInstr = 10, kBRows = 4;
+};
+template <>
+struct StreamCfg<false> {  // w2: 16 rows x 17 chunks (5 loads), 4 h_hi + 4 h_lo rows
+  static constexpr int kMats = 1, kWInstr = 5, kBRows = 8;
+};
+template <bool kGateUp>
+constexpr int kStageBytes = StreamCfg<kGateUp>::kMats * 16 * kStageRowBytes + StreamCfg<kGateUp>::kBRows * kBRowBytes;
+static_assert(2 * (StreamCfg<true>::kWInstr + StreamCfg<true>::kBRows) < 64, "vmcnt range");
+static_assert(2 * (StreamCfg<false>::kWInstr + StreamCfg<false>::kBRows) < 64, "vmcnt range");
+static_assert(kWaves * kRing * kStageBytes<true> <= 160 * 1024, "LDS");
+static_assert(kWaves * kRing * kStageBytes<false> <= 160 * 1024, "LDS");
+
+__device__ __forceinline__ float e8m0_to_f32(uint32_t e) { return __uint_as_float(e ? (e << 23) : 0x00400000u); }
+
+__device__ __forceinline__ bf16x8_t decode_dword(uint32_t q, float sf) {
+  uint4 r;
+  r.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, sf, 0));
+  r.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, sf, 1));
+  r.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, sf, 2));
+  r.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(q, sf, 3));
+  return __builtin_bit_cast(bf16x8_t, r);
+}
+
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)f);
+}
+
+// Block (4*rnd + g) of staged row `lrow`: four bf16x8 operands (P-order
+// positions 8i..8i+7, i = 0..3).  The block starts at byte 68*rnd + 17*g of the
+// row, i.e. at byte g of dword 17*rnd + 4*g; its qs dword i is bytes
+// g+1+4i .. g+4+4i, picked out of two neighbouring dwords with v_perm.
+__device__ __forceinline__ void decode_block(const uint32_t* w, int lrow, int rnd, int g, uint32_t qsel,
+                                             bf16x8_t op[4]) {
+  const uint32_t* L = w + lrow * kRowDw + 17 * rnd + 4 * g;
+  const uint32_t d0 = L[0], d1 = L[1], d2 = L[2], d3 = L[3], d4 = L[4];
+  const float sf = e8m0_to_f32(__builtin_amdgcn_ubfe(d0, 8 * g, 8));
+  op[0] = decode_dword(__builtin_amdgcn_perm(d1, d0, qsel), sf);
+  op[1] = decode_dword(__builtin_amdgcn_perm(d2, d1, qsel), sf);
+  op[2] = decode_dword(__builtin_amdgcn_perm(d3, d2, qsel), sf);
+  op[3] = decode_dword(__builtin_amdgcn_perm(d4, d3, qsel), sf);
+}
+
+// Tile list and token map are read through the constant address space so that
+// the wave-uniform reads become scalar loads: a vector load would have to be
+// waited for with the global -> LDS loads still in flight ahead of it.
+template <typename T_>
+__device__ __forceinline__ const __attribute__((address_space(4))) T_* as_const(const T_* p) {
+  return reinterpret_cast<const __attribute__((address_space(4))) T_*>(reinterpret_cast<uintptr_t>(p));
+}
+
+struct TileInfo {
+  int expert, row0, nrows;
+};
+__device__ __forceinline__ TileInfo load_tile(const Tile* tiles, int idx) {
+  const auto p = as_const(reinterpret_cast<const int32_t*>(tiles) + 4 * idx);
+  return TileInfo{p[0], p[1], p[2]};
+}
+
+// s_waitcnt vmcnt(N): at most N of this wave's vector-memory operations
+// outstanding.  Loads complete in issue order, so after the wait every load
+// issued before the newest N has landed (in LDS, for the global -> LDS loads).
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+// The same with N = kBase + b, b (0..16) known only at run time.
+template <int kBase>
+__device__ __forceinline__ void wait_vm_plus(int b) {
+  switch (b) {
+#define K3_CASE(v) \
+  case v: wait_vm<kBase + v>(); break;
+    K3_CASE(0) K3_CASE(1) K3_CASE(2) K3_CASE(3) K3_CASE(4) K3_CASE(5) K3_CASE(6) K3_CASE(7) K3_CASE(8)
+    K3_CASE(9) K3_CASE(10) K3_CASE(11) K3_CASE(12) K3_CASE(13) K3_CASE(14) K3_CASE(15) K3_CASE(16)
+#undef K3_CASE
+    default: wait_vm<0>(); break;
+  }
+}
+
+// Where a wave stands in its list of units: unit u = wid + j * nw, K stage s.
+struct Cursor {
+  int64_t u;
+  int s;
+  int fg;         // 16-feature group of the unit
+  TileInfo tile;  // tile of the unit
+};
+
+template <bool kGateUp>
+__global__ __launch_bounds__(kWaves * 64, 1) void ffn_stream_kernel(GemmArgs a) {
+  using C = StreamCfg<kGateUp>;
+  constexpr int kSB = kStageBytes<kGateUp>;
+  constexpr int kMatBytes = 16 * kStageRowBytes;  // one matrix's 16 rows of a stage
+  constexpr int kWBytes = C::kMats * kMatBytes;   // activation rows start here
+  constexpr int kW = C::kWInstr;                  // weight loads per stage
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kWaves][kRing][kSB];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int rho = lane & 15, g = lane >> 4;
+  const int nfg = a.N / 16;  // 16-feature groups
+  const auto row_tok = as_const(a.row_tok);
+  const int64_t n_units = (int64_t)(*as_const(a.tile_count)) * nfg;
+  const int64_t nw = (int64_t)gridDim.x * kWaves;
+  const int64_t wid = (int64_t)blockIdx.x * kWaves + wave;
+  if (wid >= n_units) return;  // uniform over the wave; no barriers below
+  const int64_t my_units = (n_units - wid + nw - 1) / nw;
+  const int nst = a.K / kStageK;
+  const int64_t Q = my_units * nst;
+  const uint32_t row_bytes = (uint32_t)(a.K >> 5) * 17;
+  const size_t mat_bytes = (size_t)a.N * row_bytes;
+  const uint32_t act_row_bytes = (uint32_t)a.K * 2;
+
+  // Per-lane byte offset of weight chunk c = 64j + lane of one matrix's
+  // stage (MFMA row rr = c / 17 is feature 16*fg + rr; chunk ch = c % 17),
+  // relative to the unit's first row; the stage adds 272*s in the scalar
+  // offset.  Only the last load of a matrix is partial (lanes < 16).
+  constexpr int kInstrPerMat = (16 * kRowChunks + 63) / 64;  // 5
+  uint32_t woff[kInstrPerMat];
+#pragma unroll
+  for (int j = 0; j < kInstrPerMat; ++j) {
+    const int c = 64 * j + lane;
+    const int rr = c / kRowChunks, ch = c - rr * kRowChunks;
+    woff[j] = c < 16 * kRowChunks ? (uint32_t)rr * row_bytes + 16 * ch : 0u;
+  }
+  const bool wtail = lane < 16 * kRowChunks - 64 * (kInstrPerMat - 1);  // lanes of the partial load
+
+  auto load_unit = [&](Cursor& c) {
+    const int tile_idx = __builtin_amdgcn_readfirstlane((int)(c.u / nfg));
+    c.fg = __builtin_amdgcn_readfirstlane((int)(c.u - (int64_t)tile_idx * nfg));
+    c.tile = load_tile(a.tiles, tile_idx);
+  };
+  auto advance = [&](Cursor& c) {
+    if (++c.s == nst) {
+      c.s = 0;
+      c.u += nw;
+      if (c.u < n_units) load_unit(c);
+    }
+  };
+
+  // Issue side: stage q of this wave (cursor ci) into ring buffer `buf`;
+  // returns how many activation loads it issued.
+  auto issue = [&](const Cursor& c, int buf) -> int {
+    uint8_t* dst = &lds[wave][buf][0];
+    const size_t unit_off = (size_t)c.tile.expert * mat_bytes + (size_t)(16 * c.fg) * row_bytes;
+    const uint32_t wso = (uint32_t)(kStageRowBytes * c.s);
+#pragma unroll
+    for (int mi = 0; mi < C::kMats; ++mi) {
+      const uint8_t* base = (mi == 0 ? a.wa : a.wb) + unit_off;
+      const __amdgpu_buffer_rsrc_t rsrc =
+          __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, (int)(16 * row_bytes), 0x00020000);
+#pragma unroll
+      for (int j = 0; j < kInstrPerMat - 1; ++j)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)(uintptr_t)(dst + mi * kMatBytes + 1024 * j),
+                                                 16, woff[j], wso, 0, 0);
+      if (wtail)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rsrc, (__attribute__((address_space(3))) void*)(uintptr_t)(dst + mi * kMatBytes + 1024 * (kInstrPerMat - 1)), 16,
+            woff[kInstrPerMat - 1], wso, 0, 0);
+    }
+    uint8_t* bdst = dst + kWBytes;
+    const uint32_t aso = (uint32_t)(kStageK * 2 * c.s);
+    const __amdgpu_buffer_rsrc_t xr =
+        __builtin_amdgcn_make_buffer_rsrc((void*)a.act, 0, (int)((uint32_t)a.act_rows * act_row_bytes), 0x00020000);
+    const __amdgpu_buffer_rsrc_t lr = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(kGateUp ? a.act : a.act_lo), 0, (int)((uint32_t)a.act_rows * act_row_bytes), 0x00020000);
+#pragma unroll
+    for (int m = 0; m < kTileRows; ++m) {
+      if (m < c.tile.nrows) {
+        const int row = c.tile.row0 + m;
+        const uint32_t src = (uint32_t)(kGateUp ? row_tok[row] : row) * act_row_bytes + aso;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (__attribute__((address_space(3))) void*)(uintptr_t)(bdst + kBRowBytes * m),
+                                                 16, 16 * lane, src, 0, 0);
+        if (!kGateUp)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(
+              lr, (__attribute__((address_space(3))) void*)(uintptr_t)(bdst + kBRowBytes * (kTileRows + m)), 16, 16 * lane,
+              src, 0, 0);
+      }
+    }
+    return (kGateUp ? 1 : 2) * c.tile.nrows;
+  };
+
+  f32x4_t acc[C::kMats];
+#pragma unroll
+  for (int mi = 0; mi < C::kMats; ++mi) acc[mi] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  const uint32_t qsel = 0x03020100u + 0x01010101u * (uint32_t)(g + 1);
+  Cursor ci{wid, 0, 0, {0, 0, 0}};  // issue side
+  load_unit(ci);
+  Cursor cc = ci;  // compute side
+  int buf_i = 0, buf_c = 0;
+  issue(ci, buf_i);
+  advance(ci);
+  buf_i = 1;
+  int b_next = 0;  // activation loads of stage q + 1
+  if (Q > 1) {
+    b_next = issue(ci, buf_i);
+    advance(ci);
+    buf_i = 2;
+  }
+  // B column rho reads LDS activation row brow: for gate/up the tile's row
+  // rho; for down h_hi row rho (columns 0..3) or h_lo row rho - 4 (columns
+  // 4..7), so one MFMA multiplies both halves of h (added in the epilogue).
+  // Columns without a row read row 0 (a broadcast; their sums are dropped).
+  auto brow_of = [&](int nrows) {
+    const bool has = kGateUp ? rho < nrows : (rho < 2 * kTileRows && (rho & (kTileRows - 1)) < nrows);
+    return has ? rho : 0;
+  };
+  int boff = kWBytes + kBRowBytes * brow_of(cc.tile.nrows);
+
+  for (int64_t q = 0; q < Q; ++q) {
+    // Stage q's loads are the oldest outstanding ones: wait until only the
+    // loads of stages q+1 and q+2 (and whatever follows them) may be pending.
+    if (q + 2 < Q) {
+      const int b2 = issue(ci, buf_i);
+      advance(ci);
+      buf_i = buf_i == kRing - 1 ? 0 : buf_i + 1;
+      wait_vm_plus<2 * kW>(b_next + b2);
+      b_next = b2;
+    } else if (q + 1 < Q) {
+      wait_vm_plus<kW>(b_next);
+    } else {
+      wait_vm<0>();
+    }
+    const uint8_t* st = &lds[wave][buf_c][0];
+    buf_c = buf_c == kRing - 1 ? 0 : buf_c + 1;
+    const uint32_t* wl = reinterpret_cast<const uint32_t*>(st);
+    const uint8_t* bl = st + boff;
+#pragma unroll
+    for (int rnd = 0; rnd < 4; ++rnd) {
+      bf16x8_t bop[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) bop[i] = *reinterpret_cast<const bf16x8_t*>(bl + 64 * (4 * rnd + g) + 16 * i);
+#pragma unroll
+      for (int mi = 0; mi < C::kMats; ++mi) {
+        bf16x8_t aop[4];
+        decode_block(wl, 16 * mi + rho, rnd, g, qsel, aop);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[mi] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop[i], bop[i], acc[mi], 0, 0, 0);
+      }
+    }
+
+    if (cc.s == nst - 1) {
+      // Epilogue of the unit: lane holds features 16*fg + 4g + v for tile row rho.
+      const TileInfo& tile = cc.tile;
+      const int fg = cc.fg;
+      if (!kGateUp) {
+        // y = (h_hi part in column rho) + (h_lo part in column rho + 4)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) acc[0][v] += __shfl_down(acc[0][v], kTileRows, 16);
+      }
+      if (rho < tile.nrows) {
+        const int64_t row = tile.row0 + rho;
+        if (kGateUp) {
+          uint32_t hb[4], lb[4];
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const float gt = acc[0][v], up = acc[C::kMats - 1][v];
+            const float h = gt / (1.0f + expf(-gt)) * up;
+            hb[v] = f32_to_bf16_bits(h);
+            lb[v] = f32_to_bf16_bits(h - __uint_as_float(hb[v] << 16));
+          }
+          // feature 16*fg + 4g + v is element e = 16*(fg&1) + 4g + v of
+          // I-block fg/2, stored at its P-order position 8g + 2v + (fg&1)
+          const int pos = 32 * (fg >> 1) + 8 * g + (fg & 1);
+          uint16_t* hrow = reinterpret_cast<uint16_t*>(a.out) + row * a.N + pos;
+          uint16_t* lrow = reinterpret_cast<uint16_t*>(a.out_lo) + row * a.N + pos;
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            hrow[2 * v] = (uint16_t)hb[v];
+            lrow[2 * v] = (uint16_t)lb[v];
+          }
+        } else {
+          float* yrow = reinterpret_cast<float*>(a.out) + row * a.N;
+          *reinterpret_cast<float4*>(yrow + 16 * fg + 4 * g) = make_float4(acc[0][0], acc[0][1], acc[0][2], acc[0][3]);
+        }
+      }
+#pragma unroll
+      for (int mi = 0; mi < C::kMats; ++mi) acc[mi] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+    advance(cc);
+    if (cc.s == 0 && q + 1 < Q) boff = kWBytes + kBRowBytes * brow_of(cc.tile.nrows);
+  }
+}
+
+int cu_count() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
+template <bool kGateUp>
+hipError_t launch_stream(const GemmArgs& a, hipStream_t s) {
+  const int64_t max_units = a.max_tiles * (a.N / 16);
+  int64_t grid = (max_units + kWaves - 1) / kWaves;
+  const int cus = cu_count();
+  if (grid > cus) grid = cus;
+  if (grid < 1) grid = 1;
+  hipLaunchKernelGGL(ffn_stream_kernel<kGateUp>, dim3((unsigned)grid), dim3(kWaves * 64), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+// K must be whole stages (rows of 16-block multiples, so every row and every
+// stage window starts 16-byte aligned); I must hold whole 32-feature blocks.
+bool stream_gemm_supported(int D, int I) { return (D % kStageK) == 0 && (I % kStageK) == 0; }
+
+int stream_rows_per_tile() { return kTileRows; }
+
+hipError_t launch_stream_gate_up(const GemmArgs& a, hipStream_t s) { return launch_stream<true>(a, s); }
+
+hipError_t launch_stream_down(const GemmArgs& a, hipStream_t s) { return launch_stream<false>(a, s); }
+
+}  // namespace k3moe

@@ -20,7 +20,7 @@ struct Tile {
 // Tokens per grouping chunk: one 64-bit bitmap per (chunk, expert).
 constexpr int kChunkTokens = 64;
 // The smallest tile height any GEMM variant uses; sizes the tile list.
-constexpr int kMinTileRows = 16;
+constexpr int kMinTileRows = 4;
 
 // Byte layout of the moe_mxfp4_ffn workspace (every region 256-byte aligned).
 struct FfnWorkspace {
@@ -81,6 +81,11 @@ bool big_gemm_supported(int D, int I);
 int big_rows_per_tile(bool gate_up);
 hipError_t launch_big_gate_up(const GemmArgs& a, hipStream_t s);
 hipError_t launch_big_down(const GemmArgs& a, hipStream_t s);
+
+bool stream_gemm_supported(int D, int I);
+int stream_rows_per_tile();
+hipError_t launch_stream_gate_up(const GemmArgs& a, hipStream_t s);
+hipError_t launch_stream_down(const GemmArgs& a, hipStream_t s);
 
 hipError_t launch_combine(const float* y, const int32_t* slot_row, const float* w, int64_t T, int D, int k,
                           float* out, hipStream_t s);

@@ -70,6 +70,10 @@ def test_tiny(k3):
         (8, 2, 512, 512, 300),  # large-tile path: ragged 128-row (gate/up) and 64-row (down) tiles
         (16, 4, 1024, 512, 400),  # large-tile path with two feature tiles per matrix
         (12, 4, 2048, 1024, 700),  # large-tile path, 4 gate/up feature tiles (2D work order)
+        (64, 4, 512, 512, 8),  # weight-streaming path: about one row per expert
+        (16, 4, 1024, 512, 16),  # streaming path: ~4 rows per expert, experts split over 4-row tiles
+        (32, 8, 1536, 1024, 3),  # streaming path: 3 K stages (gate/up), 2 (down)
+        (896, 16, 512, 1024, 1),  # streaming path: one token, 16 experts of 896
     ],
 )
 def test_shapes(k3, E, k, D, I, T):
@@ -98,6 +102,24 @@ def test_hot_expert_invalid_and_duplicate_ids(k3):
     a = run_ffn(k3, dev, batch.x, ids, w)
     b = run_ffn(k3, dev, batch.x, ids, w)
     assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
+def test_streaming_path_hot_invalid_and_duplicate_ids(k3):
+    # decode-sized batch (at most 4 rows per active expert on average) with one
+    # expert in every row: its 8 rows span two 4-row tiles
+    cfg = moe_inputs.TINY.with_(E=40, k=4, D=512, I=512, T=8, config_id=42)
+    g = np.random.default_rng(13)
+    ids = np.stack([g.permutation(cfg.E)[: cfg.k] for _ in range(cfg.T)]).astype(np.int32)
+    ids[:, 0] = 5
+    rest = ids[:, 1:]  # a view: keep the hot expert in slot 0 only
+    rest[rest == 5] = 6
+    ids[3, 1] = -2  # out of range -> skipped
+    ids[4, 3] = ids[4, 2]  # repeat -> skipped
+    w = g.random((cfg.T, cfg.k)).astype(np.float32)
+    got, ref, batch, dev = small_case(k3, cfg, ids, w)
+    assert_ffn_close(got, ref, "streaming hot/invalid/duplicate")
+    a = run_ffn(k3, dev, batch.x, ids, w)
+    assert np.array_equal(a.view(np.uint32), got.view(np.uint32))
 
 
 def test_identity_weights_closed_form(k3):
