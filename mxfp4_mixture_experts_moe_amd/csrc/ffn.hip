@@ -235,8 +235,10 @@ hipError_t launch_gemm(const GemmArgs& a, int rows_per_tile, hipStream_t s) {
 }
 
 // out[t] = sum_j w[t,j] * y[slot_row[t*k+j]], in slot order; 4 features per
-// thread.  The rows of up to 8 slots are loaded before any is summed, so each
-// thread keeps several independent reads in flight.
+// thread.  Slots are taken 16 at a time: all their row indices and weights
+// are loaded together, then all their y rows, so a thread waits for two
+// memory round trips per 16 slots and keeps 16 reads in flight.
+constexpr int kCombineSlots = 16;
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ y, const int32_t* __restrict__ slot_row,
                                                        const float* __restrict__ w, int64_t T, int D, int k,
                                                        float* __restrict__ out) {
@@ -246,20 +248,25 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
   const int64_t t = idx / q;
   const int d = (int)(idx - t * q) * 4;
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int j0 = 0; j0 < k; j0 += 8) {
-    f32x4_t v[8];
-    float wj[8];
+  for (int j0 = 0; j0 < k; j0 += kCombineSlots) {
+    int32_t r[kCombineSlots];
+    float wj[kCombineSlots];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int j = j0 + u;
-      const int32_t r = j < k ? slot_row[t * k + j] : -1;
-      wj[u] = r >= 0 ? w[t * k + j] : 0.f;
-      v[u] = r >= 0 ? __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(y + (int64_t)r * D + d))
-                    : f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int u = 0; u < kCombineSlots; ++u) {
+      const int j = j0 + u < k ? j0 + u : k - 1;
+      r[u] = slot_row[t * k + j];
+      wj[u] = w[t * k + j];
+    }
+    f32x4_t v[kCombineSlots];
+#pragma unroll
+    for (int u = 0; u < kCombineSlots; ++u) {
+      const bool use = j0 + u < k && r[u] >= 0;
+      v[u] = use ? __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(y + (int64_t)r[u] * D + d))
+                 : f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
     // skipped and out-of-range slots hold exact zeros: adding them changes nothing
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
+    for (int u = 0; u < kCombineSlots; ++u) {
       acc.x += wj[u] * v[u][0];
       acc.y += wj[u] * v[u][1];
       acc.z += wj[u] * v[u][2];

@@ -12,7 +12,9 @@
 // result does not depend on thread order).  A single-workgroup scan turns the
 // per-chunk popcounts into per-expert offsets and per-(chunk, expert) bases;
 // an entry's grouped row is then base + popcount(bitmap & tokens before it).
-// Small batches (one chunk) run all phases in one launch.
+// Small batches (one chunk) run all phases in one launch.  Tile counts and
+// row offsets are packed in 21-bit fields when one scan serves all three, so
+// that path needs at most 2^21 - 1 rows (it serves at most 1024 entries).
 #include "k3moe_internal.h"
 
 namespace k3moe {
@@ -65,6 +67,30 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* total_out) {
     total += tw;
   }
   __syncthreads();  // wave_tot may be reused by the next call
+  *total_out = total;
+  return before + incl - v;
+}
+
+// Block-wide exclusive scan of one uint64 per thread (blockDim.x == 1024);
+// used with three counters packed in 21-bit fields, so one scan serves all.
+__device__ __forceinline__ uint64_t block_exclusive_scan_u64(uint64_t v, uint64_t* total_out) {
+  __shared__ uint64_t wave_tot64[kScanThreads / 64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  uint64_t incl = v;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const uint64_t o = __shfl_up(incl, d, 64);
+    if (lane >= d) incl += o;
+  }
+  if (lane == 63) wave_tot64[wave] = incl;
+  __syncthreads();
+  uint64_t before = 0, total = 0;
+#pragma unroll
+  for (int w = 0; w < kScanThreads / 64; ++w) {
+    const uint64_t tw = wave_tot64[w];
+    if (w < wave) before += tw;
+    total += tw;
+  }
   *total_out = total;
   return before + incl - v;
 }
@@ -244,8 +270,8 @@ __global__ __launch_bounds__(kScanThreads) void group_scan_kernel(GroupArgs a, i
       tl.pad = 0;
       a.tiles[1][tile_off1++] = tl;
     }
+    ltot[e] = row_off;  // reuse: the expert's first grouped row
     row_off += cnt;
-    ltot[e] = a.offsets[e];  // reuse: the expert's first grouped row
   }
   if (tid == 0) {
     a.offsets[E] = total_rows;
@@ -319,6 +345,89 @@ __global__ __launch_bounds__(kScanThreads) void group_fused_kernel(GroupArgs a) 
   permute_chunk_rows(a.x, a.x_perm, a.T, a.D, 0);
 }
 
+// All phases for a batch of at most 64 tokens and 1024 entries (decode-sized),
+// one launch: thread i owns entry i for the whole kernel, the activation
+// re-layout is issued first (it does not depend on the ids), and one packed
+// scan yields row offsets and both tile lists.
+// LDS: E bitmaps (8 B) + E first rows (4 B).
+constexpr int kField = 21;  // bits per packed counter
+__global__ __launch_bounds__(kScanThreads) void group_small_kernel(GroupArgs a) {
+  extern __shared__ unsigned long long lmask[];
+  int32_t* lbase = reinterpret_cast<int32_t*>(lmask + a.E);
+  __shared__ int32_t lids[kScanThreads];
+  const int tid = threadIdx.x, E = a.E, k = a.k;
+  const int entries = (int)a.T * k;
+  const int my = tid < entries ? a.ids[tid] : -1;
+  permute_chunk_rows(a.x, a.x_perm, a.T, a.D, 0);
+  for (int i = tid; i < E; i += kScanThreads) lmask[i] = 0ull;
+  lids[tid] = my;
+  __syncthreads();
+  // skip ids outside [0, E) and repeats of an earlier slot of the same token
+  int e = -1;
+  if (tid < entries && my >= 0 && my < E) {
+    const int t = tid / k, j = tid - t * k;
+    bool first = true;
+    for (int jj = 0; jj < j; ++jj) first = first && lids[t * k + jj] != my;
+    if (first) e = my;
+  }
+  if (e >= 0) atomicOr(&lmask[e], 1ull << (tid / k));
+  __syncthreads();
+
+  const int rpt0 = a.rows_per_tile[0], rpt1 = a.rows_per_tile[1];
+  const int e0 = tid * kMaxExpertsPerScanThread;
+  uint64_t mine = 0;
+  for (int i = 0; i < kMaxExpertsPerScanThread; ++i) {
+    const int ex = e0 + i;
+    if (ex >= E) break;
+    const uint64_t cnt = (uint64_t)__popcll(lmask[ex]);
+    mine += cnt | ((cnt + rpt0 - 1) / rpt0) << kField | ((cnt + rpt1 - 1) / rpt1) << (2 * kField);
+  }
+  uint64_t total;
+  const uint64_t off = block_exclusive_scan_u64(mine, &total);
+  constexpr uint64_t kMask = (1ull << kField) - 1;
+  int row_off = (int)(off & kMask), tile_off0 = (int)((off >> kField) & kMask), tile_off1 = (int)(off >> (2 * kField));
+  for (int i = 0; i < kMaxExpertsPerScanThread; ++i) {
+    const int ex = e0 + i;
+    if (ex >= E) break;
+    const int cnt = __popcll(lmask[ex]);
+    a.counts[ex] = cnt;
+    a.offsets[ex] = row_off;
+    lbase[ex] = row_off;
+    for (int r = 0; r < cnt; r += rpt0) {
+      Tile tl;
+      tl.expert = ex;
+      tl.row0 = row_off + r;
+      tl.nrows = cnt - r < rpt0 ? cnt - r : rpt0;
+      tl.pad = 0;
+      a.tiles[0][tile_off0++] = tl;
+    }
+    for (int r = 0; r < cnt; r += rpt1) {
+      Tile tl;
+      tl.expert = ex;
+      tl.row0 = row_off + r;
+      tl.nrows = cnt - r < rpt1 ? cnt - r : rpt1;
+      tl.pad = 0;
+      a.tiles[1][tile_off1++] = tl;
+    }
+    row_off += cnt;
+  }
+  if (tid == 0) {
+    a.offsets[E] = (int)(total & kMask);
+    a.tile_count[0] = (int)((total >> kField) & kMask);
+    a.tile_count[1] = (int)(total >> (2 * kField));
+  }
+  __syncthreads();
+  if (tid < entries) {
+    const int t = tid / k;
+    int32_t row = -1;
+    if (e >= 0) {
+      row = lbase[e] + __popcll(lmask[e] & ((1ull << t) - 1ull));
+      a.row_tok[row] = t;
+    }
+    a.slot_row[tid] = row;
+  }
+}
+
 }  // namespace
 
 hipError_t launch_group(const GroupArgs& a, hipStream_t s) {
@@ -326,7 +435,10 @@ hipError_t launch_group(const GroupArgs& a, hipStream_t s) {
   const size_t fused_lds = (size_t)a.E * (sizeof(unsigned long long) + sizeof(int32_t));
   // leave room for the scan's static LDS (64 ints) under the 64 KB limit
   if (n_chunks == 1 && fused_lds <= 60 * 1024) {
-    hipLaunchKernelGGL(group_fused_kernel, dim3(1), dim3(kScanThreads), fused_lds, s, a);
+    if (a.T * a.k <= kScanThreads)
+      hipLaunchKernelGGL(group_small_kernel, dim3(1), dim3(kScanThreads), fused_lds, s, a);
+    else
+      hipLaunchKernelGGL(group_fused_kernel, dim3(1), dim3(kScanThreads), fused_lds, s, a);
     return hipGetLastError();
   }
   const size_t mask_lds = (size_t)a.E * sizeof(unsigned long long);

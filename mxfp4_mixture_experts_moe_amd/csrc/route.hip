@@ -6,13 +6,14 @@
 // that the selected ids are reproducible bit for bit; ties go to the lower
 // expert index; NaN scores rank last.
 //
-// Each wave first writes the E scores of its token to LDS (when they fit),
-// then runs k selection rounds.  Round r picks, among the experts that rank
-// strictly after the one picked in round r-1, the best one: every lane scans
-// its strided share of experts, then a 6-step butterfly reduces the 64
-// candidates.  No "already taken" flags are needed, so nothing limits E; when
-// E scores do not fit in LDS the scores are recomputed from the logits each
-// round instead.
+// Up to 1024 experts (16 per lane) the scores live in registers: lane l owns
+// experts l, l + 64, l + 128, ..., sorted once by a bitonic network, and its
+// best remaining one is its "head".  Each of the k rounds reduces the 64 heads
+// to the wave's best (four DPP exchanges inside each 16-lane row, two row
+// swaps across rows); only the lane that owned the winner moves to its next
+// expert.  Larger E falls back to a kernel that writes the scores to LDS (or
+// recomputes them) and, in round r, picks the best expert ranking strictly
+// after round r-1's pick; it needs no "taken" flags, so nothing limits E.
 #include "k3moe_internal.h"
 
 #include <math.h>
@@ -30,6 +31,159 @@ __device__ __forceinline__ double route_score(float z, float b) {
 // (sa, ea) ranks before (sb, eb): higher score, or equal score and lower index.
 __device__ __forceinline__ bool ranks_before(double sa, int ea, double sb, int eb) {
   return sa > sb || (sa == sb && ea < eb);
+}
+
+// (s, e) of the lane DPP control kCtrl names (within a row of 16 lanes).
+template <int kCtrl>
+__device__ __forceinline__ void dpp_pair(double s, int e, double& os, int& oe) {
+  const uint64_t b = __double_as_longlong(s);
+  const uint32_t lo = __builtin_amdgcn_mov_dpp((int)(uint32_t)b, kCtrl, 0xF, 0xF, false);
+  const uint32_t hi = __builtin_amdgcn_mov_dpp((int)(uint32_t)(b >> 32), kCtrl, 0xF, 0xF, false);
+  os = __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+  oe = __builtin_amdgcn_mov_dpp(e, kCtrl, 0xF, 0xF, false);
+}
+
+// Value of lane ^ 16 (kRows = 16) or lane ^ 32 (kRows = 32): the gfx950 row
+// swaps exchange the odd 16- (32-) lane rows of their first operand with the
+// even rows of their second; with both operands equal, an even row finds its
+// partner's value in the second result and an odd row in the first.
+template <int kRows>
+__device__ __forceinline__ uint32_t swap_rows(uint32_t v, int lane) {
+  if (kRows == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+    return (lane & 16) ? r[0] : r[1];
+  } else {
+    const auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+    return (lane & 32) ? r[0] : r[1];
+  }
+}
+template <int kRows>
+__device__ __forceinline__ void swap_pair(double s, int e, int lane, double& os, int& oe) {
+  const uint64_t b = __double_as_longlong(s);
+  const uint32_t lo = swap_rows<kRows>((uint32_t)b, lane);
+  const uint32_t hi = swap_rows<kRows>((uint32_t)(b >> 32), lane);
+  os = __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+  oe = (int)swap_rows<kRows>((uint32_t)e, lane);
+}
+
+// Wave-wide best (s, e) under ranks_before, in every lane: inside each
+// 16-lane row, exchanges with lane ^ 1 and ^ 2 (quad permutes) and with the
+// mirrored lane of the 8-lane half and of the row (DPP); then with the other
+// rows (lane ^ 16, lane ^ 32).
+__device__ __forceinline__ void wave_best(double& bs, int& be, int lane) {
+  double os;
+  int oe;
+#define K3_TAKE                       \
+  if (ranks_before(os, oe, bs, be)) { \
+    bs = os;                          \
+    be = oe;                          \
+  }
+  dpp_pair<0xB1>(bs, be, os, oe);  // quad_perm [1,0,3,2]
+  K3_TAKE
+  dpp_pair<0x4E>(bs, be, os, oe);  // quad_perm [2,3,0,1]
+  K3_TAKE
+  dpp_pair<0x141>(bs, be, os, oe);  // row_half_mirror
+  K3_TAKE
+  dpp_pair<0x140>(bs, be, os, oe);  // row_mirror
+  K3_TAKE
+  swap_pair<16>(bs, be, lane, os, oe);
+  K3_TAKE
+  swap_pair<32>(bs, be, lane, os, oe);
+  K3_TAKE
+#undef K3_TAKE
+}
+
+// Sort N (s, e) pairs held in registers so that x[0] ranks first (bitonic
+// network; N is a power of two, every index compile-time).
+template <int N>
+__device__ __forceinline__ void sort_desc(double (&sc)[N], int (&ix)[N]) {
+#pragma unroll
+  for (int kk = 2; kk <= N; kk <<= 1)
+#pragma unroll
+    for (int j = kk >> 1; j > 0; j >>= 1)
+#pragma unroll
+      for (int i = 0; i < N; ++i) {
+        const int l = i ^ j;
+        if (l > i) {
+          // first half of each kk-block ends up ranked first, second half last
+          const bool first = (i & kk) == 0;
+          const bool swap = first ? ranks_before(sc[l], ix[l], sc[i], ix[i]) : ranks_before(sc[i], ix[i], sc[l], ix[l]);
+          if (swap) {
+            const double ts = sc[i];
+            sc[i] = sc[l];
+            sc[l] = ts;
+            const int te = ix[i];
+            ix[i] = ix[l];
+            ix[l] = te;
+          }
+        }
+      }
+}
+
+// Register-resident router: NPER experts per lane (E <= 64 * NPER).  Each lane
+// sorts its experts once; a round takes the wave's best head and the lane that
+// owned it moves to its next expert.
+template <int NPER>
+__global__ __launch_bounds__(256) void route_topk_reg_kernel(const float* __restrict__ z, const float* __restrict__ bias,
+                                                              int64_t T, int E, int k, int normalize, float route_scale,
+                                                              int32_t* __restrict__ ids, float* __restrict__ w) {
+  const int lane = threadIdx.x & (kWaveSize - 1);
+  const int64_t t = (int64_t)blockIdx.x * (blockDim.x / kWaveSize) + threadIdx.x / kWaveSize;
+  if (t >= T) return;  // whole wave leaves; the kernel has no block-level barrier
+  const float* zt = z + t * (int64_t)E;
+
+  // all loads first (indices clamped into range), then the scores
+  float zv[NPER], bv[NPER];
+#pragma unroll
+  for (int j = 0; j < NPER; ++j) zv[j] = zt[min(lane + kWaveSize * j, E - 1)];
+  if (bias) {
+#pragma unroll
+    for (int j = 0; j < NPER; ++j) bv[j] = bias[min(lane + kWaveSize * j, E - 1)];
+  } else {
+#pragma unroll
+    for (int j = 0; j < NPER; ++j) bv[j] = 0.0f;
+  }
+  double sc[NPER];
+  int ix[NPER];
+#pragma unroll
+  for (int j = 0; j < NPER; ++j) {
+    const int e = lane + kWaveSize * j;
+    // experts past E carry index INT_MAX, so they rank after every real expert
+    sc[j] = e < E ? route_score(zv[j], bv[j]) : -INFINITY;
+    ix[j] = e < E ? e : INT_MAX;
+  }
+  sort_desc<NPER>(sc, ix);
+
+  int my_id = 0;
+  for (int r = 0; r < k; ++r) {
+    double bs = sc[0];
+    int be = ix[0];
+    wave_best(bs, be, lane);
+    if (lane == r) my_id = be;
+    if (lane == (be & (kWaveSize - 1))) {  // k <= E, so be is a real expert owned by this lane
+#pragma unroll
+      for (int j = 0; j + 1 < NPER; ++j) {
+        sc[j] = sc[j + 1];
+        ix[j] = ix[j + 1];
+      }
+      sc[NPER - 1] = -INFINITY;
+      ix[NPER - 1] = INT_MAX;
+    }
+  }
+
+  double g = 0.0;
+  if (lane < k) g = 1.0 / (1.0 + exp(-(double)zt[my_id]));
+  double sum = g;
+  if (normalize) {
+    sum = 0.0;
+    for (int r = 0; r < k; ++r) sum += __shfl(g, r, kWaveSize);
+  }
+  if (lane < k) {
+    double v = normalize ? g / sum : g;
+    v = v * (double)route_scale;
+    ids[t * k + lane] = my_id;
+    w[t * k + lane] = (float)v;
+  }
 }
 
 template <bool kScoresInLds>
@@ -101,6 +255,19 @@ __global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict
 
 hipError_t launch_route_topk(const float* z, const float* bias, int64_t T, int E, int k, int normalize,
                              float route_scale, int32_t* ids, float* w, hipStream_t s) {
+  if (E <= 16 * kWaveSize) {
+    const int64_t blocks = (T + 3) / 4;
+#define K3_ROUTE(NP)                                                                                            \
+  hipLaunchKernelGGL(route_topk_reg_kernel<NP>, dim3((unsigned)blocks), dim3(256), 0, s, z, bias, T, E, k, \
+                     normalize, route_scale, ids, w)
+    if (E <= kWaveSize) K3_ROUTE(1);
+    else if (E <= 2 * kWaveSize) K3_ROUTE(2);
+    else if (E <= 4 * kWaveSize) K3_ROUTE(4);
+    else if (E <= 8 * kWaveSize) K3_ROUTE(8);
+    else K3_ROUTE(16);
+#undef K3_ROUTE
+    return hipGetLastError();
+  }
   const size_t per_wave = (size_t)E * sizeof(double);
   constexpr size_t kLdsBudget = 64 * 1024;
   if (per_wave <= kLdsBudget) {
