@@ -10,9 +10,15 @@ several seeded routing inputs so successive steps touch different experts.
 
     python bench.py [--workload prefill|verify|decode-t8|decode-t1|tiny] [--steps K] [--warmup W]
 
-Prints one JSON line (rank 0).  The kernel timing behind "roofline" comes from
-HIP events that the library records on its own stream at the FFN's stage
-boundaries (moe_mxfp4_ffn_profiled) during the timed steps.
+Prints one JSON line (rank 0).  `value` is the wall-clock rate of K steps
+replayed from captured HIP graphs (one graph per rotated batch; --eager times
+plain launches).  The kernel timing behind "roofline" comes from HIP events
+that the library records on its own stream around the dominant stage
+(moe_mxfp4_ffn_profiled) in K eager steps run right after the timed ones; the
+stage split comes from a short eager pass with every stage boundary marked.
+`python bench.py --copy-calibration` only copies a 256 MiB buffer, the
+reference kernel whose rocprofv3 FETCH_SIZE / WRITE_SIZE readings scale the
+traffic counters.
 """
 
 from __future__ import annotations
@@ -38,25 +44,28 @@ CSRC = "mxfp4_mixture_experts_moe_amd/csrc/"
 
 def gemm_path(cfg) -> str:
     """Which grouped-GEMM kernels moe_mxfp4_ffn launches for this shape (the
-    library's own selection rule, restated for labelling the roofline)."""
+    library's own selection rule, restated for labelling the roofline):
+    "stream" (weight-streaming only), "tiled" (large-tile GEMMs for experts
+    with more than 4 rows, weight-streaming for the others) or "small"."""
     entries = cfg.T * cfg.k
-    active = min(entries, cfg.E)
     fits = entries * max(cfg.I, cfg.D) * 2 < (1 << 31)
-    if cfg.D % 512 == 0 and cfg.I % 512 == 0 and fits and entries // active >= 48:
-        return "big"
-    if cfg.D % 512 == 0 and cfg.I % 512 == 0 and entries <= 4 * active:
-        return "stream"
+    if cfg.D % 512 == 0 and cfg.I % 512 == 0 and fits:
+        return "stream" if cfg.T <= 4 else "tiled"
     return "small"
 
 
 def kernel_info(stage: str, path: str):
-    """(kernel name as rocprofv3 reports it, source file) of a stage."""
-    gemm = {"big": ("ffn_big_kernel<{}>", "ffn_big.hip"), "stream": ("ffn_stream_kernel<{}>", "ffn_stream.hip"),
-            "small": ("ffn_gemm_kernel<NT, {}, ...>", "ffn.hip")}[path]
+    """(kernel name(s) as rocprofv3 reports them, source files) of a stage."""
     if stage in ("gate_up", "down"):
-        return gemm[0].format("true" if stage == "gate_up" else "false"), CSRC + gemm[1]
-    return {"route": ("route_topk_kernel", CSRC + "route.hip"), "group": ("group_*_kernel", CSRC + "group.hip"),
-            "combine": ("combine_kernel", CSRC + "ffn.hip")}[stage]
+        flag = "true" if stage == "gate_up" else "false"
+        big, stream = f"ffn_big_kernel<{flag}>", f"ffn_stream_kernel<{flag}>"
+        if path == "stream":
+            return stream, [CSRC + "ffn_stream.hip"]
+        if path == "tiled":
+            return f"{big} + {stream}", [CSRC + "ffn_big.hip", CSRC + "ffn_stream.hip"]
+        return f"ffn_gemm_kernel<NT, {flag}, ...>", [CSRC + "ffn.hip"]
+    return {"route": ("route_topk_*kernel", [CSRC + "route.hip"]), "group": ("group_*_kernel", [CSRC + "group.hip"]),
+            "combine": ("combine_kernel", [CSRC + "ffn.hip"])}[stage]
 
 
 def parse_args():
@@ -69,15 +78,21 @@ def parse_args():
     ap.add_argument("--cpu-baseline", dest="cpu_baseline", action="store_true", default=True)
     ap.add_argument("--no-cpu-baseline", dest="cpu_baseline", action="store_false")
     ap.add_argument("--cpu-sample-tokens", type=int, default=0, help="tokens the oracle evaluates (0: auto)")
+    ap.add_argument("--eager", action="store_true", help="time eager launches instead of graph replays")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only copy a 256 MiB buffer 3 times (reference kernel for HBM traffic counters)")
     return ap.parse_args()
 
 
-def source_sha(rel: str) -> str:
-    with open(os.path.join(ROOT, rel), "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+def source_sha(rels) -> str:
+    h = hashlib.sha256()
+    for rel in rels:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
-def stored_traffic(stage: str, workload: str, source: str):
+def stored_traffic(stage: str, workload: str, sources):
     """HBM bytes per launch from a committed rocprofv3 --pmc summary, if it was taken
     on the current kernel source (else None)."""
     path = os.path.join(TRAFFIC_DIR, f"{stage}_{workload}_traffic.txt")
@@ -88,7 +103,7 @@ def stored_traffic(stage: str, workload: str, source: str):
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             kv[k.strip()] = v.strip()
-    if kv.get("source_sha") != source_sha(source):
+    if kv.get("source_sha") != source_sha(sources):
         return None
     try:
         return float(kv["hbm_bytes_per_launch"])
@@ -163,6 +178,16 @@ def main():
     import numpy as np
     import torch
 
+    if args.copy_calibration:
+        n = 1 << 28
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(f"copied {n} bytes 3 times", flush=True)
+        return
+
     import moe_inputs
     import mxfp4_mixture_experts_moe_amd as k3
     from moe_inputs.device import upload_batch, upload_experts
@@ -187,35 +212,78 @@ def main():
     setup_s = time.perf_counter() - t_setup
 
     steps, warmup = args.steps, args.warmup
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(steps)]
+    stages = ["route", "group", "gate_up", "down", "combine"]
 
     def step(i, events=None):
         j = i % rotate
         _, x, z, b = batches[j]
-        if events is not None:
+        if events is not None and events[0] is not None:
             events[0].record()
         k3.moe_route_topk(z, b, cfg.k, ids=ids[j], weights=wts[j])
         k3.moe_mxfp4_ffn(x, ids[j], wts[j], dev.w1, dev.w3, dev.w2, out=out, workspace=ws,
                          stage_events=None if events is None else events[1:])
 
+    def busy_head():
+        # keep the GPU busy while the host enqueues the measured steps, so no
+        # step waits for the host (matters for decode-sized steps)
+        torch.cuda._sleep(int(2e7))
+
     for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
+
+    # 1. stage split (eager, all stage boundaries marked) -> dominant stage
+    n_split = max(rotate, min(steps, 16))
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(n_split)]
+    busy_head()
+    for i in range(n_split):
+        step(warmup + i, ev[i])
+    torch.cuda.synchronize()
+    stage_ms = {s: float(np.mean([ev[i][n].elapsed_time(ev[i][n + 1]) for i in range(n_split)]))
+                for n, s in enumerate(stages)}
+
+    # 2. the timed steps: one captured graph per rotated batch, replayed
+    graphs = []
+    if not args.eager:
+        for j in range(rotate):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                step(j)
+            graphs.append(g)
+        for g in graphs:
+            g.replay()
+        torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
-        step(warmup + i, ev[i])
+        if graphs:
+            graphs[(warmup + i) % rotate].replay()
+        else:
+            step(warmup + i)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
 
-    stages = ["route", "group", "gate_up", "down", "combine"]
-    stage_ms = {s: float(np.mean([ev[i][n].elapsed_time(ev[i][n + 1]) for i in range(steps)]))
-                for n, s in enumerate(stages)}
+    # 3. eager steps with the dominant stage bracketed by two events on the
+    #    library's stream (its per-launch duration for the roofline), and the
+    #    eager step time from two events around all of them
     dom = max(stages, key=lambda s: stage_ms[s])
+    n = stages.index(dom)
+    dev_ev = [[torch.cuda.Event(enable_timing=True) if m in (n, n + 1) else None for m in range(6)]
+              for _ in range(steps)]
+    e_start, e_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    busy_head()
+    e_start.record()
+    for i in range(steps):
+        step(warmup + i, dev_ev[i])
+    e_end.record()
+    torch.cuda.synchronize()
+    dom_ms = float(np.mean([dev_ev[i][n].elapsed_time(dev_ev[i][n + 1]) for i in range(steps)]))
+    eager_ms = e_start.elapsed_time(e_end) / steps
+
     rows = cfg.T * cfg.k
     act_steps = [n_active[(warmup + i) % rotate] for i in range(steps)]
     flops, byts = stage_work(dom, cfg, rows, float(np.mean(act_steps)))
     bound = "mfma" if flops / max(byts, 1.0) > RIDGE else "hbm"
-    dur_s = stage_ms[dom] * 1e-3
+    dur_s = dom_ms * 1e-3
     if bound == "mfma":
         achieved, peak, unit = flops / dur_s / 1e12, PEAK_BF16_TFLOPS, "TFLOP/s"
     else:
@@ -260,8 +328,11 @@ def main():
             "traffic": traffic,
             "algorithmic_flops_per_launch": flops,
             "algorithmic_bytes_per_launch": byts,
-            "avg_launch_ms": stage_ms[dom],
+            "avg_launch_ms": dom_ms,
         },
+        "timing": ("graph replay of the step (route + FFN), one captured graph per rotated batch"
+                   if graphs else "eager launches"),
+        "eager_ms_per_step": eager_ms,
         "step_weight_GBps": weight_bytes / step_s / 1e9,
         "step_mfma_frac": cfg.T * 2 * cfg.k * 3 * cfg.D * cfg.I / step_s / (PEAK_BF16_TFLOPS * 1e12),
         "stages_ms": stage_ms,

@@ -21,9 +21,8 @@ FfnWorkspace ffn_workspace_layout(int64_t T, int32_t D, int32_t I, int32_t E, in
   };
   w.counts = take(sizeof(int32_t) * (size_t)E);
   w.offsets = take(sizeof(int32_t) * (size_t)(E + 1));
-  w.tile_count = take(2 * sizeof(int32_t));
-  w.tiles = take(sizeof(Tile) * (size_t)(w.max_tiles > 0 ? w.max_tiles : 1));
-  w.tiles_b = take(sizeof(Tile) * (size_t)(w.max_tiles > 0 ? w.max_tiles : 1));
+  w.tile_count = take(kTileLists * sizeof(int32_t));
+  for (int L = 0; L < kTileLists; ++L) w.tiles[L] = take(sizeof(Tile) * (size_t)(w.max_tiles > 0 ? w.max_tiles : 1));
   w.row_tok = take(sizeof(int32_t) * (size_t)entries);
   w.slot_row = take(sizeof(int32_t) * (size_t)entries);
   w.chunk_base = take(sizeof(int32_t) * (size_t)(w.n_chunks * E));
@@ -135,18 +134,20 @@ int moe_mxfp4_ffn_profiled(const void* x_bf16, const int32_t* topk_ids, const fl
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   const int64_t entries = T * (int64_t)k;
   const int64_t active = entries < E ? entries : E;
-  // Large-tile GEMMs once experts average 48+ rows (prefill-sized batches).
-  // They address activations through 32-bit buffer offsets, so x and h must
-  // stay below 2 GiB; bigger batches take the general path.
+  // GEMM kernels.  With D and I multiples of 512 (and activations below 2 GiB,
+  // as both address them through 32-bit buffer offsets) every expert is served
+  // by the kernel that suits its row count: the large-tile GEMMs for experts
+  // with more than kStreamMaxRows rows (MFMA-bound), the weight-streaming GEMMs
+  // for the others (HBM-bound).  A batch of at most kStreamMaxRows tokens
+  // cannot give an expert more rows (an id repeated within a token is
+  // skipped), so it launches only the streaming kernels.  Other shapes use
+  // the general small-tile GEMMs for every expert.
+  constexpr int kStreamMaxRows = 4;
   const bool offsets_fit = entries * (int64_t)(I > D ? I : D) * 2 < ((int64_t)1 << 31);
-  const bool big = big_gemm_supported(D, I) && offsets_fit && entries / active >= 48;
-  // Weight-streaming GEMMs when experts average at most 4 rows (decode-sized
-  // batches): the product is bound by reading the active experts' weights.
-  // They also address activations through 32-bit buffer offsets.
-  const bool streaming = !big && stream_gemm_supported(D, I) && offsets_fit && entries <= 4 * active;
-  const int rpt_small = streaming ? stream_rows_per_tile() : choose_rows_per_tile(T, k, E);
-  const int rpt_gu = big ? big_rows_per_tile(true) : rpt_small;
-  const int rpt_dn = big ? big_rows_per_tile(false) : rpt_small;
+  const bool tiled = big_gemm_supported(D, I) && stream_gemm_supported(D, I) && offsets_fit;
+  const bool big_lists = !tiled || T > kStreamMaxRows;  // lists 0/1 may hold tiles
+  const bool stream_lists = tiled;                      // lists 2/3 may hold tiles
+  const int rpt_small = choose_rows_per_tile(T, k, E);
 
   GroupArgs g{};
   g.ids = topk_ids;
@@ -155,13 +156,15 @@ int moe_mxfp4_ffn_profiled(const void* x_bf16, const int32_t* topk_ids, const fl
   g.D = D;
   g.E = E;
   g.k = k;
-  g.rows_per_tile[0] = rpt_gu;
-  g.rows_per_tile[1] = rpt_dn;
+  g.rows_per_tile[0] = tiled ? big_rows_per_tile(true) : rpt_small;
+  g.rows_per_tile[1] = tiled ? big_rows_per_tile(false) : rpt_small;
+  g.rows_per_tile[2] = stream_rows_per_tile();
+  g.rows_per_tile[3] = stream_rows_per_tile();
+  g.split_rows = tiled ? kStreamMaxRows : 0;
   g.counts = reinterpret_cast<int32_t*>(ws + L.counts);
   g.offsets = reinterpret_cast<int32_t*>(ws + L.offsets);
   g.tile_count = reinterpret_cast<int32_t*>(ws + L.tile_count);
-  g.tiles[0] = reinterpret_cast<Tile*>(ws + L.tiles);
-  g.tiles[1] = reinterpret_cast<Tile*>(ws + L.tiles_b);
+  for (int l = 0; l < kTileLists; ++l) g.tiles[l] = reinterpret_cast<Tile*>(ws + L.tiles[l]);
   g.row_tok = reinterpret_cast<int32_t*>(ws + L.row_tok);
   g.slot_row = reinterpret_cast<int32_t*>(ws + L.slot_row);
   g.chunk_base = reinterpret_cast<int32_t*>(ws + L.chunk_base);
@@ -175,23 +178,20 @@ int moe_mxfp4_ffn_profiled(const void* x_bf16, const int32_t* topk_ids, const fl
   hipError_t err = launch_group(g, s);
   if (err != hipSuccess || !mark(1)) return K3MOE_ERR_DEVICE;
 
-  // upper bound of each tile list's length: sum over experts of ceil(n_e / rpt)
+  // Upper bounds of the list lengths (sum over experts of ceil(n_e / rpt)):
+  // an expert in lists 0/1 has more than split_rows rows.
+  const int64_t big_experts = tiled ? (entries / (kStreamMaxRows + 1) < active ? entries / (kStreamMaxRows + 1) : active)
+                                    : active;
   GemmArgs gu{};
   gu.act = g.x_perm;
   gu.act_rows = T;
   gu.row_tok = g.row_tok;
   gu.wa = w1;
   gu.wb = w3;
-  gu.tiles = g.tiles[0];
-  gu.tile_count = g.tile_count;
-  gu.max_tiles = entries / rpt_gu + active;
   gu.K = D;
   gu.N = I;
   gu.out = ws + L.h;
   gu.out_lo = ws + L.h_lo;
-  err = big ? launch_big_gate_up(gu, s) : streaming ? launch_stream_gate_up(gu, s) : launch_gate_up(gu, rpt_gu, s);
-  if (err != hipSuccess || !mark(2)) return K3MOE_ERR_DEVICE;
-
   GemmArgs dn{};
   dn.act = reinterpret_cast<const uint16_t*>(ws + L.h);
   dn.act_lo = reinterpret_cast<const uint16_t*>(ws + L.h_lo);
@@ -199,14 +199,43 @@ int moe_mxfp4_ffn_profiled(const void* x_bf16, const int32_t* topk_ids, const fl
   dn.row_tok = nullptr;
   dn.wa = w2;
   dn.wb = nullptr;
-  dn.tiles = g.tiles[1];
-  dn.tile_count = g.tile_count + 1;
-  dn.max_tiles = entries / rpt_dn + active;
   dn.K = I;
   dn.N = D;
   dn.out = ws + L.y;
-  err = big ? launch_big_down(dn, s) : streaming ? launch_stream_down(dn, s) : launch_down(dn, rpt_dn, s);
-  if (err != hipSuccess || !mark(3)) return K3MOE_ERR_DEVICE;
+
+  // gate/up
+  if (big_lists) {
+    gu.tiles = g.tiles[0];
+    gu.tile_count = g.tile_count;
+    gu.max_tiles = entries / g.rows_per_tile[0] + big_experts;
+    err = tiled ? launch_big_gate_up(gu, s) : launch_gate_up(gu, rpt_small, s);
+    if (err != hipSuccess) return K3MOE_ERR_DEVICE;
+  }
+  if (stream_lists) {
+    gu.tiles = g.tiles[2];
+    gu.tile_count = g.tile_count + 2;
+    gu.max_tiles = active;  // at most kStreamMaxRows rows each: one tile per expert
+    err = launch_stream_gate_up(gu, s);
+    if (err != hipSuccess) return K3MOE_ERR_DEVICE;
+  }
+  if (!mark(2)) return K3MOE_ERR_DEVICE;
+
+  // down
+  if (big_lists) {
+    dn.tiles = g.tiles[1];
+    dn.tile_count = g.tile_count + 1;
+    dn.max_tiles = entries / g.rows_per_tile[1] + big_experts;
+    err = tiled ? launch_big_down(dn, s) : launch_down(dn, rpt_small, s);
+    if (err != hipSuccess) return K3MOE_ERR_DEVICE;
+  }
+  if (stream_lists) {
+    dn.tiles = g.tiles[3];
+    dn.tile_count = g.tile_count + 3;
+    dn.max_tiles = active;
+    err = launch_stream_down(dn, s);
+    if (err != hipSuccess) return K3MOE_ERR_DEVICE;
+  }
+  if (!mark(3)) return K3MOE_ERR_DEVICE;
 
   err = launch_combine(reinterpret_cast<const float*>(ws + L.y), g.slot_row, topk_w, T, D, k, out, s);
   if (err != hipSuccess || !mark(4)) return K3MOE_ERR_DEVICE;

@@ -27,6 +27,9 @@
 // down:    kF = 512 features of w2, kN = 64 tokens; wave tile 64 x 64; the B
 //          operand is h_hi and h_lo (two MFMAs per decoded weight operand).
 //
+// Token groups of 16 with no row of the tile are skipped (no activation loads,
+// no MFMAs), so a tile of few rows costs about its weight traffic only.
+//
 // Workgroups are numbered so that those the hardware sends to the same XCD
 // (consecutive ids round-robin over 8 XCDs) take a contiguous range of the
 // logical work order, which keeps the tiles that share weights (gate/up) or
@@ -141,7 +144,7 @@ __global__ __launch_bounds__(kThreads) void ffn_big_kernel(GemmArgs a) {
   const int rho = lane & 15, g = lane >> 4;
 
   if (tid < C::kN) {
-    const int m = tid < tile.nrows ? tid : 0;  // padding tokens repeat the first row
+    const int m = tid < tile.nrows ? tid : 0;  // rows past the tile repeat the first row
     const int row = tile.row0 + m;
     tok_src[tid] = kGateUp ? a.row_tok[row] : row;
   }
@@ -191,16 +194,23 @@ __global__ __launch_bounds__(kThreads) void ffn_big_kernel(GemmArgs a) {
     aoffs[j] = ((uint32_t)tok_src[t] * (uint32_t)K + 8 * ch) * 2;  // bytes
   }
 
+  // Token groups of 16 that hold rows of this tile (the others are skipped:
+  // no activation loads, no MFMAs; their output columns are never stored).
+  const int ntg = __builtin_amdgcn_readfirstlane((tile.nrows + 15) >> 4);
+  const bool aload = 16 * wave - asrc * C::kN < 16 * ntg;  // this wave's activation rows are live
+
   auto issue = [&](int stage, int buf) {
     uint32_t* wl = &lds[buf][0] + 64 * wave * kWRowDw;
     uint32_t* al = &lds[buf][kWDw] + 272 * 4 * wave;
     const int wso = 64 * stage + 16 * (stage >> 2);  // 16-byte aligned start of the step's 68 bytes
 #pragma unroll
     for (int j = 0; j < kWRowChunks; ++j) __builtin_amdgcn_raw_ptr_buffer_load_lds(wrsrc, wl + 256 * j, 16, woffs[j], wso, 0, 0);
-    const int aso = stage * kKStep * 2;
+    if (aload) {
+      const int aso = stage * kKStep * 2;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) __builtin_amdgcn_raw_ptr_buffer_load_lds(arsrc, al + 256 * j, 16, aoffs[j], aso, 0, 0);
-    if (lane < 16) __builtin_amdgcn_raw_ptr_buffer_load_lds(arsrc, al + 256 * 4, 16, aoffs[4], aso, 0, 0);
+      for (int j = 0; j < 4; ++j) __builtin_amdgcn_raw_ptr_buffer_load_lds(arsrc, al + 256 * j, 16, aoffs[j], aso, 0, 0);
+      if (lane < 16) __builtin_amdgcn_raw_ptr_buffer_load_lds(arsrc, al + 256 * 4, 16, aoffs[4], aso, 0, 0);
+    }
   };
 
   // LDS dword of chunk g of the window of MFMA row rho of row group rg (block g
@@ -226,8 +236,10 @@ __global__ __launch_bounds__(kThreads) void ffn_big_kernel(GemmArgs a) {
   const int nstages = K / kKStep;
 
   // One K step from LDS buffer `buf` whose weight window starts at phase PH.
-  auto run_stage = [&](auto ph_tag, int s) {
+  // kFull: every token group of the tile is live (the unguarded fast path)
+  auto run_stage = [&](auto ph_tag, auto full_tag, int s) {
     constexpr int PH = decltype(ph_tag)::value;
+    constexpr bool kFull = decltype(full_tag)::value;
     const int buf = PH & 1;  // s % 2 == PH % 2 because s % 4 == PH
     if (s + 1 < nstages) issue(s + 1, buf ^ 1);
     const uint32_t* wl = &lds[buf][0];
@@ -263,11 +275,13 @@ __global__ __launch_bounds__(kThreads) void ffn_big_kernel(GemmArgs a) {
         const int row = src * C::kN + tg * 16 + rho;
         return __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(al + row * kARowDw + 4 * (4 * g + i)));
       };
+      const int nlive = kFull ? kB : ntg * C::kSrc;  // operands of live token groups
       bf16x8_t bnext = bread(0);
 #pragma unroll
       for (int n = 0; n < kB; ++n) {
+        if (!kFull && n >= nlive) break;
         const bf16x8_t bop = bnext;
-        if (n + 1 < kB) bnext = bread(n + 1);
+        if (n + 1 < kB && (kFull || n + 1 < nlive)) bnext = bread(n + 1);
         const int tg = n / C::kSrc;
 #pragma unroll
         for (int mi = 0; mi < C::kMats; ++mi)
@@ -284,12 +298,18 @@ __global__ __launch_bounds__(kThreads) void ffn_big_kernel(GemmArgs a) {
   issue(0, 0);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
-  for (int s = 0; s < nstages; s += 4) {
-    run_stage(std::integral_constant<int, 0>{}, s);
-    if (s + 1 < nstages) run_stage(std::integral_constant<int, 1>{}, s + 1);
-    if (s + 2 < nstages) run_stage(std::integral_constant<int, 2>{}, s + 2);
-    if (s + 3 < nstages) run_stage(std::integral_constant<int, 3>{}, s + 3);
-  }
+  auto k_loop = [&](auto full_tag) {
+    for (int s = 0; s < nstages; s += 4) {
+      run_stage(std::integral_constant<int, 0>{}, full_tag, s);
+      if (s + 1 < nstages) run_stage(std::integral_constant<int, 1>{}, full_tag, s + 1);
+      if (s + 2 < nstages) run_stage(std::integral_constant<int, 2>{}, full_tag, s + 2);
+      if (s + 3 < nstages) run_stage(std::integral_constant<int, 3>{}, full_tag, s + 3);
+    }
+  };
+  if (ntg == C::kTG)
+    k_loop(std::true_type{});
+  else
+    k_loop(std::false_type{});
 
   // ---- epilogue ----
 #pragma unroll

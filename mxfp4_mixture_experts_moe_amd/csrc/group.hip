@@ -12,9 +12,11 @@
 // result does not depend on thread order).  A single-workgroup scan turns the
 // per-chunk popcounts into per-expert offsets and per-(chunk, expert) bases;
 // an entry's grouped row is then base + popcount(bitmap & tokens before it).
-// Small batches (one chunk) run all phases in one launch.  Tile counts and
-// row offsets are packed in 21-bit fields when one scan serves all three, so
-// that path needs at most 2^21 - 1 rows (it serves at most 1024 entries).
+// Small batches (one chunk) run all phases in one launch.
+//
+// Each expert's rows are cut into GEMM tiles in two lists (gate/up, down),
+// chosen by the expert's row count: the large-tile lists for experts with
+// more than split_rows rows, the weight-streaming lists for the others.
 #include "k3moe_internal.h"
 
 namespace k3moe {
@@ -48,114 +50,125 @@ __device__ __forceinline__ void build_masks(const int32_t* __restrict__ ids, int
   __syncthreads();
 }
 
-// Block-wide exclusive scan of one int per thread (blockDim.x == 1024).
-__device__ __forceinline__ int block_exclusive_scan(int v, int* total_out) {
-  __shared__ int wave_tot[kScanThreads / 64];
+// Block-wide exclusive scan of N ints per thread (blockDim.x == 1024): v[i]
+// becomes the sum of v[i] over lower threads, total[i] the sum over all.
+template <int N>
+__device__ __forceinline__ void block_exclusive_scan_n(int (&v)[N], int (&total)[N]) {
+  __shared__ int wave_tot[kScanThreads / 64][N];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int incl = v;
+  int incl[N];
 #pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const int o = __shfl_up(incl, d, 64);
-    if (lane >= d) incl += o;
-  }
-  if (lane == 63) wave_tot[wave] = incl;
+  for (int i = 0; i < N; ++i) incl[i] = v[i];
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1)
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const int o = __shfl_up(incl[i], d, 64);
+      if (lane >= d) incl[i] += o;
+    }
+  if (lane == 63)
+#pragma unroll
+    for (int i = 0; i < N; ++i) wave_tot[wave][i] = incl[i];
   __syncthreads();
-  int before = 0, total = 0;
-  for (int w = 0; w < kScanThreads / 64; ++w) {
-    const int tw = wave_tot[w];
-    if (w < wave) before += tw;
-    total += tw;
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    int before = 0, tot = 0;
+    for (int w = 0; w < kScanThreads / 64; ++w) {
+      const int tw = wave_tot[w][i];
+      if (w < wave) before += tw;
+      tot += tw;
+    }
+    v[i] = before + incl[i] - v[i];
+    total[i] = tot;
   }
   __syncthreads();  // wave_tot may be reused by the next call
-  *total_out = total;
-  return before + incl - v;
 }
 
-// Block-wide exclusive scan of one uint64 per thread (blockDim.x == 1024);
-// used with three counters packed in 21-bit fields, so one scan serves all.
-__device__ __forceinline__ uint64_t block_exclusive_scan_u64(uint64_t v, uint64_t* total_out) {
-  __shared__ uint64_t wave_tot64[kScanThreads / 64];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  uint64_t incl = v;
+// Tile lists.  An expert with more than split_rows rows goes to lists 0
+// (gate/up) and 1 (down), one with fewer to lists 2 and 3; list L cuts the
+// expert's rows into tiles of rows_per_tile[L].
+struct TileSpec {
+  int rpt[kTileLists];
+  int split;
+};
+__device__ __forceinline__ TileSpec tile_spec(const GroupArgs& a) {
+  TileSpec t;
 #pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const uint64_t o = __shfl_up(incl, d, 64);
-    if (lane >= d) incl += o;
-  }
-  if (lane == 63) wave_tot64[wave] = incl;
-  __syncthreads();
-  uint64_t before = 0, total = 0;
+  for (int L = 0; L < kTileLists; ++L) t.rpt[L] = a.rows_per_tile[L];
+  t.split = a.split_rows;
+  return t;
+}
+__device__ __forceinline__ int tiles_in_list(const TileSpec& t, int cnt, int L) {
+  const bool first_pair = cnt > t.split;
+  if (cnt == 0 || (L < 2) != first_pair) return 0;
+  return (cnt + t.rpt[L] - 1) / t.rpt[L];
+}
+// v[0] += cnt, v[1 + L] += tiles of list L.
+__device__ __forceinline__ void add_expert(const TileSpec& t, int cnt, int (&v)[1 + kTileLists]) {
+  v[0] += cnt;
 #pragma unroll
-  for (int w = 0; w < kScanThreads / 64; ++w) {
-    const uint64_t tw = wave_tot64[w];
-    if (w < wave) before += tw;
-    total += tw;
+  for (int L = 0; L < kTileLists; ++L) v[1 + L] += tiles_in_list(t, cnt, L);
+}
+// Writes the tiles of expert e (rows row0 .. row0 + cnt) and advances the
+// per-list write positions in off[1 + L].
+__device__ __forceinline__ void emit_tiles(const GroupArgs& a, const TileSpec& t, int e, int row0, int cnt,
+                                           int (&off)[1 + kTileLists]) {
+#pragma unroll
+  for (int L = 0; L < kTileLists; ++L) {
+    if (tiles_in_list(t, cnt, L) == 0) continue;
+    for (int r = 0; r < cnt; r += t.rpt[L]) {
+      Tile tl;
+      tl.expert = e;
+      tl.row0 = row0 + r;
+      tl.nrows = cnt - r < t.rpt[L] ? cnt - r : t.rpt[L];
+      tl.pad = 0;
+      a.tiles[L][off[1 + L]++] = tl;
+    }
   }
-  *total_out = total;
-  return before + incl - v;
+}
+__device__ __forceinline__ void write_totals(const GroupArgs& a, int E, const int (&total)[1 + kTileLists]) {
+  a.offsets[E] = total[0];
+#pragma unroll
+  for (int L = 0; L < kTileLists; ++L) a.tile_count[L] = total[1 + L];
 }
 
 // Phase 2 (one workgroup of 1024 threads): per-expert counts and offsets, the
-// two tile lists (one per tile height), and base[c][e] = offsets[e] + rows of e
-// in chunks before c.
+// tile lists, and base[c][e] = offsets[e] + rows of e in chunks before c.
 // masks: [n_chunks][E] (global, or LDS when n_chunks == 1); base: [n_chunks][E].
-__device__ __forceinline__ void scan_experts(const unsigned long long* masks, int64_t n_chunks, int E, int rpt0, int rpt1,
-                             int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
-                             int32_t* __restrict__ tile_count, Tile* __restrict__ tiles0, Tile* __restrict__ tiles1,
-                             int32_t* base) {
-  const int tid = threadIdx.x;
+__device__ __forceinline__ void scan_experts(const GroupArgs& a, const unsigned long long* masks, int64_t n_chunks,
+                                             int32_t* base) {
+  const int tid = threadIdx.x, E = a.E;
+  const TileSpec ts = tile_spec(a);
   const int e0 = tid * kMaxExpertsPerScanThread;
   // pass 1: this thread's row and tile totals (counts are recomputed in pass 2
   // rather than kept in a per-thread array)
-  int my_rows = 0, my_tiles0 = 0, my_tiles1 = 0;
+  int v[1 + kTileLists] = {0, 0, 0, 0, 0};
   for (int i = 0; i < kMaxExpertsPerScanThread; ++i) {
     const int e = e0 + i;
     if (e >= E) break;
     int cnt = 0;
     for (int64_t c = 0; c < n_chunks; ++c) cnt += __popcll(masks[c * E + e]);
-    my_rows += cnt;
-    my_tiles0 += (cnt + rpt0 - 1) / rpt0;
-    my_tiles1 += (cnt + rpt1 - 1) / rpt1;
+    add_expert(ts, cnt, v);
   }
-  int total_rows, total_tiles0, total_tiles1;
-  int row_off = block_exclusive_scan(my_rows, &total_rows);
-  int tile_off0 = block_exclusive_scan(my_tiles0, &total_tiles0);
-  int tile_off1 = block_exclusive_scan(my_tiles1, &total_tiles1);
+  int total[1 + kTileLists];
+  block_exclusive_scan_n(v, total);
   // pass 2: offsets, per-chunk bases and tiles of each expert
   for (int i = 0; i < kMaxExpertsPerScanThread; ++i) {
     const int e = e0 + i;
     if (e >= E) break;
-    offsets[e] = row_off;
+    const int row_off = v[0];
+    a.offsets[e] = row_off;
     int run = row_off;
     for (int64_t c = 0; c < n_chunks; ++c) {
       base[c * E + e] = run;
       run += __popcll(masks[c * E + e]);
     }
     const int cnt = run - row_off;
-    counts[e] = cnt;
-    for (int r = 0; r < cnt; r += rpt0) {
-      Tile tl;
-      tl.expert = e;
-      tl.row0 = row_off + r;
-      tl.nrows = cnt - r < rpt0 ? cnt - r : rpt0;
-      tl.pad = 0;
-      tiles0[tile_off0++] = tl;
-    }
-    for (int r = 0; r < cnt; r += rpt1) {
-      Tile tl;
-      tl.expert = e;
-      tl.row0 = row_off + r;
-      tl.nrows = cnt - r < rpt1 ? cnt - r : rpt1;
-      tl.pad = 0;
-      tiles1[tile_off1++] = tl;
-    }
-    row_off = run;
+    a.counts[e] = cnt;
+    emit_tiles(a, ts, e, row_off, cnt, v);
+    v[0] = run;
   }
-  if (tid == 0) {
-    offsets[E] = total_rows;
-    tile_count[0] = total_tiles0;
-    tile_count[1] = total_tiles1;
-  }
+  if (tid == 0) write_totals(a, E, total);
 }
 
 // Phase 3: grouped row of every entry of chunk c.
@@ -233,51 +246,27 @@ __global__ __launch_bounds__(kScanThreads) void group_scan_kernel(GroupArgs a, i
   }
   __syncthreads();
   // offsets and tiles: thread t owns experts 8t..8t+7
-  const int rpt0 = a.rows_per_tile[0], rpt1 = a.rows_per_tile[1];
+  const TileSpec ts = tile_spec(a);
   const int e0 = tid * kMaxExpertsPerScanThread;
-  int my_rows = 0, my_tiles0 = 0, my_tiles1 = 0;
+  int v[1 + kTileLists] = {0, 0, 0, 0, 0};
   for (int i = 0; i < kMaxExpertsPerScanThread; ++i) {
     const int e = e0 + i;
     if (e >= E) break;
-    const int cnt = ltot[e];
-    my_rows += cnt;
-    my_tiles0 += (cnt + rpt0 - 1) / rpt0;
-    my_tiles1 += (cnt + rpt1 - 1) / rpt1;
+    add_expert(ts, ltot[e], v);
   }
-  int total_rows, total_tiles0, total_tiles1;
-  int row_off = block_exclusive_scan(my_rows, &total_rows);
-  int tile_off0 = block_exclusive_scan(my_tiles0, &total_tiles0);
-  int tile_off1 = block_exclusive_scan(my_tiles1, &total_tiles1);
+  int total[1 + kTileLists];
+  block_exclusive_scan_n(v, total);
   for (int i = 0; i < kMaxExpertsPerScanThread; ++i) {
     const int e = e0 + i;
     if (e >= E) break;
     const int cnt = ltot[e];
     a.counts[e] = cnt;
-    a.offsets[e] = row_off;
-    for (int r = 0; r < cnt; r += rpt0) {
-      Tile tl;
-      tl.expert = e;
-      tl.row0 = row_off + r;
-      tl.nrows = cnt - r < rpt0 ? cnt - r : rpt0;
-      tl.pad = 0;
-      a.tiles[0][tile_off0++] = tl;
-    }
-    for (int r = 0; r < cnt; r += rpt1) {
-      Tile tl;
-      tl.expert = e;
-      tl.row0 = row_off + r;
-      tl.nrows = cnt - r < rpt1 ? cnt - r : rpt1;
-      tl.pad = 0;
-      a.tiles[1][tile_off1++] = tl;
-    }
-    ltot[e] = row_off;  // reuse: the expert's first grouped row
-    row_off += cnt;
+    a.offsets[e] = v[0];
+    emit_tiles(a, ts, e, v[0], cnt, v);
+    ltot[e] = v[0];  // reuse: the expert's first grouped row
+    v[0] += cnt;
   }
-  if (tid == 0) {
-    a.offsets[E] = total_rows;
-    a.tile_count[0] = total_tiles0;
-    a.tile_count[1] = total_tiles1;
-  }
+  if (tid == 0) write_totals(a, E, total);
   __syncthreads();
   // bases: expert-parallel running sums over the chunks (loads kept in flight)
   for (int e = tid; e < E; e += kScanThreads) {
@@ -338,8 +327,7 @@ __global__ __launch_bounds__(kScanThreads) void group_fused_kernel(GroupArgs a) 
   extern __shared__ unsigned long long lmask[];
   int32_t* lbase = reinterpret_cast<int32_t*>(lmask + a.E);
   build_masks(a.ids, a.T, a.k, a.E, 0, lmask);
-  scan_experts(lmask, 1, a.E, a.rows_per_tile[0], a.rows_per_tile[1], a.counts, a.offsets, a.tile_count,
-               a.tiles[0], a.tiles[1], lbase);
+  scan_experts(a, lmask, 1, lbase);
   __syncthreads();
   place_entries(a.ids, a.T, a.k, a.E, 0, lmask, lbase, a.row_tok, a.slot_row);
   permute_chunk_rows(a.x, a.x_perm, a.T, a.D, 0);
@@ -347,10 +335,9 @@ __global__ __launch_bounds__(kScanThreads) void group_fused_kernel(GroupArgs a) 
 
 // All phases for a batch of at most 64 tokens and 1024 entries (decode-sized),
 // one launch: thread i owns entry i for the whole kernel, the activation
-// re-layout is issued first (it does not depend on the ids), and one packed
-// scan yields row offsets and both tile lists.
+// re-layout is issued first (it does not depend on the ids), and one scan
+// yields row offsets and the tile lists.
 // LDS: E bitmaps (8 B) + E first rows (4 B).
-constexpr int kField = 21;  // bits per packed counter
 __global__ __launch_bounds__(kScanThreads) void group_small_kernel(GroupArgs a) {
   extern __shared__ unsigned long long lmask[];
   int32_t* lbase = reinterpret_cast<int32_t*>(lmask + a.E);
@@ -373,49 +360,27 @@ __global__ __launch_bounds__(kScanThreads) void group_small_kernel(GroupArgs a) 
   if (e >= 0) atomicOr(&lmask[e], 1ull << (tid / k));
   __syncthreads();
 
-  const int rpt0 = a.rows_per_tile[0], rpt1 = a.rows_per_tile[1];
+  const TileSpec ts = tile_spec(a);
   const int e0 = tid * kMaxExpertsPerScanThread;
-  uint64_t mine = 0;
+  int v[1 + kTileLists] = {0, 0, 0, 0, 0};
   for (int i = 0; i < kMaxExpertsPerScanThread; ++i) {
     const int ex = e0 + i;
     if (ex >= E) break;
-    const uint64_t cnt = (uint64_t)__popcll(lmask[ex]);
-    mine += cnt | ((cnt + rpt0 - 1) / rpt0) << kField | ((cnt + rpt1 - 1) / rpt1) << (2 * kField);
+    add_expert(ts, __popcll(lmask[ex]), v);
   }
-  uint64_t total;
-  const uint64_t off = block_exclusive_scan_u64(mine, &total);
-  constexpr uint64_t kMask = (1ull << kField) - 1;
-  int row_off = (int)(off & kMask), tile_off0 = (int)((off >> kField) & kMask), tile_off1 = (int)(off >> (2 * kField));
+  int total[1 + kTileLists];
+  block_exclusive_scan_n(v, total);
   for (int i = 0; i < kMaxExpertsPerScanThread; ++i) {
     const int ex = e0 + i;
     if (ex >= E) break;
     const int cnt = __popcll(lmask[ex]);
     a.counts[ex] = cnt;
-    a.offsets[ex] = row_off;
-    lbase[ex] = row_off;
-    for (int r = 0; r < cnt; r += rpt0) {
-      Tile tl;
-      tl.expert = ex;
-      tl.row0 = row_off + r;
-      tl.nrows = cnt - r < rpt0 ? cnt - r : rpt0;
-      tl.pad = 0;
-      a.tiles[0][tile_off0++] = tl;
-    }
-    for (int r = 0; r < cnt; r += rpt1) {
-      Tile tl;
-      tl.expert = ex;
-      tl.row0 = row_off + r;
-      tl.nrows = cnt - r < rpt1 ? cnt - r : rpt1;
-      tl.pad = 0;
-      a.tiles[1][tile_off1++] = tl;
-    }
-    row_off += cnt;
+    a.offsets[ex] = v[0];
+    lbase[ex] = v[0];
+    emit_tiles(a, ts, ex, v[0], cnt, v);
+    v[0] += cnt;
   }
-  if (tid == 0) {
-    a.offsets[E] = (int)(total & kMask);
-    a.tile_count[0] = (int)((total >> kField) & kMask);
-    a.tile_count[1] = (int)(total >> (2 * kField));
-  }
+  if (tid == 0) write_totals(a, E, total);
   __syncthreads();
   if (tid < entries) {
     const int t = tid / k;

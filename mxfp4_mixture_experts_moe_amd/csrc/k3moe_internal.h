@@ -19,12 +19,15 @@ struct Tile {
 
 // Tokens per grouping chunk: one 64-bit bitmap per (chunk, expert).
 constexpr int kChunkTokens = 64;
+// Tile lists: 0 / 1 = gate/up / down tiles of experts with many rows, 2 / 3 =
+// gate/up / down tiles of experts with few rows (see GroupArgs::split_rows).
+constexpr int kTileLists = 4;
 // The smallest tile height any GEMM variant uses; sizes the tile list.
 constexpr int kMinTileRows = 4;
 
 // Byte layout of the moe_mxfp4_ffn workspace (every region 256-byte aligned).
 struct FfnWorkspace {
-  size_t counts, offsets, tile_count, tiles, tiles_b, row_tok, slot_row, chunk_base, chunk_mask;
+  size_t counts, offsets, tile_count, tiles[kTileLists], row_tok, slot_row, chunk_base, chunk_mask;
   size_t x_perm, h, h_lo, y;
   size_t total;
   int64_t max_tiles, n_chunks;
@@ -45,12 +48,13 @@ struct GroupArgs {
   const uint16_t* x;  // bf16 bits [T, D]
   int64_t T;
   int D, E, k;
-  int rows_per_tile[2];  // tile heights of the two tile lists (gate/up, down)
+  int rows_per_tile[kTileLists];  // tile height of each list
+  int split_rows;                 // experts with more rows go to lists 0/1, the others to 2/3
   // workspace views
   int32_t* counts;
   int32_t* offsets;
-  int32_t* tile_count;  // [2]
-  Tile* tiles[2];
+  int32_t* tile_count;  // [kTileLists]
+  Tile* tiles[kTileLists];
   int32_t* row_tok;
   int32_t* slot_row;
   int32_t* chunk_base;

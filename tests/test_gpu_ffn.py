@@ -122,6 +122,45 @@ def test_streaming_path_hot_invalid_and_duplicate_ids(k3):
     assert np.array_equal(a.view(np.uint32), got.view(np.uint32))
 
 
+@pytest.mark.parametrize(
+    "E,k,D,I,T",
+    [(8, 2, 128, 256, 64), (64, 4, 512, 512, 8), (8, 2, 512, 512, 300)],  # small-tile, streaming, large-tile paths
+)
+def test_graph_replay_matches_eager(k3, E, k, D, I, T):
+    # route + FFN captured into a HIP graph: every replay, with other eager work
+    # in between, must reproduce the eager result bit for bit
+    print(f"[ffn] graph replay E={E} k={k} D={D} I={I} T={T}", flush=True)
+    cfg = moe_inputs.TINY.with_(E=E, k=k, D=D, I=I, T=T, config_id=43)
+    batch = moe_inputs.make_batch(cfg)
+    dev = device_experts(k3, cfg)
+    x = bf16_dev(batch.x)
+    z = torch.from_numpy(batch.z).cuda()
+    b = torch.from_numpy(batch.b).cuda()
+    ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    ws = torch.empty(k3.moe_mxfp4_ffn_workspace_size(T, D, I, E, k), dtype=torch.uint8, device="cuda")
+    out = torch.empty((T, D), dtype=torch.float32, device="cuda")
+
+    def step():
+        k3.moe_route_topk(z, b, k, ids=ids, weights=w)
+        k3.moe_mxfp4_ffn(x, ids, w, dev.w1, dev.w3, dev.w2, out=out, workspace=ws)
+
+    step()
+    torch.cuda.synchronize()
+    eager = out.cpu().clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for rep in range(3):
+        out.fill_(float("nan"))
+        ws.fill_(0xA5)  # stale workspace contents must not matter
+        g.replay()
+        torch.cuda.synchronize()
+        got = out.cpu()
+        assert torch.equal(got.view(torch.int32), eager.view(torch.int32)), f"replay {rep} differs"
+        _ = (x.float() * 2).sum().item()  # unrelated eager work between replays
+
+
 def test_identity_weights_closed_form(k3):
     """W1 = W3 = [I; 0], W2 = 2^e [I | 0]: out[t] = sum_j w_j 2^(e_j) SiLU(x) x."""
     E, D, I, T, k = 4, 128, 256, 48, 2
