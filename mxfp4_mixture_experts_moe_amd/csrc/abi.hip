@@ -158,8 +158,8 @@ int moe_mxfp4_ffn_profiled(const void* x_bf16, const int32_t* topk_ids, const fl
   g.k = k;
   g.rows_per_tile[0] = tiled ? big_rows_per_tile(true) : rpt_small;
   g.rows_per_tile[1] = tiled ? big_rows_per_tile(false) : rpt_small;
-  g.rows_per_tile[2] = stream_rows_per_tile();
-  g.rows_per_tile[3] = stream_rows_per_tile();
+  g.rows_per_tile[2] = stream_rows_per_tile(true);
+  g.rows_per_tile[3] = stream_rows_per_tile(false);
   g.split_rows = tiled ? kStreamMaxRows : 0;
   g.counts = reinterpret_cast<int32_t*>(ws + L.counts);
   g.offsets = reinterpret_cast<int32_t*>(ws + L.offsets);
@@ -214,7 +214,7 @@ int moe_mxfp4_ffn_profiled(const void* x_bf16, const int32_t* topk_ids, const fl
   if (stream_lists) {
     gu.tiles = g.tiles[2];
     gu.tile_count = g.tile_count + 2;
-    gu.max_tiles = active;  // at most kStreamMaxRows rows each: one tile per expert
+    gu.max_tiles = active;  // at most kStreamMaxRows rows each: one 4-row tile per expert
     err = launch_stream_gate_up(gu, s);
     if (err != hipSuccess) return K3MOE_ERR_DEVICE;
   }
@@ -231,7 +231,7 @@ int moe_mxfp4_ffn_profiled(const void* x_bf16, const int32_t* topk_ids, const fl
   if (stream_lists) {
     dn.tiles = g.tiles[3];
     dn.tile_count = g.tile_count + 3;
-    dn.max_tiles = active;
+    dn.max_tiles = (entries + active + 1) / 2;  // sum of ceil(n_e / 2) over experts
     err = launch_stream_down(dn, s);
     if (err != hipSuccess) return K3MOE_ERR_DEVICE;
   }

@@ -7,8 +7,9 @@
 // With one or two tokens per expert the product is a stream over the active
 // experts' weight bytes (about 4 flop per byte), so the kernel is laid out for
 // HBM, not for the matrix cores:
-//   - every wave works alone: a unit is 16 output features of one tile (up to
-//     4 grouped rows of one expert) over the whole K, and the wave stages the
+//   - every wave works alone: a unit is 32 weight rows of one tile (gate/up:
+//     16 features of w1 and of w3 for up to 4 grouped rows; down: 32 features
+//     of w2 for up to 2 grouped rows) over the whole K, and the wave stages the
 //     unit's weight rows through a private ring of three LDS buffers with
 //     direct global -> LDS loads of 16 bytes per lane, two stages ahead of the
 //     one it decodes; no workgroup barrier anywhere;
@@ -42,22 +43,28 @@ constexpr int kStageRowBytes = 272;  // bytes of one weight row per stage (17 ch
 constexpr int kRowChunks = 17;
 constexpr int kRowDw = 68;           // LDS dwords per staged weight row
 constexpr int kBRowBytes = 1040;     // LDS bytes per activation row per stage (1024 + 16 padding)
-constexpr int kTileRows = 4;         // grouped rows per tile
+constexpr int kRB = 2;               // 16-row weight blocks per wave and stage
+constexpr int kWInstr = kRB * 5;     // global -> LDS weight loads per stage (5 per 16-row block)
 
+// A unit is kFeat output features of one tile.  gate/up: row block 0 is w1,
+// row block 1 is w3, both rows 16*fg .. 16*fg + 15.  down: both row blocks
+// are w2, rows 32*fu .. 32*fu + 15 and 32*fu + 16 .. 32*fu + 31.  The tile's
+// activation rows: kTileRows x rows (gate/up); kTileRows h_hi rows followed
+// by kTileRows h_lo rows (down).
 template <bool kGateUp>
 struct StreamCfg;
 template <>
-struct StreamCfg<true> {  // w1 and w3: 16 rows x 17 chunks each (5 loads per matrix), 4 x rows
-  static constexpr int kMats = 2, kWInstr = 10, kBRows = 4;
+struct StreamCfg<true> {
+  static constexpr int kFeat = 16, kTileRows = 4, kBRows = 4;
 };
 template <>
-struct StreamCfg<false> {  // w2: 16 rows x 17 chunks (5 loads), 4 h_hi + 4 h_lo rows
-  static constexpr int kMats = 1, kWInstr = 5, kBRows = 8;
+struct StreamCfg<false> {
+  static constexpr int kFeat = 32, kTileRows = 2, kBRows = 4;
 };
 template <bool kGateUp>
-constexpr int kStageBytes = StreamCfg<kGateUp>::kMats * 16 * kStageRowBytes + StreamCfg<kGateUp>::kBRows * kBRowBytes;
-static_assert(2 * (StreamCfg<true>::kWInstr + StreamCfg<true>::kBRows) < 64, "vmcnt range");
-static_assert(2 * (StreamCfg<false>::kWInstr + StreamCfg<false>::kBRows) < 64, "vmcnt range");
+constexpr int kStageBytes = kRB * 16 * kStageRowBytes + StreamCfg<kGateUp>::kBRows * kBRowBytes;
+static_assert(2 * (kWInstr + StreamCfg<true>::kBRows) < 64, "vmcnt range");
+static_assert(2 * (kWInstr + StreamCfg<false>::kBRows) < 64, "vmcnt range");
 static_assert(kWaves * kRing * kStageBytes<true> <= 160 * 1024, "LDS");
 static_assert(kWaves * kRing * kStageBytes<false> <= 160 * 1024, "LDS");
 
@@ -140,15 +147,16 @@ template <bool kGateUp>
 __global__ __launch_bounds__(kWaves * 64, 1) void ffn_stream_kernel(GemmArgs a) {
   using C = StreamCfg<kGateUp>;
   constexpr int kSB = kStageBytes<kGateUp>;
-  constexpr int kMatBytes = 16 * kStageRowBytes;  // one matrix's 16 rows of a stage
-  constexpr int kWBytes = C::kMats * kMatBytes;   // activation rows start here
-  constexpr int kW = C::kWInstr;                  // weight loads per stage
+  constexpr int kMatBytes = 16 * kStageRowBytes;  // one 16-row block of a stage
+  constexpr int kWBytes = kRB * kMatBytes;        // activation rows start here
+  constexpr int kW = kWInstr;                     // weight loads per stage
+  constexpr int kTileRows = C::kTileRows;
   __shared__ __attribute__((aligned(16))) uint8_t lds[kWaves][kRing][kSB];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int rho = lane & 15, g = lane >> 4;
-  const int nfg = a.N / 16;  // 16-feature groups
+  const int nfg = a.N / C::kFeat;  // units per tile
   const auto row_tok = as_const(a.row_tok);
   const int64_t n_units = (int64_t)(*as_const(a.tile_count)) * nfg;
   const int64_t nw = (int64_t)gridDim.x * kWaves;
@@ -192,11 +200,12 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ffn_stream_kernel(GemmArgs a) 
   // returns how many activation loads it issued.
   auto issue = [&](const Cursor& c, int buf) -> int {
     uint8_t* dst = &lds[wave][buf][0];
-    const size_t unit_off = (size_t)c.tile.expert * mat_bytes + (size_t)(16 * c.fg) * row_bytes;
+    const size_t unit_off = (size_t)c.tile.expert * mat_bytes + (size_t)(C::kFeat * c.fg) * row_bytes;
     const uint32_t wso = (uint32_t)(kStageRowBytes * c.s);
 #pragma unroll
-    for (int mi = 0; mi < C::kMats; ++mi) {
-      const uint8_t* base = (mi == 0 ? a.wa : a.wb) + unit_off;
+    for (int mi = 0; mi < kRB; ++mi) {
+      const uint8_t* base =
+          kGateUp ? (mi == 0 ? a.wa : a.wb) + unit_off : a.wa + unit_off + (size_t)(16 * mi) * row_bytes;
       const __amdgpu_buffer_rsrc_t rsrc =
           __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, (int)(16 * row_bytes), 0x00020000);
 #pragma unroll
@@ -230,9 +239,9 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ffn_stream_kernel(GemmArgs a) 
     return (kGateUp ? 1 : 2) * c.tile.nrows;
   };
 
-  f32x4_t acc[C::kMats];
+  f32x4_t acc[kRB];
 #pragma unroll
-  for (int mi = 0; mi < C::kMats; ++mi) acc[mi] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int mi = 0; mi < kRB; ++mi) acc[mi] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   const uint32_t qsel = 0x03020100u + 0x01010101u * (uint32_t)(g + 1);
   Cursor ci{wid, 0, 0, {0, 0, 0}};  // issue side
@@ -249,11 +258,12 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ffn_stream_kernel(GemmArgs a) 
     buf_i = 2;
   }
   // B column rho reads LDS activation row brow: for gate/up the tile's row
-  // rho; for down h_hi row rho (columns 0..3) or h_lo row rho - 4 (columns
-  // 4..7), so one MFMA multiplies both halves of h (added in the epilogue).
-  // Columns without a row read row 0 (a broadcast; their sums are dropped).
+  // rho; for down h_hi row rho (columns 0 .. kTileRows-1) or h_lo row
+  // rho - kTileRows (the next kTileRows columns), so one MFMA multiplies both
+  // halves of h (added in the epilogue).  Columns without a row read row 0
+  // (a broadcast; their sums are dropped).
   auto brow_of = [&](int nrows) {
-    const bool has = kGateUp ? rho < nrows : (rho < 2 * kTileRows && (rho & (kTileRows - 1)) < nrows);
+    const bool has = kGateUp ? rho < nrows : (rho < 2 * kTileRows && (rho % kTileRows) < nrows);
     return has ? rho : 0;
   };
   int boff = kWBytes + kBRowBytes * brow_of(cc.tile.nrows);
@@ -282,7 +292,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ffn_stream_kernel(GemmArgs a) 
 #pragma unroll
       for (int i = 0; i < 4; ++i) bop[i] = *reinterpret_cast<const bf16x8_t*>(bl + 64 * (4 * rnd + g) + 16 * i);
 #pragma unroll
-      for (int mi = 0; mi < C::kMats; ++mi) {
+      for (int mi = 0; mi < kRB; ++mi) {
         bf16x8_t aop[4];
         decode_block(wl, 16 * mi + rho, rnd, g, qsel, aop);
 #pragma unroll
@@ -291,13 +301,16 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ffn_stream_kernel(GemmArgs a) 
     }
 
     if (cc.s == nst - 1) {
-      // Epilogue of the unit: lane holds features 16*fg + 4g + v for tile row rho.
+      // Epilogue of the unit: lane holds, for tile row rho, features 4g + v
+      // of each 16-row block.
       const TileInfo& tile = cc.tile;
       const int fg = cc.fg;
       if (!kGateUp) {
-        // y = (h_hi part in column rho) + (h_lo part in column rho + 4)
+        // y = (h_hi part in column rho) + (h_lo part in column rho + kTileRows)
 #pragma unroll
-        for (int v = 0; v < 4; ++v) acc[0][v] += __shfl_down(acc[0][v], kTileRows, 16);
+        for (int mi = 0; mi < kRB; ++mi)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) acc[mi][v] += __shfl_down(acc[mi][v], kTileRows, 16);
       }
       if (rho < tile.nrows) {
         const int64_t row = tile.row0 + rho;
@@ -305,7 +318,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ffn_stream_kernel(GemmArgs a) 
           uint32_t hb[4], lb[4];
 #pragma unroll
           for (int v = 0; v < 4; ++v) {
-            const float gt = acc[0][v], up = acc[C::kMats - 1][v];
+            const float gt = acc[0][v], up = acc[1][v];
             const float h = gt / (1.0f + expf(-gt)) * up;
             hb[v] = f32_to_bf16_bits(h);
             lb[v] = f32_to_bf16_bits(h - __uint_as_float(hb[v] << 16));
@@ -321,12 +334,14 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ffn_stream_kernel(GemmArgs a) 
             lrow[2 * v] = (uint16_t)lb[v];
           }
         } else {
-          float* yrow = reinterpret_cast<float*>(a.out) + row * a.N;
-          *reinterpret_cast<float4*>(yrow + 16 * fg + 4 * g) = make_float4(acc[0][0], acc[0][1], acc[0][2], acc[0][3]);
+          float* yrow = reinterpret_cast<float*>(a.out) + row * a.N + C::kFeat * fg + 4 * g;
+#pragma unroll
+          for (int mi = 0; mi < kRB; ++mi)
+            *reinterpret_cast<float4*>(yrow + 16 * mi) = make_float4(acc[mi][0], acc[mi][1], acc[mi][2], acc[mi][3]);
         }
       }
 #pragma unroll
-      for (int mi = 0; mi < C::kMats; ++mi) acc[mi] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      for (int mi = 0; mi < kRB; ++mi) acc[mi] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
     advance(cc);
     if (cc.s == 0 && q + 1 < Q) boff = kWBytes + kBRowBytes * brow_of(cc.tile.nrows);
@@ -347,7 +362,7 @@ int cu_count() {
 
 template <bool kGateUp>
 hipError_t launch_stream(const GemmArgs& a, hipStream_t s) {
-  const int64_t max_units = a.max_tiles * (a.N / 16);
+  const int64_t max_units = a.max_tiles * (a.N / StreamCfg<kGateUp>::kFeat);
   int64_t grid = (max_units + kWaves - 1) / kWaves;
   const int cus = cu_count();
   if (grid > cus) grid = cus;
@@ -362,7 +377,7 @@ hipError_t launch_stream(const GemmArgs& a, hipStream_t s) {
 // stage window starts 16-byte aligned); I must hold whole 32-feature blocks.
 bool stream_gemm_supported(int D, int I) { return (D % kStageK) == 0 && (I % kStageK) == 0; }
 
-int stream_rows_per_tile() { return kTileRows; }
+int stream_rows_per_tile(bool gate_up) { return gate_up ? StreamCfg<true>::kTileRows : StreamCfg<false>::kTileRows; }
 
 hipError_t launch_stream_gate_up(const GemmArgs& a, hipStream_t s) { return launch_stream<true>(a, s); }
 

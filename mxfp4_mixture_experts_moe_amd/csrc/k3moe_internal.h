@@ -23,7 +23,7 @@ constexpr int kChunkTokens = 64;
 // gate/up / down tiles of experts with few rows (see GroupArgs::split_rows).
 constexpr int kTileLists = 4;
 // The smallest tile height any GEMM variant uses; sizes the tile list.
-constexpr int kMinTileRows = 4;
+constexpr int kMinTileRows = 2;
 
 // Byte layout of the moe_mxfp4_ffn workspace (every region 256-byte aligned).
 struct FfnWorkspace {
@@ -87,7 +87,7 @@ hipError_t launch_big_gate_up(const GemmArgs& a, hipStream_t s);
 hipError_t launch_big_down(const GemmArgs& a, hipStream_t s);
 
 bool stream_gemm_supported(int D, int I);
-int stream_rows_per_tile();
+int stream_rows_per_tile(bool gate_up);
 hipError_t launch_stream_gate_up(const GemmArgs& a, hipStream_t s);
 hipError_t launch_stream_down(const GemmArgs& a, hipStream_t s);
 
