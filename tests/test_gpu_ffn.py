@@ -122,6 +122,21 @@ def test_streaming_path_hot_invalid_and_duplicate_ids(k3):
     assert np.array_equal(a.view(np.uint32), got.view(np.uint32))
 
 
+def test_mixed_large_and_streaming_experts(k3):
+    # one call in which some experts have many rows (large-tile kernels, with a
+    # partial last token group) and others 1..4 rows (weight-streaming kernels)
+    cfg = moe_inputs.TINY.with_(E=40, k=4, D=512, I=1024, T=90, config_id=44)
+    g = np.random.default_rng(14)
+    ids = np.stack([g.permutation(cfg.E)[: cfg.k] for _ in range(cfg.T)]).astype(np.int32)
+    ids[:, 0] = 3  # 90 rows: one full 64-row down tile + a partial one, 1 gate/up tile of 90
+    ids[:37, 1] = 7  # 37 rows
+    rest = ids[:, 2:]
+    rest[(rest == 3) | (rest == 7)] = 11
+    w = g.random((cfg.T, cfg.k)).astype(np.float32)
+    got, ref, _, _ = small_case(k3, cfg, ids, w)
+    assert_ffn_close(got, ref, "mixed large/streaming")
+
+
 @pytest.mark.parametrize(
     "E,k,D,I,T",
     [(8, 2, 128, 256, 64), (64, 4, 512, 512, 8), (8, 2, 512, 512, 300)],  # small-tile, streaming, large-tile paths
