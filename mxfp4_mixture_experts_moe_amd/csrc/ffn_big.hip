@@ -97,7 +97,11 @@ __device__ __forceinline__ int64_t xcd_logical(int64_t i, int64_t total) {
 template <bool kGateUp>
 __global__ __launch_bounds__(kThreads) void ffn_big_kernel(GemmArgs a) {
   using C = BigCfg<kGateUp>;
-  __shared__ uint32_t lds[2][kStageDw];
+  // One array per buffer: the compiler can then tell that the buffer being
+  // read is not the one the LDS-DMA loads in flight write.  With a single
+  // array it makes every read of the current buffer wait for the loads just
+  // issued into the other one, which serialises loading and computing.
+  __shared__ uint32_t lds0[kStageDw], lds1[kStageDw];
   __shared__ int32_t tok_src[C::kN];  // source row of every token slot of the tile
 
   const int n_ftiles = a.N / C::kF;
@@ -200,8 +204,9 @@ __global__ __launch_bounds__(kThreads) void ffn_big_kernel(GemmArgs a) {
   const bool aload = 16 * wave - asrc * C::kN < 16 * ntg;  // this wave's activation rows are live
 
   auto issue = [&](int stage, int buf) {
-    uint32_t* wl = &lds[buf][0] + 64 * wave * kWRowDw;
-    uint32_t* al = &lds[buf][kWDw] + 272 * 4 * wave;
+    uint32_t* const lb = buf ? lds1 : lds0;
+    uint32_t* wl = lb + 64 * wave * kWRowDw;
+    uint32_t* al = lb + kWDw + 272 * 4 * wave;
     const int wso = 64 * stage + 16 * (stage >> 2);  // 16-byte aligned start of the step's 68 bytes
 #pragma unroll
     for (int j = 0; j < kWRowChunks; ++j) __builtin_amdgcn_raw_ptr_buffer_load_lds(wrsrc, wl + 256 * j, 16, woffs[j], wso, 0, 0);
@@ -242,8 +247,8 @@ __global__ __launch_bounds__(kThreads) void ffn_big_kernel(GemmArgs a) {
     constexpr bool kFull = decltype(full_tag)::value;
     const int buf = PH & 1;  // s % 2 == PH % 2 because s % 4 == PH
     if (s + 1 < nstages) issue(s + 1, buf ^ 1);
-    const uint32_t* wl = &lds[buf][0];
-    const uint32_t* al = &lds[buf][kWDw];
+    const uint32_t* wl = buf ? lds1 : lds0;
+    const uint32_t* al = wl + kWDw;
 
     // qs dwords and block scale of block g of every (matrix, row group)
     uint32_t q[C::kMats][C::kRG][4];
