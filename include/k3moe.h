@@ -145,9 +145,13 @@ size_t moe_mxfp4_ffn_workspace_size(int64_t T, int32_t D, int32_t I, int32_t E, 
  *             its contents on entry do not matter and are clobbered
  *
  * act must be K3MOE_ACT_SILU_MUL: act(g, u) = g * sigmoid(g) * u.
- * Precision: bf16 x and bf16-exact weights, bf16 MFMA with fp32 accumulation;
- * h = act(g, u) is formed in fp32 and enters the down product as the bf16 pair
- * hi = bf16(h), lo = bf16(h - hi) (about 16 significant bits); fp32 output.
+ * Precision: bf16 x and exact weights, MFMA with fp32 accumulation; h =
+ * act(g, u) is formed in fp32 and enters the down product either as the bf16
+ * pair hi = bf16(h), lo = bf16(h - hi) (about 16 significant bits; experts with
+ * few rows, and shapes outside the large-tile kernels) or, for experts served
+ * by the large-tile kernels (D and I multiples of 512, I <= 16384), as fp16
+ * scaled by a power of two per (row, 256-wide slice of I) (11 significant
+ * bits; about 2e-4 relative L2 error on K3-shaped inputs); fp32 output.
  * The k expert outputs of a token are summed in slot order (deterministic, no
  * atomics).
  * Entry (t, j) is skipped (contributes nothing) when topk_ids[t,j] is outside

@@ -30,6 +30,7 @@ FfnWorkspace ffn_workspace_layout(int64_t T, int32_t D, int32_t I, int32_t E, in
   w.x_perm = take(sizeof(uint16_t) * (size_t)(T * D));
   w.h = take(sizeof(uint16_t) * (size_t)(entries * I));
   w.h_lo = take(sizeof(uint16_t) * (size_t)(entries * I));
+  w.h_scale = take((size_t)entries * (size_t)((I + 255) / 256));
   w.y = take(sizeof(float) * (size_t)(entries * D));
   w.total = off;
   return w;
@@ -192,6 +193,7 @@ int moe_mxfp4_ffn_profiled(const void* x_bf16, const int32_t* topk_ids, const fl
   gu.N = I;
   gu.out = ws + L.h;
   gu.out_lo = ws + L.h_lo;
+  gu.h_scale = reinterpret_cast<int8_t*>(ws + L.h_scale);
   GemmArgs dn{};
   dn.act = reinterpret_cast<const uint16_t*>(ws + L.h);
   dn.act_lo = reinterpret_cast<const uint16_t*>(ws + L.h_lo);
@@ -202,6 +204,7 @@ int moe_mxfp4_ffn_profiled(const void* x_bf16, const int32_t* topk_ids, const fl
   dn.K = I;
   dn.N = D;
   dn.out = ws + L.y;
+  dn.h_scale = reinterpret_cast<int8_t*>(ws + L.h_scale);
 
   // gate/up
   if (big_lists) {

@@ -1,8 +1,11 @@
 // Large-tile grouped GEMMs for batches in which experts receive many tokens
-// (prefill-sized batches).  Same arithmetic as ffn.hip (bf16 MFMA with the
-// MXFP4 block scale folded into the exact fp4 -> bf16 conversion, fp32
-// accumulation, h carried as a bf16 hi + lo pair); only the work decomposition
-// differs.
+// (prefill-sized batches).  gate/up has the arithmetic of ffn.hip (bf16 MFMA
+// with the MXFP4 block scale folded into the exact fp4 -> bf16 conversion,
+// fp32 accumulation).  h leaves it as fp16 scaled by a power of two per
+// (row, 256-feature slice) — 11 significant bits where ffn.hip's bf16 hi + lo
+// pair needs two MFMAs per product — and the down product takes it with fp16
+// MFMAs (w2 blocks converted exactly to fp16), folding each slice's partial
+// sums into the fp32 accumulators with the slice's scale.
 //
 // A workgroup of 8 waves owns an output tile of kF features x kN tokens of one
 // expert; each wave takes kF/8 features and all kN tokens, so every weight row
@@ -25,7 +28,10 @@
 //          rows are assigned so each lane's four outputs are four consecutive
 //          P-order positions of h (8-byte stores of h_hi and h_lo).
 // down:    kF = 512 features of w2, kN = 64 tokens; wave tile 64 x 64; the B
-//          operand is h_hi and h_lo (two MFMAs per decoded weight operand).
+//          operand is the scaled fp16 h.  A wave whose w2 blocks of a step
+//          include an exponent outside 104..140 (values fp16 cannot hold
+//          exactly) runs that step with bf16 weights and h split into an
+//          exact bf16 pair instead (two MFMAs per operand).
 //
 // Token groups of 16 with no row of the tile are skipped (no activation loads,
 // no MFMAs), so a tile of few rows costs about its weight traffic only.
@@ -44,6 +50,7 @@ namespace k3moe {
 namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kThreads = 512;
@@ -53,6 +60,7 @@ constexpr int kWRowChunks = 5;  // 16-byte chunks per weight row window
 constexpr int kARowDw = 68;     // LDS dwords per activation row per stage (256 + 16 bytes)
 constexpr int kARowChunks = 17; // 16-byte chunks per activation row (16 data + 1 pad)
 constexpr int kXcds = 8;
+constexpr int kMaxSlices = 64;  // 256-wide slices of I the down kernel supports (I <= 16384)
 
 template <bool kGateUp>
 struct BigCfg;
@@ -61,8 +69,8 @@ struct BigCfg<true> {  // wave: 2 row groups (32 features) x 8 token groups, 2 m
   static constexpr int kF = 256, kN = 128, kRG = 2, kTG = 8, kMats = 2, kSrc = 1;
 };
 template <>
-struct BigCfg<false> {  // wave: 4 row groups (64 features) x 4 token groups, h_hi and h_lo
-  static constexpr int kF = 512, kN = 64, kRG = 4, kTG = 4, kMats = 1, kSrc = 2;
+struct BigCfg<false> {  // wave: 4 row groups (64 features) x 4 token groups, scaled fp16 h
+  static constexpr int kF = 512, kN = 64, kRG = 4, kTG = 4, kMats = 1, kSrc = 1;
 };
 
 constexpr int kWDw = 2 * 256 * kWRowDw;        // weight dwords per stage (both variants: 512 rows)
@@ -82,8 +90,24 @@ __device__ __forceinline__ bf16x8_t decode_dword(uint32_t q, float sf) {
   return __builtin_bit_cast(bf16x8_t, r);
 }
 
-__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
-  return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)f);
+__device__ __forceinline__ f16x8_t decode_dword_f16(uint32_t q, float sf) {
+  uint4 r;
+  r.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(q, sf, 0));
+  r.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(q, sf, 1));
+  r.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(q, sf, 2));
+  r.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(q, sf, 3));
+  return __builtin_bit_cast(f16x8_t, r);
+}
+
+// Eight fp16 values as the exact bf16 pair hi = bf16(v), lo = v - hi.
+__device__ __forceinline__ void split_f16x8(uint4 b, bf16x8_t& hi, bf16x8_t& lo) {
+  const f16x8_t v = __builtin_bit_cast(f16x8_t, b);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float f = (float)v[e];
+    hi[e] = (__bf16)f;
+    lo[e] = (__bf16)(f - (float)hi[e]);
+  }
 }
 
 // Logical work index of workgroup `i` among `total` valid ones: the ids the
@@ -103,6 +127,9 @@ __global__ __launch_bounds__(kThreads) void ffn_big_kernel(GemmArgs a) {
   // issued into the other one, which serialises loading and computing.
   __shared__ uint32_t lds0[kStageDw], lds1[kStageDw];
   __shared__ int32_t tok_src[C::kN];  // source row of every token slot of the tile
+  __shared__ int8_t hs_l[kGateUp ? 1 : C::kN * kMaxSlices];  // down: h scale of every (row, slice)
+  __shared__ float red[kGateUp ? kThreads / 64 * C::kN : 1];   // gate/up: per-wave row maxima of |h|
+  __shared__ int sexp[kGateUp ? C::kN : 1];                    // gate/up: h scale exponent per row
 
   const int n_ftiles = a.N / C::kF;
   const int64_t total = (int64_t)(*a.tile_count) * n_ftiles;
@@ -151,6 +178,13 @@ __global__ __launch_bounds__(kThreads) void ffn_big_kernel(GemmArgs a) {
     const int m = tid < tile.nrows ? tid : 0;  // rows past the tile repeat the first row
     const int row = tile.row0 + m;
     tok_src[tid] = kGateUp ? a.row_tok[row] : row;
+  }
+  if constexpr (!kGateUp) {
+    const int nsl = K >> 8;  // 256-wide slices of h
+    for (int i = tid; i < C::kN * nsl; i += kThreads) {
+      const int m = i / nsl, sl = i - m * nsl;
+      hs_l[m * kMaxSlices + sl] = m < tile.nrows ? a.h_scale[(int64_t)(tile.row0 + m) * nsl + sl] : (int8_t)0;
+    }
   }
   __syncthreads();
 
@@ -201,7 +235,7 @@ __global__ __launch_bounds__(kThreads) void ffn_big_kernel(GemmArgs a) {
   // Token groups of 16 that hold rows of this tile (the others are skipped:
   // no activation loads, no MFMAs; their output columns are never stored).
   const int ntg = __builtin_amdgcn_readfirstlane((tile.nrows + 15) >> 4);
-  const bool aload = 16 * wave - asrc * C::kN < 16 * ntg;  // this wave's activation rows are live
+  const bool aload = asrc < C::kSrc && 16 * wave - asrc * C::kN < 16 * ntg;  // this wave's rows are live
 
   auto issue = [&](int stage, int buf) {
     uint32_t* const lb = buf ? lds1 : lds0;
@@ -237,22 +271,31 @@ __global__ __launch_bounds__(kThreads) void ffn_big_kernel(GemmArgs a) {
     for (int rg = 0; rg < C::kRG; ++rg)
 #pragma unroll
       for (int tg = 0; tg < C::kTG; ++tg) acc[mi][rg][tg] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  // down: partial sums of the current 256-wide slice of h, still in its scale
+  f32x4_t part[kGateUp ? 1 : C::kRG][C::kTG];
+#pragma unroll
+  for (int rg = 0; rg < (kGateUp ? 1 : C::kRG); ++rg)
+#pragma unroll
+    for (int tg = 0; tg < C::kTG; ++tg) part[rg][tg] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   const int nstages = K / kKStep;
 
   // One K step from LDS buffer `buf` whose weight window starts at phase PH.
   // kFull: every token group of the tile is live (the unguarded fast path)
-  auto run_stage = [&](auto ph_tag, auto full_tag, int s) {
+  // down: set when a wave met a w2 block the fp16 path cannot hold exactly
+  bool wide_seen = false;
+  auto run_stage = [&](auto ph_tag, auto full_tag, auto exact_tag, int s) {
     constexpr int PH = decltype(ph_tag)::value;
     constexpr bool kFull = decltype(full_tag)::value;
+    constexpr bool kExact = decltype(exact_tag)::value;  // down: the exact bf16-pair pass
     const int buf = PH & 1;  // s % 2 == PH % 2 because s % 4 == PH
     if (s + 1 < nstages) issue(s + 1, buf ^ 1);
     const uint32_t* wl = buf ? lds1 : lds0;
     const uint32_t* al = wl + kWDw;
 
-    // qs dwords and block scale of block g of every (matrix, row group)
+    // qs dwords and block exponent of block g of every (matrix, row group)
     uint32_t q[C::kMats][C::kRG][4];
-    float sf[C::kMats][C::kRG];
+    uint32_t eb[C::kMats][C::kRG];
 #pragma unroll
     for (int mi = 0; mi < C::kMats; ++mi)
 #pragma unroll
@@ -260,86 +303,207 @@ __global__ __launch_bounds__(kThreads) void ffn_big_kernel(GemmArgs a) {
         const uint4 c0 = *reinterpret_cast<const uint4*>(wl + wrow_dw[mi][rg]);
         const uint4 c1 = *reinterpret_cast<const uint4*>(wl + wrow_dw[mi][rg] + 4);
         const uint32_t w[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
-        sf[mi][rg] = e8m0_to_f32(__builtin_amdgcn_ubfe(w[PH], 8 * g, 8));
+        eb[mi][rg] = __builtin_amdgcn_ubfe(w[PH], 8 * g, 8);
 #pragma unroll
         for (int i = 0; i < 4; ++i) q[mi][rg][i] = __builtin_amdgcn_perm(w[PH + i + 1], w[PH + i], qsel);
       }
+    constexpr int kB = C::kTG * C::kSrc;
+    const int nlive = kFull ? kB : ntg * C::kSrc;  // operands of live token groups
 
+    if constexpr (kGateUp) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      bf16x8_t aop[C::kMats][C::kRG];
-#pragma unroll
-      for (int mi = 0; mi < C::kMats; ++mi)
-#pragma unroll
-        for (int rg = 0; rg < C::kRG; ++rg) aop[mi][rg] = decode_dword(q[mi][rg][i], sf[mi][rg]);
-      // activations: block g of the step, P-order positions 8i..8i+7 (chunk
-      // 4g+i); one operand is read ahead while the previous one feeds its MFMAs
-      constexpr int kB = C::kTG * C::kSrc;
-      auto bread = [&](int n) {
-        const int tg = n / C::kSrc, src = n % C::kSrc;
-        const int row = src * C::kN + tg * 16 + rho;
-        return __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(al + row * kARowDw + 4 * (4 * g + i)));
-      };
-      const int nlive = kFull ? kB : ntg * C::kSrc;  // operands of live token groups
-      bf16x8_t bnext = bread(0);
-#pragma unroll
-      for (int n = 0; n < kB; ++n) {
-        if (!kFull && n >= nlive) break;
-        const bf16x8_t bop = bnext;
-        if (n + 1 < kB && (kFull || n + 1 < nlive)) bnext = bread(n + 1);
-        const int tg = n / C::kSrc;
+      for (int i = 0; i < 4; ++i) {
+        bf16x8_t aop[C::kMats][C::kRG];
 #pragma unroll
         for (int mi = 0; mi < C::kMats; ++mi)
 #pragma unroll
-          for (int rg = 0; rg < C::kRG; ++rg)
-            acc[mi][rg][tg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop[mi][rg], bop, acc[mi][rg][tg], 0, 0, 0);
-        __builtin_amdgcn_sched_barrier(0);
+          for (int rg = 0; rg < C::kRG; ++rg) aop[mi][rg] = decode_dword(q[mi][rg][i], e8m0_to_f32(eb[mi][rg]));
+        // activations: block g of the step, P-order positions 8i..8i+7 (chunk
+        // 4g+i); one operand is read ahead while the previous one feeds its MFMAs
+        auto bread = [&](int n) {
+          const int row = n * 16 + rho;
+          return __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(al + row * kARowDw + 4 * (4 * g + i)));
+        };
+        bf16x8_t bnext = bread(0);
+#pragma unroll
+        for (int n = 0; n < kB; ++n) {
+          if (!kFull && n >= nlive) break;
+          const bf16x8_t bop = bnext;
+          if (n + 1 < kB && (kFull || n + 1 < nlive)) bnext = bread(n + 1);
+#pragma unroll
+          for (int mi = 0; mi < C::kMats; ++mi)
+#pragma unroll
+            for (int rg = 0; rg < C::kRG; ++rg)
+              acc[mi][rg][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop[mi][rg], bop, acc[mi][rg][n], 0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
+    } else {
+      // fp16 holds every w2 value of a block exactly when its exponent byte is
+      // in 104..140.  The fp16 pass notes any other block; the workgroup then
+      // redoes the tile with the exact pass.
+      if constexpr (!kExact) {
+        bool wide = false;
+#pragma unroll
+        for (int rg = 0; rg < C::kRG; ++rg) wide |= (eb[0][rg] - 104u) > 36u;
+        wide_seen |= __builtin_amdgcn_ballot_w64(wide) != 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          f16x8_t aop[C::kRG];
+#pragma unroll
+          for (int rg = 0; rg < C::kRG; ++rg) aop[rg] = decode_dword_f16(q[0][rg][i], e8m0_to_f32(eb[0][rg]));
+          auto bread = [&](int n) {
+            const int row = n * 16 + rho;
+            return __builtin_bit_cast(f16x8_t, *reinterpret_cast<const uint4*>(al + row * kARowDw + 4 * (4 * g + i)));
+          };
+          f16x8_t bnext = bread(0);
+#pragma unroll
+          for (int n = 0; n < kB; ++n) {
+            if (!kFull && n >= nlive) break;
+            const f16x8_t bop = bnext;
+            if (n + 1 < kB && (kFull || n + 1 < nlive)) bnext = bread(n + 1);
+#pragma unroll
+            for (int rg = 0; rg < C::kRG; ++rg)
+              part[rg][n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aop[rg], bop, part[rg][n], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          bf16x8_t aop[C::kRG];
+#pragma unroll
+          for (int rg = 0; rg < C::kRG; ++rg) aop[rg] = decode_dword(q[0][rg][i], e8m0_to_f32(eb[0][rg]));
+#pragma unroll
+          for (int n = 0; n < kB; ++n) {
+            if (!kFull && n >= nlive) break;
+            const int row = n * 16 + rho;
+            bf16x8_t bhi, blo;
+            split_f16x8(*reinterpret_cast<const uint4*>(al + row * kARowDw + 4 * (4 * g + i)), bhi, blo);
+#pragma unroll
+            for (int rg = 0; rg < C::kRG; ++rg) {
+              part[rg][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop[rg], bhi, part[rg][n], 0, 0, 0);
+              part[rg][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop[rg], blo, part[rg][n], 0, 0, 0);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }
+      }
+      if constexpr ((PH & 1) != 0) {
+        // the step closes a 256-wide slice of h: fold the slice's partial sums
+        // into the accumulators with the slice's scale (one per token column)
+        const int sl = s >> 1;
+#pragma unroll
+        for (int tg = 0; tg < C::kTG; ++tg) {
+          const float f = ldexpf(1.0f, (int)hs_l[(tg * 16 + rho) * kMaxSlices + sl]);
+#pragma unroll
+          for (int rg = 0; rg < C::kRG; ++rg) {
+#pragma unroll
+            for (int v = 0; v < 4; ++v) acc[0][rg][tg][v] = fmaf(part[rg][tg][v], f, acc[0][rg][tg][v]);
+            part[rg][tg] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+          }
+        }
       }
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
   };
 
+  auto k_loop = [&](auto full_tag, auto exact_tag) {
+    for (int s = 0; s < nstages; s += 4) {
+      run_stage(std::integral_constant<int, 0>{}, full_tag, exact_tag, s);
+      if (s + 1 < nstages) run_stage(std::integral_constant<int, 1>{}, full_tag, exact_tag, s + 1);
+      if (s + 2 < nstages) run_stage(std::integral_constant<int, 2>{}, full_tag, exact_tag, s + 2);
+      if (s + 3 < nstages) run_stage(std::integral_constant<int, 3>{}, full_tag, exact_tag, s + 3);
+    }
+  };
   issue(0, 0);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
-  auto k_loop = [&](auto full_tag) {
-    for (int s = 0; s < nstages; s += 4) {
-      run_stage(std::integral_constant<int, 0>{}, full_tag, s);
-      if (s + 1 < nstages) run_stage(std::integral_constant<int, 1>{}, full_tag, s + 1);
-      if (s + 2 < nstages) run_stage(std::integral_constant<int, 2>{}, full_tag, s + 2);
-      if (s + 3 < nstages) run_stage(std::integral_constant<int, 3>{}, full_tag, s + 3);
-    }
-  };
   if (ntg == C::kTG)
-    k_loop(std::true_type{});
+    k_loop(std::true_type{}, std::false_type{});
   else
-    k_loop(std::false_type{});
+    k_loop(std::false_type{}, std::false_type{});
+  if constexpr (!kGateUp) {
+    if (__syncthreads_or(wide_seen ? 1 : 0)) {  // rare: w2 exponents outside 104..140
+#pragma unroll
+      for (int rg = 0; rg < C::kRG; ++rg)
+#pragma unroll
+        for (int tg = 0; tg < C::kTG; ++tg) acc[0][rg][tg] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      issue(0, 0);
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      if (ntg == C::kTG)
+        k_loop(std::true_type{}, std::true_type{});
+      else
+        k_loop(std::false_type{}, std::true_type{});
+    }
+  }
 
   // ---- epilogue ----
+  if constexpr (kGateUp) {
+    // h = SiLU(gate) * up, in place of the gate accumulators
 #pragma unroll
-  for (int tg = 0; tg < C::kTG; ++tg) {
-    const int m = tg * 16 + rho;
-    if (m >= tile.nrows) continue;
-    const int64_t row = tile.row0 + m;
+    for (int rg = 0; rg < C::kRG; ++rg)
 #pragma unroll
-    for (int rg = 0; rg < C::kRG; ++rg) {
-      if (kGateUp) {
-        uint32_t hb[4], lb[4];
+      for (int tg = 0; tg < C::kTG; ++tg)
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-          const float gt = acc[0][rg][tg][v], up = acc[C::kMats - 1][rg][tg][v];
-          const float h = gt / (1.0f + expf(-gt)) * up;
-          hb[v] = f32_to_bf16_bits(h);
-          lb[v] = f32_to_bf16_bits(h - __uint_as_float(hb[v] << 16));
+          const float gt = acc[0][rg][tg][v], up = acc[1][rg][tg][v];
+          acc[0][rg][tg][v] = gt / (1.0f + expf(-gt)) * up;
         }
+    // Scale of each token row of this 256-feature slice: 2^s with s = the
+    // exponent of max |h| minus 14, so the scaled values stay below 2^15.
+    // Max over the wave's 32 features (lanes g = 0..3), then over the waves
+    // through LDS.
+#pragma unroll
+    for (int tg = 0; tg < C::kTG; ++tg) {
+      float m = 0.f;
+#pragma unroll
+      for (int rg = 0; rg < C::kRG; ++rg)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) m = fmaxf(m, fabsf(acc[0][rg][tg][v]));
+      m = fmaxf(m, __shfl_xor(m, 16));
+      m = fmaxf(m, __shfl_xor(m, 32));
+      if (g == 0) red[wave * C::kN + tg * 16 + rho] = m;
+    }
+    __syncthreads();
+    if (tid < C::kN) {
+      float m = 0.f;
+#pragma unroll
+      for (int w = 0; w < kThreads / 64; ++w) m = fmaxf(m, red[w * C::kN + tid]);
+      int sx = (int)((__float_as_uint(m) >> 23) & 0xFFu) - 127 - 14;
+      sx = m > 0.f ? (sx < -128 ? -128 : (sx > 113 ? 113 : sx)) : 0;
+      sexp[tid] = sx;
+      if (tid < tile.nrows) a.h_scale[(int64_t)(tile.row0 + tid) * (a.N >> 8) + ftile] = (int8_t)sx;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int tg = 0; tg < C::kTG; ++tg) {
+      const int m = tg * 16 + rho;
+      if (m >= tile.nrows) continue;
+      const int64_t row = tile.row0 + m;
+      const int sx = sexp[m];
+      uint16_t* hrow = reinterpret_cast<uint16_t*>(a.out) + row * a.N;
+#pragma unroll
+      for (int rg = 0; rg < C::kRG; ++rg) {
+        uint32_t hb[4];
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+          hb[v] = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)ldexpf(acc[0][rg][tg][v], -sx));
         const int pos = f0 + 32 * wave + 16 * rg + 4 * g;
-        uint16_t* hrow = reinterpret_cast<uint16_t*>(a.out) + row * a.N;
-        uint16_t* lrow = reinterpret_cast<uint16_t*>(a.out_lo) + row * a.N;
         *reinterpret_cast<uint2*>(hrow + pos) = make_uint2(hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16));
-        *reinterpret_cast<uint2*>(lrow + pos) = make_uint2(lb[0] | (lb[1] << 16), lb[2] | (lb[3] << 16));
-      } else {
-        float* yrow = reinterpret_cast<float*>(a.out) + row * a.N;
+      }
+    }
+  } else {
+#pragma unroll
+    for (int tg = 0; tg < C::kTG; ++tg) {
+      const int m = tg * 16 + rho;
+      if (m >= tile.nrows) continue;
+      const int64_t row = tile.row0 + m;
+      float* yrow = reinterpret_cast<float*>(a.out) + row * a.N;
+#pragma unroll
+      for (int rg = 0; rg < C::kRG; ++rg) {
         const int f = f0 + 64 * wave + 16 * rg + 4 * g;
         *reinterpret_cast<float4*>(yrow + f) =
             make_float4(acc[0][rg][tg][0], acc[0][rg][tg][1], acc[0][rg][tg][2], acc[0][rg][tg][3]);
@@ -354,7 +518,7 @@ __global__ __launch_bounds__(kThreads) void ffn_big_kernel(GemmArgs a) {
 // (512) so the last 80-byte weight window of a row ends exactly at the row end.
 bool big_gemm_supported(int D, int I) {
   return (I % BigCfg<true>::kF) == 0 && (D % BigCfg<false>::kF) == 0 && (D % (4 * kKStep)) == 0 &&
-         (I % (4 * kKStep)) == 0;
+         (I % (4 * kKStep)) == 0 && I <= 256 * kMaxSlices;
 }
 
 int big_rows_per_tile(bool gate_up) { return gate_up ? BigCfg<true>::kN : BigCfg<false>::kN; }

@@ -28,7 +28,7 @@ constexpr int kMinTileRows = 2;
 // Byte layout of the moe_mxfp4_ffn workspace (every region 256-byte aligned).
 struct FfnWorkspace {
   size_t counts, offsets, tile_count, tiles[kTileLists], row_tok, slot_row, chunk_base, chunk_mask;
-  size_t x_perm, h, h_lo, y;
+  size_t x_perm, h, h_lo, h_scale, y;
   size_t total;
   int64_t max_tiles, n_chunks;
 };
@@ -77,6 +77,10 @@ struct GemmArgs {
   int N;      // output features (I for gate/up, D for down)
   void* out;     // gate/up: h_hi bf16 [rows, I] (P-order blocks); down: y f32 [rows, D]
   void* out_lo;  // gate/up: h_lo bf16 [rows, I]
+  // Large-tile kernels only: h of their rows is carried as fp16 scaled by
+  // 2^-h_scale[row, I-slice of 256] instead of h_hi + h_lo (written by the
+  // gate/up kernel into `out`, read by the down kernel from `act`).
+  int8_t* h_scale;  // [rows, I / 256]
 };
 hipError_t launch_gate_up(const GemmArgs& a, int rows_per_tile, hipStream_t s);
 hipError_t launch_down(const GemmArgs& a, int rows_per_tile, hipStream_t s);

@@ -176,6 +176,36 @@ def test_graph_replay_matches_eager(k3, E, k, D, I, T):
         _ = (x.float() * 2).sum().item()  # unrelated eager work between replays
 
 
+@pytest.mark.parametrize("e_lo,e_hi", [(96, 150), (70, 100)])
+def test_large_tile_weights_fp16_cannot_hold(k3, e_lo, e_hi):
+    # Large-tile shapes with w2 block exponents partly (96..150) or wholly
+    # (70..100) outside the range whose values fp16 holds exactly: the down
+    # product must redo those tiles with the exact bf16 pair, and h spans
+    # magnitudes far from 1 (scaled per row and 256-feature slice).
+    print(f"[ffn] large-tile exponents {e_lo}..{e_hi}", flush=True)
+    cfg = moe_inputs.TINY.with_(E=8, k=2, D=512, I=512, T=300, e_lo=e_lo, e_hi=e_hi, config_id=60 + e_lo)
+    got, ref, _, _ = small_case(k3, cfg)
+    assert_ffn_close(got, ref, f"large-tile exponents {e_lo}..{e_hi}")
+
+
+@pytest.mark.parametrize("shift", [-40, 30])
+def test_large_tile_extreme_activation_scale(k3, shift):
+    # x scaled by 2^shift (exactly, in its bf16 exponent field): h lands far
+    # outside fp16's range unless the per-slice scale follows it
+    print(f"[ffn] large-tile x * 2^{shift}", flush=True)
+    cfg = moe_inputs.TINY.with_(E=8, k=2, D=512, I=512, T=300, config_id=70)
+    batch = moe_inputs.make_batch(cfg)
+    ids, w = route_ref(batch.z, batch.b, cfg.k)
+    xb = batch.x.astype(np.int32)
+    ex = (xb >> 7) & 0xFF
+    assert ex.min() > max(0, -shift) and ex.max() < min(255, 255 - shift)  # no zero, no under/overflow
+    x = ((xb & ~(0xFF << 7)) | ((ex + shift) << 7)).astype(np.uint16)
+    dev = device_experts(k3, cfg)
+    got = run_ffn(k3, dev, x, ids.astype(np.int32), w.astype(np.float32))
+    ref = ffn_ref(x, ids, w, HostExperts(cfg))
+    assert_ffn_close(got, ref, f"large-tile x * 2^{shift}")
+
+
 def test_identity_weights_closed_form(k3):
     """W1 = W3 = [I; 0], W2 = 2^e [I | 0]: out[t] = sum_j w_j 2^(e_j) SiLU(x) x."""
     E, D, I, T, k = 4, 128, 256, 48, 2
