@@ -311,19 +311,26 @@ __global__ __launch_bounds__(kThreads) void ffn_big_kernel(GemmArgs a) {
     const int nlive = kFull ? kB : ntg * C::kSrc;  // operands of live token groups
 
     if constexpr (kGateUp) {
+      // Slice i's weight operands are converted during slice i - 1's MFMAs
+      // (one (matrix, row group) pair per token group), so the conversion
+      // overlaps the matrix work instead of preceding it.
+      constexpr int kPairs = C::kMats * C::kRG;
+      bf16x8_t aop[kPairs];
+#pragma unroll
+      for (int pr = 0; pr < kPairs; ++pr)
+        aop[pr] = decode_dword(q[pr / C::kRG][pr % C::kRG][0], e8m0_to_f32(eb[pr / C::kRG][pr % C::kRG]));
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        bf16x8_t aop[C::kMats][C::kRG];
-#pragma unroll
-        for (int mi = 0; mi < C::kMats; ++mi)
-#pragma unroll
-          for (int rg = 0; rg < C::kRG; ++rg) aop[mi][rg] = decode_dword(q[mi][rg][i], e8m0_to_f32(eb[mi][rg]));
         // activations: block g of the step, P-order positions 8i..8i+7 (chunk
         // 4g+i); one operand is read ahead while the previous one feeds its MFMAs
         auto bread = [&](int n) {
           const int row = n * 16 + rho;
           return __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(al + row * kARowDw + 4 * (4 * g + i)));
         };
+        auto convert_next = [&](int pr) {
+          return decode_dword(q[pr / C::kRG][pr % C::kRG][i + 1], e8m0_to_f32(eb[pr / C::kRG][pr % C::kRG]));
+        };
+        bf16x8_t anext[kPairs];
         bf16x8_t bnext = bread(0);
 #pragma unroll
         for (int n = 0; n < kB; ++n) {
@@ -331,11 +338,18 @@ __global__ __launch_bounds__(kThreads) void ffn_big_kernel(GemmArgs a) {
           const bf16x8_t bop = bnext;
           if (n + 1 < kB && (kFull || n + 1 < nlive)) bnext = bread(n + 1);
 #pragma unroll
-          for (int mi = 0; mi < C::kMats; ++mi)
-#pragma unroll
-            for (int rg = 0; rg < C::kRG; ++rg)
-              acc[mi][rg][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop[mi][rg], bop, acc[mi][rg][n], 0, 0, 0);
+          for (int pr = 0; pr < kPairs; ++pr)
+            acc[pr / C::kRG][pr % C::kRG][n] =
+                __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop[pr], bop, acc[pr / C::kRG][pr % C::kRG][n], 0, 0, 0);
+          if (i + 1 < 4 && n < kPairs) anext[n] = convert_next(n);
           __builtin_amdgcn_sched_barrier(0);
+        }
+        if (i + 1 < 4) {
+#pragma unroll
+          for (int pr = 0; pr < kPairs; ++pr) {
+            if (!kFull && pr >= nlive) anext[pr] = convert_next(pr);  // fewer live token groups than pairs
+            aop[pr] = anext[pr];
+          }
         }
       }
     } else {

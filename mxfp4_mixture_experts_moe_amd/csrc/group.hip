@@ -237,12 +237,20 @@ __global__ __launch_bounds__(256) void group_count_kernel(GroupArgs a) {
 __global__ __launch_bounds__(kScanThreads) void group_scan_kernel(GroupArgs a, int64_t n_chunks) {
   extern __shared__ int32_t ltot[];  // [E] per-expert totals
   const int E = a.E, tid = threadIdx.x;
-  for (int e = tid; e < E; e += kScanThreads) ltot[e] = 0;
-  __syncthreads();
-  const int64_t n = n_chunks * E;
-  for (int64_t i = tid; i < n; i += kScanThreads) {
-    const int32_t v = a.chunk_base[i];
-    if (v) atomicAdd(&ltot[(int)(i % E)], v);
+  // totals: expert-parallel sums over the chunks, eight loads in flight (the
+  // loads of consecutive threads are consecutive in memory)
+  for (int e = tid; e < E; e += kScanThreads) {
+    int sum = 0;
+    int64_t c = 0;
+    for (; c + 8 <= n_chunks; c += 8) {
+      int32_t v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = a.chunk_base[(c + u) * E + e];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) sum += v[u];
+    }
+    for (; c < n_chunks; ++c) sum += a.chunk_base[c * E + e];
+    ltot[e] = sum;
   }
   __syncthreads();
   // offsets and tiles: thread t owns experts 8t..8t+7
