@@ -361,15 +361,17 @@ __global__ __launch_bounds__(kThreads) void ffn_big_kernel(GemmArgs a) {
 #pragma unroll
         for (int rg = 0; rg < C::kRG; ++rg) wide |= (eb[0][rg] - 104u) > 36u;
         wide_seen |= __builtin_amdgcn_ballot_w64(wide) != 0;
+        // as in gate/up, slice i's operands are converted during slice i - 1's MFMAs
+        f16x8_t aop[C::kRG];
+#pragma unroll
+        for (int rg = 0; rg < C::kRG; ++rg) aop[rg] = decode_dword_f16(q[0][rg][0], e8m0_to_f32(eb[0][rg]));
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          f16x8_t aop[C::kRG];
-#pragma unroll
-          for (int rg = 0; rg < C::kRG; ++rg) aop[rg] = decode_dword_f16(q[0][rg][i], e8m0_to_f32(eb[0][rg]));
           auto bread = [&](int n) {
             const int row = n * 16 + rho;
             return __builtin_bit_cast(f16x8_t, *reinterpret_cast<const uint4*>(al + row * kARowDw + 4 * (4 * g + i)));
           };
+          f16x8_t anext[C::kRG];
           f16x8_t bnext = bread(0);
 #pragma unroll
           for (int n = 0; n < kB; ++n) {
@@ -379,7 +381,15 @@ __global__ __launch_bounds__(kThreads) void ffn_big_kernel(GemmArgs a) {
 #pragma unroll
             for (int rg = 0; rg < C::kRG; ++rg)
               part[rg][n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aop[rg], bop, part[rg][n], 0, 0, 0);
+            if (i + 1 < 4 && n < C::kRG) anext[n] = decode_dword_f16(q[0][n][i + 1], e8m0_to_f32(eb[0][n]));
             __builtin_amdgcn_sched_barrier(0);
+          }
+          if (i + 1 < 4) {
+#pragma unroll
+            for (int rg = 0; rg < C::kRG; ++rg) {
+              if (!kFull && rg >= nlive) anext[rg] = decode_dword_f16(q[0][rg][i + 1], e8m0_to_f32(eb[0][rg]));
+              aop[rg] = anext[rg];
+            }
           }
         }
       } else {
