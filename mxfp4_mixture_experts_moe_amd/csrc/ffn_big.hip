@@ -20,18 +20,19 @@
 //                tokens a ds_read_b128 touches fall in distinct banks).
 // A lane (row rho, lane group g) owns block g of the step for its row: it reads
 // the two 16-byte chunks holding the block, pulls out the exponent byte and the
-// 16 qs bytes, and converts one qs dword per MFMA slice.  The K loop is
+// 16 qs bytes, and converts one qs dword per MFMA slice (the next slice's
+// conversions run between the current slice's MFMAs).  The K loop is
 // unrolled by four so the window phase is a compile-time constant.
 //
 // gate/up: kF = 256 features of w1 and of w3, kN = 128 tokens; wave tile
 //          32 features (one I-block) x 128 tokens for both matrices.  The MFMA
 //          rows are assigned so each lane's four outputs are four consecutive
-//          P-order positions of h (8-byte stores of h_hi and h_lo).
+//          P-order positions of h (8-byte stores of the scaled fp16 h).
 // down:    kF = 512 features of w2, kN = 64 tokens; wave tile 64 x 64; the B
-//          operand is the scaled fp16 h.  A wave whose w2 blocks of a step
-//          include an exponent outside 104..140 (values fp16 cannot hold
-//          exactly) runs that step with bf16 weights and h split into an
-//          exact bf16 pair instead (two MFMAs per operand).
+//          operand is the scaled fp16 h.  If any w2 block of the tile has an
+//          exponent outside 104..140 (values fp16 cannot hold exactly), the
+//          workgroup redoes the tile with bf16 weights and h split into an
+//          exact bf16 pair (two MFMAs per operand).
 //
 // Token groups of 16 with no row of the tile are skipped (no activation loads,
 // no MFMAs), so a tile of few rows costs about its weight traffic only.
