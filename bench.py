@@ -10,11 +10,13 @@ several seeded routing inputs so successive steps touch different experts.
 
     python bench.py [--workload prefill|verify|decode-t8|decode-t1|tiny] [--steps K] [--warmup W]
 
+Without --steps, K is chosen so the timed steps take about half a second.
+
 Prints one JSON line (rank 0).  `value` is the wall-clock rate of K steps
 replayed from captured HIP graphs (one graph per rotated batch; --eager times
 plain launches).  The kernel timing behind "roofline" comes from HIP events
 that the library records on its own stream around the dominant stage
-(moe_mxfp4_ffn_profiled) in K eager steps run right after the timed ones; the
+(moe_mxfp4_ffn_profiled) in up to 200 eager steps run right after the timed ones; the
 stage split comes from a short eager pass with every stage boundary marked.
 `python bench.py --copy-calibration` only copies a 256 MiB buffer, the
 reference kernel whose rocprofv3 FETCH_SIZE / WRITE_SIZE readings scale the
@@ -45,12 +47,13 @@ CSRC = "mxfp4_mixture_experts_moe_amd/csrc/"
 def gemm_path(cfg) -> str:
     """Which grouped-GEMM kernels moe_mxfp4_ffn launches for this shape (the
     library's own selection rule, restated for labelling the roofline):
-    "stream" (weight-streaming only), "tiled" (large-tile GEMMs for experts
-    with more than 4 rows, weight-streaming for the others) or "small"."""
+    "stream" (weight-streaming only, batches of up to 8 tokens), "tiled"
+    (large-tile GEMMs for experts with more than 4 rows, weight-streaming for
+    the others) or "small"."""
     entries = cfg.T * cfg.k
     fits = entries * max(cfg.I, cfg.D) * 2 < (1 << 31)
     if cfg.D % 512 == 0 and cfg.I % 512 == 0 and fits:
-        return "stream" if cfg.T <= 4 else "tiled"
+        return "stream" if cfg.T <= 8 else "tiled"
     return "small"
 
 
@@ -71,7 +74,8 @@ def kernel_info(stage: str, path: str):
 def parse_args():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=0,
+                    help="timed steps (0: as many as fill about 0.5 s, 20 to 5000)")
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="prefill", choices=["prefill", "verify", "decode-t8", "decode-t1", "tiny"])
     ap.add_argument("--rotate", type=int, default=0, help="distinct seeded batches cycled (0: 8 for decode, 4 else)")
@@ -233,7 +237,7 @@ def main():
     torch.cuda.synchronize()
 
     # 1. stage split (eager, all stage boundaries marked) -> dominant stage
-    n_split = max(rotate, min(steps, 16))
+    n_split = max(rotate, min(steps, 16) if steps > 0 else 16)
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(n_split)]
     busy_head()
     for i in range(n_split):
@@ -241,6 +245,11 @@ def main():
     torch.cuda.synchronize()
     stage_ms = {s: float(np.mean([ev[i][n].elapsed_time(ev[i][n + 1]) for i in range(n_split)]))
                 for n, s in enumerate(stages)}
+
+    if steps <= 0:
+        # long enough that clock ramp-up and the first replays do not show
+        est_s = sum(stage_ms.values()) * 1e-3
+        steps = int(min(5000, max(20, round(0.5 / max(est_s, 1e-6)))))
 
     # 2. the timed steps: one captured graph per rotated batch, replayed
     graphs = []
@@ -267,21 +276,23 @@ def main():
     #    eager step time from two events around all of them
     dom = max(stages, key=lambda s: stage_ms[s])
     n = stages.index(dom)
+    n_ev = min(steps, 200)
     dev_ev = [[torch.cuda.Event(enable_timing=True) if m in (n, n + 1) else None for m in range(6)]
-              for _ in range(steps)]
+              for _ in range(n_ev)]
     e_start, e_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     busy_head()
     e_start.record()
-    for i in range(steps):
+    for i in range(n_ev):
         step(warmup + i, dev_ev[i])
     e_end.record()
     torch.cuda.synchronize()
-    dom_ms = float(np.mean([dev_ev[i][n].elapsed_time(dev_ev[i][n + 1]) for i in range(steps)]))
-    eager_ms = e_start.elapsed_time(e_end) / steps
+    dom_ms = float(np.mean([dev_ev[i][n].elapsed_time(dev_ev[i][n + 1]) for i in range(n_ev)]))
+    eager_ms = e_start.elapsed_time(e_end) / n_ev
 
     rows = cfg.T * cfg.k
+    act_ev = [n_active[(warmup + i) % rotate] for i in range(n_ev)]
     act_steps = [n_active[(warmup + i) % rotate] for i in range(steps)]
-    flops, byts = stage_work(dom, cfg, rows, float(np.mean(act_steps)))
+    flops, byts = stage_work(dom, cfg, rows, float(np.mean(act_ev)))
     bound = "mfma" if flops / max(byts, 1.0) > RIDGE else "hbm"
     dur_s = dom_ms * 1e-3
     if bound == "mfma":

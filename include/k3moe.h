@@ -183,6 +183,40 @@ int moe_mxfp4_ffn_profiled(const void* x_bf16, const int32_t* topk_ids, const fl
                            int32_t k, int32_t act, float* out, void* workspace, size_t workspace_bytes,
                            void* stream, void* const* stage_events);
 
+/*
+ * moe_group_workspace_size — bytes of device workspace moe_group_by_expert
+ * needs (0 when T == 0 or the sizes are out of range). Pure host computation.
+ */
+size_t moe_group_workspace_size(int64_t T, int32_t E, int32_t k);
+
+/*
+ * moe_group_by_expert — the grouping step that moe_mxfp4_ffn runs before its
+ * products, as a call of its own: the routed entries sorted by expert.
+ * Source: llama.cpp pull request "model: add Kimi-K3 text model",
+ * LLAMA_MAX_EXPERTS comment (build_moe_ffn runs every expert on the tokens
+ * routed to it; the expert count is a run-time size, not a compile-time cap).
+ *
+ *   topk_ids i32 [T, k]   routed experts; entry q = t*k + j
+ *   counts   i32 [E]      out: valid entries per expert
+ *   offsets  i32 [E + 1]  out: exclusive prefix sum of counts; offsets[E] = n,
+ *                         the number of valid entries
+ *   row_tok  i32 [T * k]  out: token of grouped row r for r < n, rows ordered
+ *                         by (expert, token, slot); entries from n on are left
+ *                         as they were
+ *   slot_row i32 [T * k]  out: grouped row of entry q, or -1 if q is skipped
+ *   workspace device buffer of at least moe_group_workspace_size() bytes;
+ *             its contents on entry do not matter and are clobbered
+ *
+ * Entry q is skipped when its id is outside [0, E) or repeats an id earlier in
+ * the same row (the rule moe_mxfp4_ffn applies). Integer work only; the result
+ * does not depend on thread timing.
+ * Sizes: T >= 0 (T == 0 is a no-op: nothing is written), 1 <= k <=
+ * K3MOE_MAX_TOPK, 1 <= E <= K3MOE_MAX_EXPERTS_FFN, T * k < 2^31;
+ * K3MOE_ERR_SHAPE otherwise. Every pointer must be 16-byte aligned.
+ */
+int moe_group_by_expert(const int32_t* topk_ids, int64_t T, int32_t E, int32_t k, int32_t* counts, int32_t* offsets,
+                        int32_t* row_tok, int32_t* slot_row, void* workspace, size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

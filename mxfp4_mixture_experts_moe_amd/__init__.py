@@ -24,6 +24,8 @@ __all__ = [
     "mxfp4_dequant",
     "moe_mxfp4_ffn_workspace_size",
     "moe_mxfp4_ffn",
+    "moe_group_workspace_size",
+    "moe_group_by_expert",
     "FFN_STAGES",
     "status_str",
     "lib",
@@ -57,6 +59,10 @@ lib.moe_mxfp4_ffn.restype = ctypes.c_int
 lib.moe_mxfp4_ffn.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _sz, _vp]
 lib.moe_mxfp4_ffn_profiled.restype = ctypes.c_int
 lib.moe_mxfp4_ffn_profiled.argtypes = lib.moe_mxfp4_ffn.argtypes + [ctypes.POINTER(ctypes.c_void_p)]
+lib.moe_group_workspace_size.restype = _sz
+lib.moe_group_workspace_size.argtypes = [_i64, _i32, _i32]
+lib.moe_group_by_expert.restype = ctypes.c_int
+lib.moe_group_by_expert.argtypes = [_vp, _i64, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _sz, _vp]
 FFN_STAGE_EVENTS = 5
 FFN_STAGES = ("group", "gate_up", "down", "combine")
 
@@ -206,3 +212,30 @@ def moe_mxfp4_ffn(x: torch.Tensor, ids: torch.Tensor, weights: torch.Tensor, w1:
             handles[i] = None if ev is None else ev.cuda_event
         _check("moe_mxfp4_ffn_profiled", lib.moe_mxfp4_ffn_profiled(*args, handles))
     return out
+
+
+def moe_group_workspace_size(T: int, E: int, k: int) -> int:
+    return int(lib.moe_group_workspace_size(T, E, k))
+
+
+def moe_group_by_expert(ids: torch.Tensor, E: int, workspace: torch.Tensor | None = None):
+    """Grouping of routed entries by expert. ids int32 [T, k].
+
+    Returns (counts int32 [E], offsets int32 [E + 1], row_tok int32 [T * k],
+    slot_row int32 [T * k]); row_tok is meaningful up to offsets[E] (its later
+    entries are zero here)."""
+    _dev(ids, "ids", torch.int32)
+    T, k = ids.shape
+    dev = ids.device
+    counts = torch.zeros(E, dtype=torch.int32, device=dev)
+    offsets = torch.zeros(E + 1, dtype=torch.int32, device=dev)
+    row_tok = torch.zeros(T * k, dtype=torch.int32, device=dev)
+    slot_row = torch.zeros(T * k, dtype=torch.int32, device=dev)
+    need = moe_group_workspace_size(T, E, k)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _dev(workspace, "workspace", torch.uint8)
+    _check("moe_group_by_expert", lib.moe_group_by_expert(_ptr(ids), T, E, k, _ptr(counts), _ptr(offsets),
+                                                          _ptr(row_tok), _ptr(slot_row), _ptr(workspace),
+                                                          workspace.numel(), _stream(dev)))
+    return counts, offsets, row_tok, slot_row

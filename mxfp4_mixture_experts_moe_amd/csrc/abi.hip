@@ -36,6 +36,26 @@ FfnWorkspace ffn_workspace_layout(int64_t T, int32_t D, int32_t I, int32_t E, in
   return w;
 }
 
+GroupWorkspace group_workspace_layout(int64_t T, int32_t E, int32_t k) {
+  GroupWorkspace w{};
+  const int64_t entries = T * (int64_t)k;
+  const int64_t active = entries < E ? entries : E;
+  w.max_tiles = entries / kGroupTileRows + active;
+  w.n_chunks = (T + kChunkTokens - 1) / kChunkTokens;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off = align_up(off + bytes, 256);
+    return at;
+  };
+  w.tile_count = take(kTileLists * sizeof(int32_t));
+  for (int L = 0; L < kTileLists; ++L) w.tiles[L] = take(sizeof(Tile) * (size_t)(w.max_tiles > 0 ? w.max_tiles : 1));
+  w.chunk_base = take(sizeof(int32_t) * (size_t)(w.n_chunks * E));
+  w.chunk_mask = take(sizeof(unsigned long long) * (size_t)(w.n_chunks * E));
+  w.total = off;
+  return w;
+}
+
 }  // namespace k3moe
 
 using namespace k3moe;
@@ -142,12 +162,18 @@ int moe_mxfp4_ffn_profiled(const void* x_bf16, const int32_t* topk_ids, const fl
   // for the others (HBM-bound).  A batch of at most kStreamMaxRows tokens
   // cannot give an expert more rows (an id repeated within a token is
   // skipped), so it launches only the streaming kernels.  Other shapes use
-  // the general small-tile GEMMs for every expert.
+  // the general small-tile GEMMs for every expert.  Batches of up to
+  // kStreamOnlyTokens tokens send every expert to the streaming kernels (an
+  // expert with more than kStreamMaxRows rows takes several streaming tiles,
+  // whose repeated weight reads mostly hit the caches), so decode steps skip
+  // the large-tile launches.
   constexpr int kStreamMaxRows = 4;
+  constexpr int kStreamOnlyTokens = 8;
   const bool offsets_fit = entries * (int64_t)(I > D ? I : D) * 2 < ((int64_t)1 << 31);
   const bool tiled = big_gemm_supported(D, I) && stream_gemm_supported(D, I) && offsets_fit;
-  const bool big_lists = !tiled || T > kStreamMaxRows;  // lists 0/1 may hold tiles
-  const bool stream_lists = tiled;                      // lists 2/3 may hold tiles
+  const bool stream_only = tiled && T <= kStreamOnlyTokens;
+  const bool big_lists = !tiled || !stream_only;  // lists 0/1 may hold tiles
+  const bool stream_lists = tiled;                // lists 2/3 may hold tiles
   const int rpt_small = choose_rows_per_tile(T, k, E);
 
   GroupArgs g{};
@@ -161,7 +187,7 @@ int moe_mxfp4_ffn_profiled(const void* x_bf16, const int32_t* topk_ids, const fl
   g.rows_per_tile[1] = tiled ? big_rows_per_tile(false) : rpt_small;
   g.rows_per_tile[2] = stream_rows_per_tile(true);
   g.rows_per_tile[3] = stream_rows_per_tile(false);
-  g.split_rows = tiled ? kStreamMaxRows : 0;
+  g.split_rows = tiled ? (stream_only ? kStreamOnlyTokens : kStreamMaxRows) : 0;
   g.counts = reinterpret_cast<int32_t*>(ws + L.counts);
   g.offsets = reinterpret_cast<int32_t*>(ws + L.offsets);
   g.tile_count = reinterpret_cast<int32_t*>(ws + L.tile_count);
@@ -217,7 +243,8 @@ int moe_mxfp4_ffn_profiled(const void* x_bf16, const int32_t* topk_ids, const fl
   if (stream_lists) {
     gu.tiles = g.tiles[2];
     gu.tile_count = g.tile_count + 2;
-    gu.max_tiles = active;  // at most kStreamMaxRows rows each: one 4-row tile per expert
+    const int64_t r = g.rows_per_tile[2];
+    gu.max_tiles = (entries + (r - 1) * active) / r;  // bounds the sum of ceil(n_e / r) over experts
     err = launch_stream_gate_up(gu, s);
     if (err != hipSuccess) return K3MOE_ERR_DEVICE;
   }
@@ -234,7 +261,8 @@ int moe_mxfp4_ffn_profiled(const void* x_bf16, const int32_t* topk_ids, const fl
   if (stream_lists) {
     dn.tiles = g.tiles[3];
     dn.tile_count = g.tile_count + 3;
-    dn.max_tiles = (entries + active + 1) / 2;  // sum of ceil(n_e / 2) over experts
+    const int64_t r = g.rows_per_tile[3];
+    dn.max_tiles = (entries + (r - 1) * active) / r;  // bounds the sum of ceil(n_e / r) over experts
     err = launch_stream_down(dn, s);
     if (err != hipSuccess) return K3MOE_ERR_DEVICE;
   }
@@ -243,6 +271,51 @@ int moe_mxfp4_ffn_profiled(const void* x_bf16, const int32_t* topk_ids, const fl
   err = launch_combine(reinterpret_cast<const float*>(ws + L.y), g.slot_row, topk_w, T, D, k, out, s);
   if (err != hipSuccess || !mark(4)) return K3MOE_ERR_DEVICE;
   return K3MOE_OK;
+}
+
+static int group_shape_status(int64_t T, int32_t E, int32_t k) {
+  if (T < 0 || E < 1 || E > K3MOE_MAX_EXPERTS_FFN || k < 1 || k > K3MOE_MAX_TOPK) return K3MOE_ERR_SHAPE;
+  if (T * (int64_t)k > 0x7FFFFFFF) return K3MOE_ERR_SHAPE;
+  return K3MOE_OK;
+}
+
+size_t moe_group_workspace_size(int64_t T, int32_t E, int32_t k) {
+  if (group_shape_status(T, E, k) != K3MOE_OK || T == 0) return 0;
+  return group_workspace_layout(T, E, k).total;
+}
+
+int moe_group_by_expert(const int32_t* topk_ids, int64_t T, int32_t E, int32_t k, int32_t* counts, int32_t* offsets,
+                        int32_t* row_tok, int32_t* slot_row, void* workspace, size_t workspace_bytes, void* stream) {
+  const int st = group_shape_status(T, E, k);
+  if (st != K3MOE_OK) return st;
+  if (T == 0) return K3MOE_OK;
+  if (!topk_ids || !counts || !offsets || !row_tok || !slot_row || !workspace) return K3MOE_ERR_NULL;
+  if (misaligned(topk_ids) || misaligned(counts) || misaligned(offsets) || misaligned(row_tok) ||
+      misaligned(slot_row) || misaligned(workspace))
+    return K3MOE_ERR_ALIGN;
+  const GroupWorkspace L = group_workspace_layout(T, E, k);
+  if (workspace_bytes < L.total) return K3MOE_ERR_WORKSPACE;
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  GroupArgs g{};
+  g.ids = topk_ids;
+  g.x = nullptr;  // D == 0: no activation re-layout
+  g.T = T;
+  g.D = 0;
+  g.E = E;
+  g.k = k;
+  // every expert in lists 0/1, cut into tiles of kGroupTileRows rows
+  for (int l = 0; l < kTileLists; ++l) g.rows_per_tile[l] = kGroupTileRows;
+  g.split_rows = 0;
+  g.counts = counts;
+  g.offsets = offsets;
+  g.tile_count = reinterpret_cast<int32_t*>(ws + L.tile_count);
+  for (int l = 0; l < kTileLists; ++l) g.tiles[l] = reinterpret_cast<Tile*>(ws + L.tiles[l]);
+  g.row_tok = row_tok;
+  g.slot_row = slot_row;
+  g.chunk_base = reinterpret_cast<int32_t*>(ws + L.chunk_base);
+  g.chunk_mask = reinterpret_cast<unsigned long long*>(ws + L.chunk_mask);
+  g.x_perm = nullptr;
+  return device_status(launch_group(g, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

@@ -35,6 +35,17 @@ struct FfnWorkspace {
 
 FfnWorkspace ffn_workspace_layout(int64_t T, int32_t D, int32_t I, int32_t E, int32_t k);
 
+// Workspace of the stand-alone grouping call (tile lists and chunk tables; the
+// caller's buffers receive counts, offsets, row_tok and slot_row).  Its tile
+// lists use one tile height for every expert.
+constexpr int kGroupTileRows = 64;
+struct GroupWorkspace {
+  size_t tile_count, tiles[kTileLists], chunk_base, chunk_mask;
+  size_t total;
+  int64_t max_tiles, n_chunks;
+};
+GroupWorkspace group_workspace_layout(int64_t T, int32_t E, int32_t k);
+
 // ---------------------------------------------------------------------------
 // Launchers (host side; enqueue only, return the hipError_t of the launch).
 hipError_t launch_route_topk(const float* z, const float* bias, int64_t T, int E, int k, int normalize,

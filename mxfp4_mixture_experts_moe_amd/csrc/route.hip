@@ -1,4 +1,5 @@
-// Sigmoid + bias top-k router (one 64-lane wavefront per token).
+// Sigmoid + bias top-k router (one 64-lane wavefront per token; four per
+// token for batches of up to 256 tokens).
 //
 // Routing parameters from the llama.cpp pull request "model: add Kimi-K3 text
 // model", converter dry-run comment: 896 experts, 16 used, sigmoid expert
@@ -11,7 +12,9 @@
 // best remaining one is its "head".  Each of the k rounds reduces the 64 heads
 // to the wave's best (four DPP exchanges inside each 16-lane row, two row
 // swaps across rows); only the lane that owned the winner moves to its next
-// expert.  Larger E falls back to a kernel that writes the scores to LDS (or
+// expert.  Small batches split each token over a workgroup of four waves
+// (each finds the k best of a quarter of the experts; one wave orders the
+// candidates).  Larger E falls back to a kernel that writes the scores to LDS (or
 // recomputes them) and, in round r, picks the best expert ranking strictly
 // after round r-1's pick; it needs no "taken" flags, so nothing limits E.
 #include "k3moe_internal.h"
@@ -186,6 +189,115 @@ __global__ __launch_bounds__(256) void route_topk_reg_kernel(const float* __rest
   }
 }
 
+// Small batches: one workgroup of four waves per token, so the fp64 scoring
+// and the rounds of one token run on four SIMDs at once.  Thread i scores
+// experts i, i + 256, i + 512, ... (NPER of them, E <= 256 * NPER); each wave
+// takes the k best of its share by the rounds above (k <= 16) and leaves them
+// in LDS; wave 0 then holds the 4k candidates, one per lane (sentinels in the
+// rest), and orders them with a bitonic network across the wave.  The union
+// of the four per-wave top-k lists holds the token's top-k, so lanes 0..k-1
+// end with the same ids, in the same order, as the one-wave kernel.
+template <int NPER>
+__global__ __launch_bounds__(256) void route_topk_blk_kernel(const float* __restrict__ z, const float* __restrict__ bias,
+                                                              int E, int k, int normalize, float route_scale,
+                                                              int32_t* __restrict__ ids, float* __restrict__ w) {
+  constexpr int kBlkWaves = 4, kMaxK = kWaveSize / kBlkWaves;
+  __shared__ double cand_s[kBlkWaves * kMaxK];
+  __shared__ int cand_e[kBlkWaves * kMaxK];
+  __shared__ float zl[4 * 256];  // the token's logits, for the gate weights
+  const int tid = threadIdx.x, lane = tid & (kWaveSize - 1), wave = tid / kWaveSize;
+  const int64_t t = blockIdx.x;
+  const float* zt = z + t * (int64_t)E;
+
+  float zv[NPER], bv[NPER];
+#pragma unroll
+  for (int j = 0; j < NPER; ++j) zv[j] = zt[min(tid + 256 * j, E - 1)];
+#pragma unroll
+  for (int j = 0; j < NPER; ++j) bv[j] = bias ? bias[min(tid + 256 * j, E - 1)] : 0.0f;
+  double sc[NPER];
+  int ix[NPER];
+#pragma unroll
+  for (int j = 0; j < NPER; ++j) {
+    const int e = tid + 256 * j;
+    if (e < E) zl[e] = zv[j];
+    sc[j] = e < E ? route_score(zv[j], bv[j]) : -INFINITY;
+    ix[j] = e < E ? e : INT_MAX;
+  }
+  sort_desc<NPER>(sc, ix);
+
+  // k rounds over this wave's share.  Expert e sits in lane e % 64 of its
+  // wave; a sentinel winner (a share with fewer than k experts) only shifts
+  // sentinels.
+  double my_s = -INFINITY;
+  int my_e = INT_MAX;
+  for (int r = 0; r < k; ++r) {
+    double bs = sc[0];
+    int be = ix[0];
+    wave_best(bs, be, lane);
+    if (lane == r) {
+      my_s = bs;
+      my_e = be;
+    }
+    if (lane == (be & (kWaveSize - 1))) {
+#pragma unroll
+      for (int j = 0; j + 1 < NPER; ++j) {
+        sc[j] = sc[j + 1];
+        ix[j] = ix[j + 1];
+      }
+      sc[NPER - 1] = -INFINITY;
+      ix[NPER - 1] = INT_MAX;
+    }
+  }
+  if (lane < k) {
+    cand_s[wave * k + lane] = my_s;
+    cand_e[wave * k + lane] = my_e;
+  }
+  __syncthreads();
+  if (wave != 0) return;
+
+  double cs = -INFINITY;
+  int ce = INT_MAX;
+  if (lane < kBlkWaves * k) {
+    cs = cand_s[lane];
+    ce = cand_e[lane];
+  }
+  // Bitonic sort of the 64 lanes' candidates, first-ranked in lane 0.  The
+  // candidates are distinct experts or identical sentinels, so "ranks
+  // before" is a strict order on them.
+#pragma unroll
+  for (int size = 2; size <= kWaveSize; size <<= 1) {
+#pragma unroll
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      const double os = __shfl_xor(cs, stride, kWaveSize);
+      const int oe = __shfl_xor(ce, stride, kWaveSize);
+      // In a run sorted first-ranked-first the lower lane of each pair keeps
+      // the earlier-ranked candidate; runs with bit `size` set sort the other
+      // way (the last run, size 64, sorts first-ranked-first).
+      const bool keep_first = ((lane & stride) == 0) == ((lane & size) == 0);
+      const bool take = keep_first ? ranks_before(os, oe, cs, ce) : ranks_before(cs, ce, os, oe);
+      if (take) {
+        cs = os;
+        ce = oe;
+      }
+    }
+  }
+
+  const int my_id = ce;
+  double g = 0.0;
+  if (lane < k) g = 1.0 / (1.0 + exp(-(double)zl[my_id]));
+  double sum = g;
+  if (normalize) {
+    sum = 0.0;
+    for (int r = 0; r < k; ++r) sum += __shfl(g, r, kWaveSize);
+  }
+  if (lane < k) {
+    double v = normalize ? g / sum : g;
+    v = v * (double)route_scale;
+    ids[t * k + lane] = my_id;
+    w[t * k + lane] = (float)v;
+  }
+}
+
 template <bool kScoresInLds>
 __global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict__ z, const float* __restrict__ bias,
                                                           int64_t T, int E, int k, int normalize, float route_scale,
@@ -255,6 +367,20 @@ __global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict
 
 hipError_t launch_route_topk(const float* z, const float* bias, int64_t T, int E, int k, int normalize,
                              float route_scale, int32_t* ids, float* w, hipStream_t s) {
+  // Up to kBlockRouteTokens tokens the GPU has more SIMDs than the one-wave
+  // kernel has waves, so a token's latency is the whole cost: four waves per
+  // token cut it.
+  constexpr int64_t kBlockRouteTokens = 256;
+  if (T <= kBlockRouteTokens && E <= 4 * 256 && k <= 16) {
+#define K3_ROUTE_BLK(NP)                                                                                        \
+  hipLaunchKernelGGL(route_topk_blk_kernel<NP>, dim3((unsigned)T), dim3(256), 0, s, z, bias, E, k, normalize, \
+                     route_scale, ids, w)
+    if (E <= 256) K3_ROUTE_BLK(1);
+    else if (E <= 512) K3_ROUTE_BLK(2);
+    else K3_ROUTE_BLK(4);
+#undef K3_ROUTE_BLK
+    return hipGetLastError();
+  }
   if (E <= 16 * kWaveSize) {
     const int64_t blocks = (T + 3) / 4;
 #define K3_ROUTE(NP)                                                                                            \

@@ -24,7 +24,8 @@ def declared_functions():
 def test_library_exports_every_declared_symbol(k3):
     names = declared_functions()
     assert set(names) == {"k3moe_status_str", "moe_route_topk", "mxfp4_repack", "mxfp4_dequant",
-                          "moe_mxfp4_ffn_workspace_size", "moe_mxfp4_ffn", "moe_mxfp4_ffn_profiled"}
+                          "moe_mxfp4_ffn_workspace_size", "moe_mxfp4_ffn", "moe_mxfp4_ffn_profiled",
+                          "moe_group_workspace_size", "moe_group_by_expert"}
     for n in names:
         assert hasattr(k3.lib, n), n
 
@@ -100,3 +101,33 @@ def test_workspace_size(k3):
     # at least h (bf16) + y (fp32) + the re-laid-out activations
     assert b >= T * k * I * 2 + T * k * D * 4 + T * D * 2
     assert b % 256 == 0
+
+
+def group(k3, T=8, E=8, k=2, ws_bytes=None, **ptrs):
+    p = dict(ids=A, counts=A, offsets=A, row_tok=A, slot_row=A, ws=A)
+    p.update(ptrs)
+    if ws_bytes is None:
+        ws_bytes = k3.moe_group_workspace_size(T, E, k)
+    return k3.lib.moe_group_by_expert(p["ids"], T, E, k, p["counts"], p["offsets"], p["row_tok"], p["slot_row"],
+                                      p["ws"], ws_bytes, None)
+
+
+def test_group_checks(k3):
+    assert group(k3, E=0) == ERR_SHAPE
+    assert group(k3, E=8193) == ERR_SHAPE
+    assert group(k3, k=0) == ERR_SHAPE
+    assert group(k3, k=65) == ERR_SHAPE
+    assert group(k3, T=-1) == ERR_SHAPE
+    assert group(k3, T=2**31, k=1) == ERR_SHAPE  # T * k must stay below 2^31
+    assert group(k3, T=0, ids=None, counts=None, offsets=None, row_tok=None, slot_row=None, ws=None,
+                 ws_bytes=0) == OK
+    assert group(k3, slot_row=None) == ERR_NULL
+    assert group(k3, ws=None) == ERR_NULL
+    assert group(k3, offsets=A + 4) == ERR_ALIGN
+    need = k3.moe_group_workspace_size(8, 8, 2)
+    assert need > 0 and need % 256 == 0
+    assert group(k3, ws_bytes=need - 1) == ERR_WORKSPACE
+    gw = k3.moe_group_workspace_size
+    assert gw(0, 896, 16) == 0 and gw(4, 0, 16) == 0
+    # chunk tables: one 64-bit token bitmap and one base per (64-token chunk, expert)
+    assert gw(4096, 896, 16) >= 64 * 896 * 12

@@ -74,6 +74,9 @@ def test_tiny(k3):
         (16, 4, 1024, 512, 16),  # streaming path: ~4 rows per expert, experts split over 4-row tiles
         (32, 8, 1536, 1024, 3),  # streaming path: 3 K stages (gate/up), 2 (down)
         (896, 16, 512, 1024, 1),  # streaming path: one token, 16 experts of 896
+        (4, 2, 512, 512, 8),  # streaming-only batch: experts of up to 8 rows over several 4- and 2-row tiles
+        (3, 3, 512, 1024, 5),  # streaming-only batch: every expert has all 5 rows
+        (4, 2, 512, 512, 9),  # one token past the streaming-only batch: large-tile kernels for experts of 5+ rows
     ],
 )
 def test_shapes(k3, E, k, D, I, T):

@@ -52,6 +52,20 @@ def test_expert_counts(k3, E, k):
     check(k3, z, b, k, what=f"E={E} k={k}")
 
 
+@pytest.mark.parametrize("T", [1, 7, 256, 257])
+@pytest.mark.parametrize("E,k", [(8, 3), (200, 16), (256, 16), (257, 5), (513, 16), (896, 16), (1024, 16), (896, 17)])
+def test_small_batch_router(k3, T, E, k):
+    """Up to 256 tokens (E <= 1024, k <= 16) a workgroup of four waves routes each
+    token; shares of fewer than k experts (E = 8, E = 200) leave sentinels among
+    the candidates.  T = 257 and k = 17 take the one-wave-per-token kernel."""
+    g = np.random.default_rng(1000 * T + E + k)
+    z = g.standard_normal((T, E)).astype(np.float32)
+    b = (g.standard_normal(E) * 0.5).astype(np.float32)
+    check(k3, z, b, k, what=f"T={T} E={E} k={k}")
+    z[:, ::3] = 0.25  # exact ties across the four waves' shares
+    check(k3, z, None, k, what=f"T={T} E={E} k={k} ties")
+
+
 def test_ties_nan_and_options(k3):
     z = np.zeros((5, 40), np.float32)
     check(k3, z, np.zeros(40, np.float32), 7, what="all equal")
