@@ -24,6 +24,14 @@ namespace {
 
 constexpr int kScanThreads = 1024;
 constexpr int kMaxExpertsPerScanThread = 8;  // 8 * 1024 = K3MOE_MAX_EXPERTS_FFN
+constexpr int kPermBatch = 8;                // row re-layout work items per thread with loads in flight
+
+// Workgroup barrier for LDS traffic only.  __syncthreads() also waits for every
+// outstanding global load and store of the wave (its release fence), which
+// would put the latency of stores nobody in the workgroup reads on the
+// critical path; no wave here reads global memory another wave of the same
+// workgroup wrote.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 __device__ __forceinline__ bool entry_expert(const int32_t* ids_t, int j, int E, int& e_out) {
   const int e = ids_t[j];
@@ -39,7 +47,7 @@ __device__ __forceinline__ void build_masks(const int32_t* __restrict__ ids, int
                             unsigned long long* mask) {
   const int tid = threadIdx.x, nthr = blockDim.x;
   for (int e = tid; e < E; e += nthr) mask[e] = 0ull;
-  __syncthreads();
+  lds_barrier();
   const int64_t t0 = c * kChunkTokens;
   for (int idx = tid; idx < kChunkTokens * k; idx += nthr) {
     const int tl = idx / k, j = idx - tl * k;
@@ -47,7 +55,7 @@ __device__ __forceinline__ void build_masks(const int32_t* __restrict__ ids, int
     int e;
     if (t < T && entry_expert(ids + t * k, j, E, e)) atomicOr(&mask[e], 1ull << tl);
   }
-  __syncthreads();
+  lds_barrier();
 }
 
 // Block-wide exclusive scan of N ints per thread (blockDim.x == 1024): v[i]
@@ -69,7 +77,7 @@ __device__ __forceinline__ void block_exclusive_scan_n(int (&v)[N], int (&total)
   if (lane == 63)
 #pragma unroll
     for (int i = 0; i < N; ++i) wave_tot[wave][i] = incl[i];
-  __syncthreads();
+  lds_barrier();
 #pragma unroll
   for (int i = 0; i < N; ++i) {
     int before = 0, tot = 0;
@@ -81,7 +89,7 @@ __device__ __forceinline__ void block_exclusive_scan_n(int (&v)[N], int (&total)
     v[i] = before + incl[i] - v[i];
     total[i] = tot;
   }
-  __syncthreads();  // wave_tot may be reused by the next call
+  lds_barrier();  // wave_tot may be reused by the next call
 }
 
 // Tile lists.  An expert with more than split_rows rows goes to lists 0
@@ -196,28 +204,52 @@ __device__ __forceinline__ void place_entries(const int32_t* __restrict__ ids, i
 // p = 8i + 2t + h holds element 16h + 4i + t (i, t in 0..3, h in 0..1).  This
 // is the order in which the GEMM decodes a block's nibble pairs (qs byte j
 // holds elements j and j+16), so both MFMA operands see the same K order.
-__device__ __forceinline__ void perm_group(const uint16_t* __restrict__ xrow, uint16_t* __restrict__ prow, int g) {
-  const int b = g >> 2, i = g & 3;
-  const uint2 lo = *reinterpret_cast<const uint2*>(xrow + 32 * b + 4 * i);
-  const uint2 hi = *reinterpret_cast<const uint2*>(xrow + 32 * b + 16 + 4 * i);
-  uint4 o;
-  o.x = __builtin_amdgcn_perm(hi.x, lo.x, 0x05040100u);  // elements 4i,   16+4i
-  o.y = __builtin_amdgcn_perm(hi.x, lo.x, 0x07060302u);  // elements 4i+1, 17+4i
-  o.z = __builtin_amdgcn_perm(hi.y, lo.y, 0x05040100u);  // elements 4i+2, 18+4i
-  o.w = __builtin_amdgcn_perm(hi.y, lo.y, 0x07060302u);  // elements 4i+3, 19+4i
-  *reinterpret_cast<uint4*>(prow + 8 * g) = o;
-}
-
-__device__ __forceinline__ void permute_chunk_rows(const uint16_t* __restrict__ x, uint16_t* __restrict__ xp, int64_t T, int D,
-                                   int64_t c) {
-  const int groups = D / 8;
-  const int64_t t0 = c * kChunkTokens;
-  const int64_t nt = (T - t0) < kChunkTokens ? (T - t0) : kChunkTokens;
-  for (int64_t idx = threadIdx.x; idx < nt * groups; idx += blockDim.x) {
-    const int64_t tl = idx / groups;
-    const int g = (int)(idx - tl * groups);
-    const int64_t t = t0 + tl;
-    perm_group(x + t * D, xp + t * D, g);
+//
+// Re-layout of the rows [t0, t0 + nt) of x into xp; this thread takes work
+// items idx0, idx0 + stride, ... (item = one 8-element group of a row; idx0
+// and stride are below 2^31).  The loads of kPermBatch items are issued before
+// the first store, so a thread waits for one memory round trip per batch, not
+// per item.  Items past the end are clamped onto the last one, which is then
+// written more than once with the same bytes: no branch around the loads.
+// The (row, group) of an item is stepped along, not divided out per item.
+__device__ __forceinline__ void permute_rows(const uint16_t* __restrict__ x, uint16_t* __restrict__ xp, int64_t t0,
+                                             int64_t nt, int D, uint32_t idx0, uint32_t stride) {
+  const uint32_t groups = (uint32_t)D / 8;
+  if (groups == 0 || nt <= 0) return;
+  const int64_t total = nt * groups;
+  const uint32_t drow = stride / groups, dg = stride % groups;
+  int64_t idx = idx0, row = t0 + idx0 / groups;
+  uint32_t g = idx0 % groups;
+  while (idx < total) {
+    uint2 lo[kPermBatch], hi[kPermBatch];
+    int64_t rows[kPermBatch];
+    uint32_t grp[kPermBatch];
+#pragma unroll
+    for (int u = 0; u < kPermBatch; ++u) {
+      const bool in = idx < total;
+      rows[u] = in ? row : t0 + nt - 1;
+      grp[u] = in ? g : groups - 1;
+      const uint16_t* xrow = x + rows[u] * D;
+      const uint32_t b = grp[u] >> 2, i = grp[u] & 3;
+      lo[u] = *reinterpret_cast<const uint2*>(xrow + 32 * b + 4 * i);
+      hi[u] = *reinterpret_cast<const uint2*>(xrow + 32 * b + 16 + 4 * i);
+      idx += stride;
+      row += drow;
+      g += dg;
+      if (g >= groups) {
+        g -= groups;
+        ++row;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kPermBatch; ++u) {
+      uint4 o;
+      o.x = __builtin_amdgcn_perm(hi[u].x, lo[u].x, 0x05040100u);  // elements 4i,   16+4i
+      o.y = __builtin_amdgcn_perm(hi[u].x, lo[u].x, 0x07060302u);  // elements 4i+1, 17+4i
+      o.z = __builtin_amdgcn_perm(hi[u].y, lo[u].y, 0x05040100u);  // elements 4i+2, 18+4i
+      o.w = __builtin_amdgcn_perm(hi[u].y, lo[u].y, 0x07060302u);  // elements 4i+3, 19+4i
+      *reinterpret_cast<uint4*>(xp + rows[u] * D + 8 * grp[u]) = o;
+    }
   }
 }
 
@@ -252,7 +284,7 @@ __global__ __launch_bounds__(kScanThreads) void group_scan_kernel(GroupArgs a, i
     for (; c < n_chunks; ++c) sum += a.chunk_base[c * E + e];
     ltot[e] = sum;
   }
-  __syncthreads();
+  lds_barrier();
   // offsets and tiles: thread t owns experts 8t..8t+7
   const TileSpec ts = tile_spec(a);
   const int e0 = tid * kMaxExpertsPerScanThread;
@@ -275,7 +307,7 @@ __global__ __launch_bounds__(kScanThreads) void group_scan_kernel(GroupArgs a, i
     v[0] += cnt;
   }
   if (tid == 0) write_totals(a, E, total);
-  __syncthreads();
+  lds_barrier();
   // bases: expert-parallel running sums over the chunks (loads kept in flight)
   for (int e = tid; e < E; e += kScanThreads) {
     int run = ltot[e];
@@ -320,13 +352,8 @@ __global__ __launch_bounds__(256) void group_place_kernel(GroupArgs a) {
     }
     a.slot_row[t * a.k + j] = row;
   }
-  const int groups = a.D / 8;
   const int64_t nt = (a.T - t0) < kChunkTokens ? (a.T - t0) : kChunkTokens;
-  for (int64_t idx = part * blockDim.x + threadIdx.x; idx < nt * groups; idx += kPlaceParts * blockDim.x) {
-    const int64_t tl = idx / groups;
-    const int g = (int)(idx - tl * groups);
-    perm_group(a.x + (t0 + tl) * a.D, a.x_perm + (t0 + tl) * a.D, g);
-  }
+  permute_rows(a.x, a.x_perm, t0, nt, a.D, part * blockDim.x + threadIdx.x, kPlaceParts * blockDim.x);
 }
 
 // All phases for a batch of at most one chunk (T <= 64), one launch.
@@ -336,15 +363,15 @@ __global__ __launch_bounds__(kScanThreads) void group_fused_kernel(GroupArgs a) 
   int32_t* lbase = reinterpret_cast<int32_t*>(lmask + a.E);
   build_masks(a.ids, a.T, a.k, a.E, 0, lmask);
   scan_experts(a, lmask, 1, lbase);
-  __syncthreads();
+  lds_barrier();
   place_entries(a.ids, a.T, a.k, a.E, 0, lmask, lbase, a.row_tok, a.slot_row);
-  permute_chunk_rows(a.x, a.x_perm, a.T, a.D, 0);
+  permute_rows(a.x, a.x_perm, 0, a.T, a.D, threadIdx.x, blockDim.x);
 }
 
 // All phases for a batch of at most 64 tokens and 1024 entries (decode-sized),
-// one launch: thread i owns entry i for the whole kernel, the activation
-// re-layout is issued first (it does not depend on the ids), and one scan
-// yields row offsets and the tile lists.
+// one launch: thread i owns entry i for the whole kernel, one scan yields
+// row offsets and the tile lists, and the activation re-layout comes last,
+// where nothing waits for its stores.
 // LDS: E bitmaps (8 B) + E first rows (4 B).
 __global__ __launch_bounds__(kScanThreads) void group_small_kernel(GroupArgs a) {
   extern __shared__ unsigned long long lmask[];
@@ -353,10 +380,9 @@ __global__ __launch_bounds__(kScanThreads) void group_small_kernel(GroupArgs a) 
   const int tid = threadIdx.x, E = a.E, k = a.k;
   const int entries = (int)a.T * k;
   const int my = tid < entries ? a.ids[tid] : -1;
-  permute_chunk_rows(a.x, a.x_perm, a.T, a.D, 0);
   for (int i = tid; i < E; i += kScanThreads) lmask[i] = 0ull;
   lids[tid] = my;
-  __syncthreads();
+  lds_barrier();
   // skip ids outside [0, E) and repeats of an earlier slot of the same token
   int e = -1;
   if (tid < entries && my >= 0 && my < E) {
@@ -366,7 +392,7 @@ __global__ __launch_bounds__(kScanThreads) void group_small_kernel(GroupArgs a) 
     if (first) e = my;
   }
   if (e >= 0) atomicOr(&lmask[e], 1ull << (tid / k));
-  __syncthreads();
+  lds_barrier();
 
   const TileSpec ts = tile_spec(a);
   const int e0 = tid * kMaxExpertsPerScanThread;
@@ -389,7 +415,7 @@ __global__ __launch_bounds__(kScanThreads) void group_small_kernel(GroupArgs a) 
     v[0] += cnt;
   }
   if (tid == 0) write_totals(a, E, total);
-  __syncthreads();
+  lds_barrier();
   if (tid < entries) {
     const int t = tid / k;
     int32_t row = -1;
@@ -399,6 +425,7 @@ __global__ __launch_bounds__(kScanThreads) void group_small_kernel(GroupArgs a) 
     }
     a.slot_row[tid] = row;
   }
+  permute_rows(a.x, a.x_perm, 0, a.T, a.D, tid, kScanThreads);
 }
 
 }  // namespace
