@@ -24,7 +24,6 @@ namespace {
 
 constexpr int kScanThreads = 1024;
 constexpr int kMaxExpertsPerScanThread = 8;  // 8 * 1024 = K3MOE_MAX_EXPERTS_FFN
-constexpr int kPermBatch = 8;                // row re-layout work items per thread with loads in flight
 
 // Workgroup barrier for LDS traffic only.  __syncthreads() also waits for every
 // outstanding global load and store of the wave (its release fence), which
@@ -207,11 +206,12 @@ __device__ __forceinline__ void place_entries(const int32_t* __restrict__ ids, i
 //
 // Re-layout of the rows [t0, t0 + nt) of x into xp; this thread takes work
 // items idx0, idx0 + stride, ... (item = one 8-element group of a row; idx0
-// and stride are below 2^31).  The loads of kPermBatch items are issued before
+// and stride are below 2^31).  The loads of kBatch items are issued before
 // the first store, so a thread waits for one memory round trip per batch, not
 // per item.  Items past the end are clamped onto the last one, which is then
 // written more than once with the same bytes: no branch around the loads.
 // The (row, group) of an item is stepped along, not divided out per item.
+template <int kBatch>
 __device__ __forceinline__ void permute_rows(const uint16_t* __restrict__ x, uint16_t* __restrict__ xp, int64_t t0,
                                              int64_t nt, int D, uint32_t idx0, uint32_t stride) {
   const uint32_t groups = (uint32_t)D / 8;
@@ -221,11 +221,11 @@ __device__ __forceinline__ void permute_rows(const uint16_t* __restrict__ x, uin
   int64_t idx = idx0, row = t0 + idx0 / groups;
   uint32_t g = idx0 % groups;
   while (idx < total) {
-    uint2 lo[kPermBatch], hi[kPermBatch];
-    int64_t rows[kPermBatch];
-    uint32_t grp[kPermBatch];
+    uint2 lo[kBatch], hi[kBatch];
+    int64_t rows[kBatch];
+    uint32_t grp[kBatch];
 #pragma unroll
-    for (int u = 0; u < kPermBatch; ++u) {
+    for (int u = 0; u < kBatch; ++u) {
       const bool in = idx < total;
       rows[u] = in ? row : t0 + nt - 1;
       grp[u] = in ? g : groups - 1;
@@ -242,7 +242,7 @@ __device__ __forceinline__ void permute_rows(const uint16_t* __restrict__ x, uin
       }
     }
 #pragma unroll
-    for (int u = 0; u < kPermBatch; ++u) {
+    for (int u = 0; u < kBatch; ++u) {
       uint4 o;
       o.x = __builtin_amdgcn_perm(hi[u].x, lo[u].x, 0x05040100u);  // elements 4i,   16+4i
       o.y = __builtin_amdgcn_perm(hi[u].x, lo[u].x, 0x07060302u);  // elements 4i+1, 17+4i
@@ -269,17 +269,18 @@ __global__ __launch_bounds__(256) void group_count_kernel(GroupArgs a) {
 __global__ __launch_bounds__(kScanThreads) void group_scan_kernel(GroupArgs a, int64_t n_chunks) {
   extern __shared__ int32_t ltot[];  // [E] per-expert totals
   const int E = a.E, tid = threadIdx.x;
-  // totals: expert-parallel sums over the chunks, eight loads in flight (the
-  // loads of consecutive threads are consecutive in memory)
+  // totals: expert-parallel sums over the chunks, kScanLoads loads in flight
+  // (the loads of consecutive threads are consecutive in memory)
+  constexpr int kScanLoads = 8;
   for (int e = tid; e < E; e += kScanThreads) {
     int sum = 0;
     int64_t c = 0;
-    for (; c + 8 <= n_chunks; c += 8) {
-      int32_t v[8];
+    for (; c + kScanLoads <= n_chunks; c += kScanLoads) {
+      int32_t v[kScanLoads];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) v[u] = a.chunk_base[(c + u) * E + e];
+      for (int u = 0; u < kScanLoads; ++u) v[u] = a.chunk_base[(c + u) * E + e];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) sum += v[u];
+      for (int u = 0; u < kScanLoads; ++u) sum += v[u];
     }
     for (; c < n_chunks; ++c) sum += a.chunk_base[c * E + e];
     ltot[e] = sum;
@@ -312,12 +313,12 @@ __global__ __launch_bounds__(kScanThreads) void group_scan_kernel(GroupArgs a, i
   for (int e = tid; e < E; e += kScanThreads) {
     int run = ltot[e];
     int64_t c = 0;
-    for (; c + 8 <= n_chunks; c += 8) {
-      int32_t v[8];
+    for (; c + kScanLoads <= n_chunks; c += kScanLoads) {
+      int32_t v[kScanLoads];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) v[u] = a.chunk_base[(c + u) * E + e];
+      for (int u = 0; u < kScanLoads; ++u) v[u] = a.chunk_base[(c + u) * E + e];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
+      for (int u = 0; u < kScanLoads; ++u) {
         a.chunk_base[(c + u) * E + e] = run;
         run += v[u];
       }
@@ -353,7 +354,7 @@ __global__ __launch_bounds__(256) void group_place_kernel(GroupArgs a) {
     a.slot_row[t * a.k + j] = row;
   }
   const int64_t nt = (a.T - t0) < kChunkTokens ? (a.T - t0) : kChunkTokens;
-  permute_rows(a.x, a.x_perm, t0, nt, a.D, part * blockDim.x + threadIdx.x, kPlaceParts * blockDim.x);
+  permute_rows<8>(a.x, a.x_perm, t0, nt, a.D, part * blockDim.x + threadIdx.x, kPlaceParts * blockDim.x);
 }
 
 // All phases for a batch of at most one chunk (T <= 64), one launch.
@@ -365,7 +366,7 @@ __global__ __launch_bounds__(kScanThreads) void group_fused_kernel(GroupArgs a) 
   scan_experts(a, lmask, 1, lbase);
   lds_barrier();
   place_entries(a.ids, a.T, a.k, a.E, 0, lmask, lbase, a.row_tok, a.slot_row);
-  permute_rows(a.x, a.x_perm, 0, a.T, a.D, threadIdx.x, blockDim.x);
+  permute_rows<4>(a.x, a.x_perm, 0, a.T, a.D, threadIdx.x, blockDim.x);
 }
 
 // All phases for a batch of at most 64 tokens and 1024 entries (decode-sized),
@@ -425,7 +426,7 @@ __global__ __launch_bounds__(kScanThreads) void group_small_kernel(GroupArgs a) 
     }
     a.slot_row[tid] = row;
   }
-  permute_rows(a.x, a.x_perm, 0, a.T, a.D, tid, kScanThreads);
+  permute_rows<4>(a.x, a.x_perm, 0, a.T, a.D, tid, kScanThreads);
 }
 
 }  // namespace
