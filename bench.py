@@ -57,11 +57,14 @@ def gemm_path(cfg) -> str:
     return "small"
 
 
-def kernel_info(stage: str, path: str):
-    """(kernel name(s) as rocprofv3 reports them, source files) of a stage."""
+def kernel_info(stage: str, path: str, entries: int = 0):
+    """(kernel name(s) as rocprofv3 reports them, source files) of a stage.
+    The large-tile down product takes 128-row tiles from 16384 routed entries
+    on, 64-row tiles below."""
     if stage in ("gate_up", "down"):
         flag = "true" if stage == "gate_up" else "false"
-        big, stream = f"ffn_big_kernel<{flag}>", f"ffn_stream_kernel<{flag}>"
+        rows = 128 if stage == "gate_up" or entries >= 16384 else 64
+        big, stream = f"ffn_big_kernel<{flag}, {rows}>", f"ffn_stream_kernel<{flag}>"
         if path == "stream":
             return stream, [CSRC + "ffn_stream.hip"]
         if path == "tiled":
@@ -299,7 +302,7 @@ def main():
         achieved, peak, unit = flops / dur_s / 1e12, PEAK_BF16_TFLOPS, "TFLOP/s"
     else:
         achieved, peak, unit = byts / dur_s / 1e9, PEAK_HBM_GBS, "GB/s"
-    kname, ksrc = kernel_info(dom, gemm_path(cfg))
+    kname, ksrc = kernel_info(dom, gemm_path(cfg), cfg.T * cfg.k)
     traffic = stored_traffic(dom, args.workload, ksrc)
 
     value = cfg.T * steps / elapsed

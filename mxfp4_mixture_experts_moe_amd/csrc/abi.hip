@@ -175,6 +175,10 @@ int moe_mxfp4_ffn_profiled(const void* x_bf16, const int32_t* topk_ids, const fl
   const bool big_lists = !tiled || !stream_only;  // lists 0/1 may hold tiles
   const bool stream_lists = tiled;                // lists 2/3 may hold tiles
   const int rpt_small = choose_rows_per_tile(T, k, E);
+  // 128-row down tiles once the batch is large enough that the large-tile
+  // down product still has about four workgroups per CU with them
+  constexpr int64_t kWideDownEntries = 16384;
+  const bool wide_down = entries >= kWideDownEntries;
 
   GroupArgs g{};
   g.ids = topk_ids;
@@ -183,8 +187,8 @@ int moe_mxfp4_ffn_profiled(const void* x_bf16, const int32_t* topk_ids, const fl
   g.D = D;
   g.E = E;
   g.k = k;
-  g.rows_per_tile[0] = tiled ? big_rows_per_tile(true) : rpt_small;
-  g.rows_per_tile[1] = tiled ? big_rows_per_tile(false) : rpt_small;
+  g.rows_per_tile[0] = tiled ? big_rows_per_tile(true, false) : rpt_small;
+  g.rows_per_tile[1] = tiled ? big_rows_per_tile(false, wide_down) : rpt_small;
   g.rows_per_tile[2] = stream_rows_per_tile(true);
   g.rows_per_tile[3] = stream_rows_per_tile(false);
   g.split_rows = tiled ? (stream_only ? kStreamOnlyTokens : kStreamMaxRows) : 0;
@@ -255,7 +259,7 @@ int moe_mxfp4_ffn_profiled(const void* x_bf16, const int32_t* topk_ids, const fl
     dn.tiles = g.tiles[1];
     dn.tile_count = g.tile_count + 1;
     dn.max_tiles = entries / g.rows_per_tile[1] + big_experts;
-    err = tiled ? launch_big_down(dn, s) : launch_down(dn, rpt_small, s);
+    err = tiled ? launch_big_down(dn, wide_down, s) : launch_down(dn, rpt_small, s);
     if (err != hipSuccess) return K3MOE_ERR_DEVICE;
   }
   if (stream_lists) {

@@ -4,8 +4,10 @@
 // fp32 accumulation).  h leaves it as fp16 scaled by a power of two per
 // (row, 256-feature slice) — 11 significant bits where ffn.hip's bf16 hi + lo
 // pair needs two MFMAs per product — and the down product takes it with fp16
-// MFMAs (w2 blocks converted exactly to fp16), folding each slice's partial
-// sums into the fp32 accumulators with the slice's scale.
+// MFMAs (w2 blocks converted exactly to fp16): each slice of a row is first
+// multiplied by 2^(slice scale - row's largest slice scale), exact in fp16
+// except far below the row's largest values, so all slices accumulate into
+// one set of fp32 sums, which the epilogue multiplies by 2^(row scale).
 //
 // A workgroup of 8 waves owns an output tile of kF features x kN tokens of one
 // expert; each wave takes kF/8 features and all kN tokens, so every weight row
@@ -28,8 +30,9 @@
 //          32 features (one I-block) x 128 tokens for both matrices.  The MFMA
 //          rows are assigned so each lane's four outputs are four consecutive
 //          P-order positions of h (8-byte stores of the scaled fp16 h).
-// down:    kF = 512 features of w2, kN = 64 tokens; wave tile 64 x 64; the B
-//          operand is the scaled fp16 h.  If any w2 block of the tile has an
+// down:    kF = 512 features of w2, kN = 128 tokens (batches of at least
+//          16384 routed entries) or 64; wave tile 64 x kN; the B operand is
+//          the rescaled fp16 h.  If any w2 block of the tile has an
 //          exponent outside 104..140 (values fp16 cannot hold exactly), the
 //          workgroup redoes the tile with bf16 weights and h split into an
 //          exact bf16 pair (two MFMAs per operand).
@@ -63,14 +66,22 @@ constexpr int kARowChunks = 17; // 16-byte chunks per activation row (16 data + 
 constexpr int kXcds = 8;
 constexpr int kMaxSlices = 64;  // 256-wide slices of I the down kernel supports (I <= 16384)
 
-template <bool kGateUp>
+// kTok: token rows of a workgroup tile.  The down product has two: 128-row
+// tiles give a workgroup twice the matrix work between barriers (large
+// batches), 64-row tiles give twice as many workgroups (batches whose experts
+// have few rows, where the weight stream needs every CU).
+template <bool kGateUp, int kTok>
 struct BigCfg;
 template <>
-struct BigCfg<true> {  // wave: 2 row groups (32 features) x 8 token groups, 2 matrices
+struct BigCfg<true, 128> {  // wave: 2 row groups (32 features) x 8 token groups, 2 matrices
   static constexpr int kF = 256, kN = 128, kRG = 2, kTG = 8, kMats = 2, kSrc = 1;
 };
 template <>
-struct BigCfg<false> {  // wave: 4 row groups (64 features) x 4 token groups, scaled fp16 h
+struct BigCfg<false, 128> {  // wave: 4 row groups (64 features) x 8 token groups, scaled fp16 h
+  static constexpr int kF = 512, kN = 128, kRG = 4, kTG = 8, kMats = 1, kSrc = 1;
+};
+template <>
+struct BigCfg<false, 64> {  // wave: 4 row groups (64 features) x 4 token groups, scaled fp16 h
   static constexpr int kF = 512, kN = 64, kRG = 4, kTG = 4, kMats = 1, kSrc = 1;
 };
 
@@ -119,9 +130,9 @@ __device__ __forceinline__ int64_t xcd_logical(int64_t i, int64_t total) {
   return x * q + (x < r ? x : r) + j;
 }
 
-template <bool kGateUp>
+template <bool kGateUp, int kTok>
 __global__ __launch_bounds__(kThreads) void ffn_big_kernel(GemmArgs a) {
-  using C = BigCfg<kGateUp>;
+  using C = BigCfg<kGateUp, kTok>;
   // One array per buffer: the compiler can then tell that the buffer being
   // read is not the one the LDS-DMA loads in flight write.  With a single
   // array it makes every read of the current buffer wait for the loads just
@@ -129,6 +140,7 @@ __global__ __launch_bounds__(kThreads) void ffn_big_kernel(GemmArgs a) {
   __shared__ uint32_t lds0[kStageDw], lds1[kStageDw];
   __shared__ int32_t tok_src[C::kN];  // source row of every token slot of the tile
   __shared__ int8_t hs_l[kGateUp ? 1 : C::kN * kMaxSlices];  // down: h scale of every (row, slice)
+  __shared__ int srow_l[kGateUp ? 1 : C::kN];                 // down: largest h scale of every row
   __shared__ float red[kGateUp ? kThreads / 64 * C::kN : 1];   // gate/up: per-wave row maxima of |h|
   __shared__ int sexp[kGateUp ? C::kN : 1];                    // gate/up: h scale exponent per row
 
@@ -188,6 +200,15 @@ __global__ __launch_bounds__(kThreads) void ffn_big_kernel(GemmArgs a) {
     }
   }
   __syncthreads();
+  if constexpr (!kGateUp) {
+    if (tid < C::kN) {
+      const int nsl = K >> 8;
+      int mx = -128;
+      for (int sl = 0; sl < nsl; ++sl) mx = max(mx, (int)hs_l[tid * kMaxSlices + sl]);
+      srow_l[tid] = mx;
+    }
+    // read after the barrier that follows the first stage's loads
+  }
 
   // ---- per-lane load descriptors (constant over K) ----
   // All loads are buffer loads straight into LDS: an SGPR resource per source,
@@ -272,12 +293,26 @@ __global__ __launch_bounds__(kThreads) void ffn_big_kernel(GemmArgs a) {
     for (int rg = 0; rg < C::kRG; ++rg)
 #pragma unroll
       for (int tg = 0; tg < C::kTG; ++tg) acc[mi][rg][tg] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  // down: partial sums of the current 256-wide slice of h, still in its scale
-  f32x4_t part[kGateUp ? 1 : C::kRG][C::kTG];
+  // down: h of token group tg in the current 256-wide slice is brought from
+  // its slice scale to its row's largest scale by multiplying by hmul[tg] =
+  // 2^(slice scale - row scale) <= 1 (two equal fp16 halves), so every slice
+  // accumulates into the same fp32 sums, which the epilogue multiplies by
+  // 2^(row scale).  The products are exact unless they fall below fp16's
+  // normal range, i.e. below 2^-29 of the row's largest |h|.
+  uint32_t hmul[kGateUp ? 1 : C::kTG];
+  auto slice_mults = [&](int sl) {
 #pragma unroll
-  for (int rg = 0; rg < (kGateUp ? 1 : C::kRG); ++rg)
-#pragma unroll
-    for (int tg = 0; tg < C::kTG; ++tg) part[rg][tg] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int tg = 0; tg < (kGateUp ? 1 : C::kTG); ++tg) {
+      const int t = tg * 16 + rho;
+      const int d = (int)hs_l[t * kMaxSlices + sl] - srow_l[t];
+      const uint32_t hb = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)ldexpf(1.0f, d));
+      hmul[tg] = hb | (hb << 16);
+    }
+  };
+  auto scale_h = [&](f16x8_t v, int tg) {
+    const _Float16 m = __builtin_bit_cast(_Float16, (uint16_t)hmul[tg]);
+    return v * m;
+  };
 
   const int nstages = K / kKStep;
 
@@ -354,6 +389,7 @@ __global__ __launch_bounds__(kThreads) void ffn_big_kernel(GemmArgs a) {
         }
       }
     } else {
+      if constexpr ((PH & 1) == 0) slice_mults(s >> 1);  // the step opens a 256-wide slice of h
       // fp16 holds every w2 value of a block exactly when its exponent byte is
       // in 104..140.  The fp16 pass notes any other block; the workgroup then
       // redoes the tile with the exact pass.
@@ -370,7 +406,7 @@ __global__ __launch_bounds__(kThreads) void ffn_big_kernel(GemmArgs a) {
         for (int i = 0; i < 4; ++i) {
           auto bread = [&](int n) {
             const int row = n * 16 + rho;
-            return __builtin_bit_cast(f16x8_t, *reinterpret_cast<const uint4*>(al + row * kARowDw + 4 * (4 * g + i)));
+            return scale_h(__builtin_bit_cast(f16x8_t, *reinterpret_cast<const uint4*>(al + row * kARowDw + 4 * (4 * g + i))), n);
           };
           f16x8_t anext[C::kRG];
           f16x8_t bnext = bread(0);
@@ -381,7 +417,7 @@ __global__ __launch_bounds__(kThreads) void ffn_big_kernel(GemmArgs a) {
             if (n + 1 < kB && (kFull || n + 1 < nlive)) bnext = bread(n + 1);
 #pragma unroll
             for (int rg = 0; rg < C::kRG; ++rg)
-              part[rg][n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aop[rg], bop, part[rg][n], 0, 0, 0);
+              acc[0][rg][n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aop[rg], bop, acc[0][rg][n], 0, 0, 0);
             if (i + 1 < 4 && n < C::kRG) anext[n] = decode_dword_f16(q[0][n][i + 1], e8m0_to_f32(eb[0][n]));
             __builtin_amdgcn_sched_barrier(0);
           }
@@ -404,28 +440,15 @@ __global__ __launch_bounds__(kThreads) void ffn_big_kernel(GemmArgs a) {
             if (!kFull && n >= nlive) break;
             const int row = n * 16 + rho;
             bf16x8_t bhi, blo;
-            split_f16x8(*reinterpret_cast<const uint4*>(al + row * kARowDw + 4 * (4 * g + i)), bhi, blo);
+            const f16x8_t hv =
+                scale_h(__builtin_bit_cast(f16x8_t, *reinterpret_cast<const uint4*>(al + row * kARowDw + 4 * (4 * g + i))), n);
+            split_f16x8(__builtin_bit_cast(uint4, hv), bhi, blo);
 #pragma unroll
             for (int rg = 0; rg < C::kRG; ++rg) {
-              part[rg][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop[rg], bhi, part[rg][n], 0, 0, 0);
-              part[rg][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop[rg], blo, part[rg][n], 0, 0, 0);
+              acc[0][rg][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop[rg], bhi, acc[0][rg][n], 0, 0, 0);
+              acc[0][rg][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop[rg], blo, acc[0][rg][n], 0, 0, 0);
             }
             __builtin_amdgcn_sched_barrier(0);
-          }
-        }
-      }
-      if constexpr ((PH & 1) != 0) {
-        // the step closes a 256-wide slice of h: fold the slice's partial sums
-        // into the accumulators with the slice's scale (one per token column)
-        const int sl = s >> 1;
-#pragma unroll
-        for (int tg = 0; tg < C::kTG; ++tg) {
-          const float f = ldexpf(1.0f, (int)hs_l[(tg * 16 + rho) * kMaxSlices + sl]);
-#pragma unroll
-          for (int rg = 0; rg < C::kRG; ++rg) {
-#pragma unroll
-            for (int v = 0; v < 4; ++v) acc[0][rg][tg][v] = fmaf(part[rg][tg][v], f, acc[0][rg][tg][v]);
-            part[rg][tg] = f32x4_t{0.f, 0.f, 0.f, 0.f};
           }
         }
       }
@@ -527,11 +550,12 @@ __global__ __launch_bounds__(kThreads) void ffn_big_kernel(GemmArgs a) {
       if (m >= tile.nrows) continue;
       const int64_t row = tile.row0 + m;
       float* yrow = reinterpret_cast<float*>(a.out) + row * a.N;
+      const float sc = ldexpf(1.0f, srow_l[m]);  // h's row scale
 #pragma unroll
       for (int rg = 0; rg < C::kRG; ++rg) {
         const int f = f0 + 64 * wave + 16 * rg + 4 * g;
         *reinterpret_cast<float4*>(yrow + f) =
-            make_float4(acc[0][rg][tg][0], acc[0][rg][tg][1], acc[0][rg][tg][2], acc[0][rg][tg][3]);
+            make_float4(acc[0][rg][tg][0] * sc, acc[0][rg][tg][1] * sc, acc[0][rg][tg][2] * sc, acc[0][rg][tg][3] * sc);
       }
     }
   }
@@ -542,21 +566,28 @@ __global__ __launch_bounds__(kThreads) void ffn_big_kernel(GemmArgs a) {
 // Feature tiles must divide the outputs, and K must be a multiple of 4 steps
 // (512) so the last 80-byte weight window of a row ends exactly at the row end.
 bool big_gemm_supported(int D, int I) {
-  return (I % BigCfg<true>::kF) == 0 && (D % BigCfg<false>::kF) == 0 && (D % (4 * kKStep)) == 0 &&
+  return (I % BigCfg<true, 128>::kF) == 0 && (D % BigCfg<false, 128>::kF) == 0 && (D % (4 * kKStep)) == 0 &&
          (I % (4 * kKStep)) == 0 && I <= 256 * kMaxSlices;
 }
 
-int big_rows_per_tile(bool gate_up) { return gate_up ? BigCfg<true>::kN : BigCfg<false>::kN; }
+int big_rows_per_tile(bool gate_up, bool wide_down) {
+  return gate_up ? BigCfg<true, 128>::kN : wide_down ? BigCfg<false, 128>::kN : BigCfg<false, 64>::kN;
+}
 
 hipError_t launch_big_gate_up(const GemmArgs& a, hipStream_t s) {
-  const int64_t grid = a.max_tiles * (a.N / BigCfg<true>::kF);
-  hipLaunchKernelGGL(ffn_big_kernel<true>, dim3((unsigned)grid), dim3(kThreads), 0, s, a);
+  const int64_t grid = a.max_tiles * (a.N / BigCfg<true, 128>::kF);
+  hipLaunchKernelGGL((ffn_big_kernel<true, 128>), dim3((unsigned)grid), dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 
-hipError_t launch_big_down(const GemmArgs& a, hipStream_t s) {
-  const int64_t grid = a.max_tiles * (a.N / BigCfg<false>::kF);
-  hipLaunchKernelGGL(ffn_big_kernel<false>, dim3((unsigned)grid), dim3(kThreads), 0, s, a);
+hipError_t launch_big_down(const GemmArgs& a, bool wide, hipStream_t s) {
+  if (wide) {
+    const int64_t grid = a.max_tiles * (a.N / BigCfg<false, 128>::kF);
+    hipLaunchKernelGGL((ffn_big_kernel<false, 128>), dim3((unsigned)grid), dim3(kThreads), 0, s, a);
+  } else {
+    const int64_t grid = a.max_tiles * (a.N / BigCfg<false, 64>::kF);
+    hipLaunchKernelGGL((ffn_big_kernel<false, 64>), dim3((unsigned)grid), dim3(kThreads), 0, s, a);
+  }
   return hipGetLastError();
 }
 

@@ -97,9 +97,10 @@ hipError_t launch_gate_up(const GemmArgs& a, int rows_per_tile, hipStream_t s);
 hipError_t launch_down(const GemmArgs& a, int rows_per_tile, hipStream_t s);
 
 bool big_gemm_supported(int D, int I);
-int big_rows_per_tile(bool gate_up);
+// wide_down: the down product's 128-row tiles (else 64-row tiles)
+int big_rows_per_tile(bool gate_up, bool wide_down);
 hipError_t launch_big_gate_up(const GemmArgs& a, hipStream_t s);
-hipError_t launch_big_down(const GemmArgs& a, hipStream_t s);
+hipError_t launch_big_down(const GemmArgs& a, bool wide, hipStream_t s);
 
 bool stream_gemm_supported(int D, int I);
 int stream_rows_per_tile(bool gate_up);

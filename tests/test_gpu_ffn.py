@@ -70,6 +70,7 @@ def test_tiny(k3):
         (8, 2, 512, 512, 300),  # large-tile path: ragged 128-row (gate/up) and 64-row (down) tiles
         (16, 4, 1024, 512, 400),  # large-tile path with two feature tiles per matrix
         (12, 4, 2048, 1024, 700),  # large-tile path, 4 gate/up feature tiles (2D work order)
+        (12, 8, 1024, 512, 2100),  # 16800 entries: 128-row down tiles, ragged last tiles
         (64, 4, 512, 512, 8),  # weight-streaming path: about one row per expert
         (16, 4, 1024, 512, 16),  # streaming path: ~4 rows per expert, experts split over 4-row tiles
         (32, 8, 1536, 1024, 3),  # streaming path: 3 K stages (gate/up), 2 (down)
@@ -179,24 +180,26 @@ def test_graph_replay_matches_eager(k3, E, k, D, I, T):
         _ = (x.float() * 2).sum().item()  # unrelated eager work between replays
 
 
+@pytest.mark.parametrize("T,k", [(300, 2), (2048, 8)])  # 64- and 128-row down tiles
 @pytest.mark.parametrize("e_lo,e_hi", [(96, 150), (70, 100)])
-def test_large_tile_weights_fp16_cannot_hold(k3, e_lo, e_hi):
+def test_large_tile_weights_fp16_cannot_hold(k3, e_lo, e_hi, T, k):
     # Large-tile shapes with w2 block exponents partly (96..150) or wholly
     # (70..100) outside the range whose values fp16 holds exactly: the down
     # product must redo those tiles with the exact bf16 pair, and h spans
     # magnitudes far from 1 (scaled per row and 256-feature slice).
-    print(f"[ffn] large-tile exponents {e_lo}..{e_hi}", flush=True)
-    cfg = moe_inputs.TINY.with_(E=8, k=2, D=512, I=512, T=300, e_lo=e_lo, e_hi=e_hi, config_id=60 + e_lo)
+    print(f"[ffn] large-tile exponents {e_lo}..{e_hi} T={T} k={k}", flush=True)
+    cfg = moe_inputs.TINY.with_(E=8, k=k, D=512, I=512, T=T, e_lo=e_lo, e_hi=e_hi, config_id=60 + e_lo)
     got, ref, _, _ = small_case(k3, cfg)
     assert_ffn_close(got, ref, f"large-tile exponents {e_lo}..{e_hi}")
 
 
+@pytest.mark.parametrize("T,k", [(300, 2), (2048, 8)])  # 64- and 128-row down tiles
 @pytest.mark.parametrize("shift", [-40, 30])
-def test_large_tile_extreme_activation_scale(k3, shift):
+def test_large_tile_extreme_activation_scale(k3, shift, T, k):
     # x scaled by 2^shift (exactly, in its bf16 exponent field): h lands far
     # outside fp16's range unless the per-slice scale follows it
-    print(f"[ffn] large-tile x * 2^{shift}", flush=True)
-    cfg = moe_inputs.TINY.with_(E=8, k=2, D=512, I=512, T=300, config_id=70)
+    print(f"[ffn] large-tile x * 2^{shift} T={T} k={k}", flush=True)
+    cfg = moe_inputs.TINY.with_(E=8, k=k, D=512, I=512, T=T, config_id=70)
     batch = moe_inputs.make_batch(cfg)
     ids, w = route_ref(batch.z, batch.b, cfg.k)
     xb = batch.x.astype(np.int32)
