@@ -151,7 +151,9 @@ size_t moe_mxfp4_ffn_workspace_size(int64_t T, int32_t D, int32_t I, int32_t E, 
  * few rows, and shapes outside the large-tile kernels) or, for experts served
  * by the large-tile kernels (D and I multiples of 512, I <= 16384), as fp16
  * scaled by a power of two per (row, 256-wide slice of I) (11 significant
- * bits; about 2e-4 relative L2 error on K3-shaped inputs); fp32 output.
+ * bits), and those experts' outputs before the weighted sum are held as fp16
+ * scaled per (row, 32 outputs) (about 3e-4 relative L2 error on K3-shaped
+ * inputs in all); fp32 output.
  * The k expert outputs of a token are summed in slot order (deterministic, no
  * atomics).
  * Entry (t, j) is skipped (contributes nothing) when topk_ids[t,j] is outside

@@ -32,6 +32,7 @@ FfnWorkspace ffn_workspace_layout(int64_t T, int32_t D, int32_t I, int32_t E, in
   w.h_lo = take(sizeof(uint16_t) * (size_t)(entries * I));
   w.h_scale = take((size_t)entries * (size_t)((I + 255) / 256));
   w.y = take(sizeof(float) * (size_t)(entries * D));
+  w.y_scale = take((size_t)entries * (size_t)(D / 32));
   w.total = off;
   return w;
 }
@@ -192,6 +193,7 @@ int moe_mxfp4_ffn_profiled(const void* x_bf16, const int32_t* topk_ids, const fl
   g.rows_per_tile[2] = stream_rows_per_tile(true);
   g.rows_per_tile[3] = stream_rows_per_tile(false);
   g.split_rows = tiled ? (stream_only ? kStreamOnlyTokens : kStreamMaxRows) : 0;
+  g.flag_big_rows = tiled ? 1 : 0;  // the large-tile down kernel's rows hold scaled fp16 y
   g.counts = reinterpret_cast<int32_t*>(ws + L.counts);
   g.offsets = reinterpret_cast<int32_t*>(ws + L.offsets);
   g.tile_count = reinterpret_cast<int32_t*>(ws + L.tile_count);
@@ -235,6 +237,7 @@ int moe_mxfp4_ffn_profiled(const void* x_bf16, const int32_t* topk_ids, const fl
   dn.N = D;
   dn.out = ws + L.y;
   dn.h_scale = reinterpret_cast<int8_t*>(ws + L.h_scale);
+  dn.y_scale = reinterpret_cast<int8_t*>(ws + L.y_scale);
 
   // gate/up
   if (big_lists) {
@@ -272,7 +275,8 @@ int moe_mxfp4_ffn_profiled(const void* x_bf16, const int32_t* topk_ids, const fl
   }
   if (!mark(3)) return K3MOE_ERR_DEVICE;
 
-  err = launch_combine(reinterpret_cast<const float*>(ws + L.y), g.slot_row, topk_w, T, D, k, out, s);
+  err = launch_combine(reinterpret_cast<const float*>(ws + L.y), reinterpret_cast<const int8_t*>(ws + L.y_scale), tiled,
+                       g.slot_row, topk_w, T, D, k, out, s);
   if (err != hipSuccess || !mark(4)) return K3MOE_ERR_DEVICE;
   return K3MOE_OK;
 }

@@ -234,20 +234,29 @@ hipError_t launch_gemm(const GemmArgs& a, int rows_per_tile, hipStream_t s) {
   return hipGetLastError();
 }
 
-// out[t] = sum_j w[t,j] * y[slot_row[t*k+j]], in slot order; 4 features per
-// thread.  Slots are taken 16 at a time: all their row indices and weights
-// are loaded together, then all their y rows, so a thread waits for two
-// memory round trips per 16 slots and keeps 16 reads in flight.
+// out[t] = sum_j w[t,j] * y[slot_row[t*k+j]], in slot order; kF features per
+// thread (4 for fp32 y, 8 when rows may hold fp16 y, so that an fp16 row is
+// one 16-byte load).  Slots are taken 16 at a time: all their row indices and
+// weights are loaded together, then all their y rows, so a thread waits for
+// two memory round trips per 16 slots and keeps 16 reads in flight.
+// kMixed: a slot_row entry with kBigRowFlag names a row written by the
+// large-tile down kernel, which holds y as fp16 scaled by 2^y_scale[row,
+// feature / 32] at the start of the row's fp32 slot.
 constexpr int kCombineSlots = 16;
-__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ y, const int32_t* __restrict__ slot_row,
+template <bool kMixed>
+__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ y, const int8_t* __restrict__ y_scale,
+                                                       const int32_t* __restrict__ slot_row,
                                                        const float* __restrict__ w, int64_t T, int D, int k,
                                                        float* __restrict__ out) {
-  const int q = D / 4;
+  constexpr int kF = kMixed ? 8 : 4;
+  typedef float f32xF_t __attribute__((ext_vector_type(kF)));
+  typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+  const int q = D / kF;
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= T * q) return;
   const int64_t t = idx / q;
-  const int d = (int)(idx - t * q) * 4;
-  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  const int d = (int)(idx - t * q) * kF;
+  f32xF_t acc = {};
   for (int j0 = 0; j0 < k; j0 += kCombineSlots) {
     int32_t r[kCombineSlots];
     float wj[kCombineSlots];
@@ -257,23 +266,31 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
       r[u] = slot_row[t * k + j];
       wj[u] = w[t * k + j];
     }
-    f32x4_t v[kCombineSlots];
+    f32xF_t v[kCombineSlots];
 #pragma unroll
     for (int u = 0; u < kCombineSlots; ++u) {
       const bool use = j0 + u < k && r[u] >= 0;
-      v[u] = use ? __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(y + (int64_t)r[u] * D + d))
-                 : f32x4_t{0.f, 0.f, 0.f, 0.f};
+      if (!use) {
+        v[u] = f32xF_t{};
+      } else if (kMixed && (r[u] & kBigRowFlag)) {
+        const int64_t row = r[u] & ~kBigRowFlag;
+        const f16x8_t hv = __builtin_nontemporal_load(
+            reinterpret_cast<const f16x8_t*>(reinterpret_cast<const uint16_t*>(y + row * D) + d));
+        const float f = ldexpf(1.0f, (int)y_scale[row * (D >> 5) + (d >> 5)]);
+#pragma unroll
+        for (int e = 0; e < kF; ++e) v[u][e] = (float)hv[e] * f;
+      } else {
+        v[u] = __builtin_nontemporal_load(reinterpret_cast<const f32xF_t*>(y + (int64_t)r[u] * D + d));
+      }
     }
     // skipped and out-of-range slots hold exact zeros: adding them changes nothing
 #pragma unroll
     for (int u = 0; u < kCombineSlots; ++u) {
-      acc.x += wj[u] * v[u][0];
-      acc.y += wj[u] * v[u][1];
-      acc.z += wj[u] * v[u][2];
-      acc.w += wj[u] * v[u][3];
+#pragma unroll
+      for (int e = 0; e < kF; ++e) acc[e] += wj[u] * v[u][e];
     }
   }
-  *reinterpret_cast<float4*>(out + t * D + d) = acc;
+  *reinterpret_cast<f32xF_t*>(out + t * D + d) = acc;
 }
 
 }  // namespace
@@ -286,11 +303,16 @@ hipError_t launch_down(const GemmArgs& a, int rows_per_tile, hipStream_t s) {
   return launch_gemm<false>(a, rows_per_tile, s);
 }
 
-hipError_t launch_combine(const float* y, const int32_t* slot_row, const float* w, int64_t T, int D, int k,
-                          float* out, hipStream_t s) {
-  const int64_t n = T * (D / 4);
+hipError_t launch_combine(const float* y, const int8_t* y_scale, bool mixed, const int32_t* slot_row, const float* w,
+                          int64_t T, int D, int k, float* out, hipStream_t s) {
+  const int64_t n = T * (D / (mixed ? 8 : 4));
   const int64_t blocks = (n + 255) / 256;
-  hipLaunchKernelGGL(combine_kernel, dim3((unsigned)blocks), dim3(256), 0, s, y, slot_row, w, T, D, k, out);
+  if (mixed)
+    hipLaunchKernelGGL(combine_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, s, y, y_scale, slot_row, w, T, D, k,
+                       out);
+  else
+    hipLaunchKernelGGL(combine_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, s, y, y_scale, slot_row, w, T, D, k,
+                       out);
   return hipGetLastError();
 }
 

@@ -544,18 +544,41 @@ __global__ __launch_bounds__(kThreads) void ffn_big_kernel(GemmArgs a) {
       }
     }
   } else {
+    // y as fp16 scaled by 2^sy per (row, 32-feature group), sy = the exponent
+    // of the group's max |y| minus 14 (so the scaled values stay below 2^15),
+    // stored at the start of the row's fp32 slot: a group is two row groups
+    // (rg = 2q, 2q + 1) of the four lane groups g.
 #pragma unroll
     for (int tg = 0; tg < C::kTG; ++tg) {
       const int m = tg * 16 + rho;
-      if (m >= tile.nrows) continue;
-      const int64_t row = tile.row0 + m;
-      float* yrow = reinterpret_cast<float*>(a.out) + row * a.N;
       const float sc = ldexpf(1.0f, srow_l[m]);  // h's row scale
 #pragma unroll
-      for (int rg = 0; rg < C::kRG; ++rg) {
-        const int f = f0 + 64 * wave + 16 * rg + 4 * g;
-        *reinterpret_cast<float4*>(yrow + f) =
-            make_float4(acc[0][rg][tg][0] * sc, acc[0][rg][tg][1] * sc, acc[0][rg][tg][2] * sc, acc[0][rg][tg][3] * sc);
+      for (int q = 0; q < C::kRG / 2; ++q) {
+        float yv[2][4];
+        float mx = 0.f;
+#pragma unroll
+        for (int r2 = 0; r2 < 2; ++r2)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            yv[r2][v] = acc[0][2 * q + r2][tg][v] * sc;
+            mx = fmaxf(mx, fabsf(yv[r2][v]));
+          }
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        int sy = (int)((__float_as_uint(mx) >> 23) & 0xFFu) - 127 - 14;
+        sy = mx > 0.f ? (sy < -128 ? -128 : (sy > 113 ? 113 : sy)) : 0;
+        if (m >= tile.nrows) continue;
+        const int64_t row = tile.row0 + m;
+        uint16_t* yrow = reinterpret_cast<uint16_t*>(reinterpret_cast<float*>(a.out) + row * a.N);
+        const int fq = f0 + 64 * wave + 32 * q;  // first feature of the group
+#pragma unroll
+        for (int r2 = 0; r2 < 2; ++r2) {
+          uint32_t hb[4];
+#pragma unroll
+          for (int v = 0; v < 4; ++v) hb[v] = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)ldexpf(yv[r2][v], -sy));
+          *reinterpret_cast<uint2*>(yrow + fq + 16 * r2 + 4 * g) = make_uint2(hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16));
+        }
+        if (g == 0) a.y_scale[row * (a.N >> 5) + (fq >> 5)] = (int8_t)sy;
       }
     }
   }

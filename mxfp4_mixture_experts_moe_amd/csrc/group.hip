@@ -181,7 +181,7 @@ __device__ __forceinline__ void scan_experts(const GroupArgs& a, const unsigned 
 // Phase 3: grouped row of every entry of chunk c.
 __device__ __forceinline__ void place_entries(const int32_t* __restrict__ ids, int64_t T, int k, int E, int64_t c,
                               const unsigned long long* mask_c, const int32_t* base_c, int32_t* __restrict__ row_tok,
-                              int32_t* __restrict__ slot_row) {
+                              int32_t* __restrict__ slot_row, int flag_split) {
   const int tid = threadIdx.x, nthr = blockDim.x;
   const int64_t t0 = c * kChunkTokens;
   for (int idx = tid; idx < kChunkTokens * k; idx += nthr) {
@@ -194,6 +194,8 @@ __device__ __forceinline__ void place_entries(const int32_t* __restrict__ ids, i
       const unsigned long long before = tl ? (mask_c[e] & ((1ull << tl) - 1ull)) : 0ull;
       row = base_c[e] + __popcll(before);
       row_tok[row] = (int32_t)t;
+      // one chunk: its bitmap holds the expert's whole count
+      if (flag_split >= 0 && __popcll(mask_c[e]) > flag_split) row |= kBigRowFlag;
     }
     slot_row[t * k + j] = row;
   }
@@ -350,6 +352,7 @@ __global__ __launch_bounds__(256) void group_place_kernel(GroupArgs a) {
       const unsigned long long before = tl ? (mask_c[e] & ((1ull << tl) - 1ull)) : 0ull;
       row = base_c[e] + __popcll(before);
       a.row_tok[row] = (int32_t)t;
+      if (a.flag_big_rows && a.counts[e] > a.split_rows) row |= kBigRowFlag;
     }
     a.slot_row[t * a.k + j] = row;
   }
@@ -365,7 +368,7 @@ __global__ __launch_bounds__(kScanThreads) void group_fused_kernel(GroupArgs a) 
   build_masks(a.ids, a.T, a.k, a.E, 0, lmask);
   scan_experts(a, lmask, 1, lbase);
   lds_barrier();
-  place_entries(a.ids, a.T, a.k, a.E, 0, lmask, lbase, a.row_tok, a.slot_row);
+  place_entries(a.ids, a.T, a.k, a.E, 0, lmask, lbase, a.row_tok, a.slot_row, a.flag_big_rows ? a.split_rows : -1);
   permute_rows<4>(a.x, a.x_perm, 0, a.T, a.D, threadIdx.x, blockDim.x);
 }
 
@@ -423,6 +426,7 @@ __global__ __launch_bounds__(kScanThreads) void group_small_kernel(GroupArgs a) 
     if (e >= 0) {
       row = lbase[e] + __popcll(lmask[e] & ((1ull << t) - 1ull));
       a.row_tok[row] = t;
+      if (a.flag_big_rows && __popcll(lmask[e]) > a.split_rows) row |= kBigRowFlag;
     }
     a.slot_row[tid] = row;
   }

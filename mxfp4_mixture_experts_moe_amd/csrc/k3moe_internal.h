@@ -24,11 +24,15 @@ constexpr int kChunkTokens = 64;
 constexpr int kTileLists = 4;
 // The smallest tile height any GEMM variant uses; sizes the tile list.
 constexpr int kMinTileRows = 2;
+// Set in slot_row (FFN only) on rows of experts served by the large-tile
+// kernels, whose y rows are stored as scaled fp16 (grouped rows stay below
+// 2^21 on that path, so the bit is free).
+constexpr int32_t kBigRowFlag = 1 << 30;
 
 // Byte layout of the moe_mxfp4_ffn workspace (every region 256-byte aligned).
 struct FfnWorkspace {
   size_t counts, offsets, tile_count, tiles[kTileLists], row_tok, slot_row, chunk_base, chunk_mask;
-  size_t x_perm, h, h_lo, h_scale, y;
+  size_t x_perm, h, h_lo, h_scale, y, y_scale;
   size_t total;
   int64_t max_tiles, n_chunks;
 };
@@ -61,6 +65,7 @@ struct GroupArgs {
   int D, E, k;
   int rows_per_tile[kTileLists];  // tile height of each list
   int split_rows;                 // experts with more rows go to lists 0/1, the others to 2/3
+  int flag_big_rows;              // mark the slot_row entries of lists 0/1 experts with kBigRowFlag
   // workspace views
   int32_t* counts;
   int32_t* offsets;
@@ -92,6 +97,9 @@ struct GemmArgs {
   // 2^-h_scale[row, I-slice of 256] instead of h_hi + h_lo (written by the
   // gate/up kernel into `out`, read by the down kernel from `act`).
   int8_t* h_scale;  // [rows, I / 256]
+  // Large-tile down kernel only: its y rows are fp16 scaled by 2^y_scale[row,
+  // 32-feature group], stored at the start of the row's fp32 slot of `out`.
+  int8_t* y_scale;  // [rows, N / 32]
 };
 hipError_t launch_gate_up(const GemmArgs& a, int rows_per_tile, hipStream_t s);
 hipError_t launch_down(const GemmArgs& a, int rows_per_tile, hipStream_t s);
@@ -107,7 +115,9 @@ int stream_rows_per_tile(bool gate_up);
 hipError_t launch_stream_gate_up(const GemmArgs& a, hipStream_t s);
 hipError_t launch_stream_down(const GemmArgs& a, hipStream_t s);
 
-hipError_t launch_combine(const float* y, const int32_t* slot_row, const float* w, int64_t T, int D, int k,
+// mixed: rows whose slot_row entry carries kBigRowFlag hold scaled fp16 y.
+hipError_t launch_combine(const float* y, const int8_t* y_scale, bool mixed, const int32_t* slot_row, const float* w,
+                          int64_t T, int D, int k,
                           float* out, hipStream_t s);
 
 // Token-tile height the FFN uses for a batch of T tokens with k routed experts.
