@@ -64,9 +64,10 @@ def kernel_info(stage: str, path: str, entries: int = 0):
     if stage in ("gate_up", "down"):
         flag = "true" if stage == "gate_up" else "false"
         rows = 128 if stage == "gate_up" or entries >= 16384 else 64
-        big, stream = f"ffn_big_kernel<{flag}, {rows}>", f"ffn_stream_kernel<{flag}>"
+        big, stream = f"ffn_big_kernel<{flag}, {rows}>", f"ffn_stream_kernel<{flag}, false>"
         if path == "stream":
-            return stream, [CSRC + "ffn_stream.hip"]
+            # at decode the gate/up launch groups the entries itself
+            return f"ffn_stream_kernel<{flag}, {flag}>", [CSRC + "ffn_stream.hip"]
         if path == "tiled":
             return f"{big} + {stream}", [CSRC + "ffn_big.hip", CSRC + "ffn_stream.hip"]
         return f"ffn_gemm_kernel<NT, {flag}, ...>", [CSRC + "ffn.hip"]

@@ -207,8 +207,11 @@ int moe_mxfp4_ffn_profiled(const void* x_bf16, const int32_t* topk_ids, const fl
     if (!stage_events || !stage_events[i]) return true;
     return hipEventRecord(static_cast<hipEvent_t>(stage_events[i]), s) == hipSuccess;
   };
+  // A streaming-only batch of at most kSelfGroupEntries entries is grouped by
+  // the gate/up launch itself (no grouping launch; x read in place).
+  const bool self_group = stream_only && entries <= kSelfGroupEntries && E <= 0xFFFF;
   if (!mark(0)) return K3MOE_ERR_DEVICE;
-  hipError_t err = launch_group(g, s);
+  hipError_t err = self_group ? hipSuccess : launch_group(g, s);
   if (err != hipSuccess || !mark(1)) return K3MOE_ERR_DEVICE;
 
   // Upper bounds of the list lengths (sum over experts of ceil(n_e / rpt)):
@@ -252,7 +255,21 @@ int moe_mxfp4_ffn_profiled(const void* x_bf16, const int32_t* topk_ids, const fl
     gu.tile_count = g.tile_count + 2;
     const int64_t r = g.rows_per_tile[2];
     gu.max_tiles = (entries + (r - 1) * active) / r;  // bounds the sum of ceil(n_e / r) over experts
-    err = launch_stream_gate_up(gu, s);
+    if (self_group) {
+      SelfGroupArgs sg{};
+      sg.ids = topk_ids;
+      sg.T = (int)T;
+      sg.E = E;
+      sg.k = k;
+      sg.tile_count = g.tile_count;
+      sg.down_tiles = g.tiles[3];
+      sg.slot_row = g.slot_row;
+      gu.act = static_cast<const uint16_t*>(x_bf16);
+      gu.row_tok = nullptr;
+      err = launch_stream_gate_up_grouped(gu, sg, s);
+    } else {
+      err = launch_stream_gate_up(gu, s);
+    }
     if (err != hipSuccess) return K3MOE_ERR_DEVICE;
   }
   if (!mark(2)) return K3MOE_ERR_DEVICE;

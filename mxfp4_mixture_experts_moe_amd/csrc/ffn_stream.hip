@@ -108,11 +108,70 @@ __device__ __forceinline__ const __attribute__((address_space(4))) T_* as_const(
 
 struct TileInfo {
   int expert, row0, nrows;
+  int toks;  // self-grouping launch: token of tile row m in bits 4m .. 4m+3
 };
 __device__ __forceinline__ TileInfo load_tile(const Tile* tiles, int idx) {
   const auto p = as_const(reinterpret_cast<const int32_t*>(tiles) + 4 * idx);
-  return TileInfo{p[0], p[1], p[2]};
+  return TileInfo{p[0], p[1], p[2], 0};
 }
+
+// Exclusive scan of three counters over the 256 threads of the workgroup, in
+// thread order; tot = the workgroup's sums.  Contains two barriers, so every
+// thread must call it.
+__device__ __forceinline__ void block_scan3(int (&v)[3], int (&tot)[3], int (*wsum)[3]) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int incl[3] = {v[0], v[1], v[2]};
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1)
+#pragma unroll
+    for (int c = 0; c < 3; ++c) {
+      const int o = __shfl_up(incl[c], d, 64);
+      if (lane >= d) incl[c] += o;
+    }
+  if (lane == 63)
+#pragma unroll
+    for (int c = 0; c < 3; ++c) wsum[wave][c] = incl[c];
+  __syncthreads();
+#pragma unroll
+  for (int c = 0; c < 3; ++c) {
+    int before = 0, all = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const int x = wsum[w][c];
+      before += w < wave ? x : 0;
+      all += x;
+    }
+    v[c] = before + incl[c] - v[c];
+    tot[c] = all;
+  }
+  __syncthreads();
+}
+
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+// One round's activation operands of one lane when x rows sit in LDS in their
+// natural order: the 64 bytes of block 4 rnd + g, as four 16-byte reads from
+// `p`.  The reads and their wait are one asm block: written as plain loads,
+// the compiler orders them behind every global -> LDS load in flight, which
+// empties the stage ring each step.  One block per round, so the wait overlaps
+// the previous round's MFMAs.
+__device__ __forceinline__ void read_x_block(const uint8_t* p, u32x4_t (&q)[4]) {
+  const uint32_t a = (uint32_t)(uintptr_t)p;  // LDS byte address
+  asm volatile(
+      "ds_read_b128 %0, %4\n\tds_read_b128 %1, %4 offset:16\n\t"
+      "ds_read_b128 %2, %4 offset:32\n\tds_read_b128 %3, %4 offset:48\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(q[0]), "=&v"(q[1]), "=&v"(q[2]), "=&v"(q[3])
+      : "v"(a)
+      : "memory");
+}
+
+// One entry's view of the batch (self-grouping launch).
+struct EntryInfo {
+  int id, t, rank, cnt, lead;
+  unsigned mask;  // tokens that route to the entry's expert
+  bool valid;
+};
 
 // s_waitcnt vmcnt(N): at most N of this wave's vector-memory operations
 // outstanding.  Loads complete in issue order, so after the wait every load
@@ -143,8 +202,9 @@ struct Cursor {
   TileInfo tile;  // tile of the unit
 };
 
-template <bool kGateUp>
-__global__ __launch_bounds__(kWaves * 64, 1) void ffn_stream_kernel(GemmArgs a) {
+template <bool kGateUp, bool kSelfGroup>
+__global__ __launch_bounds__(kWaves * 64, 1) void ffn_stream_kernel(GemmArgs a, SelfGroupArgs sg) {
+  static_assert(kGateUp || !kSelfGroup, "only the gate/up launch groups");
   using C = StreamCfg<kGateUp>;
   constexpr int kSB = kStageBytes<kGateUp>;
   constexpr int kMatBytes = 16 * kStageRowBytes;  // one 16-row block of a stage
@@ -152,13 +212,130 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ffn_stream_kernel(GemmArgs a) 
   constexpr int kW = kWInstr;                     // weight loads per stage
   constexpr int kTileRows = C::kTileRows;
   __shared__ __attribute__((aligned(16))) uint8_t lds[kWaves][kRing][kSB];
+  // self-grouping launch: gate/up tiles {expert | (nrows-1) << 16 | row0 << 18, tokens}
+  __shared__ int2 s_tiles[kSelfGroup ? kSelfGroupEntries : 1];
+  __shared__ int s_wsum[kWaves][3];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int rho = lane & 15, g = lane >> 4;
   const int nfg = a.N / C::kFeat;  // units per tile
   const auto row_tok = as_const(a.row_tok);
-  const int64_t n_units = (int64_t)(*as_const(a.tile_count)) * nfg;
+  int n_tiles;
+  if constexpr (kSelfGroup) {
+    // Group the T*k entries in LDS (identically in every workgroup): an entry
+    // is skipped if its id is outside [0, E) or repeats an earlier slot of its
+    // token; the first entry of each expert (its leader) owns the expert's
+    // rows, ordered by token, and its tiles; leaders take rows and tiles in
+    // entry order.  The scratch lives in wave 0's first ring buffer, which is
+    // not loaded before the last barrier below.
+    constexpr int kThreads = kWaves * 64;
+    constexpr int kGuRows = StreamCfg<true>::kTileRows, kDnRows = StreamCfg<false>::kTileRows;
+    static_assert(kGuRows == 4, "tile rows travel as 2-bit counts and 4 token fields");
+    const int tid = threadIdx.x;
+    const int n = sg.T * sg.k;
+    const int n4 = (n + 3) & ~3;
+    int32_t* sid = reinterpret_cast<int32_t*>(&lds[0][0][0]);  // ids, padded with -1
+    int32_t* sbase = sid + kSelfGroupEntries;                  // first row of each leader entry
+    for (int i = tid; i < n4; i += kThreads) sid[i] = i < n ? sg.ids[i] : -1;
+    __syncthreads();
+    EntryInfo en[2];
+    int carry[3] = {0, 0, 0};
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const int i = tid + kThreads * r;
+      EntryInfo& e = en[r];
+      e = EntryInfo{-1, 0, 0, 0, -1, 0u, false};
+      if (i < n) {
+        const int id = sid[i];
+        const int t = i / sg.k, j = i - t * sg.k;
+        e.id = id;
+        e.t = t;
+        if (id >= 0 && id < sg.E) {
+          unsigned mask = 0u;
+          int first = -1;
+          bool dup = false;
+          int tt = 0, jj = 0;
+          for (int ii = 0; ii < n4; ii += 4) {
+            const int4 q = *reinterpret_cast<const int4*>(sid + ii);
+            const int qa[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+              if (qa[c] == id) {  // the -1 padding never matches
+                mask |= 1u << tt;
+                first = first < 0 ? ii + c : first;
+                dup = dup || (tt == t && jj < j);
+              }
+              if (++jj == sg.k) {
+                jj = 0;
+                ++tt;
+              }
+            }
+          }
+          if (!dup) {
+            e.valid = true;
+            e.mask = mask;
+            e.lead = first;
+            e.rank = __popc(mask & ((1u << t) - 1u));
+            e.cnt = __popc(mask);
+          }
+        }
+      }
+      const bool leader = e.valid && e.lead == i;
+      int v[3] = {0, 0, 0};
+      if (leader) {
+        v[0] = e.cnt;
+        v[1] = (e.cnt + kGuRows - 1) / kGuRows;  // gate/up tiles
+        v[2] = (e.cnt + kDnRows - 1) / kDnRows;  // down tiles
+      }
+      int tot[3];
+      block_scan3(v, tot, s_wsum);
+#pragma unroll
+      for (int c = 0; c < 3; ++c) {
+        v[c] += carry[c];
+        carry[c] += tot[c];
+      }
+      if (leader) {
+        sbase[i] = v[0];
+        unsigned m = e.mask;  // the expert's tokens, taken in row order
+        for (int jt = 0; jt < (e.cnt + kGuRows - 1) / kGuRows; ++jt) {
+          const int nr = e.cnt - kGuRows * jt < kGuRows ? e.cnt - kGuRows * jt : kGuRows;
+          int toks = 0;
+          for (int mm = 0; mm < nr; ++mm) {
+            toks |= __builtin_ctz(m) << (4 * mm);
+            m &= m - 1u;
+          }
+          s_tiles[v[1] + jt] = make_int2(e.id | (nr - 1) << 16 | (v[0] + kGuRows * jt) << 18, toks);
+        }
+        if (blockIdx.x == 0)
+          for (int jt = 0; jt < (e.cnt + kDnRows - 1) / kDnRows; ++jt) {
+            Tile tl;
+            tl.expert = e.id;
+            tl.row0 = v[0] + kDnRows * jt;
+            tl.nrows = e.cnt - kDnRows * jt < kDnRows ? e.cnt - kDnRows * jt : kDnRows;
+            tl.pad = 0;
+            sg.down_tiles[v[2] + jt] = tl;
+          }
+      }
+    }
+    __syncthreads();
+    if (blockIdx.x == 0) {
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        const int i = tid + kThreads * r;
+        if (i < n) sg.slot_row[i] = en[r].valid ? sbase[en[r].lead] + en[r].rank : -1;
+      }
+      if (tid == 0) {
+        sg.tile_count[2] = carry[1];
+        sg.tile_count[3] = carry[2];
+      }
+    }
+    __syncthreads();  // scratch reads done before the ring is loaded
+    n_tiles = __builtin_amdgcn_readfirstlane(carry[1]);
+  } else {
+    n_tiles = *as_const(a.tile_count);
+  }
+  const int64_t n_units = (int64_t)n_tiles * nfg;
   const int64_t nw = (int64_t)gridDim.x * kWaves;
   const int64_t wid = (int64_t)blockIdx.x * kWaves + wave;
   if (wid >= n_units) return;  // uniform over the wave; no barriers below
@@ -186,7 +363,13 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ffn_stream_kernel(GemmArgs a) 
   auto load_unit = [&](Cursor& c) {
     const int tile_idx = __builtin_amdgcn_readfirstlane((int)(c.u / nfg));
     c.fg = __builtin_amdgcn_readfirstlane((int)(c.u - (int64_t)tile_idx * nfg));
-    c.tile = load_tile(a.tiles, tile_idx);
+    if constexpr (kSelfGroup) {
+      const int2 pk = s_tiles[tile_idx];
+      const int p0 = __builtin_amdgcn_readfirstlane(pk.x);
+      c.tile = TileInfo{p0 & 0xFFFF, (p0 >> 18) & 0x3FF, ((p0 >> 16) & 3) + 1, __builtin_amdgcn_readfirstlane(pk.y)};
+    } else {
+      c.tile = load_tile(a.tiles, tile_idx);
+    }
   };
   auto advance = [&](Cursor& c) {
     if (++c.s == nst) {
@@ -227,7 +410,8 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ffn_stream_kernel(GemmArgs a) 
     for (int m = 0; m < kTileRows; ++m) {
       if (m < c.tile.nrows) {
         const int row = c.tile.row0 + m;
-        const uint32_t src = (uint32_t)(kGateUp ? row_tok[row] : row) * act_row_bytes + aso;
+        const int xrow = kSelfGroup ? (c.tile.toks >> (4 * m)) & 15 : (kGateUp ? row_tok[row] : row);
+        const uint32_t src = (uint32_t)xrow * act_row_bytes + aso;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (__attribute__((address_space(3))) void*)(uintptr_t)(bdst + kBRowBytes * m),
                                                  16, 16 * lane, src, 0, 0);
         if (!kGateUp)
@@ -244,7 +428,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ffn_stream_kernel(GemmArgs a) 
   for (int mi = 0; mi < kRB; ++mi) acc[mi] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   const uint32_t qsel = 0x03020100u + 0x01010101u * (uint32_t)(g + 1);
-  Cursor ci{wid, 0, 0, {0, 0, 0}};  // issue side
+  Cursor ci{wid, 0, 0, {0, 0, 0, 0}};  // issue side
   load_unit(ci);
   Cursor cc = ci;  // compute side
   int buf_i = 0, buf_c = 0;
@@ -289,8 +473,28 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ffn_stream_kernel(GemmArgs a) 
 #pragma unroll
     for (int rnd = 0; rnd < 4; ++rnd) {
       bf16x8_t bop[4];
+      if constexpr (kSelfGroup) {
+        // x rows in natural order: P-order dword t of operand i pairs
+        // elements 4i + t and 16 + 4i + t of block 4*rnd + g
+        u32x4_t q[4];  // elements 0-7, 8-15, 16-23, 24-31
+        read_x_block(bl + 64 * (4 * rnd + g), q);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) bop[i] = *reinterpret_cast<const bf16x8_t*>(bl + 64 * (4 * rnd + g) + 16 * i);
+        for (int i = 0; i < 4; ++i) {
+          const u32x4_t& L = q[i >> 1];
+          const u32x4_t& H = q[2 + (i >> 1)];
+          const uint32_t l0 = (i & 1) ? L.z : L.x, l1 = (i & 1) ? L.w : L.y;
+          const uint32_t h0 = (i & 1) ? H.z : H.x, h1 = (i & 1) ? H.w : H.y;
+          uint4 r;
+          r.x = __builtin_amdgcn_perm(h0, l0, 0x05040100u);
+          r.y = __builtin_amdgcn_perm(h0, l0, 0x07060302u);
+          r.z = __builtin_amdgcn_perm(h1, l1, 0x05040100u);
+          r.w = __builtin_amdgcn_perm(h1, l1, 0x07060302u);
+          bop[i] = __builtin_bit_cast(bf16x8_t, r);
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) bop[i] = *reinterpret_cast<const bf16x8_t*>(bl + 64 * (4 * rnd + g) + 16 * i);
+      }
 #pragma unroll
       for (int mi = 0; mi < kRB; ++mi) {
         bf16x8_t aop[4];
@@ -360,14 +564,14 @@ int cu_count() {
   return cached[dev];
 }
 
-template <bool kGateUp>
-hipError_t launch_stream(const GemmArgs& a, hipStream_t s) {
+template <bool kGateUp, bool kSelfGroup>
+hipError_t launch_stream(const GemmArgs& a, const SelfGroupArgs& sg, hipStream_t s) {
   const int64_t max_units = a.max_tiles * (a.N / StreamCfg<kGateUp>::kFeat);
   int64_t grid = (max_units + kWaves - 1) / kWaves;
   const int cus = cu_count();
   if (grid > cus) grid = cus;
-  if (grid < 1) grid = 1;
-  hipLaunchKernelGGL(ffn_stream_kernel<kGateUp>, dim3((unsigned)grid), dim3(kWaves * 64), 0, s, a);
+  if (grid < 1) grid = 1;  // the self-grouping launch needs workgroup 0 in any case
+  hipLaunchKernelGGL((ffn_stream_kernel<kGateUp, kSelfGroup>), dim3((unsigned)grid), dim3(kWaves * 64), 0, s, a, sg);
   return hipGetLastError();
 }
 
@@ -379,8 +583,12 @@ bool stream_gemm_supported(int D, int I) { return (D % kStageK) == 0 && (I % kSt
 
 int stream_rows_per_tile(bool gate_up) { return gate_up ? StreamCfg<true>::kTileRows : StreamCfg<false>::kTileRows; }
 
-hipError_t launch_stream_gate_up(const GemmArgs& a, hipStream_t s) { return launch_stream<true>(a, s); }
+hipError_t launch_stream_gate_up(const GemmArgs& a, hipStream_t s) { return launch_stream<true, false>(a, {}, s); }
 
-hipError_t launch_stream_down(const GemmArgs& a, hipStream_t s) { return launch_stream<false>(a, s); }
+hipError_t launch_stream_down(const GemmArgs& a, hipStream_t s) { return launch_stream<false, false>(a, {}, s); }
+
+hipError_t launch_stream_gate_up_grouped(const GemmArgs& a, const SelfGroupArgs& sg, hipStream_t s) {
+  return launch_stream<true, true>(a, sg, s);
+}
 
 }  // namespace k3moe

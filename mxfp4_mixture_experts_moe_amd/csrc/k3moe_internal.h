@@ -115,6 +115,21 @@ int stream_rows_per_tile(bool gate_up);
 hipError_t launch_stream_gate_up(const GemmArgs& a, hipStream_t s);
 hipError_t launch_stream_down(const GemmArgs& a, hipStream_t s);
 
+// Streaming gate/up that groups the routed entries itself (batches of at most
+// kSelfGroupEntries entries, experts below 2^16): every workgroup builds the
+// gate/up tiles in LDS from the ids, and workgroup 0 writes what the kernels
+// after it read (the down tile list, tile_count[2..3], slot_row), so no
+// grouping launch precedes it.  It reads x [T, D] in its natural layout.
+constexpr int kSelfGroupEntries = 512;
+struct SelfGroupArgs {
+  const int32_t* ids;   // [T, k]
+  int T, E, k;          // T <= 16 (tokens travel as 4-bit fields)
+  int32_t* tile_count;  // [kTileLists]; entries 2 and 3 are written
+  Tile* down_tiles;     // list 3: 2-row down tiles
+  int32_t* slot_row;    // [T * k]: grouped row of each entry, -1 if skipped
+};
+hipError_t launch_stream_gate_up_grouped(const GemmArgs& a, const SelfGroupArgs& sg, hipStream_t s);
+
 // mixed: rows whose slot_row entry carries kBigRowFlag hold scaled fp16 y.
 hipError_t launch_combine(const float* y, const int8_t* y_scale, bool mixed, const int32_t* slot_row, const float* w,
                           int64_t T, int D, int k,

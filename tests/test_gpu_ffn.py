@@ -141,6 +141,24 @@ def test_mixed_large_and_streaming_experts(k3):
     assert_ffn_close(got, ref, "mixed large/streaming")
 
 
+def test_large_batch_mixed_with_few_row_experts(k3):
+    # 16384 routed entries (128-row large-tile down tiles) with experts of
+    # 1..4 rows (weight-streaming kernels) and one of 5 rows in the same call
+    cfg = moe_inputs.TINY.with_(E=40, k=8, D=512, I=512, T=2048, config_id=45)
+    g = np.random.default_rng(15)
+    ids = np.stack([g.permutation(30)[: cfg.k] for _ in range(cfg.T)]).astype(np.int32)
+    ids[0, 7] = 30  # 1 row
+    ids[1:3, 7] = 31  # 2 rows
+    ids[3:6, 7] = 32  # 3 rows
+    ids[6:10, 7] = 33  # 4 rows
+    ids[10:15, 7] = 34  # 5 rows
+    ids[2000, 7] = 39  # 1 row, in the last token group
+    w = g.random((cfg.T, cfg.k)).astype(np.float32)
+    print(f"[ffn] large batch with few-row experts T={cfg.T}", flush=True)
+    got, ref, _, _ = small_case(k3, cfg, ids, w)
+    assert_ffn_close(got, ref, "large batch, few-row experts")
+
+
 @pytest.mark.parametrize(
     "E,k,D,I,T",
     [(8, 2, 128, 256, 64), (64, 4, 512, 512, 8), (8, 2, 512, 512, 300)],  # small-tile, streaming, large-tile paths
