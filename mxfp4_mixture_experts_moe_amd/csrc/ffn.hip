@@ -234,63 +234,96 @@ hipError_t launch_gemm(const GemmArgs& a, int rows_per_tile, hipStream_t s) {
   return hipGetLastError();
 }
 
-// out[t] = sum_j w[t,j] * y[slot_row[t*k+j]], in slot order; kF features per
-// thread (4 for fp32 y, 8 when rows may hold fp16 y, so that an fp16 row is
-// one 16-byte load).  Slots are taken 16 at a time: all their row indices and
-// weights are loaded together, then all their y rows, so a thread waits for
-// two memory round trips per 16 slots and keeps 16 reads in flight.
+// out[t] = sum_j w[t,j] * y[slot_row[t*k+j]], in slot order.  fp32 y only:
+// 4 features per thread, slots 16 at a time (all their row indices and
+// weights loaded together, then all their y rows: two memory round trips per
+// 16 slots, 16 reads in flight).  Rows that may hold fp16 y: 16 features per
+// thread (two 16-byte reads and one scale byte per slot), slots 8 at a time
+// for large batches, which keeps the thread under 128 VGPRs (four waves per
+// SIMD), and 16 at a time for batches too small to fill the GPU, where the
+// round trips matter more than the occupancy.
 // kMixed: a slot_row entry with kBigRowFlag names a row written by the
 // large-tile down kernel, which holds y as fp16 scaled by 2^y_scale[row,
 // feature / 32] at the start of the row's fp32 slot.
 constexpr int kCombineSlots = 16;
-template <bool kMixed>
+template <bool kMixed, int kB>
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ y, const int8_t* __restrict__ y_scale,
                                                        const int32_t* __restrict__ slot_row,
                                                        const float* __restrict__ w, int64_t T, int D, int k,
                                                        float* __restrict__ out) {
-  constexpr int kF = kMixed ? 8 : 4;
-  typedef float f32xF_t __attribute__((ext_vector_type(kF)));
+  constexpr int kF = kMixed ? 16 : 4;
+  typedef float f32x4_t __attribute__((ext_vector_type(4)));
   typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
   const int q = D / kF;
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (idx >= T * q) return;
   const int64_t t = idx / q;
   const int d = (int)(idx - t * q) * kF;
-  f32xF_t acc = {};
-  for (int j0 = 0; j0 < k; j0 += kCombineSlots) {
-    int32_t r[kCombineSlots];
-    float wj[kCombineSlots];
+  float acc[kF] = {};
+  for (int j0 = 0; j0 < k; j0 += kB) {
+    int32_t r[kB];
+    float wj[kB];
 #pragma unroll
-    for (int u = 0; u < kCombineSlots; ++u) {
+    for (int u = 0; u < kB; ++u) {
       const int j = j0 + u < k ? j0 + u : k - 1;
       r[u] = slot_row[t * k + j];
       wj[u] = w[t * k + j];
     }
-    f32xF_t v[kCombineSlots];
+    if constexpr (kMixed) {
+      // rows of the large-tile kernels: raw fp16 reads for the whole batch
+      // first; fp32 rows (experts served by the streaming kernels) are read
+      // when their slot is summed
+      f16x8_t h[kB][2];
+      float fs[kB];
 #pragma unroll
-    for (int u = 0; u < kCombineSlots; ++u) {
-      const bool use = j0 + u < k && r[u] >= 0;
-      if (!use) {
-        v[u] = f32xF_t{};
-      } else if (kMixed && (r[u] & kBigRowFlag)) {
-        const int64_t row = r[u] & ~kBigRowFlag;
-        const f16x8_t hv = __builtin_nontemporal_load(
-            reinterpret_cast<const f16x8_t*>(reinterpret_cast<const uint16_t*>(y + row * D) + d));
-        const float f = ldexpf(1.0f, (int)y_scale[row * (D >> 5) + (d >> 5)]);
+      for (int u = 0; u < kB; ++u) {
+        const bool big = j0 + u < k && r[u] >= 0 && (r[u] & kBigRowFlag);
+        if (big) {
+          const int64_t row = r[u] & ~kBigRowFlag;
+          const f16x8_t* src = reinterpret_cast<const f16x8_t*>(reinterpret_cast<const uint16_t*>(y + row * D) + d);
+          h[u][0] = __builtin_nontemporal_load(src);
+          h[u][1] = __builtin_nontemporal_load(src + 1);
+          fs[u] = ldexpf(1.0f, (int)y_scale[row * (D >> 5) + (d >> 5)]);
+        } else {
+          h[u][0] = f16x8_t{};
+          h[u][1] = f16x8_t{};
+          fs[u] = 0.0f;
+        }
+      }
+      // slot order; skipped slots add nothing; an fp32 row is read here (rare)
 #pragma unroll
-        for (int e = 0; e < kF; ++e) v[u][e] = (float)hv[e] * f;
-      } else {
-        v[u] = __builtin_nontemporal_load(reinterpret_cast<const f32xF_t*>(y + (int64_t)r[u] * D + d));
+      for (int u = 0; u < kB; ++u) {
+        if (j0 + u >= k || r[u] < 0) continue;
+        if (r[u] & kBigRowFlag) {
+#pragma unroll
+          for (int e = 0; e < 16; ++e) acc[e] += wj[u] * ((float)h[u][e >> 3][e & 7] * fs[u]);
+        } else {
+          const f32x4_t* src = reinterpret_cast<const f32x4_t*>(y + (int64_t)r[u] * D + d);
+#pragma unroll
+          for (int c = 0; c < kF / 4; ++c) {
+            const f32x4_t x4 = __builtin_nontemporal_load(src + c);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) acc[4 * c + e] += wj[u] * x4[e];
+          }
+        }
+      }
+    } else {
+      f32x4_t v[kB];
+#pragma unroll
+      for (int u = 0; u < kB; ++u)
+        v[u] = j0 + u < k && r[u] >= 0 ? __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(y + (int64_t)r[u] * D + d))
+                                        : f32x4_t{};
+      // skipped and out-of-range slots hold exact zeros: adding them changes nothing
+#pragma unroll
+      for (int u = 0; u < kB; ++u) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[e] += wj[u] * v[u][e];
       }
     }
-    // skipped and out-of-range slots hold exact zeros: adding them changes nothing
-#pragma unroll
-    for (int u = 0; u < kCombineSlots; ++u) {
-#pragma unroll
-      for (int e = 0; e < kF; ++e) acc[e] += wj[u] * v[u][e];
-    }
   }
-  *reinterpret_cast<f32xF_t*>(out + t * D + d) = acc;
+  f32x4_t* o = reinterpret_cast<f32x4_t*>(out + t * D + d);
+#pragma unroll
+  for (int c = 0; c < kF / 4; ++c) o[c] = f32x4_t{acc[4 * c], acc[4 * c + 1], acc[4 * c + 2], acc[4 * c + 3]};
 }
 
 }  // namespace
@@ -305,14 +338,19 @@ hipError_t launch_down(const GemmArgs& a, int rows_per_tile, hipStream_t s) {
 
 hipError_t launch_combine(const float* y, const int8_t* y_scale, bool mixed, const int32_t* slot_row, const float* w,
                           int64_t T, int D, int k, float* out, hipStream_t s) {
-  const int64_t n = T * (D / (mixed ? 8 : 4));
+  const int64_t n = T * (D / (mixed ? 16 : 4));
   const int64_t blocks = (n + 255) / 256;
-  if (mixed)
-    hipLaunchKernelGGL(combine_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, s, y, y_scale, slot_row, w, T, D, k,
-                       out);
+  // fewer threads than four waves on every SIMD of the GPU: 16-slot batches
+  constexpr int64_t kFewThreads = 4 * 4 * 64 * 256;
+  if (mixed && n >= kFewThreads)
+    hipLaunchKernelGGL((combine_kernel<true, 8>), dim3((unsigned)blocks), dim3(256), 0, s, y, y_scale, slot_row, w, T, D,
+                       k, out);
+  else if (mixed)
+    hipLaunchKernelGGL((combine_kernel<true, kCombineSlots>), dim3((unsigned)blocks), dim3(256), 0, s, y, y_scale,
+                       slot_row, w, T, D, k, out);
   else
-    hipLaunchKernelGGL(combine_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, s, y, y_scale, slot_row, w, T, D, k,
-                       out);
+    hipLaunchKernelGGL((combine_kernel<false, kCombineSlots>), dim3((unsigned)blocks), dim3(256), 0, s, y, y_scale,
+                       slot_row, w, T, D, k, out);
   return hipGetLastError();
 }
 

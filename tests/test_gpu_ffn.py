@@ -254,6 +254,20 @@ def test_identity_weights_closed_form(k3):
     assert_ffn_close(out, expect, "identity closed form")
 
 
+def test_combine_large_batch_slot_batches(k3):
+    # 8192 tokens x 32 threads: the combine takes its slots 8 at a time here;
+    # k = 12 leaves a partial second batch (oracle on sampled tokens)
+    cfg = moe_inputs.TINY.with_(E=16, k=12, D=512, I=512, T=8192, config_id=46)
+    print(f"[ffn] combine slot batches T={cfg.T} k={cfg.k}", flush=True)
+    batch = moe_inputs.make_batch(cfg)
+    ids, w = route_ref(batch.z, batch.b, cfg.k)
+    dev = device_experts(k3, cfg)
+    out = run_ffn(k3, dev, batch.x, ids.astype(np.int32), w.astype(np.float32))
+    toks = np.array([0, 1, 4095, 5000, cfg.T - 1])
+    ref = ffn_ref(batch.x, ids, w, HostExperts(cfg), tokens=toks)
+    assert_ffn_close(out[toks], ref, f"tokens {toks.tolist()}")
+
+
 # ---------------------------------------------------------------------------
 # K3-shaped configs: all 896 experts resident on the device (15.7 GB).
 
