@@ -57,7 +57,7 @@ def gemm_path(cfg) -> str:
     return "small"
 
 
-def kernel_info(stage: str, path: str, entries: int = 0):
+def kernel_info(stage: str, path: str, entries: int = 0, tokens: int = 0):
     """(kernel name(s) as rocprofv3 reports them, source files) of a stage.
     The large-tile down product takes 128-row tiles from 16384 routed entries
     on, 64-row tiles below."""
@@ -66,8 +66,9 @@ def kernel_info(stage: str, path: str, entries: int = 0):
         rows = 128 if stage == "gate_up" or entries >= 16384 else 64
         big, stream = f"ffn_big_kernel<{flag}, {rows}>", f"ffn_stream_kernel<{flag}, false>"
         if path == "stream":
-            # at decode the gate/up launch groups the entries itself
-            return f"ffn_stream_kernel<{flag}, {flag}>", [CSRC + "ffn_stream.hip"]
+            # up to 4 tokens the gate/up launch groups the entries itself
+            grouped = "true" if stage == "gate_up" and tokens <= 4 else "false"
+            return f"ffn_stream_kernel<{flag}, {grouped}>", [CSRC + "ffn_stream.hip"]
         if path == "tiled":
             return f"{big} + {stream}", [CSRC + "ffn_big.hip", CSRC + "ffn_stream.hip"]
         return f"ffn_gemm_kernel<NT, {flag}, ...>", [CSRC + "ffn.hip"]
@@ -303,7 +304,7 @@ def main():
         achieved, peak, unit = flops / dur_s / 1e12, PEAK_BF16_TFLOPS, "TFLOP/s"
     else:
         achieved, peak, unit = byts / dur_s / 1e9, PEAK_HBM_GBS, "GB/s"
-    kname, ksrc = kernel_info(dom, gemm_path(cfg), cfg.T * cfg.k)
+    kname, ksrc = kernel_info(dom, gemm_path(cfg), cfg.T * cfg.k, cfg.T)
     traffic = stored_traffic(dom, args.workload, ksrc)
 
     value = cfg.T * steps / elapsed

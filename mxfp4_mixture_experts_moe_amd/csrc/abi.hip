@@ -207,9 +207,13 @@ int moe_mxfp4_ffn_profiled(const void* x_bf16, const int32_t* topk_ids, const fl
     if (!stage_events || !stage_events[i]) return true;
     return hipEventRecord(static_cast<hipEvent_t>(stage_events[i]), s) == hipSuccess;
   };
-  // A streaming-only batch of at most kSelfGroupEntries entries is grouped by
-  // the gate/up launch itself (no grouping launch; x read in place).
-  const bool self_group = stream_only && entries <= kSelfGroupEntries && E <= 0xFFFF;
+  // A streaming-only batch of at most kSelfGroupTokens tokens (and
+  // kSelfGroupEntries entries) is grouped by the gate/up launch itself: no
+  // grouping launch, x read in place.  At one token that saves a tenth of the
+  // step; at 8 tokens both ways take the same time, and the grouping launch's
+  // pre-permuted x keeps the gate/up stream itself faster.
+  constexpr int kSelfGroupTokens = 4;
+  const bool self_group = stream_only && T <= kSelfGroupTokens && entries <= kSelfGroupEntries && E <= 0xFFFF;
   if (!mark(0)) return K3MOE_ERR_DEVICE;
   hipError_t err = self_group ? hipSuccess : launch_group(g, s);
   if (err != hipSuccess || !mark(1)) return K3MOE_ERR_DEVICE;
@@ -292,8 +296,11 @@ int moe_mxfp4_ffn_profiled(const void* x_bf16, const int32_t* topk_ids, const fl
   }
   if (!mark(3)) return K3MOE_ERR_DEVICE;
 
-  err = launch_combine(reinterpret_cast<const float*>(ws + L.y), reinterpret_cast<const int8_t*>(ws + L.y_scale), tiled,
-                       g.slot_row, topk_w, T, D, k, out, s);
+  // Rows of the large-tile down kernel hold scaled fp16 y; a streaming-only
+  // batch has none, so its combine reads fp32 rows only.
+  const bool mixed_rows = tiled && !stream_only;
+  err = launch_combine(reinterpret_cast<const float*>(ws + L.y), reinterpret_cast<const int8_t*>(ws + L.y_scale),
+                       mixed_rows, g.slot_row, topk_w, T, D, k, out, s);
   if (err != hipSuccess || !mark(4)) return K3MOE_ERR_DEVICE;
   return K3MOE_OK;
 }

@@ -108,17 +108,19 @@ def test_hot_expert_invalid_and_duplicate_ids(k3):
     assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
 
 
-def test_streaming_path_hot_invalid_and_duplicate_ids(k3):
+@pytest.mark.parametrize("T", [8, 4])  # grouping launch / grouping inside the gate/up launch
+def test_streaming_path_hot_invalid_and_duplicate_ids(k3, T):
     # decode-sized batch (at most 4 rows per active expert on average) with one
-    # expert in every row: its 8 rows span two 4-row tiles
-    cfg = moe_inputs.TINY.with_(E=40, k=4, D=512, I=512, T=8, config_id=42)
+    # expert in every row: its T rows span one or two 4-row tiles
+    print(f"[ffn] streaming hot/invalid/duplicate T={T}", flush=True)
+    cfg = moe_inputs.TINY.with_(E=40, k=4, D=512, I=512, T=T, config_id=42)
     g = np.random.default_rng(13)
     ids = np.stack([g.permutation(cfg.E)[: cfg.k] for _ in range(cfg.T)]).astype(np.int32)
     ids[:, 0] = 5
     rest = ids[:, 1:]  # a view: keep the hot expert in slot 0 only
     rest[rest == 5] = 6
     ids[3, 1] = -2  # out of range -> skipped
-    ids[4, 3] = ids[4, 2]  # repeat -> skipped
+    ids[2, 3] = ids[2, 2]  # repeat -> skipped
     w = g.random((cfg.T, cfg.k)).astype(np.float32)
     got, ref, batch, dev = small_case(k3, cfg, ids, w)
     assert_ffn_close(got, ref, "streaming hot/invalid/duplicate")
@@ -161,7 +163,8 @@ def test_large_batch_mixed_with_few_row_experts(k3):
 
 @pytest.mark.parametrize(
     "E,k,D,I,T",
-    [(8, 2, 128, 256, 64), (64, 4, 512, 512, 8), (8, 2, 512, 512, 300)],  # small-tile, streaming, large-tile paths
+    # small-tile, streaming (grouping launch; grouping inside the gate/up launch), large-tile paths
+    [(8, 2, 128, 256, 64), (64, 4, 512, 512, 8), (64, 4, 512, 512, 3), (8, 2, 512, 512, 300)],
 )
 def test_graph_replay_matches_eager(k3, E, k, D, I, T):
     # route + FFN captured into a HIP graph: every replay, with other eager work
