@@ -9,8 +9,9 @@
  *
  * General conventions (all entry points):
  *   - Array pointers are DEVICE pointers unless stated otherwise. The caller
- *     allocates and owns every buffer; the library allocates nothing, keeps no
- *     state between calls and never synchronizes the host.
+ *     allocates and owns every buffer; the library allocates no memory and
+ *     never synchronizes the host. Its only state is moe_mxfp4_ffn's side
+ *     stream (below).
  *   - `stream` is a hipStream_t (NULL = the default stream). Every call only
  *     enqueues work on it and returns; results are ready when the stream is.
  *   - Arrays are row-major and contiguous. Inputs are never written. Outputs
@@ -156,6 +157,14 @@ size_t moe_mxfp4_ffn_workspace_size(int64_t T, int32_t D, int32_t I, int32_t E, 
  * inputs in all); fp32 output.
  * The k expert outputs of a token are summed in slot order (deterministic, no
  * atomics).
+ * Side stream: when one call has experts for both GEMM kinds (many rows: the
+ * large-tile kernels; at most 4 rows: the weight-streaming kernels), the
+ * streaming launches run on a side stream forked from `stream` with an event
+ * and joined back before the combine (a graph captured from `stream` gets two
+ * parallel branches). The side stream (default priority) and its two events
+ * belong to the calling host thread and the current device; they are created
+ * by the first such call made outside a graph capture (until then the
+ * launches stay on `stream`) and kept until the process ends.
  * Entry (t, j) is skipped (contributes nothing) when topk_ids[t,j] is outside
  * [0, E) or repeats an id earlier in the same row.
  * Sizes: T >= 0 (T == 0 is a no-op), D > 0 and I > 0 multiples of 128,

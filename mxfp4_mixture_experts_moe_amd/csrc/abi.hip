@@ -67,6 +67,33 @@ bool misaligned(const void* p) { return p != nullptr && (reinterpret_cast<uintpt
 
 int device_status(hipError_t e) { return e == hipSuccess ? K3MOE_OK : K3MOE_ERR_DEVICE; }
 
+// Side stream (default priority) and fork / join events of the calling host
+// thread on the current device, created on the first call made outside a
+// graph capture and kept for the life of the thread; nullptr before that, or
+// if the runtime refuses one of them.
+struct SideStream {
+  hipStream_t s = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+};
+SideStream* side_stream(hipStream_t caller) {
+  constexpr int kMaxDevices = 64;
+  thread_local SideStream side[kMaxDevices];
+  thread_local bool tried[kMaxDevices] = {};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  SideStream& ss = side[dev];
+  if (!tried[dev]) {
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(caller, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) return nullptr;
+    tried[dev] = true;
+    if (hipStreamCreateWithFlags(&ss.s, hipStreamNonBlocking) != hipSuccess ||
+        hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&ss.join, hipEventDisableTiming) != hipSuccess)
+      ss.s = nullptr;
+  }
+  return ss.s ? &ss : nullptr;
+}
+
 }  // namespace
 
 extern "C" {
@@ -246,6 +273,18 @@ int moe_mxfp4_ffn_profiled(const void* x_bf16, const int32_t* topk_ids, const fl
   dn.h_scale = reinterpret_cast<int8_t*>(ws + L.h_scale);
   dn.y_scale = reinterpret_cast<int8_t*>(ws + L.y_scale);
 
+  // Experts of both kinds in one call (and no stage events to record): the
+  // streaming launches run on a side stream beside the large-tile launches;
+  // they read the same inputs and write other rows of h and y.  The combine
+  // waits for both branches.
+  SideStream* side = (big_lists && stream_lists && !stage_events) ? side_stream(s) : nullptr;
+  hipStream_t ss = s;
+  if (side) {
+    if (hipEventRecord(side->fork, s) != hipSuccess || hipStreamWaitEvent(side->s, side->fork, 0) != hipSuccess)
+      return K3MOE_ERR_DEVICE;
+    ss = side->s;
+  }
+
   // gate/up
   if (big_lists) {
     gu.tiles = g.tiles[0];
@@ -270,9 +309,9 @@ int moe_mxfp4_ffn_profiled(const void* x_bf16, const int32_t* topk_ids, const fl
       sg.slot_row = g.slot_row;
       gu.act = static_cast<const uint16_t*>(x_bf16);
       gu.row_tok = nullptr;
-      err = launch_stream_gate_up_grouped(gu, sg, s);
+      err = launch_stream_gate_up_grouped(gu, sg, ss);
     } else {
-      err = launch_stream_gate_up(gu, s);
+      err = launch_stream_gate_up(gu, ss);
     }
     if (err != hipSuccess) return K3MOE_ERR_DEVICE;
   }
@@ -291,8 +330,12 @@ int moe_mxfp4_ffn_profiled(const void* x_bf16, const int32_t* topk_ids, const fl
     dn.tile_count = g.tile_count + 3;
     const int64_t r = g.rows_per_tile[3];
     dn.max_tiles = (entries + (r - 1) * active) / r;  // bounds the sum of ceil(n_e / r) over experts
-    err = launch_stream_down(dn, s);
+    err = launch_stream_down(dn, ss);
     if (err != hipSuccess) return K3MOE_ERR_DEVICE;
+  }
+  if (side) {
+    if (hipEventRecord(side->join, side->s) != hipSuccess || hipStreamWaitEvent(s, side->join, 0) != hipSuccess)
+      return K3MOE_ERR_DEVICE;
   }
   if (!mark(3)) return K3MOE_ERR_DEVICE;
 

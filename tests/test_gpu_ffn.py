@@ -163,8 +163,10 @@ def test_large_batch_mixed_with_few_row_experts(k3):
 
 @pytest.mark.parametrize(
     "E,k,D,I,T",
-    # small-tile, streaming (grouping launch; grouping inside the gate/up launch), large-tile paths
-    [(8, 2, 128, 256, 64), (64, 4, 512, 512, 8), (64, 4, 512, 512, 3), (8, 2, 512, 512, 300)],
+    # small-tile, streaming (grouping launch; grouping inside the gate/up launch), large-tile paths, and
+    # large-tile + streaming experts in one call (24 + 12: the streaming launches run on a side stream)
+    [(8, 2, 128, 256, 64), (64, 4, 512, 512, 8), (64, 4, 512, 512, 3), (8, 2, 512, 512, 300),
+     (40, 4, 512, 512, 90)],
 )
 def test_graph_replay_matches_eager(k3, E, k, D, I, T):
     # route + FFN captured into a HIP graph: every replay, with other eager work
