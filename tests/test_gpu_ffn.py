@@ -78,6 +78,7 @@ def test_tiny(k3):
         (4, 2, 512, 512, 8),  # streaming-only batch: experts of up to 8 rows over several 4- and 2-row tiles
         (3, 3, 512, 1024, 5),  # streaming-only batch: every expert has all 5 rows
         (4, 2, 512, 512, 9),  # one token past the streaming-only batch: large-tile kernels for experts of 5+ rows
+        (200, 64, 512, 512, 4),  # grouping inside the gate/up launch: 256 entries, one per thread
     ],
 )
 def test_shapes(k3, E, k, D, I, T):
@@ -126,6 +127,23 @@ def test_streaming_path_hot_invalid_and_duplicate_ids(k3, T):
     assert_ffn_close(got, ref, "streaming hot/invalid/duplicate")
     a = run_ffn(k3, dev, batch.x, ids, w)
     assert np.array_equal(a.view(np.uint32), got.view(np.uint32))
+
+
+def test_self_grouping_duplicates_and_invalid_ids(k3):
+    # 3 tokens x 8 slots drawn from 6 experts with repeats (the grouping inside
+    # the gate/up launch skips repeats of a row), plus ids outside [0, E)
+    print("[ffn] self-grouping with repeated and invalid ids", flush=True)
+    cfg = moe_inputs.TINY.with_(E=40, k=8, D=512, I=512, T=3, config_id=47)
+    g = np.random.default_rng(17)
+    ids = g.integers(0, 6, size=(cfg.T, cfg.k)).astype(np.int32)
+    ids[0, 5] = cfg.E  # out of range
+    ids[2, 0] = -1
+    ids[1, :] = 4  # one expert, every slot: a single valid entry
+    w = g.random((cfg.T, cfg.k)).astype(np.float32)
+    got, ref, batch, dev = small_case(k3, cfg, ids, w)
+    assert_ffn_close(got, ref, "self-grouping repeats/invalid")
+    again = run_ffn(k3, dev, batch.x, ids, w)
+    assert np.array_equal(again.view(np.uint32), got.view(np.uint32))
 
 
 def test_mixed_large_and_streaming_experts(k3):
