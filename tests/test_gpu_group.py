@@ -52,6 +52,7 @@ def test_configs(k3, name):
         (40, 5121, 2),  # one expert more: count / scan / place kernels
         (40, 8192, 2),  # largest supported E
         (3000, 8192, 3),  # many chunks and experts
+        (5000, 896, 16),  # 79 chunks, the last one partial
     ],
 )
 def test_shapes(k3, T, E, k):
