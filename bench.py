@@ -64,15 +64,18 @@ def kernel_info(stage: str, path: str, entries: int = 0, tokens: int = 0):
     if stage in ("gate_up", "down"):
         flag = "true" if stage == "gate_up" else "false"
         rows = 128 if stage == "gate_up" or entries >= 16384 else 64
-        big, stream = f"ffn_big_kernel<{flag}, {rows}>", f"ffn_stream_kernel<{flag}, false>"
+        big, stream = f"ffn_big_kernel<{flag}, {rows}>", f"ffn_stream_kernel<{flag}, false, false>"
         if path == "stream":
-            # up to 4 tokens the gate/up launch groups the entries itself
-            grouped = "true" if stage == "gate_up" and tokens <= 4 else "false"
-            return f"ffn_stream_kernel<{flag}, {grouped}>", [CSRC + "ffn_stream.hip"]
+            # a decode batch is grouped inside the gate/up launch, which reads x in
+            # place up to 4 tokens (else x re-laid out by a small launch first)
+            if stage == "gate_up":
+                nat = "true" if tokens <= 4 else "false"
+                return f"ffn_stream_kernel<true, true, {nat}>", [CSRC + "ffn_stream.hip"]
+            return stream, [CSRC + "ffn_stream.hip"]
         if path == "tiled":
             return f"{big} + {stream}", [CSRC + "ffn_big.hip", CSRC + "ffn_stream.hip"]
         return f"ffn_gemm_kernel<NT, {flag}, ...>", [CSRC + "ffn.hip"]
-    return {"route": ("route_topk_*kernel", [CSRC + "route.hip"]), "group": ("group_*_kernel", [CSRC + "group.hip"]),
+    return {"route": ("route_topk_*kernel", [CSRC + "route.hip"]), "group": ("group_*_kernel / permute_x_kernel", [CSRC + "group.hip"]),
             "combine": ("combine_kernel", [CSRC + "ffn.hip"])}[stage]
 
 

@@ -234,15 +234,16 @@ int moe_mxfp4_ffn_profiled(const void* x_bf16, const int32_t* topk_ids, const fl
     if (!stage_events || !stage_events[i]) return true;
     return hipEventRecord(static_cast<hipEvent_t>(stage_events[i]), s) == hipSuccess;
   };
-  // A streaming-only batch of at most kSelfGroupTokens tokens (and
-  // kSelfGroupEntries entries) is grouped by the gate/up launch itself: no
-  // grouping launch, x read in place.  At one token that saves a tenth of the
-  // step; at 8 tokens both ways take the same time, and the grouping launch's
-  // pre-permuted x keeps the gate/up stream itself faster.
-  constexpr int kSelfGroupTokens = 4;
-  const bool self_group = stream_only && T <= kSelfGroupTokens && entries <= kSelfGroupEntries && E <= 0xFFFF;
+  // A streaming-only batch of at most kSelfGroupEntries entries is grouped by
+  // the gate/up launch itself (no grouping launch).  Up to kNaturalXTokens
+  // tokens that launch also reads x in place; larger decode batches have x
+  // re-laid out first by a small launch, as the operand reads of pre-permuted
+  // x keep the gate/up stream faster.
+  constexpr int kNaturalXTokens = 4;
+  const bool self_group = stream_only && entries <= kSelfGroupEntries && E <= 0xFFFF;
+  const bool natural_x = self_group && T <= kNaturalXTokens;
   if (!mark(0)) return K3MOE_ERR_DEVICE;
-  hipError_t err = self_group ? hipSuccess : launch_group(g, s);
+  hipError_t err = self_group ? (natural_x ? hipSuccess : launch_permute_x(g.x, g.x_perm, T, D, s)) : launch_group(g, s);
   if (err != hipSuccess || !mark(1)) return K3MOE_ERR_DEVICE;
 
   // Upper bounds of the list lengths (sum over experts of ceil(n_e / rpt)):
@@ -307,9 +308,9 @@ int moe_mxfp4_ffn_profiled(const void* x_bf16, const int32_t* topk_ids, const fl
       sg.tile_count = g.tile_count;
       sg.down_tiles = g.tiles[3];
       sg.slot_row = g.slot_row;
-      gu.act = static_cast<const uint16_t*>(x_bf16);
+      gu.act = natural_x ? static_cast<const uint16_t*>(x_bf16) : g.x_perm;
       gu.row_tok = nullptr;
-      err = launch_stream_gate_up_grouped(gu, sg, ss);
+      err = launch_stream_gate_up_grouped(gu, sg, natural_x, ss);
     } else {
       err = launch_stream_gate_up(gu, ss);
     }

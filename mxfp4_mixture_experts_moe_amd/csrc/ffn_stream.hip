@@ -202,9 +202,10 @@ struct Cursor {
   TileInfo tile;  // tile of the unit
 };
 
-template <bool kGateUp, bool kSelfGroup>
+template <bool kGateUp, bool kSelfGroup, bool kNatX>
 __global__ __launch_bounds__(kWaves * 64, 1) void ffn_stream_kernel(GemmArgs a, SelfGroupArgs sg) {
   static_assert(kGateUp || !kSelfGroup, "only the gate/up launch groups");
+  static_assert(kSelfGroup || !kNatX, "x in natural order only with the grouping launch's tokens");
   using C = StreamCfg<kGateUp>;
   constexpr int kSB = kStageBytes<kGateUp>;
   constexpr int kMatBytes = 16 * kStageRowBytes;  // one 16-row block of a stage
@@ -473,7 +474,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ffn_stream_kernel(GemmArgs a, 
 #pragma unroll
     for (int rnd = 0; rnd < 4; ++rnd) {
       bf16x8_t bop[4];
-      if constexpr (kSelfGroup) {
+      if constexpr (kNatX) {
         // x rows in natural order: P-order dword t of operand i pairs
         // elements 4i + t and 16 + 4i + t of block 4*rnd + g
         u32x4_t q[4];  // elements 0-7, 8-15, 16-23, 24-31
@@ -564,14 +565,15 @@ int cu_count() {
   return cached[dev];
 }
 
-template <bool kGateUp, bool kSelfGroup>
+template <bool kGateUp, bool kSelfGroup, bool kNatX>
 hipError_t launch_stream(const GemmArgs& a, const SelfGroupArgs& sg, hipStream_t s) {
   const int64_t max_units = a.max_tiles * (a.N / StreamCfg<kGateUp>::kFeat);
   int64_t grid = (max_units + kWaves - 1) / kWaves;
   const int cus = cu_count();
   if (grid > cus) grid = cus;
   if (grid < 1) grid = 1;  // the self-grouping launch needs workgroup 0 in any case
-  hipLaunchKernelGGL((ffn_stream_kernel<kGateUp, kSelfGroup>), dim3((unsigned)grid), dim3(kWaves * 64), 0, s, a, sg);
+  hipLaunchKernelGGL((ffn_stream_kernel<kGateUp, kSelfGroup, kNatX>), dim3((unsigned)grid), dim3(kWaves * 64), 0, s, a,
+                     sg);
   return hipGetLastError();
 }
 
@@ -583,12 +585,12 @@ bool stream_gemm_supported(int D, int I) { return (D % kStageK) == 0 && (I % kSt
 
 int stream_rows_per_tile(bool gate_up) { return gate_up ? StreamCfg<true>::kTileRows : StreamCfg<false>::kTileRows; }
 
-hipError_t launch_stream_gate_up(const GemmArgs& a, hipStream_t s) { return launch_stream<true, false>(a, {}, s); }
+hipError_t launch_stream_gate_up(const GemmArgs& a, hipStream_t s) { return launch_stream<true, false, false>(a, {}, s); }
 
-hipError_t launch_stream_down(const GemmArgs& a, hipStream_t s) { return launch_stream<false, false>(a, {}, s); }
+hipError_t launch_stream_down(const GemmArgs& a, hipStream_t s) { return launch_stream<false, false, false>(a, {}, s); }
 
-hipError_t launch_stream_gate_up_grouped(const GemmArgs& a, const SelfGroupArgs& sg, hipStream_t s) {
-  return launch_stream<true, true>(a, sg, s);
+hipError_t launch_stream_gate_up_grouped(const GemmArgs& a, const SelfGroupArgs& sg, bool natural_x, hipStream_t s) {
+  return natural_x ? launch_stream<true, true, true>(a, sg, s) : launch_stream<true, true, false>(a, sg, s);
 }
 
 }  // namespace k3moe

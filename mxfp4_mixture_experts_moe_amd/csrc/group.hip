@@ -433,7 +433,21 @@ __global__ __launch_bounds__(kScanThreads) void group_small_kernel(GroupArgs a) 
   permute_rows<4>(a.x, a.x_perm, 0, a.T, a.D, tid, kScanThreads);
 }
 
+// Activation re-layout only, for batches the gate/up launch groups itself.
+__global__ __launch_bounds__(256) void permute_x_kernel(const uint16_t* __restrict__ x, uint16_t* __restrict__ xp,
+                                                         int64_t T, int D) {
+  permute_rows<4>(x, xp, 0, T, D, blockIdx.x * blockDim.x + threadIdx.x, gridDim.x * blockDim.x);
+}
+
 }  // namespace
+
+hipError_t launch_permute_x(const uint16_t* x, uint16_t* xp, int64_t T, int D, hipStream_t s) {
+  const int64_t items = T * (int64_t)(D / 8);  // 8-element groups, four per thread
+  int64_t blocks = (items + 4 * 256 - 1) / (4 * 256);
+  blocks = blocks < 1 ? 1 : (blocks > 1024 ? 1024 : blocks);
+  hipLaunchKernelGGL(permute_x_kernel, dim3((unsigned)blocks), dim3(256), 0, s, x, xp, T, D);
+  return hipGetLastError();
+}
 
 hipError_t launch_group(const GroupArgs& a, hipStream_t s) {
   const int64_t n_chunks = (a.T + kChunkTokens - 1) / kChunkTokens;

@@ -78,6 +78,9 @@ struct GroupArgs {
   uint16_t* x_perm;
 };
 hipError_t launch_group(const GroupArgs& a, hipStream_t s);
+// x [T, D] -> x_perm in the P order of the GEMM operands (the re-layout the
+// grouping launch also does), for batches grouped inside the gate/up launch.
+hipError_t launch_permute_x(const uint16_t* x, uint16_t* xp, int64_t T, int D, hipStream_t s);
 
 struct GemmArgs {
   const uint16_t* act;      // gate/up: x_perm [T, D] (rows via row_tok); down: h_hi [rows, I]
@@ -119,7 +122,8 @@ hipError_t launch_stream_down(const GemmArgs& a, hipStream_t s);
 // kSelfGroupEntries entries, experts below 2^16): every workgroup builds the
 // gate/up tiles in LDS from the ids, and workgroup 0 writes what the kernels
 // after it read (the down tile list, tile_count[2..3], slot_row), so no
-// grouping launch precedes it.  It reads x [T, D] in its natural layout.
+// grouping launch precedes it.  `a.act` is x [T, D] in its natural layout
+// (natural_x) or in P order (launch_permute_x).
 constexpr int kSelfGroupEntries = 512;
 struct SelfGroupArgs {
   const int32_t* ids;   // [T, k]
@@ -128,7 +132,7 @@ struct SelfGroupArgs {
   Tile* down_tiles;     // list 3: 2-row down tiles
   int32_t* slot_row;    // [T * k]: grouped row of each entry, -1 if skipped
 };
-hipError_t launch_stream_gate_up_grouped(const GemmArgs& a, const SelfGroupArgs& sg, hipStream_t s);
+hipError_t launch_stream_gate_up_grouped(const GemmArgs& a, const SelfGroupArgs& sg, bool natural_x, hipStream_t s);
 
 // mixed: rows whose slot_row entry carries kBigRowFlag hold scaled fp16 y.
 hipError_t launch_combine(const float* y, const int8_t* y_scale, bool mixed, const int32_t* slot_row, const float* w,

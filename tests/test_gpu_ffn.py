@@ -109,7 +109,7 @@ def test_hot_expert_invalid_and_duplicate_ids(k3):
     assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
 
 
-@pytest.mark.parametrize("T", [8, 4])  # grouping launch / grouping inside the gate/up launch
+@pytest.mark.parametrize("T", [8, 4])  # grouped in the gate/up launch: x re-laid out first / x read in place
 def test_streaming_path_hot_invalid_and_duplicate_ids(k3, T):
     # decode-sized batch (at most 4 rows per active expert on average) with one
     # expert in every row: its T rows span one or two 4-row tiles
@@ -181,7 +181,7 @@ def test_large_batch_mixed_with_few_row_experts(k3):
 
 @pytest.mark.parametrize(
     "E,k,D,I,T",
-    # small-tile, streaming (grouping launch; grouping inside the gate/up launch), large-tile paths, and
+    # small-tile, streaming (grouped in the gate/up launch, x re-laid out first / read in place), large-tile, and
     # large-tile + streaming experts in one call (24 + 12: the streaming launches run on a side stream)
     [(8, 2, 128, 256, 64), (64, 4, 512, 512, 8), (64, 4, 512, 512, 3), (8, 2, 512, 512, 300),
      (40, 4, 512, 512, 90)],
