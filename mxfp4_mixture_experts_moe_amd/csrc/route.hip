@@ -8,11 +8,16 @@
 // expert index; NaN scores rank last.
 //
 // Up to 1024 experts (16 per lane) the scores live in registers: lane l owns
-// experts l, l + 64, l + 128, ..., sorted once by a bitonic network, and its
-// best remaining one is its "head".  Each of the k rounds reduces the 64 heads
-// to the wave's best (four DPP exchanges inside each 16-lane row, two row
-// swaps across rows); only the lane that owned the winner moves to its next
-// expert.  Small batches split each token over a workgroup of four waves
+// experts l, l + 64, l + 128, ....  One wave per token (large batches): the
+// 64 lane-bests are sorted across the wave; the k-th of them ranks at or
+// after every expert of the top k, so the top k are among the experts ranking
+// at or before it, which (when there are at most 64) are compacted through
+// LDS and sorted once.  Otherwise (heavy ties), and in the four-wave kernel of
+// small batches, where a token's latency is the whole cost, each lane sorts
+// its experts by a bitonic network and its best remaining one is its "head";
+// each of the k rounds reduces the 64 heads to the wave's best (four DPP
+// exchanges inside each 16-lane row, two row swaps across rows) and only the
+// lane that owned the winner moves to its next expert.  Small batches split each token over a workgroup of four waves
 // (each finds the k best of a quarter of the experts; one wave orders the
 // candidates).  Larger E falls back to a kernel that writes the scores to LDS (or
 // recomputes them) and, in round r, picks the best expert ranking strictly
@@ -123,6 +128,99 @@ __device__ __forceinline__ void sort_desc(double (&sc)[N], int (&ix)[N]) {
       }
 }
 
+// Bitonic sort of one (s, e) per lane across the wave, first-ranked in lane 0.
+// The entries are distinct experts or identical sentinels, so "ranks before"
+// is a strict order on them.
+__device__ __forceinline__ void wave_sort64(double& cs, int& ce, int lane) {
+#pragma unroll
+  for (int size = 2; size <= kWaveSize; size <<= 1) {
+#pragma unroll
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      const double os = __shfl_xor(cs, stride, kWaveSize);
+      const int oe = __shfl_xor(ce, stride, kWaveSize);
+      // In a run sorted first-ranked-first the lower lane of each pair keeps
+      // the earlier-ranked entry; runs with bit `size` set sort the other way
+      // (the last run, size 64, sorts first-ranked-first).
+      const bool keep_first = ((lane & stride) == 0) == ((lane & size) == 0);
+      const bool take = keep_first ? ranks_before(os, oe, cs, ce) : ranks_before(cs, ce, os, oe);
+      if (take) {
+        cs = os;
+        ce = oe;
+      }
+    }
+  }
+}
+
+__device__ __forceinline__ double readlane_f64(double v, int l) {
+  const uint64_t b = __double_as_longlong(v);
+  const uint32_t lo = __builtin_amdgcn_readlane((int)(uint32_t)b, l);
+  const uint32_t hi = __builtin_amdgcn_readlane((int)(uint32_t)(b >> 32), l);
+  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+
+// The k (<= 64) best (s, e) of the wave's NPER-per-lane entries, first-ranked
+// in lane 0, with no per-lane sort and no k rounds.  Of the 64 lane-bests, the
+// k-th ranks at or after every entry of the top k (the k lane-bests before it
+// are k entries ranking at or before it), so the top k are among the entries
+// that rank at or before it.  When at most 64 entries qualify they are
+// compacted through `ls` / `le` (this wave's 64 doubles and 64 ints of LDS)
+// and sorted once; otherwise (heavy ties) nothing is written to out_* and the
+// caller takes its k-round path.  Wave-uniform result.
+template <int NPER>
+__device__ __forceinline__ bool wave_topk_filtered(const double (&sc)[NPER], const int (&ix)[NPER], int k, int lane,
+                                                    double* ls, int* le, double& out_s, int& out_e) {
+  double bs = sc[0];
+  int be = ix[0];
+#pragma unroll
+  for (int j = 1; j < NPER; ++j)
+    if (ranks_before(sc[j], ix[j], bs, be)) {
+      bs = sc[j];
+      be = ix[j];
+    }
+  wave_sort64(bs, be, lane);
+  const double ts = readlane_f64(bs, k - 1);
+  const int te = __builtin_amdgcn_readlane(be, k - 1);
+  unsigned qual = 0u;
+  int cnt = 0;
+#pragma unroll
+  for (int j = 0; j < NPER; ++j) {
+    const bool q = (sc[j] == ts && ix[j] == te) || ranks_before(sc[j], ix[j], ts, te);
+    qual |= (q ? 1u : 0u) << j;
+    cnt += q ? 1 : 0;
+  }
+  int incl = cnt;
+#pragma unroll
+  for (int d = 1; d < kWaveSize; d <<= 1) {
+    const int o = __shfl_up(incl, d, kWaveSize);
+    if (lane >= d) incl += o;
+  }
+  const int total = __builtin_amdgcn_readlane(incl, kWaveSize - 1);
+  if (total > kWaveSize) return false;
+  int pos = incl - cnt;
+#pragma unroll
+  for (int j = 0; j < NPER; ++j)
+    if (qual & (1u << j)) {
+      ls[pos] = sc[j];
+      le[pos] = ix[j];
+      ++pos;
+    }
+  // LDS accesses of one wave complete in order; the fences keep the compiler
+  // from moving the reads below above these writes.
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  double cs = -INFINITY;
+  int ce = INT_MAX;  // sentinel: ranks after every real expert
+  if (lane < total) {
+    cs = ls[lane];
+    ce = le[lane];
+  }
+  wave_sort64(cs, ce, lane);
+  out_s = cs;
+  out_e = ce;
+  return true;
+}
+
 // Register-resident router: NPER experts per lane (E <= 64 * NPER).  Each lane
 // sorts its experts once; a round takes the wave's best head and the lane that
 // owned it moves to its next expert.
@@ -155,22 +253,30 @@ __global__ __launch_bounds__(256) void route_topk_reg_kernel(const float* __rest
     sc[j] = e < E ? route_score(zv[j], bv[j]) : -INFINITY;
     ix[j] = e < E ? e : INT_MAX;
   }
-  sort_desc<NPER>(sc, ix);
 
+  // lanes 0..k-1 end with the top k in rank order: filtered selection, or
+  // (more than 64 entries at or before the threshold) sorted lanes and k rounds
+  __shared__ double fs[4][kWaveSize];
+  __shared__ int fe[4][kWaveSize];
+  const int wv = threadIdx.x / kWaveSize;
+  double fs_out;
   int my_id = 0;
-  for (int r = 0; r < k; ++r) {
-    double bs = sc[0];
-    int be = ix[0];
-    wave_best(bs, be, lane);
-    if (lane == r) my_id = be;
-    if (lane == (be & (kWaveSize - 1))) {  // k <= E, so be is a real expert owned by this lane
+  if (!wave_topk_filtered<NPER>(sc, ix, k, lane, fs[wv], fe[wv], fs_out, my_id)) {
+    sort_desc<NPER>(sc, ix);
+    for (int r = 0; r < k; ++r) {
+      double bs = sc[0];
+      int be = ix[0];
+      wave_best(bs, be, lane);
+      if (lane == r) my_id = be;
+      if (lane == (be & (kWaveSize - 1))) {  // k <= E, so be is a real expert owned by this lane
 #pragma unroll
-      for (int j = 0; j + 1 < NPER; ++j) {
-        sc[j] = sc[j + 1];
-        ix[j] = ix[j + 1];
+        for (int j = 0; j + 1 < NPER; ++j) {
+          sc[j] = sc[j + 1];
+          ix[j] = ix[j + 1];
+        }
+        sc[NPER - 1] = -INFINITY;
+        ix[NPER - 1] = INT_MAX;
       }
-      sc[NPER - 1] = -INFINITY;
-      ix[NPER - 1] = INT_MAX;
     }
   }
 
@@ -223,29 +329,33 @@ __global__ __launch_bounds__(256) void route_topk_blk_kernel(const float* __rest
     sc[j] = e < E ? route_score(zv[j], bv[j]) : -INFINITY;
     ix[j] = e < E ? e : INT_MAX;
   }
-  sort_desc<NPER>(sc, ix);
 
-  // k rounds over this wave's share.  Expert e sits in lane e % 64 of its
-  // wave; a sentinel winner (a share with fewer than k experts) only shifts
-  // sentinels.
+  // k rounds over this wave's share (a token's latency is the whole cost
+  // here, and the rounds' DPP exchanges are shorter than the filtered
+  // selection's two 21-step shuffle networks).  Expert e sits in lane e % 64
+  // of its wave; a sentinel winner (a share with fewer than k experts) only
+  // shifts sentinels.
   double my_s = -INFINITY;
   int my_e = INT_MAX;
-  for (int r = 0; r < k; ++r) {
-    double bs = sc[0];
-    int be = ix[0];
-    wave_best(bs, be, lane);
-    if (lane == r) {
-      my_s = bs;
-      my_e = be;
-    }
-    if (lane == (be & (kWaveSize - 1))) {
-#pragma unroll
-      for (int j = 0; j + 1 < NPER; ++j) {
-        sc[j] = sc[j + 1];
-        ix[j] = ix[j + 1];
+  {
+    sort_desc<NPER>(sc, ix);
+    for (int r = 0; r < k; ++r) {
+      double bs = sc[0];
+      int be = ix[0];
+      wave_best(bs, be, lane);
+      if (lane == r) {
+        my_s = bs;
+        my_e = be;
       }
-      sc[NPER - 1] = -INFINITY;
-      ix[NPER - 1] = INT_MAX;
+      if (lane == (be & (kWaveSize - 1))) {
+#pragma unroll
+        for (int j = 0; j + 1 < NPER; ++j) {
+          sc[j] = sc[j + 1];
+          ix[j] = ix[j + 1];
+        }
+        sc[NPER - 1] = -INFINITY;
+        ix[NPER - 1] = INT_MAX;
+      }
     }
   }
   if (lane < k) {
@@ -261,26 +371,8 @@ __global__ __launch_bounds__(256) void route_topk_blk_kernel(const float* __rest
     cs = cand_s[lane];
     ce = cand_e[lane];
   }
-  // Bitonic sort of the 64 lanes' candidates, first-ranked in lane 0.  The
-  // candidates are distinct experts or identical sentinels, so "ranks
-  // before" is a strict order on them.
-#pragma unroll
-  for (int size = 2; size <= kWaveSize; size <<= 1) {
-#pragma unroll
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      const double os = __shfl_xor(cs, stride, kWaveSize);
-      const int oe = __shfl_xor(ce, stride, kWaveSize);
-      // In a run sorted first-ranked-first the lower lane of each pair keeps
-      // the earlier-ranked candidate; runs with bit `size` set sort the other
-      // way (the last run, size 64, sorts first-ranked-first).
-      const bool keep_first = ((lane & stride) == 0) == ((lane & size) == 0);
-      const bool take = keep_first ? ranks_before(os, oe, cs, ce) : ranks_before(cs, ce, os, oe);
-      if (take) {
-        cs = os;
-        ce = oe;
-      }
-    }
-  }
+  // the 4k candidates, first-ranked in lane 0
+  wave_sort64(cs, ce, lane);
 
   const int my_id = ce;
   double g = 0.0;
