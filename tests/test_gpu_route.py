@@ -84,6 +84,24 @@ def test_ties_nan_and_options(k3):
     check(k3, zz[:, :16].copy(), bb[:16].copy(), 16, what="k == E")
 
 
+def test_large_batch_router_ties_and_fallback(k3):
+    # more than 256 tokens: the one-wave router's filtered selection, and its
+    # k-round fallback when more than 64 experts tie at the threshold
+    g = np.random.default_rng(10)
+    z = np.round(g.standard_normal((300, 896)), 1).astype(np.float32)  # many exact ties
+    z[0, :] = 0.25  # every expert equal: fallback
+    z[1, :448] = 1.0  # half the experts tie for first place: fallback
+    z[2, 5] = np.nan
+    z[3, :] = np.nan
+    z[4, 9] = np.inf
+    check(k3, z, None, 16, what="T=300 rounded/equal/nan")
+    b = np.round(g.standard_normal(896) * 0.1, 2).astype(np.float32)
+    check(k3, z, b, 16, what="T=300 rounded with bias")
+    z2 = g.standard_normal((300, 1024)).astype(np.float32)
+    check(k3, z2, None, 64, what="T=300 E=1024 k=64")
+    check(k3, z2[:, :70].copy(), None, 64, what="T=300 E=70 k=64")
+
+
 def test_empty_and_determinism(k3):
     ids, w = k3.moe_route_topk(torch.empty((0, 896), device="cuda"), None, 16)
     assert ids.shape == (0, 16)
