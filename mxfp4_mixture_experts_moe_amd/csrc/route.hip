@@ -128,28 +128,60 @@ __device__ __forceinline__ void sort_desc(double (&sc)[N], int (&ix)[N]) {
       }
 }
 
+// (s, e) of lane ^ S, by DPP and row swaps only (no LDS round trip): quad
+// permutes for S = 1, 2; for S = 4 the half-row mirror (lane ^ 7 within 8)
+// followed by the quad reversal (^ 3); for S = 8 the row mirror (^ 15 within
+// 16) followed by the half-row mirror (^ 7); row swaps for S = 16, 32.
+template <int S>
+__device__ __forceinline__ void xor_pair(double s, int e, int lane, double& os, int& oe) {
+  if constexpr (S == 1) {
+    dpp_pair<0xB1>(s, e, os, oe);  // quad_perm [1,0,3,2]
+  } else if constexpr (S == 2) {
+    dpp_pair<0x4E>(s, e, os, oe);  // quad_perm [2,3,0,1]
+  } else if constexpr (S == 4) {
+    double ts;
+    int te;
+    dpp_pair<0x141>(s, e, ts, te);  // row_half_mirror
+    dpp_pair<0x1B>(ts, te, os, oe);  // quad_perm [3,2,1,0]
+  } else if constexpr (S == 8) {
+    double ts;
+    int te;
+    dpp_pair<0x140>(s, e, ts, te);   // row_mirror
+    dpp_pair<0x141>(ts, te, os, oe);  // row_half_mirror
+  } else {
+    static_assert(S == 16 || S == 32, "lane xor stride");
+    swap_pair<S>(s, e, lane, os, oe);
+  }
+}
+
+// One compare-exchange step of the bitonic network (runs of SIZE, partner
+// lane ^ STRIDE) and the steps after it within the same merge.  In a run
+// sorted first-ranked-first the lower lane of each pair keeps the earlier-
+// ranked entry; runs with bit SIZE set sort the other way (the last run, size
+// 64, sorts first-ranked-first).
+template <int SIZE, int STRIDE>
+__device__ __forceinline__ void bitonic_steps(double& cs, int& ce, int lane) {
+  double os;
+  int oe;
+  xor_pair<STRIDE>(cs, ce, lane, os, oe);
+  const bool keep_first = ((lane & STRIDE) == 0) == ((lane & SIZE) == 0);
+  const bool take = keep_first ? ranks_before(os, oe, cs, ce) : ranks_before(cs, ce, os, oe);
+  if (take) {
+    cs = os;
+    ce = oe;
+  }
+  if constexpr (STRIDE > 1) bitonic_steps<SIZE, STRIDE / 2>(cs, ce, lane);
+}
+template <int SIZE>
+__device__ __forceinline__ void bitonic_merges(double& cs, int& ce, int lane) {
+  bitonic_steps<SIZE, SIZE / 2>(cs, ce, lane);
+  if constexpr (SIZE < kWaveSize) bitonic_merges<SIZE * 2>(cs, ce, lane);
+}
+
 // Bitonic sort of one (s, e) per lane across the wave, first-ranked in lane 0.
 // The entries are distinct experts or identical sentinels, so "ranks before"
 // is a strict order on them.
-__device__ __forceinline__ void wave_sort64(double& cs, int& ce, int lane) {
-#pragma unroll
-  for (int size = 2; size <= kWaveSize; size <<= 1) {
-#pragma unroll
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      const double os = __shfl_xor(cs, stride, kWaveSize);
-      const int oe = __shfl_xor(ce, stride, kWaveSize);
-      // In a run sorted first-ranked-first the lower lane of each pair keeps
-      // the earlier-ranked entry; runs with bit `size` set sort the other way
-      // (the last run, size 64, sorts first-ranked-first).
-      const bool keep_first = ((lane & stride) == 0) == ((lane & size) == 0);
-      const bool take = keep_first ? ranks_before(os, oe, cs, ce) : ranks_before(cs, ce, os, oe);
-      if (take) {
-        cs = os;
-        ce = oe;
-      }
-    }
-  }
-}
+__device__ __forceinline__ void wave_sort64(double& cs, int& ce, int lane) { bitonic_merges<2>(cs, ce, lane); }
 
 __device__ __forceinline__ double readlane_f64(double v, int l) {
   const uint64_t b = __double_as_longlong(v);
