@@ -242,8 +242,13 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ffn_stream_kernel(GemmArgs a, 
     __syncthreads();
     EntryInfo en[2];
     int carry[3] = {0, 0, 0};
+    const int rounds = n > kThreads ? 2 : 1;  // uniform: every thread takes the scans' barriers
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
+      if (r >= rounds) {
+        en[r] = EntryInfo{-1, 0, 0, 0, -1, 0u, false};
+        continue;
+      }
       const int i = tid + kThreads * r;
       EntryInfo& e = en[r];
       e = EntryInfo{-1, 0, 0, 0, -1, 0u, false};
