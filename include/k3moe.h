@@ -12,8 +12,9 @@
  *     allocates and owns every buffer; the library allocates no memory and
  *     never synchronizes the host. Its only state is moe_mxfp4_ffn's side
  *     stream (below).
- *   - `stream` is a hipStream_t (NULL = the default stream). Every call only
- *     enqueues work on it and returns; results are ready when the stream is.
+ *   - `stream` is a hipStream_t (NULL = the default stream) of the current
+ *     device, which also holds every buffer passed. Every call only enqueues
+ *     work on it and returns; results are ready when the stream is.
  *   - Arrays are row-major and contiguous. Inputs are never written. Outputs
  *     are fully overwritten (never accumulated into).
  *   - Every argument check runs on the host before anything is enqueued; a
