@@ -24,6 +24,9 @@ namespace {
 
 constexpr int kScanThreads = 1024;
 constexpr int kMaxExpertsPerScanThread = 8;  // 8 * 1024 = K3MOE_MAX_EXPERTS_FFN
+// Experts per scan thread: thread t owns experts t*n .. t*n + n - 1, so the
+// block scan runs in expert order.  As few as possible (one up to 1024
+// experts): the owner also writes its experts' tiles one after another.
 
 // Workgroup barrier for LDS traffic only.  __syncthreads() also waits for every
 // outstanding global load and store of the wave (its release fence), which
@@ -146,11 +149,12 @@ __device__ __forceinline__ void scan_experts(const GroupArgs& a, const unsigned 
                                              int32_t* base) {
   const int tid = threadIdx.x, E = a.E;
   const TileSpec ts = tile_spec(a);
-  const int e0 = tid * kMaxExpertsPerScanThread;
+  const int per = (E + kScanThreads - 1) / kScanThreads;  // <= kMaxExpertsPerScanThread
+  const int e0 = tid * per;
   // pass 1: this thread's row and tile totals (counts are recomputed in pass 2
   // rather than kept in a per-thread array)
   int v[1 + kTileLists] = {0, 0, 0, 0, 0};
-  for (int i = 0; i < kMaxExpertsPerScanThread; ++i) {
+  for (int i = 0; i < per; ++i) {
     const int e = e0 + i;
     if (e >= E) break;
     int cnt = 0;
@@ -160,7 +164,7 @@ __device__ __forceinline__ void scan_experts(const GroupArgs& a, const unsigned 
   int total[1 + kTileLists];
   block_exclusive_scan_n(v, total);
   // pass 2: offsets, per-chunk bases and tiles of each expert
-  for (int i = 0; i < kMaxExpertsPerScanThread; ++i) {
+  for (int i = 0; i < per; ++i) {
     const int e = e0 + i;
     if (e >= E) break;
     const int row_off = v[0];
@@ -290,16 +294,17 @@ __global__ __launch_bounds__(kScanThreads) void group_scan_kernel(GroupArgs a, i
   lds_barrier();
   // offsets and tiles: thread t owns experts 8t..8t+7
   const TileSpec ts = tile_spec(a);
-  const int e0 = tid * kMaxExpertsPerScanThread;
+  const int per = (E + kScanThreads - 1) / kScanThreads;  // <= kMaxExpertsPerScanThread
+  const int e0 = tid * per;
   int v[1 + kTileLists] = {0, 0, 0, 0, 0};
-  for (int i = 0; i < kMaxExpertsPerScanThread; ++i) {
+  for (int i = 0; i < per; ++i) {
     const int e = e0 + i;
     if (e >= E) break;
     add_expert(ts, ltot[e], v);
   }
   int total[1 + kTileLists];
   block_exclusive_scan_n(v, total);
-  for (int i = 0; i < kMaxExpertsPerScanThread; ++i) {
+  for (int i = 0; i < per; ++i) {
     const int e = e0 + i;
     if (e >= E) break;
     const int cnt = ltot[e];
@@ -399,16 +404,17 @@ __global__ __launch_bounds__(kScanThreads) void group_small_kernel(GroupArgs a) 
   lds_barrier();
 
   const TileSpec ts = tile_spec(a);
-  const int e0 = tid * kMaxExpertsPerScanThread;
+  const int per = (E + kScanThreads - 1) / kScanThreads;  // <= kMaxExpertsPerScanThread
+  const int e0 = tid * per;
   int v[1 + kTileLists] = {0, 0, 0, 0, 0};
-  for (int i = 0; i < kMaxExpertsPerScanThread; ++i) {
+  for (int i = 0; i < per; ++i) {
     const int ex = e0 + i;
     if (ex >= E) break;
     add_expert(ts, __popcll(lmask[ex]), v);
   }
   int total[1 + kTileLists];
   block_exclusive_scan_n(v, total);
-  for (int i = 0; i < kMaxExpertsPerScanThread; ++i) {
+  for (int i = 0; i < per; ++i) {
     const int ex = e0 + i;
     if (ex >= E) break;
     const int cnt = __popcll(lmask[ex]);
