@@ -23,9 +23,9 @@ namespace k3moe {
 namespace {
 
 constexpr int kScanThreads = 1024;
-constexpr int kMaxExpertsPerScanThread = 8;  // 8 * 1024 = K3MOE_MAX_EXPERTS_FFN
-// Experts per scan thread: thread t owns experts t*n .. t*n + n - 1, so the
-// block scan runs in expert order.  As few as possible (one up to 1024
+// Experts per scan thread: thread t owns experts t*n .. t*n + n - 1 with
+// n = ceil(E / kScanThreads) (at most 8 for the largest expert count, 8192),
+// so the block scan runs in expert order.  As few as possible (one up to 1024
 // experts): the owner also writes its experts' tiles one after another.
 
 // Workgroup barrier for LDS traffic only.  __syncthreads() also waits for every
@@ -149,7 +149,7 @@ __device__ __forceinline__ void scan_experts(const GroupArgs& a, const unsigned 
                                              int32_t* base) {
   const int tid = threadIdx.x, E = a.E;
   const TileSpec ts = tile_spec(a);
-  const int per = (E + kScanThreads - 1) / kScanThreads;  // <= kMaxExpertsPerScanThread
+  const int per = (E + kScanThreads - 1) / kScanThreads;
   const int e0 = tid * per;
   // pass 1: this thread's row and tile totals (counts are recomputed in pass 2
   // rather than kept in a per-thread array)
@@ -294,7 +294,7 @@ __global__ __launch_bounds__(kScanThreads) void group_scan_kernel(GroupArgs a, i
   lds_barrier();
   // offsets and tiles: thread t owns experts 8t..8t+7
   const TileSpec ts = tile_spec(a);
-  const int per = (E + kScanThreads - 1) / kScanThreads;  // <= kMaxExpertsPerScanThread
+  const int per = (E + kScanThreads - 1) / kScanThreads;
   const int e0 = tid * per;
   int v[1 + kTileLists] = {0, 0, 0, 0, 0};
   for (int i = 0; i < per; ++i) {
@@ -404,7 +404,7 @@ __global__ __launch_bounds__(kScanThreads) void group_small_kernel(GroupArgs a) 
   lds_barrier();
 
   const TileSpec ts = tile_spec(a);
-  const int per = (E + kScanThreads - 1) / kScanThreads;  // <= kMaxExpertsPerScanThread
+  const int per = (E + kScanThreads - 1) / kScanThreads;
   const int e0 = tid * per;
   int v[1 + kTileLists] = {0, 0, 0, 0, 0};
   for (int i = 0; i < per; ++i) {
