@@ -26,6 +26,13 @@
 // The MFMA still does the multiply: its 16 columns are the tile's (up to 4)
 // rows, the unused columns hold whatever the LDS row slots hold and are never
 // stored.
+//
+// Decode batches (kSelfGroup): the gate/up launch first groups the routed
+// entries itself, identically in every workgroup, from the ids (tiles in LDS,
+// tokens of a tile's rows in 4-bit fields), and workgroup 0 writes the down
+// tile list, tile counts and slot_row for the launches after it.  With kNatX
+// it reads x in its natural layout and builds the P-order operand pairs with
+// v_perm; otherwise x arrives re-laid out (P order) by a small launch.
 #include "k3moe_internal.h"
 
 #include <math.h>
@@ -205,7 +212,7 @@ struct Cursor {
 template <bool kGateUp, bool kSelfGroup, bool kNatX>
 __global__ __launch_bounds__(kWaves * 64, 1) void ffn_stream_kernel(GemmArgs a, SelfGroupArgs sg) {
   static_assert(kGateUp || !kSelfGroup, "only the gate/up launch groups");
-  static_assert(kSelfGroup || !kNatX, "x in natural order only with the grouping launch's tokens");
+  static_assert(kSelfGroup || !kNatX, "natural-order x only in the self-grouping launch (x rows by token)");
   using C = StreamCfg<kGateUp>;
   constexpr int kSB = kStageBytes<kGateUp>;
   constexpr int kMatBytes = 16 * kStageRowBytes;  // one 16-row block of a stage
