@@ -65,6 +65,7 @@ constexpr int kARowDw = 68;     // LDS dwords per activation row per stage (256 
 constexpr int kARowChunks = 17; // 16-byte chunks per activation row (16 data + 1 pad)
 constexpr int kXcds = 8;
 constexpr int kMaxSlices = 64;  // 256-wide slices of I the down kernel supports (I <= 16384)
+constexpr int kRescaleSpan = 64;  // down: largest slice-scale spread of a row for the rescaling K loop
 
 // kTok: token rows of a workgroup tile.  The down product has two: 128-row
 // tiles give a workgroup twice the matrix work between barriers (large
@@ -200,14 +201,25 @@ __global__ __launch_bounds__(kThreads) void ffn_big_kernel(GemmArgs a) {
     }
   }
   __syncthreads();
+  // down: true when every row's slice scales lie within kRescaleSpan of its
+  // largest (always, for h a gated MLP produces): the K loop then reads h as
+  // stored and rescales the fp32 sums at each slice boundary instead
+  bool rescale = false;
   if constexpr (!kGateUp) {
+    int spread = 0;
     if (tid < C::kN) {
       const int nsl = K >> 8;
-      int mx = -128;
-      for (int sl = 0; sl < nsl; ++sl) mx = max(mx, (int)hs_l[tid * kMaxSlices + sl]);
+      int mx = -128, mn = 127;
+      for (int sl = 0; sl < nsl; ++sl) {
+        const int v = hs_l[tid * kMaxSlices + sl];
+        mx = max(mx, v);
+        mn = min(mn, v);
+      }
       srow_l[tid] = mx;
+      spread = mx - mn;
     }
-    // read after the barrier that follows the first stage's loads
+    rescale = !__syncthreads_or(spread > kRescaleSpan ? 1 : 0);
+    // srow_l is read after the barrier that follows the first stage's loads
   }
 
   // ---- per-lane load descriptors (constant over K) ----
@@ -313,6 +325,24 @@ __global__ __launch_bounds__(kThreads) void ffn_big_kernel(GemmArgs a) {
     const _Float16 m = __builtin_bit_cast(_Float16, (uint16_t)hmul[tg]);
     return v * m;
   };
+  // Rescaling variant: the sums of token row t are kept in units of 2^(scale
+  // of the slice being read); entering slice sl they are multiplied by
+  // 2^(scale[sl-1] - scale[sl]), after the last slice by 2^(scale - row
+  // scale), so the epilogue finds them in row-scale units as above.  The
+  // factors are powers of two within 2^+-kRescaleSpan: exact, and with h below
+  // 2^15 in every slice's units the sums stay far inside the fp32 range.
+  auto rescale_acc = [&](int sl_from, int to_row) {
+#pragma unroll
+    for (int tg = 0; tg < (kGateUp ? 1 : C::kTG); ++tg) {
+      const int t = tg * 16 + rho;
+      const int to = to_row ? srow_l[t] : (int)hs_l[t * kMaxSlices + sl_from + 1];
+      const float f = ldexpf(1.0f, (int)hs_l[t * kMaxSlices + sl_from] - to);
+#pragma unroll
+      for (int rg = 0; rg < C::kRG; ++rg)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) acc[0][rg][tg][v] *= f;
+    }
+  };
 
   const int nstages = K / kKStep;
 
@@ -320,10 +350,11 @@ __global__ __launch_bounds__(kThreads) void ffn_big_kernel(GemmArgs a) {
   // kFull: every token group of the tile is live (the unguarded fast path)
   // down: set when a wave met a w2 block the fp16 path cannot hold exactly
   bool wide_seen = false;
-  auto run_stage = [&](auto ph_tag, auto full_tag, auto exact_tag, int s) {
+  auto run_stage = [&](auto ph_tag, auto full_tag, auto exact_tag, auto resc_tag, int s) {
     constexpr int PH = decltype(ph_tag)::value;
     constexpr bool kFull = decltype(full_tag)::value;
     constexpr bool kExact = decltype(exact_tag)::value;  // down: the exact bf16-pair pass
+    constexpr bool kResc = decltype(resc_tag)::value;    // down, fp16 pass: rescaled sums, h read as stored
     const int buf = PH & 1;  // s % 2 == PH % 2 because s % 4 == PH
     if (s + 1 < nstages) issue(s + 1, buf ^ 1);
     const uint32_t* wl = buf ? lds1 : lds0;
@@ -389,7 +420,13 @@ __global__ __launch_bounds__(kThreads) void ffn_big_kernel(GemmArgs a) {
         }
       }
     } else {
-      if constexpr ((PH & 1) == 0) slice_mults(s >> 1);  // the step opens a 256-wide slice of h
+      if constexpr ((PH & 1) == 0) {  // the step opens a 256-wide slice of h
+        if constexpr (kResc) {
+          if (s > 0) rescale_acc((s >> 1) - 1, 0);
+        } else {
+          slice_mults(s >> 1);
+        }
+      }
       // fp16 holds every w2 value of a block exactly when its exponent byte is
       // in 104..140.  The fp16 pass notes any other block; the workgroup then
       // redoes the tile with the exact pass.
@@ -406,7 +443,9 @@ __global__ __launch_bounds__(kThreads) void ffn_big_kernel(GemmArgs a) {
         for (int i = 0; i < 4; ++i) {
           auto bread = [&](int n) {
             const int row = n * 16 + rho;
-            return scale_h(__builtin_bit_cast(f16x8_t, *reinterpret_cast<const uint4*>(al + row * kARowDw + 4 * (4 * g + i))), n);
+            const f16x8_t hv = __builtin_bit_cast(f16x8_t, *reinterpret_cast<const uint4*>(al + row * kARowDw + 4 * (4 * g + i)));
+            if constexpr (kResc) return hv;
+            else return scale_h(hv, n);
           };
           f16x8_t anext[C::kRG];
           f16x8_t bnext = bread(0);
@@ -457,21 +496,29 @@ __global__ __launch_bounds__(kThreads) void ffn_big_kernel(GemmArgs a) {
     __syncthreads();
   };
 
-  auto k_loop = [&](auto full_tag, auto exact_tag) {
+  auto k_loop = [&](auto full_tag, auto exact_tag, auto resc_tag) {
     for (int s = 0; s < nstages; s += 4) {
-      run_stage(std::integral_constant<int, 0>{}, full_tag, exact_tag, s);
-      if (s + 1 < nstages) run_stage(std::integral_constant<int, 1>{}, full_tag, exact_tag, s + 1);
-      if (s + 2 < nstages) run_stage(std::integral_constant<int, 2>{}, full_tag, exact_tag, s + 2);
-      if (s + 3 < nstages) run_stage(std::integral_constant<int, 3>{}, full_tag, exact_tag, s + 3);
+      run_stage(std::integral_constant<int, 0>{}, full_tag, exact_tag, resc_tag, s);
+      if (s + 1 < nstages) run_stage(std::integral_constant<int, 1>{}, full_tag, exact_tag, resc_tag, s + 1);
+      if (s + 2 < nstages) run_stage(std::integral_constant<int, 2>{}, full_tag, exact_tag, resc_tag, s + 2);
+      if (s + 3 < nstages) run_stage(std::integral_constant<int, 3>{}, full_tag, exact_tag, resc_tag, s + 3);
     }
   };
   issue(0, 0);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
-  if (ntg == C::kTG)
-    k_loop(std::true_type{}, std::false_type{});
-  else
-    k_loop(std::false_type{}, std::false_type{});
+  if (!kGateUp && rescale) {
+    if (ntg == C::kTG)
+      k_loop(std::true_type{}, std::false_type{}, std::true_type{});
+    else
+      k_loop(std::false_type{}, std::false_type{}, std::true_type{});
+    rescale_acc((K >> 8) - 1, 1);  // to row-scale units
+  } else {
+    if (ntg == C::kTG)
+      k_loop(std::true_type{}, std::false_type{}, std::false_type{});
+    else
+      k_loop(std::false_type{}, std::false_type{}, std::false_type{});
+  }
   if constexpr (!kGateUp) {
     if (__syncthreads_or(wide_seen ? 1 : 0)) {  // rare: w2 exponents outside 104..140
 #pragma unroll
@@ -482,9 +529,9 @@ __global__ __launch_bounds__(kThreads) void ffn_big_kernel(GemmArgs a) {
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
       if (ntg == C::kTG)
-        k_loop(std::true_type{}, std::true_type{});
+        k_loop(std::true_type{}, std::true_type{}, std::false_type{});
       else
-        k_loop(std::false_type{}, std::true_type{});
+        k_loop(std::false_type{}, std::true_type{}, std::false_type{});
     }
   }
 
