@@ -276,6 +276,57 @@ def test_large_tile_extreme_activation_scale(k3, shift, T, k):
     assert_ffn_close(got, ref, f"large-tile x * 2^{shift}")
 
 
+class ScaledExperts:
+    """Source-layout experts of `cfg` with the E8M0 bytes of the first 256
+    intermediate features overridden: w1 / w3 rows 0..255 get `e_gu`, w2
+    blocks 0..7 (columns 0..255) get `e_dn`."""
+
+    def __init__(self, cfg, e_gu, e_dn):
+        src = moe_inputs.ExpertSource(cfg)
+        self.mats = []
+        for e in range(cfg.E):
+            (p1, s1), (p3, s3), (p2, s2) = src[e]
+            s1, s3, s2 = s1.copy(), s3.copy(), s2.copy()
+            s1[:256, :] = e_gu
+            s3[:256, :] = e_gu
+            s2[:, :8] = e_dn
+            self.mats.append(((p1, s1), (p3, s3), (p2, s2)))
+
+    def __getitem__(self, e):
+        return self.mats[e]
+
+    def __len__(self):
+        return len(self.mats)
+
+    def upload(self, k3, cfg):
+        dev = {}
+        for name, (shape, i) in {"w1": ((cfg.I, cfg.D), 0), "w3": ((cfg.I, cfg.D), 1), "w2": ((cfg.D, cfg.I), 2)}.items():
+            t = torch.empty((cfg.E, shape[0], shape[1] // 32, 17), dtype=torch.uint8, device="cuda")
+            for e in range(cfg.E):
+                p, sc = self.mats[e][i]
+                k3.mxfp4_repack(torch.from_numpy(p).cuda(), torch.from_numpy(sc).cuda(), blocks=t[e])
+            dev[name] = t
+        return dev
+
+
+@pytest.mark.parametrize("e_gu,e_dn", [(114, 140), (80, 140)])
+def test_large_tile_h_slices_far_apart(k3, e_gu, e_dn):
+    # h of the first 256-wide slice about 2^-14 of the others' (rescaled sums
+    # with factors near 2^14; through w2's large columns that slice makes
+    # about 45% of the output) or about 2^-80 (a spread beyond the rescaling
+    # span: the per-operand scaling path)
+    cfg = moe_inputs.TINY.with_(E=4, k=2, D=512, I=512, T=300, config_id=48)
+    print(f"[ffn] large-tile h slice scales e_gu={e_gu} e_dn={e_dn}", flush=True)
+    batch = moe_inputs.make_batch(cfg)
+    ids, w = route_ref(batch.z, batch.b, cfg.k)
+    ex = ScaledExperts(cfg, e_gu, e_dn)
+    dev = ex.upload(k3, cfg)
+    out = k3.moe_mxfp4_ffn(bf16_dev(batch.x), torch.from_numpy(ids.astype(np.int32)).cuda(),
+                           torch.from_numpy(w.astype(np.float32)).cuda(), dev["w1"], dev["w3"], dev["w2"])
+    ref = ffn_ref(batch.x, ids, w, ex)
+    assert_ffn_close(out.cpu().numpy(), ref, f"e_gu={e_gu} e_dn={e_dn}")
+
+
 def test_identity_weights_closed_form(k3):
     """W1 = W3 = [I; 0], W2 = 2^e [I | 0]: out[t] = sum_j w_j 2^(e_j) SiLU(x) x."""
     E, D, I, T, k = 4, 128, 256, 48, 2
