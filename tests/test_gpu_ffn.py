@@ -202,6 +202,88 @@ def test_side_stream_matches_serial_launches(k3):
         assert torch.equal(again.view(torch.int32), conc.view(torch.int32))
 
 
+def _mixed_inputs(k3):
+    cfg = moe_inputs.TINY.with_(E=40, k=4, D=512, I=512, T=90, config_id=43)  # 24 large-tile + 12 streaming
+    batch = moe_inputs.make_batch(cfg)
+    ids, w = route_ref(batch.z, batch.b, cfg.k)
+    dev = device_experts(k3, cfg)
+    x = bf16_dev(batch.x)
+    ids_d = torch.from_numpy(ids.astype(np.int32)).cuda()
+    w_d = torch.from_numpy(w.astype(np.float32)).cuda()
+    return cfg, dev, x, ids_d, w_d
+
+
+def test_side_streams_of_concurrent_threads(k3):
+    # two host threads, each on its own stream with its own buffers (and its
+    # own side stream): the same bits as one call on the main thread
+    import threading
+    cfg, dev, x, ids_d, w_d = _mixed_inputs(k3)
+    ref = k3.moe_mxfp4_ffn(x, ids_d, w_d, dev.w1, dev.w3, dev.w2)
+    torch.cuda.synchronize()
+    results, errors = {}, []
+
+    def worker(i):
+        try:
+            st = torch.cuda.Stream()
+            with torch.cuda.stream(st):
+                outs = [k3.moe_mxfp4_ffn(x, ids_d, w_d, dev.w1, dev.w3, dev.w2) for _ in range(4)]
+            st.synchronize()
+            results[i] = [o.cpu() for o in outs]
+        except Exception as exc:  # surfaced below
+            errors.append(exc)
+
+    threads = [threading.Thread(target=worker, args=(i,)) for i in range(2)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert not errors, errors
+    want = ref.cpu().view(torch.int32)
+    for i in range(2):
+        for o in results[i]:
+            assert torch.equal(o.view(torch.int32), want)
+
+
+def test_first_call_of_a_thread_inside_capture(k3):
+    # a thread whose first call is captured has no side stream yet (serial
+    # launches); after an eager call it has one, and a new capture holds the
+    # two branches; every replay gives the eager bits
+    import threading
+    cfg, dev, x, ids_d, w_d = _mixed_inputs(k3)
+    ref = k3.moe_mxfp4_ffn(x, ids_d, w_d, dev.w1, dev.w3, dev.w2).cpu()
+    torch.cuda.synchronize()
+    errors = []
+
+    def worker():
+        try:
+            st = torch.cuda.Stream()
+            with torch.cuda.stream(st):
+                out = torch.empty((cfg.T, cfg.D), dtype=torch.float32, device="cuda")
+                ws = torch.empty(k3.moe_mxfp4_ffn_workspace_size(cfg.T, cfg.D, cfg.I, cfg.E, cfg.k),
+                                 dtype=torch.uint8, device="cuda")
+            st.synchronize()
+            for round_ in range(2):
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=st):
+                    k3.moe_mxfp4_ffn(x, ids_d, w_d, dev.w1, dev.w3, dev.w2, out=out, workspace=ws)
+                for _ in range(2):
+                    out.fill_(float("nan"))
+                    g.replay()
+                    torch.cuda.synchronize()
+                    assert torch.equal(out.cpu().view(torch.int32), ref.view(torch.int32)), f"capture {round_}"
+                with torch.cuda.stream(st):  # eager: creates this thread's side stream
+                    k3.moe_mxfp4_ffn(x, ids_d, w_d, dev.w1, dev.w3, dev.w2, out=out, workspace=ws)
+                st.synchronize()
+                assert torch.equal(out.cpu().view(torch.int32), ref.view(torch.int32)), f"eager {round_}"
+        except Exception as exc:
+            errors.append(exc)
+
+    t = threading.Thread(target=worker)
+    t.start()
+    t.join()
+    assert not errors, errors
+
+
 @pytest.mark.parametrize(
     "E,k,D,I,T",
     # small-tile, streaming (grouped in the gate/up launch, x re-laid out first / read in place), large-tile, and
