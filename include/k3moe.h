@@ -9,9 +9,9 @@
  *
  * General conventions (all entry points):
  *   - Array pointers are DEVICE pointers unless stated otherwise. The caller
- *     allocates and owns every buffer; the library allocates no memory and
- *     never synchronizes the host. Its only state is moe_mxfp4_ffn's side
- *     stream (below).
+ *     allocates and owns every buffer; no entry point allocates device memory
+ *     or synchronizes the host. The library's state: moe_mxfp4_ffn's
+ *     per-thread side stream (below).
  *   - `stream` is a hipStream_t (NULL = the default stream) of the current
  *     device, which also holds every buffer passed. Every call only enqueues
  *     work on it and returns; results are ready when the stream is.
@@ -49,6 +49,8 @@ typedef enum {
 /* Largest expert count moe_mxfp4_ffn accepts (its grouping keeps one 64-bit
    token bitmap per expert in LDS). moe_route_topk has no expert limit. */
 #define K3MOE_MAX_EXPERTS_FFN 8192
+/* Largest latent dim D and expert intermediate I moe_mxfp4_ffn accepts. */
+#define K3MOE_MAX_DIM_FFN 65536
 
 /* Activation hook ids ("situ" is named but not defined by the sources; the
    only hook provided is SiLU(gate) * up). */
@@ -158,18 +160,27 @@ size_t moe_mxfp4_ffn_workspace_size(int64_t T, int32_t D, int32_t I, int32_t E, 
  * inputs in all); fp32 output.
  * The k expert outputs of a token are summed in slot order (deterministic, no
  * atomics).
+ * Large batches run as consecutive chunks of tokens that reuse one workspace
+ * (at most (2^31 - 1) / (2 * k * max(D, I)) tokens each, rounded down to a
+ * multiple of 64: the GEMM kernels address activations with 32-bit offsets);
+ * moe_mxfp4_ffn_workspace_size() is that of one chunk.
  * Side stream: when one call has experts for both GEMM kinds (many rows: the
  * large-tile kernels; at most 4 rows: the weight-streaming kernels), the
  * streaming launches run on a side stream forked from `stream` with an event
  * and joined back before the combine (a graph captured from `stream` gets two
  * parallel branches). The side stream (default priority) and its two events
  * belong to the calling host thread and the current device; they are created
- * by the first such call made outside a graph capture (until then the
- * launches stay on `stream`) and kept until the process ends.
- * Entry (t, j) is skipped (contributes nothing) when topk_ids[t,j] is outside
- * [0, E) or repeats an id earlier in the same row.
- * Sizes: T >= 0 (T == 0 is a no-op), D > 0 and I > 0 multiples of 128,
- * 1 <= k <= K3MOE_MAX_TOPK, 1 <= E <= K3MOE_MAX_EXPERTS_FFN.
+ * by the thread's first such call made outside a graph capture (until then
+ * the launches stay on `stream`) and destroyed when the thread exits (those of
+ * the process's main thread are kept until the process ends). A side stream
+ * that is part of an open capture (an earlier call of the thread during that
+ * capture forked it) is used only by calls captured into that same capture;
+ * the thread's other calls meanwhile launch everything on `stream`.
+ * Entry (t, j) is skipped (contributes nothing, whatever its weight) when
+ * topk_ids[t,j] is outside [0, E) or repeats an id earlier in the same row.
+ * Sizes: T >= 0 (T == 0 is a no-op), D > 0 and I > 0 multiples of 32 and at
+ * most K3MOE_MAX_DIM_FFN, 1 <= k <= min(E, K3MOE_MAX_TOPK),
+ * 1 <= E <= K3MOE_MAX_EXPERTS_FFN, T * k < 2^31.
  * E8M0 exponent bytes of the weights must be <= 254 (255 is not supported).
  */
 int moe_mxfp4_ffn(const void* x_bf16, const int32_t* topk_ids, const float* topk_w, const uint8_t* w1,
@@ -183,13 +194,20 @@ int moe_mxfp4_ffn(const void* x_bf16, const int32_t* topk_ids, const float* topk
  *
  *   stage_events  host array of K3MOE_FFN_STAGE_EVENTS hipEvent_t (each may be
  *                 NULL to skip it): [0] before grouping, [1] before the gate/up
- *                 product, [2] before the down product, [3] before the combine,
- *                 [4] after the combine. NULL array = plain moe_mxfp4_ffn.
+ *                 product's large-tile (or small-tile) launch, [2] before its
+ *                 weight-streaming launch, [3] before the down product's
+ *                 large-tile (or small-tile) launch, [4] before its
+ *                 weight-streaming launch, [5] before the combine, [6] after
+ *                 the combine. A stage the batch does not need leaves two
+ *                 consecutive events with nothing between them. NULL array =
+ *                 plain moe_mxfp4_ffn. With several token chunks every chunk
+ *                 records the events, so they end up bounding the last chunk.
  *
- * Same arguments, checks and results as moe_mxfp4_ffn; an event the runtime
- * refuses to record gives K3MOE_ERR_DEVICE.
+ * Same arguments, checks and results as moe_mxfp4_ffn, except that every
+ * launch stays on `stream` (no side stream, so the events bound each
+ * launch); an event the runtime refuses to record gives K3MOE_ERR_DEVICE.
  */
-#define K3MOE_FFN_STAGE_EVENTS 5
+#define K3MOE_FFN_STAGE_EVENTS 7
 int moe_mxfp4_ffn_profiled(const void* x_bf16, const int32_t* topk_ids, const float* topk_w, const uint8_t* w1,
                            const uint8_t* w3, const uint8_t* w2, int64_t T, int32_t D, int32_t I, int32_t E,
                            int32_t k, int32_t act, float* out, void* workspace, size_t workspace_bytes,

@@ -63,8 +63,9 @@ lib.moe_group_workspace_size.restype = _sz
 lib.moe_group_workspace_size.argtypes = [_i64, _i32, _i32]
 lib.moe_group_by_expert.restype = ctypes.c_int
 lib.moe_group_by_expert.argtypes = [_vp, _i64, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _sz, _vp]
-FFN_STAGE_EVENTS = 5
-FFN_STAGES = ("group", "gate_up", "down", "combine")
+FFN_STAGE_EVENTS = 7
+# launches between consecutive events of moe_mxfp4_ffn_profiled
+FFN_STAGES = ("group", "gate_up", "gate_up_stream", "down", "down_stream", "combine")
 
 
 class K3MoeError(RuntimeError):
@@ -171,14 +172,7 @@ def moe_mxfp4_ffn_workspace_size(T: int, D: int, I: int, E: int, k: int) -> int:
     return int(lib.moe_mxfp4_ffn_workspace_size(T, D, I, E, k))
 
 
-def moe_mxfp4_ffn(x: torch.Tensor, ids: torch.Tensor, weights: torch.Tensor, w1: torch.Tensor, w3: torch.Tensor,
-                  w2: torch.Tensor, act: int = ACT_SILU_MUL, out: torch.Tensor | None = None,
-                  workspace: torch.Tensor | None = None, stage_events=None) -> torch.Tensor:
-    """Routed-expert FFN. x bf16 [T, D]; ids int32 [T, k]; weights f32 [T, k];
-    w1/w3 u8 [E, I, D/32, 17]; w2 u8 [E, D, I/32, 17]. Returns out f32 [T, D].
-
-    stage_events: optional list of 5 torch.cuda.Event recorded at the stage
-    boundaries (moe_mxfp4_ffn_profiled)."""
+def _ffn_operands(x, ids, weights, w1, w3, w2, out):
     _dev(x, "x", torch.bfloat16)
     _dev(ids, "ids", torch.int32)
     _dev(weights, "weights", torch.float32)
@@ -194,6 +188,18 @@ def moe_mxfp4_ffn(x: torch.Tensor, ids: torch.Tensor, weights: torch.Tensor, w1:
     if out is None:
         out = torch.empty((T, D), dtype=torch.float32, device=x.device)
     _dev(out, "out", torch.float32)
+    return T, D, I, E, k, out
+
+
+def moe_mxfp4_ffn(x: torch.Tensor, ids: torch.Tensor, weights: torch.Tensor, w1: torch.Tensor, w3: torch.Tensor,
+                  w2: torch.Tensor, act: int = ACT_SILU_MUL, out: torch.Tensor | None = None,
+                  workspace: torch.Tensor | None = None, stage_events=None) -> torch.Tensor:
+    """Routed-expert FFN. x bf16 [T, D]; ids int32 [T, k]; weights f32 [T, k];
+    w1/w3 u8 [E, I, D/32, 17]; w2 u8 [E, D, I/32, 17]. Returns out f32 [T, D].
+
+    stage_events: optional list of FFN_STAGE_EVENTS torch.cuda.Event recorded
+    at the launch boundaries (moe_mxfp4_ffn_profiled)."""
+    T, D, I, E, k, out = _ffn_operands(x, ids, weights, w1, w3, w2, out)
     need = moe_mxfp4_ffn_workspace_size(T, D, I, E, k)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)

@@ -3,9 +3,24 @@
 #include "k3moe.h"
 #include "k3moe_internal.h"
 
+#include <sys/syscall.h>
+#include <unistd.h>
+
 namespace k3moe {
 
 static size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+int64_t ffn_chunk_tokens(int64_t T, int32_t D, int32_t I, int32_t k) {
+  // The GEMM kernels address x, h and the grouped rows through buffer
+  // resources with 32-bit byte offsets: a chunk keeps k * max(D, I) * 2 bytes
+  // per token below 2^31.  Chunks start on a multiple of 64 tokens (16-byte
+  // aligned ids and weights for every k).
+  const int64_t per_token = 2 * (int64_t)k * (int64_t)(D > I ? D : I);
+  int64_t tc = (((int64_t)1 << 31) - 1) / per_token;
+  tc = tc >= 64 ? tc / 64 * 64 : tc;
+  if (tc < 1) tc = 1;
+  return T < tc ? T : tc;
+}
 
 FfnWorkspace ffn_workspace_layout(int64_t T, int32_t D, int32_t I, int32_t E, int32_t k) {
   FfnWorkspace w{};
@@ -63,35 +78,284 @@ using namespace k3moe;
 
 namespace {
 
+constexpr int kMaxDevices = 64;
+
 bool misaligned(const void* p) { return p != nullptr && (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
 
 int device_status(hipError_t e) { return e == hipSuccess ? K3MOE_OK : K3MOE_ERR_DEVICE; }
 
+// ---------------------------------------------------------------------------
 // Side stream (default priority) and fork / join events of the calling host
-// thread on the current device, created on the first call made outside a
-// graph capture and kept for the life of the thread; nullptr before that, or
-// if the runtime refuses one of them.
+// thread on each device, created by the thread's first call outside a graph
+// capture that has experts of both GEMM kinds.  A thread other than the
+// process's main thread destroys them when it exits; the main thread's are
+// left to the end of the process (its thread-local objects are destroyed
+// during exit, possibly after the HIP runtime).
 struct SideStream {
   hipStream_t s = nullptr;
   hipEvent_t fork = nullptr, join = nullptr;
 };
+struct ThreadSideStreams {
+  SideStream dev[kMaxDevices];
+  bool tried[kMaxDevices] = {};
+  ~ThreadSideStreams() {
+    if ((pid_t)syscall(SYS_gettid) == getpid()) return;
+    for (int d = 0; d < kMaxDevices; ++d) {
+      if (dev[d].s) (void)hipStreamDestroy(dev[d].s);
+      if (dev[d].fork) (void)hipEventDestroy(dev[d].fork);
+      if (dev[d].join) (void)hipEventDestroy(dev[d].join);
+    }
+  }
+};
+thread_local ThreadSideStreams t_side;
+
+// The calling thread's side stream for a call on `caller`, or nullptr when the
+// launches must stay on `caller`: no side stream yet and `caller` is being
+// captured (creating one then is not allowed), the runtime refused one, or the
+// side stream already belongs to an open capture other than `caller`'s (it
+// joined that capture through an earlier call of this thread).
 SideStream* side_stream(hipStream_t caller) {
-  constexpr int kMaxDevices = 64;
-  thread_local SideStream side[kMaxDevices];
-  thread_local bool tried[kMaxDevices] = {};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
-  SideStream& ss = side[dev];
-  if (!tried[dev]) {
-    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
-    if (hipStreamIsCapturing(caller, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone) return nullptr;
-    tried[dev] = true;
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  unsigned long long cid = 0;
+  if (hipStreamGetCaptureInfo(caller, &cs, &cid) != hipSuccess) return nullptr;
+  SideStream& ss = t_side.dev[dev];
+  if (!t_side.tried[dev]) {
+    if (cs != hipStreamCaptureStatusNone) return nullptr;
+    t_side.tried[dev] = true;
     if (hipStreamCreateWithFlags(&ss.s, hipStreamNonBlocking) != hipSuccess ||
         hipEventCreateWithFlags(&ss.fork, hipEventDisableTiming) != hipSuccess ||
-        hipEventCreateWithFlags(&ss.join, hipEventDisableTiming) != hipSuccess)
-      ss.s = nullptr;
+        hipEventCreateWithFlags(&ss.join, hipEventDisableTiming) != hipSuccess) {
+      if (ss.s) (void)hipStreamDestroy(ss.s);
+      if (ss.fork) (void)hipEventDestroy(ss.fork);
+      if (ss.join) (void)hipEventDestroy(ss.join);
+      ss = SideStream{};
+    }
   }
-  return ss.s ? &ss : nullptr;
+  if (!ss.s) return nullptr;
+  hipStreamCaptureStatus side_cs = hipStreamCaptureStatusNone;
+  unsigned long long side_id = 0;
+  if (hipStreamGetCaptureInfo(ss.s, &side_cs, &side_id) != hipSuccess) return nullptr;
+  if (side_cs != hipStreamCaptureStatusNone && (cs != hipStreamCaptureStatusActive || side_id != cid)) return nullptr;
+  return &ss;
+}
+
+// ---------------------------------------------------------------------------
+int ffn_shape_status(int64_t T, int32_t D, int32_t I, int32_t E, int32_t k) {
+  if (T < 0 || D <= 0 || I <= 0 || (D % 32) != 0 || (I % 32) != 0) return K3MOE_ERR_SHAPE;
+  if (D > K3MOE_MAX_DIM_FFN || I > K3MOE_MAX_DIM_FFN) return K3MOE_ERR_SHAPE;
+  if (E < 1 || E > K3MOE_MAX_EXPERTS_FFN || k < 1 || k > E || k > K3MOE_MAX_TOPK) return K3MOE_ERR_SHAPE;
+  // grouped rows are int32 inside the kernels
+  if (T * (int64_t)k > 0x7FFFFFFF || T > 0x7FFFFFFF) return K3MOE_ERR_SHAPE;
+  return K3MOE_OK;
+}
+
+// Events recorded at the launch boundaries (moe_mxfp4_ffn_profiled).
+enum { kEvGroup = 0, kEvGateUp, kEvGateUpStream, kEvDown, kEvDownStream, kEvCombine, kEvEnd };
+static_assert(kEvEnd + 1 == K3MOE_FFN_STAGE_EVENTS, "event slots");
+
+// One chunk of at most ffn_chunk_tokens() tokens: grouping, gate/up, down,
+// combine, enqueued on `s` (the streaming launches on a side stream when
+// `side` is set).
+int run_ffn_chunk(const void* x_bf16, const int32_t* topk_ids, const float* topk_w, const uint8_t* w1,
+                  const uint8_t* w3, const uint8_t* w2, int64_t T, int32_t D, int32_t I, int32_t E, int32_t k,
+                  float* out, uint8_t* ws, hipStream_t s, void* const* stage_events, bool allow_side) {
+  const FfnWorkspace L = ffn_workspace_layout(T, D, I, E, k);
+  const int64_t entries = T * (int64_t)k;
+  const int64_t active = entries < E ? entries : E;
+  // GEMM kernels.  With D and I multiples of 512 every expert is served by
+  // the kernel that suits its row count: the large-tile GEMMs for experts
+  // with more than kStreamMaxRows rows (MFMA-bound), the weight-streaming
+  // GEMMs for the others (HBM-bound).  Batches of up to kStreamOnlyTokens
+  // tokens send every expert to the streaming kernels (an expert with more
+  // than kStreamMaxRows rows takes several streaming tiles, whose repeated
+  // weight reads mostly hit the caches), so decode steps skip the large-tile
+  // launches.  Other shapes use the general small-tile GEMMs for every expert.
+  constexpr int kStreamMaxRows = 4;
+  constexpr int kStreamOnlyTokens = 8;
+  const bool tiled = big_gemm_supported(D, I) && stream_gemm_supported(D, I);
+  const bool stream_only = tiled && T <= kStreamOnlyTokens;
+  const bool big_lists = !tiled || !stream_only;  // lists 0/1 may hold tiles
+  const bool stream_lists = tiled;                // lists 2/3 may hold tiles
+  const int rpt_small = choose_rows_per_tile(T, k, E);
+  // 128-row down tiles once the batch is large enough that the large-tile
+  // down product still has about four workgroups per CU with them
+  constexpr int64_t kWideDownEntries = 16384;
+  const bool wide_down = entries >= kWideDownEntries;
+
+  GroupArgs g{};
+  g.ids = topk_ids;
+  g.x = static_cast<const uint16_t*>(x_bf16);
+  g.T = T;
+  g.D = D;
+  g.E = E;
+  g.k = k;
+  g.rows_per_tile[0] = tiled ? big_rows_per_tile(true, false) : rpt_small;
+  g.rows_per_tile[1] = tiled ? big_rows_per_tile(false, wide_down) : rpt_small;
+  g.rows_per_tile[2] = stream_rows_per_tile(true);
+  g.rows_per_tile[3] = stream_rows_per_tile(false);
+  g.split_rows = tiled ? (stream_only ? kStreamOnlyTokens : kStreamMaxRows) : 0;
+  g.flag_big_rows = tiled ? 1 : 0;  // the large-tile down kernel's rows hold scaled fp16 y
+  g.counts = reinterpret_cast<int32_t*>(ws + L.counts);
+  g.offsets = reinterpret_cast<int32_t*>(ws + L.offsets);
+  g.tile_count = reinterpret_cast<int32_t*>(ws + L.tile_count);
+  for (int l = 0; l < kTileLists; ++l) g.tiles[l] = reinterpret_cast<Tile*>(ws + L.tiles[l]);
+  g.row_tok = reinterpret_cast<int32_t*>(ws + L.row_tok);
+  g.slot_row = reinterpret_cast<int32_t*>(ws + L.slot_row);
+  g.chunk_base = reinterpret_cast<int32_t*>(ws + L.chunk_base);
+  g.chunk_mask = reinterpret_cast<unsigned long long*>(ws + L.chunk_mask);
+  g.x_perm = reinterpret_cast<uint16_t*>(ws + L.x_perm);
+  auto mark = [&](int i) -> bool {
+    if (!stage_events || !stage_events[i]) return true;
+    return hipEventRecord(static_cast<hipEvent_t>(stage_events[i]), s) == hipSuccess;
+  };
+  // A streaming-only batch of at most kSelfGroupEntries entries is grouped by
+  // the gate/up launch itself (no grouping launch).  Up to kNaturalXTokens
+  // tokens that launch also reads x in place; larger decode batches have x
+  // re-laid out first by a small launch, as the operand reads of pre-permuted
+  // x keep the gate/up stream faster.
+  constexpr int kNaturalXTokens = 4;
+  const bool self_group = stream_only && entries <= kSelfGroupEntries && E <= 0xFFFF;
+  const bool natural_x = self_group && T <= kNaturalXTokens;
+  if (!mark(kEvGroup)) return K3MOE_ERR_DEVICE;
+  hipError_t err = self_group ? (natural_x ? hipSuccess : launch_permute_x(g.x, g.x_perm, T, D, s)) : launch_group(g, s);
+  if (err != hipSuccess) return K3MOE_ERR_DEVICE;
+
+  // Upper bounds of the list lengths (sum over experts of ceil(n_e / rpt)):
+  // an expert in lists 0/1 has more than split_rows rows.
+  const int64_t big_experts = tiled ? (entries / (kStreamMaxRows + 1) < active ? entries / (kStreamMaxRows + 1) : active)
+                                    : active;
+  GemmArgs gu{};
+  gu.act = g.x_perm;
+  gu.act_rows = T;
+  gu.row_tok = g.row_tok;
+  gu.wa = w1;
+  gu.wb = w3;
+  gu.K = D;
+  gu.N = I;
+  gu.out = ws + L.h;
+  gu.out_lo = ws + L.h_lo;
+  gu.h_scale = reinterpret_cast<int8_t*>(ws + L.h_scale);
+  GemmArgs dn{};
+  dn.act = reinterpret_cast<const uint16_t*>(ws + L.h);
+  dn.act_lo = reinterpret_cast<const uint16_t*>(ws + L.h_lo);
+  dn.act_rows = entries;
+  dn.row_tok = nullptr;
+  dn.wa = w2;
+  dn.wb = nullptr;
+  dn.K = I;
+  dn.N = D;
+  dn.out = ws + L.y;
+  dn.h_scale = reinterpret_cast<int8_t*>(ws + L.h_scale);
+  dn.y_scale = reinterpret_cast<int8_t*>(ws + L.y_scale);
+
+  // Experts of both kinds in one call (and no stage events to record): the
+  // streaming launches run on a side stream beside the large-tile launches;
+  // they read the same inputs and write other rows of h and y.  The combine
+  // waits for both branches.
+  SideStream* side = (allow_side && big_lists && stream_lists && !stage_events) ? side_stream(s) : nullptr;
+  hipStream_t ss = s;
+  if (side) {
+    if (hipEventRecord(side->fork, s) != hipSuccess || hipStreamWaitEvent(side->s, side->fork, 0) != hipSuccess)
+      return K3MOE_ERR_DEVICE;
+    ss = side->s;
+  }
+
+  // gate/up
+  if (!mark(kEvGateUp)) return K3MOE_ERR_DEVICE;
+  if (big_lists) {
+    gu.tiles = g.tiles[0];
+    gu.tile_count = g.tile_count;
+    gu.max_tiles = entries / g.rows_per_tile[0] + big_experts;
+    err = tiled ? launch_big_gate_up(gu, s) : launch_gate_up(gu, rpt_small, s);
+    if (err != hipSuccess) return K3MOE_ERR_DEVICE;
+  }
+  if (!mark(kEvGateUpStream)) return K3MOE_ERR_DEVICE;
+  if (stream_lists) {
+    gu.tiles = g.tiles[2];
+    gu.tile_count = g.tile_count + 2;
+    const int64_t r = g.rows_per_tile[2];
+    gu.max_tiles = (entries + (r - 1) * active) / r;  // bounds the sum of ceil(n_e / r) over experts
+    if (self_group) {
+      SelfGroupArgs sg{};
+      sg.ids = topk_ids;
+      sg.T = (int)T;
+      sg.E = E;
+      sg.k = k;
+      sg.tile_count = g.tile_count;
+      sg.down_tiles = g.tiles[3];
+      sg.slot_row = g.slot_row;
+      gu.act = natural_x ? static_cast<const uint16_t*>(x_bf16) : g.x_perm;
+      gu.row_tok = nullptr;
+      err = launch_stream_gate_up_grouped(gu, sg, natural_x, ss);
+    } else {
+      err = launch_stream_gate_up(gu, ss);
+    }
+    if (err != hipSuccess) return K3MOE_ERR_DEVICE;
+  }
+
+  // down
+  if (!mark(kEvDown)) return K3MOE_ERR_DEVICE;
+  if (big_lists) {
+    dn.tiles = g.tiles[1];
+    dn.tile_count = g.tile_count + 1;
+    dn.max_tiles = entries / g.rows_per_tile[1] + big_experts;
+    err = tiled ? launch_big_down(dn, wide_down, s) : launch_down(dn, rpt_small, s);
+    if (err != hipSuccess) return K3MOE_ERR_DEVICE;
+  }
+  if (!mark(kEvDownStream)) return K3MOE_ERR_DEVICE;
+  if (stream_lists) {
+    dn.tiles = g.tiles[3];
+    dn.tile_count = g.tile_count + 3;
+    const int64_t r = g.rows_per_tile[3];
+    dn.max_tiles = (entries + (r - 1) * active) / r;  // bounds the sum of ceil(n_e / r) over experts
+    err = launch_stream_down(dn, ss);
+    if (err != hipSuccess) return K3MOE_ERR_DEVICE;
+  }
+  if (side) {
+    if (hipEventRecord(side->join, side->s) != hipSuccess || hipStreamWaitEvent(s, side->join, 0) != hipSuccess)
+      return K3MOE_ERR_DEVICE;
+  }
+  if (!mark(kEvCombine)) return K3MOE_ERR_DEVICE;
+
+  // Rows of the large-tile down kernel hold scaled fp16 y; a streaming-only
+  // batch has none, so its combine reads fp32 rows only.
+  const bool mixed_rows = tiled && !stream_only;
+  err = launch_combine(reinterpret_cast<const float*>(ws + L.y), reinterpret_cast<const int8_t*>(ws + L.y_scale),
+                       mixed_rows, g.slot_row, topk_w, T, D, k, out, s);
+  if (err != hipSuccess || !mark(kEvEnd)) return K3MOE_ERR_DEVICE;
+  return K3MOE_OK;
+}
+
+// The FFN over all T tokens, one chunk of ffn_chunk_tokens() after another
+// (the chunks reuse one workspace; stream order serialises them).
+int run_ffn(const void* x_bf16, const int32_t* topk_ids, const float* topk_w, const uint8_t* w1, const uint8_t* w3,
+            const uint8_t* w2, int64_t T, int32_t D, int32_t I, int32_t E, int32_t k, float* out, uint8_t* ws,
+            hipStream_t s, void* const* stage_events, bool allow_side) {
+  const int64_t tc = ffn_chunk_tokens(T, D, I, k);
+  for (int64_t t0 = 0; t0 < T; t0 += tc) {
+    const int64_t n = T - t0 < tc ? T - t0 : tc;
+    const int st = run_ffn_chunk(static_cast<const uint16_t*>(x_bf16) + t0 * D, topk_ids + t0 * k, topk_w + t0 * k,
+                                 w1, w3, w2, n, D, I, E, k, out + t0 * D, ws, s, stage_events, allow_side);
+    if (st != K3MOE_OK) return st;
+  }
+  return K3MOE_OK;
+}
+
+// Argument checks shared by the FFN entry points (workspace excluded).
+int ffn_arg_status(const void* x_bf16, const int32_t* topk_ids, const float* topk_w, const uint8_t* w1,
+                   const uint8_t* w3, const uint8_t* w2, int64_t T, int32_t D, int32_t I, int32_t E, int32_t k,
+                   int32_t act, const float* out) {
+  const int st = ffn_shape_status(T, D, I, E, k);
+  if (st != K3MOE_OK) return st;
+  if (act != K3MOE_ACT_SILU_MUL) return K3MOE_ERR_UNSUPPORTED;
+  if (T == 0) return K3MOE_OK;
+  if (!x_bf16 || !topk_ids || !topk_w || !w1 || !w3 || !w2 || !out) return K3MOE_ERR_NULL;
+  if (misaligned(x_bf16) || misaligned(topk_ids) || misaligned(topk_w) || misaligned(w1) || misaligned(w3) ||
+      misaligned(w2) || misaligned(out))
+    return K3MOE_ERR_ALIGN;
+  return K3MOE_OK;
 }
 
 }  // namespace
@@ -145,17 +409,9 @@ int mxfp4_dequant(const uint8_t* blocks, int64_t R, int64_t K, int32_t out_dtype
                                       static_cast<hipStream_t>(stream)));
 }
 
-static int ffn_shape_status(int64_t T, int32_t D, int32_t I, int32_t E, int32_t k) {
-  if (T < 0 || D <= 0 || I <= 0 || (D % 128) != 0 || (I % 128) != 0) return K3MOE_ERR_SHAPE;
-  if (E < 1 || E > K3MOE_MAX_EXPERTS_FFN || k < 1 || k > K3MOE_MAX_TOPK) return K3MOE_ERR_SHAPE;
-  // grouped rows and element offsets are int32 / int64 inside the kernels
-  if (T * (int64_t)k > 0x7FFFFFFF || T > 0x7FFFFFFF) return K3MOE_ERR_SHAPE;
-  return K3MOE_OK;
-}
-
 size_t moe_mxfp4_ffn_workspace_size(int64_t T, int32_t D, int32_t I, int32_t E, int32_t k) {
   if (ffn_shape_status(T, D, I, E, k) != K3MOE_OK || T == 0) return 0;
-  return ffn_workspace_layout(T, D, I, E, k).total;
+  return ffn_workspace_layout(ffn_chunk_tokens(T, D, I, k), D, I, E, k).total;
 }
 
 int moe_mxfp4_ffn(const void* x_bf16, const int32_t* topk_ids, const float* topk_w, const uint8_t* w1,
@@ -169,184 +425,13 @@ int moe_mxfp4_ffn_profiled(const void* x_bf16, const int32_t* topk_ids, const fl
                            const uint8_t* w3, const uint8_t* w2, int64_t T, int32_t D, int32_t I, int32_t E,
                            int32_t k, int32_t act, float* out, void* workspace, size_t workspace_bytes,
                            void* stream, void* const* stage_events) {
-  const int st = ffn_shape_status(T, D, I, E, k);
-  if (st != K3MOE_OK) return st;
-  if (act != K3MOE_ACT_SILU_MUL) return K3MOE_ERR_UNSUPPORTED;
-  if (T == 0) return K3MOE_OK;
-  if (!x_bf16 || !topk_ids || !topk_w || !w1 || !w3 || !w2 || !out || !workspace) return K3MOE_ERR_NULL;
-  if (misaligned(x_bf16) || misaligned(topk_ids) || misaligned(topk_w) || misaligned(w1) || misaligned(w3) ||
-      misaligned(w2) || misaligned(out) || misaligned(workspace))
-    return K3MOE_ERR_ALIGN;
-  const FfnWorkspace L = ffn_workspace_layout(T, D, I, E, k);
-  if (workspace_bytes < L.total) return K3MOE_ERR_WORKSPACE;
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  uint8_t* ws = static_cast<uint8_t*>(workspace);
-  const int64_t entries = T * (int64_t)k;
-  const int64_t active = entries < E ? entries : E;
-  // GEMM kernels.  With D and I multiples of 512 (and activations below 2 GiB,
-  // as both address them through 32-bit buffer offsets) every expert is served
-  // by the kernel that suits its row count: the large-tile GEMMs for experts
-  // with more than kStreamMaxRows rows (MFMA-bound), the weight-streaming GEMMs
-  // for the others (HBM-bound).  A batch of at most kStreamMaxRows tokens
-  // cannot give an expert more rows (an id repeated within a token is
-  // skipped), so it launches only the streaming kernels.  Other shapes use
-  // the general small-tile GEMMs for every expert.  Batches of up to
-  // kStreamOnlyTokens tokens send every expert to the streaming kernels (an
-  // expert with more than kStreamMaxRows rows takes several streaming tiles,
-  // whose repeated weight reads mostly hit the caches), so decode steps skip
-  // the large-tile launches.
-  constexpr int kStreamMaxRows = 4;
-  constexpr int kStreamOnlyTokens = 8;
-  const bool offsets_fit = entries * (int64_t)(I > D ? I : D) * 2 < ((int64_t)1 << 31);
-  const bool tiled = big_gemm_supported(D, I) && stream_gemm_supported(D, I) && offsets_fit;
-  const bool stream_only = tiled && T <= kStreamOnlyTokens;
-  const bool big_lists = !tiled || !stream_only;  // lists 0/1 may hold tiles
-  const bool stream_lists = tiled;                // lists 2/3 may hold tiles
-  const int rpt_small = choose_rows_per_tile(T, k, E);
-  // 128-row down tiles once the batch is large enough that the large-tile
-  // down product still has about four workgroups per CU with them
-  constexpr int64_t kWideDownEntries = 16384;
-  const bool wide_down = entries >= kWideDownEntries;
-
-  GroupArgs g{};
-  g.ids = topk_ids;
-  g.x = static_cast<const uint16_t*>(x_bf16);
-  g.T = T;
-  g.D = D;
-  g.E = E;
-  g.k = k;
-  g.rows_per_tile[0] = tiled ? big_rows_per_tile(true, false) : rpt_small;
-  g.rows_per_tile[1] = tiled ? big_rows_per_tile(false, wide_down) : rpt_small;
-  g.rows_per_tile[2] = stream_rows_per_tile(true);
-  g.rows_per_tile[3] = stream_rows_per_tile(false);
-  g.split_rows = tiled ? (stream_only ? kStreamOnlyTokens : kStreamMaxRows) : 0;
-  g.flag_big_rows = tiled ? 1 : 0;  // the large-tile down kernel's rows hold scaled fp16 y
-  g.counts = reinterpret_cast<int32_t*>(ws + L.counts);
-  g.offsets = reinterpret_cast<int32_t*>(ws + L.offsets);
-  g.tile_count = reinterpret_cast<int32_t*>(ws + L.tile_count);
-  for (int l = 0; l < kTileLists; ++l) g.tiles[l] = reinterpret_cast<Tile*>(ws + L.tiles[l]);
-  g.row_tok = reinterpret_cast<int32_t*>(ws + L.row_tok);
-  g.slot_row = reinterpret_cast<int32_t*>(ws + L.slot_row);
-  g.chunk_base = reinterpret_cast<int32_t*>(ws + L.chunk_base);
-  g.chunk_mask = reinterpret_cast<unsigned long long*>(ws + L.chunk_mask);
-  g.x_perm = reinterpret_cast<uint16_t*>(ws + L.x_perm);
-  auto mark = [&](int i) -> bool {
-    if (!stage_events || !stage_events[i]) return true;
-    return hipEventRecord(static_cast<hipEvent_t>(stage_events[i]), s) == hipSuccess;
-  };
-  // A streaming-only batch of at most kSelfGroupEntries entries is grouped by
-  // the gate/up launch itself (no grouping launch).  Up to kNaturalXTokens
-  // tokens that launch also reads x in place; larger decode batches have x
-  // re-laid out first by a small launch, as the operand reads of pre-permuted
-  // x keep the gate/up stream faster.
-  constexpr int kNaturalXTokens = 4;
-  const bool self_group = stream_only && entries <= kSelfGroupEntries && E <= 0xFFFF;
-  const bool natural_x = self_group && T <= kNaturalXTokens;
-  if (!mark(0)) return K3MOE_ERR_DEVICE;
-  hipError_t err = self_group ? (natural_x ? hipSuccess : launch_permute_x(g.x, g.x_perm, T, D, s)) : launch_group(g, s);
-  if (err != hipSuccess || !mark(1)) return K3MOE_ERR_DEVICE;
-
-  // Upper bounds of the list lengths (sum over experts of ceil(n_e / rpt)):
-  // an expert in lists 0/1 has more than split_rows rows.
-  const int64_t big_experts = tiled ? (entries / (kStreamMaxRows + 1) < active ? entries / (kStreamMaxRows + 1) : active)
-                                    : active;
-  GemmArgs gu{};
-  gu.act = g.x_perm;
-  gu.act_rows = T;
-  gu.row_tok = g.row_tok;
-  gu.wa = w1;
-  gu.wb = w3;
-  gu.K = D;
-  gu.N = I;
-  gu.out = ws + L.h;
-  gu.out_lo = ws + L.h_lo;
-  gu.h_scale = reinterpret_cast<int8_t*>(ws + L.h_scale);
-  GemmArgs dn{};
-  dn.act = reinterpret_cast<const uint16_t*>(ws + L.h);
-  dn.act_lo = reinterpret_cast<const uint16_t*>(ws + L.h_lo);
-  dn.act_rows = entries;
-  dn.row_tok = nullptr;
-  dn.wa = w2;
-  dn.wb = nullptr;
-  dn.K = I;
-  dn.N = D;
-  dn.out = ws + L.y;
-  dn.h_scale = reinterpret_cast<int8_t*>(ws + L.h_scale);
-  dn.y_scale = reinterpret_cast<int8_t*>(ws + L.y_scale);
-
-  // Experts of both kinds in one call (and no stage events to record): the
-  // streaming launches run on a side stream beside the large-tile launches;
-  // they read the same inputs and write other rows of h and y.  The combine
-  // waits for both branches.
-  SideStream* side = (big_lists && stream_lists && !stage_events) ? side_stream(s) : nullptr;
-  hipStream_t ss = s;
-  if (side) {
-    if (hipEventRecord(side->fork, s) != hipSuccess || hipStreamWaitEvent(side->s, side->fork, 0) != hipSuccess)
-      return K3MOE_ERR_DEVICE;
-    ss = side->s;
-  }
-
-  // gate/up
-  if (big_lists) {
-    gu.tiles = g.tiles[0];
-    gu.tile_count = g.tile_count;
-    gu.max_tiles = entries / g.rows_per_tile[0] + big_experts;
-    err = tiled ? launch_big_gate_up(gu, s) : launch_gate_up(gu, rpt_small, s);
-    if (err != hipSuccess) return K3MOE_ERR_DEVICE;
-  }
-  if (stream_lists) {
-    gu.tiles = g.tiles[2];
-    gu.tile_count = g.tile_count + 2;
-    const int64_t r = g.rows_per_tile[2];
-    gu.max_tiles = (entries + (r - 1) * active) / r;  // bounds the sum of ceil(n_e / r) over experts
-    if (self_group) {
-      SelfGroupArgs sg{};
-      sg.ids = topk_ids;
-      sg.T = (int)T;
-      sg.E = E;
-      sg.k = k;
-      sg.tile_count = g.tile_count;
-      sg.down_tiles = g.tiles[3];
-      sg.slot_row = g.slot_row;
-      gu.act = natural_x ? static_cast<const uint16_t*>(x_bf16) : g.x_perm;
-      gu.row_tok = nullptr;
-      err = launch_stream_gate_up_grouped(gu, sg, natural_x, ss);
-    } else {
-      err = launch_stream_gate_up(gu, ss);
-    }
-    if (err != hipSuccess) return K3MOE_ERR_DEVICE;
-  }
-  if (!mark(2)) return K3MOE_ERR_DEVICE;
-
-  // down
-  if (big_lists) {
-    dn.tiles = g.tiles[1];
-    dn.tile_count = g.tile_count + 1;
-    dn.max_tiles = entries / g.rows_per_tile[1] + big_experts;
-    err = tiled ? launch_big_down(dn, wide_down, s) : launch_down(dn, rpt_small, s);
-    if (err != hipSuccess) return K3MOE_ERR_DEVICE;
-  }
-  if (stream_lists) {
-    dn.tiles = g.tiles[3];
-    dn.tile_count = g.tile_count + 3;
-    const int64_t r = g.rows_per_tile[3];
-    dn.max_tiles = (entries + (r - 1) * active) / r;  // bounds the sum of ceil(n_e / r) over experts
-    err = launch_stream_down(dn, ss);
-    if (err != hipSuccess) return K3MOE_ERR_DEVICE;
-  }
-  if (side) {
-    if (hipEventRecord(side->join, side->s) != hipSuccess || hipStreamWaitEvent(s, side->join, 0) != hipSuccess)
-      return K3MOE_ERR_DEVICE;
-  }
-  if (!mark(3)) return K3MOE_ERR_DEVICE;
-
-  // Rows of the large-tile down kernel hold scaled fp16 y; a streaming-only
-  // batch has none, so its combine reads fp32 rows only.
-  const bool mixed_rows = tiled && !stream_only;
-  err = launch_combine(reinterpret_cast<const float*>(ws + L.y), reinterpret_cast<const int8_t*>(ws + L.y_scale),
-                       mixed_rows, g.slot_row, topk_w, T, D, k, out, s);
-  if (err != hipSuccess || !mark(4)) return K3MOE_ERR_DEVICE;
-  return K3MOE_OK;
+  int st = ffn_arg_status(x_bf16, topk_ids, topk_w, w1, w3, w2, T, D, I, E, k, act, out);
+  if (st != K3MOE_OK || T == 0) return st;
+  if (!workspace) return K3MOE_ERR_NULL;
+  if (misaligned(workspace)) return K3MOE_ERR_ALIGN;
+  if (workspace_bytes < moe_mxfp4_ffn_workspace_size(T, D, I, E, k)) return K3MOE_ERR_WORKSPACE;
+  return run_ffn(x_bf16, topk_ids, topk_w, w1, w3, w2, T, D, I, E, k, out, static_cast<uint8_t*>(workspace),
+                 static_cast<hipStream_t>(stream), stage_events, true);
 }
 
 static int group_shape_status(int64_t T, int32_t E, int32_t k) {

@@ -66,22 +66,32 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
   return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)f);  // round to nearest even
 }
 
-// Stage rows [0, 64) x bytes [byte0, byte0 + seg_bytes) of a weight tile into LDS.
+// Stage rows [0, nrows) x bytes [byte0, byte0 + seg_bytes) of a weight tile
+// into LDS (row r at dword r * kLdsRowDw); rows nrows..63 are left as they
+// are (the MFMA rows they feed are never stored).
 // kVec16: rows and the segment are 16-byte aligned and 272 bytes long.
+// Otherwise dword copies when rows and the segment are 4-byte multiples, and
+// byte copies for the rest (K not a multiple of 128).
 template <bool kVec16>
 __device__ __forceinline__ void stage_weights(const uint8_t* __restrict__ w, size_t row_bytes, size_t byte0,
-                                              int seg_bytes, uint32_t* lds) {
+                                              int seg_bytes, int nrows, uint32_t* lds) {
   if (kVec16) {
-    for (int idx = threadIdx.x; idx < kFeatPerWg * 17; idx += blockDim.x) {
+    for (int idx = threadIdx.x; idx < nrows * 17; idx += blockDim.x) {
       const int r = idx / 17, c = idx - r * 17;
       const uint4 v = *reinterpret_cast<const uint4*>(w + r * row_bytes + byte0 + 16 * c);
       *reinterpret_cast<uint4*>(lds + r * kLdsRowDw + 4 * c) = v;
     }
-  } else {
-    const int dpr = seg_bytes >> 2;  // seg_bytes = 17 * (multiple of 4 blocks)
-    for (int idx = threadIdx.x; idx < kFeatPerWg * dpr; idx += blockDim.x) {
+  } else if (((row_bytes | byte0 | (size_t)seg_bytes) & 3) == 0) {
+    const int dpr = seg_bytes >> 2;
+    for (int idx = threadIdx.x; idx < nrows * dpr; idx += blockDim.x) {
       const int r = idx / dpr, c = idx - r * dpr;
       lds[r * kLdsRowDw + c] = *reinterpret_cast<const uint32_t*>(w + r * row_bytes + byte0 + 4 * c);
+    }
+  } else {
+    uint8_t* lb = reinterpret_cast<uint8_t*>(lds);
+    for (int idx = threadIdx.x; idx < nrows * seg_bytes; idx += blockDim.x) {
+      const int r = idx / seg_bytes, c = idx - r * seg_bytes;
+      lb[r * kLdsRowDw * 4 + c] = w[r * row_bytes + byte0 + c];
     }
   }
 }
@@ -119,6 +129,9 @@ __global__ __launch_bounds__(256) void ffn_gemm_kernel(GemmArgs a) {
   if (tile_idx >= *a.tile_count) return;  // uniform over the workgroup
   const Tile tile = a.tiles[tile_idx];
   const int f0 = blockIdx.y * kFeatPerWg;
+  // output features of this workgroup: 64, or 32 in the last feature tile
+  // when N is an odd multiple of 32
+  const int nfeat = a.N - f0 < kFeatPerWg ? a.N - f0 : kFeatPerWg;
   const int nb = a.K >> 5;
   const size_t row_bytes = (size_t)nb * 17;
   const size_t mat_bytes = (size_t)a.N * row_bytes;
@@ -129,8 +142,10 @@ __global__ __launch_bounds__(256) void ffn_gemm_kernel(GemmArgs a) {
   const int rho = lane & 15, g = lane >> 4;
   // LDS row (feature f0 + lrow) that feeds MFMA row rho of this wave.  For
   // gate/up the rows are chosen so that a lane's four outputs are four
-  // consecutive P-order positions of h (one 8-byte store).
+  // consecutive P-order positions of h (one 8-byte store).  A wave's features
+  // are f0 + 32 * (wave / 2) + 0..31 (gate/up) or f0 + 16 * wave + 0..15 (down).
   const int lrow = kGateUp ? 32 * (wave >> 1) + p_to_elem(16 * (wave & 1) + rho) : 16 * wave + rho;
+  const bool wave_live = (kGateUp ? 32 * (wave >> 1) : 16 * wave) < nfeat;
 
   const uint16_t* brow[NT];
   const uint16_t* brow_lo[NT];
@@ -152,28 +167,36 @@ __global__ __launch_bounds__(256) void ffn_gemm_kernel(GemmArgs a) {
     for (int nt = 0; nt < NT; ++nt) acc[mi][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   for (int seg0 = 0; seg0 < nb; seg0 += kSegBlocks) {
-    const int nbs = (nb - seg0) < kSegBlocks ? (nb - seg0) : kSegBlocks;  // multiple of 4
+    const int nbs = (nb - seg0) < kSegBlocks ? (nb - seg0) : kSegBlocks;
     __syncthreads();  // previous segment fully consumed
-    stage_weights<kVec16>(wA, row_bytes, (size_t)seg0 * 17, nbs * 17, wlds[0]);
-    if (kGateUp) stage_weights<kVec16>(wB, row_bytes, (size_t)seg0 * 17, nbs * 17, wlds[kMats - 1]);
+    stage_weights<kVec16>(wA, row_bytes, (size_t)seg0 * 17, nbs * 17, nfeat, wlds[0]);
+    if (kGateUp) stage_weights<kVec16>(wB, row_bytes, (size_t)seg0 * 17, nbs * 17, nfeat, wlds[kMats - 1]);
     __syncthreads();
-    for (int rnd = 0; rnd < (nbs >> 2); ++rnd) {
-      // activations: block (seg0 + 4*rnd + g), P-order positions 8i..8i+7
+    if (!wave_live) continue;  // no feature of this wave exists (uniform over the wave)
+    for (int rnd = 0; rnd < ((nbs + 3) >> 2); ++rnd) {
+      // lane group g takes block seg0 + 4*rnd + g; in a last round of fewer
+      // than four blocks the groups past the end multiply zeros
+      const bool blk = 4 * rnd + g < nbs;
+      // activations: that block, P-order positions 8i..8i+7
       bf16x8_t bop[NT][4];
       bf16x8_t bop_lo[kGateUp ? 1 : NT][4];
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt) {
         const size_t off = (size_t)(seg0 + 4 * rnd + g) * 32;
+        const bool ld = bvalid[nt] && blk;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          bop[nt][i] = bvalid[nt] ? load_bf16x8(brow[nt] + off + 8 * i) : bf16x8_t{};
-          if (!kGateUp) bop_lo[kGateUp ? 0 : nt][i] = bvalid[nt] ? load_bf16x8(brow_lo[nt] + off + 8 * i) : bf16x8_t{};
+          bop[nt][i] = ld ? load_bf16x8(brow[nt] + off + 8 * i) : bf16x8_t{};
+          if (!kGateUp) bop_lo[kGateUp ? 0 : nt][i] = ld ? load_bf16x8(brow_lo[nt] + off + 8 * i) : bf16x8_t{};
         }
       }
 #pragma unroll
       for (int mi = 0; mi < kMats; ++mi) {
         bf16x8_t aop[4];
         decode_block(wlds[mi], lrow, rnd, g, aop);
+        if (!blk)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) aop[i] = bf16x8_t{};
 #pragma unroll
         for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -186,6 +209,7 @@ __global__ __launch_bounds__(256) void ffn_gemm_kernel(GemmArgs a) {
       }
     }
   }
+  if (!wave_live) return;
 
   // Epilogue.  Lane holds rows 4g..4g+3 (features) of column rho (token).
 #pragma unroll
@@ -219,7 +243,7 @@ __global__ __launch_bounds__(256) void ffn_gemm_kernel(GemmArgs a) {
 
 template <bool kGateUp>
 hipError_t launch_gemm(const GemmArgs& a, int rows_per_tile, hipStream_t s) {
-  const dim3 grid((unsigned)a.max_tiles, (unsigned)(a.N / kFeatPerWg));
+  const dim3 grid((unsigned)a.max_tiles, (unsigned)((a.N + kFeatPerWg - 1) / kFeatPerWg));
   const bool vec16 = ((a.K / 32) % kSegBlocks) == 0;
   const int nt = rows_per_tile / 16;
 #define K3_LAUNCH(NT_, V_) hipLaunchKernelGGL((ffn_gemm_kernel<NT_, kGateUp, V_>), grid, dim3(256), 0, s, a)
@@ -313,9 +337,11 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
       for (int u = 0; u < kB; ++u)
         v[u] = j0 + u < k && r[u] >= 0 ? __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(y + (int64_t)r[u] * D + d))
                                         : f32x4_t{};
-      // skipped and out-of-range slots hold exact zeros: adding them changes nothing
+      // slot order; skipped and out-of-range slots add nothing, whatever
+      // their weight (a NaN or inf weight there must not reach the sum)
 #pragma unroll
       for (int u = 0; u < kB; ++u) {
+        if (j0 + u >= k || r[u] < 0) continue;
 #pragma unroll
         for (int e = 0; e < 4; ++e) acc[e] += wj[u] * v[u][e];
       }

@@ -38,6 +38,9 @@ struct FfnWorkspace {
 };
 
 FfnWorkspace ffn_workspace_layout(int64_t T, int32_t D, int32_t I, int32_t E, int32_t k);
+// Tokens per chunk of moe_mxfp4_ffn (min(T, the largest chunk whose
+// activations the GEMM kernels address with 32-bit offsets)).
+int64_t ffn_chunk_tokens(int64_t T, int32_t D, int32_t I, int32_t k);
 
 // Workspace of the stand-alone grouping call (tile lists and chunk tables; the
 // caller's buffers receive counts, offsets, row_tok and slot_row).  Its tile

@@ -11,7 +11,7 @@ import pytest
 
 HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "k3moe.h")
 
-OK, ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_WORKSPACE, ERR_UNSUPPORTED = 0, -1, -2, -3, -4, -5
+OK, ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_WORKSPACE, ERR_UNSUPPORTED, ERR_DEVICE = 0, -1, -2, -3, -4, -5, -6
 A = 0x10000  # an aligned fake device address (never dereferenced)
 
 
@@ -75,13 +75,17 @@ def ffn(k3, T=8, D=256, I=256, E=8, k=2, act=0, ws_bytes=None, **ptrs):
 
 
 def test_ffn_checks(k3):
-    assert ffn(k3, D=96) == ERR_SHAPE  # D % 128
-    assert ffn(k3, I=200) == ERR_SHAPE
+    assert ffn(k3, D=96 + 16) == ERR_SHAPE  # D % 32
+    assert ffn(k3, I=200) == ERR_SHAPE  # I % 32
+    assert ffn(k3, D=65536 + 32) == ERR_SHAPE  # above K3MOE_MAX_DIM_FFN
+    assert ffn(k3, I=65536 + 32) == ERR_SHAPE
     assert ffn(k3, E=0) == ERR_SHAPE
     assert ffn(k3, E=8193, k=2) == ERR_SHAPE
     assert ffn(k3, k=0) == ERR_SHAPE
-    assert ffn(k3, k=65) == ERR_SHAPE
+    assert ffn(k3, k=65, E=100) == ERR_SHAPE
+    assert ffn(k3, k=9, E=8) == ERR_SHAPE  # k > E
     assert ffn(k3, T=-3) == ERR_SHAPE
+    assert ffn(k3, T=2**31, k=1) == ERR_SHAPE  # T * k must stay below 2^31
     assert ffn(k3, act=1) == ERR_UNSUPPORTED
     assert ffn(k3, T=0, x=None, ids=None, w=None, w1=None, w3=None, w2=None, out=None, ws=None, ws_bytes=0) == OK
     assert ffn(k3, w3=None) == ERR_NULL
@@ -91,6 +95,14 @@ def test_ffn_checks(k3):
     assert ffn(k3, ws_bytes=need - 1) == ERR_WORKSPACE
 
 
+@pytest.mark.parametrize("D,I", [(96, 160), (224, 288), (32, 32), (3584, 3072)])
+def test_ffn_accepts_multiples_of_32(k3, D, I):
+    # shapes that pass every host check fail only at the workspace check here
+    # (a 1-byte workspace), before anything is enqueued
+    assert k3.moe_mxfp4_ffn_workspace_size(8, D, I, 8, 2) > 0
+    assert ffn(k3, D=D, I=I, ws_bytes=1) == ERR_WORKSPACE
+
+
 def test_workspace_size(k3):
     ws = k3.moe_mxfp4_ffn_workspace_size
     assert ws(0, 3584, 3072, 896, 16) == 0
@@ -98,9 +110,20 @@ def test_workspace_size(k3):
     a, b = ws(1, 3584, 3072, 896, 16), ws(4096, 3584, 3072, 896, 16)
     assert 0 < a < b
     T, D, I, k = 4096, 3584, 3072, 16
-    # at least h (bf16) + y (fp32) + the re-laid-out activations
-    assert b >= T * k * I * 2 + T * k * D * 4 + T * D * 2
+    # at least h (fp16 / bf16) + y (fp16) + the re-laid-out activations
+    assert b >= T * k * I * 2 + T * k * D * 2 + T * D * 2
     assert b % 256 == 0
+
+
+def test_workspace_is_one_token_chunk(k3):
+    # past (2^31 - 1) / (2 k max(D, I)) tokens (rounded down to 64) the layer
+    # runs in chunks that reuse one chunk's workspace
+    ws = k3.moe_mxfp4_ffn_workspace_size
+    D, I, E, k = 3584, 3072, 896, 16
+    chunk = ((2**31 - 1) // (2 * k * max(D, I))) // 64 * 64
+    assert chunk == 18688
+    assert ws(chunk, D, I, E, k) == ws(chunk + 1, D, I, E, k) == ws(5 * chunk + 7, D, I, E, k)
+    assert ws(chunk - 1, D, I, E, k) < ws(chunk, D, I, E, k)
 
 
 def group(k3, T=8, E=8, k=2, ws_bytes=None, **ptrs):

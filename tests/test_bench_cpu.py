@@ -5,6 +5,7 @@ the per-token flop count and per-expert byte count of the K3 shape."""
 import os
 import sys
 
+import numpy as np
 import pytest
 
 import moe_inputs
@@ -14,6 +15,7 @@ import bench  # noqa: E402
 
 K3_FLOPS_PER_TOKEN = 1_056_964_608  # 2 * k * 3 * D * I at k=16, D=3584, I=3072
 K3_EXPERT_BYTES = 17_547_264  # 3 matrices of 3072 x 3584 weights, 17 bytes per 32
+GEMM_LAUNCHES = ("gate_up", "gate_up_stream", "down", "down_stream")
 
 
 @pytest.mark.parametrize(
@@ -24,35 +26,79 @@ def test_gemm_path(name, path):
     assert bench.gemm_path(moe_inputs.CONFIGS[name]) == path
 
 
+def test_gemm_path_no_size_cliff():
+    # prefill far beyond 2^31 bytes of grouped h: still the tiled path (the
+    # library runs it in token chunks)
+    assert bench.gemm_path(moe_inputs.PREFILL.with_(T=40000)) == "tiled"
+
+
 @pytest.mark.parametrize(
-    "name,stage,kernel",
+    "name,launch,kernel",
     [
-        ("decode-t1", "gate_up", "ffn_stream_kernel<true, true, true>"),
-        ("decode-t8", "gate_up", "ffn_stream_kernel<true, true, false>"),
-        ("decode-t8", "down", "ffn_stream_kernel<false, false, false>"),
-        ("verify", "gate_up", "ffn_big_kernel<true, 128> + ffn_stream_kernel<true, false, false>"),
-        ("verify", "down", "ffn_big_kernel<false, 64> + ffn_stream_kernel<false, false, false>"),
-        ("prefill", "down", "ffn_big_kernel<false, 128> + ffn_stream_kernel<false, false, false>"),
+        ("decode-t1", "gate_up_stream", "ffn_stream_kernel<true, true, true>"),
+        ("decode-t8", "gate_up_stream", "ffn_stream_kernel<true, true, false>"),
+        ("decode-t8", "down_stream", "ffn_stream_kernel<false, false, false>"),
+        ("decode-t1", "gate_up", None),
+        ("decode-t8", "down", None),
+        ("verify", "gate_up", "ffn_big_kernel<true, 128>"),
+        ("verify", "gate_up_stream", "ffn_stream_kernel<true, false, false>"),
+        ("verify", "down", "ffn_big_kernel<false, 64>"),
+        ("prefill", "down", "ffn_big_kernel<false, 128>"),
+        ("tiny", "gate_up", "ffn_gemm_kernel<NT, true, ...>"),
+        ("tiny", "down_stream", None),
     ],
 )
-def test_kernel_names(name, stage, kernel):
+def test_kernel_names(name, launch, kernel):
     cfg = moe_inputs.CONFIGS[name]
-    got, sources = bench.kernel_info(stage, bench.gemm_path(cfg), cfg.T * cfg.k, cfg.T)
+    info = bench.kernel_info(launch, bench.gemm_path(cfg), cfg.T * cfg.k, cfg.T)
+    if kernel is None:
+        assert info is None
+        return
+    got, sources = info
     assert got == kernel
     assert all(os.path.exists(os.path.join(bench.ROOT, s)) for s in sources)
 
 
-@pytest.mark.parametrize("name", ["decode-t1", "decode-t8", "verify", "prefill"])
+def _counts(cfg, seed=0):
+    g = np.random.default_rng(seed)
+    ids = np.stack([g.permutation(cfg.E)[: cfg.k] for _ in range(cfg.T)])
+    return np.bincount(ids.reshape(-1), minlength=cfg.E)
+
+
+@pytest.mark.parametrize("name", ["decode-t1", "decode-t8", "verify", "prefill", "tiny"])
 def test_work_per_token_and_expert(name):
     cfg = moe_inputs.CONFIGS[name]
-    rows = cfg.T * cfg.k
-    f_gu, _ = bench.stage_work("gate_up", cfg, rows, 0)
-    f_dn, _ = bench.stage_work("down", cfg, rows, 0)
-    assert f_gu + f_dn == K3_FLOPS_PER_TOKEN * cfg.T
-    # weight bytes of one active expert: the gate/up and down byte counts grow
-    # by exactly one expert's matrices per extra active expert
-    _, b0 = bench.stage_work("gate_up", cfg, rows, 0)
-    _, b1 = bench.stage_work("gate_up", cfg, rows, 1)
-    _, d0 = bench.stage_work("down", cfg, rows, 0)
-    _, d1 = bench.stage_work("down", cfg, rows, 1)
-    assert (b1 - b0) + (d1 - d0) == K3_EXPERT_BYTES
+    path = bench.gemm_path(cfg)
+    counts = _counts(cfg)
+    st = bench.routing_stats(counts, path)
+    assert st[0] + st[2] == cfg.T * cfg.k and st[1] + st[3] == int((counts > 0).sum())
+    flops = sum(bench.launch_work(l, cfg, path, st)[0] for l in GEMM_LAUNCHES)
+    if name != "tiny":
+        assert flops == K3_FLOPS_PER_TOKEN * cfg.T
+    else:
+        assert flops == 2 * cfg.k * 3 * cfg.D * cfg.I * cfg.T
+    # one more expert served by the streaming kernels adds exactly one
+    # expert's matrices to the weight bytes
+    if path != "small":
+        rb, nb, rs, ns = st
+        more = (rb, nb, rs, ns + 1)
+        d = sum(bench.launch_work(l, cfg, path, more)[1] - bench.launch_work(l, cfg, path, st)[1]
+                for l in GEMM_LAUNCHES)
+        assert d == K3_EXPERT_BYTES
+
+
+def test_large_tile_h_and_y_counted_at_two_bytes():
+    cfg = moe_inputs.PREFILL
+    st = (1000, 1, 0, 0)  # one large-tile expert with 1000 rows
+    _, b = bench.launch_work("down", cfg, "tiled", st)
+    mat2 = cfg.D * (cfg.I // 32) * 17
+    assert b == mat2 + 1000 * cfg.I * 2 + 1000 * cfg.D * 2
+    _, s = bench.launch_work("down", cfg, "small", st)
+    assert s == mat2 + 1000 * cfg.I * 4 + 1000 * cfg.D * 4
+
+
+def test_routing_stats_split_at_four_rows():
+    counts = np.array([0, 1, 4, 5, 100, 0, 3])
+    assert bench.routing_stats(counts, "tiled") == (105, 2, 8, 3)
+    assert bench.routing_stats(counts, "stream") == (0, 0, 113, 5)
+    assert bench.routing_stats(counts, "small") == (113, 5, 0, 0)

@@ -79,6 +79,11 @@ def test_tiny(k3):
         (3, 3, 512, 1024, 5),  # streaming-only batch: every expert has all 5 rows
         (4, 2, 512, 512, 9),  # one token past the streaming-only batch: large-tile kernels for experts of 5+ rows
         (200, 64, 512, 512, 4),  # grouping inside the gate/up launch: 256 entries, one per thread
+        (8, 2, 96, 160, 50),  # D, I multiples of 32 only: odd block counts (unaligned rows), a 32-feature tile
+        (6, 3, 224, 288, 70),  # 7 and 9 blocks per row, 224 / 288 outputs (a partial last feature tile)
+        (4, 2, 32, 32, 10),  # one block per row, one 32-feature tile
+        (8, 2, 384, 640, 33),  # 12 and 20 blocks per row (4-byte rows, a partial last K segment)
+        (5, 2, 544, 96, 130),  # 17 blocks per row: one full K segment plus one block
     ],
 )
 def test_shapes(k3, E, k, D, I, T):
@@ -127,6 +132,30 @@ def test_streaming_path_hot_invalid_and_duplicate_ids(k3, T):
     assert_ffn_close(got, ref, "streaming hot/invalid/duplicate")
     a = run_ffn(k3, dev, batch.x, ids, w)
     assert np.array_equal(a.view(np.uint32), got.view(np.uint32))
+
+
+@pytest.mark.parametrize("T,D,I", [(3, 512, 512), (8, 512, 512), (40, 128, 256)])
+def test_nan_and_inf_weights_on_skipped_entries(k3, T, D, I):
+    # an entry that is skipped (id out of range, or a repeat within its row)
+    # contributes nothing whatever its weight: NaN and inf there must not
+    # reach the output (streaming path grouped in the gate/up launch with x
+    # read in place / re-laid out, and the small-tile path)
+    print(f"[ffn] NaN/inf weights on skipped entries T={T} D={D} I={I}", flush=True)
+    cfg = moe_inputs.TINY.with_(E=40, k=4, D=D, I=I, T=T, config_id=49)
+    g = np.random.default_rng(19)
+    ids = np.stack([g.permutation(cfg.E)[: cfg.k] for _ in range(cfg.T)]).astype(np.int32)
+    w = g.random((cfg.T, cfg.k)).astype(np.float32)
+    ids[0, 1] = -1
+    w[0, 1] = np.nan
+    ids[1, 3] = cfg.E + 2
+    w[1, 3] = np.inf
+    ids[2, 2] = ids[2, 0]  # repeat -> skipped
+    w[2, 2] = np.nan
+    ids[T - 1, 3] = ids[T - 1, 1]
+    w[T - 1, 3] = -np.inf
+    got, ref, _, _ = small_case(k3, cfg, ids, w)
+    assert np.all(np.isfinite(ref))
+    assert_ffn_close(got, ref, f"NaN/inf on skipped entries T={T} D={D}")
 
 
 def test_self_grouping_duplicates_and_invalid_ids(k3):
@@ -456,26 +485,123 @@ def k3_experts(k3):
     return device_experts(k3, moe_inputs.PREFILL)
 
 
-def sample_tokens(T, n, seed):
-    if T <= n:
-        return np.arange(T)
-    return np.sort(np.random.default_rng(seed).choice(T, size=n, replace=False))
+def last_tokens_of(ids, experts):
+    """The largest token routed to each expert (its last grouped row)."""
+    return [int(np.argwhere(ids == e)[:, 0].max()) for e in experts]
 
 
-@pytest.mark.parametrize("name,n_sample", [("decode-t1", 1), ("decode-t8", 2), ("verify", 2), ("prefill", 2)])
-def test_k3_configs_end_to_end(k3, k3_experts, name, n_sample):
-    """GPU route -> GPU FFN at full size vs oracle route -> oracle FFN on sampled tokens."""
+def covering_tokens(ids, experts):
+    """A small set of tokens that together route to every expert listed (greedy cover)."""
+    need = set(int(e) for e in experts)
+    chosen = []
+    while need:
+        best = max(range(ids.shape[0]), key=lambda t: len(need & set(ids[t].tolist())))
+        chosen.append(best)
+        need -= set(ids[best].tolist())
+    return chosen
+
+
+def split_by_experts(ids, toks, parts):
+    """Split the tokens into `parts` groups of about equal distinct-expert counts."""
+    toks = sorted(set(int(t) for t in toks))
+    total = len(np.unique(ids[toks]))
+    groups, cur, seen = [], [], set()
+    for t in toks:
+        cur.append(t)
+        seen |= set(ids[t].tolist())
+        if len(seen) >= total / parts * (len(groups) + 1) and len(groups) < parts - 1:
+            groups.append(cur)
+            cur = []
+    groups.append(cur)
+    groups += [[] for _ in range(parts - len(groups))]
+    return groups
+
+
+def checked_tokens(name, ids, E):
+    """Tokens of a K3 workload that the oracle checks, and why.
+
+    decode: every token.  verify / prefill: the last token of every expert
+    served by the large-tile kernels (more than 4 rows: its last row tile of
+    both products) among the hottest (all of them at verify, the 8 hottest at
+    prefill), and tokens covering every expert served by the weight-streaming
+    kernels (at most 4 rows; at prefill at least one such expert).
+    """
+    T = ids.shape[0]
+    if T <= 8:
+        return list(range(T))
+    counts = np.bincount(ids.reshape(-1), minlength=E)
+    big = np.argsort(-counts, kind="stable")
+    big = [int(e) for e in big if counts[e] > 4]
+    stream = [int(e) for e in np.flatnonzero((counts > 0) & (counts <= 4))]
+    if name == "prefill":
+        big = big[:8]
+        stream = stream[:1]
+    return sorted(set(last_tokens_of(ids, big)) | set(covering_tokens(ids, stream)))
+
+
+K3_PARTS = {"decode-t1": 1, "decode-t8": 4, "verify": 4, "prefill": 2}
+
+
+@pytest.mark.parametrize("name,part", [(n, p) for n, c in K3_PARTS.items() for p in range(c)])
+def test_k3_configs_end_to_end(k3, k3_experts, name, part):
+    """GPU route -> GPU FFN at full size vs oracle route -> oracle FFN on the
+    checked tokens (split into parts of about equal oracle cost)."""
     cfg = moe_inputs.CONFIGS[name]
-    print(f"[ffn] K3 {name} T={cfg.T}", flush=True)
     batch, x, z, b = moe_inputs.device.upload_batch(cfg)
     ids_d, w_d = k3.moe_route_topk(z, b, cfg.k)
     out = k3.moe_mxfp4_ffn(x, ids_d, w_d, k3_experts.w1, k3_experts.w3, k3_experts.w2).cpu().numpy()
     ids, w = route_ref(batch.z, batch.b, cfg.k)
     assert np.array_equal(ids_d.cpu().numpy(), ids)
     assert np.all(np.isfinite(out))
-    toks = sample_tokens(cfg.T, n_sample, seed=cfg.config_id)
-    # include the token routed to the hottest expert (the longest run of tiles)
-    hot = np.bincount(ids.reshape(-1), minlength=cfg.E).argmax()
-    toks = np.unique(np.concatenate([toks, [np.argwhere(ids == hot)[-1][0]]]))
-    ref = ffn_ref(batch.x, ids, w, batch.experts, tokens=toks)
-    assert_ffn_close(out[toks], ref, f"{name} tokens {toks.tolist()}")
+    toks = split_by_experts(ids, checked_tokens(name, ids, cfg.E), K3_PARTS[name])[part]
+    print(f"[ffn] K3 {name} T={cfg.T} part {part}: tokens {toks}", flush=True)
+    assert toks
+    ref = ffn_ref(batch.x, ids, w, batch.experts, tokens=np.array(toks))
+    assert_ffn_close(out[toks], ref, f"{name} tokens {toks}")
+
+
+def test_k3_checked_tokens_cover_every_tile_kind():
+    # the token selection itself (host only): verify covers every expert of
+    # either GEMM kind, prefill the 8 hottest experts' last rows and a
+    # streaming expert
+    for name in ("verify", "prefill"):
+        cfg = moe_inputs.CONFIGS[name]
+        batch = moe_inputs.make_batch(cfg)
+        ids, _ = route_ref(batch.z, batch.b, cfg.k)
+        toks = checked_tokens(name, ids, cfg.E)
+        counts = np.bincount(ids.reshape(-1), minlength=cfg.E)
+        covered = set(ids[toks].reshape(-1).tolist())
+        if name == "verify":
+            assert covered >= set(np.flatnonzero(counts).tolist())
+        hot = np.argsort(-counts, kind="stable")[:8]
+        for e in hot:
+            assert int(np.argwhere(ids == e)[:, 0].max()) in toks
+        assert any(0 < counts[e] <= 4 for e in covered)
+        parts = split_by_experts(ids, toks, K3_PARTS[name])
+        assert sorted(t for p in parts for t in p) == sorted(set(toks)) and all(parts)
+
+
+def test_k3_prefill_beyond_32bit_offsets(k3, k3_experts):
+    """20000 tokens at K3 shape: more than (2^31 - 1) / (2 k max(D, I)) =
+    18724 tokens, so the layer runs as a chunk of 18688 tokens and one of
+    1312 with the large-tile and streaming kernels (there is no fallback
+    path); the oracle checks the last rows of the hottest experts of each
+    chunk, both sides of the chunk boundary and the last token."""
+    cfg = moe_inputs.PREFILL.with_(T=20000, config_id=84)
+    batch, x, z, b = moe_inputs.device.upload_batch(cfg)
+    ids_d, w_d = k3.moe_route_topk(z, b, cfg.k)
+    out = k3.moe_mxfp4_ffn(x, ids_d, w_d, k3_experts.w1, k3_experts.w3, k3_experts.w2).cpu().numpy()
+    ids, w = route_ref(batch.z, batch.b, cfg.k)
+    assert np.array_equal(ids_d.cpu().numpy(), ids)
+    assert np.all(np.isfinite(out))
+    chunk = 18688
+    toks = {chunk - 1, chunk, cfg.T - 1}
+    for lo, hi in ((0, chunk), (chunk, cfg.T)):
+        sub = ids[lo:hi]
+        counts = np.bincount(sub.reshape(-1), minlength=cfg.E)
+        for e in np.argsort(-counts, kind="stable")[:2]:
+            toks.add(lo + int(np.argwhere(sub == e)[:, 0].max()))
+    toks = sorted(toks)
+    print(f"[ffn] K3 prefill T={cfg.T}: tokens {toks}", flush=True)
+    ref = ffn_ref(batch.x, ids, w, batch.experts, tokens=np.array(toks))
+    assert_ffn_close(out[toks], ref, f"T=20000 tokens {toks}")
