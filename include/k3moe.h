@@ -11,7 +11,8 @@
  *   - Array pointers are DEVICE pointers unless stated otherwise. The caller
  *     allocates and owns every buffer; no entry point allocates device memory
  *     or synchronizes the host. The library's state: moe_mxfp4_ffn's
- *     per-thread side stream (below).
+ *     per-thread side stream (below) and moe_mxfp4_ffn_noalloc's fixed
+ *     scratch array, one per device.
  *   - `stream` is a hipStream_t (NULL = the default stream) of the current
  *     device, which also holds every buffer passed. Every call only enqueues
  *     work on it and returns; results are ready when the stream is.
@@ -41,7 +42,8 @@ typedef enum {
   K3MOE_ERR_ALIGN = -3,       /* a device pointer is not 16-byte aligned */
   K3MOE_ERR_WORKSPACE = -4,   /* workspace smaller than moe_mxfp4_ffn_workspace_size() */
   K3MOE_ERR_UNSUPPORTED = -5, /* unknown enum value (activation, output dtype) */
-  K3MOE_ERR_DEVICE = -6       /* the HIP runtime refused a launch (e.g. no gfx950 device) */
+  K3MOE_ERR_DEVICE = -6,      /* the HIP runtime refused a launch (e.g. no gfx950 device) */
+  K3MOE_ERR_TOO_LARGE = -7    /* moe_mxfp4_ffn_noalloc: the sizes need more than its fixed scratch */
 } k3moe_status;
 
 /* Largest top-k the router and FFN accept. */
@@ -212,6 +214,30 @@ int moe_mxfp4_ffn_profiled(const void* x_bf16, const int32_t* topk_ids, const fl
                            const uint8_t* w3, const uint8_t* w2, int64_t T, int32_t D, int32_t I, int32_t E,
                            int32_t k, int32_t act, float* out, void* workspace, size_t workspace_bytes,
                            void* stream, void* const* stage_events);
+
+/*
+ * moe_mxfp4_ffn_noalloc — moe_mxfp4_ffn for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc): the workspace is a fixed scratch array inside the
+ * library, so the caller passes only inputs and outputs.
+ *
+ * Same arguments (without workspace), checks and results as moe_mxfp4_ffn;
+ * every launch stays on `stream` (no side stream). The scratch holds
+ * K3MOE_NOALLOC_SCRATCH_BYTES on every device the library runs on, from the
+ * first use there until the process ends; sizes whose
+ * moe_mxfp4_ffn_workspace_size() exceeds it give K3MOE_ERR_TOO_LARGE and
+ * enqueue nothing (K3 shape: up to 128 tokens at k = 16). The call calls no
+ * allocating routine; its first call on a device looks up the array's
+ * device address (K3MOE_ERR_DEVICE if the runtime refuses).
+ * All calls on one device share its one array: calls that overlap on a
+ * device (different streams, or host threads, without ordering between
+ * them) race on it and give undefined results. Nothing in the array needs
+ * to start at a known value.
+ */
+#define K3MOE_NOALLOC_SCRATCH_BYTES (64u << 20)
+int moe_mxfp4_ffn_noalloc(const void* x_bf16, const int32_t* topk_ids, const float* topk_w, const uint8_t* w1,
+                          const uint8_t* w3, const uint8_t* w2, int64_t T, int32_t D, int32_t I, int32_t E,
+                          int32_t k, int32_t act, float* out, void* stream);
 
 /*
  * moe_group_workspace_size — bytes of device workspace moe_group_by_expert

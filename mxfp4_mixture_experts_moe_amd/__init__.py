@@ -24,6 +24,8 @@ __all__ = [
     "mxfp4_dequant",
     "moe_mxfp4_ffn_workspace_size",
     "moe_mxfp4_ffn",
+    "moe_mxfp4_ffn_noalloc",
+    "NOALLOC_SCRATCH_BYTES",
     "moe_group_workspace_size",
     "moe_group_by_expert",
     "FFN_STAGES",
@@ -59,6 +61,9 @@ lib.moe_mxfp4_ffn.restype = ctypes.c_int
 lib.moe_mxfp4_ffn.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _sz, _vp]
 lib.moe_mxfp4_ffn_profiled.restype = ctypes.c_int
 lib.moe_mxfp4_ffn_profiled.argtypes = lib.moe_mxfp4_ffn.argtypes + [ctypes.POINTER(ctypes.c_void_p)]
+lib.moe_mxfp4_ffn_noalloc.restype = ctypes.c_int
+lib.moe_mxfp4_ffn_noalloc.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _i32, _i32, _vp, _vp]
+NOALLOC_SCRATCH_BYTES = 64 << 20
 lib.moe_group_workspace_size.restype = _sz
 lib.moe_group_workspace_size.argtypes = [_i64, _i32, _i32]
 lib.moe_group_by_expert.restype = ctypes.c_int
@@ -217,6 +222,18 @@ def moe_mxfp4_ffn(x: torch.Tensor, ids: torch.Tensor, weights: torch.Tensor, w1:
                 ev.record()  # torch creates its events lazily
             handles[i] = None if ev is None else ev.cuda_event
         _check("moe_mxfp4_ffn_profiled", lib.moe_mxfp4_ffn_profiled(*args, handles))
+    return out
+
+
+def moe_mxfp4_ffn_noalloc(x: torch.Tensor, ids: torch.Tensor, weights: torch.Tensor, w1: torch.Tensor,
+                          w3: torch.Tensor, w2: torch.Tensor, out: torch.Tensor, act: int = ACT_SILU_MUL) -> torch.Tensor:
+    """moe_mxfp4_ffn in the library's fixed device scratch (no workspace, no
+    allocation: `out` is required). Raises K3MoeError (status -7) when the
+    sizes need more than NOALLOC_SCRATCH_BYTES of workspace."""
+    T, D, I, E, k, out = _ffn_operands(x, ids, weights, w1, w3, w2, out)
+    _check("moe_mxfp4_ffn_noalloc", lib.moe_mxfp4_ffn_noalloc(_ptr(x), _ptr(ids), _ptr(weights), _ptr(w1), _ptr(w3),
+                                                              _ptr(w2), T, D, I, E, k, act, _ptr(out),
+                                                              _stream(x.device)))
     return out
 
 

@@ -6,6 +6,9 @@
 #include <sys/syscall.h>
 #include <unistd.h>
 
+#include <atomic>
+#include <mutex>
+
 namespace k3moe {
 
 static size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
@@ -139,6 +142,34 @@ SideStream* side_stream(hipStream_t caller) {
   if (hipStreamGetCaptureInfo(ss.s, &side_cs, &side_id) != hipSuccess) return nullptr;
   if (side_cs != hipStreamCaptureStatusNone && (cs != hipStreamCaptureStatusActive || side_id != cid)) return nullptr;
   return &ss;
+}
+
+// ---------------------------------------------------------------------------
+// Fixed scratch of moe_mxfp4_ffn_noalloc: one copy per device, held from the
+// library's first use on that device until the process ends.  Host code never
+// passes the array's name (a host-side stand-in) to a kernel; it uses the
+// device address looked up once per device.
+static __device__ __align__(256) uint8_t scratch[K3MOE_NOALLOC_SCRATCH_BYTES];
+
+std::mutex g_scratch_mu;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+
+// Device address of the current device's scratch (nullptr if the runtime
+// refuses the lookup).
+void* scratch_ptr() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p) return p;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+  if (!p) {
+    void* q = nullptr;
+    if (hipGetSymbolAddress((void**)&q, HIP_SYMBOL(scratch)) != hipSuccess || q == nullptr) return nullptr;
+    g_scratch_ptr[dev].store(q, std::memory_order_release);
+    p = q;
+  }
+  return p;
 }
 
 // ---------------------------------------------------------------------------
@@ -371,6 +402,8 @@ const char* k3moe_status_str(int status) {
     case K3MOE_ERR_WORKSPACE: return "workspace is smaller than moe_mxfp4_ffn_workspace_size()";
     case K3MOE_ERR_UNSUPPORTED: return "unsupported enum value";
     case K3MOE_ERR_DEVICE: return "the HIP runtime refused a launch";
+    case K3MOE_ERR_TOO_LARGE:
+      return "the sizes need more workspace than the library's fixed scratch holds (K3MOE_NOALLOC_SCRATCH_BYTES)";
     default: return "unknown status";
   }
 }
@@ -432,6 +465,19 @@ int moe_mxfp4_ffn_profiled(const void* x_bf16, const int32_t* topk_ids, const fl
   if (workspace_bytes < moe_mxfp4_ffn_workspace_size(T, D, I, E, k)) return K3MOE_ERR_WORKSPACE;
   return run_ffn(x_bf16, topk_ids, topk_w, w1, w3, w2, T, D, I, E, k, out, static_cast<uint8_t*>(workspace),
                  static_cast<hipStream_t>(stream), stage_events, true);
+}
+
+int moe_mxfp4_ffn_noalloc(const void* x_bf16, const int32_t* topk_ids, const float* topk_w, const uint8_t* w1,
+                          const uint8_t* w3, const uint8_t* w2, int64_t T, int32_t D, int32_t I, int32_t E,
+                          int32_t k, int32_t act, float* out, void* stream) {
+  int st = ffn_arg_status(x_bf16, topk_ids, topk_w, w1, w3, w2, T, D, I, E, k, act, out);
+  if (st != K3MOE_OK || T == 0) return st;
+  if (moe_mxfp4_ffn_workspace_size(T, D, I, E, k) > (size_t)K3MOE_NOALLOC_SCRATCH_BYTES) return K3MOE_ERR_TOO_LARGE;
+  void* ws = scratch_ptr();
+  if (!ws) return K3MOE_ERR_DEVICE;
+  // every launch on the caller's stream: no side stream (creating one may allocate)
+  return run_ffn(x_bf16, topk_ids, topk_w, w1, w3, w2, T, D, I, E, k, out, static_cast<uint8_t*>(ws),
+                 static_cast<hipStream_t>(stream), nullptr, false);
 }
 
 static int group_shape_status(int64_t T, int32_t E, int32_t k) {

@@ -11,7 +11,7 @@ import pytest
 
 HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "k3moe.h")
 
-OK, ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_WORKSPACE, ERR_UNSUPPORTED, ERR_DEVICE = 0, -1, -2, -3, -4, -5, -6
+OK, ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_WORKSPACE, ERR_UNSUPPORTED, ERR_DEVICE, ERR_TOO_LARGE = 0, -1, -2, -3, -4, -5, -6, -7
 A = 0x10000  # an aligned fake device address (never dereferenced)
 
 
@@ -25,13 +25,13 @@ def test_library_exports_every_declared_symbol(k3):
     names = declared_functions()
     assert set(names) == {"k3moe_status_str", "moe_route_topk", "mxfp4_repack", "mxfp4_dequant",
                           "moe_mxfp4_ffn_workspace_size", "moe_mxfp4_ffn", "moe_mxfp4_ffn_profiled",
-                          "moe_group_workspace_size", "moe_group_by_expert"}
+                          "moe_mxfp4_ffn_noalloc", "moe_group_workspace_size", "moe_group_by_expert"}
     for n in names:
         assert hasattr(k3.lib, n), n
 
 
 def test_status_strings(k3):
-    for s in range(-6, 1):
+    for s in range(-7, 1):
         assert k3.status_str(s) and k3.status_str(s) != "unknown status"
     assert k3.status_str(-99) == "unknown status"
 
@@ -101,6 +101,27 @@ def test_ffn_accepts_multiples_of_32(k3, D, I):
     # (a 1-byte workspace), before anything is enqueued
     assert k3.moe_mxfp4_ffn_workspace_size(8, D, I, 8, 2) > 0
     assert ffn(k3, D=D, I=I, ws_bytes=1) == ERR_WORKSPACE
+
+
+def noalloc(k3, T=8, D=256, I=256, E=8, k=2, act=0, **ptrs):
+    p = dict(x=A, ids=A, w=A, w1=A, w3=A, w2=A, out=A)
+    p.update(ptrs)
+    return k3.lib.moe_mxfp4_ffn_noalloc(p["x"], p["ids"], p["w"], p["w1"], p["w3"], p["w2"], T, D, I, E, k, act,
+                                        p["out"], None)
+
+
+def test_ffn_noalloc_checks(k3):
+    assert noalloc(k3, D=100) == ERR_SHAPE
+    assert noalloc(k3, k=9) == ERR_SHAPE
+    assert noalloc(k3, act=3) == ERR_UNSUPPORTED
+    assert noalloc(k3, T=0, x=None, ids=None, w=None, w1=None, w3=None, w2=None, out=None) == OK
+    assert noalloc(k3, out=None) == ERR_NULL
+    assert noalloc(k3, w1=A + 8) == ERR_ALIGN
+    # K3 shape: 128 tokens fit the fixed scratch, 4096 do not
+    ws = k3.moe_mxfp4_ffn_workspace_size
+    assert ws(128, 3584, 3072, 896, 16) <= k3.NOALLOC_SCRATCH_BYTES < ws(4096, 3584, 3072, 896, 16)
+    assert noalloc(k3, T=4096, D=3584, I=3072, E=896, k=16) == ERR_TOO_LARGE
+    assert "scratch" in k3.status_str(ERR_TOO_LARGE)
 
 
 def test_workspace_size(k3):
