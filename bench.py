@@ -109,6 +109,11 @@ def parse_args():
     ap.add_argument("--no-cpu-baseline", dest="cpu_baseline", action="store_false")
     ap.add_argument("--cpu-sample-tokens", type=int, default=0, help="tokens the oracle evaluates (0: auto)")
     ap.add_argument("--eager", action="store_true", help="time eager launches instead of graph replays")
+    ap.add_argument("--serial-launches", action="store_true",
+                    help="launch every FFN kernel on the caller's stream (no side-stream branch); the roofline's "
+                         "timed launches are always serial, so profiles taken with this flag match them")
+    ap.add_argument("--cold-steps", type=int, default=21,
+                    help="steps timed one at a time after a 1 GiB cache-evicting read (median reported; 0: none)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only copy a 256 MiB buffer 3 times (reference kernel for HBM traffic counters)")
     return ap.parse_args()
@@ -230,7 +235,7 @@ def cpu_baseline(cfg, batch, sample_tokens):
     }
 
 
-def measure(name, cfg, dev, k3, steps, warmup, rotate, eager):
+def measure(name, cfg, dev, k3, steps, warmup, rotate, eager, cold_steps=0, serial=False):
     """Time one workload on the resident experts; returns its result fields."""
     import numpy as np
     import torch
@@ -253,6 +258,10 @@ def measure(name, cfg, dev, k3, steps, warmup, rotate, eager):
         n_active.append(int((counts > 0).sum()))
     torch.cuda.synchronize()
 
+    # serial: every FFN launch on the caller's stream (moe_mxfp4_ffn_profiled
+    # with no events), as in the timed-launch pass below
+    no_events = [None] * k3.FFN_STAGE_EVENTS if serial else None
+
     def step(i, events=None):
         j = i % rotate
         _, x, z, b = batches[j]
@@ -260,7 +269,7 @@ def measure(name, cfg, dev, k3, steps, warmup, rotate, eager):
             events[0].record()
         k3.moe_route_topk(z, b, cfg.k, ids=ids[j], weights=wts[j])
         k3.moe_mxfp4_ffn(x, ids[j], wts[j], dev.w1, dev.w3, dev.w2, out=out, workspace=ws,
-                         stage_events=None if events is None else events[1:])
+                         stage_events=no_events if events is None else events[1:])
 
     def busy_head():
         # keep the GPU busy while the host enqueues the measured steps, so no
@@ -307,6 +316,23 @@ def measure(name, cfg, dev, k3, steps, warmup, rotate, eager):
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
 
+    # 2b. cold steps: before each one a read of a 1 GiB buffer evicts the
+    #     experts from the 256 MiB Infinity Cache and the L2s; each replay is
+    #     timed alone by two events, and the median is reported
+    cold_ms = []
+    if graphs and cold_steps > 0:
+        flush = torch.ones(1 << 28, dtype=torch.int32, device="cuda")  # 1 GiB
+        sink = torch.empty((), dtype=torch.int64, device="cuda")
+        ce = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(cold_steps)]
+        for i in range(cold_steps):
+            torch.sum(flush, dim=0, dtype=torch.int64, out=sink)
+            ce[i][0].record()
+            graphs[(warmup + i) % rotate].replay()
+            ce[i][1].record()
+        torch.cuda.synchronize()
+        cold_ms = [a.elapsed_time(b) for a, b in ce]
+        del flush
+
     # 3. eager steps with the longest launch bracketed by two events on the
     #    library's stream (its per-launch duration for the roofline), and the
     #    eager step time from two events around all of them
@@ -316,17 +342,26 @@ def measure(name, cfg, dev, k3, steps, warmup, rotate, eager):
     # measure mostly their own overhead)
     dom = max([s for s in have if s in GEMM_LAUNCHES], key=lambda s: launch_ms[s])
     n = LAUNCHES.index(dom)
+    #    Each step also records two events back to back on the same stream
+    #    (nothing between them): their mean interval is the fixed cost an
+    #    event pair adds around a launch, which the per-launch duration has
+    #    subtracted (the raw interval is reported beside it).
     n_ev = min(steps, 200)
     dev_ev = [[torch.cuda.Event(enable_timing=True) if m in (n, n + 1) else None for m in range(n_ev_slots)]
               for _ in range(n_ev)]
+    pair = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_ev)]
     e_start, e_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     busy_head()
     e_start.record()
     for i in range(n_ev):
         step(warmup + i, dev_ev[i])
+        pair[i][0].record()
+        pair[i][1].record()
     e_end.record()
     torch.cuda.synchronize()
-    dom_ms = float(np.mean([dev_ev[i][n].elapsed_time(dev_ev[i][n + 1]) for i in range(n_ev)]))
+    dom_raw_ms = float(np.mean([dev_ev[i][n].elapsed_time(dev_ev[i][n + 1]) for i in range(n_ev)]))
+    pair_ms = float(np.mean([a.elapsed_time(b) for a, b in pair]))
+    dom_ms = dom_raw_ms - pair_ms
     eager_ms = e_start.elapsed_time(e_end) / n_ev
 
     work = [launch_work(dom, cfg, path, stats[(warmup + i) % rotate]) for i in range(n_ev)]
@@ -342,10 +377,11 @@ def measure(name, cfg, dev, k3, steps, warmup, rotate, eager):
     traffic = stored_traffic(dom, name, ksrc)
 
     act_steps = [n_active[(warmup + i) % rotate] for i in range(steps)]
-    weight_bytes = float(np.mean(act_steps)) * (2 * cfg.I * (cfg.D // 32) * 17 + cfg.D * (cfg.I // 32) * 17)
+    expert_bytes = 2 * cfg.I * (cfg.D // 32) * 17 + cfg.D * (cfg.I // 32) * 17
+    weight_bytes = float(np.mean(act_steps)) * expert_bytes
     step_s = elapsed / steps
     dtype, arith = arithmetic(path)
-    return {
+    res = {
         "value": cfg.T * steps / elapsed,
         "steps": steps,
         "ms_per_step": step_s * 1e3,
@@ -373,10 +409,12 @@ def measure(name, cfg, dev, k3, steps, warmup, rotate, eager):
             "algorithmic_flops_per_launch": flops,
             "algorithmic_bytes_per_launch": byts,
             "avg_launch_ms": dom_ms,
+            "avg_launch_ms_raw_events": dom_raw_ms,
+            "event_pair_overhead_ms": pair_ms,
             "launches_timed": n_ev,
         },
         "timing": ("graph replay of the step (route + FFN), one captured graph per rotated batch"
-                   if graphs else "eager launches"),
+                   if graphs else "eager launches") + (", every FFN launch on one stream" if serial else ""),
         "eager_ms_per_step": eager_ms,
         "step_weight_GBps": weight_bytes / step_s / 1e9,
         "step_hbm_frac": weight_bytes / step_s / (PEAK_HBM_GBS * 1e9),
@@ -384,6 +422,19 @@ def measure(name, cfg, dev, k3, steps, warmup, rotate, eager):
         "launches_ms": {s: v for s, v in launch_ms.items() if s in have},
         "_batch0": batches[0][0],
     }
+    if cold_ms:
+        med = float(np.median(cold_ms))
+        cold_act = float(np.mean([n_active[(warmup + i) % rotate] for i in range(len(cold_ms))]))
+        res["cold"] = {
+            "protocol": "1 GiB read between steps (caches evicted), each step timed alone by HIP events",
+            "steps": len(cold_ms),
+            "median_ms_per_step": med,
+            "tokens_per_s": cfg.T / (med * 1e-3),
+            "step_weight_GBps": cold_act * expert_bytes / (med * 1e-3) / 1e9,
+            "step_hbm_frac": cold_act * expert_bytes / (med * 1e-3) / (PEAK_HBM_GBS * 1e9),
+            "step_mfma_frac": cfg.T * 2 * cfg.k * 3 * cfg.D * cfg.I / (med * 1e-3) / (PEAK_BF16_TFLOPS * 1e12),
+        }
+    return res
 
 
 def main():
@@ -420,7 +471,8 @@ def main():
     def rot(c):
         return args.rotate or (8 if c.T <= 8 else 4)
 
-    head = measure(args.workload, cfg, dev, k3, args.steps, args.warmup, rot(cfg), args.eager)
+    head = measure(args.workload, cfg, dev, k3, args.steps, args.warmup, rot(cfg), args.eager, args.cold_steps,
+                   args.serial_launches)
     batch0 = head.pop("_batch0")
     result = {
         "metric": METRIC,
@@ -442,7 +494,7 @@ def main():
         extra = {}
         for w in EXTRA_WORKLOADS:
             c = moe_inputs.CONFIGS[w]
-            r = measure(w, c, dev, k3, 0, args.warmup, rot(c), args.eager)
+            r = measure(w, c, dev, k3, 0, args.warmup, rot(c), args.eager, args.cold_steps, args.serial_launches)
             r.pop("_batch0")
             r["tokens_per_s"] = r.pop("value")
             extra[w] = r
