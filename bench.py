@@ -437,6 +437,83 @@ def measure(name, cfg, dev, k3, steps, warmup, rotate, eager, cold_steps=0, seri
     return res
 
 
+def measure_verify_width(dev, k3, warmup, reps=100):
+    """The verify cost hint on the verify workload's seed-0 batch: distinct
+    experts by verify width (moe_verify_width_distinct), the FFN step time
+    of every truncated width (positions < w of each of the 16 sequences,
+    graph replay), a least-squares fit time = fixed + distinct * expert_bytes
+    / bytes_per_s, and the width moe_verify_width_choose picks at an
+    acceptance of 0.8 per proposal (the pages report 4 of 5 verified rows
+    accepted) for experts in HBM and for experts streamed over the host link."""
+    import numpy as np
+    import torch
+
+    import moe_inputs
+    from moe_inputs.device import upload_batch
+
+    cfg = moe_inputs.VERIFY
+    S, W = 16, 8
+    _, x, z, b = upload_batch(cfg, seed=0)
+    ids, wts = k3.moe_route_topk(z, b, cfg.k)
+    distinct = k3.moe_verify_width_distinct(ids, S, W, cfg.E)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for _ in range(reps):
+        k3.moe_verify_width_distinct(ids, S, W, cfg.E, out=distinct)
+    ev1.record()
+    torch.cuda.synchronize()
+    kernel_ms = ev0.elapsed_time(ev1) / reps
+    d = distinct.cpu().numpy().astype(np.int64)
+    expert_bytes = 2 * cfg.I * (cfg.D // 32) * 17 + cfg.D * (cfg.I // 32) * 17
+    ffn_ms = []
+    for w in range(1, W + 1):
+        rows = torch.tensor([s_ * W + p for s_ in range(S) for p in range(w)], dtype=torch.long, device="cuda")
+        xw, iw, ww = x[rows].contiguous(), ids[rows].contiguous(), wts[rows].contiguous()
+        T = S * w
+        out = torch.empty((T, cfg.D), dtype=torch.float32, device="cuda")
+        ws = torch.empty(max(1, k3.moe_mxfp4_ffn_workspace_size(T, cfg.D, cfg.I, cfg.E, cfg.k)), dtype=torch.uint8,
+                         device="cuda")
+        for _ in range(warmup):
+            k3.moe_mxfp4_ffn(xw, iw, ww, dev.w1, dev.w3, dev.w2, out=out, workspace=ws)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            k3.moe_mxfp4_ffn(xw, iw, ww, dev.w1, dev.w3, dev.w2, out=out, workspace=ws)
+        g.replay()
+        torch.cuda.synchronize()
+        ev0.record()
+        for _ in range(reps):
+            g.replay()
+        ev1.record()
+        torch.cuda.synchronize()
+        ffn_ms.append(ev0.elapsed_time(ev1) / reps)
+    A = np.stack([np.ones(W), d.astype(np.float64)], axis=1)
+    (fixed_ms, ms_per_expert), *_ = np.linalg.lstsq(A, np.array(ffn_ms), rcond=None)
+    if fixed_ms < 0:  # no fixed part: a line through the origin
+        fixed_ms = 0.0
+        ms_per_expert = float(np.dot(d, ffn_ms) / np.dot(d, d))
+    model_ms = (A @ np.array([fixed_ms, ms_per_expert])).tolist()
+    bytes_per_s = expert_bytes / (ms_per_expert * 1e-3)
+    accept = [0.8] * (W - 1)
+    best_hbm, rates_hbm = k3.moe_verify_width_choose(d.tolist(), S, accept, expert_bytes, bytes_per_s, fixed_ms * 1e-3)
+    host_link = 64e9  # PCIe 5.0 x16, one direction
+    best_host, rates_host = k3.moe_verify_width_choose(d.tolist(), S, accept, expert_bytes, host_link, fixed_ms * 1e-3)
+    return {
+        "sequences": S,
+        "width": W,
+        "distinct_experts_by_width": d.tolist(),
+        "distinct_kernel_ms": kernel_ms,
+        "ffn_ms_by_width": ffn_ms,
+        "fit": {"fixed_ms": float(fixed_ms), "bytes_per_s": float(bytes_per_s), "model_ms_by_width": model_ms,
+                "max_rel_error": float(np.max(np.abs(np.array(model_ms) - np.array(ffn_ms)) / np.array(ffn_ms)))},
+        "accept_per_proposal": 0.8,
+        "best_width_hbm": best_hbm,
+        "committed_tokens_per_s_hbm": rates_hbm,
+        "best_width_host_link_64GBps": best_host,
+        "committed_tokens_per_s_host_link": rates_host,
+    }
+
+
 def main():
     args = parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -499,6 +576,7 @@ def main():
             r["tokens_per_s"] = r.pop("value")
             extra[w] = r
         result["workloads"] = extra
+        result["verify_width"] = measure_verify_width(dev, k3, args.warmup)
     if args.cpu_baseline:
         sample = args.cpu_sample_tokens or (cfg.T if cfg.T <= 64 else 2)
         result["cpu_baseline"] = cpu_baseline(cfg, batch0, sample)

@@ -273,6 +273,66 @@ size_t moe_group_workspace_size(int64_t T, int32_t E, int32_t k);
 int moe_group_by_expert(const int32_t* topk_ids, int64_t T, int32_t E, int32_t k, int32_t* counts, int32_t* offsets,
                         int32_t* row_tok, int32_t* slot_row, void* workspace, size_t workspace_bytes, void* stream);
 
+/* Largest verify width (rows per sequence) of the verify-width calls. */
+#define K3MOE_MAX_VERIFY_WIDTH 64
+
+/*
+ * moe_verify_width_distinct — distinct routed experts of a speculative verify
+ * batch, for every verify width at once.
+ * Source: lucebox pull request "feat(kimi-k3): add DSpark Q8 artifact and
+ * shared speculative runtime": Summary (target cost hints so that
+ * external-memory targets avoid over-verification), "Kimi-K3 DSpark workload
+ * probe" (expert traffic scales with every verified row) and "DSpark
+ * acceptance-contract correction" (verification is the current token plus 7
+ * proposals: width 8).
+ *
+ *   topk_ids  i32 [S * W, k]  routed experts of the batch's rows; row
+ *                             r = s * W + w is position w (0 = the current
+ *                             token, 1.. = the proposals) of sequence s
+ *   distinct  i32 [W]         out: distinct[w] = number of distinct ids in
+ *                             [0, E) routed by the rows of position <= w of
+ *                             all S sequences
+ *
+ * A verify pass of width w (positions 0 .. w-1 of every sequence) streams
+ * distinct[w-1] experts' weights once through the FFN. Ids outside [0, E) and
+ * repeats add nothing. Integer result, independent of thread timing.
+ * Sizes: S >= 0 (S == 0 writes zeros), 1 <= W <= K3MOE_MAX_VERIFY_WIDTH,
+ * 1 <= E <= K3MOE_MAX_EXPERTS_FFN, 1 <= k <= K3MOE_MAX_TOPK, S * W * k < 2^31.
+ */
+int moe_verify_width_distinct(const int32_t* topk_ids, int32_t S, int32_t W, int32_t E, int32_t k, int32_t* distinct,
+                              void* stream);
+
+/*
+ * moe_verify_width_choose — the verify width a cost hint picks (HOST call:
+ * every pointer is host memory; nothing is enqueued).
+ * Source: as moe_verify_width_distinct (cost hints; adaptive verification
+ * reduced the streamed expert payload from 73.4 to 47.4 GiB).
+ *
+ *   distinct      i32 [W]      distinct experts by width (host copy of
+ *                              moe_verify_width_distinct's output)
+ *   accept        f64 [W - 1]  accept[j-1] = probability that proposal j is
+ *                              accepted given that the ones before it were, or
+ *                              NULL for all ones
+ *   expert_bytes  bytes of one expert's weights (17,547,264 at K3 shape)
+ *   bytes_per_s   rate at which those bytes reach the GPU (HBM, or the host
+ *                 link for streamed experts)
+ *   fixed_s       time of a pass that moves no expert bytes
+ *   best_w        out: the width in 1 .. W with the highest rate (the
+ *                 smallest one among equal rates)
+ *   rates         out (optional, NULL to skip) f64 [W]: expected committed
+ *                 tokens per second of every width
+ *
+ * A pass of width w commits, per sequence, the target's next token plus the
+ * accepted prefix of its w - 1 proposals, 1 + sum_{i<w} prod_{j<=i} accept[j-1]
+ * tokens in expectation, and takes fixed_s + distinct[w-1] * expert_bytes /
+ * bytes_per_s seconds; rate = S * committed / time.
+ * K3MOE_ERR_SHAPE for W outside 1 .. K3MOE_MAX_VERIFY_WIDTH, S < 1,
+ * bytes_per_s <= 0, expert_bytes or fixed_s < 0; K3MOE_ERR_NULL for a missing
+ * required pointer.
+ */
+int moe_verify_width_choose(const int32_t* distinct, int32_t W, int32_t S, const double* accept, double expert_bytes,
+                            double bytes_per_s, double fixed_s, int32_t* best_w, double* rates);
+
 #ifdef __cplusplus
 }
 #endif

@@ -26,6 +26,8 @@ __all__ = [
     "moe_mxfp4_ffn",
     "moe_mxfp4_ffn_noalloc",
     "NOALLOC_SCRATCH_BYTES",
+    "moe_verify_width_distinct",
+    "moe_verify_width_choose",
     "moe_group_workspace_size",
     "moe_group_by_expert",
     "FFN_STAGES",
@@ -68,6 +70,12 @@ lib.moe_group_workspace_size.restype = _sz
 lib.moe_group_workspace_size.argtypes = [_i64, _i32, _i32]
 lib.moe_group_by_expert.restype = ctypes.c_int
 lib.moe_group_by_expert.argtypes = [_vp, _i64, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _sz, _vp]
+lib.moe_verify_width_distinct.restype = ctypes.c_int
+lib.moe_verify_width_distinct.argtypes = [_vp, _i32, _i32, _i32, _i32, _vp, _vp]
+lib.moe_verify_width_choose.restype = ctypes.c_int
+lib.moe_verify_width_choose.argtypes = [ctypes.POINTER(ctypes.c_int32), _i32, _i32, ctypes.POINTER(ctypes.c_double),
+                                        ctypes.c_double, ctypes.c_double, ctypes.c_double,
+                                        ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_double)]
 FFN_STAGE_EVENTS = 7
 # launches between consecutive events of moe_mxfp4_ffn_profiled
 FFN_STAGES = ("group", "gate_up", "gate_up_stream", "down", "down_stream", "combine")
@@ -262,3 +270,34 @@ def moe_group_by_expert(ids: torch.Tensor, E: int, workspace: torch.Tensor | Non
                                                           _ptr(row_tok), _ptr(slot_row), _ptr(workspace),
                                                           workspace.numel(), _stream(dev)))
     return counts, offsets, row_tok, slot_row
+
+
+def moe_verify_width_distinct(ids: torch.Tensor, S: int, W: int, E: int, out: torch.Tensor | None = None) -> torch.Tensor:
+    """Distinct experts routed by positions <= w of S sequences of W rows.
+    ids int32 [S * W, k] (row r = s * W + w). Returns int32 [W]."""
+    _dev(ids, "ids", torch.int32)
+    if ids.dim() != 2 or ids.shape[0] != S * W:
+        raise ValueError("ids must be [S * W, k]")
+    k = ids.shape[1]
+    if out is None:
+        out = torch.empty(W, dtype=torch.int32, device=ids.device)
+    _dev(out, "out", torch.int32)
+    if out.numel() != W:
+        raise ValueError("out must hold W counts")
+    _check("moe_verify_width_distinct", lib.moe_verify_width_distinct(_ptr(ids), S, W, E, k, _ptr(out),
+                                                                      _stream(ids.device)))
+    return out
+
+
+def moe_verify_width_choose(distinct, S: int, accept=None, expert_bytes: float = 0.0, bytes_per_s: float = 1.0,
+                            fixed_s: float = 0.0):
+    """Host call: (best width, [W] expected committed tokens per second).
+    distinct: W counts (any int sequence); accept: W - 1 probabilities or None."""
+    W = len(distinct)
+    d = (ctypes.c_int32 * W)(*[int(v) for v in distinct])
+    a = None if accept is None else (ctypes.c_double * max(W - 1, 1))(*[float(v) for v in accept])
+    best = ctypes.c_int32(0)
+    rates = (ctypes.c_double * W)()
+    _check("moe_verify_width_choose", lib.moe_verify_width_choose(d, W, S, a, float(expert_bytes), float(bytes_per_s),
+                                                                  float(fixed_s), ctypes.byref(best), rates))
+    return int(best.value), [float(r) for r in rates]

@@ -480,6 +480,43 @@ int moe_mxfp4_ffn_noalloc(const void* x_bf16, const int32_t* topk_ids, const flo
                  static_cast<hipStream_t>(stream), nullptr, false);
 }
 
+int moe_verify_width_distinct(const int32_t* topk_ids, int32_t S, int32_t W, int32_t E, int32_t k, int32_t* distinct,
+                              void* stream) {
+  if (S < 0 || W < 1 || W > K3MOE_MAX_VERIFY_WIDTH || E < 1 || E > K3MOE_MAX_EXPERTS_FFN || k < 1 ||
+      k > K3MOE_MAX_TOPK)
+    return K3MOE_ERR_SHAPE;
+  if ((int64_t)S * W * k > 0x7FFFFFFF) return K3MOE_ERR_SHAPE;
+  if (!distinct) return K3MOE_ERR_NULL;
+  if (S > 0 && !topk_ids) return K3MOE_ERR_NULL;
+  if (misaligned(topk_ids) || misaligned(distinct)) return K3MOE_ERR_ALIGN;
+  return device_status(launch_verify_distinct(topk_ids, S, W, E, k, distinct, static_cast<hipStream_t>(stream)));
+}
+
+int moe_verify_width_choose(const int32_t* distinct, int32_t W, int32_t S, const double* accept, double expert_bytes,
+                            double bytes_per_s, double fixed_s, int32_t* best_w, double* rates) {
+  if (W < 1 || W > K3MOE_MAX_VERIFY_WIDTH || S < 1) return K3MOE_ERR_SHAPE;
+  if (!distinct || !best_w) return K3MOE_ERR_NULL;
+  if (!(expert_bytes >= 0.0) || !(bytes_per_s > 0.0) || !(fixed_s >= 0.0)) return K3MOE_ERR_SHAPE;
+  int best = 1;
+  double best_rate = -1.0;
+  double committed = 1.0, run = 1.0;  // expected tokens one sequence commits at width w
+  for (int w = 1; w <= W; ++w) {
+    if (w > 1) {
+      run *= accept ? accept[w - 2] : 1.0;
+      committed += run;
+    }
+    const double t = fixed_s + (double)distinct[w - 1] * expert_bytes / bytes_per_s;
+    const double rate = (double)S * committed / t;
+    if (rates) rates[w - 1] = rate;
+    if (rate > best_rate) {  // strictly higher: ties keep the smaller width
+      best_rate = rate;
+      best = w;
+    }
+  }
+  *best_w = best;
+  return K3MOE_OK;
+}
+
 static int group_shape_status(int64_t T, int32_t E, int32_t k) {
   if (T < 0 || E < 1 || E > K3MOE_MAX_EXPERTS_FFN || k < 1 || k > K3MOE_MAX_TOPK) return K3MOE_ERR_SHAPE;
   if (T * (int64_t)k > 0x7FFFFFFF) return K3MOE_ERR_SHAPE;

@@ -142,6 +142,11 @@ hipError_t launch_combine(const float* y, const int8_t* y_scale, bool mixed, con
                           int64_t T, int D, int k,
                           float* out, hipStream_t s);
 
+// Verify batches: distinct[w] = distinct experts routed by the rows of
+// position <= w of S sequences of W rows (W <= kMaxVerifyWidth, E <= 8192).
+constexpr int kMaxVerifyWidth = 64;
+hipError_t launch_verify_distinct(const int32_t* ids, int S, int W, int E, int k, int32_t* distinct, hipStream_t s);
+
 // Token-tile height the FFN uses for a batch of T tokens with k routed experts.
 int choose_rows_per_tile(int64_t T, int k, int E);
 

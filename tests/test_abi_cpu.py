@@ -25,7 +25,8 @@ def test_library_exports_every_declared_symbol(k3):
     names = declared_functions()
     assert set(names) == {"k3moe_status_str", "moe_route_topk", "mxfp4_repack", "mxfp4_dequant",
                           "moe_mxfp4_ffn_workspace_size", "moe_mxfp4_ffn", "moe_mxfp4_ffn_profiled",
-                          "moe_mxfp4_ffn_noalloc", "moe_group_workspace_size", "moe_group_by_expert"}
+                          "moe_mxfp4_ffn_noalloc", "moe_group_workspace_size", "moe_group_by_expert",
+                          "moe_verify_width_distinct", "moe_verify_width_choose"}
     for n in names:
         assert hasattr(k3.lib, n), n
 
@@ -175,3 +176,37 @@ def test_group_checks(k3):
     assert gw(0, 896, 16) == 0 and gw(4, 0, 16) == 0
     # chunk tables: one 64-bit token bitmap and one base per (64-token chunk, expert)
     assert gw(4096, 896, 16) >= 64 * 896 * 12
+
+
+def test_verify_width_checks(k3):
+    f = k3.lib.moe_verify_width_distinct
+    assert f(A, 16, 0, 896, 16, A, None) == ERR_SHAPE  # W < 1
+    assert f(A, 16, 65, 896, 16, A, None) == ERR_SHAPE  # W > 64
+    assert f(A, -1, 8, 896, 16, A, None) == ERR_SHAPE
+    assert f(A, 16, 8, 0, 16, A, None) == ERR_SHAPE
+    assert f(A, 16, 8, 8193, 16, A, None) == ERR_SHAPE
+    assert f(A, 16, 8, 896, 65, A, None) == ERR_SHAPE
+    assert f(None, 16, 8, 896, 16, A, None) == ERR_NULL
+    assert f(A, 16, 8, 896, 16, None, None) == ERR_NULL
+    assert f(A + 4, 16, 8, 896, 16, A, None) == ERR_ALIGN
+
+
+def test_verify_width_choose_matches_oracle(k3):
+    # a host call: the library's choice and rates against the oracle's
+    import numpy as np
+
+    from oracle.verify import verify_width_choose_ref
+
+    g = np.random.default_rng(21)
+    for W in (1, 2, 8, 64):
+        distinct = np.cumsum(g.integers(0, 40, size=W)) + 16
+        accept = g.random(W - 1)
+        for fixed in (0.0, 2e-4, 5e-3):
+            best, rates = k3.moe_verify_width_choose(distinct.tolist(), 16, accept.tolist(), 17_547_264.0, 6.3e12, fixed)
+            rbest, rrates = verify_width_choose_ref(distinct, 16, accept, 17_547_264.0, 6.3e12, fixed)
+            assert best == rbest
+            assert np.allclose(rates, rrates, rtol=1e-12, atol=0)
+    best, _ = k3.moe_verify_width_choose([16, 16, 16], 4, None, 1e6, 1e9, 0.0)
+    assert best == 3
+    with pytest.raises(k3.K3MoeError):
+        k3.moe_verify_width_choose([16, 20], 4, None, 1e6, 0.0, 0.0)  # no bandwidth
