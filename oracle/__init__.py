@@ -17,13 +17,15 @@ Modules
 ``permute`` stable grouping of (token, slot) entries by expert
 ``ffn``     the routed-expert FFN: route -> per-expert SiLU-gated MLP -> weighted sum
 ``verify``  expert bytes of a speculative verify batch by width, and the width a cost hint picks
+``cache``   a least-recently-used device expert cache in front of an external expert store
 
 Parity status
 -------------
 Every function here is pinned by ``tests/test_oracle_*.py`` against something
 other than itself (values printed on the pages, IEEE-754 closed forms, a
 library decode of E8M0, a textbook sort, brute-force loops, an identity-weight
-closed form, a hand-worked verify-width choice).  The FFN's numerics beyond those closed forms have no worked
+closed form, a hand-worked verify-width choice, a hand-worked cache sequence
+and an independent last-use LRU simulation).  The FFN's numerics beyond those closed forms have no worked
 example on the pages; ``ffn_ref`` is pinned by a pure-Python loop evaluation
 and the identity case only.
 """
@@ -41,3 +43,4 @@ from .route import route_ref  # noqa: F401
 from .permute import permute_ref, valid_entries  # noqa: F401
 from .ffn import ffn_ref, silu_mul  # noqa: F401
 from .verify import expected_committed, verify_distinct_ref, verify_width_choose_ref  # noqa: F401
+from .cache import ExpertCacheRef  # noqa: F401
