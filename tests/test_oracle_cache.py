@@ -37,35 +37,34 @@ def test_hand_worked_sequence():
 
 
 class LastUseLRU:
-    """Independent simulation: per slot the step of its last use (-1: never),
-    victims = non-hit slots by (last use, position in the previous order)."""
+    """Independent simulation: every slot carries a recency key compared as a
+    tuple, no ordered list.  Never used: (-1, slot index); hit at step t:
+    (t, 0, its previous key); filled at step t: (t, 1, miss index).  Victims
+    are the non-hit slots with the smallest keys."""
 
     def __init__(self, E, C):
         self.E, self.C = E, C
         self.exp = [-1] * C
-        self.last = [-1] * C
-        self.rank = list(range(C))  # position of each slot in the recency list
+        self.key = [(-1, s) for s in range(C)]
         self.t = 0
 
     def route(self, ids):
         self.t += 1
         used = sorted({int(e) for e in np.asarray(ids).reshape(-1) if 0 <= e < self.E})
         where = {e: s for s, e in enumerate(self.exp) if e >= 0}
-        hits = [where[e] for e in used if e in where]
+        hits = {where[e] for e in used if e in where}
         misses = [e for e in used if e not in where]
-        cand = sorted((s for s in range(self.C) if s not in hits), key=lambda s: self.rank[s])
+        cand = sorted((s for s in range(self.C) if s not in hits), key=lambda s: self.key[s])
         fetch = list(zip(misses, cand[: len(misses)]))
-        for e, s in fetch:
+        for s in hits:
+            self.key[s] = (self.t, 0, self.key[s])
+        for i, (e, s) in enumerate(fetch):
             self.exp[s] = e
-        # recency list: untouched, then hits by previous rank, then fills in miss order
-        untouched = cand[len(misses):]
-        hits_sorted = sorted(hits, key=lambda s: self.rank[s])
-        new = untouched + hits_sorted + [s for _, s in fetch]
-        for i, s in enumerate(new):
-            self.rank[s] = i
-        for s in hits + [s for _, s in fetch]:
-            self.last[s] = self.t
+            self.key[s] = (self.t, 1, i)
         return fetch
+
+    def order(self):
+        return sorted(range(self.C), key=lambda s: self.key[s])
 
 
 @pytest.mark.parametrize("E,C,T,k", [(896, 160, 8, 16), (40, 12, 3, 4), (6, 6, 2, 3), (1000, 600, 1, 16)])
@@ -79,6 +78,7 @@ def test_matches_independent_lru(E, C, T, k):
         slot_ids, fetch, h, m = a.route(ids)
         assert fetch == b.route(ids)
         assert a.expert_in == b.exp
+        assert a.order == b.order()
         # invariants: the two tables agree, every used expert is cached, the
         # renamed entries name the slots holding their experts
         for s, e in enumerate(a.expert_in):
