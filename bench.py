@@ -14,7 +14,10 @@ several seeded routing inputs so successive steps touch different experts.
 The headline workload (default: prefill, 4096 tokens) gives the JSON line's
 `value`.  With the default workload the same process also measures the 8- and
 1-token decode batches and the 128-token verify batch on the same resident
-experts and reports them under "workloads" (--no-extra skips them).
+experts and reports them under "workloads", the verify cost hint under
+"verify_width", and 8-token decode with the experts streamed from an external
+store (pinned host memory) through an 8 GiB device expert cache under
+"expert_cache" (--no-extra skips all of these).
 
 Without --steps, K is chosen so the timed steps take about half a second.
 
@@ -514,6 +517,91 @@ def measure_verify_width(dev, k3, warmup, reps=100):
     }
 
 
+HOST_LINK_PEAK_GBS = 63.0  # PCIe 5.0 x16, one direction: 32 GT/s x 16 lanes x 128/130 / 8
+
+
+def measure_expert_cache(dev, k3, warmup, steps=40, cache_gib=8.0):
+    """Decode batches of 8 tokens with the experts in an external store behind
+    a device expert cache of cache_gib GiB (the lucebox runtime's 8 GiB): each
+    step routes the batch, stages its missing experts into the cache
+    (moe_expert_cache_route: plan + fetch, GPU loads from the store) and runs
+    the FFN on the cache's slots.  The store is pinned host memory (the fetch
+    crosses the host link) or the resident HBM copy (an HBM-to-HBM copy).
+    Consecutive steps draw fresh seeded batches; the first `warmup + 24`
+    steps fill the cache and are not timed."""
+    import numpy as np
+    import torch
+
+    import moe_inputs
+    from moe_inputs.device import upload_batch
+
+    base = moe_inputs.DECODE8
+    E = base.E
+    expert_bytes = 2 * base.I * (base.D // 32) * 17 + base.D * (base.I // 32) * 17
+    C = int(cache_gib * (1 << 30) // expert_bytes)
+    cache = (torch.empty((C, base.I, base.D // 32, 17), dtype=torch.uint8, device="cuda"),
+             torch.empty((C, base.I, base.D // 32, 17), dtype=torch.uint8, device="cuda"),
+             torch.empty((C, base.D, base.I // 32, 17), dtype=torch.uint8, device="cuda"))
+    t0 = time.perf_counter()
+    host = []
+    for t in (dev.w1, dev.w3, dev.w2):
+        h = torch.empty(t.shape, dtype=torch.uint8, pin_memory=True)
+        h.copy_(t)
+        host.append(h)
+    pin_s = time.perf_counter() - t0
+    fill = warmup + 24
+    out = {"slots": C, "cache_GiB": C * expert_bytes / (1 << 30), "expert_bytes": expert_bytes,
+           "host_link_peak_GBps": HOST_LINK_PEAK_GBS, "pin_store_s": pin_s}
+    cases = (("uniform", base, host, "pinned host"), ("zipf", base.with_(logits="zipf"), host, "pinned host"),
+             ("uniform-hbm-store", base, [dev.w1, dev.w3, dev.w2], "HBM"))
+    for name, cfg, store, where in cases:
+        batches = [upload_batch(cfg, seed=5000 + i) for i in range(fill + steps)]
+        state = k3.moe_expert_cache_init(E, C)
+        slot_ids = torch.empty((cfg.T, cfg.k), dtype=torch.int32, device="cuda")
+        y = torch.empty((cfg.T, cfg.D), dtype=torch.float32, device="cuda")
+        ws = torch.empty(k3.moe_mxfp4_ffn_workspace_size(cfg.T, cfg.D, cfg.I, C, cfg.k), dtype=torch.uint8,
+                         device="cuda")
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+        misses, hits = [], []
+        for i, (_, x, z, b) in enumerate(batches):
+            e = evs[i - fill] if i >= fill else None
+            if e:
+                e[0].record()
+            ids, w = k3.moe_route_topk(z, b, cfg.k)
+            if e:
+                e[1].record()
+            k3.moe_expert_cache_route(state, E, C, ids, *store, *cache, slot_ids=slot_ids)
+            if e:
+                e[2].record()
+            k3.moe_mxfp4_ffn(x, slot_ids, w, *cache, out=y, workspace=ws)
+            if e:
+                e[3].record()
+                torch.cuda.synchronize()
+                hdr = k3.moe_expert_cache_header(state)
+                misses.append(hdr["misses"])
+                hits.append(hdr["hits"])
+        torch.cuda.synchronize()
+        step_ms = np.array([e[0].elapsed_time(e[3]) for e in evs])
+        stage_ms = np.array([e[1].elapsed_time(e[2]) for e in evs])
+        ffn_ms = np.array([e[2].elapsed_time(e[3]) for e in evs])
+        moved = float(np.sum(misses)) * expert_bytes
+        r = {"store": where, "steps": steps, "ms_per_step": float(step_ms.mean()),
+             "tokens_per_s": cfg.T * steps / (step_ms.sum() * 1e-3),
+             "hit_rate": float(np.sum(hits) / max(1, np.sum(hits) + np.sum(misses))),
+             "distinct_experts_per_step": float(np.mean(np.add(hits, misses))),
+             "misses_per_step": float(np.mean(misses)), "stage_ms_per_step": float(stage_ms.mean()),
+             "ffn_ms_per_step": float(ffn_ms.mean()),
+             "staged_GBps": moved / (stage_ms.sum() * 1e-3) / 1e9}
+        if where == "HBM":
+            # read and write once per staged byte
+            r["hbm_GBps"] = 2 * r["staged_GBps"]
+            r["frac_of_hbm_peak"] = r["hbm_GBps"] / PEAK_HBM_GBS
+        else:
+            r["frac_of_host_link_peak"] = r["staged_GBps"] / HOST_LINK_PEAK_GBS
+        out[name] = r
+    return out
+
+
 def main():
     args = parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -577,6 +665,7 @@ def main():
             extra[w] = r
         result["workloads"] = extra
         result["verify_width"] = measure_verify_width(dev, k3, args.warmup)
+        result["expert_cache"] = measure_expert_cache(dev, k3, args.warmup)
     if args.cpu_baseline:
         sample = args.cpu_sample_tokens or (cfg.T if cfg.T <= 64 else 2)
         result["cpu_baseline"] = cpu_baseline(cfg, batch0, sample)

@@ -333,6 +333,87 @@ int moe_verify_width_distinct(const int32_t* topk_ids, int32_t S, int32_t W, int
 int moe_verify_width_choose(const int32_t* distinct, int32_t W, int32_t S, const double* accept, double expert_bytes,
                             double bytes_per_s, double fixed_s, int32_t* best_w, double* rates);
 
+/*
+ * Device expert cache — routed experts kept in an external store (any memory
+ * the GPU can read: pinned, mapped host memory, or device memory) and staged
+ * on demand into C expert slots in HBM.
+ * Sources: Hugging Face card "K3-Stuff", llama-cpp-patches item 2 (experts
+ * paged in on demand; the page cache is the hot-expert cache, with LRU
+ * eviction); lucebox pull request "feat(kimi-k3): add DSpark Q8 artifact and
+ * shared speculative runtime", "Runtime validation" (SSD-routed experts
+ * behind an 8 GiB device expert cache).
+ *
+ * Policy (least recently used): a batch uses the distinct ids in [0, E) of
+ * its entries; used experts already in a slot are hits; the i-th miss (in
+ * increasing expert order) takes the i-th slot, in least-recently-used order,
+ * that no hit holds (empty slots come first), evicting what it held; the slots
+ * the batch did not touch keep their order, then come the hit slots (old
+ * order), then the filled slots (miss order). At init every slot is empty,
+ * listed 0 .. C-1.
+ *
+ * The state is a caller-allocated device buffer of
+ * moe_expert_cache_state_size(E, C) bytes: this header, then i32 slot_of[E]
+ * (slot of each expert, -1: not cached), i32 expert_in[C] (expert in each
+ * slot, -1: empty), i32 order[C] (slots from least to most recently used) and
+ * i32 fetch[2 * C] (the last batch's (expert, slot) pairs, n_fetch of them),
+ * each starting on a 256-byte boundary.  The caller may copy it to the host
+ * to read the counters or the tables; only init and route write it.
+ */
+typedef struct {
+  uint32_t step;          /* batches routed since init */
+  uint32_t n_fetch;       /* experts the last batch fetched (its misses) */
+  uint32_t hits;          /* used experts of the last batch found cached */
+  uint32_t misses;        /* = n_fetch */
+  uint64_t hits_total;    /* since init */
+  uint64_t misses_total;  /* since init */
+  int32_t E, C;           /* sizes given at init */
+  uint32_t tag;           /* K3MOE_EXPERT_CACHE_TAG once initialised */
+  uint32_t reserved;
+} k3moe_expert_cache_header;
+#define K3MOE_EXPERT_CACHE_TAG 0x4B334543u
+
+/* Bytes of cache state for E experts and C slots (0 if out of range:
+   1 <= E, C <= K3MOE_MAX_EXPERTS_FFN). Pure host computation. */
+size_t moe_expert_cache_state_size(int32_t E, int32_t C);
+
+/* Empty cache: every slot empty, LRU order 0 .. C-1, counters zero.
+   K3MOE_ERR_SHAPE / _NULL / _ALIGN / _WORKSPACE (state too small). */
+int moe_expert_cache_init(void* state, size_t state_bytes, int32_t E, int32_t C, void* stream);
+
+/*
+ * moe_expert_cache_route — stage a routed batch's experts into the cache.
+ *
+ *   state      the cache state (same E and C as at init)
+ *   topk_ids   i32 [T, k]   routed experts of the batch
+ *   slot_ids   i32 [T, k]   out: the slot of each entry's expert (entries whose
+ *                           id is outside [0, E) get -1); pass it with
+ *                           cache_w1/w3/w2 and E = C to moe_mxfp4_ffn, which
+ *                           then computes exactly what it computes on the
+ *                           store's experts with topk_ids
+ *   store_w1, store_w3 u8 [E, I, D/32, 17], store_w2 u8 [E, D, I/32, 17]
+ *                           all experts (pinned host memory, or device memory)
+ *   cache_w1, cache_w3 u8 [C, I, D/32, 17], cache_w2 u8 [C, D, I/32, 17]
+ *                           device: the slots
+ *
+ * Two launches on `stream`: a one-workgroup plan (the policy above; it
+ * writes slot_ids, the fetch list and the header) and a copy of every missed
+ * expert's three matrices from the store into its slot (GPU loads from the
+ * store: over the host link for host memory). Nothing waits for the host.
+ * A state whose header does not carry the tag, E and C of an init with these
+ * sizes is left untouched: every slot_ids entry becomes -1 and nothing is
+ * fetched (so the FFN then contributes nothing).
+ * The store pointers must be device memory or pinned host memory the GPU can
+ * map (checked with hipPointerGetAttributes: K3MOE_ERR_UNSUPPORTED for memory
+ * the GPU cannot read, such as pageable host memory).
+ * Sizes: T >= 0 (T == 0 is a no-op), 1 <= k <= K3MOE_MAX_TOPK, D and I as for
+ * moe_mxfp4_ffn, C >= min(E, T * k) (any batch fits), 1 <= E, C <=
+ * K3MOE_MAX_EXPERTS_FFN; K3MOE_ERR_SHAPE otherwise.
+ */
+int moe_expert_cache_route(void* state, size_t state_bytes, int32_t E, int32_t C, const int32_t* topk_ids, int64_t T,
+                           int32_t k, int32_t* slot_ids, const uint8_t* store_w1, const uint8_t* store_w3,
+                           const uint8_t* store_w2, uint8_t* cache_w1, uint8_t* cache_w3, uint8_t* cache_w2, int32_t D,
+                           int32_t I, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -12,6 +12,7 @@ from __future__ import annotations
 
 import ctypes
 import os
+import struct
 
 import torch
 
@@ -28,6 +29,10 @@ __all__ = [
     "NOALLOC_SCRATCH_BYTES",
     "moe_verify_width_distinct",
     "moe_verify_width_choose",
+    "moe_expert_cache_state_size",
+    "moe_expert_cache_init",
+    "moe_expert_cache_route",
+    "moe_expert_cache_header",
     "moe_group_workspace_size",
     "moe_group_by_expert",
     "FFN_STAGES",
@@ -76,6 +81,14 @@ lib.moe_verify_width_choose.restype = ctypes.c_int
 lib.moe_verify_width_choose.argtypes = [ctypes.POINTER(ctypes.c_int32), _i32, _i32, ctypes.POINTER(ctypes.c_double),
                                         ctypes.c_double, ctypes.c_double, ctypes.c_double,
                                         ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_double)]
+lib.moe_expert_cache_state_size.restype = _sz
+lib.moe_expert_cache_state_size.argtypes = [_i32, _i32]
+lib.moe_expert_cache_init.restype = ctypes.c_int
+lib.moe_expert_cache_init.argtypes = [_vp, _sz, _i32, _i32, _vp]
+lib.moe_expert_cache_route.restype = ctypes.c_int
+lib.moe_expert_cache_route.argtypes = [_vp, _sz, _i32, _i32, _vp, _i64, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                       _i32, _i32, _vp]
+EXPERT_CACHE_TAG = 0x4B334543
 FFN_STAGE_EVENTS = 7
 # launches between consecutive events of moe_mxfp4_ffn_profiled
 FFN_STAGES = ("group", "gate_up", "gate_up_stream", "down", "down_stream", "combine")
@@ -301,3 +314,68 @@ def moe_verify_width_choose(distinct, S: int, accept=None, expert_bytes: float =
     _check("moe_verify_width_choose", lib.moe_verify_width_choose(d, W, S, a, float(expert_bytes), float(bytes_per_s),
                                                                   float(fixed_s), ctypes.byref(best), rates))
     return int(best.value), [float(r) for r in rates]
+
+
+def moe_expert_cache_state_size(E: int, C: int) -> int:
+    return int(lib.moe_expert_cache_state_size(E, C))
+
+
+def moe_expert_cache_init(E: int, C: int, state: torch.Tensor | None = None,
+                          device: torch.device | str = "cuda") -> torch.Tensor:
+    """Empty cache state for E experts and C slots (u8 device tensor)."""
+    need = moe_expert_cache_state_size(E, C)
+    if state is None:
+        state = torch.empty(max(need, 1), dtype=torch.uint8, device=device)
+    _dev(state, "state", torch.uint8)
+    _check("moe_expert_cache_init", lib.moe_expert_cache_init(_ptr(state), state.numel(), E, C,
+                                                              _stream(state.device)))
+    return state
+
+
+def _store(t: torch.Tensor, name: str) -> None:
+    if t.dtype != torch.uint8:
+        raise TypeError(f"{name}: expected uint8, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    if t.device.type != "cuda" and not t.is_pinned():
+        raise ValueError(f"{name}: must be a device tensor or pinned host memory")
+
+
+def moe_expert_cache_route(state: torch.Tensor, E: int, C: int, ids: torch.Tensor, store_w1: torch.Tensor,
+                           store_w3: torch.Tensor, store_w2: torch.Tensor, cache_w1: torch.Tensor,
+                           cache_w3: torch.Tensor, cache_w2: torch.Tensor,
+                           slot_ids: torch.Tensor | None = None) -> torch.Tensor:
+    """Stage a batch's routed experts into the C slots; returns slot_ids
+    int32 [T, k] (the FFN then runs on cache_w* with slot_ids and E = C).
+    store_w*: all E experts, device tensors or pinned host tensors."""
+    _dev(state, "state", torch.uint8)
+    _dev(ids, "ids", torch.int32)
+    for n, t in (("store_w1", store_w1), ("store_w3", store_w3), ("store_w2", store_w2)):
+        _store(t, n)
+    for n, t in (("cache_w1", cache_w1), ("cache_w3", cache_w3), ("cache_w2", cache_w2)):
+        _dev(t, n, torch.uint8)
+    T, k = ids.shape
+    I, D = store_w1.shape[1], store_w2.shape[1]
+    if store_w1.shape != (E, I, D // 32, 17) or store_w3.shape != store_w1.shape or \
+            store_w2.shape != (E, D, I // 32, 17):
+        raise ValueError("store matrices must be [E, I, D/32, 17] and [E, D, I/32, 17]")
+    if cache_w1.shape != (C, I, D // 32, 17) or cache_w3.shape != cache_w1.shape or \
+            cache_w2.shape != (C, D, I // 32, 17):
+        raise ValueError("cache matrices must be [C, I, D/32, 17] and [C, D, I/32, 17]")
+    if slot_ids is None:
+        slot_ids = torch.empty((T, k), dtype=torch.int32, device=ids.device)
+    _dev(slot_ids, "slot_ids", torch.int32)
+    if slot_ids.shape != (T, k):
+        raise ValueError("slot_ids must be [T, k]")
+    _check("moe_expert_cache_route", lib.moe_expert_cache_route(
+        _ptr(state), state.numel(), E, C, _ptr(ids), T, k, _ptr(slot_ids), _ptr(store_w1), _ptr(store_w3),
+        _ptr(store_w2), _ptr(cache_w1), _ptr(cache_w3), _ptr(cache_w2), D, I, _stream(ids.device)))
+    return slot_ids
+
+
+def moe_expert_cache_header(state: torch.Tensor) -> dict:
+    """The state's header fields, copied to the host (synchronizes)."""
+    raw = state[:48].cpu().numpy().tobytes()
+    step, n_fetch, hits, misses, hits_total, misses_total, E, C, tag, _ = struct.unpack("<4I2Q2i2I", raw)
+    return {"step": step, "n_fetch": n_fetch, "hits": hits, "misses": misses, "hits_total": hits_total,
+            "misses_total": misses_total, "E": E, "C": C, "tag": tag}

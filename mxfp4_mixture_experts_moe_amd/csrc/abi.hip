@@ -517,6 +517,72 @@ int moe_verify_width_choose(const int32_t* distinct, int32_t W, int32_t S, const
   return K3MOE_OK;
 }
 
+size_t moe_expert_cache_state_size(int32_t E, int32_t C) {
+  if (E < 1 || C < 1 || E > K3MOE_MAX_EXPERTS_FFN || C > K3MOE_MAX_EXPERTS_FFN) return 0;
+  return cache_state_view(nullptr, E, C).bytes;
+}
+
+int moe_expert_cache_init(void* state, size_t state_bytes, int32_t E, int32_t C, void* stream) {
+  const size_t need = moe_expert_cache_state_size(E, C);
+  if (need == 0) return K3MOE_ERR_SHAPE;
+  if (!state) return K3MOE_ERR_NULL;
+  if (misaligned(state)) return K3MOE_ERR_ALIGN;
+  if (state_bytes < need) return K3MOE_ERR_WORKSPACE;
+  return device_status(launch_cache_init(cache_state_view(state, E, C), static_cast<hipStream_t>(stream)));
+}
+
+// A pointer the GPU can read, for the store: device memory as it is, pinned
+// host memory through its device mapping; nullptr for anything else.
+static const uint8_t* device_readable(const uint8_t* p) {
+  hipPointerAttribute_t at{};
+  if (hipPointerGetAttributes(&at, p) != hipSuccess) {
+    (void)hipGetLastError();  // clear the sticky error of an unknown pointer
+    return nullptr;
+  }
+  if (at.type == hipMemoryTypeDevice) return p;
+  if (at.type == hipMemoryTypeHost && at.devicePointer) return static_cast<const uint8_t*>(at.devicePointer);
+  return nullptr;
+}
+
+int moe_expert_cache_route(void* state, size_t state_bytes, int32_t E, int32_t C, const int32_t* topk_ids, int64_t T,
+                           int32_t k, int32_t* slot_ids, const uint8_t* store_w1, const uint8_t* store_w3,
+                           const uint8_t* store_w2, uint8_t* cache_w1, uint8_t* cache_w3, uint8_t* cache_w2, int32_t D,
+                           int32_t I, void* stream) {
+  const size_t need = moe_expert_cache_state_size(E, C);
+  if (need == 0 || T < 0 || k < 1 || k > K3MOE_MAX_TOPK) return K3MOE_ERR_SHAPE;
+  if (D <= 0 || I <= 0 || (D % 32) != 0 || (I % 32) != 0 || D > K3MOE_MAX_DIM_FFN || I > K3MOE_MAX_DIM_FFN)
+    return K3MOE_ERR_SHAPE;
+  if (T * (int64_t)k > 0x7FFFFFFF) return K3MOE_ERR_SHAPE;
+  const int64_t entries = T * (int64_t)k;
+  if ((int64_t)C < (entries < E ? entries : (int64_t)E)) return K3MOE_ERR_SHAPE;
+  if (T == 0) return K3MOE_OK;
+  if (!state || !topk_ids || !slot_ids || !store_w1 || !store_w3 || !store_w2 || !cache_w1 || !cache_w3 || !cache_w2)
+    return K3MOE_ERR_NULL;
+  if (misaligned(state) || misaligned(topk_ids) || misaligned(slot_ids) || misaligned(store_w1) ||
+      misaligned(store_w3) || misaligned(store_w2) || misaligned(cache_w1) || misaligned(cache_w3) ||
+      misaligned(cache_w2))
+    return K3MOE_ERR_ALIGN;
+  if (state_bytes < need) return K3MOE_ERR_WORKSPACE;
+  CacheFetchArgs f{};
+  f.store_w1 = device_readable(store_w1);
+  f.store_w3 = device_readable(store_w3);
+  f.store_w2 = device_readable(store_w2);
+  if (!f.store_w1 || !f.store_w3 || !f.store_w2) return K3MOE_ERR_UNSUPPORTED;
+  const CacheState st = cache_state_view(state, E, C);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (launch_cache_plan(st, topk_ids, entries, slot_ids, s) != hipSuccess) return K3MOE_ERR_DEVICE;
+  f.header = st.header;
+  f.fetch = st.fetch;
+  f.cache_w1 = cache_w1;
+  f.cache_w3 = cache_w3;
+  f.cache_w2 = cache_w2;
+  f.mat13 = (int64_t)I * (D / 32) * 17;
+  f.mat2 = (int64_t)D * (I / 32) * 17;
+  f.E = E;
+  f.C = C;
+  return device_status(launch_cache_fetch(f, s));
+}
+
 static int group_shape_status(int64_t T, int32_t E, int32_t k) {
   if (T < 0 || E < 1 || E > K3MOE_MAX_EXPERTS_FFN || k < 1 || k > K3MOE_MAX_TOPK) return K3MOE_ERR_SHAPE;
   if (T * (int64_t)k > 0x7FFFFFFF) return K3MOE_ERR_SHAPE;

@@ -2,6 +2,8 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+
+#include "k3moe.h"
 #include <stddef.h>
 #include <stdint.h>
 
@@ -146,6 +148,30 @@ hipError_t launch_combine(const float* y, const int8_t* y_scale, bool mixed, con
 // position <= w of S sequences of W rows (W <= kMaxVerifyWidth, E <= 8192).
 constexpr int kMaxVerifyWidth = 64;
 hipError_t launch_verify_distinct(const int32_t* ids, int S, int W, int E, int k, int32_t* distinct, hipStream_t s);
+
+// Device expert cache (state layout inside the caller's buffer; the header
+// type is public, k3moe_expert_cache_header).
+struct CacheState {
+  k3moe_expert_cache_header* header;
+  int32_t* slot_of;    // [E]: slot of expert e, -1 if not cached
+  int32_t* expert_in;  // [C]: expert in slot s, -1 if empty
+  int32_t* order;      // [C]: slots, least recently used first
+  int32_t* fetch;      // [2C]: (expert, slot) of the last batch's misses
+  size_t bytes;        // total state bytes
+  int32_t E, C;
+};
+CacheState cache_state_view(void* state, int32_t E, int32_t C);
+hipError_t launch_cache_init(const CacheState& st, hipStream_t s);
+hipError_t launch_cache_plan(const CacheState& st, const int32_t* ids, int64_t n, int32_t* slot_ids, hipStream_t s);
+struct CacheFetchArgs {
+  const k3moe_expert_cache_header* header;
+  const int32_t* fetch;
+  const uint8_t *store_w1, *store_w3, *store_w2;  // device-readable store [E, ...]
+  uint8_t *cache_w1, *cache_w3, *cache_w2;        // slots [C, ...]
+  int64_t mat13, mat2;                            // bytes of one w1 / w3 and one w2 matrix
+  int32_t E, C;
+};
+hipError_t launch_cache_fetch(const CacheFetchArgs& a, hipStream_t s);
 
 // Token-tile height the FFN uses for a batch of T tokens with k routed experts.
 int choose_rows_per_tile(int64_t T, int k, int E);

@@ -49,3 +49,14 @@ def k3():
     import mxfp4_mixture_experts_moe_amd as m
 
     return m
+
+
+@pytest.fixture(scope="session")
+def k3_experts(k3):
+    """All 896 K3-shaped experts resident on the device (15.7 GB), shared by
+    every GPU test module that needs them."""
+    import moe_inputs
+    from moe_inputs.device import upload_experts
+
+    print("[k3] uploading 896 K3 experts", flush=True)
+    return upload_experts(moe_inputs.PREFILL, lambda p, s, out: k3.mxfp4_repack(p, s, blocks=out))

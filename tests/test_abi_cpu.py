@@ -26,7 +26,8 @@ def test_library_exports_every_declared_symbol(k3):
     assert set(names) == {"k3moe_status_str", "moe_route_topk", "mxfp4_repack", "mxfp4_dequant",
                           "moe_mxfp4_ffn_workspace_size", "moe_mxfp4_ffn", "moe_mxfp4_ffn_profiled",
                           "moe_mxfp4_ffn_noalloc", "moe_group_workspace_size", "moe_group_by_expert",
-                          "moe_verify_width_distinct", "moe_verify_width_choose"}
+                          "moe_verify_width_distinct", "moe_verify_width_choose", "moe_expert_cache_state_size",
+                          "moe_expert_cache_init", "moe_expert_cache_route"}
     for n in names:
         assert hasattr(k3.lib, n), n
 
@@ -210,3 +211,34 @@ def test_verify_width_choose_matches_oracle(k3):
     assert best == 3
     with pytest.raises(k3.K3MoeError):
         k3.moe_verify_width_choose([16, 20], 4, None, 1e6, 0.0, 0.0)  # no bandwidth
+
+
+def test_expert_cache_state_size(k3):
+    sz = k3.moe_expert_cache_state_size
+    assert sz(0, 4) == 0 and sz(4, 0) == 0 and sz(8193, 4) == 0 and sz(4, 8193) == 0
+    # header, slot_of[E], expert_in[C], order[C], fetch[2C], each on 256 bytes
+    assert sz(896, 160) == 256 + 3584 + 768 + 768 + 1280
+    assert sz(8192, 8192) >= 4 * (8192 + 4 * 8192)
+
+
+def test_expert_cache_checks(k3):
+    init, route = k3.lib.moe_expert_cache_init, k3.lib.moe_expert_cache_route
+    need = k3.moe_expert_cache_state_size(896, 160)
+    assert init(A, need, 0, 160, None) == ERR_SHAPE
+    assert init(None, need, 896, 160, None) == ERR_NULL
+    assert init(A + 4, need, 896, 160, None) == ERR_ALIGN
+    assert init(A, need - 1, 896, 160, None) == ERR_WORKSPACE
+
+    def r(state=A, nbytes=need, E=896, C=160, ids=A, T=8, k=16, sid=A, st=(A, A, A), ca=(A, A, A), D=7168, I=2048):
+        return route(state, nbytes, E, C, ids, T, k, sid, *st, *ca, D, I, None)
+
+    assert r(T=0) == OK  # an empty batch is a no-op
+    assert r(C=127) == ERR_SHAPE  # 8 x 16 entries may use 128 experts
+    assert r(E=100, C=99) == ERR_SHAPE  # ... and 100 experts of 100 (C = E holds any batch)
+    assert r(k=0) == ERR_SHAPE and r(k=65) == ERR_SHAPE and r(T=-1) == ERR_SHAPE
+    assert r(D=7000) == ERR_SHAPE and r(I=2050) == ERR_SHAPE and r(D=0) == ERR_SHAPE
+    assert r(E=0) == ERR_SHAPE and r(C=8193) == ERR_SHAPE
+    assert r(state=None) == ERR_NULL and r(ids=None) == ERR_NULL and r(sid=None) == ERR_NULL
+    assert r(st=(A, None, A)) == ERR_NULL and r(ca=(A, A, None)) == ERR_NULL
+    assert r(state=A + 4) == ERR_ALIGN and r(st=(A + 8, A, A)) == ERR_ALIGN and r(ca=(A, A + 2, A)) == ERR_ALIGN
+    assert r(nbytes=need - 1) == ERR_WORKSPACE

@@ -477,12 +477,8 @@ def test_combine_large_batch_slot_batches(k3):
 
 
 # ---------------------------------------------------------------------------
-# K3-shaped configs: all 896 experts resident on the device (15.7 GB).
-
-@pytest.fixture(scope="module")
-def k3_experts(k3):
-    print("[ffn] uploading 896 K3 experts", flush=True)
-    return device_experts(k3, moe_inputs.PREFILL)
+# K3-shaped configs: all 896 experts resident on the device (15.7 GB; the
+# session fixture k3_experts in conftest.py).
 
 
 def last_tokens_of(ids, experts):
