@@ -29,6 +29,8 @@ import numpy as np
 
 # tensor ids used as keys of the per-tensor streams
 T_W1, T_W3, T_W2, T_X, T_LOGITS, T_BIAS, T_PERM, T_SINGLE = 1, 2, 3, 4, 5, 6, 7, 8
+# latent-MoE block: hidden rows and the dense weights around the experts
+T_H, T_WG, T_WD, T_GAMMA, T_WU, T_WS1, T_WS3, T_WS2 = 9, 10, 11, 12, 13, 14, 15, 16
 
 
 def rng(seed: int, *key: int) -> np.random.Generator:
@@ -192,3 +194,77 @@ class Batch:
 def make_batch(cfg: LayerConfig, seed: int | None = None) -> Batch:
     z, b = router_inputs(cfg, seed)
     return Batch(cfg, activations(cfg, seed), z, b, ExpertSource(cfg))
+
+
+# ---------------------------------------------------------------------------
+# Latent-MoE block workloads: hidden rows h [T, H] go through the gate
+# projection (router logits), ffn_routed_down / _norm into the latent width,
+# the routed experts, ffn_routed_up back to H, plus a shared expert (tensor
+# names from the llama.cpp page's dry-run comment; hidden width 7168 there).
+
+
+@dataclass(frozen=True)
+class BlockConfig:
+    """One synthetic latent-MoE block workload.
+
+    ``layer`` carries the routed part (E, k, latent D, expert I, T, the
+    selection bias and the expert weights); its router-logit settings are
+    unused, the logits come from the gate projection."""
+
+    name: str
+    config_id: int
+    layer: LayerConfig
+    H: int  # hidden width
+    Is: int  # shared-expert intermediate width
+    eps: float = 1e-6
+    dense_id: int = -1  # key of the dense weight streams; -1 -> config_id
+    notes: str = ""
+
+    @property
+    def T(self):
+        return self.layer.T
+
+    def with_(self, **kw) -> "BlockConfig":
+        d = dict(self.__dict__)
+        d.update(kw)
+        return BlockConfig(**d)
+
+
+K3_DENSE = 3
+BLOCK_TINY = BlockConfig("block-tiny", 20, TINY.with_(E=8, k=2, D=128, I=256, T=40, bias_sigma=0.1, config_id=21),
+                         H=256, Is=192, notes="8 experts top-2, H 256, latent 128, shared 192, 40 tokens")
+BLOCK_DECODE1 = BlockConfig("block-decode-t1", 22, DECODE1.with_(config_id=23), H=7168, Is=3072, dense_id=K3_DENSE,
+                            notes="K3 block decode, 1 token")
+BLOCK_DECODE8 = BlockConfig("block-decode-t8", 24, DECODE8.with_(config_id=25), H=7168, Is=3072, dense_id=K3_DENSE,
+                            notes="K3 block decode, 8 tokens")
+BLOCK_PREFILL = BlockConfig("block-prefill", 26, PREFILL.with_(config_id=27), H=7168, Is=3072, dense_id=K3_DENSE,
+                            notes="K3 block prefill, 4096 tokens, bias N(0,0.5)")
+BLOCK_CONFIGS = {c.name: c for c in (BLOCK_TINY, BLOCK_DECODE1, BLOCK_DECODE8, BLOCK_PREFILL)}
+
+
+def block_hidden(cfg: BlockConfig, seed: int | None = None) -> np.ndarray:
+    """h ~ bf16(N(0,1)), shape [T, H], as raw bf16 bits."""
+    s = cfg.layer.seed if seed is None else seed
+    g = rng(s, cfg.config_id, T_H)
+    return bf16_bits(g.standard_normal((cfg.T, cfg.H), dtype=np.float32))
+
+
+def block_dense_weights(cfg: BlockConfig) -> dict:
+    """The dense weights as raw bf16 bits: each ~ N(0, 1/fan_in) (so every
+    product's outputs are about unit scale), gamma ~ 1 + N(0, 0.1^2)."""
+    L = cfg.layer
+    wid = cfg.config_id if cfg.dense_id < 0 else cfg.dense_id
+    shapes = {"Wg": (T_WG, L.E, cfg.H), "Wd": (T_WD, L.D, cfg.H), "Wu": (T_WU, cfg.H, L.D),
+              "Ws1": (T_WS1, cfg.Is, cfg.H), "Ws3": (T_WS3, cfg.Is, cfg.H), "Ws2": (T_WS2, cfg.H, cfg.Is)}
+    out = {}
+    for name, (tid, rows, cols) in shapes.items():
+        g = rng(L.seed, 200 + wid, tid)
+        out[name] = bf16_bits(g.standard_normal((rows, cols), dtype=np.float32) * np.float32(cols ** -0.5))
+    g = rng(L.seed, 200 + wid, T_GAMMA)
+    out["gamma"] = bf16_bits((1.0 + 0.1 * g.standard_normal(L.D)).astype(np.float32))
+    return out
+
+
+def block_bias(cfg: BlockConfig) -> np.ndarray:
+    """The selection bias of the routed part (zero when its sigma is 0)."""
+    return router_inputs(cfg.layer.with_(T=1))[1]

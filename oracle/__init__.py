@@ -18,6 +18,8 @@ Modules
 ``ffn``     the routed-expert FFN: route -> per-expert SiLU-gated MLP -> weighted sum
 ``verify``  expert bytes of a speculative verify batch by width, and the width a cost hint picks
 ``cache``   a least-recently-used device expert cache in front of an external expert store
+``latent``  the latent-MoE block: gate projection, latent down + RMS norm, routed
+            experts, latent up, shared expert
 
 Parity status
 -------------
@@ -25,7 +27,9 @@ Every function here is pinned by ``tests/test_oracle_*.py`` against something
 other than itself (values printed on the pages, IEEE-754 closed forms, a
 library decode of E8M0, a textbook sort, brute-force loops, an identity-weight
 closed form, a hand-worked verify-width choice, a hand-worked cache sequence
-and an independent last-use LRU simulation).  The FFN's numerics beyond those closed forms have no worked
+and an independent last-use LRU simulation, bf16 rounding against every bf16
+value and torch's conversion, an identity-weight closed form of the latent
+block and its pure-Python loop evaluation).  The FFN's numerics beyond those closed forms have no worked
 example on the pages; ``ffn_ref`` is pinned by a pure-Python loop evaluation
 and the identity case only.
 """
@@ -44,3 +48,4 @@ from .permute import permute_ref, valid_entries  # noqa: F401
 from .ffn import ffn_ref, silu_mul  # noqa: F401
 from .verify import expected_committed, verify_distinct_ref, verify_width_choose_ref  # noqa: F401
 from .cache import ExpertCacheRef  # noqa: F401
+from .latent import bf16_round, latent_block_ref, rms_norm  # noqa: F401
