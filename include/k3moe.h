@@ -414,6 +414,66 @@ int moe_expert_cache_route(void* state, size_t state_bytes, int32_t E, int32_t C
                            const uint8_t* store_w2, uint8_t* cache_w1, uint8_t* cache_w3, uint8_t* cache_w2, int32_t D,
                            int32_t I, void* stream);
 
+/*
+ * moe_latent_block — the latent-MoE block around the routed experts.
+ * Sources: llama.cpp pull request "model: add Kimi-K3 text model": opening
+ * comment (latent MoE: routed experts run at a latent width), dry-run comment
+ * (per-layer gate with exp_probs_b, ffn_routed_down, ffn_routed_norm and
+ * ffn_routed_up beside the experts; hidden width 7168, 896 experts, 16 used,
+ * sigmoid gating), review comment (shared-expert invariants). The pages give
+ * no formula for the block; the reading this library computes, for hidden
+ * rows h (bf16() = round to nearest even; every product takes bf16 operands
+ * and sums in fp32):
+ *
+ *   z    = h Wg^T                          (router logits, fp32)
+ *   ids, w = moe_route_topk(z, bias, k, normalize, route_scale)
+ *   xl   = bf16(gamma * d / sqrt(mean(d^2) + eps)),  d = h Wd^T
+ *   yl   = bf16(moe_mxfp4_ffn(xl, ids, w, w1, w3, w2))   (routed experts at width D)
+ *   s    = bf16(SiLU(h Ws1^T) * (h Ws3^T))               (shared expert)
+ *   out  = yl Wu^T + s Ws2^T
+ *
+ *   h        bf16 [T, H]         hidden rows
+ *   wg       bf16 [E, H]         gate projection
+ *   bias     f32 [E] or NULL     selection bias (NULL: zero)
+ *   wd       bf16 [D, H]         ffn_routed_down
+ *   gamma    bf16 [D]            ffn_routed_norm
+ *   w1, w3, w2                   routed experts exactly as for moe_mxfp4_ffn
+ *                                (E experts, latent width D, intermediate I)
+ *   wu       bf16 [H, D]         ffn_routed_up
+ *   ws1, ws3 bf16 [Is, H]        shared expert gate / up
+ *   ws2      bf16 [H, Is]        shared expert down
+ *   out      f32 [T, H]
+ *   topk_ids i32 [T, k], topk_w f32 [T, k]: optional outputs of the routing
+ *                                (NULL: kept in the workspace)
+ *   workspace  moe_latent_block_workspace_size(T, H, D, I, Is, E, k) bytes
+ *
+ * Sizes: T >= 0 (T == 0 is a no-op), H a multiple of 128, D and Is multiples
+ * of 64, I a multiple of 32, H, D, I, Is <= K3MOE_MAX_DIM_FFN, 1 <= k <=
+ * min(E, K3MOE_MAX_TOPK), E <= K3MOE_MAX_EXPERTS_FFN, T * k < 2^31, eps >= 0
+ * (K3MOE_ERR_SHAPE otherwise). Every pointer 16-byte aligned. Launches on
+ * `stream` only (the routed FFN may fork to its side stream and joins back);
+ * nothing synchronizes with the host; capturable in a graph.
+ */
+#define K3MOE_BLOCK_STAGE_EVENTS 6
+size_t moe_latent_block_workspace_size(int64_t T, int32_t H, int32_t D, int32_t I, int32_t Is, int32_t E, int32_t k);
+int moe_latent_block(const void* h_bf16, const void* wg, const float* bias, const void* wd, const void* gamma,
+                     const uint8_t* w1, const uint8_t* w3, const uint8_t* w2, const void* wu, const void* ws1,
+                     const void* ws3, const void* ws2, int64_t T, int32_t H, int32_t D, int32_t I, int32_t Is,
+                     int32_t E, int32_t k, int32_t normalize, float route_scale, float eps, float* out,
+                     int32_t* topk_ids, float* topk_w, void* workspace, size_t workspace_bytes, void* stream);
+/* The same block with every launch on `stream` (the FFN's side stream is not
+   used) and, when `events` is not NULL, K3MOE_BLOCK_STAGE_EVENTS caller-owned
+   hipEvent_t recorded on `stream` before the first product, the epilogue
+   after it (logits, latent norm, shared h), the routing, the routed FFN, the
+   second product (with its split sum) and after the last launch (NULL
+   entries are skipped). */
+int moe_latent_block_profiled(const void* h_bf16, const void* wg, const float* bias, const void* wd, const void* gamma,
+                              const uint8_t* w1, const uint8_t* w3, const uint8_t* w2, const void* wu,
+                              const void* ws1, const void* ws3, const void* ws2, int64_t T, int32_t H, int32_t D,
+                              int32_t I, int32_t Is, int32_t E, int32_t k, int32_t normalize, float route_scale,
+                              float eps, float* out, int32_t* topk_ids, float* topk_w, void* workspace,
+                              size_t workspace_bytes, void* stream, void* const* events);
+
 #ifdef __cplusplus
 }
 #endif

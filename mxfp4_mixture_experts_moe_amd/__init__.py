@@ -33,6 +33,9 @@ __all__ = [
     "moe_expert_cache_init",
     "moe_expert_cache_route",
     "moe_expert_cache_header",
+    "moe_latent_block_workspace_size",
+    "moe_latent_block",
+    "BLOCK_STAGES",
     "moe_group_workspace_size",
     "moe_group_by_expert",
     "FFN_STAGES",
@@ -89,6 +92,16 @@ lib.moe_expert_cache_route.restype = ctypes.c_int
 lib.moe_expert_cache_route.argtypes = [_vp, _sz, _i32, _i32, _vp, _i64, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                        _i32, _i32, _vp]
 EXPERT_CACHE_TAG = 0x4B334543
+lib.moe_latent_block_workspace_size.restype = _sz
+lib.moe_latent_block_workspace_size.argtypes = [_i64, _i32, _i32, _i32, _i32, _i32, _i32]
+_block_args = [_vp] * 12 + [_i64] + [_i32] * 6 + [_i32, _f32, _f32, _vp, _vp, _vp, _vp, _sz, _vp]
+lib.moe_latent_block.restype = ctypes.c_int
+lib.moe_latent_block.argtypes = _block_args
+lib.moe_latent_block_profiled.restype = ctypes.c_int
+lib.moe_latent_block_profiled.argtypes = _block_args + [ctypes.POINTER(ctypes.c_void_p)]
+BLOCK_STAGE_EVENTS = 6
+# launches between consecutive events of moe_latent_block_profiled
+BLOCK_STAGES = ("dense1", "mid", "route", "ffn", "dense2")
 FFN_STAGE_EVENTS = 7
 # launches between consecutive events of moe_mxfp4_ffn_profiled
 FFN_STAGES = ("group", "gate_up", "gate_up_stream", "down", "down_stream", "combine")
@@ -379,3 +392,64 @@ def moe_expert_cache_header(state: torch.Tensor) -> dict:
     step, n_fetch, hits, misses, hits_total, misses_total, E, C, tag, _ = struct.unpack("<4I2Q2i2I", raw)
     return {"step": step, "n_fetch": n_fetch, "hits": hits, "misses": misses, "hits_total": hits_total,
             "misses_total": misses_total, "E": E, "C": C, "tag": tag}
+
+
+def moe_latent_block_workspace_size(T: int, H: int, D: int, I: int, Is: int, E: int, k: int) -> int:
+    return int(lib.moe_latent_block_workspace_size(T, H, D, I, Is, E, k))
+
+
+def moe_latent_block(h: torch.Tensor, wg: torch.Tensor, bias: torch.Tensor | None, wd: torch.Tensor,
+                     gamma: torch.Tensor, w1: torch.Tensor, w3: torch.Tensor, w2: torch.Tensor, wu: torch.Tensor,
+                     ws1: torch.Tensor, ws3: torch.Tensor, ws2: torch.Tensor, k: int, normalize: bool = True,
+                     route_scale: float = 1.0, eps: float = 1e-6, out: torch.Tensor | None = None,
+                     topk_ids: torch.Tensor | None = None, topk_w: torch.Tensor | None = None,
+                     workspace: torch.Tensor | None = None, stage_events=None) -> torch.Tensor:
+    """Latent-MoE block. h bf16 [T, H]; wg bf16 [E, H]; bias f32 [E] or None;
+    wd bf16 [D, H]; gamma bf16 [D]; w1/w3 u8 [E, I, D/32, 17], w2 u8 [E, D,
+    I/32, 17]; wu bf16 [H, D]; ws1/ws3 bf16 [Is, H]; ws2 bf16 [H, Is].
+    Returns out f32 [T, H]; topk_ids / topk_w (int32 / f32 [T, k]) receive the
+    routing when given.  stage_events: BLOCK_STAGE_EVENTS torch.cuda.Event
+    (moe_latent_block_profiled)."""
+    T, H = h.shape
+    E, D, Is = wg.shape[0], wd.shape[0], ws1.shape[0]
+    I = w1.shape[1]
+    for n, t in (("h", h), ("wg", wg), ("wd", wd), ("gamma", gamma), ("wu", wu), ("ws1", ws1), ("ws3", ws3),
+                 ("ws2", ws2)):
+        _dev(t, n, torch.bfloat16)
+    for n, t in (("w1", w1), ("w3", w3), ("w2", w2)):
+        _dev(t, n, torch.uint8)
+    shapes = {"wg": (wg, (E, H)), "wd": (wd, (D, H)), "gamma": (gamma, (D,)), "wu": (wu, (H, D)),
+              "ws1": (ws1, (Is, H)), "ws3": (ws3, (Is, H)), "ws2": (ws2, (H, Is)),
+              "w1": (w1, (E, I, D // 32, 17)), "w3": (w3, (E, I, D // 32, 17)), "w2": (w2, (E, D, I // 32, 17))}
+    for n, (t, shp) in shapes.items():
+        if tuple(t.shape) != shp:
+            raise ValueError(f"{n}: expected shape {shp}, got {tuple(t.shape)}")
+    if bias is not None:
+        _dev(bias, "bias", torch.float32)
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.float32, device=h.device)
+    _dev(out, "out", torch.float32)
+    for n, t, dt in (("topk_ids", topk_ids, torch.int32), ("topk_w", topk_w, torch.float32)):
+        if t is not None:
+            _dev(t, n, dt)
+            if tuple(t.shape) != (T, k):
+                raise ValueError(f"{n} must be [T, k]")
+    need = moe_latent_block_workspace_size(T, H, D, I, Is, E, k)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=h.device)
+    _dev(workspace, "workspace", torch.uint8)
+    args = (_ptr(h), _ptr(wg), _ptr(bias), _ptr(wd), _ptr(gamma), _ptr(w1), _ptr(w3), _ptr(w2), _ptr(wu), _ptr(ws1),
+            _ptr(ws3), _ptr(ws2), T, H, D, I, Is, E, k, int(bool(normalize)), float(route_scale), float(eps),
+            _ptr(out), _ptr(topk_ids), _ptr(topk_w), _ptr(workspace), workspace.numel(), _stream(h.device))
+    if stage_events is None:
+        _check("moe_latent_block", lib.moe_latent_block(*args))
+    else:
+        if len(stage_events) != BLOCK_STAGE_EVENTS:
+            raise ValueError(f"stage_events must hold {BLOCK_STAGE_EVENTS} events")
+        handles = (ctypes.c_void_p * BLOCK_STAGE_EVENTS)()
+        for i, ev in enumerate(stage_events):
+            if ev is not None and not ev.cuda_event:
+                ev.record()
+            handles[i] = None if ev is None else ev.cuda_event
+        _check("moe_latent_block_profiled", lib.moe_latent_block_profiled(*args, handles))
+    return out

@@ -3,6 +3,7 @@
 #include "k3moe.h"
 #include "k3moe_internal.h"
 
+#include <math.h>
 #include <sys/syscall.h>
 #include <unistd.h>
 
@@ -191,7 +192,8 @@ static_assert(kEvEnd + 1 == K3MOE_FFN_STAGE_EVENTS, "event slots");
 // `side` is set).
 int run_ffn_chunk(const void* x_bf16, const int32_t* topk_ids, const float* topk_w, const uint8_t* w1,
                   const uint8_t* w3, const uint8_t* w2, int64_t T, int32_t D, int32_t I, int32_t E, int32_t k,
-                  float* out, uint8_t* ws, hipStream_t s, void* const* stage_events, bool allow_side) {
+                  void* out, bool out_bf16, uint8_t* ws, hipStream_t s, void* const* stage_events,
+                  bool allow_side) {
   const FfnWorkspace L = ffn_workspace_layout(T, D, I, E, k);
   const int64_t entries = T * (int64_t)k;
   const int64_t active = entries < E ? entries : E;
@@ -353,8 +355,12 @@ int run_ffn_chunk(const void* x_bf16, const int32_t* topk_ids, const float* topk
   // Rows of the large-tile down kernel hold scaled fp16 y; a streaming-only
   // batch has none, so its combine reads fp32 rows only.
   const bool mixed_rows = tiled && !stream_only;
-  err = launch_combine(reinterpret_cast<const float*>(ws + L.y), reinterpret_cast<const int8_t*>(ws + L.y_scale),
-                       mixed_rows, g.slot_row, topk_w, T, D, k, out, s);
+  if (out_bf16)
+    err = launch_combine_bf16(reinterpret_cast<const float*>(ws + L.y), reinterpret_cast<const int8_t*>(ws + L.y_scale),
+                              mixed_rows, g.slot_row, topk_w, T, D, k, static_cast<uint16_t*>(out), s);
+  else
+    err = launch_combine(reinterpret_cast<const float*>(ws + L.y), reinterpret_cast<const int8_t*>(ws + L.y_scale),
+                         mixed_rows, g.slot_row, topk_w, T, D, k, static_cast<float*>(out), s);
   if (err != hipSuccess || !mark(kEvEnd)) return K3MOE_ERR_DEVICE;
   return K3MOE_OK;
 }
@@ -362,13 +368,14 @@ int run_ffn_chunk(const void* x_bf16, const int32_t* topk_ids, const float* topk
 // The FFN over all T tokens, one chunk of ffn_chunk_tokens() after another
 // (the chunks reuse one workspace; stream order serialises them).
 int run_ffn(const void* x_bf16, const int32_t* topk_ids, const float* topk_w, const uint8_t* w1, const uint8_t* w3,
-            const uint8_t* w2, int64_t T, int32_t D, int32_t I, int32_t E, int32_t k, float* out, uint8_t* ws,
-            hipStream_t s, void* const* stage_events, bool allow_side) {
+            const uint8_t* w2, int64_t T, int32_t D, int32_t I, int32_t E, int32_t k, void* out, bool out_bf16,
+            uint8_t* ws, hipStream_t s, void* const* stage_events, bool allow_side) {
   const int64_t tc = ffn_chunk_tokens(T, D, I, k);
   for (int64_t t0 = 0; t0 < T; t0 += tc) {
     const int64_t n = T - t0 < tc ? T - t0 : tc;
+    void* o = static_cast<uint8_t*>(out) + t0 * D * (out_bf16 ? 2 : 4);
     const int st = run_ffn_chunk(static_cast<const uint16_t*>(x_bf16) + t0 * D, topk_ids + t0 * k, topk_w + t0 * k,
-                                 w1, w3, w2, n, D, I, E, k, out + t0 * D, ws, s, stage_events, allow_side);
+                                 w1, w3, w2, n, D, I, E, k, o, out_bf16, ws, s, stage_events, allow_side);
     if (st != K3MOE_OK) return st;
   }
   return K3MOE_OK;
@@ -463,7 +470,7 @@ int moe_mxfp4_ffn_profiled(const void* x_bf16, const int32_t* topk_ids, const fl
   if (!workspace) return K3MOE_ERR_NULL;
   if (misaligned(workspace)) return K3MOE_ERR_ALIGN;
   if (workspace_bytes < moe_mxfp4_ffn_workspace_size(T, D, I, E, k)) return K3MOE_ERR_WORKSPACE;
-  return run_ffn(x_bf16, topk_ids, topk_w, w1, w3, w2, T, D, I, E, k, out, static_cast<uint8_t*>(workspace),
+  return run_ffn(x_bf16, topk_ids, topk_w, w1, w3, w2, T, D, I, E, k, out, false, static_cast<uint8_t*>(workspace),
                  static_cast<hipStream_t>(stream), stage_events, true);
 }
 
@@ -476,7 +483,7 @@ int moe_mxfp4_ffn_noalloc(const void* x_bf16, const int32_t* topk_ids, const flo
   void* ws = scratch_ptr();
   if (!ws) return K3MOE_ERR_DEVICE;
   // every launch on the caller's stream: no side stream (creating one may allocate)
-  return run_ffn(x_bf16, topk_ids, topk_w, w1, w3, w2, T, D, I, E, k, out, static_cast<uint8_t*>(ws),
+  return run_ffn(x_bf16, topk_ids, topk_w, w1, w3, w2, T, D, I, E, k, out, false, static_cast<uint8_t*>(ws),
                  static_cast<hipStream_t>(stream), nullptr, false);
 }
 
@@ -581,6 +588,191 @@ int moe_expert_cache_route(void* state, size_t state_bytes, int32_t E, int32_t C
   f.E = E;
   f.C = C;
   return device_status(launch_cache_fetch(f, s));
+}
+
+// ---------------------------------------------------------------------------
+// Latent-MoE block.
+
+struct BlockPlan {
+  int base_z, base_d, base_g, base_u, NV1;  // first product's segments (virtual feature offsets)
+  int ksteps1, split1_steps, splits1;
+  int ksteps2, split2_steps, splits2;
+  size_t z, xl, s, ids, w, yl, region, total;  // workspace offsets (256-aligned); region: products' partials and
+                                               // the FFN's workspace, which never live at the same time
+};
+
+static int dense_split_steps(int64_t T, int NV, int ksteps, int* splits) {
+  int steps;
+  if (T <= kDenseStreamMaxTokens) {
+    steps = kDenseStreamSplitSteps;
+  } else {
+    const int n = dense_tile_splits(T, NV, ksteps);
+    steps = (ksteps + n - 1) / n;
+  }
+  *splits = (ksteps + steps - 1) / steps;
+  return steps;
+}
+
+static BlockPlan block_plan(int64_t T, int32_t H, int32_t D, int32_t I, int32_t Is, int32_t E, int32_t k) {
+  auto up = [](int64_t v, int64_t a) { return (v + a - 1) / a * a; };
+  BlockPlan P{};
+  P.base_z = 0;
+  P.base_d = (int)up(E, kDenseSegAlign);
+  P.base_g = P.base_d + (int)up(D, kDenseSegAlign);
+  P.base_u = P.base_g + (int)up(Is, kDenseSegAlign);
+  P.NV1 = P.base_u + (int)up(Is, kDenseSegAlign);
+  P.ksteps1 = H / kDenseKStep;
+  P.split1_steps = dense_split_steps(T, P.NV1, P.ksteps1, &P.splits1);
+  P.ksteps2 = D / kDenseKStep + Is / kDenseKStep;
+  P.split2_steps = dense_split_steps(T, H, P.ksteps2, &P.splits2);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = (size_t)up((int64_t)(off + bytes), 256);
+    return o;
+  };
+  P.z = take((size_t)T * E * 4);
+  P.xl = take((size_t)T * D * 2);
+  P.s = take((size_t)T * Is * 2);
+  P.ids = take((size_t)T * k * 4);
+  P.w = take((size_t)T * k * 4);
+  P.yl = take((size_t)T * D * 2);
+  size_t region = (size_t)P.splits1 * T * P.NV1 * 4;
+  if (P.splits2 > 1 && (size_t)P.splits2 * T * H * 4 > region) region = (size_t)P.splits2 * T * H * 4;
+  const size_t ffn = moe_mxfp4_ffn_workspace_size(T, D, I, E, k);
+  if (ffn > region) region = ffn;
+  P.region = take(region);
+  P.total = off;
+  return P;
+}
+
+static int block_shape_status(int64_t T, int32_t H, int32_t D, int32_t I, int32_t Is, int32_t E, int32_t k,
+                              float eps) {
+  if (T < 0 || k < 1 || E < k || k > K3MOE_MAX_TOPK || E > K3MOE_MAX_EXPERTS_FFN) return K3MOE_ERR_SHAPE;
+  if (H <= 0 || D <= 0 || I <= 0 || Is <= 0 || H % 128 || D % 64 || Is % 64 || I % 32) return K3MOE_ERR_SHAPE;
+  if (H > K3MOE_MAX_DIM_FFN || D > K3MOE_MAX_DIM_FFN || I > K3MOE_MAX_DIM_FFN || Is > K3MOE_MAX_DIM_FFN)
+    return K3MOE_ERR_SHAPE;
+  if (T * (int64_t)k > 0x7FFFFFFF || !(eps >= 0.0f) || !isfinite(eps)) return K3MOE_ERR_SHAPE;
+  // launch grids: tile-kernel workgroups and epilogue rows fit 32-bit counts
+  const BlockPlan P = block_plan(T > 0 ? T : 1, H, D, I, Is, E, k);
+  const int64_t tiles1 = (int64_t)(P.NV1 / 128) * ((T + 127) / 128) * P.splits1;
+  if (tiles1 > 0x7FFFFFFF || T * (int64_t)(H / 4) / 256 > 0x7FFFFFFF) return K3MOE_ERR_SHAPE;
+  return K3MOE_OK;
+}
+
+size_t moe_latent_block_workspace_size(int64_t T, int32_t H, int32_t D, int32_t I, int32_t Is, int32_t E, int32_t k) {
+  if (block_shape_status(T, H, D, I, Is, E, k, 0.0f) != K3MOE_OK || T == 0) return 0;
+  return block_plan(T, H, D, I, Is, E, k).total;
+}
+
+int moe_latent_block_profiled(const void* h_bf16, const void* wg, const float* bias, const void* wd, const void* gamma,
+                              const uint8_t* w1, const uint8_t* w3, const uint8_t* w2, const void* wu,
+                              const void* ws1, const void* ws3, const void* ws2, int64_t T, int32_t H, int32_t D,
+                              int32_t I, int32_t Is, int32_t E, int32_t k, int32_t normalize, float route_scale,
+                              float eps, float* out, int32_t* topk_ids, float* topk_w, void* workspace,
+                              size_t workspace_bytes, void* stream, void* const* events) {
+  const int st = block_shape_status(T, H, D, I, Is, E, k, eps);
+  if (st != K3MOE_OK) return st;
+  if (T == 0) return K3MOE_OK;
+  if (!h_bf16 || !wg || !wd || !gamma || !w1 || !w3 || !w2 || !wu || !ws1 || !ws3 || !ws2 || !out || !workspace)
+    return K3MOE_ERR_NULL;
+  const void* ptrs[] = {h_bf16, wg, bias, wd, gamma, w1, w3, w2, wu, ws1, ws3, ws2, out, topk_ids, topk_w, workspace};
+  for (const void* q : ptrs)
+    if (misaligned(q)) return K3MOE_ERR_ALIGN;
+  const BlockPlan P = block_plan(T, H, D, I, Is, E, k);
+  if (workspace_bytes < P.total) return K3MOE_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  float* z = reinterpret_cast<float*>(ws + P.z);
+  uint16_t* xl = reinterpret_cast<uint16_t*>(ws + P.xl);
+  uint16_t* sh = reinterpret_cast<uint16_t*>(ws + P.s);
+  int32_t* ids = topk_ids ? topk_ids : reinterpret_cast<int32_t*>(ws + P.ids);
+  float* wts = topk_w ? topk_w : reinterpret_cast<float*>(ws + P.w);
+  uint16_t* yl = reinterpret_cast<uint16_t*>(ws + P.yl);
+  float* region = reinterpret_cast<float*>(ws + P.region);
+  auto mark = [&](int i) { return !events || !events[i] || hipEventRecord((hipEvent_t)events[i], s) == hipSuccess; };
+
+  // first product: gate | latent down | shared gate | shared up, all on h
+  DenseGemmArgs g1{};
+  g1.a[0] = static_cast<const uint16_t*>(h_bf16);
+  g1.lda[0] = H;
+  g1.ksteps[0] = P.ksteps1;
+  g1.nseg = 4;
+  const void* w1seg[4] = {wg, wd, ws1, ws3};
+  const int rows1[4] = {E, D, Is, Is};
+  const int base1[4] = {P.base_z, P.base_d, P.base_g, P.base_u};
+  for (int i = 0; i < 4; ++i) {
+    g1.rows[i] = rows1[i];
+    g1.base[i] = base1[i];
+    g1.w[i][0] = static_cast<const uint16_t*>(w1seg[i]);
+    g1.ldw[i][0] = H;
+  }
+  g1.T = T;
+  g1.NV = P.NV1;
+  g1.split_steps = P.split1_steps;
+  g1.splits = P.splits1;
+  g1.p = region;
+  if (!mark(0) || launch_dense_gemm(g1, s) != hipSuccess) return K3MOE_ERR_DEVICE;
+
+  BlockMidArgs m{};
+  m.p = region;
+  m.splits = P.splits1;
+  m.NV = P.NV1;
+  m.T = T;
+  m.E = E;
+  m.D = D;
+  m.Is = Is;
+  m.base_z = P.base_z;
+  m.base_d = P.base_d;
+  m.base_g = P.base_g;
+  m.base_u = P.base_u;
+  m.gamma = static_cast<const uint16_t*>(gamma);
+  m.eps = eps;
+  m.z = z;
+  m.xl = xl;
+  m.s = sh;
+  if (!mark(1) || launch_block_mid(m, s) != hipSuccess) return K3MOE_ERR_DEVICE;
+  if (!mark(2) || launch_route_topk(z, bias, T, E, k, normalize, route_scale, ids, wts, s) != hipSuccess)
+    return K3MOE_ERR_DEVICE;
+  if (!mark(3)) return K3MOE_ERR_DEVICE;
+  const int fst = run_ffn(xl, ids, wts, w1, w3, w2, T, D, I, E, k, yl, true, reinterpret_cast<uint8_t*>(region), s,
+                          nullptr, events == nullptr);
+  if (fst != K3MOE_OK) return fst;
+
+  // second product: [yl | s] (K segments) times [Wu | Ws2], one sum
+  DenseGemmArgs g2{};
+  g2.a[0] = yl;
+  g2.lda[0] = D;
+  g2.ksteps[0] = D / kDenseKStep;
+  g2.a[1] = sh;
+  g2.lda[1] = Is;
+  g2.ksteps[1] = Is / kDenseKStep;
+  g2.nseg = 1;
+  g2.rows[0] = H;
+  g2.base[0] = 0;
+  g2.w[0][0] = static_cast<const uint16_t*>(wu);
+  g2.ldw[0][0] = D;
+  g2.w[0][1] = static_cast<const uint16_t*>(ws2);
+  g2.ldw[0][1] = Is;
+  g2.T = T;
+  g2.NV = H;
+  g2.split_steps = P.split2_steps;
+  g2.splits = P.splits2;
+  g2.p = P.splits2 == 1 ? out : region;
+  if (!mark(4) || launch_dense_gemm(g2, s) != hipSuccess) return K3MOE_ERR_DEVICE;
+  if (P.splits2 > 1 && launch_dense_sum(region, P.splits2, T, H, out, s) != hipSuccess) return K3MOE_ERR_DEVICE;
+  if (!mark(5)) return K3MOE_ERR_DEVICE;
+  return K3MOE_OK;
+}
+
+int moe_latent_block(const void* h_bf16, const void* wg, const float* bias, const void* wd, const void* gamma,
+                     const uint8_t* w1, const uint8_t* w3, const uint8_t* w2, const void* wu, const void* ws1,
+                     const void* ws3, const void* ws2, int64_t T, int32_t H, int32_t D, int32_t I, int32_t Is,
+                     int32_t E, int32_t k, int32_t normalize, float route_scale, float eps, float* out,
+                     int32_t* topk_ids, float* topk_w, void* workspace, size_t workspace_bytes, void* stream) {
+  return moe_latent_block_profiled(h_bf16, wg, bias, wd, gamma, w1, w3, w2, wu, ws1, ws3, ws2, T, H, D, I, Is, E, k,
+                                   normalize, route_scale, eps, out, topk_ids, topk_w, workspace, workspace_bytes,
+                                   stream, nullptr);
 }
 
 static int group_shape_status(int64_t T, int32_t E, int32_t k) {

@@ -269,12 +269,13 @@ hipError_t launch_gemm(const GemmArgs& a, int rows_per_tile, hipStream_t s) {
 // kMixed: a slot_row entry with kBigRowFlag names a row written by the
 // large-tile down kernel, which holds y as fp16 scaled by 2^y_scale[row,
 // feature / 32] at the start of the row's fp32 slot.
+// OutT: float, or uint16_t for bf16 outputs (rounded to nearest even).
 constexpr int kCombineSlots = 16;
-template <bool kMixed, int kB>
+template <bool kMixed, int kB, typename OutT = float>
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ y, const int8_t* __restrict__ y_scale,
                                                        const int32_t* __restrict__ slot_row,
                                                        const float* __restrict__ w, int64_t T, int D, int k,
-                                                       float* __restrict__ out) {
+                                                       OutT* __restrict__ out) {
   constexpr int kF = kMixed ? 16 : 4;
   typedef float f32x4_t __attribute__((ext_vector_type(4)));
   typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
@@ -347,9 +348,21 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
       }
     }
   }
-  f32x4_t* o = reinterpret_cast<f32x4_t*>(out + t * D + d);
+  if constexpr (sizeof(OutT) == 4) {
+    f32x4_t* o = reinterpret_cast<f32x4_t*>(out + t * D + d);
 #pragma unroll
-  for (int c = 0; c < kF / 4; ++c) o[c] = f32x4_t{acc[4 * c], acc[4 * c + 1], acc[4 * c + 2], acc[4 * c + 3]};
+    for (int c = 0; c < kF / 4; ++c) o[c] = f32x4_t{acc[4 * c], acc[4 * c + 1], acc[4 * c + 2], acc[4 * c + 3]};
+  } else {
+    // kF bf16 values: 8 bytes (kF = 4) or 32 bytes (kF = 16), aligned since D % 32 == 0
+    uint32_t pk[kF / 2];
+#pragma unroll
+    for (int c = 0; c < kF / 2; ++c)
+      pk[c] = (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)acc[2 * c]) |
+              ((uint32_t)__builtin_bit_cast(uint16_t, (__bf16)acc[2 * c + 1]) << 16);
+    uint2* o = reinterpret_cast<uint2*>(out + t * D + d);
+#pragma unroll
+    for (int c = 0; c < kF / 4; ++c) o[c] = uint2{pk[2 * c], pk[2 * c + 1]};
+  }
 }
 
 }  // namespace
@@ -377,6 +390,19 @@ hipError_t launch_combine(const float* y, const int8_t* y_scale, bool mixed, con
   else
     hipLaunchKernelGGL((combine_kernel<false, kCombineSlots>), dim3((unsigned)blocks), dim3(256), 0, s, y, y_scale,
                        slot_row, w, T, D, k, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_combine_bf16(const float* y, const int8_t* y_scale, bool mixed, const int32_t* slot_row,
+                               const float* w, int64_t T, int D, int k, uint16_t* out, hipStream_t s) {
+  const int64_t n = T * (D / (mixed ? 16 : 4));
+  const int64_t blocks = (n + 255) / 256;
+  if (mixed)
+    hipLaunchKernelGGL((combine_kernel<true, 8, uint16_t>), dim3((unsigned)blocks), dim3(256), 0, s, y, y_scale,
+                       slot_row, w, T, D, k, out);
+  else
+    hipLaunchKernelGGL((combine_kernel<false, kCombineSlots, uint16_t>), dim3((unsigned)blocks), dim3(256), 0, s, y,
+                       y_scale, slot_row, w, T, D, k, out);
   return hipGetLastError();
 }
 

@@ -176,4 +176,60 @@ hipError_t launch_cache_fetch(const CacheFetchArgs& a, hipStream_t s);
 // Token-tile height the FFN uses for a batch of T tokens with k routed experts.
 int choose_rows_per_tile(int64_t T, int k, int E);
 
+// combine with a bf16 output (round to nearest even) instead of fp32.
+hipError_t launch_combine_bf16(const float* y, const int8_t* y_scale, bool mixed, const int32_t* slot_row,
+                               const float* w, int64_t T, int D, int k, uint16_t* out, hipStream_t s);
+
+// ---------------------------------------------------------------------------
+// Dense bf16 GEMMs of the latent-MoE block: P[split][t][n] = sum over the
+// split's K steps of A[t, k] * W[n, k] (fp32 accumulation).  N is made of up to
+// kDenseMaxSeg segments (each its own [rows, K] matrix, placed at a multiple
+// of kDenseSegAlign in P's row), K of up to 2 segments (each its own A and,
+// per N segment, its own W).  K segments are whole 64-wide steps.
+constexpr int kDenseMaxSeg = 4;
+constexpr int kDenseKStep = 64;
+constexpr int kDenseSegAlign = 128;
+struct DenseGemmArgs {
+  const uint16_t* a[2];  // bf16 [T, K_ks], row stride lda[ks] elements
+  int64_t lda[2];
+  int ksteps[2];  // K_ks / 64 (ksteps[1] = 0: one K segment)
+  int nseg;
+  int rows[kDenseMaxSeg];  // output features of segment s
+  int base[kDenseMaxSeg];  // offset of segment s in P's row (a multiple of kDenseSegAlign)
+  const uint16_t* w[kDenseMaxSeg][2];  // bf16 [rows, K_ks], row stride ldw[s][ks] elements
+  int64_t ldw[kDenseMaxSeg][2];
+  int64_t T;
+  int NV;           // P's row length (the last segment's end, rounded up to kDenseSegAlign)
+  int split_steps;  // K steps per split (the last split takes what is left)
+  int splits;
+  float* p;  // [splits][T][NV]
+};
+// Tokens up to which the weight-streaming kernel serves a product (each
+// 32-token chunk re-reads the weights); beyond, the 128 x 128 tile kernel.
+constexpr int64_t kDenseStreamMaxTokens = 64;
+// K steps per split of the streaming kernel (weights held in registers).
+constexpr int kDenseStreamSplitSteps = 7;
+hipError_t launch_dense_gemm(const DenseGemmArgs& a, hipStream_t s);
+// Splits the tile kernel uses for T tokens and NV features over `ksteps` steps.
+int dense_tile_splits(int64_t T, int NV, int ksteps);
+
+// Block epilogue after the first product (segments: gate logits [E], latent
+// [D], shared gate [Is], shared up [Is]): z fp32 [T, E]; xl bf16 [T, D] =
+// RMS-normed latent times gamma; s bf16 [T, Is] = SiLU(g) * u.
+struct BlockMidArgs {
+  const float* p;  // [splits][T][NV]
+  int splits, NV;
+  int64_t T;
+  int E, D, Is;
+  int base_z, base_d, base_g, base_u;
+  const uint16_t* gamma;  // bf16 [D]
+  float eps;
+  float* z;
+  uint16_t* xl;
+  uint16_t* s;
+};
+hipError_t launch_block_mid(const BlockMidArgs& a, hipStream_t s);
+// out[t][n] = sum over splits of p[split][t][n] (n < N, row length N).
+hipError_t launch_dense_sum(const float* p, int splits, int64_t T, int N, float* out, hipStream_t s);
+
 }  // namespace k3moe

@@ -27,7 +27,8 @@ def test_library_exports_every_declared_symbol(k3):
                           "moe_mxfp4_ffn_workspace_size", "moe_mxfp4_ffn", "moe_mxfp4_ffn_profiled",
                           "moe_mxfp4_ffn_noalloc", "moe_group_workspace_size", "moe_group_by_expert",
                           "moe_verify_width_distinct", "moe_verify_width_choose", "moe_expert_cache_state_size",
-                          "moe_expert_cache_init", "moe_expert_cache_route"}
+                          "moe_expert_cache_init", "moe_expert_cache_route", "moe_latent_block_workspace_size",
+                          "moe_latent_block", "moe_latent_block_profiled"}
     for n in names:
         assert hasattr(k3.lib, n), n
 
@@ -242,3 +243,40 @@ def test_expert_cache_checks(k3):
     assert r(st=(A, None, A)) == ERR_NULL and r(ca=(A, A, None)) == ERR_NULL
     assert r(state=A + 4) == ERR_ALIGN and r(st=(A + 8, A, A)) == ERR_ALIGN and r(ca=(A, A + 2, A)) == ERR_ALIGN
     assert r(nbytes=need - 1) == ERR_WORKSPACE
+
+
+K3_BLOCK = dict(H=7168, D=3584, I=3072, Is=3072, E=896, k=16)
+
+
+def test_latent_block_workspace_size(k3):
+    ws = k3.moe_latent_block_workspace_size
+    assert ws(0, **K3_BLOCK) == 0
+    assert ws(8, 7000, 3584, 3072, 3072, 896, 16) == 0  # H not a multiple of 128
+    assert ws(8, 7168, 3584, 3072, 3000, 896, 16) == 0  # Is not a multiple of 64
+    assert ws(8, 7168, 3584, 3072, 3072, 8, 16) == 0    # k > E
+    for T in (1, 8, 64, 65, 128, 4096):
+        n = ws(T, **K3_BLOCK)
+        # at least the FFN's own workspace and the block's activations
+        assert n >= k3.moe_mxfp4_ffn_workspace_size(T, 3584, 3072, 896, 16) + T * (896 * 4 + 3584 * 4 + 3072 * 2)
+    # the first product's partials (16 splits of 7 steps at decode, fp32 rows of
+    # 896 + 3584 + 3072 + 3072 features) fit the shared region
+    assert ws(1, **K3_BLOCK) >= 16 * 10624 * 4
+
+
+def test_latent_block_checks(k3):
+    f = k3.lib.moe_latent_block
+    need = k3.moe_latent_block_workspace_size(8, **K3_BLOCK)
+
+    def call(T=8, H=7168, D=3584, I=3072, Is=3072, E=896, k=16, eps=1e-6, ptr=A, out=A, ws=A, nbytes=need,
+             bias=None, ids=None):
+        return f(ptr, ptr, bias, ptr, ptr, ptr, ptr, ptr, ptr, ptr, ptr, ptr, T, H, D, I, Is, E, k, 1, 1.0, eps, out,
+                 ids, None, ws, nbytes, None)
+
+    assert call(T=0, ptr=None, out=None, ws=None) == OK
+    assert call(T=-1) == ERR_SHAPE and call(H=7040 + 64) == ERR_SHAPE and call(D=3584 + 32) == ERR_SHAPE
+    assert call(Is=3072 + 32) == ERR_SHAPE and call(I=3072 + 16) == ERR_SHAPE and call(k=0) == ERR_SHAPE
+    assert call(E=8, k=16) == ERR_SHAPE and call(k=65, E=896) == ERR_SHAPE and call(E=8193) == ERR_SHAPE
+    assert call(eps=-1.0) == ERR_SHAPE and call(eps=float("nan")) == ERR_SHAPE and call(H=65536 + 128) == ERR_SHAPE
+    assert call(ptr=None) == ERR_NULL and call(out=None) == ERR_NULL and call(ws=None) == ERR_NULL
+    assert call(ptr=A + 2) == ERR_ALIGN and call(bias=A + 4) == ERR_ALIGN and call(ids=A + 8) == ERR_ALIGN
+    assert call(nbytes=need - 1) == ERR_WORKSPACE
