@@ -105,6 +105,8 @@ def parse_args():
                     help="timed steps (0: as many as fill about 0.5 s, 20 to 5000)")
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="prefill", choices=["prefill", "verify", "decode-t8", "decode-t1", "tiny"])
+    ap.add_argument("--block", default=None, choices=[b[0] for b in BLOCK_SIZES],
+                    help="measure only the latent-MoE block at this size (prints its result line)")
     ap.add_argument("--rotate", type=int, default=0, help="distinct seeded batches cycled (0: 8 for decode, 4 else)")
     ap.add_argument("--no-extra", dest="extra", action="store_false", default=True,
                     help="measure only the headline workload")
@@ -517,6 +519,128 @@ def measure_verify_width(dev, k3, warmup, reps=100):
     }
 
 
+BLOCK_SIZES = (("decode-t1", "block-decode-t1", 1), ("decode-t8", "block-decode-t8", 8),
+               ("t128", "block-prefill", 128), ("prefill", "block-prefill", 4096))
+
+
+def block_dense_work(launch, T, E, D, Is, H):
+    """Algorithmic (flops, bytes) of one dense product launch of the block:
+    weights once, inputs once, fp32 outputs once."""
+    if launch == "dense1":
+        n = E + D + 2 * Is
+        return 2.0 * T * n * H, 2.0 * n * H + 2.0 * T * H + 4.0 * T * n
+    n = D + Is
+    return 2.0 * T * H * n, 2.0 * H * n + 2.0 * T * n + 4.0 * T * H
+
+
+def measure_block(label, cfg, dense, dev, k3, warmup, rotate=4, steps=0):
+    """The latent-MoE block (moe_latent_block) at cfg's size on resident
+    weights: graph-replayed steps over `rotate` seeded hidden batches, a
+    stage split from the profiled entry point's events, and the roofline of
+    both dense products (event pairs right around each launch, minus the mean
+    interval of an empty event pair)."""
+    import numpy as np
+    import torch
+
+    import moe_inputs
+
+    L = cfg.layer
+    T, H, D, I, Is, E, k = L.T, cfg.H, L.D, L.I, cfg.Is, L.E, L.k
+    hs = [torch.from_numpy(moe_inputs.block_hidden(cfg, seed=s).view(np.int16)).view(torch.bfloat16).cuda()
+          for s in range(rotate)]
+    bias = torch.from_numpy(moe_inputs.block_bias(cfg)).cuda()
+    ws = torch.empty(k3.moe_latent_block_workspace_size(T, H, D, I, Is, E, k), dtype=torch.uint8, device="cuda")
+    out = torch.empty((T, H), dtype=torch.float32, device="cuda")
+    d = dense
+
+    def step(i, events=None):
+        k3.moe_latent_block(hs[i % rotate], d["Wg"], bias, d["Wd"], d["gamma"], dev.w1, dev.w3, dev.w2, d["Wu"],
+                            d["Ws1"], d["Ws3"], d["Ws2"], k, eps=cfg.eps, out=out, workspace=ws, stage_events=events)
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    n_ev = 50
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(k3.BLOCK_STAGE_EVENTS)] for _ in range(n_ev)]
+    pair = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_ev)]
+    torch.cuda._sleep(int(2e7))
+    for i in range(n_ev):
+        step(i, evs[i])
+        pair[i][0].record()
+        pair[i][1].record()
+    torch.cuda.synchronize()
+    stage = {s: float(np.mean([evs[i][n].elapsed_time(evs[i][n + 1]) for i in range(n_ev)]))
+             for n, s in enumerate(k3.BLOCK_STAGES)}
+    pair_ms = float(np.mean([a.elapsed_time(b) for a, b in pair]))
+    if steps <= 0:
+        steps = int(min(5000, max(20, round(0.5 / max(sum(stage.values()) * 1e-3, 1e-6)))))
+    graphs = []
+    for j in range(rotate):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step(j)
+        graphs.append(g)
+    for g in graphs:
+        g.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        graphs[i % rotate].replay()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    kname = "dense_stream_kernel" if T <= 64 else "dense_tile_kernel"
+    roof = {}
+    for launch in ("dense1", "dense2"):
+        kname_l = f"{kname}<{launch[-1]}>"
+        flops, byts = block_dense_work(launch, T, E, D, Is, H)
+        ms = stage[launch] - pair_ms
+        bound = "mfma" if flops / byts > RIDGE else "hbm"
+        if bound == "mfma":
+            ach, peak, unit = flops / (ms * 1e-3) / 1e12, PEAK_BF16_TFLOPS, "TFLOP/s"
+        else:
+            ach, peak, unit = byts / (ms * 1e-3) / 1e9, PEAK_HBM_GBS, "GB/s"
+        roof[launch] = {"kernel": kname_l, "bound": bound, "achieved": ach, "peak": peak, "unit": unit,
+                        "frac": ach / peak, "algorithmic_flops_per_launch": flops,
+                        "algorithmic_bytes_per_launch": byts, "avg_launch_ms": ms,
+                        "avg_launch_ms_raw_events": stage[launch], "event_pair_overhead_ms": pair_ms}
+    step_s = elapsed / steps
+    dense_bytes = 2.0 * H * (E + D + 2 * Is) + 2.0 * H * (D + Is)
+    return {
+        "workload": label,
+        "tokens": T,
+        "shape": {"hidden": H, "latent": D, "expert_intermediate": I, "shared_intermediate": Is, "experts": E,
+                  "top_k": k},
+        "steps": steps,
+        "ms_per_step": step_s * 1e3,
+        "tokens_per_s": T / step_s,
+        "timing": "graph replay of moe_latent_block, one captured graph per rotated hidden batch",
+        "stages_ms": stage,
+        "dense_weight_bytes": dense_bytes,
+        "step_dense_GBps": dense_bytes / step_s / 1e9,
+        "roofline": roof,
+    }
+
+
+def measure_blocks(dev, k3, warmup, only=None):
+    """Every block size (or only the one named) on one set of dense weights."""
+    import numpy as np
+    import torch
+
+    import moe_inputs
+
+    base = moe_inputs.BLOCK_DECODE8
+    host = moe_inputs.block_dense_weights(base)
+    dense = {n: torch.from_numpy(v.view(np.int16)).view(torch.bfloat16).cuda() for n, v in host.items()}
+    res = {}
+    for label, name, T in BLOCK_SIZES:
+        if only is not None and label != only:
+            continue
+        cfg = moe_inputs.BLOCK_CONFIGS[name]
+        cfg = cfg.with_(layer=cfg.layer.with_(T=T))
+        res[label] = measure_block(label, cfg, dense, dev, k3, warmup, rotate=8 if T <= 8 else 4)
+    return res
+
+
 HOST_LINK_PEAK_GBS = 63.0  # PCIe 5.0 x16, one direction: 32 GT/s x 16 lanes x 128/130 / 8
 
 
@@ -627,6 +751,13 @@ def main():
     from moe_inputs.device import upload_experts
 
     torch.cuda.set_device(0)
+    if args.block is not None:
+        dev = upload_experts(moe_inputs.PREFILL, lambda p, s, out: k3.mxfp4_repack(p, s, blocks=out))
+        r = measure_blocks(dev, k3, args.warmup, only=args.block)[args.block]
+        print(json.dumps({"metric": "latent-MoE block tokens/s at K3 shape", "value": r["tokens_per_s"],
+                          "unit": "tokens/s", "n_gpus": 1, "higher_is_better": True, "data": "synthetic",
+                          "latent_block": r}), flush=True)
+        return
     cfg = moe_inputs.CONFIGS[args.workload]
     t_setup = time.perf_counter()
     dev = upload_experts(cfg, lambda p, s, out: k3.mxfp4_repack(p, s, blocks=out))
@@ -666,6 +797,7 @@ def main():
         result["workloads"] = extra
         result["verify_width"] = measure_verify_width(dev, k3, args.warmup)
         result["expert_cache"] = measure_expert_cache(dev, k3, args.warmup)
+        result["latent_block"] = measure_blocks(dev, k3, args.warmup)
     if args.cpu_baseline:
         sample = args.cpu_sample_tokens or (cfg.T if cfg.T <= 64 else 2)
         result["cpu_baseline"] = cpu_baseline(cfg, batch0, sample)

@@ -454,7 +454,7 @@ int moe_expert_cache_route(void* state, size_t state_bytes, int32_t E, int32_t C
  * `stream` only (the routed FFN may fork to its side stream and joins back);
  * nothing synchronizes with the host; capturable in a graph.
  */
-#define K3MOE_BLOCK_STAGE_EVENTS 6
+#define K3MOE_BLOCK_STAGE_EVENTS 7
 size_t moe_latent_block_workspace_size(int64_t T, int32_t H, int32_t D, int32_t I, int32_t Is, int32_t E, int32_t k);
 int moe_latent_block(const void* h_bf16, const void* wg, const float* bias, const void* wd, const void* gamma,
                      const uint8_t* w1, const uint8_t* w3, const uint8_t* w2, const void* wu, const void* ws1,
@@ -465,8 +465,8 @@ int moe_latent_block(const void* h_bf16, const void* wg, const float* bias, cons
    used) and, when `events` is not NULL, K3MOE_BLOCK_STAGE_EVENTS caller-owned
    hipEvent_t recorded on `stream` before the first product, the epilogue
    after it (logits, latent norm, shared h), the routing, the routed FFN, the
-   second product (with its split sum) and after the last launch (NULL
-   entries are skipped). */
+   second product, the sum of its split-K partials (no launch when it has one
+   split) and after the last launch (NULL entries are skipped). */
 int moe_latent_block_profiled(const void* h_bf16, const void* wg, const float* bias, const void* wd, const void* gamma,
                               const uint8_t* w1, const uint8_t* w3, const uint8_t* w2, const void* wu,
                               const void* ws1, const void* ws3, const void* ws2, int64_t T, int32_t H, int32_t D,

@@ -99,9 +99,9 @@ lib.moe_latent_block.restype = ctypes.c_int
 lib.moe_latent_block.argtypes = _block_args
 lib.moe_latent_block_profiled.restype = ctypes.c_int
 lib.moe_latent_block_profiled.argtypes = _block_args + [ctypes.POINTER(ctypes.c_void_p)]
-BLOCK_STAGE_EVENTS = 6
+BLOCK_STAGE_EVENTS = 7
 # launches between consecutive events of moe_latent_block_profiled
-BLOCK_STAGES = ("dense1", "mid", "route", "ffn", "dense2")
+BLOCK_STAGES = ("dense1", "mid", "route", "ffn", "dense2", "sum")
 FFN_STAGE_EVENTS = 7
 # launches between consecutive events of moe_mxfp4_ffn_profiled
 FFN_STAGES = ("group", "gate_up", "gate_up_stream", "down", "down_stream", "combine")

@@ -597,14 +597,14 @@ struct BlockPlan {
   int base_z, base_d, base_g, base_u, NV1;  // first product's segments (virtual feature offsets)
   int ksteps1, split1_steps, splits1;
   int ksteps2, split2_steps, splits2;
-  size_t z, xl, s, ids, w, yl, region, total;  // workspace offsets (256-aligned); region: products' partials and
+  size_t z, xl, s, ids, w, yl, dbuf, ssq, region, total;  // workspace offsets (256-aligned); region: products' partials and
                                                // the FFN's workspace, which never live at the same time
 };
 
 static int dense_split_steps(int64_t T, int NV, int ksteps, int* splits) {
   int steps;
   if (T <= kDenseStreamMaxTokens) {
-    steps = kDenseStreamSplitSteps;
+    steps = ksteps;  // the streaming kernel splits K among its own waves
   } else {
     const int n = dense_tile_splits(T, NV, ksteps);
     steps = (ksteps + n - 1) / n;
@@ -637,6 +637,8 @@ static BlockPlan block_plan(int64_t T, int32_t H, int32_t D, int32_t I, int32_t 
   P.ids = take((size_t)T * k * 4);
   P.w = take((size_t)T * k * 4);
   P.yl = take((size_t)T * D * 2);
+  P.dbuf = take((size_t)T * D * 4);
+  P.ssq = take((size_t)T * block_mid_blocks(E, D, Is) * 4);
   size_t region = (size_t)P.splits1 * T * P.NV1 * 4;
   if (P.splits2 > 1 && (size_t)P.splits2 * T * H * 4 > region) region = (size_t)P.splits2 * T * H * 4;
   const size_t ffn = moe_mxfp4_ffn_workspace_size(T, D, I, E, k);
@@ -712,7 +714,7 @@ int moe_latent_block_profiled(const void* h_bf16, const void* wg, const float* b
   g1.split_steps = P.split1_steps;
   g1.splits = P.splits1;
   g1.p = region;
-  if (!mark(0) || launch_dense_gemm(g1, s) != hipSuccess) return K3MOE_ERR_DEVICE;
+  if (!mark(0) || launch_dense_gemm(g1, 1, s) != hipSuccess) return K3MOE_ERR_DEVICE;
 
   BlockMidArgs m{};
   m.p = region;
@@ -731,6 +733,10 @@ int moe_latent_block_profiled(const void* h_bf16, const void* wg, const float* b
   m.z = z;
   m.xl = xl;
   m.s = sh;
+  m.dbuf = reinterpret_cast<float*>(ws + P.dbuf);
+  m.ssq = reinterpret_cast<float*>(ws + P.ssq);
+  m.nblk = block_mid_blocks(E, D, Is);
+  m.tok_per_wg = T >= 512 ? 8 : 1;
   if (!mark(1) || launch_block_mid(m, s) != hipSuccess) return K3MOE_ERR_DEVICE;
   if (!mark(2) || launch_route_topk(z, bias, T, E, k, normalize, route_scale, ids, wts, s) != hipSuccess)
     return K3MOE_ERR_DEVICE;
@@ -759,9 +765,9 @@ int moe_latent_block_profiled(const void* h_bf16, const void* wg, const float* b
   g2.split_steps = P.split2_steps;
   g2.splits = P.splits2;
   g2.p = P.splits2 == 1 ? out : region;
-  if (!mark(4) || launch_dense_gemm(g2, s) != hipSuccess) return K3MOE_ERR_DEVICE;
+  if (!mark(4) || launch_dense_gemm(g2, 2, s) != hipSuccess || !mark(5)) return K3MOE_ERR_DEVICE;
   if (P.splits2 > 1 && launch_dense_sum(region, P.splits2, T, H, out, s) != hipSuccess) return K3MOE_ERR_DEVICE;
-  if (!mark(5)) return K3MOE_ERR_DEVICE;
+  if (!mark(6)) return K3MOE_ERR_DEVICE;
   return K3MOE_OK;
 }
 

@@ -14,7 +14,7 @@
 //                   down matrix) — the block output is their sum.
 //
 // Two kernels:
-//   tile kernel   (more than 64 tokens): 128 tokens x 128 features per
+//   tile kernel   (more than 16 tokens): 128 tokens x 128 features per
 //                 workgroup of 4 waves (64 x 64 each: 2 x 2 MFMA 32x32x16
 //                 bf16 blocks), K in steps of 64 double-buffered in LDS and
 //                 filled by direct global -> LDS buffer loads; the eight
@@ -24,13 +24,13 @@
 //                 contiguous runs of a grouped order (8 feature tiles x every
 //                 token tile), so tiles that share operands share an L2.
 //                 Split-K when the tiles alone cannot fill the GPU.
-//   stream kernel (up to 64 tokens): bound by the weight stream.  128
-//                 features x 32 tokens x up to 7 K steps per workgroup; each
-//                 wave loads its 32 weight rows for all its steps straight
-//                 into registers (64 contiguous bytes per lane and step, all in
-//                 flight at once), the split's 32 token rows are staged in LDS.
-// Splits write partial sums that the consumer adds in split order, so every
-// result is deterministic.
+//   stream kernel (up to 16 tokens): bound by the weight stream.  16 features
+//                 x 16 tokens x all of K per workgroup, each wave streaming a
+//                 contiguous quarter of the 16 weight rows through its own
+//                 4-stage LDS ring (3 K steps in flight), the quarters added
+//                 through LDS in wave order.
+// Splits of the tile kernel write partial sums that the consumer adds in
+// split order, so every result is deterministic.
 #include "k3moe_internal.h"
 
 #include <math.h>
@@ -47,7 +47,7 @@ constexpr int kThreads = 256;
 constexpr int kTile = 128;              // tokens and features of a tile-kernel workgroup
 constexpr int kRowB = 2 * kDenseKStep;  // bytes of one K step of a bf16 row (128)
 constexpr int kOpB = kTile * kRowB;     // bytes of one operand tile per stage (16 KB)
-constexpr int kStreamTok = 32;          // token rows of a stream-kernel workgroup
+constexpr int kStreamRows = 16;         // features and tokens of a stream-kernel workgroup
 constexpr int kXcds = 8;
 constexpr int kTargetGroups = 512;      // workgroups that fill the GPU (2 per CU)
 
@@ -59,14 +59,23 @@ __device__ __forceinline__ int64_t xcd_order(int64_t i, int64_t total) {
   return x * q + (x < r ? x : r) + j;
 }
 
-// N segment of the tile starting at virtual feature n0 (segments start at
-// multiples of the tile width, so a tile never straddles two).
-__device__ __forceinline__ int seg_of(const DenseGemmArgs& a, int n0) {
-  int s = 0;
+// The N segment holding the tile that starts at virtual feature n0
+// (segments start at multiples of the tile width, so a tile never straddles
+// two).  Fields are picked with constant indices, so they stay in scalar
+// registers (an index computed at run time would send the argument struct to
+// memory and load it with vector loads, whose waits also drain the weight
+// loads in flight).
+struct SegView {
+  const uint16_t* w[2];
+  int64_t ldw[2];
+  int rows, base;
+};
+__device__ __forceinline__ SegView seg_view(const DenseGemmArgs& a, int n0) {
+  SegView v{{a.w[0][0], a.w[0][1]}, {a.ldw[0][0], a.ldw[0][1]}, a.rows[0], a.base[0]};
 #pragma unroll
   for (int i = 1; i < kDenseMaxSeg; ++i)
-    if (i < a.nseg && n0 >= a.base[i]) s = i;
-  return s;
+    if (i < a.nseg && n0 >= a.base[i]) v = SegView{{a.w[i][0], a.w[i][1]}, {a.ldw[i][0], a.ldw[i][1]}, a.rows[i], a.base[i]};
+  return v;
 }
 
 __device__ __forceinline__ uint16_t bf16_bits(float v) { return __builtin_bit_cast(uint16_t, (__bf16)v); }
@@ -85,9 +94,12 @@ __device__ __forceinline__ void store4(float* dst, const f32x16_t& acc, int q, i
   }
 }
 
+// kProduct (1 or 2) only names the block's first or second product, so that
+// profiles list the two separately.
+template <int kProduct>
 __global__ __launch_bounds__(kThreads, 2) void dense_tile_kernel(DenseGemmArgs a) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[2][2 * kOpB];  // [buffer][weights | tokens]
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int nT = a.NV / kTile;
   const int64_t tT = (a.T + kTile - 1) / kTile;
   const int64_t tiles = (int64_t)nT * tT;
@@ -103,9 +115,9 @@ __global__ __launch_bounds__(kThreads, 2) void dense_tile_kernel(DenseGemmArgs a
   const int nt = 8 * grp + (int)(r - tt * gn);
 
   const int n0 = nt * kTile;
-  const int s = seg_of(a, n0);
-  const int f0 = n0 - a.base[s];
-  const int frows = a.rows[s] - f0 < kTile ? a.rows[s] - f0 : kTile;  // >= 1
+  const SegView sv = seg_view(a, n0);
+  const int f0 = n0 - sv.base;
+  const int frows = sv.rows - f0 < kTile ? sv.rows - f0 : kTile;  // >= 1
   const int64_t t0 = tt * kTile;
   const int trows = a.T - t0 < kTile ? (int)(a.T - t0) : kTile;
   const int ktot = a.ksteps[0] + a.ksteps[1];
@@ -121,19 +133,19 @@ __global__ __launch_bounds__(kThreads, 2) void dense_tile_kernel(DenseGemmArgs a
   for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      woff[ks][j] = (uint32_t)((lrow + 8 * j) * a.ldw[s][ks] * 2 + 16 * lchunk);
+      woff[ks][j] = (uint32_t)((lrow + 8 * j) * sv.ldw[ks] * 2 + 16 * lchunk);
       aoff[ks][j] = (uint32_t)((lrow + 8 * j) * a.lda[ks] * 2 + 16 * lchunk);
     }
 
   auto issue = [&](int k, int buf) {
     const int ks = k < a.ksteps[0] ? 0 : 1;
     const int kin = k - (ks ? a.ksteps[0] : 0);
-    const uint16_t* wb = a.w[s][ks] + (int64_t)f0 * a.ldw[s][ks];
-    const uint16_t* ab = a.a[ks] + t0 * a.lda[ks];
-    const __amdgpu_buffer_rsrc_t wr =
-        __builtin_amdgcn_make_buffer_rsrc((void*)wb, 0, (int)(frows * a.ldw[s][ks] * 2), 0x00020000);
+    const uint16_t* wb = (ks ? sv.w[1] : sv.w[0]) + (int64_t)f0 * (ks ? sv.ldw[1] : sv.ldw[0]);
+    const uint16_t* ab = (ks ? a.a[1] : a.a[0]) + t0 * (ks ? a.lda[1] : a.lda[0]);
+    const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)wb, 0, (int)(frows * (ks ? sv.ldw[1] : sv.ldw[0]) * 2), 0x00020000);
     const __amdgpu_buffer_rsrc_t ar =
-        __builtin_amdgcn_make_buffer_rsrc((void*)ab, 0, (int)(trows * a.lda[ks] * 2), 0x00020000);
+        __builtin_amdgcn_make_buffer_rsrc((void*)ab, 0, (int)(trows * (ks ? a.lda[1] : a.lda[0]) * 2), 0x00020000);
     uint8_t* lb = lds[buf];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -203,117 +215,202 @@ __global__ __launch_bounds__(kThreads, 2) void dense_tile_kernel(DenseGemmArgs a
   }
 }
 
-__global__ __launch_bounds__(kThreads) void dense_stream_kernel(DenseGemmArgs a) {
-  constexpr int kSteps = kDenseStreamSplitSteps;
-  __shared__ __attribute__((aligned(16))) uint8_t xs[kSteps][kStreamTok * kRowB];  // 28 KB
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int hb = lane >> 5, l32 = lane & 31;
-  const int nT = a.NV / kTile;
-  const int nt = blockIdx.x % nT;
-  const int split = blockIdx.x / nT;
-  const int n0 = nt * kTile;
-  const int s = seg_of(a, n0);
-  const int f0 = n0 - a.base[s];
-  const int frows = a.rows[s] - f0 < kTile ? a.rows[s] - f0 : kTile;
-  const int64_t t0 = (int64_t)blockIdx.y * kStreamTok;
-  const int trows = a.T - t0 < kStreamTok ? (int)(a.T - t0) : kStreamTok;
+// A step's operands for one lane: weight and token chunks at LDS byte
+// addresses a0 and a1 (tokens 2 KB further).  The reads and their wait are one
+// asm block: written as plain loads, the compiler would order them behind
+// every global -> LDS load in flight and empty the ring each step.
+__device__ __forceinline__ void read_step(uint32_t a0, uint32_t a1, bf16x8_t& w0, bf16x8_t& x0, bf16x8_t& w1,
+                                          bf16x8_t& x1) {
+  asm volatile(
+      "ds_read_b128 %0, %4\n\tds_read_b128 %1, %4 offset:2048\n\t"
+      "ds_read_b128 %2, %5\n\tds_read_b128 %3, %5 offset:2048\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(w0), "=&v"(x0), "=&v"(w1), "=&v"(x1)
+      : "v"(a0), "v"(a1)
+      : "memory");
+}
+
+// Weight-streaming product for up to 16 tokens.  A workgroup owns 16 features
+// of one segment (the rows of MFMA 16x16x32 blocks) and every token; its 4
+// waves take a quarter of K each, so each wave streams a contiguous quarter of
+// its 16 weight rows.  Every wave has its own ring of kRing stages in LDS (one
+// 64-wide K step: 16 weight rows and 16 token rows of 128 bytes, chunks
+// XOR-swizzled by row) filled by direct global -> LDS loads, and waits for a
+// stage with an explicit count of the loads issued after it, so kRing - 1
+// steps stay in flight (no barrier in the loop).  Rows past the edge re-read
+// the last valid row (their outputs are never stored); the tail re-reads its
+// last step, so every stage has the same 4 loads.  The two MFMAs of a step
+// take chunks 2g and 2g + 1 for lane group g (the same K order on both
+// operands).  The quarters are added in wave order through LDS.
+template <int kProduct>
+__global__ __launch_bounds__(kThreads, 2) void dense_stream_kernel(DenseGemmArgs a) {
+  constexpr int kRing = 4;
+  constexpr int kStageB = 2 * kStreamRows * kRowB;  // 4 KB: weights, then tokens
+  __shared__ __attribute__((aligned(16))) uint8_t ring[4][kRing][kStageB];
+  __shared__ f32x4_t red[4][64];
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g = lane >> 4, l16 = lane & 15;
+  const int n0 = blockIdx.x * kStreamRows;
+  const SegView sv = seg_view(a, n0);
+  const int f0 = n0 - sv.base;
+  const int frows = sv.rows - f0 < kStreamRows ? sv.rows - f0 : kStreamRows;
+  if (frows <= 0) return;  // a tile in the padding after a segment (uniform over the workgroup)
+  const int64_t t0 = (int64_t)blockIdx.y * kStreamRows;
+  const int trows = a.T - t0 < kStreamRows ? (int)(a.T - t0) : kStreamRows;
   const int ktot = a.ksteps[0] + a.ksteps[1];
-  const int kbeg = split * a.split_steps;
-  const int nsteps = (kbeg + a.split_steps < ktot ? kbeg + a.split_steps : ktot) - kbeg;  // 1..kSteps
+  const int per = (ktot + 3) / 4;
+  const int kbeg = wave * per;
+  const int nst = (kbeg + per < ktot ? kbeg + per : ktot) - kbeg;  // may be <= 0 for the last wave
+  const int last = nst > 0 ? nst - 1 : 0;
 
-  // token rows: wave w fills rows 8w .. 8w+7 of every step (rows past the
-  // last token keep stale data, which only reaches outputs never stored)
-  const int xrow = 8 * wave + (lane >> 3);
-  const int xchunk = (lane & 7) ^ (lane >> 3);
-  if (8 * wave < trows) {
+  // load j (0, 1) of an operand moves rows 8j .. 8j+7: lane -> row 8j + lane/8,
+  // the chunk that lands at position lane % 8
+  const int chunk = (lane & 7) ^ (lane >> 3);
+  uint32_t woff[2][2], xoff[2][2];
 #pragma unroll
-    for (int i = 0; i < kSteps; ++i) {
-      if (i >= nsteps) break;
-      const int k = kbeg + i;
-      const int ks = k < a.ksteps[0] ? 0 : 1;
-      const int kin = k - (ks ? a.ksteps[0] : 0);
-      const uint16_t* ab = a.a[ks] + t0 * a.lda[ks];
-      const __amdgpu_buffer_rsrc_t ar =
-          __builtin_amdgcn_make_buffer_rsrc((void*)ab, 0, (int)(trows * a.lda[ks] * 2), 0x00020000);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(ar, xs[i] + 8 * wave * kRowB, 16,
-                                               (uint32_t)(xrow * a.lda[ks] * 2 + 16 * xchunk), kin * kRowB, 0, 0);
+  for (int j = 0; j < 2; ++j) {
+    const int r = 8 * j + (lane >> 3);
+    const int wr = r < frows ? r : frows - 1, xr = r < trows ? r : trows - 1;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      woff[ks][j] = (uint32_t)(wr * sv.ldw[ks] * 2 + 16 * chunk);
+      xoff[ks][j] = (uint32_t)(xr * a.lda[ks] * 2 + 16 * chunk);
     }
   }
-  // weights: lane (row l32 of the wave's 32, half hb) takes bytes 64*hb ..
-  // 64*hb + 63 of every step of its row; all steps are loaded up front
-  const int frow = 32 * wave + l32;
-  const bool wvalid = frow < frows;
-  u32x4_t wv[kSteps][4];
+  // buffer resources of both K segments (built once)
+  const __amdgpu_buffer_rsrc_t wrs0 = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(sv.w[0] + (int64_t)f0 * sv.ldw[0]), 0, (int)(frows * sv.ldw[0] * 2), 0x00020000);
+  const __amdgpu_buffer_rsrc_t wrs1 = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(sv.w[1] + (int64_t)f0 * sv.ldw[1]), 0, (int)(frows * sv.ldw[1] * 2), 0x00020000);
+  const __amdgpu_buffer_rsrc_t xrs0 = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(a.a[0] + t0 * a.lda[0]), 0, (int)(trows * a.lda[0] * 2), 0x00020000);
+  const __amdgpu_buffer_rsrc_t xrs1 = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(a.a[1] + t0 * a.lda[1]), 0, (int)(trows * a.lda[1] * 2), 0x00020000);
+  const int ks0 = a.ksteps[0];
+  auto issue = [&](int i) {
+    const int k = kbeg + (i < last ? i : last);
+    const int ks = k < ks0 ? 0 : 1;
+    const int kin = k - (ks ? ks0 : 0);
+    const __amdgpu_buffer_rsrc_t wr = ks ? wrs1 : wrs0;
+    const __amdgpu_buffer_rsrc_t xr = ks ? xrs1 : xrs0;
+    uint8_t* st = ring[wave][i & (kRing - 1)];
 #pragma unroll
-  for (int i = 0; i < kSteps; ++i) {
-    const int k = kbeg + i;
-    const int ks = k < a.ksteps[0] ? 0 : 1;
-    const int kin = k - (ks ? a.ksteps[0] : 0);
-    const u32x4_t* src = reinterpret_cast<const u32x4_t*>(a.w[s][ks] + (int64_t)(f0 + frow) * a.ldw[s][ks] +
-                                                          kin * kDenseKStep + 32 * hb);
+    for (int j = 0; j < 2; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, st + 8 * j * kRowB, 16, ks ? woff[1][j] : woff[0][j], kin * kRowB,
+                                               0, 0);
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) wv[i][kk] = (wvalid && i < nsteps) ? __builtin_nontemporal_load(src + kk) : u32x4_t{};
+    for (int j = 0; j < 2; ++j)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, st + (kStreamRows + 8 * j) * kRowB, 16,
+                                               ks ? xoff[1][j] : xoff[0][j], kin * kRowB, 0, 0);
+  };
+
+  // operand offsets in a stage: row l16, chunks 2g and 2g + 1
+  const uint32_t op0 = (uint32_t)swz(l16, 2 * g), op1 = (uint32_t)swz(l16, 2 * g + 1);
+  static_assert(kStreamRows * kRowB == 2048, "token rows start 2 KB into a stage");
+  f32x4_t acc = f32x4_t{};
+  if (nst > 0) {
+#pragma unroll
+    for (int i = 0; i < kRing; ++i) issue(i);
+    for (int i = 0; i < nst; ++i) {
+      // stage i has landed once at most the (kRing - 1) later stages' 4 loads each are in flight
+      asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
+      const uint32_t st = (uint32_t)(uintptr_t)ring[wave][i & (kRing - 1)];
+      bf16x8_t w0, x0, w1, x1;
+      read_step(st + op0, st + op1, w0, x0, w1, x1);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w0, x0, acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(w1, x1, acc, 0, 0, 0);
+      issue(i + kRing);
+    }
+    // no load may still be landing in this workgroup's LDS when it exits
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   }
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  static_assert(kRing == 4, "the wait count above assumes 3 later stages of 4 loads");
+  red[wave][lane] = acc;
   __syncthreads();
-
-  // MFMA rows = the wave's 32 features, columns = the 32 tokens; the K order
-  // inside a step is permuted the same way on both operands (substep kk of
-  // half hb is chunk 4*hb + kk)
-  f32x16_t acc = f32x16_t{};
-  if (32 * wave < frows) {
+  if (wave != 0) return;
+  const f32x4_t sum = ((red[0][lane] + red[1][lane]) + red[2][lane]) + red[3][lane];
+  // lane holds token l16, features 4g .. 4g+3
+  const int f = 4 * g;
+  if (l16 < trows && f < frows) {
+    float* dst = a.p + (t0 + l16) * a.NV + n0 + f;
+    if (frows - f >= 4) {
+      *reinterpret_cast<f32x4_t*>(dst) = sum;
+    } else {
 #pragma unroll
-    for (int i = 0; i < kSteps; ++i) {
-      if (i >= nsteps) break;
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) {
-        const bf16x8_t xo = *reinterpret_cast<const bf16x8_t*>(xs[i] + swz(l32, 4 * hb + kk));
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, wv[i][kk]), xo, acc, 0, 0, 0);
-      }
-    }
-    if (l32 < trows) {
-      float* prow = a.p + ((int64_t)split * a.T + t0 + l32) * a.NV + n0;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int f = 32 * wave + 8 * q + 4 * hb;
-        if (f < frows) store4(prow + f, acc, q, frows - f);
-      }
+      for (int u = 0; u < 4; ++u)
+        if (u < frows - f) dst[u] = sum[u];
     }
   }
 }
 
-// One workgroup per token: logits, RMS-normed latent, shared-expert h.
-__global__ __launch_bounds__(kThreads) void block_mid_kernel(BlockMidArgs a) {
-  __shared__ float red[kThreads / 64];
+// Block epilogue, first half: one thread per column of the logits, the latent
+// and the shared expert, for a.tok_per_wg consecutive tokens (1 for small
+// batches, so they spread over more workgroups).  Sums the split partials;
+// writes z, the raw latent d (fp32) and the shared expert's h; each workgroup
+// also writes, per token, the sum of squares of its latent columns (0 if it
+// has none).
+constexpr int kMidTok = 8;  // most tokens per workgroup
+__global__ __launch_bounds__(kThreads) void block_cols_kernel(BlockMidArgs a) {
+  __shared__ float red[kMidTok][kThreads / 64];
   const int tid = threadIdx.x;
-  const int64_t t = blockIdx.x;
-  const float* row = a.p + t * a.NV;
+  const int c = blockIdx.y * kThreads + tid;  // column blocks on y (a few hundred at most), token chunks on x
   const int64_t sstride = a.T * a.NV;
-  auto col = [&](int c) {
-    float v = 0.0f;
-    for (int sp = 0; sp < a.splits; ++sp) v += row[sp * sstride + c];
-    return v;
-  };
-  for (int e = tid; e < a.E; e += kThreads) a.z[t * a.E + e] = col(a.base_z + e);
-  float ss = 0.0f;
-  for (int r = tid; r < a.D; r += kThreads) {
-    const float d = col(a.base_d + r);
-    ss += d * d;
-  }
+  const int64_t tb = (int64_t)blockIdx.x * a.tok_per_wg;
+  const int nt = a.T - tb < a.tok_per_wg ? (int)(a.T - tb) : a.tok_per_wg;
+  for (int u = 0; u < nt; ++u) {
+    const int64_t t = tb + u;
+    const float* row = a.p + t * a.NV;
+    auto col = [&](int cc) {
+      float v = 0.0f;
+      for (int sp = 0; sp < a.splits; ++sp) v += row[sp * sstride + cc];
+      return v;
+    };
+    float sq = 0.0f;
+    if (c < a.E) {
+      a.z[t * a.E + c] = col(a.base_z + c);
+    } else if (c < a.E + a.D) {
+      const int r = c - a.E;
+      const float d = col(a.base_d + r);
+      a.dbuf[t * a.D + r] = d;
+      sq = d * d;
+    } else if (c < a.E + a.D + a.Is) {
+      const int i = c - a.E - a.D;
+      const float gt = col(a.base_g + i), uu = col(a.base_u + i);
+      a.s[t * a.Is + i] = bf16_bits(gt / (1.0f + expf(-gt)) * uu);
+    }
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) ss += __shfl_xor(ss, o, 64);
-  if ((tid & 63) == 0) red[tid >> 6] = ss;
-  __syncthreads();
-  const float total = red[0] + red[1] + red[2] + red[3];
-  const float inv = 1.0f / sqrtf(total / (float)a.D + a.eps);
-  for (int r = tid; r < a.D; r += kThreads) {
-    const float d = col(a.base_d + r);
-    const float gm = __uint_as_float((uint32_t)a.gamma[r] << 16);
-    a.xl[t * a.D + r] = bf16_bits(gm * (d * inv));
+    for (int o = 32; o > 0; o >>= 1) sq += __shfl_xor(sq, o, 64);
+    if ((tid & 63) == 0) red[u][tid >> 6] = sq;
   }
-  for (int i = tid; i < a.Is; i += kThreads) {
-    const float g = col(a.base_g + i), u = col(a.base_u + i);
-    a.s[t * a.Is + i] = bf16_bits(g / (1.0f + expf(-g)) * u);
+  __syncthreads();
+  if (tid < nt) a.ssq[(tb + tid) * a.nblk + blockIdx.y] = ((red[tid][0] + red[tid][1]) + red[tid][2]) + red[tid][3];
+}
+
+// Second half: xl = bf16(gamma * d / sqrt(mean(d^2) + eps)) for the
+// workgroup's tokens.  Each token's sum of squares over its column blocks is
+// reduced by 32 lanes (lane j takes blocks j, j + 32, ...; then a fixed
+// butterfly), so the order never depends on timing.
+__global__ __launch_bounds__(kThreads) void block_norm_kernel(BlockMidArgs a) {
+  __shared__ float inv_l[kMidTok];
+  const int tid = threadIdx.x;
+  const int r = blockIdx.y * kThreads + tid;
+  const int64_t tb = (int64_t)blockIdx.x * a.tok_per_wg;
+  const int nt = a.T - tb < a.tok_per_wg ? (int)(a.T - tb) : a.tok_per_wg;
+  {
+    const int u = tid >> 5, j0 = tid & 31;  // 8 tokens x 32 lanes
+    float part = 0.0f;
+    if (u < nt)
+      for (int j = j0; j < a.nblk; j += 32) part += a.ssq[(tb + u) * a.nblk + j];
+#pragma unroll
+    for (int o = 16; o > 0; o >>= 1) part += __shfl_xor(part, o, 32);
+    if (j0 == 0 && u < nt) inv_l[u] = 1.0f / sqrtf(part / (float)a.D + a.eps);
+  }
+  __syncthreads();
+  if (r >= a.D) return;
+  const float gm = __uint_as_float((uint32_t)a.gamma[r] << 16);
+  for (int u = 0; u < nt; ++u) {
+    const int64_t t = tb + u;
+    a.xl[t * a.D + r] = bf16_bits(gm * (a.dbuf[t * a.D + r] * inv_l[u]));
   }
 }
 
@@ -341,23 +438,35 @@ int dense_tile_splits(int64_t T, int NV, int ksteps) {
   return splits < most ? splits : most;
 }
 
-hipError_t launch_dense_gemm(const DenseGemmArgs& a, hipStream_t s) {
+hipError_t launch_dense_gemm(const DenseGemmArgs& a, int product, hipStream_t s) {
   if (a.T <= 0) return hipSuccess;
   const int nT = a.NV / kTile;
   if (a.T <= kDenseStreamMaxTokens) {
-    if (a.split_steps > kDenseStreamSplitSteps) return hipErrorInvalidValue;
-    const unsigned tchunks = (unsigned)((a.T + kStreamTok - 1) / kStreamTok);
-    hipLaunchKernelGGL(dense_stream_kernel, dim3((unsigned)(nT * a.splits), tchunks), dim3(kThreads), 0, s, a);
+    if (a.splits != 1) return hipErrorInvalidValue;
+    const dim3 grid((unsigned)(a.NV / kStreamRows), (unsigned)((a.T + kStreamRows - 1) / kStreamRows));
+    if (product == 1)
+      hipLaunchKernelGGL(dense_stream_kernel<1>, grid, dim3(kThreads), 0, s, a);
+    else
+      hipLaunchKernelGGL(dense_stream_kernel<2>, grid, dim3(kThreads), 0, s, a);
   } else {
-    const int64_t total = (int64_t)nT * ((a.T + kTile - 1) / kTile) * a.splits;
-    hipLaunchKernelGGL(dense_tile_kernel, dim3((unsigned)total), dim3(kThreads), 0, s, a);
+    const dim3 grid((unsigned)((int64_t)nT * ((a.T + kTile - 1) / kTile) * a.splits));
+    if (product == 1)
+      hipLaunchKernelGGL(dense_tile_kernel<1>, grid, dim3(kThreads), 0, s, a);
+    else
+      hipLaunchKernelGGL(dense_tile_kernel<2>, grid, dim3(kThreads), 0, s, a);
   }
   return hipGetLastError();
 }
 
+int block_mid_blocks(int E, int D, int Is) { return (E + D + Is + kThreads - 1) / kThreads; }
+
 hipError_t launch_block_mid(const BlockMidArgs& a, hipStream_t s) {
   if (a.T <= 0) return hipSuccess;
-  hipLaunchKernelGGL(block_mid_kernel, dim3((unsigned)a.T), dim3(kThreads), 0, s, a);
+  if (a.tok_per_wg < 1 || a.tok_per_wg > kMidTok) return hipErrorInvalidValue;
+  const unsigned tchunks = (unsigned)((a.T + a.tok_per_wg - 1) / a.tok_per_wg);
+  hipLaunchKernelGGL(block_cols_kernel, dim3(tchunks, (unsigned)a.nblk), dim3(kThreads), 0, s, a);
+  hipLaunchKernelGGL(block_norm_kernel, dim3(tchunks, (unsigned)((a.D + kThreads - 1) / kThreads)), dim3(kThreads),
+                     0, s, a);
   return hipGetLastError();
 }
 

@@ -204,18 +204,18 @@ struct DenseGemmArgs {
   int splits;
   float* p;  // [splits][T][NV]
 };
-// Tokens up to which the weight-streaming kernel serves a product (each
-// 32-token chunk re-reads the weights); beyond, the 128 x 128 tile kernel.
-constexpr int64_t kDenseStreamMaxTokens = 64;
-// K steps per split of the streaming kernel (weights held in registers).
-constexpr int kDenseStreamSplitSteps = 7;
-hipError_t launch_dense_gemm(const DenseGemmArgs& a, hipStream_t s);
+// Tokens up to which the weight-streaming kernel serves a product (one split;
+// each 16-token chunk re-reads the weights); beyond, the 128 x 128 tile kernel.
+constexpr int64_t kDenseStreamMaxTokens = 16;
+// product: 1 or 2 (the block's first or second product; names the kernel only)
+hipError_t launch_dense_gemm(const DenseGemmArgs& a, int product, hipStream_t s);
 // Splits the tile kernel uses for T tokens and NV features over `ksteps` steps.
 int dense_tile_splits(int64_t T, int NV, int ksteps);
 
 // Block epilogue after the first product (segments: gate logits [E], latent
 // [D], shared gate [Is], shared up [Is]): z fp32 [T, E]; xl bf16 [T, D] =
-// RMS-normed latent times gamma; s bf16 [T, Is] = SiLU(g) * u.
+// RMS-normed latent times gamma; s bf16 [T, Is] = SiLU(g) * u.  Two launches
+// (column sums, then the norm), both parallel over tokens and columns.
 struct BlockMidArgs {
   const float* p;  // [splits][T][NV]
   int splits, NV;
@@ -227,7 +227,12 @@ struct BlockMidArgs {
   float* z;
   uint16_t* xl;
   uint16_t* s;
+  float* dbuf;  // [T, D] raw latent (fp32)
+  float* ssq;   // [T, nblk] per-workgroup sums of squares of the latent
+  int nblk;     // block_mid_blocks(E, D, Is)
+  int tok_per_wg;  // tokens per workgroup, 1..8
 };
+int block_mid_blocks(int E, int D, int Is);
 hipError_t launch_block_mid(const BlockMidArgs& a, hipStream_t s);
 // out[t][n] = sum over splits of p[split][t][n] (n < N, row length N).
 hipError_t launch_dense_sum(const float* p, int splits, int64_t T, int N, float* out, hipStream_t s);
