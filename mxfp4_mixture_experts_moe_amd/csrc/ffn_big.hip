@@ -382,12 +382,16 @@ __global__ __launch_bounds__(kThreads) void ffn_big_kernel(GemmArgs a) {
       // (one (matrix, row group) pair per token group), so the conversion
       // overlaps the matrix work instead of preceding it.
       constexpr int kPairs = C::kMats * C::kRG;
-      bf16x8_t aop[kPairs];
+      // two operand sets used in turn (slice i reads set i % 2 and fills the
+      // other), indexed by constants after unrolling, so no register copies
+      bf16x8_t ops[2][kPairs];
 #pragma unroll
       for (int pr = 0; pr < kPairs; ++pr)
-        aop[pr] = decode_dword(q[pr / C::kRG][pr % C::kRG][0], e8m0_to_f32(eb[pr / C::kRG][pr % C::kRG]));
+        ops[0][pr] = decode_dword(q[pr / C::kRG][pr % C::kRG][0], e8m0_to_f32(eb[pr / C::kRG][pr % C::kRG]));
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
+        bf16x8_t(&aop)[kPairs] = ops[i & 1];
+        bf16x8_t(&anext)[kPairs] = ops[(i + 1) & 1];
         // activations: block g of the step, P-order positions 8i..8i+7 (chunk
         // 4g+i); one operand is read ahead while the previous one feeds its MFMAs
         auto bread = [&](int n) {
@@ -397,13 +401,14 @@ __global__ __launch_bounds__(kThreads) void ffn_big_kernel(GemmArgs a) {
         auto convert_next = [&](int pr) {
           return decode_dword(q[pr / C::kRG][pr % C::kRG][i + 1], e8m0_to_f32(eb[pr / C::kRG][pr % C::kRG]));
         };
-        bf16x8_t anext[kPairs];
         bf16x8_t bnext = bread(0);
 #pragma unroll
         for (int n = 0; n < kB; ++n) {
           if (!kFull && n >= nlive) break;
           const bf16x8_t bop = bnext;
-          if (n + 1 < kB && (kFull || n + 1 < nlive)) bnext = bread(n + 1);
+          // the next operand is read even if its token group is dead (an
+          // in-bounds LDS read whose value is then unused): no copy, no branch
+          if (n + 1 < kB) bnext = bread(n + 1);
 #pragma unroll
           for (int pr = 0; pr < kPairs; ++pr)
             acc[pr / C::kRG][pr % C::kRG][n] =
@@ -411,12 +416,10 @@ __global__ __launch_bounds__(kThreads) void ffn_big_kernel(GemmArgs a) {
           if (i + 1 < 4 && n < kPairs) anext[n] = convert_next(n);
           __builtin_amdgcn_sched_barrier(0);
         }
-        if (i + 1 < 4) {
+        if (i + 1 < 4 && !kFull) {
 #pragma unroll
-          for (int pr = 0; pr < kPairs; ++pr) {
-            if (!kFull && pr >= nlive) anext[pr] = convert_next(pr);  // fewer live token groups than pairs
-            aop[pr] = anext[pr];
-          }
+          for (int pr = 0; pr < kPairs; ++pr)
+            if (pr >= nlive) anext[pr] = convert_next(pr);  // fewer live token groups than pairs
         }
       }
     } else {
@@ -436,36 +439,35 @@ __global__ __launch_bounds__(kThreads) void ffn_big_kernel(GemmArgs a) {
         for (int rg = 0; rg < C::kRG; ++rg) wide |= (eb[0][rg] - 104u) > 36u;
         wide_seen |= __builtin_amdgcn_ballot_w64(wide) != 0;
         // as in gate/up, slice i's operands are converted during slice i - 1's MFMAs
-        f16x8_t aop[C::kRG];
+        f16x8_t ops[2][C::kRG];  // used in turn, as in gate/up
 #pragma unroll
-        for (int rg = 0; rg < C::kRG; ++rg) aop[rg] = decode_dword_f16(q[0][rg][0], e8m0_to_f32(eb[0][rg]));
+        for (int rg = 0; rg < C::kRG; ++rg) ops[0][rg] = decode_dword_f16(q[0][rg][0], e8m0_to_f32(eb[0][rg]));
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
+          f16x8_t(&aop)[C::kRG] = ops[i & 1];
+          f16x8_t(&anext)[C::kRG] = ops[(i + 1) & 1];
           auto bread = [&](int n) {
             const int row = n * 16 + rho;
             const f16x8_t hv = __builtin_bit_cast(f16x8_t, *reinterpret_cast<const uint4*>(al + row * kARowDw + 4 * (4 * g + i)));
             if constexpr (kResc) return hv;
             else return scale_h(hv, n);
           };
-          f16x8_t anext[C::kRG];
           f16x8_t bnext = bread(0);
 #pragma unroll
           for (int n = 0; n < kB; ++n) {
             if (!kFull && n >= nlive) break;
             const f16x8_t bop = bnext;
-            if (n + 1 < kB && (kFull || n + 1 < nlive)) bnext = bread(n + 1);
+            if (n + 1 < kB) bnext = bread(n + 1);  // as in gate/up
 #pragma unroll
             for (int rg = 0; rg < C::kRG; ++rg)
               acc[0][rg][n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aop[rg], bop, acc[0][rg][n], 0, 0, 0);
             if (i + 1 < 4 && n < C::kRG) anext[n] = decode_dword_f16(q[0][n][i + 1], e8m0_to_f32(eb[0][n]));
             __builtin_amdgcn_sched_barrier(0);
           }
-          if (i + 1 < 4) {
+          if (i + 1 < 4 && !kFull) {
 #pragma unroll
-            for (int rg = 0; rg < C::kRG; ++rg) {
-              if (!kFull && rg >= nlive) anext[rg] = decode_dword_f16(q[0][rg][i + 1], e8m0_to_f32(eb[0][rg]));
-              aop[rg] = anext[rg];
-            }
+            for (int rg = 0; rg < C::kRG; ++rg)
+              if (rg >= nlive) anext[rg] = decode_dword_f16(q[0][rg][i + 1], e8m0_to_f32(eb[0][rg]));
           }
         }
       } else {
