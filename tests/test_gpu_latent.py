@@ -4,7 +4,7 @@ Routing ids bit-exact (the inputs are checked to keep every checked token's
 k-th and (k+1)-th scores apart by far more than the fp32 sums can move them);
 the block output within the FFN bar: relative L2 error <= 2e-3 and max abs
 error <= 1e-2 * max|ref|.  Small shapes on every token, through both dense
-kernels (up to 64 tokens the weight-streaming kernel, beyond it the tile
+kernels (up to 16 tokens the weight-streaming kernel, beyond it the tile
 kernel, with and without split-K) and ragged feature segments; the K3 shape
 on chosen tokens at decode, verify and prefill sizes.
 """
@@ -68,11 +68,12 @@ def tiny(k3):
     return cfg, DenseDev(cfg), experts
 
 
-@pytest.mark.parametrize("T", [1, 5, 32, 40, 64, 65, 200, 600])
+@pytest.mark.parametrize("T", [1, 5, 16, 17, 32, 40, 64, 65, 200, 600, 1100])
 def test_tiny_block_every_token(k3, tiny, T):
     # 8 experts top-2, H 256, latent 128, shared 192 (ragged 128-wide
-    # segments: gate 8 of 128, shared 192 of 256); T <= 64: streaming kernel,
-    # 65 / 200: tile kernel with split-K, 600: five token tiles
+    # segments: gate 8 of 128, shared 192 of 256); T <= 16: streaming kernel,
+    # 17 .. 200: the tile kernel with split-K, 600 and 1100: several token
+    # tiles, the last one ragged
     cfg, dense, experts = tiny
     cfg = cfg.with_(layer=cfg.layer.with_(T=T))
     h_bits = moe_inputs.block_hidden(cfg, seed=T)
@@ -132,8 +133,8 @@ def k3_dense(k3):
 
 
 # (workload, token count, checked tokens): decode through the streaming
-# kernel, 128 tokens through the tile kernel with split-K, 4096 tokens with
-# one split
+# kernel, 64 and 128 tokens through the tile kernel with split-K, 4096 tokens
+# with one split
 K3_CASES = [("block-decode-t1", 1, [0]), ("block-decode-t8", 8, [7]), ("block-decode-t8", 64, [63]),
             ("block-prefill", 128, [127]), ("block-prefill", 4096, [1, 4095])]
 
