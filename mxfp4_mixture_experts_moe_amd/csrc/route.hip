@@ -1,5 +1,4 @@
-// Sigmoid + bias top-k router (one 64-lane wavefront per token; four per
-// token for batches of up to 256 tokens).
+// Sigmoid + bias top-k router (one 64-lane wavefront per token).
 //
 // Routing parameters from the llama.cpp pull request "model: add Kimi-K3 text
 // model", converter dry-run comment: 896 experts, 16 used, sigmoid expert
@@ -7,21 +6,21 @@
 // that the selected ids are reproducible bit for bit; ties go to the lower
 // expert index; NaN scores rank last.
 //
-// Up to 1024 experts (16 per lane) the scores live in registers: lane l owns
-// experts l, l + 64, l + 128, ....  One wave per token (large batches): the
-// 64 lane-bests are sorted across the wave; the k-th of them ranks at or
-// after every expert of the top k, so the top k are among the experts ranking
-// at or before it, which (when there are at most 64) are compacted through
-// LDS and sorted once.  Otherwise (heavy ties), and in the four-wave kernel of
-// small batches, where a token's latency is the whole cost, each lane sorts
-// its experts by a bitonic network and its best remaining one is its "head";
-// each of the k rounds reduces the 64 heads to the wave's best (four DPP
-// exchanges inside each 16-lane row, two row swaps across rows) and only the
-// lane that owned the winner moves to its next expert.  Small batches split each token over a workgroup of four waves
-// (each finds the k best of a quarter of the experts; one wave orders the
-// candidates).  Larger E falls back to a kernel that writes the scores to LDS (or
-// recomputes them) and, in round r, picks the best expert ranking strictly
-// after round r-1's pick; it needs no "taken" flags, so nothing limits E.
+// Up to 1024 experts (16 per lane) one wave handles a token with the logits
+// in registers: lane l owns experts l, l + 64, l + 128, ....  An fp32 score
+// pre-filters: the k-th of the 64 fp32 lane-bests bounds the k-th fp32 score
+// from below, so every expert of the exact top k has an fp32 score no lower
+// than that bound minus a small margin (the fp32 error bound is stated at
+// route_score32); those candidates (at most 64) are scored in fp64 and sorted
+// once across the wave.
+// Otherwise (heavy ties, non-finite scores at the threshold) the fp64 scores of
+// all experts are used: the 64 fp64 lane-bests are sorted, the experts ranking
+// at or before the k-th of them are compacted and sorted, and with more than
+// 64 of those each lane sorts its experts and k rounds take the wave's best
+// head (DPP exchanges inside 16-lane rows, row swaps across rows).  Larger E
+// falls back to a kernel that writes the scores to LDS (or recomputes them)
+// and, in round r, picks the best expert ranking strictly after round r-1's
+// pick; it needs no "taken" flags, so nothing limits E.
 #include "k3moe_internal.h"
 
 #include <math.h>
@@ -33,6 +32,16 @@ constexpr int kWaveSize = 64;
 
 __device__ __forceinline__ double route_score(float z, float b) {
   double s = 1.0 / (1.0 + exp(-(double)z)) + (double)b;
+  return isnan(s) ? -INFINITY : s;
+}
+
+// The same score in fp32 (a pre-filter only: every decision is taken on the
+// fp64 score).  |score32 - score| <= 2^-21 * (1 + |score|): sigmoid32 is within
+// 2^-22 of the exact sigmoid (exp, add and divide each within an ulp of its
+// result, the sigmoid below 1), and the bias add rounds by at most 2^-24 of
+// the sum.
+__device__ __forceinline__ float route_score32(float z, float b) {
+  const float s = 1.0f / (1.0f + expf(-z)) + b;
   return isnan(s) ? -INFINITY : s;
 }
 
@@ -276,24 +285,96 @@ __global__ __launch_bounds__(256) void route_topk_reg_kernel(const float* __rest
 #pragma unroll
     for (int j = 0; j < NPER; ++j) bv[j] = 0.0f;
   }
-  double sc[NPER];
-  int ix[NPER];
-#pragma unroll
-  for (int j = 0; j < NPER; ++j) {
-    const int e = lane + kWaveSize * j;
-    // experts past E carry index INT_MAX, so they rank after every real expert
-    sc[j] = e < E ? route_score(zv[j], bv[j]) : -INFINITY;
-    ix[j] = e < E ? e : INT_MAX;
-  }
-
-  // lanes 0..k-1 end with the top k in rank order: filtered selection, or
-  // (more than 64 entries at or before the threshold) sorted lanes and k rounds
   __shared__ double fs[4][kWaveSize];
   __shared__ int fe[4][kWaveSize];
+  // the token's logits and bias, so later reads of single experts (the
+  // candidates, the chosen ones) come from LDS, not another global round trip
+  __shared__ float zl[4][NPER * kWaveSize], bl[4][NPER * kWaveSize];
   const int wv = threadIdx.x / kWaveSize;
-  double fs_out;
   int my_id = 0;
-  if (!wave_topk_filtered<NPER>(sc, ix, k, lane, fs[wv], fe[wv], fs_out, my_id)) {
+#pragma unroll
+  for (int j = 0; j < NPER; ++j) {
+    zl[wv][lane + kWaveSize * j] = zv[j];
+    bl[wv][lane + kWaveSize * j] = bv[j];
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+  // fp32 pre-filter.  Of the 64 fp32 lane-bests, the k-th (m) is at most the
+  // k-th best fp32 score overall (k distinct experts score at least m); an
+  // expert of the fp64 top k cannot score below (k-th best fp32) - 2 * err in
+  // fp32 (err: the fp32 error bound above), else the k experts above that
+  // k-th value would all outrank it in fp64.  So every expert within a margin
+  // of m, taken as 2^-16 * (1 + |m|) (16 times 2 * err), is a candidate; the
+  // candidates (at most 64) are scored in fp64 and sorted once.  A non-finite
+  // m or more than 64 candidates (heavy ties) take the fp64 path below.
+  bool done = false;
+  {
+    float s32[NPER];
+    float lb = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < NPER; ++j) {
+      const int e = lane + kWaveSize * j;
+      s32[j] = e < E ? route_score32(zv[j], bv[j]) : -INFINITY;
+      lb = fmaxf(lb, s32[j]);
+    }
+    double cs = (double)lb;
+    int ce = lane;  // distinct entries: the lane numbers
+    wave_sort64(cs, ce, lane);
+    const float m = (float)readlane_f64(cs, k - 1);
+    if (isfinite(m)) {
+      const float theta = m - ldexpf(1.0f + fabsf(m), -16);
+      // slots by ballots: item j of a lane goes after every candidate of
+      // items < j and after item j of the lanes below (the order is
+      // irrelevant: the candidates are sorted next)
+      uint64_t mask[NPER];
+      int total = 0;
+#pragma unroll
+      for (int j = 0; j < NPER; ++j) {
+        mask[j] = __builtin_amdgcn_ballot_w64(s32[j] >= theta);  // experts past E score -inf
+        total += __builtin_popcountll(mask[j]);
+      }
+      if (total <= kWaveSize) {
+        int base = 0;
+#pragma unroll
+        for (int j = 0; j < NPER; ++j) {
+          const int below = __builtin_amdgcn_mbcnt_hi((uint32_t)(mask[j] >> 32),
+                                                      __builtin_amdgcn_mbcnt_lo((uint32_t)mask[j], 0u));
+          if ((mask[j] >> lane) & 1ull) fe[wv][base + below] = lane + kWaveSize * j;
+          base += __builtin_popcountll(mask[j]);
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        double ds = -INFINITY;
+        int de = INT_MAX;  // sentinel: ranks after every real expert
+        if (lane < total) {
+          de = fe[wv][lane];
+          ds = route_score(zl[wv][de], bl[wv][de]);
+        }
+        wave_sort64(ds, de, lane);
+        my_id = de;
+        done = true;
+      }
+    }
+  }
+
+  // fp64 path: lanes 0..k-1 end with the top k in rank order: filtered
+  // selection, or (more than 64 entries at or before the threshold) sorted
+  // lanes and k rounds
+  if (!done) {
+    double sc[NPER];
+    int ix[NPER];
+#pragma unroll
+    for (int j = 0; j < NPER; ++j) {
+      const int e = lane + kWaveSize * j;
+      // experts past E carry index INT_MAX, so they rank after every real expert
+      sc[j] = e < E ? route_score(zv[j], bv[j]) : -INFINITY;
+      ix[j] = e < E ? e : INT_MAX;
+    }
+    double fs_out;
+    if (!wave_topk_filtered<NPER>(sc, ix, k, lane, fs[wv], fe[wv], fs_out, my_id)) {
     sort_desc<NPER>(sc, ix);
     for (int r = 0; r < k; ++r) {
       double bs = sc[0];
@@ -310,109 +391,15 @@ __global__ __launch_bounds__(256) void route_topk_reg_kernel(const float* __rest
         ix[NPER - 1] = INT_MAX;
       }
     }
-  }
-
-  double g = 0.0;
-  if (lane < k) g = 1.0 / (1.0 + exp(-(double)zt[my_id]));
-  double sum = g;
-  if (normalize) {
-    sum = 0.0;
-    for (int r = 0; r < k; ++r) sum += __shfl(g, r, kWaveSize);
-  }
-  if (lane < k) {
-    double v = normalize ? g / sum : g;
-    v = v * (double)route_scale;
-    ids[t * k + lane] = my_id;
-    w[t * k + lane] = (float)v;
-  }
-}
-
-// Small batches: one workgroup of four waves per token, so the fp64 scoring
-// and the rounds of one token run on four SIMDs at once.  Thread i scores
-// experts i, i + 256, i + 512, ... (NPER of them, E <= 256 * NPER); each wave
-// takes the k best of its share by the rounds above (k <= 16) and leaves them
-// in LDS; wave 0 then holds the 4k candidates, one per lane (sentinels in the
-// rest), and orders them with a bitonic network across the wave.  The union
-// of the four per-wave top-k lists holds the token's top-k, so lanes 0..k-1
-// end with the same ids, in the same order, as the one-wave kernel.
-template <int NPER>
-__global__ __launch_bounds__(256) void route_topk_blk_kernel(const float* __restrict__ z, const float* __restrict__ bias,
-                                                              int E, int k, int normalize, float route_scale,
-                                                              int32_t* __restrict__ ids, float* __restrict__ w) {
-  constexpr int kBlkWaves = 4, kMaxK = kWaveSize / kBlkWaves;
-  __shared__ double cand_s[kBlkWaves * kMaxK];
-  __shared__ int cand_e[kBlkWaves * kMaxK];
-  __shared__ float zl[4 * 256];  // the token's logits, for the gate weights
-  const int tid = threadIdx.x, lane = tid & (kWaveSize - 1), wave = tid / kWaveSize;
-  const int64_t t = blockIdx.x;
-  const float* zt = z + t * (int64_t)E;
-
-  float zv[NPER], bv[NPER];
-#pragma unroll
-  for (int j = 0; j < NPER; ++j) zv[j] = zt[min(tid + 256 * j, E - 1)];
-#pragma unroll
-  for (int j = 0; j < NPER; ++j) bv[j] = bias ? bias[min(tid + 256 * j, E - 1)] : 0.0f;
-  double sc[NPER];
-  int ix[NPER];
-#pragma unroll
-  for (int j = 0; j < NPER; ++j) {
-    const int e = tid + 256 * j;
-    if (e < E) zl[e] = zv[j];
-    sc[j] = e < E ? route_score(zv[j], bv[j]) : -INFINITY;
-    ix[j] = e < E ? e : INT_MAX;
-  }
-
-  // k rounds over this wave's share (a token's latency is the whole cost
-  // here, and the rounds' DPP exchanges are shorter than the filtered
-  // selection's two 21-step shuffle networks).  Expert e sits in lane e % 64
-  // of its wave; a sentinel winner (a share with fewer than k experts) only
-  // shifts sentinels.
-  double my_s = -INFINITY;
-  int my_e = INT_MAX;
-  {
-    sort_desc<NPER>(sc, ix);
-    for (int r = 0; r < k; ++r) {
-      double bs = sc[0];
-      int be = ix[0];
-      wave_best(bs, be, lane);
-      if (lane == r) {
-        my_s = bs;
-        my_e = be;
-      }
-      if (lane == (be & (kWaveSize - 1))) {
-#pragma unroll
-        for (int j = 0; j + 1 < NPER; ++j) {
-          sc[j] = sc[j + 1];
-          ix[j] = ix[j + 1];
-        }
-        sc[NPER - 1] = -INFINITY;
-        ix[NPER - 1] = INT_MAX;
-      }
     }
   }
-  if (lane < k) {
-    cand_s[wave * k + lane] = my_s;
-    cand_e[wave * k + lane] = my_e;
-  }
-  __syncthreads();
-  if (wave != 0) return;
 
-  double cs = -INFINITY;
-  int ce = INT_MAX;
-  if (lane < kBlkWaves * k) {
-    cs = cand_s[lane];
-    ce = cand_e[lane];
-  }
-  // the 4k candidates, first-ranked in lane 0
-  wave_sort64(cs, ce, lane);
-
-  const int my_id = ce;
   double g = 0.0;
-  if (lane < k) g = 1.0 / (1.0 + exp(-(double)zl[my_id]));
+  if (lane < k) g = 1.0 / (1.0 + exp(-(double)zl[wv][my_id]));
   double sum = g;
   if (normalize) {
     sum = 0.0;
-    for (int r = 0; r < k; ++r) sum += __shfl(g, r, kWaveSize);
+    for (int r = 0; r < k; ++r) sum += readlane_f64(g, r);  // lane by lane
   }
   if (lane < k) {
     double v = normalize ? g / sum : g;
@@ -477,7 +464,7 @@ __global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict
   if (normalize) {
     // Sum in slot order 0..k-1 so the result does not depend on a tree shape.
     sum = 0.0;
-    for (int r = 0; r < k; ++r) sum += __shfl(g, r, kWaveSize);
+    for (int r = 0; r < k; ++r) sum += readlane_f64(g, r);  // lane by lane
   }
   if (lane < k) {
     double v = normalize ? g / sum : g;
@@ -491,20 +478,6 @@ __global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict
 
 hipError_t launch_route_topk(const float* z, const float* bias, int64_t T, int E, int k, int normalize,
                              float route_scale, int32_t* ids, float* w, hipStream_t s) {
-  // Up to kBlockRouteTokens tokens the GPU has more SIMDs than the one-wave
-  // kernel has waves, so a token's latency is the whole cost: four waves per
-  // token cut it.
-  constexpr int64_t kBlockRouteTokens = 256;
-  if (T <= kBlockRouteTokens && E <= 4 * 256 && k <= 16) {
-#define K3_ROUTE_BLK(NP)                                                                                        \
-  hipLaunchKernelGGL(route_topk_blk_kernel<NP>, dim3((unsigned)T), dim3(256), 0, s, z, bias, E, k, normalize, \
-                     route_scale, ids, w)
-    if (E <= 256) K3_ROUTE_BLK(1);
-    else if (E <= 512) K3_ROUTE_BLK(2);
-    else K3_ROUTE_BLK(4);
-#undef K3_ROUTE_BLK
-    return hipGetLastError();
-  }
   if (E <= 16 * kWaveSize) {
     const int64_t blocks = (T + 3) / 4;
 #define K3_ROUTE(NP)                                                                                            \

@@ -109,3 +109,24 @@ def test_empty_and_determinism(k3):
     a = run(k3, z, b, 16)
     c = run(k3, z, b, 16)
     assert np.array_equal(a[0], c[0]) and np.array_equal(a[1].view(np.uint32), c[1].view(np.uint32))
+
+
+@pytest.mark.parametrize("n_close,E,k,T", [(40, 896, 16, 1), (40, 896, 16, 8), (20, 256, 16, 3), (100, 896, 16, 2),
+                                           (70, 1024, 64, 1), (17, 896, 16, 300)])
+def test_scores_closer_than_fp32_resolves(k3, n_close, E, k, T):
+    # n_close experts get logits one fp32 ulp apart near 2.0, whose sigmoids
+    # differ by about 2.5e-8: below what an fp32 score resolves, so the fp32
+    # pre-filter keeps all of them as candidates and the fp64 scores decide
+    # (more than 64 of them: the all-fp64 path); the others sit at 0 (score
+    # 0.5, far below), with one token also carrying a bias that lifts an
+    # outsider into the top k
+    g = np.random.default_rng(n_close + E + k + T)
+    z = np.zeros((T, E), np.float32)
+    for t in range(T):
+        pick = g.choice(E, size=n_close, replace=False)
+        z[t, pick] = (np.float32(2.0) + np.arange(n_close, dtype=np.float32) * np.float32(2.0 ** -22))[g.permutation(n_close)]
+    b = np.zeros(E, np.float32)
+    b[g.integers(0, E)] = np.float32(0.4)
+    print(f"[route] {n_close} close scores, E={E} k={k} T={T}", flush=True)
+    check(k3, z, b, k, what=f"close scores n={n_close} E={E} k={k} T={T}")
+    check(k3, z, None, k, what=f"close scores n={n_close} E={E} k={k} T={T}, no bias")
