@@ -8,11 +8,12 @@
 //
 // Up to 1024 experts (16 per lane) one wave handles a token with the logits
 // in registers: lane l owns experts l, l + 64, l + 128, ....  An fp32 score
-// pre-filters: the k-th of the 64 fp32 lane-bests bounds the k-th fp32 score
-// from below, so every expert of the exact top k has an fp32 score no lower
-// than that bound minus a small margin (the fp32 error bound is stated at
-// route_score32); those candidates (at most 64) are scored in fp64 and sorted
-// once across the wave.
+// pre-filters: the k-th of the 64 fp32 lane-bests (a bitwise radix select over
+// ballots) bounds the k-th fp32 score from below, so every expert of the exact
+// top k has an fp32 score no lower than that bound minus a small margin (the
+// fp32 error bound is stated at route_score32); those candidates (at most 64)
+// are scored in fp64 and each counts how many of the others rank before it,
+// which places the top k in order without a sort.
 // Otherwise (heavy ties, non-finite scores at the threshold) the fp64 scores of
 // all experts are used: the 64 fp64 lane-bests are sorted, the experts ranking
 // at or before the k-th of them are compacted and sorted, and with more than
@@ -30,19 +31,42 @@ namespace {
 
 constexpr int kWaveSize = 64;
 
+__device__ __forceinline__ double sigmoid64(float z) { return 1.0 / (1.0 + exp(-(double)z)); }
+
 __device__ __forceinline__ double route_score(float z, float b) {
-  double s = 1.0 / (1.0 + exp(-(double)z)) + (double)b;
+  double s = sigmoid64(z) + (double)b;
   return isnan(s) ? -INFINITY : s;
 }
 
-// The same score in fp32 (a pre-filter only: every decision is taken on the
-// fp64 score).  |score32 - score| <= 2^-21 * (1 + |score|): sigmoid32 is within
-// 2^-22 of the exact sigmoid (exp, add and divide each within an ulp of its
-// result, the sigmoid below 1), and the bias add rounds by at most 2^-24 of
-// the sum.
+// The same score in fp32 from the hardware exp2 and reciprocal (a pre-filter
+// only: every decision is taken on the fp64 score).  With u = 2^-24:
+// -z * log2(e) is off by at most 2|z|u in the exponent, v_exp_f32 and
+// v_rcp_f32 are within 1 ulp (2u) of their results, and the add rounds by u,
+// so e^-z carries a relative error of at most (2|z| + 2)u and the sigmoid an
+// absolute one of at most 3u + 2u * sigma(1 - sigma)(|z| + 1) <= 4u
+// (sigma(1 - sigma)|z| <= 0.224).  Outputs flushed to zero (exponents below
+// -126) move the sigmoid by less than 2^-126, an overflow to +inf gives the
+// limit 0.  With the bias add (u of the sum): |score32 - score| <=
+// 5u(1 + |score|) < 2^-21 (1 + |score|).
 __device__ __forceinline__ float route_score32(float z, float b) {
-  const float s = 1.0f / (1.0f + expf(-z)) + b;
+  const float e = __builtin_amdgcn_exp2f(-z * 1.44269504088896341f);
+  const float s = __builtin_amdgcn_rcpf(1.0f + e) + b;
   return isnan(s) ? -INFINITY : s;
+}
+
+// The k-th largest (1 <= k <= 64) of the wave's 64 values, none NaN: the
+// largest x that at least k lanes reach, found one bit at a time on integer
+// keys that order like the floats.
+__device__ __forceinline__ float wave_kth_largest(float v, int k) {
+  const uint32_t b = __float_as_uint(v);
+  const uint32_t key = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+  uint32_t x = 0;
+#pragma unroll
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t c = x | (1u << bit);
+    if (__builtin_popcountll(__builtin_amdgcn_ballot_w64(key >= c)) >= k) x = c;
+  }
+  return __uint_as_float((x & 0x80000000u) ? (x & 0x7FFFFFFFu) : ~x);
 }
 
 // (sa, ea) ranks before (sb, eb): higher score, or equal score and lower index.
@@ -285,21 +309,15 @@ __global__ __launch_bounds__(256) void route_topk_reg_kernel(const float* __rest
 #pragma unroll
     for (int j = 0; j < NPER; ++j) bv[j] = 0.0f;
   }
+  // candidates: fp64 score, expert, logit and bias; the top k by rank: gate
+  // value and expert
   __shared__ double fs[4][kWaveSize];
   __shared__ int fe[4][kWaveSize];
-  // the token's logits and bias, so later reads of single experts (the
-  // candidates, the chosen ones) come from LDS, not another global round trip
-  __shared__ float zl[4][NPER * kWaveSize], bl[4][NPER * kWaveSize];
+  __shared__ float cz[4][kWaveSize], cb[4][kWaveSize];
+  __shared__ double tg[4][kWaveSize];
+  __shared__ int te[4][kWaveSize];
   const int wv = threadIdx.x / kWaveSize;
   int my_id = 0;
-#pragma unroll
-  for (int j = 0; j < NPER; ++j) {
-    zl[wv][lane + kWaveSize * j] = zv[j];
-    bl[wv][lane + kWaveSize * j] = bv[j];
-  }
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
   // fp32 pre-filter.  Of the 64 fp32 lane-bests, the k-th (m) is at most the
   // k-th best fp32 score overall (k distinct experts score at least m); an
@@ -307,9 +325,11 @@ __global__ __launch_bounds__(256) void route_topk_reg_kernel(const float* __rest
   // fp32 (err: the fp32 error bound above), else the k experts above that
   // k-th value would all outrank it in fp64.  So every expert within a margin
   // of m, taken as 2^-16 * (1 + |m|) (16 times 2 * err), is a candidate; the
-  // candidates (at most 64) are scored in fp64 and sorted once.  A non-finite
+  // candidates (at least k, at most 64) are scored in fp64, each one's rank
+  // among them is counted, and the first k land in rank order.  A non-finite
   // m or more than 64 candidates (heavy ties) take the fp64 path below.
   bool done = false;
+  double g = 0.0;
   {
     float s32[NPER];
     float lb = -INFINITY;
@@ -319,15 +339,12 @@ __global__ __launch_bounds__(256) void route_topk_reg_kernel(const float* __rest
       s32[j] = e < E ? route_score32(zv[j], bv[j]) : -INFINITY;
       lb = fmaxf(lb, s32[j]);
     }
-    double cs = (double)lb;
-    int ce = lane;  // distinct entries: the lane numbers
-    wave_sort64(cs, ce, lane);
-    const float m = (float)readlane_f64(cs, k - 1);
+    const float m = wave_kth_largest(lb, k);
     if (isfinite(m)) {
       const float theta = m - ldexpf(1.0f + fabsf(m), -16);
       // slots by ballots: item j of a lane goes after every candidate of
       // items < j and after item j of the lanes below (the order is
-      // irrelevant: the candidates are sorted next)
+      // irrelevant: the ranks are counted next)
       uint64_t mask[NPER];
       int total = 0;
 #pragma unroll
@@ -341,20 +358,59 @@ __global__ __launch_bounds__(256) void route_topk_reg_kernel(const float* __rest
         for (int j = 0; j < NPER; ++j) {
           const int below = __builtin_amdgcn_mbcnt_hi((uint32_t)(mask[j] >> 32),
                                                       __builtin_amdgcn_mbcnt_lo((uint32_t)mask[j], 0u));
-          if ((mask[j] >> lane) & 1ull) fe[wv][base + below] = lane + kWaveSize * j;
+          if ((mask[j] >> lane) & 1ull) {
+            fe[wv][base + below] = lane + kWaveSize * j;
+            cz[wv][base + below] = zv[j];
+            cb[wv][base + below] = bv[j];
+          }
           base += __builtin_popcountll(mask[j]);
         }
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        double ds = -INFINITY;
-        int de = INT_MAX;  // sentinel: ranks after every real expert
+        // slots past the candidates hold sentinels, which rank after every
+        // candidate, so the rank count below runs in blocks of 8
+        double cs = -INFINITY, cg = 0.0;
+        int ce = INT_MAX;
         if (lane < total) {
-          de = fe[wv][lane];
-          ds = route_score(zl[wv][de], bl[wv][de]);
+          ce = fe[wv][lane];
+          cg = sigmoid64(cz[wv][lane]);
+          cs = cg + (double)cb[wv][lane];
+          cs = isnan(cs) ? -INFINITY : cs;  // the value route_score gives
         }
-        wave_sort64(ds, de, lane);
-        my_id = de;
+        fs[wv][lane] = cs;
+        fe[wv][lane] = ce;
+        tg[wv][lane] = 0.0;
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        // candidates are distinct experts, so the ranks 0 .. total-1 are
+        // distinct and the top k are exactly ranks 0 .. k-1
+        // (all 8 entries read first, the test without short-circuit
+        // branches, so the reads overlap)
+        int rank = 0;
+        for (int j0 = 0; j0 < total; j0 += 8) {
+          double os[8];
+          int oe[8];
+#pragma unroll
+          for (int u = 0; u < 8; ++u) {
+            os[u] = fs[wv][j0 + u];
+            oe[u] = fe[wv][j0 + u];
+          }
+#pragma unroll
+          for (int u = 0; u < 8; ++u) rank += (int)((os[u] > cs) | ((os[u] == cs) & (oe[u] < ce)));
+        }
+        if (lane < total && rank < k) {
+          tg[wv][rank] = cg;
+          te[wv][rank] = ce;
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        if (lane < k) {
+          my_id = te[wv][lane];
+          g = tg[wv][lane];
+        }
         done = true;
       }
     }
@@ -394,12 +450,20 @@ __global__ __launch_bounds__(256) void route_topk_reg_kernel(const float* __rest
     }
   }
 
-  double g = 0.0;
-  if (lane < k) g = 1.0 / (1.0 + exp(-(double)zl[wv][my_id]));
+  if (!done && lane < k) g = sigmoid64(zt[my_id]);
   double sum = g;
   if (normalize) {
+    // in rank order; on the fast path from LDS in blocks of 8 (the slots
+    // past k hold zeros, which leave the sum unchanged)
     sum = 0.0;
-    for (int r = 0; r < k; ++r) sum += readlane_f64(g, r);  // lane by lane
+    if (done) {
+      for (int r0 = 0; r0 < k; r0 += 8) {
+#pragma unroll
+        for (int u = 0; u < 8; ++u) sum += tg[wv][r0 + u];
+      }
+    } else {
+      for (int r = 0; r < k; ++r) sum += readlane_f64(g, r);  // lane by lane
+    }
   }
   if (lane < k) {
     double v = normalize ? g / sum : g;
@@ -459,7 +523,7 @@ __global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict
 
   // Gate weights: sigmoid(z) of the selected experts (lane r holds slot r).
   double g = 0.0;
-  if (lane < k) g = 1.0 / (1.0 + exp(-(double)zt[my_id]));
+  if (lane < k) g = sigmoid64(zt[my_id]);
   double sum = g;
   if (normalize) {
     // Sum in slot order 0..k-1 so the result does not depend on a tree shape.
