@@ -752,7 +752,7 @@ def main():
 
     torch.cuda.set_device(0)
     if args.block is not None:
-        dev = upload_experts(moe_inputs.PREFILL, lambda p, s, out: k3.mxfp4_repack(p, s, blocks=out))
+        dev = upload_experts(moe_inputs.PREFILL, lambda p, s, out: k3.mxfp4_tile(k3.mxfp4_repack(p, s), out=out))
         r = measure_blocks(dev, k3, args.warmup, only=args.block)[args.block]
         print(json.dumps({"metric": "latent-MoE block tokens/s at K3 shape", "value": r["tokens_per_s"],
                           "unit": "tokens/s", "n_gpus": 1, "higher_is_better": True, "data": "synthetic",
@@ -760,7 +760,7 @@ def main():
         return
     cfg = moe_inputs.CONFIGS[args.workload]
     t_setup = time.perf_counter()
-    dev = upload_experts(cfg, lambda p, s, out: k3.mxfp4_repack(p, s, blocks=out))
+    dev = upload_experts(cfg, lambda p, s, out: k3.mxfp4_tile(k3.mxfp4_repack(p, s), out=out))
     torch.cuda.synchronize()
     setup_s = time.perf_counter() - t_setup
 

@@ -109,6 +109,32 @@ int mxfp4_repack(const uint8_t* packed, const uint8_t* scale, int64_t R, int64_t
                  void* stream);
 
 /*
+ * mxfp4_tile — reorder MXFP4 matrices from ggml row order into the stage-tiled
+ * order that moe_mxfp4_ffn, its variants, moe_expert_cache_route and
+ * moe_latent_block read. A pure permutation of whole 17-byte blocks (the block
+ * encoding is the one mxfp4_repack writes, from the same review comment); the
+ * order itself is this library's own: it makes every 16-row x 512-column
+ * piece of a matrix one contiguous run, so the kernels that stream weights
+ * read memory front to back.
+ *
+ *   src  u8 [nmat, N, K/32, 17]  matrices in ggml row order (row r, block b at
+ *                                block index r * K/32 + b)
+ *   dst  u8 [nmat, N, K/32, 17]  out: the same blocks, stage-tiled
+ *
+ * Stage-tiled order of one N x nb matrix (nb = K/32): rows in groups of 16,
+ * a group's blocks in stages of 16 (the last group and the last stage may be
+ * shorter); groups one after another, a group stage by stage, a stage row by
+ * row, a row's blocks in order. Block b of row r sits at block index
+ *   16*G*nb + 16*s*rG + (r % 16)*wS + (b % 16),
+ * G = r / 16, s = b / 16, rG = min(16, N - 16*G), wS = min(16, nb - 16*s).
+ * mxfp4_dequant decodes blocks in storage order, so on tiled data its output
+ * rows are permuted the same way. Sizes: nmat >= 0 (0 is a no-op), N >= 1,
+ * K > 0, K % 32 == 0, at most 2^31 - 1 pieces of 16 x 16 blocks in all.
+ * src and dst must not overlap (K3MOE_ERR_SHAPE).
+ */
+int mxfp4_tile(const uint8_t* src, int64_t nmat, int64_t N, int64_t K, uint8_t* dst, void* stream);
+
+/*
  * mxfp4_dequant — decode 17-byte ggml MXFP4 blocks.
  * Source: same review comment (ggml-side decode: dequantize_row_mxfp4 with
  * kvalues_fp4 = doubled E2M1 values and the half scale 2^(x-128), whose bits
@@ -144,8 +170,9 @@ size_t moe_mxfp4_ffn_workspace_size(int64_t T, int32_t D, int32_t I, int32_t E, 
  *   topk_ids i32  [T, k]        routed experts of each token
  *   topk_w   f32  [T, k]        gate weights
  *   w1, w3   u8 [E, I, D/32, 17] gate / up matrices ([I, D] per expert,
- *                               blocks along D) as ggml MXFP4 blocks
- *   w2       u8 [E, D, I/32, 17] down matrix ([D, I] per expert)
+ *                               blocks along D) as ggml MXFP4 blocks in the
+ *                               stage-tiled order of mxfp4_tile
+ *   w2       u8 [E, D, I/32, 17] down matrix ([D, I] per expert), likewise
  *   out      f32  [T, D]        out[t] = sum_j w[t,j] * W2 act(W1 x_t, W3 x_t)
  *   workspace device buffer of at least moe_mxfp4_ffn_workspace_size() bytes;
  *             its contents on entry do not matter and are clobbered
@@ -391,7 +418,9 @@ int moe_expert_cache_init(void* state, size_t state_bytes, int32_t E, int32_t C,
  *                           then computes exactly what it computes on the
  *                           store's experts with topk_ids
  *   store_w1, store_w3 u8 [E, I, D/32, 17], store_w2 u8 [E, D, I/32, 17]
- *                           all experts (pinned host memory, or device memory)
+ *                           all experts (pinned host memory, or device
+ *                           memory), stage-tiled as moe_mxfp4_ffn reads them
+ *                           (whole experts are copied unchanged)
  *   cache_w1, cache_w3 u8 [C, I, D/32, 17], cache_w2 u8 [C, D, I/32, 17]
  *                           device: the slots
  *

@@ -1,8 +1,9 @@
 """Upload a workload's synthetic inputs to the GPU.
 
 Data movement only: the caller passes the function that turns source-layout
-MXFP4 matrices into device blocks (the library's ``mxfp4_repack``), so this
-module itself performs none of the method's arithmetic.
+MXFP4 matrices into device blocks (the library's ``mxfp4_repack`` followed by
+``mxfp4_tile``), so this module itself performs none of the method's
+arithmetic.
 """
 
 from __future__ import annotations
@@ -26,7 +27,7 @@ def upload_experts(cfg: LayerConfig, repack, device="cuda", progress=None) -> De
     """Generate every expert's source-layout matrices and repack them on the device.
 
     ``repack(packed_dev, scale_dev, out=blocks_view)`` must write the 17-byte
-    blocks of one matrix into ``blocks_view``.
+    blocks of one matrix into ``blocks_view``, in the order the FFN reads.
     """
     E, D, I = cfg.E, cfg.D, cfg.I
     w1 = torch.empty((E, I, D // 32, 17), dtype=torch.uint8, device=device)

@@ -23,6 +23,7 @@ __all__ = [
     "moe_route_topk",
     "mxfp4_repack",
     "mxfp4_dequant",
+    "mxfp4_tile",
     "moe_mxfp4_ffn_workspace_size",
     "moe_mxfp4_ffn",
     "moe_mxfp4_ffn_noalloc",
@@ -65,6 +66,8 @@ lib.mxfp4_repack.restype = ctypes.c_int
 lib.mxfp4_repack.argtypes = [_vp, _vp, _i64, _i64, _vp, _vp]
 lib.mxfp4_dequant.restype = ctypes.c_int
 lib.mxfp4_dequant.argtypes = [_vp, _i64, _i64, _i32, _vp, _vp]
+lib.mxfp4_tile.restype = ctypes.c_int
+lib.mxfp4_tile.argtypes = [_vp, _i64, _i64, _i64, _vp, _vp]
 lib.moe_mxfp4_ffn_workspace_size.restype = _sz
 lib.moe_mxfp4_ffn_workspace_size.argtypes = [_i64, _i32, _i32, _i32, _i32]
 lib.moe_mxfp4_ffn.restype = ctypes.c_int
@@ -184,6 +187,26 @@ def mxfp4_repack(packed: torch.Tensor, scale: torch.Tensor, blocks: torch.Tensor
         raise ValueError("blocks has the wrong size")
     _check("mxfp4_repack", lib.mxfp4_repack(_ptr(packed), _ptr(scale), R, K, _ptr(blocks), _stream(packed.device)))
     return blocks
+
+
+def mxfp4_tile(blocks: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    """ggml-row-order MXFP4 matrices u8 [..., N, K/32, 17] -> the same blocks in
+    the stage-tiled order the FFN entry points read (same shape; leading
+    dimensions are separate matrices)."""
+    _dev(blocks, "blocks", torch.uint8)
+    if blocks.dim() < 3 or blocks.shape[-1] != 17:
+        raise ValueError("blocks must be [..., N, K/32, 17]")
+    N, nb = blocks.shape[-3], blocks.shape[-2]
+    nmat = blocks.numel() // (N * nb * 17) if N * nb else 0
+    if out is None:
+        out = torch.empty_like(blocks)
+    _dev(out, "out", torch.uint8)
+    if out.numel() != blocks.numel():
+        raise ValueError("out has the wrong size")
+    if blocks.numel() == 0:
+        return out
+    _check("mxfp4_tile", lib.mxfp4_tile(_ptr(blocks), nmat, N, nb * 32, _ptr(out), _stream(blocks.device)))
+    return out
 
 
 def mxfp4_dequant(blocks: torch.Tensor, out_dtype: torch.dtype = torch.float32,

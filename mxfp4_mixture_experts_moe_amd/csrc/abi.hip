@@ -437,6 +437,20 @@ int mxfp4_repack(const uint8_t* packed, const uint8_t* scale, int64_t R, int64_t
   return device_status(launch_repack(packed, scale, nblocks, blocks, static_cast<hipStream_t>(stream)));
 }
 
+int mxfp4_tile(const uint8_t* src, int64_t nmat, int64_t N, int64_t K, uint8_t* dst, void* stream) {
+  if (nmat < 0 || N < 1 || N > 0x7FFFFFFF || K <= 0 || (K % 32) != 0 || K / 32 > 0x7FFFFFFF) return K3MOE_ERR_SHAPE;
+  const int64_t nb = K / 32;
+  const int64_t pieces = ((N + 15) / 16) * ((nb + 15) / 16);
+  if (nmat > 0 && pieces > 0x7FFFFFFF / nmat) return K3MOE_ERR_SHAPE;
+  if (nmat == 0) return K3MOE_OK;
+  if (!src || !dst) return K3MOE_ERR_NULL;
+  if (misaligned(src) || misaligned(dst)) return K3MOE_ERR_ALIGN;
+  const uint64_t bytes = (uint64_t)nmat * (uint64_t)N * (uint64_t)nb * 17u;
+  const uintptr_t a = (uintptr_t)src, b = (uintptr_t)dst;
+  if (a < b + bytes && b < a + bytes) return K3MOE_ERR_SHAPE;  // overlapping buffers
+  return device_status(launch_tile(src, nmat, (int)N, (int)nb, dst, static_cast<hipStream_t>(stream)));
+}
+
 int mxfp4_dequant(const uint8_t* blocks, int64_t R, int64_t K, int32_t out_dtype, void* out, void* stream) {
   if (R < 0 || K <= 0 || (K % 32) != 0) return K3MOE_ERR_SHAPE;
   if (out_dtype != K3MOE_DTYPE_F32 && out_dtype != K3MOE_DTYPE_BF16) return K3MOE_ERR_UNSUPPORTED;

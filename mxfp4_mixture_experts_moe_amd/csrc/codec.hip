@@ -1,5 +1,6 @@
-// MXFP4 codec kernels: compressed-tensors layout -> 17-byte ggml blocks, and
-// ggml blocks -> fp32 / bf16 values.
+// MXFP4 codec kernels: compressed-tensors layout -> 17-byte ggml blocks,
+// ggml blocks -> fp32 / bf16 values, and ggml row order -> the stage-tiled
+// order the FFN kernels read.
 //
 // Layouts (llama.cpp pull request "model: add Kimi-K3 text model", review
 // comment "repack_mxfp4_blocks is bit-exact"):
@@ -156,7 +157,52 @@ __global__ __launch_bounds__(256) void dequant_kernel(const uint8_t* __restrict_
   }
 }
 
+// ----------------------------------------------------------------------------
+// Tile: ggml row order -> stage-tiled order (tiled_block_index).  Workgroup
+// (matrix, group G, stage s) moves one piece: its rG rows of wS blocks, row r
+// from source blocks (16G + r) * nb + 16s onwards to the piece's row r.  With
+// nb a multiple of 16 every row of a piece is 272 bytes at 16-byte aligned
+// offsets on both sides and moves as 17 chunks of 16 bytes; otherwise bytes.
+template <bool kVec16>
+__global__ __launch_bounds__(256) void tile_kernel(const uint8_t* __restrict__ src, int N, int nb, int ngroups,
+                                                    int nstages, uint8_t* __restrict__ dst) {
+  const int64_t piece = blockIdx.x;
+  const int s = (int)(piece % nstages);
+  const int64_t mg = piece / nstages;
+  const int G = (int)(mg % ngroups);
+  const int64_t m = mg / ngroups;
+  const int rG = N - 16 * G < 16 ? N - 16 * G : 16;
+  const int wS = nb - 16 * s < 16 ? nb - 16 * s : 16;
+  const int64_t mat = m * (int64_t)N * nb * 17;
+  const int64_t src0 = mat + ((int64_t)16 * G * nb + 16 * s) * 17;  // row 0 of the piece in the source
+  const int64_t dst0 = mat + tiled_block_index(N, nb, 16 * G, 16 * s) * 17;
+  const int64_t src_row = (int64_t)nb * 17;
+  if (kVec16) {
+    for (int i = threadIdx.x; i < rG * 17; i += 256) {
+      const int r = i / 17, c = i - 17 * r;
+      *reinterpret_cast<uint4*>(dst + dst0 + 272 * r + 16 * c) =
+          *reinterpret_cast<const uint4*>(src + src0 + src_row * r + 16 * c);
+    }
+  } else {
+    const int row_b = wS * 17;
+    for (int i = threadIdx.x; i < rG * row_b; i += 256) {
+      const int r = i / row_b, c = i - row_b * r;
+      dst[dst0 + (int64_t)row_b * r + c] = src[src0 + src_row * r + c];
+    }
+  }
+}
+
 }  // namespace
+
+hipError_t launch_tile(const uint8_t* src, int64_t nmat, int N, int nb, uint8_t* dst, hipStream_t s) {
+  const int ngroups = (N + 15) / 16, nstages = (nb + 15) / 16;
+  const int64_t wgs = nmat * ngroups * nstages;
+  if (nb % 16 == 0)
+    hipLaunchKernelGGL(tile_kernel<true>, dim3((unsigned)wgs), dim3(256), 0, s, src, N, nb, ngroups, nstages, dst);
+  else
+    hipLaunchKernelGGL(tile_kernel<false>, dim3((unsigned)wgs), dim3(256), 0, s, src, N, nb, ngroups, nstages, dst);
+  return hipGetLastError();
+}
 
 hipError_t launch_repack(const uint8_t* packed, const uint8_t* scale, int64_t nblocks, uint8_t* blocks,
                          hipStream_t s) {

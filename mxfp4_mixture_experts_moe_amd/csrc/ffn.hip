@@ -24,7 +24,8 @@
 // Work decomposition: a workgroup of 4 waves computes 64 output features for
 // one tile of up to 16*NT grouped rows of one expert.  Weight rows are staged
 // through LDS one K segment (up to 16 blocks = 272 bytes per row) at a time
-// with coalesced loads; each wave decodes its own 16 rows.
+// with coalesced loads (in the stage-tiled weight order a segment of 16 rows
+// is one contiguous run); each wave decodes its own 16 rows.
 #include "k3moe_internal.h"
 
 #include <math.h>
@@ -66,32 +67,37 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
   return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)f);  // round to nearest even
 }
 
-// Stage rows [0, nrows) x bytes [byte0, byte0 + seg_bytes) of a weight tile
-// into LDS (row r at dword r * kLdsRowDw); rows nrows..63 are left as they
-// are (the MFMA rows they feed are never stored).
-// kVec16: rows and the segment are 16-byte aligned and 272 bytes long.
-// Otherwise dword copies when rows and the segment are 4-byte multiples, and
-// byte copies for the rest (K not a multiple of 128).
+// Stage K segment `seg` (nbs blocks: 16, fewer in a last segment) of rows
+// f0 .. f0 + nrows - 1 of one expert's stage-tiled matrix `w` (N rows x nb
+// blocks) into LDS (row r at dword r * kLdsRowDw); rows nrows..63 are left
+// as they are (the MFMA rows they feed are never stored).  In the tiled order
+// a row's blocks of one segment are contiguous, starting at block
+// tiled_block_index(N, nb, row, 16 * seg).
+// kVec16 (nb a multiple of 16): every row piece is 272 bytes at a 16-byte
+// aligned offset.  Otherwise dword copies when nb is a multiple of 4 (then
+// every piece's offset and length are), and byte copies for the rest.
 template <bool kVec16>
-__device__ __forceinline__ void stage_weights(const uint8_t* __restrict__ w, size_t row_bytes, size_t byte0,
-                                              int seg_bytes, int nrows, uint32_t* lds) {
+__device__ __forceinline__ void stage_weights(const uint8_t* __restrict__ w, int N, int nb, int f0, int seg,
+                                              int nbs, int nrows, uint32_t* lds) {
   if (kVec16) {
     for (int idx = threadIdx.x; idx < nrows * 17; idx += blockDim.x) {
       const int r = idx / 17, c = idx - r * 17;
-      const uint4 v = *reinterpret_cast<const uint4*>(w + r * row_bytes + byte0 + 16 * c);
-      *reinterpret_cast<uint4*>(lds + r * kLdsRowDw + 4 * c) = v;
+      const uint8_t* src = w + tiled_block_index(N, nb, f0 + r, 16 * seg) * 17;
+      *reinterpret_cast<uint4*>(lds + r * kLdsRowDw + 4 * c) = *reinterpret_cast<const uint4*>(src + 16 * c);
     }
-  } else if (((row_bytes | byte0 | (size_t)seg_bytes) & 3) == 0) {
-    const int dpr = seg_bytes >> 2;
+  } else if ((nb & 3) == 0) {
+    const int dpr = nbs * 17 / 4;
     for (int idx = threadIdx.x; idx < nrows * dpr; idx += blockDim.x) {
       const int r = idx / dpr, c = idx - r * dpr;
-      lds[r * kLdsRowDw + c] = *reinterpret_cast<const uint32_t*>(w + r * row_bytes + byte0 + 4 * c);
+      const uint8_t* src = w + tiled_block_index(N, nb, f0 + r, 16 * seg) * 17;
+      lds[r * kLdsRowDw + c] = *reinterpret_cast<const uint32_t*>(src + 4 * c);
     }
   } else {
     uint8_t* lb = reinterpret_cast<uint8_t*>(lds);
+    const int seg_bytes = nbs * 17;
     for (int idx = threadIdx.x; idx < nrows * seg_bytes; idx += blockDim.x) {
       const int r = idx / seg_bytes, c = idx - r * seg_bytes;
-      lb[r * kLdsRowDw * 4 + c] = w[r * row_bytes + byte0 + c];
+      lb[r * kLdsRowDw * 4 + c] = w[tiled_block_index(N, nb, f0 + r, 16 * seg) * 17 + c];
     }
   }
 }
@@ -135,8 +141,8 @@ __global__ __launch_bounds__(256) void ffn_gemm_kernel(GemmArgs a) {
   const int nb = a.K >> 5;
   const size_t row_bytes = (size_t)nb * 17;
   const size_t mat_bytes = (size_t)a.N * row_bytes;
-  const uint8_t* wA = a.wa + (size_t)tile.expert * mat_bytes + (size_t)f0 * row_bytes;
-  const uint8_t* wB = kGateUp ? a.wb + (size_t)tile.expert * mat_bytes + (size_t)f0 * row_bytes : nullptr;
+  const uint8_t* wA = a.wa + (size_t)tile.expert * mat_bytes;
+  const uint8_t* wB = kGateUp ? a.wb + (size_t)tile.expert * mat_bytes : nullptr;
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int rho = lane & 15, g = lane >> 4;
@@ -169,8 +175,8 @@ __global__ __launch_bounds__(256) void ffn_gemm_kernel(GemmArgs a) {
   for (int seg0 = 0; seg0 < nb; seg0 += kSegBlocks) {
     const int nbs = (nb - seg0) < kSegBlocks ? (nb - seg0) : kSegBlocks;
     __syncthreads();  // previous segment fully consumed
-    stage_weights<kVec16>(wA, row_bytes, (size_t)seg0 * 17, nbs * 17, nfeat, wlds[0]);
-    if (kGateUp) stage_weights<kVec16>(wB, row_bytes, (size_t)seg0 * 17, nbs * 17, nfeat, wlds[kMats - 1]);
+    stage_weights<kVec16>(wA, a.N, nb, f0, seg0 / kSegBlocks, nbs, nfeat, wlds[0]);
+    if (kGateUp) stage_weights<kVec16>(wB, a.N, nb, f0, seg0 / kSegBlocks, nbs, nfeat, wlds[kMats - 1]);
     __syncthreads();
     if (!wave_live) continue;  // no feature of this wave exists (uniform over the wave)
     for (int rnd = 0; rnd < ((nbs + 3) >> 2); ++rnd) {

@@ -244,7 +244,11 @@ __global__ __launch_bounds__(kThreads) void ffn_big_kernel(GemmArgs a) {
     const int cw = r_tile / (C::kRG * 16);           // consumer wave
     const int r = r_tile - cw * (C::kRG * 16);       // (row group, rho) within the consumer wave
     const int feat_in_wave = kGateUp ? p_to_elem(r) : r;
-    woffs[j] = (uint32_t)((cw * (C::kRG * 16) + feat_in_wave) * row_bytes) + 16 * ch;
+    // stage-tiled weights (tiled_block_index; N and nb multiples of 16):
+    // row f of the tile is row f % 16 of group f / 16, 272 bytes per row in
+    // a stage; the K step adds its stage's offset in the scalar offset
+    const int f = cw * (C::kRG * 16) + feat_in_wave;
+    woffs[j] = (uint32_t)((f >> 4) * 16 * row_bytes) + (uint32_t)(f & 15) * 272u + 16 * ch;
   }
   // Activations: wave w fills rows 16w..16w+15 (272 flat 16-byte chunks), all
   // of one source (x / h_hi for gate/up, h_hi or h_lo for down); load j moves
@@ -275,7 +279,9 @@ __global__ __launch_bounds__(kThreads) void ffn_big_kernel(GemmArgs a) {
     uint32_t* const lb = buf ? lds1 : lds0;
     uint32_t* wl = lb + 64 * wave * kWRowDw;
     uint32_t* al = lb + kWDw + 272 * 4 * wave;
-    const int wso = 64 * stage + 16 * (stage >> 2);  // 16-byte aligned start of the step's 68 bytes
+    // 16-byte aligned start of the step's 68 bytes: byte 68 * (stage % 4) of
+    // the row's 272 bytes in 512-wide stage stage / 4 (4352 bytes per stage)
+    const int wso = 4352 * (stage >> 2) + 64 * (stage & 3);
 #pragma unroll
     for (int j = 0; j < kWRowChunks; ++j) __builtin_amdgcn_raw_ptr_buffer_load_lds(wrsrc, wl + 256 * j, 16, woffs[j], wso, 0, 0);
     if (aload) {

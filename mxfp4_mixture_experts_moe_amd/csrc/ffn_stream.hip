@@ -15,6 +15,10 @@
 //     one it decodes; no workgroup barrier anywhere;
 //   - a stage is 16 MXFP4 blocks (512 K) of each row: 272 bytes, 17 aligned
 //     16-byte chunks, so rows of 1904 / 1632 bytes stream without over-fetch;
+//     the weights are stage-tiled (tiled_block_index), so the stage of a
+//     16-row block is one contiguous 4352-byte run and a unit's weights are
+//     read front to back (HBM delivers a fifth less when the same bytes are
+//     read as 272-byte pieces of rows 1904 bytes apart);
 //   - the tile's activation rows for the same 512 K (x for gate/up, h_hi and
 //     h_lo for down) ride in the same stage, one 1 KB load per row the tile
 //     actually has (the wait counts follow the per-stage load count); for down
@@ -52,6 +56,7 @@ constexpr int kRowDw = 68;           // LDS dwords per staged weight row
 constexpr int kBRowBytes = 1040;     // LDS bytes per activation row per stage (1024 + 16 padding)
 constexpr int kRB = 2;               // 16-row weight blocks per wave and stage
 constexpr int kWInstr = kRB * 5;     // global -> LDS weight loads per stage (5 per 16-row block)
+constexpr int kNt = 2;               // cache policy of the weight loads: nontemporal (read once per call)
 
 // A unit is kFeat output features of one tile.  gate/up: row block 0 is w1,
 // row block 1 is w3, both rows 16*fg .. 16*fg + 15.  down: both row blocks
@@ -90,19 +95,17 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
   return (uint32_t)__builtin_bit_cast(uint16_t, (__bf16)f);
 }
 
-// Block (4*rnd + g) of staged row `lrow`: four bf16x8 operands (P-order
-// positions 8i..8i+7, i = 0..3).  The block starts at byte 68*rnd + 17*g of the
-// row, i.e. at byte g of dword 17*rnd + 4*g; its qs dword i is bytes
-// g+1+4i .. g+4+4i, picked out of two neighbouring dwords with v_perm.
-__device__ __forceinline__ void decode_block(const uint32_t* w, int lrow, int rnd, int g, uint32_t qsel,
-                                             bf16x8_t op[4]) {
-  const uint32_t* L = w + lrow * kRowDw + 17 * rnd + 4 * g;
-  const uint32_t d0 = L[0], d1 = L[1], d2 = L[2], d3 = L[3], d4 = L[4];
-  const float sf = e8m0_to_f32(__builtin_amdgcn_ubfe(d0, 8 * g, 8));
-  op[0] = decode_dword(__builtin_amdgcn_perm(d1, d0, qsel), sf);
-  op[1] = decode_dword(__builtin_amdgcn_perm(d2, d1, qsel), sf);
-  op[2] = decode_dword(__builtin_amdgcn_perm(d3, d2, qsel), sf);
-  op[3] = decode_dword(__builtin_amdgcn_perm(d4, d3, qsel), sf);
+// Block (4*rnd + g) of a staged row: four bf16x8 operands (P-order
+// positions 8i..8i+7, i = 0..3) from the five dwords d[0..4] (LDS dwords
+// 17*rnd + 4*g .. +4 of the row).  The block starts at byte g of d[0], so its
+// exponent is byte g and its qs dword i is bytes g+1+4i .. g+4+4i, picked out
+// of two neighbouring dwords with v_perm.
+__device__ __forceinline__ void decode_dwords(const uint32_t (&d)[5], int g, uint32_t qsel, bf16x8_t op[4]) {
+  const float sf = e8m0_to_f32(__builtin_amdgcn_ubfe(d[0], 8 * g, 8));
+  op[0] = decode_dword(__builtin_amdgcn_perm(d[1], d[0], qsel), sf);
+  op[1] = decode_dword(__builtin_amdgcn_perm(d[2], d[1], qsel), sf);
+  op[2] = decode_dword(__builtin_amdgcn_perm(d[3], d[2], qsel), sf);
+  op[3] = decode_dword(__builtin_amdgcn_perm(d[4], d[3], qsel), sf);
 }
 
 // Tile list and token map are read through the constant address space so that
@@ -156,19 +159,27 @@ __device__ __forceinline__ void block_scan3(int (&v)[3], int (&tot)[3], int (*ws
 
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
-// One round's activation operands of one lane when x rows sit in LDS in their
-// natural order: the 64 bytes of block 4 rnd + g, as four 16-byte reads from
-// `p`.  The reads and their wait are one asm block: written as plain loads,
-// the compiler orders them behind every global -> LDS load in flight, which
-// empties the stage ring each step.  One block per round, so the wait overlaps
-// the previous round's MFMAs.
-__device__ __forceinline__ void read_x_block(const uint8_t* p, u32x4_t (&q)[4]) {
+// The whole stage's activation operands of one lane when x rows sit in LDS in
+// their natural order: block 4 rnd + g of each round rnd, 64 bytes at p +
+// 256 rnd, as sixteen 16-byte reads and their wait in one asm block, so the
+// LDS latency is paid once per stage.  Written as plain loads, the compiler
+// orders these reads behind every global -> LDS load in flight, which empties
+// the stage ring each step.
+__device__ __forceinline__ void read_x_stage(const uint8_t* p, u32x4_t (&q)[4][4]) {
   const uint32_t a = (uint32_t)(uintptr_t)p;  // LDS byte address
   asm volatile(
-      "ds_read_b128 %0, %4\n\tds_read_b128 %1, %4 offset:16\n\t"
-      "ds_read_b128 %2, %4 offset:32\n\tds_read_b128 %3, %4 offset:48\n\t"
+      "ds_read_b128 %0, %16\n\tds_read_b128 %1, %16 offset:16\n\t"
+      "ds_read_b128 %2, %16 offset:32\n\tds_read_b128 %3, %16 offset:48\n\t"
+      "ds_read_b128 %4, %16 offset:256\n\tds_read_b128 %5, %16 offset:272\n\t"
+      "ds_read_b128 %6, %16 offset:288\n\tds_read_b128 %7, %16 offset:304\n\t"
+      "ds_read_b128 %8, %16 offset:512\n\tds_read_b128 %9, %16 offset:528\n\t"
+      "ds_read_b128 %10, %16 offset:544\n\tds_read_b128 %11, %16 offset:560\n\t"
+      "ds_read_b128 %12, %16 offset:768\n\tds_read_b128 %13, %16 offset:784\n\t"
+      "ds_read_b128 %14, %16 offset:800\n\tds_read_b128 %15, %16 offset:816\n\t"
       "s_waitcnt lgkmcnt(0)"
-      : "=&v"(q[0]), "=&v"(q[1]), "=&v"(q[2]), "=&v"(q[3])
+      : "=&v"(q[0][0]), "=&v"(q[0][1]), "=&v"(q[0][2]), "=&v"(q[0][3]), "=&v"(q[1][0]), "=&v"(q[1][1]),
+        "=&v"(q[1][2]), "=&v"(q[1][3]), "=&v"(q[2][0]), "=&v"(q[2][1]), "=&v"(q[2][2]), "=&v"(q[2][3]),
+        "=&v"(q[3][0]), "=&v"(q[3][1]), "=&v"(q[3][2]), "=&v"(q[3][3])
       : "v"(a)
       : "memory");
 }
@@ -359,17 +370,18 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ffn_stream_kernel(GemmArgs a, 
   const size_t mat_bytes = (size_t)a.N * row_bytes;
   const uint32_t act_row_bytes = (uint32_t)a.K * 2;
 
-  // Per-lane byte offset of weight chunk c = 64j + lane of one matrix's
-  // stage (MFMA row rr = c / 17 is feature 16*fg + rr; chunk ch = c % 17),
-  // relative to the unit's first row; the stage adds 272*s in the scalar
-  // offset.  Only the last load of a matrix is partial (lanes < 16).
+  // The weights are stage-tiled (tiled_block_index): stage s of a 16-row
+  // group is one contiguous run of 16 rows x 272 bytes, laid out exactly as
+  // the LDS stage holds it, so chunk c = 64j + lane of one matrix's stage is
+  // byte 16c of the run (MFMA row c / 17, chunk c % 17) and the stage adds
+  // 4352*s in the scalar offset.  Only the last load of a matrix is partial
+  // (lanes < 16).
   constexpr int kInstrPerMat = (16 * kRowChunks + 63) / 64;  // 5
   uint32_t woff[kInstrPerMat];
 #pragma unroll
   for (int j = 0; j < kInstrPerMat; ++j) {
     const int c = 64 * j + lane;
-    const int rr = c / kRowChunks, ch = c - rr * kRowChunks;
-    woff[j] = c < 16 * kRowChunks ? (uint32_t)rr * row_bytes + 16 * ch : 0u;
+    woff[j] = c < 16 * kRowChunks ? 16u * (uint32_t)c : 0u;
   }
   const bool wtail = lane < 16 * kRowChunks - 64 * (kInstrPerMat - 1);  // lanes of the partial load
 
@@ -397,7 +409,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ffn_stream_kernel(GemmArgs a, 
   auto issue = [&](const Cursor& c, int buf) -> int {
     uint8_t* dst = &lds[wave][buf][0];
     const size_t unit_off = (size_t)c.tile.expert * mat_bytes + (size_t)(C::kFeat * c.fg) * row_bytes;
-    const uint32_t wso = (uint32_t)(kStageRowBytes * c.s);
+    const uint32_t wso = (uint32_t)(16 * kStageRowBytes * c.s);
 #pragma unroll
     for (int mi = 0; mi < kRB; ++mi) {
       const uint8_t* base =
@@ -407,11 +419,11 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ffn_stream_kernel(GemmArgs a, 
 #pragma unroll
       for (int j = 0; j < kInstrPerMat - 1; ++j)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (__attribute__((address_space(3))) void*)(uintptr_t)(dst + mi * kMatBytes + 1024 * j),
-                                                 16, woff[j], wso, 0, 0);
+                                                 16, woff[j], wso, 0, kNt);
       if (wtail)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
             rsrc, (__attribute__((address_space(3))) void*)(uintptr_t)(dst + mi * kMatBytes + 1024 * (kInstrPerMat - 1)), 16,
-            woff[kInstrPerMat - 1], wso, 0, 0);
+            woff[kInstrPerMat - 1], wso, 0, kNt);
     }
     uint8_t* bdst = dst + kWBytes;
     const uint32_t aso = (uint32_t)(kStageK * 2 * c.s);
@@ -436,9 +448,9 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ffn_stream_kernel(GemmArgs a, 
     return (kGateUp ? 1 : 2) * c.tile.nrows;
   };
 
-  f32x4_t acc[kRB];
+  f32x4_t acc[kRB][2];  // per row block: the even and the odd rounds
 #pragma unroll
-  for (int mi = 0; mi < kRB; ++mi) acc[mi] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int mi = 0; mi < kRB; ++mi) acc[mi][0] = acc[mi][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   const uint32_t qsel = 0x03020100u + 0x01010101u * (uint32_t)(g + 1);
   Cursor ci{wid, 0, 0, {0, 0, 0, 0}};  // issue side
@@ -483,18 +495,23 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ffn_stream_kernel(GemmArgs a, 
     buf_c = buf_c == kRing - 1 ? 0 : buf_c + 1;
     const uint32_t* wl = reinterpret_cast<const uint32_t*>(st);
     const uint8_t* bl = st + boff;
+    // Every LDS read of the stage first (the activation operands of the four
+    // rounds, the five weight dwords per round and row block), then the
+    // decodes two rounds at a time and the MFMAs on four accumulator chains
+    // (row block x round parity), so neither the LDS latency nor an MFMA's
+    // dependence on the previous one is exposed each round.
+    bf16x8_t bop[4][4];
+    if constexpr (kNatX) {
+      // x rows in natural order: P-order dword t of operand i pairs
+      // elements 4i + t and 16 + 4i + t of block 4*rnd + g
+      u32x4_t q[4][4];  // per round: elements 0-7, 8-15, 16-23, 24-31
+      read_x_stage(bl + 64 * g, q);
 #pragma unroll
-    for (int rnd = 0; rnd < 4; ++rnd) {
-      bf16x8_t bop[4];
-      if constexpr (kNatX) {
-        // x rows in natural order: P-order dword t of operand i pairs
-        // elements 4i + t and 16 + 4i + t of block 4*rnd + g
-        u32x4_t q[4];  // elements 0-7, 8-15, 16-23, 24-31
-        read_x_block(bl + 64 * (4 * rnd + g), q);
+      for (int rnd = 0; rnd < 4; ++rnd)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const u32x4_t& L = q[i >> 1];
-          const u32x4_t& H = q[2 + (i >> 1)];
+          const u32x4_t& L = q[rnd][i >> 1];
+          const u32x4_t& H = q[rnd][2 + (i >> 1)];
           const uint32_t l0 = (i & 1) ? L.z : L.x, l1 = (i & 1) ? L.w : L.y;
           const uint32_t h0 = (i & 1) ? H.z : H.x, h1 = (i & 1) ? H.w : H.y;
           uint4 r;
@@ -502,19 +519,35 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ffn_stream_kernel(GemmArgs a, 
           r.y = __builtin_amdgcn_perm(h0, l0, 0x07060302u);
           r.z = __builtin_amdgcn_perm(h1, l1, 0x05040100u);
           r.w = __builtin_amdgcn_perm(h1, l1, 0x07060302u);
-          bop[i] = __builtin_bit_cast(bf16x8_t, r);
+          bop[rnd][i] = __builtin_bit_cast(bf16x8_t, r);
         }
-      } else {
+    } else {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) bop[i] = *reinterpret_cast<const bf16x8_t*>(bl + 64 * (4 * rnd + g) + 16 * i);
-      }
+      for (int rnd = 0; rnd < 4; ++rnd)
 #pragma unroll
-      for (int mi = 0; mi < kRB; ++mi) {
-        bf16x8_t aop[4];
-        decode_block(wl, 16 * mi + rho, rnd, g, qsel, aop);
+        for (int i = 0; i < 4; ++i) bop[rnd][i] = *reinterpret_cast<const bf16x8_t*>(bl + 64 * (4 * rnd + g) + 16 * i);
+    }
+    uint32_t wd[kRB][4][5];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) acc[mi] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop[i], bop[i], acc[mi], 0, 0, 0);
-      }
+    for (int mi = 0; mi < kRB; ++mi)
+#pragma unroll
+      for (int rnd = 0; rnd < 4; ++rnd)
+#pragma unroll
+        for (int j = 0; j < 5; ++j) wd[mi][rnd][j] = wl[(16 * mi + rho) * kRowDw + 17 * rnd + 4 * g + j];
+#pragma unroll
+    for (int r0 = 0; r0 < 4; r0 += 2) {
+      bf16x8_t aop[kRB][2][4];
+#pragma unroll
+      for (int mi = 0; mi < kRB; ++mi)
+#pragma unroll
+        for (int rr = 0; rr < 2; ++rr) decode_dwords(wd[mi][r0 + rr], g, qsel, aop[mi][rr]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int rr = 0; rr < 2; ++rr)
+#pragma unroll
+          for (int mi = 0; mi < kRB; ++mi)
+            acc[mi][rr] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop[mi][rr][i], bop[r0 + rr][i], acc[mi][rr], 0, 0, 0);
     }
 
     if (cc.s == nst - 1) {
@@ -522,12 +555,15 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ffn_stream_kernel(GemmArgs a, 
       // of each 16-row block.
       const TileInfo& tile = cc.tile;
       const int fg = cc.fg;
+      f32x4_t sum[kRB];
+#pragma unroll
+      for (int mi = 0; mi < kRB; ++mi) sum[mi] = acc[mi][0] + acc[mi][1];
       if (!kGateUp) {
         // y = (h_hi part in column rho) + (h_lo part in column rho + kTileRows)
 #pragma unroll
         for (int mi = 0; mi < kRB; ++mi)
 #pragma unroll
-          for (int v = 0; v < 4; ++v) acc[mi][v] += __shfl_down(acc[mi][v], kTileRows, 16);
+          for (int v = 0; v < 4; ++v) sum[mi][v] += __shfl_down(sum[mi][v], kTileRows, 16);
       }
       if (rho < tile.nrows) {
         const int64_t row = tile.row0 + rho;
@@ -535,7 +571,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ffn_stream_kernel(GemmArgs a, 
           uint32_t hb[4], lb[4];
 #pragma unroll
           for (int v = 0; v < 4; ++v) {
-            const float gt = acc[0][v], up = acc[1][v];
+            const float gt = sum[0][v], up = sum[1][v];
             const float h = gt / (1.0f + expf(-gt)) * up;
             hb[v] = f32_to_bf16_bits(h);
             lb[v] = f32_to_bf16_bits(h - __uint_as_float(hb[v] << 16));
@@ -554,11 +590,11 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ffn_stream_kernel(GemmArgs a, 
           float* yrow = reinterpret_cast<float*>(a.out) + row * a.N + C::kFeat * fg + 4 * g;
 #pragma unroll
           for (int mi = 0; mi < kRB; ++mi)
-            *reinterpret_cast<float4*>(yrow + 16 * mi) = make_float4(acc[mi][0], acc[mi][1], acc[mi][2], acc[mi][3]);
+            *reinterpret_cast<float4*>(yrow + 16 * mi) = make_float4(sum[mi][0], sum[mi][1], sum[mi][2], sum[mi][3]);
         }
       }
 #pragma unroll
-      for (int mi = 0; mi < kRB; ++mi) acc[mi] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      for (int mi = 0; mi < kRB; ++mi) acc[mi][0] = acc[mi][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
     advance(cc);
     if (cc.s == 0 && q + 1 < Q) boff = kWBytes + kBRowBytes * brow_of(cc.tile.nrows);

@@ -62,6 +62,22 @@ hipError_t launch_route_topk(const float* z, const float* bias, int64_t T, int E
 hipError_t launch_repack(const uint8_t* packed, const uint8_t* scale, int64_t nblocks, uint8_t* blocks,
                          hipStream_t s);
 hipError_t launch_dequant(const uint8_t* blocks, int64_t nblocks, int out_bf16, void* out, hipStream_t s);
+hipError_t launch_tile(const uint8_t* src, int64_t nmat, int N, int nb, uint8_t* dst, hipStream_t s);
+
+// Stage-tiled order of an MXFP4 matrix of N rows x nb 17-byte blocks (the
+// order mxfp4_tile writes and the FFN kernels read): rows in groups of 16 and
+// a group's blocks in stages of 16 (the last group / stage may be shorter);
+// groups one after another, a group stage by stage, a stage row by row, a
+// row's blocks in order.  So a stage of a group (16 rows x 16 blocks, 4352
+// bytes) is one contiguous piece, and a kernel that streams a 16-row group
+// one 512-wide K stage at a time reads memory front to back.  Block index of
+// block b of row r.
+__host__ __device__ inline int64_t tiled_block_index(int N, int nb, int r, int b) {
+  const int G = r >> 4, rr = r & 15, s = b >> 4, bb = b & 15;
+  const int rG = N - 16 * G < 16 ? N - 16 * G : 16;
+  const int wS = nb - 16 * s < 16 ? nb - 16 * s : 16;
+  return (int64_t)16 * G * nb + (int64_t)16 * s * rG + (int64_t)rr * wS + bb;
+}
 
 struct GroupArgs {
   const int32_t* ids;

@@ -57,6 +57,7 @@ def k3_experts(k3):
     every GPU test module that needs them."""
     import moe_inputs
     from moe_inputs.device import upload_experts
+    from tests.gpu_util import expert_blocks
 
     print("[k3] uploading 896 K3 experts", flush=True)
-    return upload_experts(moe_inputs.PREFILL, lambda p, s, out: k3.mxfp4_repack(p, s, blocks=out))
+    return upload_experts(moe_inputs.PREFILL, expert_blocks(k3))

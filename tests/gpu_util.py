@@ -25,6 +25,12 @@ def assert_ffn_close(got, ref, what=""):
     assert max_abs <= FFN_MAX_ABS_FRAC * scale, (what, max_abs, scale)
 
 
+def expert_blocks(k3):
+    """Upload step of one expert matrix: source layout -> ggml blocks
+    (mxfp4_repack) -> the stage-tiled order the FFN reads (mxfp4_tile)."""
+    return lambda p, s, out: k3.mxfp4_tile(k3.mxfp4_repack(p, s), out=out)
+
+
 def to_dev_u8(a: np.ndarray) -> torch.Tensor:
     return torch.from_numpy(np.ascontiguousarray(a)).cuda()
 

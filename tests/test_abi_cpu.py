@@ -23,7 +23,7 @@ def declared_functions():
 
 def test_library_exports_every_declared_symbol(k3):
     names = declared_functions()
-    assert set(names) == {"k3moe_status_str", "moe_route_topk", "mxfp4_repack", "mxfp4_dequant",
+    assert set(names) == {"k3moe_status_str", "moe_route_topk", "mxfp4_repack", "mxfp4_dequant", "mxfp4_tile",
                           "moe_mxfp4_ffn_workspace_size", "moe_mxfp4_ffn", "moe_mxfp4_ffn_profiled",
                           "moe_mxfp4_ffn_noalloc", "moe_group_workspace_size", "moe_group_by_expert",
                           "moe_verify_width_distinct", "moe_verify_width_choose", "moe_expert_cache_state_size",
@@ -66,6 +66,25 @@ def test_codec_checks(k3):
     assert d(None, 0, 64, 1, None, None) == OK
     assert d(A, 4, 64, 0, None, None) == ERR_NULL
     assert d(A + 2, 4, 64, 0, A, None) == ERR_ALIGN
+
+
+def test_tile_checks(k3):
+    t = k3.lib.mxfp4_tile
+    B = A + 0x100000  # a second aligned fake address, far from A
+    assert t(A, 2, 16, 48, B, None) == ERR_SHAPE  # K % 32
+    assert t(A, 2, 16, 0, B, None) == ERR_SHAPE
+    assert t(A, -1, 16, 64, B, None) == ERR_SHAPE
+    assert t(A, 2, 0, 64, B, None) == ERR_SHAPE  # N < 1
+    assert t(A, 1 << 40, 1024, 4096, B, None) == ERR_SHAPE  # too many pieces
+    assert t(None, 0, 16, 64, None, None) == OK  # nmat == 0: no-op
+    assert t(None, 2, 16, 64, B, None) == ERR_NULL
+    assert t(A, 2, 16, 64, None, None) == ERR_NULL
+    assert t(A + 1, 2, 16, 64, B, None) == ERR_ALIGN
+    assert t(A, 2, 16, 64, B + 8, None) == ERR_ALIGN
+    # 2 matrices of 16 x 2 blocks = 1088 bytes: destinations that overlap the source
+    assert t(A, 2, 16, 64, A, None) == ERR_SHAPE
+    assert t(A, 2, 16, 64, A + 1072, None) == ERR_SHAPE
+    assert t(A + 1072, 2, 16, 64, A, None) == ERR_SHAPE
 
 
 def ffn(k3, T=8, D=256, I=256, E=8, k=2, act=0, ws_bytes=None, **ptrs):
@@ -258,9 +277,10 @@ def test_latent_block_workspace_size(k3):
         n = ws(T, **K3_BLOCK)
         # at least the FFN's own workspace and the block's activations
         assert n >= k3.moe_mxfp4_ffn_workspace_size(T, 3584, 3072, 896, 16) + T * (896 * 4 + 3584 * 4 + 3072 * 2)
-    # the first product's partials (16 splits of 7 steps at decode, fp32 rows of
-    # 896 + 3584 + 3072 + 3072 features) fit the shared region
-    assert ws(1, **K3_BLOCK) >= 16 * 10624 * 4
+    # the first product's sums (at decode the streaming kernel splits K inside
+    # a workgroup and writes one fp32 row of 896 + 3584 + 3072 + 3072
+    # features per token) fit the shared region
+    assert ws(1, **K3_BLOCK) >= 10624 * 4
 
 
 def test_latent_block_checks(k3):

@@ -16,7 +16,7 @@ from moe_inputs.device import upload_experts
 from oracle.cache import ExpertCacheRef
 from oracle.ffn import ffn_ref
 from oracle.route import route_ref
-from tests.gpu_util import assert_ffn_close, bf16_dev
+from tests.gpu_util import assert_ffn_close, bf16_dev, expert_blocks
 
 pytestmark = pytest.mark.gpu
 
@@ -159,7 +159,7 @@ def test_pageable_host_store_is_refused(k3):
 def ffn_case(k3, cfg, C, where, steps, seed0):
     """Route `steps` batches of cfg through a cache of C slots; the FFN on the
     cache must give the FFN-on-the-store bits every step."""
-    dev = upload_experts(cfg, lambda p, s, out: k3.mxfp4_repack(p, s, blocks=out))
+    dev = upload_experts(cfg, expert_blocks(k3))
     if where == "pinned":
         store = [t.cpu().pin_memory() for t in (dev.w1, dev.w3, dev.w2)]
     else:
@@ -200,7 +200,7 @@ def test_ffn_on_cache_inside_graph(k3):
     # captured input between replays): every replay matches the eager FFN on
     # the store and the oracle's tables
     cfg = moe_inputs.TINY.with_(E=40, k=4, D=512, I=512, T=4, logits="zipf", config_id=92)
-    dev = upload_experts(cfg, lambda p, s, out: k3.mxfp4_repack(p, s, blocks=out))
+    dev = upload_experts(cfg, expert_blocks(k3))
     C = 16
     cache = cache_buffers(C, cfg.D, cfg.I)
     state = k3.moe_expert_cache_init(cfg.E, C)

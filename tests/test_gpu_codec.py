@@ -1,4 +1,5 @@
-"""GPU parity of mxfp4_repack / mxfp4_dequant: bit-exact against the oracle."""
+"""GPU parity of mxfp4_repack / mxfp4_dequant: bit-exact against the oracle;
+mxfp4_tile bit-exact against its order built step by step from the definition."""
 
 import numpy as np
 import pytest
@@ -85,3 +86,47 @@ def test_empty_and_determinism(k3):
     b = k3.mxfp4_repack(to_dev_u8(packed), to_dev_u8(scale))
     assert torch.equal(a, b)
     assert torch.equal(k3.mxfp4_dequant(a), k3.mxfp4_dequant(b))
+
+
+def tiled_ref(blocks: np.ndarray) -> np.ndarray:
+    """Stage-tiled order built as its definition reads: groups of 16 rows one
+    after another, a group stage by stage (16 blocks, fewer at the end), a
+    stage row by row, a row's blocks in order."""
+    N, nb = blocks.shape[-3], blocks.shape[-2]
+    out = []
+    for m in blocks.reshape(-1, N, nb, 17):
+        runs = []
+        for g0 in range(0, N, 16):
+            for b0 in range(0, nb, 16):
+                for r in range(g0, min(g0 + 16, N)):
+                    runs.append(m[r, b0:b0 + 16])
+        out.append(np.concatenate(runs).reshape(N, nb, 17))
+    return np.stack(out).reshape(blocks.shape)
+
+
+# K3 gate/up and down matrices (16-byte copies), ragged row groups, ragged
+# stages (byte copies: 23 and 17 blocks per row), a single block, a single row
+@pytest.mark.parametrize("nmat,N,K", [(1, 3072, 3584), (3, 3584, 3072), (2, 40, 512), (2, 37, 736), (1, 5, 96),
+                                      (2, 16, 32), (1, 1, 544)])
+def test_tile_matches_definition(k3, nmat, N, K):
+    print(f"[codec] tile nmat={nmat} N={N} K={K}", flush=True)
+    g = np.random.default_rng(N * 7 + K)
+    src = g.integers(0, 256, size=(nmat, N, K // 32, 17), dtype=np.uint8)
+    got = k3.mxfp4_tile(to_dev_u8(src)).cpu().numpy()
+    assert np.array_equal(got, tiled_ref(src))
+    # the K3 order: stage s of group G is the contiguous 4352 bytes at
+    # (G * (K / 512) + s) * 4352
+    if N % 16 == 0 and K % 512 == 0:
+        flat = got.reshape(nmat, -1)
+        G, s = N // 16 - 1, K // 512 - 1
+        piece = flat[:, (G * (K // 512) + s) * 4352:(G * (K // 512) + s + 1) * 4352].reshape(nmat, 16, 16, 17)
+        assert np.array_equal(piece, src[:, 16 * G:16 * G + 16, 16 * s:16 * s + 16])
+
+
+def test_tile_empty_and_out_argument(k3):
+    z = torch.empty((0, 16, 2, 17), dtype=torch.uint8, device="cuda")
+    assert k3.mxfp4_tile(z).shape == z.shape
+    src = to_dev_u8(np.random.default_rng(1).integers(0, 256, size=(2, 20, 3, 17), dtype=np.uint8))
+    out = torch.full_like(src, 7)
+    assert k3.mxfp4_tile(src, out=out) is out
+    assert np.array_equal(out.cpu().numpy(), tiled_ref(src.cpu().numpy()))

@@ -14,7 +14,7 @@ import moe_inputs
 from moe_inputs.device import upload_experts
 from oracle.ffn import ffn_ref
 from oracle.route import route_ref
-from tests.gpu_util import assert_ffn_close, bf16_dev, to_dev_u8
+from tests.gpu_util import assert_ffn_close, bf16_dev, expert_blocks, to_dev_u8
 
 pytestmark = pytest.mark.gpu
 
@@ -34,7 +34,7 @@ class HostExperts:
 
 
 def device_experts(k3, cfg):
-    return upload_experts(cfg, lambda p, s, out: k3.mxfp4_repack(p, s, blocks=out))
+    return upload_experts(cfg, expert_blocks(k3))
 
 
 def run_ffn(k3, dev, x_bits, ids, w):
@@ -415,7 +415,7 @@ class ScaledExperts:
             t = torch.empty((cfg.E, shape[0], shape[1] // 32, 17), dtype=torch.uint8, device="cuda")
             for e in range(cfg.E):
                 p, sc = self.mats[e][i]
-                k3.mxfp4_repack(torch.from_numpy(p).cuda(), torch.from_numpy(sc).cuda(), blocks=t[e])
+                k3.mxfp4_tile(k3.mxfp4_repack(torch.from_numpy(p).cuda(), torch.from_numpy(sc).cuda()), out=t[e])
             dev[name] = t
         return dev
 
@@ -449,8 +449,8 @@ def test_identity_weights_closed_form(k3):
         codes[np.arange(n), np.arange(n)] = 2
         return (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8), np.full((rows, cols // 32), 127 + p, np.uint8)
 
-    w1 = torch.stack([k3.mxfp4_repack(*map(to_dev_u8, ident(I, D, 0))) for _ in range(E)])
-    w2 = torch.stack([k3.mxfp4_repack(*map(to_dev_u8, ident(D, I, e))) for e in range(E)])
+    w1 = k3.mxfp4_tile(torch.stack([k3.mxfp4_repack(*map(to_dev_u8, ident(I, D, 0))) for _ in range(E)]))
+    w2 = k3.mxfp4_tile(torch.stack([k3.mxfp4_repack(*map(to_dev_u8, ident(D, I, e))) for e in range(E)]))
     x_bits = moe_inputs.bf16_bits(g.standard_normal((T, D)).astype(np.float32))
     ids = np.stack([g.permutation(E)[:k] for _ in range(T)]).astype(np.int32)
     w = g.random((T, k)).astype(np.float32)

@@ -17,7 +17,7 @@ import moe_inputs
 from moe_inputs.device import upload_experts
 from oracle.latent import latent_block_ref
 from oracle.route import scores
-from tests.gpu_util import assert_ffn_close
+from tests.gpu_util import assert_ffn_close, expert_blocks
 
 pytestmark = pytest.mark.gpu
 
@@ -64,7 +64,7 @@ def check(cfg, dense, h_bits, got, gids, gw, tokens, what):
 @pytest.fixture(scope="module")
 def tiny(k3):
     cfg = moe_inputs.BLOCK_TINY
-    experts = upload_experts(cfg.layer, lambda p, s, out: k3.mxfp4_repack(p, s, blocks=out))
+    experts = upload_experts(cfg.layer, expert_blocks(k3))
     return cfg, DenseDev(cfg), experts
 
 

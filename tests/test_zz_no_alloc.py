@@ -13,7 +13,7 @@ import moe_inputs
 from moe_inputs.device import upload_experts
 from oracle.ffn import ffn_ref
 from oracle.route import route_ref
-from tests.gpu_util import assert_ffn_close, bf16_dev
+from tests.gpu_util import assert_ffn_close, bf16_dev, expert_blocks
 
 pytestmark = pytest.mark.gpu
 
@@ -32,7 +32,7 @@ def _noalloc(k3, x, ids, w, dev, out):
 
 def test_noalloc_matches_workspace_entry_point(k3):
     cfg = moe_inputs.TINY.with_(E=40, k=4, D=512, I=1024, T=90, config_id=81)
-    dev = upload_experts(cfg, lambda p, s, out: k3.mxfp4_repack(p, s, blocks=out))
+    dev = upload_experts(cfg, expert_blocks(k3))
     batch = moe_inputs.make_batch(cfg)
     ids, w = route_ref(batch.z, batch.b, cfg.k)
     x = bf16_dev(batch.x)
@@ -56,7 +56,7 @@ def test_noalloc_inside_graph_capture(k3):
     # a captured noalloc call replays to the eager bits (the scratch keeps
     # whatever the previous call left; nothing in it needs clearing)
     cfg = moe_inputs.TINY.with_(E=16, k=4, D=512, I=512, T=40, config_id=82)
-    dev = upload_experts(cfg, lambda p, s, out: k3.mxfp4_repack(p, s, blocks=out))
+    dev = upload_experts(cfg, expert_blocks(k3))
     batch = moe_inputs.make_batch(cfg)
     ids, w = route_ref(batch.z, batch.b, cfg.k)
     x = bf16_dev(batch.x)
