@@ -257,7 +257,42 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ffn_stream_kernel(GemmArgs a, 
     const int n4 = (n + 3) & ~3;
     int32_t* sid = reinterpret_cast<int32_t*>(&lds[0][0][0]);  // ids, padded with -1
     int32_t* sbase = sid + kSelfGroupEntries;                  // first row of each leader entry
+    // Each expert's first entry and token set come from a hash table on the
+    // expert id in LDS (linear probing; twice as many slots as entries, so a
+    // probe ends at the id's slot or an empty one long before it wraps).
+    constexpr int kH = 2 * kSelfGroupEntries;
+    static_assert(kH == 1024, "the hash takes the top 10 bits");
+    int32_t* hkey = sbase + kSelfGroupEntries;
+    int32_t* hfirst = hkey + kH;
+    uint32_t* hmask = reinterpret_cast<uint32_t*>(hfirst + kH);
+    for (int h = tid; h < kH; h += kThreads) {
+      hkey[h] = -1;
+      hfirst[h] = 0x7FFFFFFF;
+      hmask[h] = 0u;
+    }
     for (int i = tid; i < n4; i += kThreads) sid[i] = i < n ? sg.ids[i] : -1;
+    __syncthreads();
+    int slot[2] = {-1, -1};  // hash slot of the entry's expert; -1: not a valid first slot of its token
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const int i = tid + kThreads * r;
+      if (i >= n) continue;
+      const int id = sid[i];
+      if (id < 0 || id >= sg.E) continue;
+      const int t = i / sg.k, j = i - t * sg.k;
+      bool dup = false;  // the same expert in an earlier slot of the token
+      for (int jj = 0; jj < j; ++jj) dup = dup || sid[t * sg.k + jj] == id;
+      if (dup) continue;
+      int h = (int)(((uint32_t)id * 2654435761u) >> 22);
+      for (int probe = 0; probe < kH; ++probe) {
+        const int old = atomicCAS(&hkey[h], -1, id);
+        if (old == -1 || old == id) break;
+        h = (h + 1) & (kH - 1);
+      }
+      atomicMin(&hfirst[h], i);
+      atomicOr(&hmask[h], 1u << t);
+      slot[r] = h;
+    }
     __syncthreads();
     EntryInfo en[2];
     int carry[3] = {0, 0, 0};
@@ -273,37 +308,16 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ffn_stream_kernel(GemmArgs a, 
       e = EntryInfo{-1, 0, 0, 0, -1, 0u, false};
       if (i < n) {
         const int id = sid[i];
-        const int t = i / sg.k, j = i - t * sg.k;
+        const int t = i / sg.k;
         e.id = id;
         e.t = t;
-        if (id >= 0 && id < sg.E) {
-          unsigned mask = 0u;
-          int first = -1;
-          bool dup = false;
-          int tt = 0, jj = 0;
-          for (int ii = 0; ii < n4; ii += 4) {
-            const int4 q = *reinterpret_cast<const int4*>(sid + ii);
-            const int qa[4] = {q.x, q.y, q.z, q.w};
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-              if (qa[c] == id) {  // the -1 padding never matches
-                mask |= 1u << tt;
-                first = first < 0 ? ii + c : first;
-                dup = dup || (tt == t && jj < j);
-              }
-              if (++jj == sg.k) {
-                jj = 0;
-                ++tt;
-              }
-            }
-          }
-          if (!dup) {
-            e.valid = true;
-            e.mask = mask;
-            e.lead = first;
-            e.rank = __popc(mask & ((1u << t) - 1u));
-            e.cnt = __popc(mask);
-          }
+        if (slot[r] >= 0) {
+          const unsigned mask = hmask[slot[r]];
+          e.valid = true;
+          e.mask = mask;
+          e.lead = hfirst[slot[r]];
+          e.rank = __popc(mask & ((1u << t) - 1u));
+          e.cnt = __popc(mask);
         }
       }
       const bool leader = e.valid && e.lead == i;
