@@ -232,8 +232,11 @@ __device__ __forceinline__ void read_step(uint32_t a0, uint32_t a1, bf16x8_t& w0
 
 // Weight-streaming product for up to 16 tokens.  A workgroup owns 16 features
 // of one segment (the rows of MFMA 16x16x32 blocks) and every token; its 4
-// waves take a quarter of K each, so each wave streams a contiguous quarter of
-// its 16 weight rows.  Every wave has its own ring of kRing stages in LDS (one
+// waves take every fourth 64-wide K step (wave w: steps w, w + 4, ...), so at
+// any time the workgroup reads 512 contiguous bytes of each of its rows (HBM
+// serves that better than four separate 128-byte streams per row), with
+// nontemporal weight loads (read once per call).  Every wave has its own ring
+// of kRing stages in LDS (one
 // 64-wide K step: 16 weight rows and 16 token rows of 128 bytes, chunks
 // XOR-swizzled by row) filled by direct global -> LDS loads, and waits for a
 // stage with an explicit count of the loads issued after it, so kRing - 1
@@ -241,7 +244,7 @@ __device__ __forceinline__ void read_step(uint32_t a0, uint32_t a1, bf16x8_t& w0
 // the last valid row (their outputs are never stored); the tail re-reads its
 // last step, so every stage has the same 4 loads.  The two MFMAs of a step
 // take chunks 2g and 2g + 1 for lane group g (the same K order on both
-// operands).  The quarters are added in wave order through LDS.
+// operands).  The four partial sums are added in wave order through LDS.
 template <int kProduct>
 __global__ __launch_bounds__(kThreads, 2) void dense_stream_kernel(DenseGemmArgs a) {
   constexpr int kRing = 4;
@@ -258,9 +261,7 @@ __global__ __launch_bounds__(kThreads, 2) void dense_stream_kernel(DenseGemmArgs
   const int64_t t0 = (int64_t)blockIdx.y * kStreamRows;
   const int trows = a.T - t0 < kStreamRows ? (int)(a.T - t0) : kStreamRows;
   const int ktot = a.ksteps[0] + a.ksteps[1];
-  const int per = (ktot + 3) / 4;
-  const int kbeg = wave * per;
-  const int nst = (kbeg + per < ktot ? kbeg + per : ktot) - kbeg;  // may be <= 0 for the last wave
+  const int nst = ktot > wave ? (ktot - wave + 3) / 4 : 0;  // steps wave, wave + 4, ... below ktot
   const int last = nst > 0 ? nst - 1 : 0;
 
   // load j (0, 1) of an operand moves rows 8j .. 8j+7: lane -> row 8j + lane/8,
@@ -288,7 +289,7 @@ __global__ __launch_bounds__(kThreads, 2) void dense_stream_kernel(DenseGemmArgs
       (void*)(a.a[1] + t0 * a.lda[1]), 0, (int)(trows * a.lda[1] * 2), 0x00020000);
   const int ks0 = a.ksteps[0];
   auto issue = [&](int i) {
-    const int k = kbeg + (i < last ? i : last);
+    const int k = wave + 4 * (i < last ? i : last);
     const int ks = k < ks0 ? 0 : 1;
     const int kin = k - (ks ? ks0 : 0);
     const __amdgpu_buffer_rsrc_t wr = ks ? wrs1 : wrs0;
@@ -297,7 +298,7 @@ __global__ __launch_bounds__(kThreads, 2) void dense_stream_kernel(DenseGemmArgs
 #pragma unroll
     for (int j = 0; j < 2; ++j)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, st + 8 * j * kRowB, 16, ks ? woff[1][j] : woff[0][j], kin * kRowB,
-                                               0, 0);
+                                               0, 2 /* nontemporal */);
 #pragma unroll
     for (int j = 0; j < 2; ++j)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, st + (kStreamRows + 8 * j) * kRowB, 16,
