@@ -53,7 +53,7 @@ PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 (and fp16) MFMA
 RIDGE = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)  # flop per byte
 TRAFFIC_DIR = os.path.join(ROOT, "profiles")
 CSRC = "mxfp4_mixture_experts_moe_amd/csrc/"
-STREAM_MAX_ROWS = 4  # experts with more rows go to the large-tile kernels (tiled path)
+STREAM_MAX_ROWS = 16  # experts with more rows go to the large-tile kernels (tiled path)
 EXTRA_WORKLOADS = ("decode-t1", "decode-t8", "verify")
 
 # launch slots of one step; event i is recorded right before launch i
@@ -65,8 +65,9 @@ def gemm_path(cfg) -> str:
     """Which grouped-GEMM kernels moe_mxfp4_ffn launches for this shape (the
     library's own selection rule, restated for labelling the roofline):
     "stream" (weight-streaming only, batches of up to 8 tokens), "tiled"
-    (large-tile GEMMs for experts with more than 4 rows, weight-streaming for
-    the others) or "small" (the small-tile GEMMs for every expert)."""
+    (large-tile GEMMs for experts with more than 16 rows, shared-tile
+    weight-streaming for the others) or "small" (the small-tile GEMMs for
+    every expert)."""
     if cfg.D % 512 == 0 and cfg.I % 512 == 0:
         return "stream" if cfg.T <= 8 else "tiled"
     return "small"
@@ -90,9 +91,11 @@ def kernel_info(launch: str, path: str, entries: int = 0, tokens: int = 0):
             # a decode batch is grouped inside the gate/up launch, which reads x
             # in place up to 4 tokens (else x re-laid out by a small launch first)
             return f"ffn_stream_kernel<true, true, {'true' if tokens <= 4 else 'false'}>", [stream]
-        return ("ffn_stream_kernel<true, false, false>", [stream]) if path == "tiled" else None
+        return ("ffn_stream_shared_kernel<true>", [stream]) if path == "tiled" else None
     if launch == "down_stream":
-        return ("ffn_stream_kernel<false, false, false>", [stream]) if path != "small" else None
+        if path == "tiled":
+            return "ffn_stream_shared_kernel<false>", [stream]
+        return ("ffn_stream_kernel<false, false, false>", [stream]) if path == "stream" else None
     return {"route": ("route_topk_*kernel", [CSRC + "route.hip"]),
             "group": ("group_*_kernel / permute_x_kernel", [CSRC + "group.hip"]),
             "combine": ("combine_kernel", [ffn])}[launch]
@@ -204,7 +207,7 @@ def arithmetic(path: str):
     """(dtype, description) of what the path computes in."""
     if path == "tiled":
         return ("bf16+fp16", "MXFP4 weights decoded exactly to bf16 (gate/up) and fp16 (down); bf16 MFMA gate/up, "
-                "fp16 MFMA down on h scaled per (row, 256 features); experts with <= 4 rows: bf16 MFMA with h "
+                "fp16 MFMA down on h scaled per (row, 256 features); experts with <= 16 rows: bf16 MFMA with h "
                 "as a bf16 hi+lo pair; fp32 accumulation; large-tile expert outputs held as scaled fp16; "
                 "fp32 combine; fp64 routing scores")
     return ("bf16", "MXFP4 weights decoded exactly to bf16; bf16 MFMA with fp32 accumulation, h as a bf16 hi+lo "

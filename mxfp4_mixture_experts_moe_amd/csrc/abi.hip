@@ -200,12 +200,14 @@ int run_ffn_chunk(const void* x_bf16, const int32_t* topk_ids, const float* topk
   // GEMM kernels.  With D and I multiples of 512 every expert is served by
   // the kernel that suits its row count: the large-tile GEMMs for experts
   // with more than kStreamMaxRows rows (MFMA-bound), the weight-streaming
-  // GEMMs for the others (HBM-bound).  Batches of up to kStreamOnlyTokens
-  // tokens send every expert to the streaming kernels (an expert with more
-  // than kStreamMaxRows rows takes several streaming tiles, whose repeated
-  // weight reads mostly hit the caches), so decode steps skip the large-tile
-  // launches.  Other shapes use the general small-tile GEMMs for every expert.
-  constexpr int kStreamMaxRows = 4;
+  // GEMMs for the others (HBM-bound; in a grouped batch the shared-tile
+  // form, whose 16-row gate/up and 8-row down tiles stream an expert of up
+  // to 16 rows once).  Batches of up to kStreamOnlyTokens tokens send every
+  // expert to the streaming kernels (an expert with more rows than a tile
+  // takes several, whose repeated weight reads mostly hit the caches), so
+  // decode steps skip the large-tile launches.  Other shapes use the general
+  // small-tile GEMMs for every expert.
+  constexpr int kStreamMaxRows = 16;
   constexpr int kStreamOnlyTokens = 8;
   const bool tiled = big_gemm_supported(D, I) && stream_gemm_supported(D, I);
   const bool stream_only = tiled && T <= kStreamOnlyTokens;
@@ -226,8 +228,17 @@ int run_ffn_chunk(const void* x_bf16, const int32_t* topk_ids, const float* topk
   g.k = k;
   g.rows_per_tile[0] = tiled ? big_rows_per_tile(true, false) : rpt_small;
   g.rows_per_tile[1] = tiled ? big_rows_per_tile(false, wide_down) : rpt_small;
-  g.rows_per_tile[2] = stream_rows_per_tile(true);
-  g.rows_per_tile[3] = stream_rows_per_tile(false);
+  // A streaming-only batch of at most kSelfGroupEntries entries is grouped by
+  // the gate/up launch itself (no grouping launch), in the per-wave streaming
+  // form's 4-row gate/up and 2-row down tiles.  Up to kNaturalXTokens tokens
+  // that launch also reads x in place; larger decode batches have x re-laid
+  // out first by a small launch, as the operand reads of pre-permuted x keep
+  // the gate/up stream faster.  Grouped batches stream in the shared-tile form.
+  constexpr int kNaturalXTokens = 4;
+  const bool self_group = stream_only && entries <= kSelfGroupEntries && E <= 0xFFFF;
+  const bool natural_x = self_group && T <= kNaturalXTokens;
+  g.rows_per_tile[2] = self_group ? stream_rows_per_tile(true) : stream_shared_rows_per_tile(true);
+  g.rows_per_tile[3] = self_group ? stream_rows_per_tile(false) : stream_shared_rows_per_tile(false);
   g.split_rows = tiled ? (stream_only ? kStreamOnlyTokens : kStreamMaxRows) : 0;
   g.flag_big_rows = tiled ? 1 : 0;  // the large-tile down kernel's rows hold scaled fp16 y
   g.counts = reinterpret_cast<int32_t*>(ws + L.counts);
@@ -243,14 +254,6 @@ int run_ffn_chunk(const void* x_bf16, const int32_t* topk_ids, const float* topk
     if (!stage_events || !stage_events[i]) return true;
     return hipEventRecord(static_cast<hipEvent_t>(stage_events[i]), s) == hipSuccess;
   };
-  // A streaming-only batch of at most kSelfGroupEntries entries is grouped by
-  // the gate/up launch itself (no grouping launch).  Up to kNaturalXTokens
-  // tokens that launch also reads x in place; larger decode batches have x
-  // re-laid out first by a small launch, as the operand reads of pre-permuted
-  // x keep the gate/up stream faster.
-  constexpr int kNaturalXTokens = 4;
-  const bool self_group = stream_only && entries <= kSelfGroupEntries && E <= 0xFFFF;
-  const bool natural_x = self_group && T <= kNaturalXTokens;
   if (!mark(kEvGroup)) return K3MOE_ERR_DEVICE;
   hipError_t err = self_group ? (natural_x ? hipSuccess : launch_permute_x(g.x, g.x_perm, T, D, s)) : launch_group(g, s);
   if (err != hipSuccess) return K3MOE_ERR_DEVICE;
@@ -323,7 +326,7 @@ int run_ffn_chunk(const void* x_bf16, const int32_t* topk_ids, const float* topk
       gu.row_tok = nullptr;
       err = launch_stream_gate_up_grouped(gu, sg, natural_x, ss);
     } else {
-      err = launch_stream_gate_up(gu, ss);
+      err = launch_stream_shared(gu, true, ss);
     }
     if (err != hipSuccess) return K3MOE_ERR_DEVICE;
   }
@@ -343,7 +346,7 @@ int run_ffn_chunk(const void* x_bf16, const int32_t* topk_ids, const float* topk
     dn.tile_count = g.tile_count + 3;
     const int64_t r = g.rows_per_tile[3];
     dn.max_tiles = (entries + (r - 1) * active) / r;  // bounds the sum of ceil(n_e / r) over experts
-    err = launch_stream_down(dn, ss);
+    err = self_group ? launch_stream_down(dn, ss) : launch_stream_shared(dn, false, ss);
     if (err != hipSuccess) return K3MOE_ERR_DEVICE;
   }
   if (side) {

@@ -653,6 +653,264 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ffn_stream_kernel(GemmArgs a, 
   }
 }
 
+// Shared-tile streaming, for batches a grouping launch has grouped (verify,
+// the few-row experts of prefill).  A stage's decode and MFMA work per wave is
+// that of ffn_stream_kernel, but the four waves of a workgroup take four
+// consecutive feature groups of ONE tile, so the tile's activation rows travel
+// once per stage into a ring the workgroup shares: 16 rows (gate/up: 16 token
+// rows; down: 8 h_hi rows, then the same 8 rows of h_lo), so every MFMA column
+// is a live row and an expert with up to 16 (gate/up) / 8 (down) rows streams
+// its weights once.  Each wave loads its share of a stage's live activation
+// rows (B rows 4w .. 4w+3 that the tile has) and waits for exactly the loads
+// it issued; one barrier per stage, after each wave's wait for its own loads of
+// that stage, completes the stage for all waves and frees the activation
+// buffer the previous stage used, which the loads issued right after the
+// barrier refill.  The barrier is a bare s_barrier: a fenced one would also
+// wait for the two weight stages in flight.
+template <bool kGateUp>
+struct SharedCfg;
+template <>
+struct SharedCfg<true> {
+  static constexpr int kFeat = 16, kTileRows = 16;
+};
+template <>
+struct SharedCfg<false> {
+  static constexpr int kFeat = 32, kTileRows = 8;
+};
+constexpr int kSharedBRows = 16;
+constexpr int kSharedABytes = kSharedBRows * kBRowBytes;
+constexpr int kSharedWBytes = kRB * 16 * kStageRowBytes;
+static_assert(kWaves * kRing * kSharedWBytes + kRing * kSharedABytes <= 160 * 1024, "LDS");
+
+template <bool kGateUp>
+__global__ __launch_bounds__(kWaves * 64, 1) void ffn_stream_shared_kernel(GemmArgs a) {
+  using C = SharedCfg<kGateUp>;
+  constexpr int kTileRows = C::kTileRows;
+  constexpr int kMatBytes = 16 * kStageRowBytes;
+  constexpr int kW = kWInstr;        // weight loads per stage and wave
+  constexpr int kA = kSharedBRows / kWaves;  // activation loads per stage and wave
+  static_assert(2 * kW + kA < 64, "vmcnt range");
+  __shared__ __attribute__((aligned(16))) uint8_t wlds[kWaves][kRing][kSharedWBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t alds[kRing][kSharedABytes];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int rho = lane & 15, g = lane >> 4;
+  const int ngr = a.N / C::kFeat / kWaves;  // workgroup units per tile
+  const auto row_tok = as_const(a.row_tok);
+  const int n_tiles = *as_const(a.tile_count);
+  const int64_t n_units = (int64_t)n_tiles * ngr;
+  const int64_t nwg = gridDim.x;
+  const int64_t wg = blockIdx.x;
+  if (wg >= n_units) return;  // uniform over the workgroup; every later barrier is reached by all waves
+  const int64_t my_units = (n_units - wg + nwg - 1) / nwg;
+  const int nst = a.K / kStageK;
+  const int64_t Q = my_units * nst;
+  const uint32_t row_bytes = (uint32_t)(a.K >> 5) * 17;
+  const size_t mat_bytes = (size_t)a.N * row_bytes;
+  const uint32_t act_row_bytes = (uint32_t)a.K * 2;
+
+  constexpr int kInstrPerMat = (16 * kRowChunks + 63) / 64;  // 5
+  uint32_t woff[kInstrPerMat];
+#pragma unroll
+  for (int j = 0; j < kInstrPerMat; ++j) {
+    const int c = 64 * j + lane;
+    woff[j] = c < 16 * kRowChunks ? 16u * (uint32_t)c : 0u;
+  }
+  const bool wtail = lane < 16 * kRowChunks - 64 * (kInstrPerMat - 1);
+
+  // Cursor: the workgroup's units are wg, wg + nwg, ...; tile u / ngr and
+  // group u % ngr step with a carry; the wave's feature group is 4 * group + wave.
+  struct SCursor {
+    int64_t u;
+    int s, ti, gr;
+    TileInfo tile;
+  };
+  const int step_ti = (int)(nwg / ngr), step_gr = (int)(nwg % ngr);
+  auto load_unit = [&](SCursor& c) { c.tile = load_tile(a.tiles, __builtin_amdgcn_readfirstlane(c.ti)); };
+  auto next_stage = [&](SCursor& c) {
+    if (++c.s < nst) return;
+    c.s = 0;
+    c.u += nwg;
+    c.ti += step_ti;
+    c.gr += step_gr;
+    if (c.gr >= ngr) {
+      c.gr -= ngr;
+      ++c.ti;
+    }
+    if (c.u < n_units) load_unit(c);
+  };
+
+  // weight loads of the issue cursor's stage (this wave's feature group)
+  auto issue_w = [&](const SCursor& c, int buf) {
+    const int fg = kWaves * c.gr + wave;
+    const size_t unit_off = (size_t)c.tile.expert * mat_bytes + (size_t)(C::kFeat * fg) * row_bytes;
+    uint8_t* dst = &wlds[wave][buf][0];
+    const uint32_t wso = (uint32_t)(16 * kStageRowBytes * c.s);
+#pragma unroll
+    for (int mi = 0; mi < kRB; ++mi) {
+      const uint8_t* base =
+          kGateUp ? (mi == 0 ? a.wa : a.wb) + unit_off : a.wa + unit_off + (size_t)(16 * mi) * row_bytes;
+      const __amdgpu_buffer_rsrc_t wr =
+          __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, (int)(16 * row_bytes), 0x00020000);
+#pragma unroll
+      for (int j = 0; j < kInstrPerMat - 1; ++j)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, (__attribute__((address_space(3))) void*)(uintptr_t)(dst + mi * kMatBytes + 1024 * j),
+                                                 16, woff[j], wso, 0, kNt);
+      if (wtail)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            wr, (__attribute__((address_space(3))) void*)(uintptr_t)(dst + mi * kMatBytes + 1024 * (kInstrPerMat - 1)), 16,
+            woff[kInstrPerMat - 1], wso, 0, kNt);
+    }
+  };
+  // this wave's share (B rows 4 * wave .. 4 * wave + 3) of the stage's live
+  // activation rows (B row m: gate/up token row m of the tile; down h_hi row
+  // m, or h_lo row m - 8); columns of absent rows read whatever their LDS row
+  // holds and are never stored.  Returns how many loads it issued.
+  auto issue_a = [&](const SCursor& c, int buf) -> int {
+    uint8_t* dst = &alds[buf][0];
+    const uint32_t aso = (uint32_t)(kStageK * 2 * c.s);
+    const __amdgpu_buffer_rsrc_t xr =
+        __builtin_amdgcn_make_buffer_rsrc((void*)a.act, 0, (int)((uint32_t)a.act_rows * act_row_bytes), 0x00020000);
+    const __amdgpu_buffer_rsrc_t lr = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(kGateUp ? a.act : a.act_lo), 0, (int)((uint32_t)a.act_rows * act_row_bytes), 0x00020000);
+    int n = 0;
+#pragma unroll
+    for (int r = 0; r < kA; ++r) {
+      const int m = kA * wave + r;
+      const int mr = kGateUp ? m : (m < kTileRows ? m : m - kTileRows);
+      if (mr < c.tile.nrows) {
+        const int row = c.tile.row0 + mr;
+        const int xrow = kGateUp ? row_tok[row] : row;
+        const uint32_t so = (uint32_t)xrow * act_row_bytes + aso;
+        if (kGateUp || m < kTileRows)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (__attribute__((address_space(3))) void*)(uintptr_t)(dst + kBRowBytes * m),
+                                                   16, 16 * lane, so, 0, 0);
+        else
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(lr, (__attribute__((address_space(3))) void*)(uintptr_t)(dst + kBRowBytes * m),
+                                                   16, 16 * lane, so, 0, 0);
+        ++n;
+      }
+    }
+    return n;
+  };
+
+  f32x4_t acc[kRB][2];
+#pragma unroll
+  for (int mi = 0; mi < kRB; ++mi) acc[mi][0] = acc[mi][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  const uint32_t qsel = 0x03020100u + 0x01010101u * (uint32_t)(g + 1);
+
+  SCursor ci{wg, 0, (int)(wg / ngr), (int)(wg % ngr), {0, 0, 0, 0}};
+  load_unit(ci);
+  SCursor cc = ci;
+  int buf_i = 0, buf_c = 0;
+  int a_next = 0;  // this wave's activation loads of stage q + 1
+  issue_w(ci, 0);
+  issue_a(ci, 0);
+  next_stage(ci);
+  if (Q > 1) {
+    issue_w(ci, 1);
+    a_next = issue_a(ci, 1);
+    next_stage(ci);
+  }
+  buf_i = 2;
+  SCursor ca = ci;  // the stage whose activations the next issue_a loads
+  for (int64_t q = 0; q < Q; ++q) {
+    // stage q landed for this wave once at most the loads issued after it
+    // are pending: W(q+1), A(q+1), W(q+2) (those that were issued)
+    if (q + 2 < Q) {
+      issue_w(ci, buf_i);
+      next_stage(ci);
+      wait_vm_plus<2 * kW>(a_next);
+    } else if (q + 1 < Q) {
+      wait_vm_plus<kW>(a_next);
+    } else {
+      wait_vm<0>();
+    }
+    asm volatile("s_barrier" ::: "memory");
+    if (q + 2 < Q) {
+      a_next = issue_a(ca, buf_i);
+      next_stage(ca);
+      buf_i = buf_i == kRing - 1 ? 0 : buf_i + 1;
+    }
+    const uint32_t* wl = reinterpret_cast<const uint32_t*>(&wlds[wave][buf_c][0]);
+    const uint8_t* bl = &alds[buf_c][0] + kBRowBytes * rho;
+    buf_c = buf_c == kRing - 1 ? 0 : buf_c + 1;
+    bf16x8_t bop[4][4];
+#pragma unroll
+    for (int rnd = 0; rnd < 4; ++rnd)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) bop[rnd][i] = *reinterpret_cast<const bf16x8_t*>(bl + 64 * (4 * rnd + g) + 16 * i);
+    uint32_t wd[kRB][4][5];
+#pragma unroll
+    for (int mi = 0; mi < kRB; ++mi)
+#pragma unroll
+      for (int rnd = 0; rnd < 4; ++rnd)
+#pragma unroll
+        for (int j = 0; j < 5; ++j) wd[mi][rnd][j] = wl[(16 * mi + rho) * kRowDw + 17 * rnd + 4 * g + j];
+#pragma unroll
+    for (int r0 = 0; r0 < 4; r0 += 2) {
+      bf16x8_t aop[kRB][2][4];
+#pragma unroll
+      for (int mi = 0; mi < kRB; ++mi)
+#pragma unroll
+        for (int rr = 0; rr < 2; ++rr) decode_dwords(wd[mi][r0 + rr], g, qsel, aop[mi][rr]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int rr = 0; rr < 2; ++rr)
+#pragma unroll
+          for (int mi = 0; mi < kRB; ++mi)
+            acc[mi][rr] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aop[mi][rr][i], bop[r0 + rr][i], acc[mi][rr], 0, 0, 0);
+    }
+
+    if (cc.s == nst - 1) {
+      // lane holds, for tile row rho (down: h_hi part in columns 0-7, h_lo
+      // part in columns 8-15), features 4g + v of each 16-row block
+      const TileInfo& tile = cc.tile;
+      const int fg = kWaves * cc.gr + wave;
+      f32x4_t sum[kRB];
+#pragma unroll
+      for (int mi = 0; mi < kRB; ++mi) sum[mi] = acc[mi][0] + acc[mi][1];
+      if (!kGateUp) {
+#pragma unroll
+        for (int mi = 0; mi < kRB; ++mi)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) sum[mi][v] += __shfl_down(sum[mi][v], kTileRows, 16);
+      }
+      if (rho < tile.nrows) {
+        const int64_t row = tile.row0 + rho;
+        if (kGateUp) {
+          uint32_t hb[4], lb[4];
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const float gt = sum[0][v], up = sum[1][v];
+            const float h = gt / (1.0f + expf(-gt)) * up;
+            hb[v] = f32_to_bf16_bits(h);
+            lb[v] = f32_to_bf16_bits(h - __uint_as_float(hb[v] << 16));
+          }
+          const int pos = 32 * (fg >> 1) + 8 * g + (fg & 1);
+          uint16_t* hrow = reinterpret_cast<uint16_t*>(a.out) + row * a.N + pos;
+          uint16_t* lrow = reinterpret_cast<uint16_t*>(a.out_lo) + row * a.N + pos;
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            hrow[2 * v] = (uint16_t)hb[v];
+            lrow[2 * v] = (uint16_t)lb[v];
+          }
+        } else {
+          float* yrow = reinterpret_cast<float*>(a.out) + row * a.N + C::kFeat * fg + 4 * g;
+#pragma unroll
+          for (int mi = 0; mi < kRB; ++mi)
+            *reinterpret_cast<float4*>(yrow + 16 * mi) = make_float4(sum[mi][0], sum[mi][1], sum[mi][2], sum[mi][3]);
+        }
+      }
+#pragma unroll
+      for (int mi = 0; mi < kRB; ++mi) acc[mi][0] = acc[mi][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+    next_stage(cc);
+  }
+}
+
 int cu_count() {
   static int cached[64] = {0};
   int dev = 0;
@@ -685,9 +943,25 @@ bool stream_gemm_supported(int D, int I) { return (D % kStageK) == 0 && (I % kSt
 
 int stream_rows_per_tile(bool gate_up) { return gate_up ? StreamCfg<true>::kTileRows : StreamCfg<false>::kTileRows; }
 
-hipError_t launch_stream_gate_up(const GemmArgs& a, hipStream_t s) { return launch_stream<true, false, false>(a, {}, s); }
-
 hipError_t launch_stream_down(const GemmArgs& a, hipStream_t s) { return launch_stream<false, false, false>(a, {}, s); }
+
+int stream_shared_rows_per_tile(bool gate_up) {
+  return gate_up ? SharedCfg<true>::kTileRows : SharedCfg<false>::kTileRows;
+}
+
+hipError_t launch_stream_shared(const GemmArgs& a, bool gate_up, hipStream_t s) {
+  const int feat = gate_up ? SharedCfg<true>::kFeat : SharedCfg<false>::kFeat;
+  const int64_t max_units = a.max_tiles * (a.N / feat / kWaves);
+  int64_t grid = max_units;
+  const int cus = cu_count();
+  if (grid > cus) grid = cus;
+  if (grid < 1) grid = 1;
+  if (gate_up)
+    hipLaunchKernelGGL(ffn_stream_shared_kernel<true>, dim3((unsigned)grid), dim3(kWaves * 64), 0, s, a);
+  else
+    hipLaunchKernelGGL(ffn_stream_shared_kernel<false>, dim3((unsigned)grid), dim3(kWaves * 64), 0, s, a);
+  return hipGetLastError();
+}
 
 hipError_t launch_stream_gate_up_grouped(const GemmArgs& a, const SelfGroupArgs& sg, bool natural_x, hipStream_t s) {
   return natural_x ? launch_stream<true, true, true>(a, sg, s) : launch_stream<true, true, false>(a, sg, s);

@@ -136,7 +136,10 @@ hipError_t launch_big_down(const GemmArgs& a, bool wide, hipStream_t s);
 
 bool stream_gemm_supported(int D, int I);
 int stream_rows_per_tile(bool gate_up);
-hipError_t launch_stream_gate_up(const GemmArgs& a, hipStream_t s);
+// Shared-tile streaming GEMMs (batches grouped by a grouping launch): tiles of
+// 16 rows (gate/up) or 8 rows (down), one tile per workgroup at a time.
+int stream_shared_rows_per_tile(bool gate_up);
+hipError_t launch_stream_shared(const GemmArgs& a, bool gate_up, hipStream_t s);
 hipError_t launch_stream_down(const GemmArgs& a, hipStream_t s);
 
 // Streaming gate/up that groups the routed entries itself (batches of at most

@@ -41,7 +41,8 @@ def test_gemm_path_no_size_cliff():
         ("decode-t1", "gate_up", None),
         ("decode-t8", "down", None),
         ("verify", "gate_up", "ffn_big_kernel<true, 128>"),
-        ("verify", "gate_up_stream", "ffn_stream_kernel<true, false, false>"),
+        ("verify", "gate_up_stream", "ffn_stream_shared_kernel<true>"),
+        ("verify", "down_stream", "ffn_stream_shared_kernel<false>"),
         ("verify", "down", "ffn_big_kernel<false, 64>"),
         ("prefill", "down", "ffn_big_kernel<false, 128>"),
         ("tiny", "gate_up", "ffn_gemm_kernel<NT, true, ...>"),
@@ -97,8 +98,8 @@ def test_large_tile_h_and_y_counted_at_two_bytes():
     assert s == mat2 + 1000 * cfg.I * 4 + 1000 * cfg.D * 4
 
 
-def test_routing_stats_split_at_four_rows():
-    counts = np.array([0, 1, 4, 5, 100, 0, 3])
-    assert bench.routing_stats(counts, "tiled") == (105, 2, 8, 3)
-    assert bench.routing_stats(counts, "stream") == (0, 0, 113, 5)
-    assert bench.routing_stats(counts, "small") == (113, 5, 0, 0)
+def test_routing_stats_split_at_sixteen_rows():
+    counts = np.array([0, 1, 16, 17, 100, 0, 3])
+    assert bench.routing_stats(counts, "tiled") == (117, 2, 20, 3)
+    assert bench.routing_stats(counts, "stream") == (0, 0, 137, 5)
+    assert bench.routing_stats(counts, "small") == (137, 5, 0, 0)

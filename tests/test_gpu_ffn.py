@@ -177,7 +177,7 @@ def test_self_grouping_duplicates_and_invalid_ids(k3):
 
 def test_mixed_large_and_streaming_experts(k3):
     # one call in which some experts have many rows (large-tile kernels, with a
-    # partial last token group) and others 1..4 rows (weight-streaming kernels)
+    # partial last token group) and others a few rows (weight-streaming kernels)
     cfg = moe_inputs.TINY.with_(E=40, k=4, D=512, I=1024, T=90, config_id=44)
     g = np.random.default_rng(14)
     ids = np.stack([g.permutation(cfg.E)[: cfg.k] for _ in range(cfg.T)]).astype(np.int32)
@@ -190,9 +190,40 @@ def test_mixed_large_and_streaming_experts(k3):
     assert_ffn_close(got, ref, "mixed large/streaming")
 
 
+def test_shared_streaming_tiles_around_their_limits(k3):
+    # grouped batch (more than 8 tokens): experts of at most 16 rows go to the
+    # shared-tile streaming kernels (16-row gate/up, 8-row down tiles), larger
+    # ones to the large-tile kernels.  Row counts 1, 4, 8, 9, 15, 16 (one
+    # gate/up tile; one or two down tiles, ragged), 17 (just past the limit)
+    # and 40; every token checked
+    cfg = moe_inputs.TINY.with_(E=24, k=4, D=512, I=1024, T=64, config_id=49)
+    g = np.random.default_rng(16)
+    ids = np.full((cfg.T, cfg.k), -1, np.int32)
+    col = {}
+    t0 = 0
+    for e, n in ((0, 1), (1, 4), (2, 8), (3, 9), (4, 15), (5, 16), (6, 17), (7, 40)):
+        rows = (t0 + np.arange(n)) % cfg.T
+        t0 += n
+        for t in rows:
+            j = col.get(t, 0)
+            ids[t, j] = e
+            col[t] = j + 1
+    # the free slots go to experts 8..23 (9 or 10 rows each), no repeats in a row
+    free = np.argwhere(ids < 0)
+    fill = 8 + np.arange(len(free)) % 16
+    for (t, j), e in zip(free, fill):
+        ids[t, j] = e if e not in ids[t] else -1
+    w = g.random((cfg.T, cfg.k)).astype(np.float32)
+    counts = [int((ids == e).sum()) for e in range(8)]
+    assert counts == [1, 4, 8, 9, 15, 16, 17, 40], counts
+    print(f"[ffn] shared streaming tiles around their limits", flush=True)
+    got, ref, _, _ = small_case(k3, cfg, ids, w)
+    assert_ffn_close(got, ref, "shared streaming tiles")
+
+
 def test_large_batch_mixed_with_few_row_experts(k3):
     # 16384 routed entries (128-row large-tile down tiles) with experts of
-    # 1..4 rows (weight-streaming kernels) and one of 5 rows in the same call
+    # 1..5 rows (weight-streaming kernels) in the same call
     cfg = moe_inputs.TINY.with_(E=40, k=8, D=512, I=512, T=2048, config_id=45)
     g = np.random.default_rng(15)
     ids = np.stack([g.permutation(30)[: cfg.k] for _ in range(cfg.T)]).astype(np.int32)
