@@ -194,7 +194,7 @@ size_t moe_mxfp4_ffn_workspace_size(int64_t T, int32_t D, int32_t I, int32_t E, 
  * multiple of 64: the GEMM kernels address activations with 32-bit offsets);
  * moe_mxfp4_ffn_workspace_size() is that of one chunk.
  * Side stream: when one call has experts for both GEMM kinds (many rows: the
- * large-tile kernels; at most 4 rows: the weight-streaming kernels), the
+ * large-tile kernels; at most 16 rows: the weight-streaming kernels), the
  * streaming launches run on a side stream forked from `stream` with an event
  * and joined back before the combine (a graph captured from `stream` gets two
  * parallel branches). The side stream (default priority) and its two events
