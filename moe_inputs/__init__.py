@@ -51,6 +51,27 @@ def mxfp4_source(g: np.random.Generator, rows: int, cols: int, e_lo: int, e_hi: 
     return packed, scale
 
 
+def q4k_blocks(g: np.random.Generator, rows: int, cols: int, e_lo: int = 3, e_hi: int = 5) -> np.ndarray:
+    """Q4_K matrix u8 [rows, cols/256, 144] (ggml ``block_q4_K`` per 256 weights).
+
+    The 12 packed scale/min bytes and the 128 code bytes are uniform random
+    bytes; ``d`` and ``dmin`` (bytes 0-1 and 2-3, little-endian fp16) are
+    positive with their 5-bit exponent field uniform over [e_lo, e_hi] and a
+    uniform 10-bit mantissa (2^-12 up to just below 2^-9 for the defaults), so
+    the weights span about the range of the MXFP4 experts' weights.
+    """
+    assert cols % 256 == 0
+    nb = cols // 256
+    b = np.frombuffer(g.bytes(rows * nb * 144), dtype=np.uint8).reshape(rows, nb, 144).copy()
+    for off in (0, 2):
+        e = g.integers(e_lo, e_hi + 1, size=(rows, nb), dtype=np.uint16)
+        mant = g.integers(0, 1024, size=(rows, nb), dtype=np.uint16)
+        bits = (e << 10) | mant
+        b[..., off] = (bits & 0xFF).astype(np.uint8)
+        b[..., off + 1] = (bits >> 8).astype(np.uint8)
+    return b
+
+
 def bf16_bits(a: np.ndarray) -> np.ndarray:
     """Round fp32 values to bfloat16 (nearest-even) and return the raw u16 bits.
 
@@ -135,6 +156,30 @@ class ExpertSource:
         rows, cols = (c.I, c.D) if tensor_id in (T_W1, T_W3) else (c.D, c.I)
         wid = c.config_id if c.weight_id < 0 else c.weight_id
         return mxfp4_source(rng(c.seed, 100 + wid, tensor_id, e), rows, cols, c.e_lo, c.e_hi)
+
+    def __getitem__(self, e: int):
+        return self.matrix(T_W1, e), self.matrix(T_W3, e), self.matrix(T_W2, e)
+
+    def __len__(self):
+        return self.cfg.E
+
+
+class ExpertSourceQ4K:
+    """Lazily generated Q4_K weights of every expert of one config.
+
+    ``src[e]`` returns ``(w1, w3, w2)``: w1 and w3 u8 [I, D/256, 144], w2 u8
+    [D, I/256, 144], each from its own keyed stream (keys 200 + weight id, so
+    they never share a stream with the MXFP4 experts).
+    """
+
+    def __init__(self, cfg: LayerConfig):
+        self.cfg = cfg
+
+    def matrix(self, tensor_id: int, e: int) -> np.ndarray:
+        c = self.cfg
+        rows, cols = (c.I, c.D) if tensor_id in (T_W1, T_W3) else (c.D, c.I)
+        wid = c.config_id if c.weight_id < 0 else c.weight_id
+        return q4k_blocks(rng(c.seed, 200 + wid, tensor_id, e), rows, cols)
 
     def __getitem__(self, e: int):
         return self.matrix(T_W1, e), self.matrix(T_W3, e), self.matrix(T_W2, e)

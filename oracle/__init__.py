@@ -20,6 +20,8 @@ Modules
 ``cache``   a least-recently-used device expert cache in front of an external expert store
 ``latent``  the latent-MoE block: gate projection, latent down + RMS norm, routed
             experts, latent up, shared expert
+``q4k``     Q4_K expert blocks (ggml's 4-bit k-quant): decode, and the routed FFN
+            over Q4_K experts
 
 Parity status
 -------------
@@ -31,7 +33,11 @@ and an independent last-use LRU simulation, bf16 rounding against every bf16
 value and torch's conversion, an identity-weight closed form of the latent
 block and its pure-Python loop evaluation).  The FFN's numerics beyond those closed forms have no worked
 example on the pages; ``ffn_ref`` is pinned by a pure-Python loop evaluation
-and the identity case only.
+and the identity case only.  The pages name Q4_K without defining it:
+``q4k`` follows ggml's published block layout and is pinned to a hand-encoded
+block, an inverse-packing round trip over every 6-bit value, fp16 closed
+forms and a pure-Python loop evaluation of the FFN on design values, none of
+which the pages can confirm.
 """
 
 from .mxfp4 import (  # noqa: F401
@@ -49,3 +55,4 @@ from .ffn import ffn_ref, silu_mul  # noqa: F401
 from .verify import expected_committed, verify_distinct_ref, verify_width_choose_ref  # noqa: F401
 from .cache import ExpertCacheRef  # noqa: F401
 from .latent import bf16_round, latent_block_ref, rms_norm  # noqa: F401
+from .q4k import ffn_q4k_ref, q4k_codes, q4k_decode, q4k_scale_min  # noqa: F401

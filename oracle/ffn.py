@@ -61,13 +61,14 @@ def expert_ffn(x: np.ndarray, src, act: int = ACT_SILU_MUL) -> np.ndarray:
 
 
 def ffn_ref(x_bits: np.ndarray, ids: np.ndarray, w: np.ndarray, experts, act: int = ACT_SILU_MUL,
-            tokens=None) -> np.ndarray:
+            tokens=None, expert_fn=expert_ffn) -> np.ndarray:
     """The routed FFN for every token (or the listed ``tokens``), fp64 [T', D].
 
     x_bits: bf16 bits [T, D]; ids int [T, k]; w fp32 [T, k] (used as given);
-    experts: ``experts[e]`` -> source-layout triple of expert e.
-    Invalid entries (id out of range, or repeating an earlier id of the same
-    token) contribute nothing.
+    experts: ``experts[e]`` -> source-layout triple of expert e, evaluated by
+    ``expert_fn(rows, experts[e], act)`` (another expert encoding passes its
+    own).  Invalid entries (id out of range, or repeating an earlier id of the
+    same token) contribute nothing.
     """
     ids = np.asarray(ids)
     T, k = ids.shape
@@ -82,6 +83,6 @@ def ffn_ref(x_bits: np.ndarray, ids: np.ndarray, w: np.ndarray, experts, act: in
     out = np.zeros((tokens.size, x.shape[1]), dtype=np.float64)
     for e in np.unique(sub_ids[ok]):
         rows, slots = np.nonzero((sub_ids == e) & ok)
-        y = expert_ffn(x[rows], experts[int(e)], act)
+        y = expert_fn(x[rows], experts[int(e)], act)
         out[rows] += sub_w[rows, slots][:, None] * y
     return out
