@@ -243,6 +243,68 @@ int moe_mxfp4_ffn_profiled(const void* x_bf16, const int32_t* topk_ids, const fl
                            void* stream, void* const* stage_events);
 
 /*
+ * moe_q4k_ffn_workspace_size — bytes of device workspace moe_q4k_ffn needs for
+ * these sizes (0 when T == 0 or the sizes are invalid). Pure host computation.
+ */
+size_t moe_q4k_ffn_workspace_size(int64_t T, int32_t D, int32_t I, int32_t E, int32_t k);
+
+/*
+ * moe_q4k_ffn — the same routed-expert FFN as moe_mxfp4_ffn with the experts
+ * stored as Q4_K blocks. Sources: the pages run K3 requantized (Hugging Face
+ * card "K3-Stuff", scripts list: a trunk rewritten from Q8_0 to Q4_K;
+ * llama.cpp page "model: add Kimi-K3 text model", a Q3_K_M deployment;
+ * lucebox page, "Runtime validation": a UD-IQ1_S target) and warn that the
+ * QAT-trained MXFP4 experts should stay as they are ("K3-Stuff", Key facts);
+ * they name Q4_K without defining it, so the block is ggml's published
+ * block_q4_K:
+ *   256 consecutive weights of a row in 144 bytes: fp16 d (bytes 0-1), fp16
+ *   dmin (2-3), 12 bytes (4-15) packing eight 6-bit (scale, min) pairs, one
+ *   per 32-weight sub-block (sub-block j < 4: scale = b[j] & 63, min =
+ *   b[j+4] & 63; j >= 4: scale = (b[j+4] & 15) | (b[j-4] >> 6) << 4, min =
+ *   (b[j+4] >> 4) | (b[j] >> 6) << 4, b = those 12 bytes), and 128 bytes of
+ *   4-bit codes (code bytes 32c..32c+31 hold sub-block 2c in their low and
+ *   2c+1 in their high nibbles); weight = d * scale * code - dmin * min.
+ *
+ *   x_bf16   bf16 [T, D]            latent activations
+ *   topk_ids i32  [T, k]            routed experts of each token
+ *   topk_w   f32  [T, k]            gate weights
+ *   w1, w3   u8 [E, I, D/256, 144]  gate / up matrices ([I, D] per expert), Q4_K
+ *                                   blocks along D, in ggml's row-major order
+ *                                   (no repacking)
+ *   w2       u8 [E, D, I/256, 144]  down matrix ([D, I] per expert), likewise
+ *   out      f32  [T, D]            out[t] = sum_j w[t,j] * W2 act(W1 x_t, W3 x_t)
+ *   workspace device buffer of at least moe_q4k_ffn_workspace_size() bytes;
+ *             its contents on entry do not matter and are clobbered
+ *
+ * act must be K3MOE_ACT_SILU_MUL. Precision: bf16 x and exact weights, bf16
+ * MFMA on the exact codes with fp32 accumulation and the block's scales and
+ * mins applied in fp32; h enters the down product as the bf16 pair hi =
+ * bf16(h), lo = bf16(h - hi); fp32 output. The k expert outputs of a token
+ * are summed in slot order (deterministic); skipped entries as in
+ * moe_mxfp4_ffn. Every launch stays on `stream`; the library keeps no state.
+ * Sizes: as moe_mxfp4_ffn, with D and I multiples of 256 (else
+ * K3MOE_ERR_SHAPE). Large batches run in the same token chunks as
+ * moe_mxfp4_ffn. Non-finite d or dmin give non-finite outputs.
+ */
+int moe_q4k_ffn(const void* x_bf16, const int32_t* topk_ids, const float* topk_w, const uint8_t* w1,
+                const uint8_t* w3, const uint8_t* w2, int64_t T, int32_t D, int32_t I, int32_t E, int32_t k,
+                int32_t act, float* out, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * moe_q4k_ffn_profiled — moe_q4k_ffn recording caller-created hipEvent_t
+ * handles at its launch boundaries, in the slots of moe_mxfp4_ffn_profiled:
+ * [0] before grouping, [1] before the gate/up product, [3] before the down
+ * product, [5] before the combine, [6] after it ([2] and [4], the streaming
+ * slots, follow [1] and [3] with nothing between). Same arguments, checks and
+ * results as moe_q4k_ffn; an event the runtime refuses to record gives
+ * K3MOE_ERR_DEVICE.
+ */
+int moe_q4k_ffn_profiled(const void* x_bf16, const int32_t* topk_ids, const float* topk_w, const uint8_t* w1,
+                         const uint8_t* w3, const uint8_t* w2, int64_t T, int32_t D, int32_t I, int32_t E, int32_t k,
+                         int32_t act, float* out, void* workspace, size_t workspace_bytes, void* stream,
+                         void* const* stage_events);
+
+/*
  * moe_mxfp4_ffn_noalloc — moe_mxfp4_ffn for callers that cannot allocate
  * device memory (code under HIP graph capture, tight serving loops, harnesses
  * that forbid hipMalloc): the workspace is a fixed scratch array inside the

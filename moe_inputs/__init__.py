@@ -51,13 +51,13 @@ def mxfp4_source(g: np.random.Generator, rows: int, cols: int, e_lo: int, e_hi: 
     return packed, scale
 
 
-def q4k_blocks(g: np.random.Generator, rows: int, cols: int, e_lo: int = 3, e_hi: int = 5) -> np.ndarray:
+def q4k_blocks(g: np.random.Generator, rows: int, cols: int, e_lo: int = 1, e_hi: int = 3) -> np.ndarray:
     """Q4_K matrix u8 [rows, cols/256, 144] (ggml ``block_q4_K`` per 256 weights).
 
     The 12 packed scale/min bytes and the 128 code bytes are uniform random
     bytes; ``d`` and ``dmin`` (bytes 0-1 and 2-3, little-endian fp16) are
     positive with their 5-bit exponent field uniform over [e_lo, e_hi] and a
-    uniform 10-bit mantissa (2^-12 up to just below 2^-9 for the defaults), so
+    uniform 10-bit mantissa (2^-14 up to just below 2^-11 for the defaults), so
     the weights span about the range of the MXFP4 experts' weights.
     """
     assert cols % 256 == 0

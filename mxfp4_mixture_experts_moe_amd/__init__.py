@@ -28,6 +28,8 @@ __all__ = [
     "moe_mxfp4_ffn",
     "moe_mxfp4_ffn_noalloc",
     "NOALLOC_SCRATCH_BYTES",
+    "moe_q4k_ffn_workspace_size",
+    "moe_q4k_ffn",
     "moe_verify_width_distinct",
     "moe_verify_width_choose",
     "moe_expert_cache_state_size",
@@ -75,6 +77,10 @@ lib.moe_mxfp4_ffn.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _i
 lib.moe_mxfp4_ffn_profiled.restype = ctypes.c_int
 lib.moe_mxfp4_ffn_profiled.argtypes = lib.moe_mxfp4_ffn.argtypes + [ctypes.POINTER(ctypes.c_void_p)]
 lib.moe_mxfp4_ffn_noalloc.restype = ctypes.c_int
+lib.moe_q4k_ffn_workspace_size.restype = _sz
+lib.moe_q4k_ffn_workspace_size.argtypes = [_i64, _i32, _i32, _i32, _i32]
+lib.moe_q4k_ffn.argtypes = lib.moe_mxfp4_ffn.argtypes
+lib.moe_q4k_ffn_profiled.argtypes = lib.moe_mxfp4_ffn_profiled.argtypes
 lib.moe_mxfp4_ffn_noalloc.argtypes = [_vp, _vp, _vp, _vp, _vp, _vp, _i64, _i32, _i32, _i32, _i32, _i32, _vp, _vp]
 NOALLOC_SCRATCH_BYTES = 64 << 20
 lib.moe_group_workspace_size.restype = _sz
@@ -253,6 +259,17 @@ def _ffn_operands(x, ids, weights, w1, w3, w2, out):
     return T, D, I, E, k, out
 
 
+def _event_handles(stage_events):
+    if len(stage_events) != FFN_STAGE_EVENTS:
+        raise ValueError(f"stage_events must hold {FFN_STAGE_EVENTS} events")
+    handles = (ctypes.c_void_p * FFN_STAGE_EVENTS)()
+    for i, ev in enumerate(stage_events):
+        if ev is not None and not ev.cuda_event:
+            ev.record()  # torch creates its events lazily
+        handles[i] = None if ev is None else ev.cuda_event
+    return handles
+
+
 def moe_mxfp4_ffn(x: torch.Tensor, ids: torch.Tensor, weights: torch.Tensor, w1: torch.Tensor, w3: torch.Tensor,
                   w2: torch.Tensor, act: int = ACT_SILU_MUL, out: torch.Tensor | None = None,
                   workspace: torch.Tensor | None = None, stage_events=None) -> torch.Tensor:
@@ -271,14 +288,48 @@ def moe_mxfp4_ffn(x: torch.Tensor, ids: torch.Tensor, weights: torch.Tensor, w1:
     if stage_events is None:
         _check("moe_mxfp4_ffn", lib.moe_mxfp4_ffn(*args))
     else:
-        if len(stage_events) != FFN_STAGE_EVENTS:
-            raise ValueError(f"stage_events must hold {FFN_STAGE_EVENTS} events")
-        handles = (ctypes.c_void_p * FFN_STAGE_EVENTS)()
-        for i, ev in enumerate(stage_events):
-            if ev is not None and not ev.cuda_event:
-                ev.record()  # torch creates its events lazily
-            handles[i] = None if ev is None else ev.cuda_event
-        _check("moe_mxfp4_ffn_profiled", lib.moe_mxfp4_ffn_profiled(*args, handles))
+        _check("moe_mxfp4_ffn_profiled", lib.moe_mxfp4_ffn_profiled(*args, _event_handles(stage_events)))
+    return out
+
+
+def moe_q4k_ffn_workspace_size(T: int, D: int, I: int, E: int, k: int) -> int:
+    return int(lib.moe_q4k_ffn_workspace_size(T, D, I, E, k))
+
+
+def moe_q4k_ffn(x: torch.Tensor, ids: torch.Tensor, weights: torch.Tensor, w1: torch.Tensor, w3: torch.Tensor,
+                w2: torch.Tensor, act: int = ACT_SILU_MUL, out: torch.Tensor | None = None,
+                workspace: torch.Tensor | None = None, stage_events=None) -> torch.Tensor:
+    """Routed-expert FFN over Q4_K experts. x bf16 [T, D]; ids int32 [T, k];
+    weights f32 [T, k]; w1/w3 u8 [E, I, D/256, 144]; w2 u8 [E, D, I/256, 144]
+    (ggml block_q4_K, row-major). Returns out f32 [T, D].
+
+    stage_events: optional list of FFN_STAGE_EVENTS torch.cuda.Event recorded
+    at the launch boundaries (moe_q4k_ffn_profiled)."""
+    _dev(x, "x", torch.bfloat16)
+    _dev(ids, "ids", torch.int32)
+    _dev(weights, "weights", torch.float32)
+    for n, t in (("w1", w1), ("w3", w3), ("w2", w2)):
+        _dev(t, n, torch.uint8)
+    T, D = x.shape
+    k = ids.shape[1]
+    E, I = w1.shape[0], w1.shape[1]
+    if ids.shape != (T, k) or weights.shape != (T, k):
+        raise ValueError("ids / weights must be [T, k]")
+    if w1.shape != (E, I, D // 256, 144) or w3.shape != w1.shape or w2.shape != (E, D, I // 256, 144):
+        raise ValueError("Q4_K expert weights have inconsistent shapes")
+    if out is None:
+        out = torch.empty((T, D), dtype=torch.float32, device=x.device)
+    _dev(out, "out", torch.float32)
+    need = moe_q4k_ffn_workspace_size(T, D, I, E, k)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    _dev(workspace, "workspace", torch.uint8)
+    args = (_ptr(x), _ptr(ids), _ptr(weights), _ptr(w1), _ptr(w3), _ptr(w2), T, D, I, E, k, act, _ptr(out),
+            _ptr(workspace), workspace.numel(), _stream(x.device))
+    if stage_events is None:
+        _check("moe_q4k_ffn", lib.moe_q4k_ffn(*args))
+    else:
+        _check("moe_q4k_ffn_profiled", lib.moe_q4k_ffn_profiled(*args, _event_handles(stage_events)))
     return out
 
 

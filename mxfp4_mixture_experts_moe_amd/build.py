@@ -25,7 +25,7 @@ LIB_NAME = "libk3moe.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
 INCLUDE = os.path.join(os.path.dirname(PKG_DIR), "include")
 
-SOURCES = ["abi.hip", "route.hip", "codec.hip", "group.hip", "ffn.hip", "ffn_big.hip", "ffn_stream.hip", "verify.hip", "cache.hip", "dense.hip"]
+SOURCES = ["abi.hip", "route.hip", "codec.hip", "group.hip", "ffn.hip", "ffn_big.hip", "ffn_stream.hip", "ffn_q4k.hip", "verify.hip", "cache.hip", "dense.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

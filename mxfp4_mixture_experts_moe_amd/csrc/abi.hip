@@ -384,6 +384,86 @@ int run_ffn(const void* x_bf16, const int32_t* topk_ids, const float* topk_w, co
   return K3MOE_OK;
 }
 
+// The FFN over Q4_K experts, one chunk: grouping (every expert in lists 0/1,
+// 16-row gate/up and 8-row down tiles, x read in place), the two Q4_K GEMMs,
+// combine.  Events (if given) mark the same launch boundaries as the MXFP4
+// path's; the streaming slots stay empty.
+int run_q4k_chunk(const void* x_bf16, const int32_t* topk_ids, const float* topk_w, const uint8_t* w1,
+                  const uint8_t* w3, const uint8_t* w2, int64_t T, int32_t D, int32_t I, int32_t E, int32_t k,
+                  float* out, uint8_t* ws, hipStream_t s, void* const* stage_events) {
+  const FfnWorkspace L = ffn_workspace_layout(T, D, I, E, k);
+  const int64_t entries = T * (int64_t)k;
+  const int64_t active = entries < E ? entries : E;
+  GroupArgs g{};
+  g.ids = topk_ids;
+  g.x = static_cast<const uint16_t*>(x_bf16);
+  g.T = T;
+  g.D = D;
+  g.E = E;
+  g.k = k;
+  g.rows_per_tile[0] = g.rows_per_tile[2] = q4k_rows_per_tile(true);
+  g.rows_per_tile[1] = g.rows_per_tile[3] = q4k_rows_per_tile(false);
+  g.split_rows = -1;  // every expert in lists 0 / 1
+  g.flag_big_rows = 0;
+  g.counts = reinterpret_cast<int32_t*>(ws + L.counts);
+  g.offsets = reinterpret_cast<int32_t*>(ws + L.offsets);
+  g.tile_count = reinterpret_cast<int32_t*>(ws + L.tile_count);
+  for (int l = 0; l < kTileLists; ++l) g.tiles[l] = reinterpret_cast<Tile*>(ws + L.tiles[l]);
+  g.row_tok = reinterpret_cast<int32_t*>(ws + L.row_tok);
+  g.slot_row = reinterpret_cast<int32_t*>(ws + L.slot_row);
+  g.chunk_base = reinterpret_cast<int32_t*>(ws + L.chunk_base);
+  g.chunk_mask = reinterpret_cast<unsigned long long*>(ws + L.chunk_mask);
+  g.x_perm = nullptr;
+  auto mark = [&](int i) -> bool {
+    if (!stage_events || !stage_events[i]) return true;
+    return hipEventRecord(static_cast<hipEvent_t>(stage_events[i]), s) == hipSuccess;
+  };
+  if (!mark(kEvGroup) || launch_group(g, s) != hipSuccess) return K3MOE_ERR_DEVICE;
+
+  GemmArgs gu{};
+  gu.act = static_cast<const uint16_t*>(x_bf16);
+  gu.act_rows = T;
+  gu.row_tok = g.row_tok;
+  gu.wa = w1;
+  gu.wb = w3;
+  gu.tiles = g.tiles[0];
+  gu.tile_count = g.tile_count;
+  const int64_t r_gu = q4k_rows_per_tile(true);
+  gu.max_tiles = (entries + (r_gu - 1) * active) / r_gu;  // bounds the sum of ceil(n_e / r) over experts
+  gu.K = D;
+  gu.N = I;
+  gu.out = ws + L.h;
+  gu.out_lo = ws + L.h_lo;
+  if (!mark(kEvGateUp) || launch_q4k_gemm(gu, true, s) != hipSuccess || !mark(kEvGateUpStream))
+    return K3MOE_ERR_DEVICE;
+
+  GemmArgs dn{};
+  dn.act = reinterpret_cast<const uint16_t*>(ws + L.h);
+  dn.act_lo = reinterpret_cast<const uint16_t*>(ws + L.h_lo);
+  dn.act_rows = entries;
+  dn.wa = w2;
+  dn.tiles = g.tiles[1];
+  dn.tile_count = g.tile_count + 1;
+  const int64_t r_dn = q4k_rows_per_tile(false);
+  dn.max_tiles = (entries + (r_dn - 1) * active) / r_dn;
+  dn.K = I;
+  dn.N = D;
+  dn.out = ws + L.y;
+  if (!mark(kEvDown) || launch_q4k_gemm(dn, false, s) != hipSuccess || !mark(kEvDownStream) || !mark(kEvCombine))
+    return K3MOE_ERR_DEVICE;
+  if (launch_combine(reinterpret_cast<const float*>(ws + L.y), nullptr, false, g.slot_row, topk_w, T, D, k, out, s) !=
+          hipSuccess ||
+      !mark(kEvEnd))
+    return K3MOE_ERR_DEVICE;
+  return K3MOE_OK;
+}
+
+int q4k_shape_status(int64_t T, int32_t D, int32_t I, int32_t E, int32_t k) {
+  const int st = ffn_shape_status(T, D, I, E, k);
+  if (st != K3MOE_OK) return st;
+  return q4k_gemm_supported(D, I) ? K3MOE_OK : K3MOE_ERR_SHAPE;
+}
+
 // Argument checks shared by the FFN entry points (workspace excluded).
 int ffn_arg_status(const void* x_bf16, const int32_t* topk_ids, const float* topk_w, const uint8_t* w1,
                    const uint8_t* w3, const uint8_t* w2, int64_t T, int32_t D, int32_t I, int32_t E, int32_t k,
@@ -502,6 +582,40 @@ int moe_mxfp4_ffn_noalloc(const void* x_bf16, const int32_t* topk_ids, const flo
   // every launch on the caller's stream: no side stream (creating one may allocate)
   return run_ffn(x_bf16, topk_ids, topk_w, w1, w3, w2, T, D, I, E, k, out, false, static_cast<uint8_t*>(ws),
                  static_cast<hipStream_t>(stream), nullptr, false);
+}
+
+size_t moe_q4k_ffn_workspace_size(int64_t T, int32_t D, int32_t I, int32_t E, int32_t k) {
+  if (q4k_shape_status(T, D, I, E, k) != K3MOE_OK || T == 0) return 0;
+  return ffn_workspace_layout(ffn_chunk_tokens(T, D, I, k), D, I, E, k).total;
+}
+
+int moe_q4k_ffn(const void* x_bf16, const int32_t* topk_ids, const float* topk_w, const uint8_t* w1,
+                const uint8_t* w3, const uint8_t* w2, int64_t T, int32_t D, int32_t I, int32_t E, int32_t k,
+                int32_t act, float* out, void* workspace, size_t workspace_bytes, void* stream) {
+  return moe_q4k_ffn_profiled(x_bf16, topk_ids, topk_w, w1, w3, w2, T, D, I, E, k, act, out, workspace,
+                              workspace_bytes, stream, nullptr);
+}
+
+int moe_q4k_ffn_profiled(const void* x_bf16, const int32_t* topk_ids, const float* topk_w, const uint8_t* w1,
+                         const uint8_t* w3, const uint8_t* w2, int64_t T, int32_t D, int32_t I, int32_t E, int32_t k,
+                         int32_t act, float* out, void* workspace, size_t workspace_bytes, void* stream,
+                         void* const* stage_events) {
+  int st = ffn_arg_status(x_bf16, topk_ids, topk_w, w1, w3, w2, T, D, I, E, k, act, out);
+  if (st != K3MOE_OK) return st;
+  st = q4k_shape_status(T, D, I, E, k);
+  if (st != K3MOE_OK || T == 0) return st;
+  if (!workspace) return K3MOE_ERR_NULL;
+  if (misaligned(workspace)) return K3MOE_ERR_ALIGN;
+  if (workspace_bytes < moe_q4k_ffn_workspace_size(T, D, I, E, k)) return K3MOE_ERR_WORKSPACE;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const int64_t tc = ffn_chunk_tokens(T, D, I, k);
+  for (int64_t t0 = 0; t0 < T; t0 += tc) {
+    const int64_t n = T - t0 < tc ? T - t0 : tc;
+    st = run_q4k_chunk(static_cast<const uint16_t*>(x_bf16) + t0 * D, topk_ids + t0 * k, topk_w + t0 * k, w1, w3, w2,
+                       n, D, I, E, k, out + t0 * D, static_cast<uint8_t*>(workspace), s, stage_events);
+    if (st != K3MOE_OK) return st;
+  }
+  return K3MOE_OK;
 }
 
 int moe_verify_width_distinct(const int32_t* topk_ids, int32_t S, int32_t W, int32_t E, int32_t k, int32_t* distinct,

@@ -362,7 +362,7 @@ __global__ __launch_bounds__(256) void group_place_kernel(GroupArgs a) {
     a.slot_row[t * a.k + j] = row;
   }
   const int64_t nt = (a.T - t0) < kChunkTokens ? (a.T - t0) : kChunkTokens;
-  permute_rows<8>(a.x, a.x_perm, t0, nt, a.D, part * blockDim.x + threadIdx.x, kPlaceParts * blockDim.x);
+  if (a.x_perm) permute_rows<8>(a.x, a.x_perm, t0, nt, a.D, part * blockDim.x + threadIdx.x, kPlaceParts * blockDim.x);
 }
 
 // All phases for a batch of at most one chunk (T <= 64), one launch.
@@ -374,7 +374,7 @@ __global__ __launch_bounds__(kScanThreads) void group_fused_kernel(GroupArgs a) 
   scan_experts(a, lmask, 1, lbase);
   lds_barrier();
   place_entries(a.ids, a.T, a.k, a.E, 0, lmask, lbase, a.row_tok, a.slot_row, a.flag_big_rows ? a.split_rows : -1);
-  permute_rows<4>(a.x, a.x_perm, 0, a.T, a.D, threadIdx.x, blockDim.x);
+  if (a.x_perm) permute_rows<4>(a.x, a.x_perm, 0, a.T, a.D, threadIdx.x, blockDim.x);
 }
 
 // All phases for a batch of at most 64 tokens and 1024 entries (decode-sized),
@@ -436,7 +436,7 @@ __global__ __launch_bounds__(kScanThreads) void group_small_kernel(GroupArgs a) 
     }
     a.slot_row[tid] = row;
   }
-  permute_rows<4>(a.x, a.x_perm, 0, a.T, a.D, tid, kScanThreads);
+  if (a.x_perm) permute_rows<4>(a.x, a.x_perm, 0, a.T, a.D, tid, kScanThreads);
 }
 
 // Activation re-layout only, for batches the gate/up launch groups itself.

@@ -96,7 +96,7 @@ struct GroupArgs {
   int32_t* slot_row;
   int32_t* chunk_base;
   unsigned long long* chunk_mask;
-  uint16_t* x_perm;
+  uint16_t* x_perm;  // null: no re-laid-out copy of x (a GEMM that reads x in its natural order)
 };
 hipError_t launch_group(const GroupArgs& a, hipStream_t s);
 // x [T, D] -> x_perm in the P order of the GEMM operands (the re-layout the
@@ -157,6 +157,14 @@ struct SelfGroupArgs {
   int32_t* slot_row;    // [T * k]: grouped row of each entry, -1 if skipped
 };
 hipError_t launch_stream_gate_up_grouped(const GemmArgs& a, const SelfGroupArgs& sg, bool natural_x, hipStream_t s);
+
+// Q4_K expert GEMMs (ggml block_q4_K, [E][rows][K / 256][144]): tiles of 16
+// token rows (gate/up) or 8 rows of h (down).  D and I multiples of 256.
+bool q4k_gemm_supported(int D, int I);
+int q4k_rows_per_tile(bool gate_up);
+hipError_t launch_q4k_gemm(const GemmArgs& a, bool gate_up, hipStream_t s);
+// Compute units of the current device (cached per device).
+int device_cu_count();
 
 // mixed: rows whose slot_row entry carries kBigRowFlag hold scaled fp16 y.
 hipError_t launch_combine(const float* y, const int8_t* y_scale, bool mixed, const int32_t* slot_row, const float* w,

@@ -25,7 +25,8 @@ def test_library_exports_every_declared_symbol(k3):
     names = declared_functions()
     assert set(names) == {"k3moe_status_str", "moe_route_topk", "mxfp4_repack", "mxfp4_dequant", "mxfp4_tile",
                           "moe_mxfp4_ffn_workspace_size", "moe_mxfp4_ffn", "moe_mxfp4_ffn_profiled",
-                          "moe_mxfp4_ffn_noalloc", "moe_group_workspace_size", "moe_group_by_expert",
+                          "moe_mxfp4_ffn_noalloc", "moe_q4k_ffn_workspace_size", "moe_q4k_ffn",
+                          "moe_q4k_ffn_profiled", "moe_group_workspace_size", "moe_group_by_expert",
                           "moe_verify_width_distinct", "moe_verify_width_choose", "moe_expert_cache_state_size",
                           "moe_expert_cache_init", "moe_expert_cache_route", "moe_latent_block_workspace_size",
                           "moe_latent_block", "moe_latent_block_profiled"}
@@ -123,6 +124,35 @@ def test_ffn_accepts_multiples_of_32(k3, D, I):
     # (a 1-byte workspace), before anything is enqueued
     assert k3.moe_mxfp4_ffn_workspace_size(8, D, I, 8, 2) > 0
     assert ffn(k3, D=D, I=I, ws_bytes=1) == ERR_WORKSPACE
+
+
+def q4k_ffn(k3, T=8, D=256, I=512, E=8, k=2, act=0, ws_bytes=1 << 30, **ptrs):
+    p = dict(x=A, ids=A, w=A, w1=A, w3=A, w2=A, out=A, ws=A)
+    p.update(ptrs)
+    return k3.lib.moe_q4k_ffn(p["x"], p["ids"], p["w"], p["w1"], p["w3"], p["w2"], T, D, I, E, k, act, p["out"],
+                              p["ws"], ws_bytes, None)
+
+
+def test_q4k_ffn_checks(k3):
+    # Q4_K blocks cover 256 weights: D and I must be multiples of 256
+    assert q4k_ffn(k3, D=128) == ERR_SHAPE
+    assert q4k_ffn(k3, I=96) == ERR_SHAPE
+    assert q4k_ffn(k3, D=256 + 32) == ERR_SHAPE
+    assert q4k_ffn(k3, D=65536 + 256) == ERR_SHAPE
+    assert q4k_ffn(k3, k=9, E=8) == ERR_SHAPE
+    assert q4k_ffn(k3, T=-1) == ERR_SHAPE
+    assert q4k_ffn(k3, act=1) == ERR_UNSUPPORTED
+    assert q4k_ffn(k3, T=0, x=None, ids=None, w=None, w1=None, w3=None, w2=None, out=None, ws=None, ws_bytes=0) == OK
+    assert q4k_ffn(k3, w2=None) == ERR_NULL
+    assert q4k_ffn(k3, ws=None) == ERR_NULL
+    assert q4k_ffn(k3, w1=A + 8) == ERR_ALIGN
+    need = k3.moe_q4k_ffn_workspace_size(8, 256, 512, 8, 2)
+    assert need > 0
+    assert q4k_ffn(k3, ws_bytes=need - 1) == ERR_WORKSPACE
+    assert k3.moe_q4k_ffn_workspace_size(8, 128, 512, 8, 2) == 0
+    assert k3.moe_q4k_ffn_workspace_size(0, 256, 512, 8, 2) == 0
+    # the same workspace layout as the MXFP4 path (grouping, h pair, fp32 y)
+    assert k3.moe_q4k_ffn_workspace_size(128, 3584, 3072, 896, 16) == k3.moe_mxfp4_ffn_workspace_size(128, 3584, 3072, 896, 16)
 
 
 def noalloc(k3, T=8, D=256, I=256, E=8, k=2, act=0, **ptrs):
