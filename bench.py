@@ -8,16 +8,20 @@ and the SiLU gating fused in, down grouped GEMM, weighted combine).  All 896
 experts (15.7 GB of 17-byte MXFP4 blocks) are resident; the batches rotate over
 several seeded routing inputs so successive steps touch different experts.
 
-    python bench.py [--workload prefill|verify|decode-t8|decode-t1|tiny] [--steps K] [--warmup W]
+    python bench.py [--workload prefill|verify|decode-t8|decode-t1|tiny|q4k-decode-t1|q4k-decode-t8|q4k-verify]
+                    [--steps K] [--warmup W]
                     [--no-extra] [--no-cpu-baseline]
 
 The headline workload (default: prefill, 4096 tokens) gives the JSON line's
 `value`.  With the default workload the same process also measures the 8- and
 1-token decode batches and the 128-token verify batch on the same resident
 experts and reports them under "workloads", the verify cost hint under
-"verify_width", and 8-token decode with the experts streamed from an external
+"verify_width", 8-token decode with the experts streamed from an external
 store (pinned host memory) through an 8 GiB device expert cache under
-"expert_cache" (--no-extra skips all of these).
+"expert_cache", the latent-MoE block under "latent_block", and then the
+decode and verify batches again with the experts stored as Q4_K blocks
+(moe_q4k_ffn), under "workloads" as q4k-decode-t1, q4k-decode-t8 and
+q4k-verify (--no-extra skips all of these; --workload q4k-... runs one alone).
 
 Without --steps, K is chosen so the timed steps take about half a second.
 
@@ -55,6 +59,9 @@ TRAFFIC_DIR = os.path.join(ROOT, "profiles")
 CSRC = "mxfp4_mixture_experts_moe_amd/csrc/"
 STREAM_MAX_ROWS = 16  # experts with more rows go to the large-tile kernels (tiled path)
 EXTRA_WORKLOADS = ("decode-t1", "decode-t8", "verify")
+# the same batches with the experts stored as Q4_K blocks (moe_q4k_ffn)
+Q4K_WORKLOADS = ("q4k-decode-t1", "q4k-decode-t8", "q4k-verify")
+Q4K_PREFIX = "q4k-"
 
 # launch slots of one step; event i is recorded right before launch i
 LAUNCHES = ("route", "group", "gate_up", "gate_up_stream", "down", "down_stream", "combine")
@@ -78,6 +85,11 @@ def kernel_info(launch: str, path: str, entries: int = 0, tokens: int = 0):
     None when the path has no launch there.  The large-tile down product takes
     128-row tiles from 16384 routed entries on, 64-row tiles below."""
     big, stream, ffn = CSRC + "ffn_big.hip", CSRC + "ffn_stream.hip", CSRC + "ffn.hip"
+    if path == "q4k":
+        if launch in ("gate_up", "down"):
+            return f"ffn_q4k_kernel<{'true' if launch == 'gate_up' else 'false'}>", [CSRC + "ffn_q4k.hip"]
+        if launch in ("gate_up_stream", "down_stream"):
+            return None
     if launch in ("gate_up", "down"):
         flag = "true" if launch == "gate_up" else "false"
         if path == "tiled":
@@ -107,7 +119,8 @@ def parse_args():
     ap.add_argument("--steps", type=int, default=0,
                     help="timed steps (0: as many as fill about 0.5 s, 20 to 5000)")
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="prefill", choices=["prefill", "verify", "decode-t8", "decode-t1", "tiny"])
+    ap.add_argument("--workload", default="prefill",
+                    choices=["prefill", "verify", "decode-t8", "decode-t1", "tiny", *Q4K_WORKLOADS])
     ap.add_argument("--block", default=None, choices=[b[0] for b in BLOCK_SIZES],
                     help="measure only the latent-MoE block at this size (prints its result line)")
     ap.add_argument("--rotate", type=int, default=0, help="distinct seeded batches cycled (0: 8 for decode, 4 else)")
@@ -163,7 +176,7 @@ def routing_stats(counts, path: str):
         c = int(c)
         if c == 0:
             continue
-        big = (path == "small") or (path == "tiled" and c > STREAM_MAX_ROWS)
+        big = (path in ("small", "q4k")) or (path == "tiled" and c > STREAM_MAX_ROWS)
         if big:
             rows_big += c
             experts_big += 1
@@ -184,8 +197,7 @@ def launch_work(launch, cfg, path, stats):
     """
     T, D, I, E, k = cfg.T, cfg.D, cfg.I, cfg.E, cfg.k
     rows_b, n_b, rows_s, n_s = stats
-    mat13 = I * (D // 32) * 17
-    mat2 = D * (I // 32) * 17
+    mat13, mat2 = matrix_bytes(cfg, path)
     hb = 2 if path == "tiled" else 4  # h bytes per element, big slot
     yb = 2 if path == "tiled" else 4  # y bytes per element, big slot
     if launch == "gate_up":
@@ -203,8 +215,20 @@ def launch_work(launch, cfg, path, stats):
     return 0.0, T * k * 4 * 3 + T * D * 4  # group: ids in, maps out, x in and re-laid out
 
 
+def matrix_bytes(cfg, path: str):
+    """Bytes of one w1 (or w3) and of one w2 matrix: 17 per 32 MXFP4 weights,
+    144 per 256 Q4_K weights."""
+    if path == "q4k":
+        return cfg.I * (cfg.D // 256) * 144, cfg.D * (cfg.I // 256) * 144
+    return cfg.I * (cfg.D // 32) * 17, cfg.D * (cfg.I // 32) * 17
+
+
 def arithmetic(path: str):
     """(dtype, description) of what the path computes in."""
+    if path == "q4k":
+        return ("bf16", "Q4_K codes exact in bf16 (as 128 + code); bf16 MFMA with fp32 accumulation, block scales "
+                "and mins applied in fp32 (the min terms as fp32 MFMAs); h as a bf16 hi+lo pair; fp32 expert "
+                "outputs and combine; fp64 routing scores")
     if path == "tiled":
         return ("bf16+fp16", "MXFP4 weights decoded exactly to bf16 (gate/up) and fp16 (down); bf16 MFMA gate/up, "
                 "fp16 MFMA down on h scaled per (row, 256 features); experts with <= 16 rows: bf16 MFMA with h "
@@ -243,17 +267,19 @@ def cpu_baseline(cfg, batch, sample_tokens):
     }
 
 
-def measure(name, cfg, dev, k3, steps, warmup, rotate, eager, cold_steps=0, serial=False):
-    """Time one workload on the resident experts; returns its result fields."""
+def measure(name, cfg, dev, k3, steps, warmup, rotate, eager, cold_steps=0, serial=False, q4k=False):
+    """Time one workload on the resident experts; returns its result fields.
+    q4k: the experts in `dev` are Q4_K blocks and the FFN is moe_q4k_ffn."""
     import numpy as np
     import torch
 
     from moe_inputs.device import upload_batch
 
-    path = gemm_path(cfg)
+    path = "q4k" if q4k else gemm_path(cfg)
+    ffn = k3.moe_q4k_ffn if q4k else k3.moe_mxfp4_ffn
+    ws_size = k3.moe_q4k_ffn_workspace_size if q4k else k3.moe_mxfp4_ffn_workspace_size
     batches = [upload_batch(cfg, seed=s) for s in range(rotate)]
-    ws = torch.empty(max(1, k3.moe_mxfp4_ffn_workspace_size(cfg.T, cfg.D, cfg.I, cfg.E, cfg.k)), dtype=torch.uint8,
-                     device="cuda")
+    ws = torch.empty(max(1, ws_size(cfg.T, cfg.D, cfg.I, cfg.E, cfg.k)), dtype=torch.uint8, device="cuda")
     out = torch.empty((cfg.T, cfg.D), dtype=torch.float32, device="cuda")
     ids = [torch.empty((cfg.T, cfg.k), dtype=torch.int32, device="cuda") for _ in range(rotate)]
     wts = [torch.empty((cfg.T, cfg.k), dtype=torch.float32, device="cuda") for _ in range(rotate)]
@@ -276,8 +302,8 @@ def measure(name, cfg, dev, k3, steps, warmup, rotate, eager, cold_steps=0, seri
         if events is not None and events[0] is not None:
             events[0].record()
         k3.moe_route_topk(z, b, cfg.k, ids=ids[j], weights=wts[j])
-        k3.moe_mxfp4_ffn(x, ids[j], wts[j], dev.w1, dev.w3, dev.w2, out=out, workspace=ws,
-                         stage_events=no_events if events is None else events[1:])
+        ffn(x, ids[j], wts[j], dev.w1, dev.w3, dev.w2, out=out, workspace=ws,
+            stage_events=no_events if events is None else events[1:])
 
     def busy_head():
         # keep the GPU busy while the host enqueues the measured steps, so no
@@ -385,7 +411,8 @@ def measure(name, cfg, dev, k3, steps, warmup, rotate, eager, cold_steps=0, seri
     traffic = stored_traffic(dom, name, ksrc)
 
     act_steps = [n_active[(warmup + i) % rotate] for i in range(steps)]
-    expert_bytes = 2 * cfg.I * (cfg.D // 32) * 17 + cfg.D * (cfg.I // 32) * 17
+    m13, m2 = matrix_bytes(cfg, path)
+    expert_bytes = 2 * m13 + m2
     weight_bytes = float(np.mean(act_steps)) * expert_bytes
     step_s = elapsed / steps
     dtype, arith = arithmetic(path)
@@ -402,7 +429,8 @@ def measure(name, cfg, dev, k3, steps, warmup, rotate, eager, cold_steps=0, seri
             "top_k": cfg.k,
             "latent_dim": cfg.D,
             "expert_intermediate": cfg.I,
-            "weights": "MXFP4 E2M1 + E8M0 in 17-byte blocks",
+            "weights": ("Q4_K (ggml block_q4_K): 144-byte blocks of 256 weights" if q4k
+                        else "MXFP4 E2M1 + E8M0 in 17-byte blocks"),
             "routing_inputs_rotated": rotate,
             "mean_active_experts": float(np.mean(act_steps)),
         },
@@ -443,6 +471,33 @@ def measure(name, cfg, dev, k3, steps, warmup, rotate, eager, cold_steps=0, seri
             "step_mfma_frac": cfg.T * 2 * cfg.k * 3 * cfg.D * cfg.I / (med * 1e-3) / (PEAK_BF16_TFLOPS * 1e12),
         }
     return res
+
+
+def q4k_device_experts(cfg, seed: int = 0):
+    """All E experts as Q4_K blocks drawn on the device (the recipe of
+    moe_inputs.q4k_blocks: uniform code and scale bytes, positive fp16 d and
+    dmin with exponent fields 1..3 and uniform mantissas) from a seeded torch
+    generator: 16.6 GB at K3 shape, which host generation would take a minute
+    to write.  Timing only; the parity tests draw their Q4_K experts on the host."""
+    import torch
+
+    from moe_inputs.device import DeviceExperts
+
+    g = torch.Generator(device="cuda")
+    g.manual_seed(1000 + seed)
+
+    def mat(rows, cols):
+        nb = cols // 256
+        b = torch.randint(0, 256, (cfg.E, rows, nb, 144), generator=g, dtype=torch.uint8, device="cuda")
+        for off in (0, 2):
+            e = torch.randint(1, 4, (cfg.E, rows, nb), generator=g, dtype=torch.int32, device="cuda")
+            m = torch.randint(0, 1024, (cfg.E, rows, nb), generator=g, dtype=torch.int32, device="cuda")
+            bits = (e << 10) | m
+            b[..., off] = (bits & 0xFF).to(torch.uint8)
+            b[..., off + 1] = (bits >> 8).to(torch.uint8)
+        return b
+
+    return DeviceExperts(mat(cfg.I, cfg.D), mat(cfg.I, cfg.D), mat(cfg.D, cfg.I))
 
 
 def measure_verify_width(dev, k3, warmup, reps=100):
@@ -761,9 +816,13 @@ def main():
                           "unit": "tokens/s", "n_gpus": 1, "higher_is_better": True, "data": "synthetic",
                           "latent_block": r}), flush=True)
         return
-    cfg = moe_inputs.CONFIGS[args.workload]
+    head_q4k = args.workload.startswith(Q4K_PREFIX)
+    cfg = moe_inputs.CONFIGS[args.workload[len(Q4K_PREFIX):] if head_q4k else args.workload]
     t_setup = time.perf_counter()
-    dev = upload_experts(cfg, lambda p, s, out: k3.mxfp4_tile(k3.mxfp4_repack(p, s), out=out))
+    if head_q4k:
+        dev = q4k_device_experts(cfg)
+    else:
+        dev = upload_experts(cfg, lambda p, s, out: k3.mxfp4_tile(k3.mxfp4_repack(p, s), out=out))
     torch.cuda.synchronize()
     setup_s = time.perf_counter() - t_setup
 
@@ -771,7 +830,7 @@ def main():
         return args.rotate or (8 if c.T <= 8 else 4)
 
     head = measure(args.workload, cfg, dev, k3, args.steps, args.warmup, rot(cfg), args.eager, args.cold_steps,
-                   args.serial_launches)
+                   args.serial_launches, q4k=head_q4k)
     batch0 = head.pop("_batch0")
     result = {
         "metric": METRIC,
@@ -785,7 +844,9 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": head["dtype"],
-        "data": "synthetic (seeded MXFP4 weights for all experts, bf16 N(0,1) activations, seeded router logits)",
+        "data": ("synthetic (seeded Q4_K weights for all experts drawn on the device, bf16 N(0,1) activations, "
+                 "seeded router logits)" if head_q4k else
+                 "synthetic (seeded MXFP4 weights for all experts, bf16 N(0,1) activations, seeded router logits)"),
     }
     result.update({k: v for k, v in head.items() if k not in ("value", "steps", "ms_per_step", "dtype")})
     result["setup_s"] = setup_s
@@ -801,7 +862,18 @@ def main():
         result["verify_width"] = measure_verify_width(dev, k3, args.warmup)
         result["expert_cache"] = measure_expert_cache(dev, k3, args.warmup)
         result["latent_block"] = measure_blocks(dev, k3, args.warmup)
-    if args.cpu_baseline:
+        del dev
+        torch.cuda.empty_cache()
+        dq = q4k_device_experts(cfg)
+        for w in Q4K_WORKLOADS:
+            c = moe_inputs.CONFIGS[w[len(Q4K_PREFIX):]]
+            r = measure(w, c, dq, k3, 0, args.warmup, rot(c), args.eager, args.cold_steps, args.serial_launches,
+                        q4k=True)
+            r.pop("_batch0")
+            r["tokens_per_s"] = r.pop("value")
+            extra[w] = r
+        del dq
+    if args.cpu_baseline and not head_q4k:
         sample = args.cpu_sample_tokens or (cfg.T if cfg.T <= 64 else 2)
         result["cpu_baseline"] = cpu_baseline(cfg, batch0, sample)
     print(json.dumps(result), flush=True)

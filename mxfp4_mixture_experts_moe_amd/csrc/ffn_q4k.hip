@@ -22,18 +22,19 @@
 //
 // Work decomposition.  The path serves every batch, and is laid out for the
 // few-token batches that stream the experts' weight bytes (HBM-bound):
-//   - persistent, one workgroup of four waves per CU; a unit is one tile of
+//   - persistent, two workgroups of four waves per CU (two waves per SIMD, so
+//     one wave's conversions and scaling overlap the other's MFMA and LDS
+//     latencies); a unit is one tile of
 //     one expert (gate/up: up to 16 token rows; down: up to 8 rows of h, as
 //     h_hi rows 0-7 and h_lo rows 8-15 of the MFMA) times four waves'
 //     features (gate/up: 16 features of w1 and of w3 per wave; down: 32 of
 //     w2), over the whole K;
-//   - a stage is two blocks (512 K, 288 bytes) of each of a wave's 32 weight
+//   - a stage is one block (256 K, 144 bytes) of each of a wave's 32 weight
 //     rows, copied by direct global -> LDS loads of 16 bytes per lane into the
 //     wave's own ring of three stage buffers, two stages ahead of the one it
-//     computes; the tile's activation rows for the same 512 K ride in a ring
+//     computes; the tile's activation rows for the same 256 K ride in a ring
 //     the four waves share (each wave loads its share of the live rows), with
-//     one barrier per stage; with an odd number of blocks the last stage
-//     carries one block and loads only that;
+//     one barrier per stage;
 //   - the MFMA output is 16 token rows x 16 features; rows of the tile that
 //     do not exist read whatever their LDS slot holds and are never stored.
 #include "k3moe_internal.h"
@@ -61,22 +62,23 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
-constexpr int kWaves = 4;            // waves per workgroup (one workgroup per CU)
+constexpr int kWaves = 4;            // waves per workgroup
+constexpr int kWgPerCu = 2;          // workgroups per CU (the LDS of two fits)
 constexpr int kRing = 3;             // stage buffers
 constexpr int kBlkBytes = 144;       // one Q4_K block
-constexpr int kStageK = 512;         // two blocks per row and stage
-constexpr int kStageRowBytes = 288;  // one row's share of a stage
-constexpr int kRowChunks = 18;       // 16-byte chunks of it
+constexpr int kStageK = 256;         // one block per row and stage
+constexpr int kStageRowBytes = kBlkBytes;  // one row's share of a stage
+constexpr int kRowChunks = 9;        // 16-byte chunks of it
 constexpr int kMatBytes = 16 * kStageRowBytes;     // a 16-row weight block of a stage
-constexpr int kMatInstr = (16 * kRowChunks + 63) / 64;  // 5 loads (the fifth for 32 lanes)
+constexpr int kMatInstr = (16 * kRowChunks + 63) / 64;  // 3 loads (the third for 16 lanes)
 constexpr int kRB = 2;                             // 16-row weight blocks per wave
 constexpr int kW = kRB * kMatInstr;                // weight loads per wave and stage
 constexpr int kWBytes = kRB * kMatBytes;           // a wave's stage buffer
 constexpr int kBRows = 16;                         // activation rows of a tile in the MFMA
-constexpr int kBRowBytes = 1040;                   // 1 KB per row and stage + 16 bytes against bank conflicts
+constexpr int kBRowBytes = 528;                    // 512 bytes per row and stage + 16 against bank conflicts
 constexpr int kA = kBRows / kWaves;                // activation rows each wave loads
 constexpr int kNt = 2;                             // weights: nontemporal (read once per call)
-static_assert(kWaves * kRing * kWBytes + kRing * kBRows * kBRowBytes <= 160 * 1024, "LDS");
+static_assert(kWaves * kRing * kWBytes + kRing * kBRows * kBRowBytes <= 160 * 1024 / kWgPerCu, "LDS");
 static_assert(2 * kW + kA < 64, "vmcnt range");
 
 template <bool kGateUp>
@@ -128,8 +130,7 @@ __device__ __forceinline__ Q4Tile load_q4_tile(const Tile* tiles, int idx) {
 // own wait (as plain loads the compiler would wait for every global -> LDS
 // load in flight before them):
 //   x[j]  (j = 0..7): 16 bytes of the activations of sub-block j for this
-//         lane's token row (ap = row start + 512 * block + 16 * g; sub-block j
-//         at +64 j);
+//         lane's token row (ap = row start + 16 * g; sub-block j at +64 j);
 //   hd[r] (r = 0..1): the 16-byte header of the block in weight block r's
 //         row of this lane (h0 / h1 = the block's first byte);
 //   qd[r][c] (c = 0..3): code bytes 32c + 8g .. 32c + 8g + 7 of the same
@@ -174,7 +175,7 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
 }
 
 template <bool kGateUp>
-__global__ __launch_bounds__(kWaves * 64, 1) void ffn_q4k_kernel(GemmArgs a) {
+__global__ __launch_bounds__(kWaves * 64, kWgPerCu) void ffn_q4k_kernel(GemmArgs a) {
   using C = Q4KCfg<kGateUp>;
   constexpr int kTileRows = C::kTileRows;
   __shared__ __attribute__((aligned(16))) uint8_t wlds[kWaves][kRing][kWBytes];
@@ -192,22 +193,20 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ffn_q4k_kernel(GemmArgs a) {
   if (wg >= n_units) return;  // uniform over the workgroup; every later barrier is reached by all waves
   const int64_t my_units = (n_units - wg + nwg - 1) / nwg;
   const int nb = a.K >> 8;                  // blocks per row
-  const int nst = (nb + 1) >> 1;            // stages per unit
+  const int nst = nb;                       // stages per unit
   const int64_t Q = my_units * nst;
   const uint32_t row_bytes = (uint32_t)nb * kBlkBytes;
   const size_t mat_bytes = (size_t)a.N * row_bytes;
   const uint32_t act_row_bytes = (uint32_t)a.K * 2;
 
   // per-lane source offsets of a 16-row weight block's stage: chunk c = 64 j +
-  // lane is 16 bytes at row c / 18, byte 16 (c % 18) of the row's stage
+  // lane is 16 bytes at row c / 9, byte 16 (c % 9) of the row's block
   uint32_t woff[kMatInstr];
-  bool wfirst[kMatInstr];  // the chunk belongs to the stage's first block
 #pragma unroll
   for (int j = 0; j < kMatInstr; ++j) {
     const int c = 64 * j + lane;
     const int r = c / kRowChunks, p = c - r * kRowChunks;
     woff[j] = c < 16 * kRowChunks ? (uint32_t)r * row_bytes + 16u * (uint32_t)p : 0u;
-    wfirst[j] = p < kRowChunks / 2;
   }
   const bool wtail = lane < 16 * kRowChunks - 64 * (kMatInstr - 1);
 
@@ -231,14 +230,12 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ffn_q4k_kernel(GemmArgs a) {
     if (c.u < n_units) load_unit(c);
   };
 
-  // weight loads of cursor c's stage into stage buffer buf (this wave's rows);
-  // a one-block stage loads only the first block of each row
+  // weight loads of cursor c's stage into stage buffer buf (this wave's rows)
   auto issue_w = [&](const Cur& c, int buf) {
     const int fg = kWaves * c.gr + wave;
     const size_t unit_off = (size_t)c.tile.expert * mat_bytes + (size_t)(C::kFeat * fg) * row_bytes;
     uint8_t* dst = &wlds[wave][buf][0];
     const uint32_t wso = (uint32_t)(kStageRowBytes * c.s);
-    const bool half = 2 * c.s + 1 == nb;
 #pragma unroll
     for (int mi = 0; mi < kRB; ++mi) {
       const uint8_t* base =
@@ -248,8 +245,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ffn_q4k_kernel(GemmArgs a) {
 #pragma unroll
       for (int j = 0; j < kMatInstr; ++j) {
         // every load keeps at least one lane, so each one is issued and counted
-        const bool on = (j < kMatInstr - 1 || wtail) && (!half || wfirst[j]);
-        if (on)
+        if (j < kMatInstr - 1 || wtail)
           __builtin_amdgcn_raw_ptr_buffer_load_lds(
               wr, (__attribute__((address_space(3))) void*)(uintptr_t)(dst + mi * kMatBytes + 1024 * j), 16, woff[j],
               wso, 0, kNt);
@@ -261,7 +257,6 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ffn_q4k_kernel(GemmArgs a) {
   auto issue_a = [&](const Cur& c, int buf) -> int {
     uint8_t* dst = &alds[buf][0];
     const uint32_t aso = (uint32_t)(kStageK * 2 * c.s);
-    const bool half = 2 * c.s + 1 == nb;
     const __amdgpu_buffer_rsrc_t xr =
         __builtin_amdgcn_make_buffer_rsrc((void*)a.act, 0, (int)((uint32_t)a.act_rows * act_row_bytes), 0x00020000);
     const __amdgpu_buffer_rsrc_t lr = __builtin_amdgcn_make_buffer_rsrc(
@@ -275,7 +270,7 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ffn_q4k_kernel(GemmArgs a) {
         const int row = c.tile.row0 + mr;
         const int xrow = kGateUp ? row_tok[row] : row;
         const uint32_t so = (uint32_t)xrow * act_row_bytes + aso;
-        if (!half || lane < 32) {
+        if (lane < kStageK * 2 / 16) {  // 512 bytes: 32 lanes
           if (kGateUp || m < kTileRows)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(
                 xr, (__attribute__((address_space(3))) void*)(uintptr_t)(dst + kBRowBytes * m), 16, 16 * lane, so, 0, 0);
@@ -338,22 +333,17 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ffn_q4k_kernel(GemmArgs a) {
     const uint32_t wl = (uint32_t)(uintptr_t)&wlds[wave][buf_c][0];
     const uint32_t al = (uint32_t)(uintptr_t)&alds[buf_c][0] + kBRowBytes * fl + 16 * g;
     buf_c = buf_c == kRing - 1 ? 0 : buf_c + 1;
-    const int nblk = 2 * cc.s + 1 == nb ? 1 : 2;
-    for (int b = 0; b < nblk; ++b) {
+    {
       u32x4_t xr[8], hd[2];
       u32x2_t qd[2][4];
-      const uint32_t w0 = wl + kStageRowBytes * fl + kBlkBytes * b;
-      read_block_operands(al + 512 * b, w0, w0 + kMatBytes, w0 + 8 * g, w0 + kMatBytes + 8 * g, xr, hd, qd);
+      const uint32_t w0 = wl + kStageRowBytes * fl;
+      read_block_operands(al, w0, w0 + kMatBytes, w0 + 8 * g, w0 + kMatBytes + 8 * g, xr, hd, qd);
       bf16x8_t xo[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) xo[j] = __builtin_bit_cast(bf16x8_t, xr[j]);
-      // Sx of sub-blocks g and g + 4 for token fl, in every element
-      f32x4_t s0 = f32x4_t{0.f, 0.f, 0.f, 0.f}, s1 = s0;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ind[j], xo[j], s0, 0, 0, 0);
-        s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ind[j], xo[4 + j], s1, 0, 0, 0);
-      }
+      // each lane decodes sub-blocks g and g + 4 of its feature's block in
+      // both weight blocks: ds = d * scale, nc = -(128 ds + dmin * min)
+      float dsa[kRB], dsb[kRB], nca[kRB], ncb[kRB];
 #pragma unroll
       for (int mi = 0; mi < kRB; ++mi) {
         const u32x4_t h = hd[mi];
@@ -362,29 +352,50 @@ __global__ __launch_bounds__(kWaves * 64, 1) void ffn_q4k_kernel(GemmArgs a) {
         const uint32_t sca = __builtin_amdgcn_ubfe(h.y, sh, 6), ma = __builtin_amdgcn_ubfe(h.z, sh, 6);
         const uint32_t scb = __builtin_amdgcn_ubfe(h.w, sh, 4) | (__builtin_amdgcn_ubfe(h.y, sh + 6, 2) << 4);
         const uint32_t mb = __builtin_amdgcn_ubfe(h.w, sh + 4, 4) | (__builtin_amdgcn_ubfe(h.z, sh + 6, 2) << 4);
-        const float dsa = d * (float)sca, dsb = d * (float)scb;
-        const float nca = fmaf(-128.f, dsa, -(dmin * (float)ma));
-        const float ncb = fmaf(-128.f, dsb, -(dmin * (float)mb));
-        acc[mi] = __builtin_amdgcn_mfma_f32_16x16x4f32(s0[0], nca, acc[mi], 0, 0, 0);
-        acc[mi] = __builtin_amdgcn_mfma_f32_16x16x4f32(s1[0], ncb, acc[mi], 0, 0, 0);
-        // ds of all eight sub-blocks of feature fl: sub-block j sits in lane fl + 16 (j % 4)
-        float ds[8];
+        dsa[mi] = d * (float)sca;
+        dsb[mi] = d * (float)scb;
+        nca[mi] = fmaf(-128.f, dsa[mi], -(dmin * (float)ma));
+        ncb[mi] = fmaf(-128.f, dsb[mi], -(dmin * (float)mb));
+      }
+      // ds of all eight sub-blocks of feature fl: sub-block j sits in lane fl + 16 (j % 4)
+      float ds[kRB][8];
+#pragma unroll
+      for (int mi = 0; mi < kRB; ++mi)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          ds[j] = __shfl(dsa, fl + 16 * j, 64);
-          ds[4 + j] = __shfl(dsb, fl + 16 * j, 64);
+          ds[mi][j] = __shfl(dsa[mi], fl + 16 * j, 64);
+          ds[mi][4 + j] = __shfl(dsb[mi], fl + 16 * j, 64);
         }
+      // Sx of sub-blocks g (s0) and g + 4 (s1) for token fl, in every element
+      f32x4_t s0 = f32x4_t{0.f, 0.f, 0.f, 0.f}, s1 = s0;
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
+      for (int c = 0; c < 4; ++c) {
+        const int j0 = 2 * c, j1 = 2 * c + 1;
+        if (j0 < 4)
+          s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ind[j0], xo[j0], s0, 0, 0, 0);
+        else
+          s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ind[j0 - 4], xo[j0], s1, 0, 0, 0);
+        if (j1 < 4)
+          s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ind[j1], xo[j1], s0, 0, 0, 0);
+        else
+          s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ind[j1 - 4], xo[j1], s1, 0, 0, 0);
+#pragma unroll
+        for (int mi = 0; mi < kRB; ++mi) {
           const u32x2_t qv = qd[mi][c];
           const bf16x8_t wlo = codes_to_bf16(qv.x & 0x0F0F0F0Fu, qv.y & 0x0F0F0F0Fu);
           const bf16x8_t whi = codes_to_bf16((qv.x >> 4) & 0x0F0F0F0Fu, (qv.y >> 4) & 0x0F0F0F0Fu);
           const f32x4_t z = f32x4_t{0.f, 0.f, 0.f, 0.f};
-          const f32x4_t t0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xo[2 * c], wlo, z, 0, 0, 0);
-          const f32x4_t t1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xo[2 * c + 1], whi, z, 0, 0, 0);
+          const f32x4_t t0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xo[j0], wlo, z, 0, 0, 0);
+          const f32x4_t t1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(xo[j1], whi, z, 0, 0, 0);
 #pragma unroll
-          for (int v = 0; v < 4; ++v) acc[mi][v] = fmaf(t1[v], ds[2 * c + 1], fmaf(t0[v], ds[2 * c], acc[mi][v]));
+          for (int v = 0; v < 4; ++v) acc[mi][v] = fmaf(t1[v], ds[mi][j1], fmaf(t0[v], ds[mi][j0], acc[mi][v]));
         }
+      }
+      // the min terms (and the 128 Sx the codes carried), one fp32 MFMA per four sub-blocks
+#pragma unroll
+      for (int mi = 0; mi < kRB; ++mi) {
+        acc[mi] = __builtin_amdgcn_mfma_f32_16x16x4f32(s0[0], nca[mi], acc[mi], 0, 0, 0);
+        acc[mi] = __builtin_amdgcn_mfma_f32_16x16x4f32(s1[0], ncb[mi], acc[mi], 0, 0, 0);
       }
     }
 
@@ -441,8 +452,8 @@ int q4k_rows_per_tile(bool gate_up) { return gate_up ? Q4KCfg<true>::kTileRows :
 hipError_t launch_q4k_gemm(const GemmArgs& a, bool gate_up, hipStream_t s) {
   const int feat = gate_up ? Q4KCfg<true>::kFeat : Q4KCfg<false>::kFeat;
   int64_t grid = a.max_tiles * (a.N / feat / kWaves);
-  const int cus = device_cu_count();
-  if (grid > cus) grid = cus;
+  const int64_t slots = (int64_t)kWgPerCu * device_cu_count();
+  if (grid > slots) grid = slots;
   if (grid < 1) grid = 1;
   if (gate_up)
     hipLaunchKernelGGL(ffn_q4k_kernel<true>, dim3((unsigned)grid), dim3(kWaves * 64), 0, s, a);

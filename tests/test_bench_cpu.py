@@ -103,3 +103,23 @@ def test_routing_stats_split_at_sixteen_rows():
     assert bench.routing_stats(counts, "tiled") == (117, 2, 20, 3)
     assert bench.routing_stats(counts, "stream") == (0, 0, 137, 5)
     assert bench.routing_stats(counts, "small") == (137, 5, 0, 0)
+
+
+def test_q4k_accounting():
+    # the Q4_K path: every expert in the gate_up / down launches of
+    # ffn_q4k_kernel, 144 bytes per 256 weights
+    cfg = moe_inputs.DECODE8
+    assert bench.kernel_info("gate_up", "q4k")[0] == "ffn_q4k_kernel<true>"
+    assert bench.kernel_info("down", "q4k")[0] == "ffn_q4k_kernel<false>"
+    assert bench.kernel_info("gate_up_stream", "q4k") is None and bench.kernel_info("down_stream", "q4k") is None
+    assert os.path.exists(os.path.join(bench.ROOT, bench.kernel_info("down", "q4k")[1][0]))
+    counts = _counts(cfg)
+    st = bench.routing_stats(counts, "q4k")
+    assert st[0] == cfg.T * cfg.k and st[1] == int((counts > 0).sum()) and st[2] == st[3] == 0
+    more = (st[0], st[1] + 1, 0, 0)
+    d = sum(bench.launch_work(l, cfg, "q4k", more)[1] - bench.launch_work(l, cfg, "q4k", st)[1]
+            for l in GEMM_LAUNCHES)
+    assert d == 3 * cfg.I * cfg.D // 256 * 144 == 18579456
+    flops = sum(bench.launch_work(l, cfg, "q4k", st)[0] for l in GEMM_LAUNCHES)
+    assert flops == K3_FLOPS_PER_TOKEN * cfg.T
+    assert set(bench.Q4K_WORKLOADS) <= set(["q4k-" + w for w in moe_inputs.CONFIGS])
