@@ -77,7 +77,7 @@ constexpr int kWBytes = kRB * kMatBytes;           // a wave's stage buffer
 constexpr int kBRows = 16;                         // activation rows of a tile in the MFMA
 constexpr int kBRowBytes = 528;                    // 512 bytes per row and stage + 16 against bank conflicts
 constexpr int kA = kBRows / kWaves;                // activation rows each wave loads
-constexpr int kNt = 2;                             // weights: nontemporal (read once per call)
+constexpr int kNt = 0;                             // weights: default caching (a 144-byte piece shares cache lines with the next stage's)
 static_assert(kWaves * kRing * kWBytes + kRing * kBRows * kBRowBytes <= 160 * 1024 / kWgPerCu, "LDS");
 static_assert(2 * kW + kA < 64, "vmcnt range");
 
