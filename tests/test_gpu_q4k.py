@@ -5,8 +5,8 @@ and, tighter, relative L2 <= 1e-4: the codes enter the MFMA exactly, the
 block scales and mins are applied in fp32 and h carries about 16 significant
 bits (the bf16 hi + lo pair), so the kernel's error is fp32 rounding, far
 below the bar.  Small configs are compared on every output, the K3-shaped
-decode batches on every token (1 token) or sampled tokens (8 tokens), which
-the oracle evaluates one expert at a time.
+batches on every token (1 token) or chosen tokens (8 tokens; the verify
+batch's hottest expert), which the oracle evaluates one expert at a time.
 """
 
 import numpy as np
@@ -85,10 +85,10 @@ def routed_case(cfg, seed=None):
 @pytest.mark.parametrize(
     "E,k,D,I,T",
     [
-        (8, 2, 512, 768, 1),  # odd block count on the down product's K (a one-block last stage)
+        (8, 2, 512, 768, 1),  # three blocks per row on the down product's K
         (8, 2, 512, 768, 5),
-        (8, 2, 768, 512, 40),  # odd block count on gate/up's K
-        (8, 2, 256, 256, 3),  # one block per row: the only stage is a one-block stage
+        (8, 2, 768, 512, 40),  # three blocks per row on gate/up's K
+        (8, 2, 256, 256, 3),  # one block per row: a unit is a single stage
         (16, 4, 512, 512, 64),
         (8, 8, 512, 1280, 17),  # k = E: every expert sees every token (two 16-row tiles + 1)
     ],
@@ -222,3 +222,21 @@ def test_q4k_k3_decode(k3, name, tokens):
     sel = np.arange(cfg.T) if tokens is None else np.asarray(tokens)
     ref = ffn_q4k_ref(batch.x, ids, w, host, tokens=sel)
     check(got[sel], ref, f"q4k K3 {name}")
+
+
+def test_q4k_k3_verify_hot_expert_tiles(k3):
+    # K3 verify batch (128 tokens, Zipf-skewed routing): the hottest expert has
+    # about 127 rows (eight 16-row gate/up and sixteen 8-row down tiles); the
+    # checked tokens are its last and first rows and the batch's last token
+    cfg = moe_inputs.VERIFY
+    batch, ids, w = routed_case(cfg)
+    counts = np.bincount(ids.reshape(-1), minlength=cfg.E)
+    hot = int(np.argmax(counts))
+    rows = np.nonzero((ids == hot).any(axis=1))[0]
+    assert counts[hot] > 64, counts[hot]
+    sel = np.unique([rows[-1], rows[0], cfg.T - 1])
+    host = Q4KExperts(cfg)
+    print(f"[q4k] K3 verify, hot expert {hot} with {counts[hot]} rows, tokens {sel.tolist()}", flush=True)
+    got, _ = run(k3, host, batch.x, ids, w)
+    ref = ffn_q4k_ref(batch.x, ids, w, host, tokens=sel)
+    check(got[sel], ref, "q4k K3 verify")
