@@ -240,3 +240,24 @@ def test_q4k_k3_verify_hot_expert_tiles(k3):
     got, _ = run(k3, host, batch.x, ids, w)
     ref = ffn_q4k_ref(batch.x, ids, w, host, tokens=sel)
     check(got[sel], ref, "q4k K3 verify")
+
+
+def test_q4k_k3_prefill_two_token_chunks(k3):
+    # 20000 tokens at K3 shape run as a chunk of 18688 tokens and one of 1312
+    # (32-bit activation offsets); checked: both sides of the chunk boundary,
+    # the last token and the last row of each chunk's hottest expert
+    cfg = moe_inputs.PREFILL.with_(T=20000, config_id=85)
+    batch, ids, w = routed_case(cfg)
+    host = Q4KExperts(cfg)
+    chunk = 18688
+    toks = {chunk - 1, chunk, cfg.T - 1}
+    for lo, hi in ((0, chunk), (chunk, cfg.T)):
+        sub = ids[lo:hi]
+        e = int(np.argmax(np.bincount(sub.reshape(-1), minlength=cfg.E)))
+        toks.add(lo + int(np.argwhere(sub == e)[:, 0].max()))
+    toks = sorted(toks)
+    print(f"[q4k] K3 prefill T={cfg.T}: tokens {toks}", flush=True)
+    got, _ = run(k3, host, batch.x, ids, w)
+    assert np.all(np.isfinite(got))
+    ref = ffn_q4k_ref(batch.x, ids, w, host, tokens=np.array(toks))
+    check(got[toks], ref, f"q4k T=20000 tokens {toks}")
