@@ -79,6 +79,7 @@ def test_tiny(k3):
         (3, 3, 512, 1024, 5),  # streaming-only batch: every expert has all 5 rows
         (4, 2, 512, 512, 9),  # one token past the streaming-only batch: large-tile kernels for experts of 5+ rows
         (200, 64, 512, 512, 4),  # grouping inside the gate/up launch: 256 entries, one per thread
+        (200, 64, 512, 512, 8),  # grouping inside the gate/up launch at its limit: 512 entries
         (8, 2, 96, 160, 50),  # D, I multiples of 32 only: odd block counts (unaligned rows), a 32-feature tile
         (6, 3, 224, 288, 70),  # 7 and 9 blocks per row, 224 / 288 outputs (a partial last feature tile)
         (4, 2, 32, 32, 10),  # one block per row, one 32-feature tile

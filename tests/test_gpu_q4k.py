@@ -91,6 +91,7 @@ def routed_case(cfg, seed=None):
         (8, 2, 256, 256, 3),  # one block per row: a unit is a single stage
         (16, 4, 512, 512, 64),
         (8, 8, 512, 1280, 17),  # k = E: every expert sees every token (two 16-row tiles + 1)
+        (200, 64, 512, 512, 8),  # the largest top-k: 512 routed entries
     ],
 )
 def test_q4k_shapes(k3, E, k, D, I, T):
