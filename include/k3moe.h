@@ -506,6 +506,19 @@ int moe_expert_cache_route(void* state, size_t state_bytes, int32_t E, int32_t C
                            int32_t I, void* stream);
 
 /*
+ * moe_expert_cache_route_q4k — moe_expert_cache_route for experts stored as
+ * Q4_K blocks (the encoding moe_q4k_ffn reads): store_w1 / store_w3 u8
+ * [E, I, D/256, 144], store_w2 u8 [E, D, I/256, 144], the slots likewise with
+ * C; pass slot_ids and the slots to moe_q4k_ffn with E = C. Same state,
+ * policy, launches, checks and results, with D and I multiples of 256
+ * (K3MOE_ERR_SHAPE otherwise).
+ */
+int moe_expert_cache_route_q4k(void* state, size_t state_bytes, int32_t E, int32_t C, const int32_t* topk_ids,
+                               int64_t T, int32_t k, int32_t* slot_ids, const uint8_t* store_w1,
+                               const uint8_t* store_w3, const uint8_t* store_w2, uint8_t* cache_w1,
+                               uint8_t* cache_w3, uint8_t* cache_w2, int32_t D, int32_t I, void* stream);
+
+/*
  * moe_latent_block — the latent-MoE block around the routed experts.
  * Sources: llama.cpp pull request "model: add Kimi-K3 text model": opening
  * comment (latent MoE: routed experts run at a latent width), dry-run comment

@@ -100,6 +100,7 @@ lib.moe_expert_cache_init.argtypes = [_vp, _sz, _i32, _i32, _vp]
 lib.moe_expert_cache_route.restype = ctypes.c_int
 lib.moe_expert_cache_route.argtypes = [_vp, _sz, _i32, _i32, _vp, _i64, _i32, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
                                        _i32, _i32, _vp]
+lib.moe_expert_cache_route_q4k.argtypes = lib.moe_expert_cache_route.argtypes
 EXPERT_CACHE_TAG = 0x4B334543
 lib.moe_latent_block_workspace_size.restype = _sz
 lib.moe_latent_block_workspace_size.argtypes = [_i64, _i32, _i32, _i32, _i32, _i32, _i32]
@@ -431,10 +432,11 @@ def _store(t: torch.Tensor, name: str) -> None:
 def moe_expert_cache_route(state: torch.Tensor, E: int, C: int, ids: torch.Tensor, store_w1: torch.Tensor,
                            store_w3: torch.Tensor, store_w2: torch.Tensor, cache_w1: torch.Tensor,
                            cache_w3: torch.Tensor, cache_w2: torch.Tensor,
-                           slot_ids: torch.Tensor | None = None) -> torch.Tensor:
+                           slot_ids: torch.Tensor | None = None, q4k: bool = False) -> torch.Tensor:
     """Stage a batch's routed experts into the C slots; returns slot_ids
     int32 [T, k] (the FFN then runs on cache_w* with slot_ids and E = C).
-    store_w*: all E experts, device tensors or pinned host tensors."""
+    store_w*: all E experts, device tensors or pinned host tensors; MXFP4
+    blocks, or Q4_K blocks with q4k=True (moe_expert_cache_route_q4k)."""
     _dev(state, "state", torch.uint8)
     _dev(ids, "ids", torch.int32)
     for n, t in (("store_w1", store_w1), ("store_w3", store_w3), ("store_w2", store_w2)):
@@ -443,18 +445,20 @@ def moe_expert_cache_route(state: torch.Tensor, E: int, C: int, ids: torch.Tenso
         _dev(t, n, torch.uint8)
     T, k = ids.shape
     I, D = store_w1.shape[1], store_w2.shape[1]
-    if store_w1.shape != (E, I, D // 32, 17) or store_w3.shape != store_w1.shape or \
-            store_w2.shape != (E, D, I // 32, 17):
-        raise ValueError("store matrices must be [E, I, D/32, 17] and [E, D, I/32, 17]")
-    if cache_w1.shape != (C, I, D // 32, 17) or cache_w3.shape != cache_w1.shape or \
-            cache_w2.shape != (C, D, I // 32, 17):
-        raise ValueError("cache matrices must be [C, I, D/32, 17] and [C, D, I/32, 17]")
+    blk, nbytes = (256, 144) if q4k else (32, 17)
+    if store_w1.shape != (E, I, D // blk, nbytes) or store_w3.shape != store_w1.shape or \
+            store_w2.shape != (E, D, I // blk, nbytes):
+        raise ValueError(f"store matrices must be [E, I, D/{blk}, {nbytes}] and [E, D, I/{blk}, {nbytes}]")
+    if cache_w1.shape != (C, I, D // blk, nbytes) or cache_w3.shape != cache_w1.shape or \
+            cache_w2.shape != (C, D, I // blk, nbytes):
+        raise ValueError(f"cache matrices must be [C, I, D/{blk}, {nbytes}] and [C, D, I/{blk}, {nbytes}]")
     if slot_ids is None:
         slot_ids = torch.empty((T, k), dtype=torch.int32, device=ids.device)
     _dev(slot_ids, "slot_ids", torch.int32)
     if slot_ids.shape != (T, k):
         raise ValueError("slot_ids must be [T, k]")
-    _check("moe_expert_cache_route", lib.moe_expert_cache_route(
+    fn = "moe_expert_cache_route_q4k" if q4k else "moe_expert_cache_route"
+    _check(fn, getattr(lib, fn)(
         _ptr(state), state.numel(), E, C, _ptr(ids), T, k, _ptr(slot_ids), _ptr(store_w1), _ptr(store_w3),
         _ptr(store_w2), _ptr(cache_w1), _ptr(cache_w3), _ptr(cache_w2), D, I, _stream(ids.device)))
     return slot_ids

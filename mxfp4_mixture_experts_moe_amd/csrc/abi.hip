@@ -682,13 +682,16 @@ static const uint8_t* device_readable(const uint8_t* p) {
   return nullptr;
 }
 
-int moe_expert_cache_route(void* state, size_t state_bytes, int32_t E, int32_t C, const int32_t* topk_ids, int64_t T,
-                           int32_t k, int32_t* slot_ids, const uint8_t* store_w1, const uint8_t* store_w3,
-                           const uint8_t* store_w2, uint8_t* cache_w1, uint8_t* cache_w3, uint8_t* cache_w2, int32_t D,
-                           int32_t I, void* stream) {
+// Both cache entry points: `block` weights per `bytes` bytes (MXFP4: 32 per 17,
+// Q4_K: 256 per 144); the experts are copied whole, so the kernels never look
+// inside the blocks.
+static int cache_route(void* state, size_t state_bytes, int32_t E, int32_t C, const int32_t* topk_ids, int64_t T,
+                       int32_t k, int32_t* slot_ids, const uint8_t* store_w1, const uint8_t* store_w3,
+                       const uint8_t* store_w2, uint8_t* cache_w1, uint8_t* cache_w3, uint8_t* cache_w2, int32_t D,
+                       int32_t I, int32_t block, int32_t bytes, void* stream) {
   const size_t need = moe_expert_cache_state_size(E, C);
   if (need == 0 || T < 0 || k < 1 || k > K3MOE_MAX_TOPK) return K3MOE_ERR_SHAPE;
-  if (D <= 0 || I <= 0 || (D % 32) != 0 || (I % 32) != 0 || D > K3MOE_MAX_DIM_FFN || I > K3MOE_MAX_DIM_FFN)
+  if (D <= 0 || I <= 0 || (D % block) != 0 || (I % block) != 0 || D > K3MOE_MAX_DIM_FFN || I > K3MOE_MAX_DIM_FFN)
     return K3MOE_ERR_SHAPE;
   if (T * (int64_t)k > 0x7FFFFFFF) return K3MOE_ERR_SHAPE;
   const int64_t entries = T * (int64_t)k;
@@ -714,11 +717,27 @@ int moe_expert_cache_route(void* state, size_t state_bytes, int32_t E, int32_t C
   f.cache_w1 = cache_w1;
   f.cache_w3 = cache_w3;
   f.cache_w2 = cache_w2;
-  f.mat13 = (int64_t)I * (D / 32) * 17;
-  f.mat2 = (int64_t)D * (I / 32) * 17;
+  f.mat13 = (int64_t)I * (D / block) * bytes;
+  f.mat2 = (int64_t)D * (I / block) * bytes;
   f.E = E;
   f.C = C;
   return device_status(launch_cache_fetch(f, s));
+}
+
+int moe_expert_cache_route(void* state, size_t state_bytes, int32_t E, int32_t C, const int32_t* topk_ids, int64_t T,
+                           int32_t k, int32_t* slot_ids, const uint8_t* store_w1, const uint8_t* store_w3,
+                           const uint8_t* store_w2, uint8_t* cache_w1, uint8_t* cache_w3, uint8_t* cache_w2, int32_t D,
+                           int32_t I, void* stream) {
+  return cache_route(state, state_bytes, E, C, topk_ids, T, k, slot_ids, store_w1, store_w3, store_w2, cache_w1,
+                     cache_w3, cache_w2, D, I, 32, 17, stream);
+}
+
+int moe_expert_cache_route_q4k(void* state, size_t state_bytes, int32_t E, int32_t C, const int32_t* topk_ids,
+                               int64_t T, int32_t k, int32_t* slot_ids, const uint8_t* store_w1,
+                               const uint8_t* store_w3, const uint8_t* store_w2, uint8_t* cache_w1,
+                               uint8_t* cache_w3, uint8_t* cache_w2, int32_t D, int32_t I, void* stream) {
+  return cache_route(state, state_bytes, E, C, topk_ids, T, k, slot_ids, store_w1, store_w3, store_w2, cache_w1,
+                     cache_w3, cache_w2, D, I, 256, 144, stream);
 }
 
 // ---------------------------------------------------------------------------

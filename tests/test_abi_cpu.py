@@ -28,7 +28,7 @@ def test_library_exports_every_declared_symbol(k3):
                           "moe_mxfp4_ffn_noalloc", "moe_q4k_ffn_workspace_size", "moe_q4k_ffn",
                           "moe_q4k_ffn_profiled", "moe_group_workspace_size", "moe_group_by_expert",
                           "moe_verify_width_distinct", "moe_verify_width_choose", "moe_expert_cache_state_size",
-                          "moe_expert_cache_init", "moe_expert_cache_route", "moe_latent_block_workspace_size",
+                          "moe_expert_cache_init", "moe_expert_cache_route", "moe_expert_cache_route_q4k", "moe_latent_block_workspace_size",
                           "moe_latent_block", "moe_latent_block_profiled"}
     for n in names:
         assert hasattr(k3.lib, n), n
@@ -292,6 +292,24 @@ def test_expert_cache_checks(k3):
     assert r(st=(A, None, A)) == ERR_NULL and r(ca=(A, A, None)) == ERR_NULL
     assert r(state=A + 4) == ERR_ALIGN and r(st=(A + 8, A, A)) == ERR_ALIGN and r(ca=(A, A + 2, A)) == ERR_ALIGN
     assert r(nbytes=need - 1) == ERR_WORKSPACE
+
+
+def test_expert_cache_q4k_checks(k3):
+    # the Q4_K entry: same checks, D and I multiples of 256 (Q4_K blocks)
+    route = k3.lib.moe_expert_cache_route_q4k
+    need = k3.moe_expert_cache_state_size(896, 160)
+
+    def r(state=A, nbytes=need, E=896, C=160, ids=A, T=8, k=16, sid=A, st=(A, A, A), ca=(A, A, A), D=3584, I=3072):
+        return route(state, nbytes, E, C, ids, T, k, sid, *st, *ca, D, I, None)
+
+    assert r(T=0) == OK
+    assert r(D=3584 + 32) == ERR_SHAPE and r(I=3072 + 128) == ERR_SHAPE  # multiples of 32 but not of 256
+    assert r(C=127) == ERR_SHAPE and r(k=65) == ERR_SHAPE
+    assert r(st=(A, A, None)) == ERR_NULL and r(ca=(A, A + 8, A)) == ERR_ALIGN
+    assert r(nbytes=need - 1) == ERR_WORKSPACE
+    # the MXFP4 entry accepts the same D as a multiple of 32 (it fails later, at the workspace check)
+    assert k3.lib.moe_expert_cache_route(A, need - 1, 896, 160, A, 8, 16, A, A, A, A, A, A, A, 3584 + 32, 3072,
+                                         None) == ERR_WORKSPACE
 
 
 K3_BLOCK = dict(H=7168, D=3584, I=3072, Is=3072, E=896, k=16)

@@ -262,3 +262,38 @@ def test_q4k_k3_prefill_two_token_chunks(k3):
     assert np.all(np.isfinite(got))
     ref = ffn_q4k_ref(batch.x, ids, w, host, tokens=np.array(toks))
     check(got[toks], ref, f"q4k T=20000 tokens {toks}")
+
+
+@pytest.mark.parametrize("where", ["device", "pinned"])
+def test_q4k_ffn_through_expert_cache(k3, where):
+    # Q4_K experts staged by moe_expert_cache_route_q4k into 12 slots over 12
+    # Zipf-skewed 3-token batches (hits and evictions): every step the FFN on
+    # the slots gives exactly the bits of the FFN on the store's experts, the
+    # renamed ids follow the oracle's LRU, and the last step matches the oracle
+    from oracle.cache import ExpertCacheRef
+
+    cfg = moe_inputs.TINY.with_(E=40, k=4, D=512, I=768, T=3, logits="zipf", config_id=75)
+    C = 12
+    host = Q4KExperts(cfg)
+    w1, w3, w2 = upload(host, range(cfg.E))
+    store = [w1, w3, w2] if where == "device" else [t.cpu().pin_memory() for t in (w1, w3, w2)]
+    cache = [torch.zeros((C,) + tuple(t.shape[1:]), dtype=torch.uint8, device="cuda") for t in (w1, w3, w2)]
+    state = k3.moe_expert_cache_init(cfg.E, C)
+    ref = ExpertCacheRef(cfg.E, C)
+    print(f"[q4k] through the expert cache, store={where}", flush=True)
+    for step in range(12):
+        batch, x, z, b = moe_inputs.device.upload_batch(cfg, seed=200 + step)
+        ids_d, w_d = k3.moe_route_topk(z, b, cfg.k)
+        slot_ids = k3.moe_expert_cache_route(state, cfg.E, C, ids_d, *store, *cache, q4k=True)
+        got = k3.moe_q4k_ffn(x, slot_ids, w_d, *cache)
+        want = k3.moe_q4k_ffn(x, ids_d, w_d, w1, w3, w2)
+        torch.cuda.synchronize()
+        ids = ids_d.cpu().numpy()
+        ref.route(ids)
+        want_slots = np.array([[ref.slot_of[e] if 0 <= e < cfg.E else -1 for e in row] for row in ids], np.int32)
+        assert np.array_equal(slot_ids.cpu().numpy(), want_slots), step
+        assert torch.equal(got.view(torch.int32), want.view(torch.int32)), step
+    ids_o, w_o = route_ref(batch.z, batch.b, cfg.k)
+    assert np.array_equal(ids, ids_o)
+    check(got.cpu().numpy(), ffn_q4k_ref(batch.x, ids_o, w_o, host), "q4k through the cache")
+    assert ref.hits_total > 0 and ref.misses_total > C  # the cache filled and evicted
