@@ -176,6 +176,44 @@ def test_self_grouping_duplicates_and_invalid_ids(k3):
     assert np.array_equal(again.view(np.uint32), got.view(np.uint32))
 
 
+@pytest.mark.parametrize("T", [1, 3, 8])
+def test_decode_outputs_whatever_the_workspace_holds(k3, T):
+    # decode batches (grouped inside the gate/up launch): the workspace starts
+    # as 0xFF bytes and the output as NaN, so state the launches failed to set
+    # or an output the combine failed to write shows; a second call reuses the
+    # workspace.  A token whose every slot is skipped gets zeros, and a batch
+    # of only skipped entries (no tiles at all) all zeros.
+    print(f"[ffn] decode outputs over a dirty workspace T={T}", flush=True)
+    cfg = moe_inputs.TINY.with_(E=40, k=4, D=512, I=1024, T=T, config_id=50)
+    g = np.random.default_rng(23)
+    ids = np.stack([g.permutation(cfg.E)[: cfg.k] for _ in range(cfg.T)]).astype(np.int32)
+    w = g.random((cfg.T, cfg.k)).astype(np.float32)
+    if T > 1:
+        ids[T // 2, :] = -1  # every slot skipped
+    batch = moe_inputs.make_batch(cfg)
+    dev = device_experts(k3, cfg)
+    ref = ffn_ref(batch.x, ids, w, HostExperts(cfg))
+    x = bf16_dev(batch.x)
+    need = k3.moe_mxfp4_ffn_workspace_size(cfg.T, cfg.D, cfg.I, cfg.E, cfg.k)
+    ws = torch.full((need,), 0xFF, dtype=torch.uint8, device="cuda")
+    outs = []
+    for _ in range(2):
+        out = torch.full((cfg.T, cfg.D), float("nan"), dtype=torch.float32, device="cuda")
+        k3.moe_mxfp4_ffn(x, torch.from_numpy(ids).cuda(), torch.from_numpy(w).cuda(), dev.w1, dev.w3, dev.w2,
+                         out=out, workspace=ws)
+        outs.append(out.cpu().numpy())
+    assert np.all(np.isfinite(outs[0]))
+    assert_ffn_close(outs[0], ref, f"decode over a dirty workspace T={T}")
+    if T > 1:
+        assert np.all(outs[0][T // 2] == 0)
+    assert np.array_equal(outs[0].view(np.uint32), outs[1].view(np.uint32))
+    bad = np.full_like(ids, cfg.E + 1)
+    out = torch.full((cfg.T, cfg.D), float("nan"), dtype=torch.float32, device="cuda")
+    k3.moe_mxfp4_ffn(x, torch.from_numpy(bad).cuda(), torch.from_numpy(w).cuda(), dev.w1, dev.w3, dev.w2,
+                     out=out, workspace=ws)
+    assert np.all(out.cpu().numpy() == 0)
+
+
 def test_mixed_large_and_streaming_experts(k3):
     # one call in which some experts have many rows (large-tile kernels, with a
     # partial last token group) and others a few rows (weight-streaming kernels)
