@@ -17,9 +17,11 @@
 // VGPRs:
 //   weights:     kMats * kF rows x 80 bytes: the 16-byte-aligned window that
 //                holds the step's 68 bytes of the row (its four 17-byte ggml
-//                blocks, exactly as stored) starting at byte 4*(step % 4);
-//   activations: kSrc * kN rows x 256 bytes (+16 bytes of padding so the 16
-//                tokens a ds_read_b128 touches fall in distinct banks).
+//                blocks, exactly as stored) starting at byte 4*(step % 4),
+//                chunk-major within each 16-row group;
+//   activations: kSrc * kN rows x 256 bytes (+16 bytes of padding), the
+//                row's 64-byte quarters rotated by the row (act_rot), so that
+//                no operand read meets a bank conflict.
 // A lane (row rho, lane group g) owns block g of the step for its row: it reads
 // the two 16-byte chunks holding the block, pulls out the exponent byte and the
 // 16 qs bytes, and converts one qs dword per MFMA slice (the next slice's
@@ -63,6 +65,7 @@ constexpr int kWRowDw = 20;     // LDS dwords per weight row per stage: an align
 constexpr int kWRowChunks = 5;  // 16-byte chunks per weight row window
 constexpr int kARowDw = 68;     // LDS dwords per activation row per stage (256 + 16 bytes)
 constexpr int kARowChunks = 17; // 16-byte chunks per activation row (16 data + 1 pad)
+constexpr int kWGroupDw = 16 * kWRowDw;  // LDS dwords of a 16-row weight group per stage (chunk-major)
 constexpr int kXcds = 8;
 constexpr int kMaxSlices = 64;  // 256-wide slices of I the down kernel supports (I <= 16384)
 constexpr int kRescaleSpan = 64;  // down: largest slice-scale spread of a row for the rescaling K loop
@@ -89,6 +92,19 @@ struct BigCfg<false, 64> {  // wave: 4 row groups (64 features) x 4 token groups
 constexpr int kWDw = 2 * 256 * kWRowDw;        // weight dwords per stage (both variants: 512 rows)
 constexpr int kADw = 128 * kARowDw;            // activation dwords per stage (both variants: 128 rows)
 constexpr int kStageDw = kWDw + kADw;          // 18944 dwords = 75776 bytes
+
+// LDS layouts that keep every ds_read_b128 of the K loop free of bank
+// conflicts (measured on gfx950 with the LDS conflict counters: a 16-lane
+// read of 16-byte pieces 272 or 80 bytes apart takes two passes; the layouts
+// below take one):
+//   weights:     a 16-row group of a stage is chunk-major: chunk c of row r at
+//                dword 64 c + 4 r, so the 64 lanes reading chunk g of rows
+//                rho (lane = rho + 16 g) read 1 KB in order;
+//   activations: rows of 256 + 16 bytes; the row's four 64-byte quarters
+//                rotated by act_rot(r % 16), so quarter q of row r is stored at
+//                quarter (q + act_rot(r)) % 4 and chunk i of a quarter stays
+//                at offset 16 i (an immediate of the read).
+__device__ __forceinline__ int act_rot(int r) { return (r >> 2) & 3; }
 
 __device__ __forceinline__ int p_to_elem(int p) { return 16 * (p & 1) + 4 * (p >> 3) + ((p >> 1) & 3); }
 
@@ -227,9 +243,11 @@ __global__ __launch_bounds__(kThreads) void ffn_big_kernel(GemmArgs a) {
   // a per-lane byte offset fixed for the whole kernel, and the K step in the
   // scalar offset.  Out-of-range offsets would read zeros instead of faulting.
   //
-  // Weights: loader wave w fills LDS rows 64w..64w+63, all of one matrix; load
-  // j moves 16-byte chunk t = 64j + lane of those rows (row t/5, chunk t%5).
-  // LDS rows are in consumer order: row (mi, consumer wave, row group, rho).
+  // Weights: loader wave w fills LDS rows 64w..64w+63 (four 16-row groups),
+  // all of one matrix; load j moves 16-byte chunk t = 64j + lane of them, in
+  // the chunk-major order of each group (group t/80, chunk (t%80)/16, row
+  // t%16).  LDS rows are in consumer order: row (mi, consumer wave, row
+  // group, rho).
   const int wmat = (64 * wave) / C::kF;  // matrix of the rows this wave loads
   const int wrow0 = 64 * wave - wmat * C::kF;
   const uint8_t* wmat_base = (wmat == 0 ? a.wa : a.wb) + (size_t)tile.expert * mat_bytes + (size_t)f0 * row_bytes;
@@ -239,7 +257,8 @@ __global__ __launch_bounds__(kThreads) void ffn_big_kernel(GemmArgs a) {
 #pragma unroll
   for (int j = 0; j < kWRowChunks; ++j) {
     const int t = 64 * j + lane;
-    const int sl = t / kWRowChunks, ch = t - sl * kWRowChunks;
+    const int grp = t / (16 * kWRowChunks), q = t - grp * (16 * kWRowChunks);
+    const int sl = 16 * grp + (q & 15), ch = q >> 4;
     const int r_tile = wrow0 + sl;                   // LDS row within the matrix tile
     const int cw = r_tile / (C::kRG * 16);           // consumer wave
     const int r = r_tile - cw * (C::kRG * 16);       // (row group, rho) within the consumer wave
@@ -252,8 +271,10 @@ __global__ __launch_bounds__(kThreads) void ffn_big_kernel(GemmArgs a) {
   }
   // Activations: wave w fills rows 16w..16w+15 (272 flat 16-byte chunks), all
   // of one source (x / h_hi for gate/up, h_hi or h_lo for down); load j moves
-  // chunk f = 64j + lane of them (row f/17, chunk f%17; chunk 16 is padding and
-  // re-reads chunk 15; lanes past the 272 chunks are never issued).
+  // LDS chunk f = 64j + lane of them (row f/17, stored position p = f%17,
+  // which holds chunk 4 ((p/4 - act_rot(row)) % 4) + p%4 of the row; position
+  // 16 is padding and re-reads chunk 15; lanes past the 272 chunks are never
+  // issued).
   const int asrc = (16 * wave) / C::kN;
   const uint16_t* abase = (kGateUp || asrc == 0) ? a.act : a.act_lo;
   const __amdgpu_buffer_rsrc_t arsrc =
@@ -263,9 +284,9 @@ __global__ __launch_bounds__(kThreads) void ffn_big_kernel(GemmArgs a) {
   for (int j = 0; j < 5; ++j) {
     const int f = 64 * j + lane;
     int rl = f / kARowChunks;
-    int ch = f - rl * kARowChunks;
-    ch = ch > 15 ? 15 : ch;
+    int p = f - rl * kARowChunks;
     rl = rl > 15 ? 15 : rl;
+    const int ch = p > 15 ? 15 : 4 * (((p >> 2) - act_rot(rl)) & 3) + (p & 3);
     const int t = 16 * wave + rl - asrc * C::kN;
     aoffs[j] = ((uint32_t)tok_src[t] * (uint32_t)K + 8 * ch) * 2;  // bytes
   }
@@ -278,7 +299,7 @@ __global__ __launch_bounds__(kThreads) void ffn_big_kernel(GemmArgs a) {
   auto issue = [&](int stage, int buf) {
     uint32_t* const lb = buf ? lds1 : lds0;
     uint32_t* wl = lb + 64 * wave * kWRowDw;
-    uint32_t* al = lb + kWDw + 272 * 4 * wave;
+    uint32_t* al = lb + kWDw + 16 * kARowDw * wave;  // 272 chunks per wave
     // 16-byte aligned start of the step's 68 bytes: byte 68 * (stage % 4) of
     // the row's 272 bytes in 512-wide stage stage / 4 (4352 bytes per stage)
     const int wso = 4352 * (stage >> 2) + 64 * (stage & 3);
@@ -293,13 +314,16 @@ __global__ __launch_bounds__(kThreads) void ffn_big_kernel(GemmArgs a) {
   };
 
   // LDS dword of chunk g of the window of MFMA row rho of row group rg (block g
-  // of the step lies in chunks g and g+1).
+  // of the step lies in chunks g and g+1, 64 dwords apart).
   int wrow_dw[C::kMats][C::kRG];
 #pragma unroll
   for (int mi = 0; mi < C::kMats; ++mi)
 #pragma unroll
     for (int rg = 0; rg < C::kRG; ++rg)
-      wrow_dw[mi][rg] = (mi * C::kF + wave * (C::kRG * 16) + rg * 16 + rho) * kWRowDw + 4 * g;
+      wrow_dw[mi][rg] = ((mi * C::kF + wave * (C::kRG * 16)) / 16 + rg) * kWGroupDw + 64 * g + 4 * rho;
+  // LDS dword of this lane's activation chunk 4g (quarter g) in token group 0;
+  // chunk 4g + i adds 4 i, token group n adds 16 * kARowDw * n
+  const int aread_dw = rho * kARowDw + 16 * ((g + act_rot(rho)) & 3);
   // block g starts at byte 4*phase + g of chunk g; its qs dword i is bytes
   // g+1..g+4 of the dword pair (phase+i, phase+i+1) of the two chunks
   const uint32_t qsel = 0x03020100u + 0x01010101u * (uint32_t)(g + 1);
@@ -374,7 +398,7 @@ __global__ __launch_bounds__(kThreads) void ffn_big_kernel(GemmArgs a) {
 #pragma unroll
       for (int rg = 0; rg < C::kRG; ++rg) {
         const uint4 c0 = *reinterpret_cast<const uint4*>(wl + wrow_dw[mi][rg]);
-        const uint4 c1 = *reinterpret_cast<const uint4*>(wl + wrow_dw[mi][rg] + 4);
+        const uint4 c1 = *reinterpret_cast<const uint4*>(wl + wrow_dw[mi][rg] + 64);
         const uint32_t w[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
         eb[mi][rg] = __builtin_amdgcn_ubfe(w[PH], 8 * g, 8);
 #pragma unroll
@@ -401,8 +425,7 @@ __global__ __launch_bounds__(kThreads) void ffn_big_kernel(GemmArgs a) {
         // activations: block g of the step, P-order positions 8i..8i+7 (chunk
         // 4g+i); one operand is read ahead while the previous one feeds its MFMAs
         auto bread = [&](int n) {
-          const int row = n * 16 + rho;
-          return __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(al + row * kARowDw + 4 * (4 * g + i)));
+          return __builtin_bit_cast(bf16x8_t, *reinterpret_cast<const uint4*>(al + n * 16 * kARowDw + aread_dw + 4 * i));
         };
         auto convert_next = [&](int pr) {
           return decode_dword(q[pr / C::kRG][pr % C::kRG][i + 1], e8m0_to_f32(eb[pr / C::kRG][pr % C::kRG]));
@@ -453,8 +476,8 @@ __global__ __launch_bounds__(kThreads) void ffn_big_kernel(GemmArgs a) {
           f16x8_t(&aop)[C::kRG] = ops[i & 1];
           f16x8_t(&anext)[C::kRG] = ops[(i + 1) & 1];
           auto bread = [&](int n) {
-            const int row = n * 16 + rho;
-            const f16x8_t hv = __builtin_bit_cast(f16x8_t, *reinterpret_cast<const uint4*>(al + row * kARowDw + 4 * (4 * g + i)));
+            const f16x8_t hv =
+                __builtin_bit_cast(f16x8_t, *reinterpret_cast<const uint4*>(al + n * 16 * kARowDw + aread_dw + 4 * i));
             if constexpr (kResc) return hv;
             else return scale_h(hv, n);
           };
@@ -485,10 +508,9 @@ __global__ __launch_bounds__(kThreads) void ffn_big_kernel(GemmArgs a) {
 #pragma unroll
           for (int n = 0; n < kB; ++n) {
             if (!kFull && n >= nlive) break;
-            const int row = n * 16 + rho;
             bf16x8_t bhi, blo;
             const f16x8_t hv =
-                scale_h(__builtin_bit_cast(f16x8_t, *reinterpret_cast<const uint4*>(al + row * kARowDw + 4 * (4 * g + i))), n);
+                scale_h(__builtin_bit_cast(f16x8_t, *reinterpret_cast<const uint4*>(al + n * 16 * kARowDw + aread_dw + 4 * i)), n);
             split_f16x8(__builtin_bit_cast(uint4, hv), bhi, blo);
 #pragma unroll
             for (int rg = 0; rg < C::kRG; ++rg) {
