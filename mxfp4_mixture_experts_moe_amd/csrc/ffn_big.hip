@@ -106,6 +106,25 @@ constexpr int kStageDw = kWDw + kADw;          // 18944 dwords = 75776 bytes
 //                at offset 16 i (an immediate of the read).
 __device__ __forceinline__ int act_rot(int r) { return (r >> 2) & 3; }
 
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+// Both weight chunks (g and g + 1, 256 bytes apart) of the four (matrix, row
+// group) pairs, as whole 16-byte reads: with separate reads the compiler
+// keeps only the dwords a step's phase uses, and 4- or 8-byte reads of these
+// 16-byte-strided rows meet bank conflicts.  One wait for all eight.
+__device__ __forceinline__ void read_weight_chunks(uint32_t a0, uint32_t a1, uint32_t a2, uint32_t a3,
+                                                   u32x4_t (&c)[4][2]) {
+  asm volatile(
+      "ds_read_b128 %0, %8\n\tds_read_b128 %1, %8 offset:256\n\t"
+      "ds_read_b128 %2, %9\n\tds_read_b128 %3, %9 offset:256\n\t"
+      "ds_read_b128 %4, %10\n\tds_read_b128 %5, %10 offset:256\n\t"
+      "ds_read_b128 %6, %11\n\tds_read_b128 %7, %11 offset:256\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(c[0][0]), "=&v"(c[0][1]), "=&v"(c[1][0]), "=&v"(c[1][1]), "=&v"(c[2][0]), "=&v"(c[2][1]),
+        "=&v"(c[3][0]), "=&v"(c[3][1])
+      : "v"(a0), "v"(a1), "v"(a2), "v"(a3)
+      : "memory");
+}
+
 __device__ __forceinline__ int p_to_elem(int p) { return 16 * (p & 1) + 4 * (p >> 3) + ((p >> 1) & 3); }
 
 __device__ __forceinline__ float e8m0_to_f32(uint32_t e) { return __uint_as_float(e ? (e << 23) : 0x00400000u); }
@@ -156,7 +175,9 @@ __global__ __launch_bounds__(kThreads) void ffn_big_kernel(GemmArgs a) {
   // issued into the other one, which serialises loading and computing.
   __shared__ uint32_t lds0[kStageDw], lds1[kStageDw];
   __shared__ int32_t tok_src[C::kN];  // source row of every token slot of the tile
-  __shared__ int8_t hs_l[kGateUp ? 1 : C::kN * kMaxSlices];  // down: h scale of every (row, slice)
+  // down: h scale of every (slice, row), rows contiguous so that the 16 rows of
+  // a token group are read without bank conflicts
+  __shared__ int8_t hs_l[kGateUp ? 1 : C::kN * kMaxSlices];
   __shared__ int srow_l[kGateUp ? 1 : C::kN];                 // down: largest h scale of every row
   __shared__ float red[kGateUp ? kThreads / 64 * C::kN : 1];   // gate/up: per-wave row maxima of |h|
   __shared__ int sexp[kGateUp ? C::kN : 1];                    // gate/up: h scale exponent per row
@@ -213,7 +234,7 @@ __global__ __launch_bounds__(kThreads) void ffn_big_kernel(GemmArgs a) {
     const int nsl = K >> 8;  // 256-wide slices of h
     for (int i = tid; i < C::kN * nsl; i += kThreads) {
       const int m = i / nsl, sl = i - m * nsl;
-      hs_l[m * kMaxSlices + sl] = m < tile.nrows ? a.h_scale[(int64_t)(tile.row0 + m) * nsl + sl] : (int8_t)0;
+      hs_l[sl * C::kN + m] = m < tile.nrows ? a.h_scale[(int64_t)(tile.row0 + m) * nsl + sl] : (int8_t)0;
     }
   }
   __syncthreads();
@@ -227,7 +248,7 @@ __global__ __launch_bounds__(kThreads) void ffn_big_kernel(GemmArgs a) {
       const int nsl = K >> 8;
       int mx = -128, mn = 127;
       for (int sl = 0; sl < nsl; ++sl) {
-        const int v = hs_l[tid * kMaxSlices + sl];
+        const int v = hs_l[sl * C::kN + tid];
         mx = max(mx, v);
         mn = min(mn, v);
       }
@@ -346,7 +367,7 @@ __global__ __launch_bounds__(kThreads) void ffn_big_kernel(GemmArgs a) {
 #pragma unroll
     for (int tg = 0; tg < (kGateUp ? 1 : C::kTG); ++tg) {
       const int t = tg * 16 + rho;
-      const int d = (int)hs_l[t * kMaxSlices + sl] - srow_l[t];
+      const int d = (int)hs_l[sl * C::kN + t] - srow_l[t];
       const uint32_t hb = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)ldexpf(1.0f, d));
       hmul[tg] = hb | (hb << 16);
     }
@@ -365,8 +386,8 @@ __global__ __launch_bounds__(kThreads) void ffn_big_kernel(GemmArgs a) {
 #pragma unroll
     for (int tg = 0; tg < (kGateUp ? 1 : C::kTG); ++tg) {
       const int t = tg * 16 + rho;
-      const int to = to_row ? srow_l[t] : (int)hs_l[t * kMaxSlices + sl_from + 1];
-      const float f = ldexpf(1.0f, (int)hs_l[t * kMaxSlices + sl_from] - to);
+      const int to = to_row ? srow_l[t] : (int)hs_l[(sl_from + 1) * C::kN + t];
+      const float f = ldexpf(1.0f, (int)hs_l[sl_from * C::kN + t] - to);
 #pragma unroll
       for (int rg = 0; rg < C::kRG; ++rg)
 #pragma unroll
@@ -393,12 +414,19 @@ __global__ __launch_bounds__(kThreads) void ffn_big_kernel(GemmArgs a) {
     // qs dwords and block exponent of block g of every (matrix, row group)
     uint32_t q[C::kMats][C::kRG][4];
     uint32_t eb[C::kMats][C::kRG];
+    static_assert(C::kMats * C::kRG == 4, "four (matrix, row group) pairs per wave");
+    u32x4_t wc[4][2];
+    {
+      const uint32_t wb = (uint32_t)(uintptr_t)wl;
+      read_weight_chunks(wb + 4u * (uint32_t)wrow_dw[0][0], wb + 4u * (uint32_t)wrow_dw[(1 / C::kRG) % C::kMats][1 % C::kRG],
+                         wb + 4u * (uint32_t)wrow_dw[(2 / C::kRG) % C::kMats][2 % C::kRG],
+                         wb + 4u * (uint32_t)wrow_dw[(3 / C::kRG) % C::kMats][3 % C::kRG], wc);
+    }
 #pragma unroll
     for (int mi = 0; mi < C::kMats; ++mi)
 #pragma unroll
       for (int rg = 0; rg < C::kRG; ++rg) {
-        const uint4 c0 = *reinterpret_cast<const uint4*>(wl + wrow_dw[mi][rg]);
-        const uint4 c1 = *reinterpret_cast<const uint4*>(wl + wrow_dw[mi][rg] + 64);
+        const u32x4_t c0 = wc[mi * C::kRG + rg][0], c1 = wc[mi * C::kRG + rg][1];
         const uint32_t w[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
         eb[mi][rg] = __builtin_amdgcn_ubfe(w[PH], 8 * g, 8);
 #pragma unroll
