@@ -18,9 +18,9 @@
 //                 workgroup of 4 waves (64 x 64 each: 2 x 2 MFMA 32x32x16
 //                 bf16 blocks), K in steps of 64 double-buffered in LDS and
 //                 filled by direct global -> LDS buffer loads; the eight
-//                 16-byte chunks of a 128-byte LDS row are XOR-swizzled by the
-//                 row's low 3 bits so that an operand read (32 rows, one chunk
-//                 each) touches distinct banks.  Workgroups go to XCDs in
+//                 16-byte chunks of a 128-byte LDS row are XOR-swizzled by
+//                 (row / 2) % 8 so that an operand read (32 rows, one chunk
+//                 each) meets no bank conflict.  Workgroups go to XCDs in
 //                 contiguous runs of a grouped order (8 feature tiles x every
 //                 token tile), so tiles that share operands share an L2.
 //                 Split-K when the tiles alone cannot fill the GPU.
@@ -82,6 +82,11 @@ __device__ __forceinline__ uint16_t bf16_bits(float v) { return __builtin_bit_ca
 
 // LDS byte offset of 16-byte chunk c of row r of an operand tile.
 __device__ __forceinline__ int swz(int r, int c) { return r * kRowB + ((c ^ (r & 7)) << 4); }
+// The tile kernel's operand reads (lanes 0-31: rows r..r+31 at chunk c, lanes
+// 32-63: the same rows at chunk c + 1) meet no bank conflict when the key is
+// (r / 2) % 8; with r % 8 rows r and r + 8 of a 16-lane group share banks
+// (measured on gfx950 with the LDS conflict counters).
+__device__ __forceinline__ int swz_tile(int r, int c) { return r * kRowB + ((c ^ ((r >> 1) & 7)) << 4); }
 
 // Store a lane's 4 consecutive features of one token (masked at the edges).
 __device__ __forceinline__ void store4(float* dst, const f32x16_t& acc, int q, int valid) {
@@ -125,14 +130,15 @@ __global__ __launch_bounds__(kThreads, 2) void dense_tile_kernel(DenseGemmArgs a
   const int kend = kbeg + a.split_steps < ktot ? kbeg + a.split_steps : ktot;
 
   // per-lane load offsets of the 4 row groups this wave fills (rows
-  // 32*wave + 8j + lane/8, the chunk that lands at position lane%8)
+  // r = 32*wave + 8j + lane/8, the chunk that lands at position lane%8, i.e.
+  // chunk (lane%8) ^ ((r/2) % 8) with (r/2) % 8 = (4j + lane/16) % 8)
   const int lrow = 32 * wave + (lane >> 3);
-  const int lchunk = (lane & 7) ^ (lane >> 3);
   uint32_t woff[2][4], aoff[2][4];
 #pragma unroll
   for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
+      const int lchunk = (lane & 7) ^ ((4 * j + (lane >> 4)) & 7);
       woff[ks][j] = (uint32_t)((lrow + 8 * j) * sv.ldw[ks] * 2 + 16 * lchunk);
       aoff[ks][j] = (uint32_t)((lrow + 8 * j) * a.lda[ks] * 2 + 16 * lchunk);
     }
@@ -184,8 +190,8 @@ __global__ __launch_bounds__(kThreads, 2) void dense_tile_kernel(DenseGemmArgs a
       bf16x8_t wf[2], af[2];
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
-        wf[i] = *reinterpret_cast<const bf16x8_t*>(wl + swz(64 * fm + 32 * i + l32, c));
-        af[i] = *reinterpret_cast<const bf16x8_t*>(al + swz(64 * tm + 32 * i + l32, c));
+        wf[i] = *reinterpret_cast<const bf16x8_t*>(wl + swz_tile(64 * fm + 32 * i + l32, c));
+        af[i] = *reinterpret_cast<const bf16x8_t*>(al + swz_tile(64 * tm + 32 * i + l32, c));
       }
 #pragma unroll
       for (int i = 0; i < 2; ++i)
