@@ -874,7 +874,7 @@ def main():
             extra[w] = r
         del dq
     if args.cpu_baseline and not head_q4k:
-        sample = args.cpu_sample_tokens or (cfg.T if cfg.T <= 64 else 8)  # about 11 s of oracle work at K3 shape
+        sample = args.cpu_sample_tokens or (cfg.T if cfg.T <= 64 else 12)  # about 12 s of oracle work at K3 shape
         result["cpu_baseline"] = cpu_baseline(cfg, batch0, sample)
     print(json.dumps(result), flush=True)
 
